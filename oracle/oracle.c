@@ -1,0 +1,314 @@
+/*
+ * CPU oracle for per-GPU MoE expert-parallel dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg use it.  It shares no source with the HIP kernels.
+ *
+ * Plain, slow, single-threaded loops in the order the definitions are stated.
+ * Floating point that the pages leave open is done in fp64 and rounded once.
+ *
+ * Sources (page title, then section):
+ *  [EC]  "Expert Coupling in MoE Pretraining: Reducing All-to-All Overhead with
+ *        Correlated Placement and Token Shuffling" (summary page).
+ *        - "Background": each token goes to its top-k experts.
+ *        - "Method 1: Correlated Expert Placement + Deduplicating Dispatcher":
+ *          the conventional dispatch sends one row per (token, expert); the
+ *          deduplicating dispatcher sends one row per distinct (token,
+ *          destination rank) carrying the expert ids and routing probabilities
+ *          of that rank's experts; the correlation graph W[e][e'] counts the
+ *          tokens that select both e and e'; each GPU holds E/EP experts.
+ *  [DD]  "DODOCO: MoE AlltoAll Traffic Matrices on Real Text" (dataset card).
+ *        - "Setup": contiguous placement, rank r holds experts r*E/R..;
+ *          the counts are the dispatcher's per-destination input splits.
+ *        - "Reading the counts": one count per token-expert assignment, even when
+ *          several experts share a destination; each row sums to tokens*top-k;
+ *          each rank's expert-block sum is its receive total.
+ *        - "send_matrices.csv columns": combine returns the same volumes in
+ *          reverse.
+ *
+ * Readings where the pages are silent (each one is listed in the design notes):
+ *  - gates: softmax over the k selected logits, in fp64, rounded once to fp32;
+ *  - top-k order: logit descending, ties to the lower expert index, IEEE
+ *    comparison (so -0.0 ties +0.0);
+ *  - send buffer order: rank ascending, then expert id, then token (non-dedup);
+ *    rank ascending, then token (dedup);
+ *  - dedup row weight: sum of that rank's gates in ascending expert order, fp64,
+ *    rounded once to fp32;
+ *  - combine: sum over the distinct rows serving a token of weight*row, exact
+ *    products summed in fp64, rounded once to bf16 (round to nearest even);
+ *  - W's diagonal counts the tokens selecting e.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- route --- */
+
+typedef struct {
+    float logit;
+    int32_t expert;
+} oracle_cand;
+
+/* Order: larger logit first; equal logits (IEEE ==, so -0.0 == +0.0): lower
+ * expert index first. */
+static int oracle_cand_cmp(const void* pa, const void* pb) {
+    const oracle_cand* a = (const oracle_cand*)pa;
+    const oracle_cand* b = (const oracle_cand*)pb;
+    if (a->logit > b->logit) return -1;
+    if (a->logit < b->logit) return 1;
+    return (a->expert > b->expert) - (a->expert < b->expert);
+}
+
+/* [EC] "Background": each token is routed to its top-k experts.
+ * idx[t][j] = the j-th expert of token t in (logit desc, index asc) order.
+ * gate[t][j] = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0), fp64, rounded once. */
+int oracle_route_topk(const float* logits, int64_t tokens, int n_experts, int top_k,
+                      int32_t* idx, float* gate) {
+    if (top_k < 1 || top_k > n_experts) return 1;
+    oracle_cand* c = (oracle_cand*)malloc(sizeof(oracle_cand) * (size_t)n_experts);
+    double* ex = (double*)malloc(sizeof(double) * (size_t)top_k);
+    if (!c || !ex) { free(c); free(ex); return 2; }
+    for (int64_t t = 0; t < tokens; ++t) {
+        const float* row = logits + t * n_experts;
+        for (int e = 0; e < n_experts; ++e) {
+            c[e].logit = row[e];
+            c[e].expert = e;
+        }
+        qsort(c, (size_t)n_experts, sizeof(oracle_cand), oracle_cand_cmp);
+        const double l0 = (double)c[0].logit;
+        double s = 0.0;
+        for (int j = 0; j < top_k; ++j) {
+            ex[j] = exp((double)c[j].logit - l0);
+            s += ex[j];
+        }
+        for (int j = 0; j < top_k; ++j) {
+            idx[t * top_k + j] = c[j].expert;
+            gate[t * top_k + j] = (float)(ex[j] / s);
+        }
+    }
+    free(c);
+    free(ex);
+    return 0;
+}
+
+/* ------------------------------------------------------- counts, offsets --- */
+
+/* [DD] "Reading the counts" and [EC] "Method 1".
+ * expert_counts[e] = #(t, j) with idx[t][j] == e.
+ * Non-dedup: rank_counts[r] = sum of expert_counts over the experts placed on r.
+ * Dedup:     rank_counts[r] = #tokens with at least one selected expert on r.
+ * rank_offsets = exclusive scan of rank_counts (R+1 entries).
+ * expert_offsets[e] = rank_offsets[place[e]] + counts of the experts on the same
+ * rank with a lower id (the start of e's segment in the non-dedup buffer). */
+int oracle_send_counts(const int32_t* idx, int64_t tokens, int n_experts, int top_k,
+                       int n_ranks, const int32_t* place, int dedup,
+                       int32_t* expert_counts, int32_t* rank_counts,
+                       int32_t* rank_offsets, int32_t* expert_offsets) {
+    for (int e = 0; e < n_experts; ++e) expert_counts[e] = 0;
+    for (int r = 0; r < n_ranks; ++r) rank_counts[r] = 0;
+    for (int64_t t = 0; t < tokens; ++t)
+        for (int j = 0; j < top_k; ++j) expert_counts[idx[t * top_k + j]] += 1;
+    if (!dedup) {
+        for (int e = 0; e < n_experts; ++e) rank_counts[place[e]] += expert_counts[e];
+    } else {
+        for (int64_t t = 0; t < tokens; ++t) {
+            for (int r = 0; r < n_ranks; ++r) {
+                int hit = 0;
+                for (int j = 0; j < top_k; ++j)
+                    if (place[idx[t * top_k + j]] == r) hit = 1;
+                rank_counts[r] += hit;
+            }
+        }
+    }
+    rank_offsets[0] = 0;
+    for (int r = 0; r < n_ranks; ++r) rank_offsets[r + 1] = rank_offsets[r] + rank_counts[r];
+    if (expert_offsets) {
+        for (int e = 0; e < n_experts; ++e) {
+            int32_t off = rank_offsets[place[e]];
+            for (int e2 = 0; e2 < e; ++e2)
+                if (place[e2] == place[e]) off += expert_counts[e2];
+            expert_offsets[e] = off;
+        }
+    }
+    return 0;
+}
+
+/* --------------------------------------------------- non-dedup dispatch --- */
+
+/* [EC] "Method 1" (conventional top-k dispatch) and [DD] "Reading the counts":
+ * one row per (token, expert).  Rows are written in the order the send buffer
+ * is laid out: rank ascending, expert ascending within a rank, token ascending
+ * within an expert.  Walking tokens in order and bumping a per-expert cursor
+ * that starts at expert_offsets[e] produces exactly that order. */
+int oracle_dispatch(const uint8_t* x, const int32_t* idx, const float* gate,
+                    int64_t tokens, int row_bytes, int n_experts, int top_k,
+                    const int32_t* expert_offsets, uint8_t* send, int32_t* row_token,
+                    int32_t* row_expert, float* row_weight, int32_t* slot_row) {
+    int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_experts);
+    if (!cursor) return 2;
+    for (int e = 0; e < n_experts; ++e) cursor[e] = expert_offsets[e];
+    for (int64_t t = 0; t < tokens; ++t) {
+        for (int j = 0; j < top_k; ++j) {
+            const int e = idx[t * top_k + j];
+            const int32_t p = cursor[e]++;
+            if (send) memcpy(send + (int64_t)p * row_bytes, x + t * row_bytes, (size_t)row_bytes);
+            row_token[p] = (int32_t)t;
+            row_expert[p] = e;
+            row_weight[p] = gate[t * top_k + j];
+            slot_row[t * top_k + j] = p;
+        }
+    }
+    free(cursor);
+    return 0;
+}
+
+/* ------------------------------------------------------- dedup dispatch --- */
+
+/* [EC] "Method 1", deduplicating dispatcher: one row per distinct (token,
+ * destination rank).  The row carries the ids of that rank's selected experts
+ * (ascending, padded with -1), their gates (aligned, padded with 0) and
+ * row_weight = the sum of those gates.  Send buffer order: rank ascending,
+ * token ascending within a rank.  slot_row[t][j] = the row serving slot j. */
+int oracle_dispatch_dedup(const uint8_t* x, const int32_t* idx, const float* gate,
+                          int64_t tokens, int row_bytes, int n_experts, int top_k,
+                          int n_ranks, const int32_t* place, const int32_t* rank_offsets,
+                          uint8_t* send, int32_t* row_token, int32_t* row_experts,
+                          float* row_gates, float* row_weight, int32_t* slot_row,
+                          int32_t* n_rows) {
+    (void)n_experts;
+    int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_ranks);
+    int* sel = (int*)malloc(sizeof(int) * (size_t)top_k);
+    if (!cursor || !sel) { free(cursor); free(sel); return 2; }
+    for (int r = 0; r < n_ranks; ++r) cursor[r] = rank_offsets[r];
+    for (int64_t t = 0; t < tokens; ++t) {
+        const int32_t* ti = idx + t * top_k;
+        for (int r = 0; r < n_ranks; ++r) {
+            /* the slots of token t whose expert lives on rank r */
+            int ns = 0;
+            for (int j = 0; j < top_k; ++j)
+                if (place[ti[j]] == r) sel[ns++] = j;
+            if (ns == 0) continue;
+            /* order those slots by expert id (insertion sort, ns <= k) */
+            for (int a = 1; a < ns; ++a) {
+                int v = sel[a], b = a - 1;
+                while (b >= 0 && ti[sel[b]] > ti[v]) { sel[b + 1] = sel[b]; --b; }
+                sel[b + 1] = v;
+            }
+            const int32_t p = cursor[r]++;
+            if (send) memcpy(send + (int64_t)p * row_bytes, x + t * row_bytes, (size_t)row_bytes);
+            row_token[p] = (int32_t)t;
+            double wsum = 0.0;
+            for (int c = 0; c < top_k; ++c) {
+                if (c < ns) {
+                    row_experts[(int64_t)p * top_k + c] = ti[sel[c]];
+                    row_gates[(int64_t)p * top_k + c] = gate[t * top_k + sel[c]];
+                    wsum += (double)gate[t * top_k + sel[c]];
+                } else {
+                    row_experts[(int64_t)p * top_k + c] = -1;
+                    row_gates[(int64_t)p * top_k + c] = 0.0f;
+                }
+            }
+            row_weight[p] = (float)wsum;
+            for (int c = 0; c < ns; ++c) slot_row[t * top_k + sel[c]] = p;
+        }
+    }
+    *n_rows = rank_offsets[n_ranks];
+    free(cursor);
+    free(sel);
+    return 0;
+}
+
+/* -------------------------------------------------------------- combine --- */
+
+/* bf16 value nearest to d, ties to even (IEEE round to nearest even), as bits.
+ * Written from the definition: the quantum of a bf16 with leading-bit exponent
+ * p is 2^(p-7) (7 fraction bits), with p clamped at -126 below (subnormals);
+ * d / quantum is exact, nearbyint rounds it half-to-even in the default mode. */
+uint16_t oracle_bf16_from_double(double d) {
+    if (isnan(d)) return (uint16_t)(signbit(d) ? 0xFFC0u : 0x7FC0u);
+    if (isinf(d)) return (uint16_t)(signbit(d) ? 0xFF80u : 0x7F80u);
+    if (d == 0.0) return (uint16_t)(signbit(d) ? 0x8000u : 0x0000u);
+    int ex;
+    (void)frexp(d, &ex);          /* |d| = m * 2^ex, 0.5 <= m < 1 */
+    int lead = ex - 1;            /* exponent of d's leading bit */
+    if (lead < -126) lead = -126;
+    const double q = ldexp(1.0, lead - 7);
+    const double r = nearbyint(d / q) * q;
+    const double max_bf16 = ldexp(255.0, 127 - 7);   /* 0x7F7F = (2 - 2^-7) * 2^127 */
+    if (fabs(r) > max_bf16) return (uint16_t)(signbit(d) ? 0xFF80u : 0x7F80u);
+    if (r == 0.0) return (uint16_t)(signbit(d) ? 0x8000u : 0x0000u);
+    const float f = (float)r;     /* exact: r is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+static double oracle_bf16_to_double(uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* [EC] "The Communication Bottleneck" (dispatch, experts, combine) and [DD]
+ * "send_matrices.csv columns" (combine is the reverse exchange): each token's
+ * output is the weighted sum of the rows that served it.
+ * out[t][h] = bf16( sum over distinct rows r in slot_row[t][.] (r >= 0) of
+ *                   w[r] * rows[r][h] ), summed exactly enough in fp64
+ * (each product of an fp32 and a bf16 is exact in fp64), rounded once.
+ * w == NULL means weight 1 for every row.  Rows are visited in ascending index
+ * order; the sum starts at -0.0 so that an all-(-0) input stays -0. */
+int oracle_combine(const uint16_t* rows, const float* w, const int32_t* slot_row,
+                   int64_t tokens, int hidden_dim, int top_k, uint16_t* out) {
+    int32_t* rs = (int32_t*)malloc(sizeof(int32_t) * (size_t)top_k);
+    if (!rs) return 2;
+    for (int64_t t = 0; t < tokens; ++t) {
+        /* distinct non-negative rows, ascending */
+        int nr = 0;
+        for (int j = 0; j < top_k; ++j) {
+            const int32_t r = slot_row[t * top_k + j];
+            if (r < 0) continue;
+            int seen = 0;
+            for (int i = 0; i < nr; ++i) if (rs[i] == r) seen = 1;
+            if (!seen) rs[nr++] = r;
+        }
+        for (int a = 1; a < nr; ++a) {
+            int32_t v = rs[a];
+            int b = a - 1;
+            while (b >= 0 && rs[b] > v) { rs[b + 1] = rs[b]; --b; }
+            rs[b + 1] = v;
+        }
+        for (int h = 0; h < hidden_dim; ++h) {
+            double acc = -0.0;
+            for (int i = 0; i < nr; ++i) {
+                const double wr = w ? (double)w[rs[i]] : 1.0;
+                acc += wr * oracle_bf16_to_double(rows[(int64_t)rs[i] * hidden_dim + h]);
+            }
+            out[t * hidden_dim + h] = oracle_bf16_from_double(acc);
+        }
+    }
+    free(rs);
+    return 0;
+}
+
+/* --------------------------------------------------------- co-selection --- */
+
+/* [EC] "Method 1": W[e][e'] counts the tokens that select both e and e'
+ * (e != e'); the diagonal W[e][e] counts the tokens selecting e.  Only the first
+ * `tokens` tokens are used ("Correlation Formation and Stability": ~4096 tokens
+ * suffice).  Accumulates into W. */
+int oracle_coselect(const int32_t* idx, int64_t tokens, int n_experts, int top_k,
+                    int32_t* W) {
+    for (int64_t t = 0; t < tokens; ++t) {
+        const int32_t* ti = idx + t * top_k;
+        for (int a = 0; a < top_k; ++a) {
+            for (int b = 0; b < top_k; ++b) {
+                /* a == b: the diagonal; a != b: each ordered pair once */
+                W[(int64_t)ti[a] * n_experts + ti[b]] += 1;
+            }
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,173 @@
+"""numpy front end of the CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product path.  It does not import
+the HIP package and the HIP package does not import it.
+
+Every function takes and returns numpy arrays on the host and runs the plain C
+loops of oracle.c on one host thread.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# Plain IEEE double arithmetic: no fast-math, no contraction into FMA.
+GCC_CMD = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", _LIB, _SRC, "-lm"]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (gcc, host only)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        subprocess.run(GCC_CMD, check=True)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int
+        L.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
+        L.oracle_send_counts.argtypes = [P, i64, i32, i32, i32, P, i32, P, P, P, P]
+        L.oracle_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, P, P, P, P, P, P]
+        L.oracle_dispatch_dedup.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P,
+                                            P, P, P, P, P, P, P]
+        L.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
+        L.oracle_coselect.argtypes = [P, i64, i32, i32, P]
+        L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+        L.oracle_bf16_from_double.restype = ctypes.c_uint16
+        for f in ("oracle_route_topk", "oracle_send_counts", "oracle_dispatch",
+                  "oracle_dispatch_dedup", "oracle_combine", "oracle_coselect"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise RuntimeError(f"{name} returned {rc}")
+
+
+def contiguous(n_experts, n_ranks):
+    return (np.arange(n_experts, dtype=np.int32) // (n_experts // n_ranks)).astype(np.int32)
+
+
+def route_topk(logits, top_k):
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, top_k), np.int32)
+    gate = np.empty((T, top_k), np.float32)
+    _check(lib().oracle_route_topk(_p(logits), T, E, top_k, _p(idx), _p(gate)), "route")
+    return idx, gate
+
+
+def send_counts(idx, n_experts, n_ranks, placement=None, dedup=False):
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    place = contiguous(n_experts, n_ranks) if placement is None else _c(placement, np.int32)
+    ec = np.empty(n_experts, np.int32)
+    rc = np.empty(n_ranks, np.int32)
+    ro = np.empty(n_ranks + 1, np.int32)
+    eo = np.empty(n_experts, np.int32)
+    _check(lib().oracle_send_counts(_p(idx), T, n_experts, k, n_ranks, _p(place),
+                                    int(bool(dedup)), _p(ec), _p(rc), _p(ro), _p(eo)),
+           "send_counts")
+    return {"expert_counts": ec, "rank_counts": rc, "rank_offsets": ro,
+            "expert_offsets": eo}
+
+
+def dispatch(x_bits, idx, gate, n_experts, n_ranks, placement=None, with_rows=True):
+    """Non-dedup pack.  x_bits: [T][H] of any 1/2/4-byte dtype (copied bitwise)."""
+    idx = _c(idx, np.int32)
+    gate = _c(gate, np.float32)
+    T, k = idx.shape
+    x = np.ascontiguousarray(x_bits)
+    row_bytes = x.shape[1] * x.itemsize
+    cnt = send_counts(idx, n_experts, n_ranks, placement, dedup=False)
+    N = T * k
+    send = np.empty((N,) + x.shape[1:], x.dtype) if with_rows else None
+    row_token = np.empty(N, np.int32)
+    row_expert = np.empty(N, np.int32)
+    row_weight = np.empty(N, np.float32)
+    slot_row = np.empty((T, k), np.int32)
+    _check(lib().oracle_dispatch(_p(x), _p(idx), _p(gate), T, row_bytes, n_experts, k,
+                                 _p(cnt["expert_offsets"]), _p(send), _p(row_token),
+                                 _p(row_expert), _p(row_weight), _p(slot_row)), "dispatch")
+    return dict(cnt, send=send, row_token=row_token, row_expert=row_expert,
+                row_weight=row_weight, slot_row=slot_row, n_rows=N)
+
+
+def dispatch_dedup(x_bits, idx, gate, n_experts, n_ranks, placement=None, with_rows=True):
+    idx = _c(idx, np.int32)
+    gate = _c(gate, np.float32)
+    T, k = idx.shape
+    x = np.ascontiguousarray(x_bits)
+    row_bytes = x.shape[1] * x.itemsize
+    place = contiguous(n_experts, n_ranks) if placement is None else _c(placement, np.int32)
+    cnt = send_counts(idx, n_experts, n_ranks, place, dedup=True)
+    D = int(cnt["rank_offsets"][-1])
+    send = np.empty((D,) + x.shape[1:], x.dtype) if with_rows else None
+    row_token = np.empty(D, np.int32)
+    row_experts = np.empty((D, k), np.int32)
+    row_gates = np.empty((D, k), np.float32)
+    row_weight = np.empty(D, np.float32)
+    slot_row = np.empty((T, k), np.int32)
+    n_rows = np.zeros(1, np.int32)
+    _check(lib().oracle_dispatch_dedup(_p(x), _p(idx), _p(gate), T, row_bytes, n_experts,
+                                       k, n_ranks, _p(place), _p(cnt["rank_offsets"]),
+                                       _p(send), _p(row_token), _p(row_experts),
+                                       _p(row_gates), _p(row_weight), _p(slot_row),
+                                       _p(n_rows)), "dispatch_dedup")
+    return dict(cnt, send=send, row_token=row_token, row_experts=row_experts,
+                row_gates=row_gates, row_weight=row_weight, slot_row=slot_row,
+                n_rows=int(n_rows[0]))
+
+
+def combine(rows_bits, row_weight, slot_row):
+    rows = _c(rows_bits, np.uint16)
+    slot_row = _c(slot_row, np.int32)
+    T, k = slot_row.shape
+    H = rows.shape[1]
+    w = None if row_weight is None else _c(row_weight, np.float32)
+    out = np.empty((T, H), np.uint16)
+    _check(lib().oracle_combine(_p(rows), _p(w), _p(slot_row), T, H, k, _p(out)), "combine")
+    return out
+
+
+def coselect(idx, n_experts, tokens=None, W=None):
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    n = T if tokens is None else min(int(tokens), T)
+    if W is None:
+        W = np.zeros((n_experts, n_experts), np.int32)
+    else:
+        assert W.dtype == np.int32 and W.flags.c_contiguous
+    _check(lib().oracle_coselect(_p(idx), n, n_experts, k, _p(W)), "coselect")
+    return W
+
+
+def bf16_from_double(d: float) -> int:
+    return int(lib().oracle_bf16_from_double(float(d)))

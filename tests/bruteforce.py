@@ -1,0 +1,128 @@
+"""Brute-force enumerators for tiny inputs (pure Python, test-only).
+
+Written independently of oracle.c, from the same definitions but by other
+means: top-k membership by counting the experts strictly ahead, buffer
+positions by a full sort of (rank, expert, token) keys, dedup rows from a set,
+combine by exact rational arithmetic.
+"""
+from __future__ import annotations
+
+import math
+import struct
+from collections import Counter
+from fractions import Fraction
+
+
+def topk(logits_row, k):
+    """Expert e takes slot s iff exactly s experts are strictly ahead of it,
+    where e' is ahead of e if l[e'] > l[e], or l[e'] == l[e] and e' < e."""
+    E = len(logits_row)
+    slots = [None] * k
+    for e in range(E):
+        ahead = sum(1 for f in range(E)
+                    if logits_row[f] > logits_row[e]
+                    or (logits_row[f] == logits_row[e] and f < e))
+        if ahead < k:
+            slots[ahead] = e
+    return slots
+
+
+def nondedup_layout(idx, place):
+    """Row position of every (t, j): sort all (place[e], e, t) keys."""
+    keys = []
+    for t, row in enumerate(idx):
+        for j, e in enumerate(row):
+            keys.append((place[e], e, t, j))
+    keys.sort()
+    pos = {}
+    for p, (_, e, t, j) in enumerate(keys):
+        pos[(t, j)] = p
+    return keys, pos
+
+
+def dedup_layout(idx, place):
+    """Rows = sorted set of (rank, token)."""
+    pairs = sorted({(place[e], t) for t, row in enumerate(idx) for e in row})
+    return pairs
+
+
+def bf16_to_fraction(bits):
+    f = struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+    return Fraction(f)
+
+
+def _bf16_value(bits):
+    return struct.unpack("<f", struct.pack("<I", (bits & 0xFFFF) << 16))[0]
+
+
+def nearest_bf16(q: Fraction, negative_zero=False):
+    """Nearest bf16 to an exact rational, ties to the even bit pattern, found by
+    comparing q with the finite bf16 values around it (no overflow handling:
+    |q| must be below the largest finite bf16)."""
+    if q == 0:
+        return 0x8000 if negative_zero else 0x0000
+    sign = 0x8000 if q < 0 else 0
+    a = abs(q)
+    # Bisect over non-negative finite bf16 patterns 0x0000..0x7F7F (monotone).
+    lo, hi = 0, 0x7F7F
+    while lo < hi:                      # smallest pattern with value >= a
+        mid = (lo + hi) // 2
+        if Fraction(_bf16_value(mid)) >= a:
+            hi = mid
+        else:
+            lo = mid + 1
+    up = lo
+    if Fraction(_bf16_value(up)) == a:
+        return sign | up
+    down = up - 1
+    du = Fraction(_bf16_value(up)) - a
+    dd = a - Fraction(_bf16_value(down))
+    if du < dd:
+        b = up
+    elif dd < du:
+        b = down
+    else:
+        b = up if (up & 1) == 0 else down
+    return sign | b
+
+
+def combine(rows_bits, weights, slot_row):
+    """Exact rational weighted sum of the distinct rows of each token."""
+    T, k = len(slot_row), len(slot_row[0])
+    H = len(rows_bits[0])
+    out = []
+    for t in range(T):
+        rs = sorted({r for r in slot_row[t] if r >= 0})
+        o = []
+        for h in range(H):
+            acc = Fraction(0)
+            all_neg_zero = True
+            for r in rs:
+                w = Fraction(1) if weights is None else Fraction(float(weights[r]))
+                v = bf16_to_fraction(rows_bits[r][h])
+                acc += w * v
+                b = int(rows_bits[r][h])
+                if not (b == 0x8000 and (weights is None or float(weights[r]) > 0)):
+                    all_neg_zero = False
+            # the sum starts at -0.0: it stays -0 only if every term is -0 (or none)
+            o.append(nearest_bf16(acc, negative_zero=(acc == 0 and all_neg_zero)))
+        out.append(o)
+    return out
+
+
+def coselect(idx, n_experts, n_tokens):
+    c = Counter()
+    for t in range(min(n_tokens, len(idx))):
+        s = list(idx[t])
+        for a in s:
+            for b in s:
+                c[(a, b)] += 1
+    return [[c[(a, b)] for b in range(n_experts)] for a in range(n_experts)]
+
+
+def softmax_desc(values):
+    """Full softmax of a list, in descending order of the values (textbook form)."""
+    m = max(values)
+    ex = [math.exp(v - m) for v in values]
+    s = math.fsum(ex)
+    return sorted((e / s for e in ex), reverse=True)
