@@ -1,0 +1,281 @@
+"""Benchmark of the per-GPU MoE dispatch/combine hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
+                    [--graph] [--no-cpu-baseline] [--calib-copy]
+
+A step is one pass of the whole path over one batch of the workload's seeded
+synthetic input, with inputs resident in HBM: top-k routing -> send counts and
+offsets -> dispatch permute -> combine (identity experts: the combine reads the
+send buffer) -> co-selection counts.  The workload defaults to 4096 tokens,
+hidden 2048 bf16, 64 experts, top-6, 16 logical ranks, contiguous placement
+(DeepSeek-MoE-16B-shaped), plain (one row per token-expert) dispatch.
+
+To keep the last-level (Infinity) cache from serving the data, steps rotate
+over enough independent buffer sets to exceed it several times over, so each
+step's inputs and outputs were last touched many hundreds of MB earlier.
+
+Prints one JSON line.  `roofline` reports the dominant kernel's algorithmic HBM
+bytes per launch divided by its mean duration (HIP events on the stream the
+kernels run on); `cpu_baseline` times the CPU oracle on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="deepseek_moe_16b")
+    p.add_argument("--dedup", action="store_true")
+    p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--footprint-gib", type=float, default=2.0,
+                   help="total size of the rotated buffer sets")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def calib_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
+                      "ms": ms, "GBps_rw": 2 * n / ms / 1e6}), flush=True)
+
+
+class BufferSet:
+    """Device buffers for one step (inputs resident, outputs preallocated)."""
+
+    def __init__(self, torch, ops, inp, w, dedup, dev):
+        T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
+        N = T * k
+        self.logits = torch.from_numpy(inp["logits"]).to(dev)
+        self.x = torch.from_numpy(inp["x_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        self.place = (torch.from_numpy(inp["placement"]).to(dev)
+                      if inp["placement"] is not None else None)
+        i32, f32 = torch.int32, torch.float32
+        self.idx = torch.empty((T, k), dtype=i32, device=dev)
+        self.gate = torch.empty((T, k), dtype=f32, device=dev)
+        self.ws = ops.workspace(T, E, k, R, dedup, dev)
+        self.cnt = {"expert_counts": torch.empty(E, dtype=i32, device=dev),
+                    "rank_counts": torch.empty(R, dtype=i32, device=dev),
+                    "rank_offsets": torch.empty(R + 1, dtype=i32, device=dev)}
+        if not dedup:
+            self.cnt["expert_offsets"] = torch.empty(E, dtype=i32, device=dev)
+        self.disp = {"send": torch.empty((N, H), dtype=torch.bfloat16, device=dev),
+                     "row_token": torch.empty(N, dtype=i32, device=dev),
+                     "row_weight": torch.empty(N, dtype=f32, device=dev),
+                     "slot_row": torch.empty((T, k), dtype=i32, device=dev)}
+        if dedup:
+            self.disp.update(row_experts=torch.empty((N, k), dtype=i32, device=dev),
+                             row_gates=torch.empty((N, k), dtype=f32, device=dev),
+                             n_rows=torch.empty(1, dtype=i32, device=dev))
+        else:
+            self.disp["row_expert"] = torch.empty(N, dtype=i32, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.W = torch.zeros((E, E), dtype=i32, device=dev)
+
+    def nbytes(self):
+        tot = 0
+        for v in vars(self).values():
+            if hasattr(v, "element_size"):
+                tot += v.numel() * v.element_size()
+            elif isinstance(v, dict):
+                tot += sum(t.numel() * t.element_size() for t in v.values())
+        return tot
+
+
+def gpu_step(ops, b, w, dedup, ev=None):
+    """One pass of the hot path.  ev = (e0, e1, e2, e3) events bracketing the
+    dispatch and the combine kernels, recorded on the current stream."""
+    E, k, R = w.n_experts, w.top_k, w.n_ranks
+    ops.moe_route_topk(b.logits, k, b.idx, b.gate)
+    c = ops.moe_send_counts(b.idx, E, R, b.place, dedup, ws=b.ws, out=b.cnt)
+    f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+    if ev:
+        ev[0].record()
+    d = f(b.x, b.idx, b.gate, E, R, c["ws"], b.place, out=b.disp)
+    if ev:
+        ev[1].record()
+        ev[2].record()
+    ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b.out)
+    if ev:
+        ev[3].record()
+    ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W)
+
+
+def cpu_baseline(inp, w, dedup, seconds):
+    """The CPU oracle as it stands (single host thread), on whole steps of the
+    same workload, repeated until `seconds` have elapsed."""
+    from oracle import oracle as O
+    O.lib()
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        idx, gate = O.route_topk(inp["logits"], w.top_k)
+        f = O.dispatch_dedup if dedup else O.dispatch
+        d = f(inp["x_bits"], idx, gate, w.n_experts, w.n_ranks, inp["placement"])
+        O.combine(d["send"], d["row_weight"], d["slot_row"])
+        O.coselect(idx, w.n_experts, tokens=w.coselect_tokens)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": steps * w.tokens / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole steps of the same workload ({w.tokens} tokens each), "
+                      f"{el:.1f} s on one host thread"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): destination ranks are "
+              "logical partitions of one GPU's buffers; there is no multi-GPU path to time.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if a.calib_copy:
+        calib_copy()
+        return
+    from combine_top_router_select_amd import ops
+    from combine_top_router_select_amd import workloads as WL
+    ops.lib()
+    w = WL.get(a.workload)
+    dedup = bool(a.dedup)
+    if dedup and "dedup" not in w.dispatch:
+        print(f"warning: {w.name} is not normally run with dedup dispatch", file=sys.stderr)
+    dev = torch.device("cuda:0")
+    inp = WL.make_inputs(w)
+    T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
+
+    first = BufferSet(torch, ops, inp, w, dedup, dev)
+    per_set = first.nbytes()
+    nsets = max(2, int(np.ceil(a.footprint_gib * 2 ** 30 / per_set)))
+    sets = [first] + [BufferSet(torch, ops, inp, w, dedup, dev) for _ in range(nsets - 1)]
+    torch.cuda.synchronize()
+
+    graphs = None
+    if a.graph:
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for b in sets:       # warm the code paths once outside capture
+                gpu_step(ops, b, w, dedup)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for b in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                gpu_step(ops, b, w, dedup)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        if graphs is not None:
+            graphs[i % nsets].replay()
+        else:
+            gpu_step(ops, sets[i % nsets], w, dedup, ev)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: exactly K steps, synchronised on both sides
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(a.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+
+    # per-kernel durations with HIP events on the stream the kernels run on
+    # (eager launches of the same step, same rotation)
+    K2 = min(a.steps, 100)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K2)]
+    for i in range(K2):
+        gpu_step(ops, sets[(a.warmup + a.steps + i) % nsets], w, dedup, evs[i])
+    torch.cuda.synchronize()
+    t_disp = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    t_comb = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e-3
+
+    # rows actually written (N, or D for dedup)
+    b = sets[0]
+    n_rows = int(b.cnt["rank_offsets"][R].item())
+    row_bytes = H * 2
+    disp_bytes = row_bytes * (T + n_rows)   # read x once, write each row once
+    comb_bytes = row_bytes * (n_rows + T)   # read each row once, write out once
+    meta_bytes = n_rows * (12 if not dedup else 8 + 8 * k) + T * k * 4
+    dom = ("moe_dispatch_permute" + ("_dedup" if dedup else ""), t_disp, disp_bytes)
+    if t_comb > t_disp:
+        dom = ("moe_combine", t_comb, comb_bytes)
+    achieved = dom[2] / dom[1] / 1e9
+    dc_gbps = (disp_bytes + comb_bytes) / (t_disp + t_comb) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": T * a.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": elapsed / a.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "hidden_dim": H, "n_experts": E,
+                   "top_k": k, "n_ranks": R, "placement": w.placement,
+                   "dispatch": "dedup" if dedup else "nondedup",
+                   "bytes_per_element": 2, "graph": bool(a.graph),
+                   "buffer_sets": nsets, "footprint_MiB": round(nsets * per_set / 2 ** 20)},
+        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "dispatch_us": round(t_disp * 1e6, 2),
+        "combine_us": round(t_comb * 1e6, 2),
+        "dispatch_combine_tokens_per_s": T / (t_disp + t_comb),
+        "dispatch_combine_GBps": round(dc_gbps, 1),
+        "dispatch_combine_hbm_frac": round(dc_gbps / HBM_PEAK_GBPS, 4),
+        "rows": n_rows,
+        "algorithmic_bytes": {"dispatch": disp_bytes, "combine": comb_bytes,
+                              "metadata": meta_bytes},
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, w, dedup, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

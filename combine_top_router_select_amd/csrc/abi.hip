@@ -1,0 +1,173 @@
+// C ABI of libmoe_route.so: host-side argument checks, then launches on the
+// caller's stream.  Everything that can be checked without reading device
+// memory is checked here, before anything is enqueued.
+#include <limits.h>
+
+#include "common.hpp"
+#include "moe_route.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace moe {
+hipError_t launch_route_topk(const float*, int64_t, int, int, int32_t*, float*, hipStream_t);
+hipError_t launch_send_counts(const int32_t*, int64_t, int, int, int, const int32_t*, int,
+                              int32_t*, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
+hipError_t launch_dispatch(const void*, const int32_t*, const float*, int64_t, int, int, int,
+                           int, const int32_t*, const void*, int, void*, int32_t*, int32_t*,
+                           float*, float*, int32_t*, int32_t*, hipStream_t);
+hipError_t launch_combine(const void*, const float*, const int32_t*, int64_t, int, int, void*,
+                          hipStream_t);
+hipError_t launch_coselect(const int32_t*, int64_t, int, int, int32_t*, hipStream_t);
+}  // namespace moe
+
+namespace {
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// tokens, experts and top_k: shared by every entry point.
+int check_tek(int64_t tokens, int n_experts, int top_k) {
+  if (tokens < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts) return MOE_EINVAL;
+  if (n_experts > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOP_K) return MOE_EUNSUPPORTED;
+  if (tokens > int64_t(INT_MAX) / top_k) return MOE_EUNSUPPORTED;  // rows indexed by int32
+  return MOE_OK;
+}
+
+int check_ranks(int n_experts, int n_ranks) {
+  if (n_ranks < 1 || n_experts % n_ranks != 0) return MOE_EINVAL;
+  if (n_ranks > MOE_MAX_RANKS) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_rows(int hidden_dim, int bytes_per_element) {
+  if (hidden_dim < 1 || bytes_per_element < 1) return MOE_EINVAL;
+  if (bytes_per_element != 1 && bytes_per_element != 2 && bytes_per_element != 4)
+    return MOE_EUNSUPPORTED;
+  const int64_t rb = int64_t(hidden_dim) * bytes_per_element;
+  if (rb % 16 != 0 || rb > INT_MAX / 2) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: outside the library's supported limits";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace smaller than moe_workspace_bytes()";
+    case MOE_EHIP: return "MOE_EHIP: a HIP launch failed";
+    default: return "unknown moe_route status";
+  }
+}
+
+MOE_API size_t moe_workspace_bytes(int64_t tokens, int n_experts, int top_k, int n_ranks,
+                                   int dedup) {
+  if (check_tek(tokens, n_experts, top_k) != MOE_OK) return 0;
+  if (check_ranks(n_experts, n_ranks) != MOE_OK) return 0;
+  return moe::plan_layout(tokens, n_experts, top_k, n_ranks, dedup ? 1 : 0).bytes;
+}
+
+MOE_API int moe_route_topk(const float* logits, int64_t tokens, int n_experts, int top_k,
+                           int32_t* topk_idx, float* topk_gate, void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if (tokens == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_gate) return MOE_EINVAL;
+  return hip_status(moe::launch_route_topk(logits, tokens, n_experts, top_k, topk_idx,
+                                           topk_gate, as_stream(stream)));
+}
+
+MOE_API int moe_send_counts(const int32_t* topk_idx, int64_t tokens, int n_experts, int top_k,
+                            int n_ranks, const int32_t* placement, int dedup,
+                            int32_t* expert_counts, int32_t* rank_counts,
+                            int32_t* rank_offsets, int32_t* expert_offsets, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if ((tokens > 0 && !topk_idx) || !expert_counts || !rank_counts || !rank_offsets || !workspace)
+    return MOE_EINVAL;
+  if (workspace_bytes < moe_workspace_bytes(tokens, n_experts, top_k, n_ranks, dedup))
+    return MOE_EWORKSPACE;
+  return hip_status(moe::launch_send_counts(topk_idx, tokens, n_experts, top_k, n_ranks,
+                                            placement, dedup ? 1 : 0, expert_counts,
+                                            rank_counts, rank_offsets,
+                                            dedup ? nullptr : expert_offsets, workspace,
+                                            as_stream(stream)));
+}
+
+MOE_API int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* topk_gate,
+                                 int64_t tokens, int hidden_dim, int n_experts, int top_k,
+                                 int n_ranks, const int32_t* placement, int bytes_per_element,
+                                 const void* workspace, size_t workspace_bytes, void* send,
+                                 int32_t* row_token, int32_t* row_expert, float* row_weight,
+                                 int32_t* slot_row, void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if ((st = check_rows(hidden_dim, bytes_per_element)) != MOE_OK) return st;
+  if (!workspace) return MOE_EINVAL;
+  if (workspace_bytes < moe_workspace_bytes(tokens, n_experts, top_k, n_ranks, 0))
+    return MOE_EWORKSPACE;
+  if (tokens == 0) return MOE_OK;
+  if (!x || !topk_idx || !topk_gate || !send || !row_token || !row_expert || !row_weight ||
+      !slot_row)
+    return MOE_EINVAL;
+  (void)placement;  // the plan in the workspace already encodes it
+  return hip_status(moe::launch_dispatch(x, topk_idx, topk_gate, tokens,
+                                         hidden_dim * bytes_per_element, n_experts, top_k,
+                                         n_ranks, placement, workspace, 0, send, row_token,
+                                         row_expert, nullptr, row_weight, slot_row, nullptr,
+                                         as_stream(stream)));
+}
+
+MOE_API int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx,
+                                       const float* topk_gate, int64_t tokens, int hidden_dim,
+                                       int n_experts, int top_k, int n_ranks,
+                                       const int32_t* placement, int bytes_per_element,
+                                       const void* workspace, size_t workspace_bytes,
+                                       void* send, int32_t* row_token, int32_t* row_experts,
+                                       float* row_gates, float* row_weight, int32_t* slot_row,
+                                       int32_t* n_rows, void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if ((st = check_rows(hidden_dim, bytes_per_element)) != MOE_OK) return st;
+  if (!workspace || !n_rows) return MOE_EINVAL;
+  if (workspace_bytes < moe_workspace_bytes(tokens, n_experts, top_k, n_ranks, 1))
+    return MOE_EWORKSPACE;
+  if (tokens > 0 && (!x || !topk_idx || !topk_gate || !send || !row_token || !row_experts ||
+                     !row_gates || !row_weight || !slot_row))
+    return MOE_EINVAL;
+  return hip_status(moe::launch_dispatch(x, topk_idx, topk_gate, tokens,
+                                         hidden_dim * bytes_per_element, n_experts, top_k,
+                                         n_ranks, placement, workspace, 1, send, row_token,
+                                         row_experts, row_gates, row_weight, slot_row, n_rows,
+                                         as_stream(stream)));
+}
+
+MOE_API int moe_combine(const void* rows, const float* row_weight, const int32_t* slot_row,
+                        int64_t tokens, int hidden_dim, int top_k, int bytes_per_element,
+                        void* out, void* stream) {
+  if (tokens < 0 || top_k < 1 || hidden_dim < 1 || bytes_per_element < 1) return MOE_EINVAL;
+  if (top_k > MOE_MAX_TOP_K || bytes_per_element != 2) return MOE_EUNSUPPORTED;
+  if (tokens > int64_t(INT_MAX) / top_k) return MOE_EUNSUPPORTED;
+  const int64_t rb = int64_t(hidden_dim) * 2;
+  if (rb % 16 != 0 || rb > INT_MAX / 2) return MOE_EUNSUPPORTED;
+  if (tokens == 0) return MOE_OK;
+  if (!rows || !slot_row || !out) return MOE_EINVAL;
+  return hip_status(moe::launch_combine(rows, row_weight, slot_row, tokens, int(rb), top_k, out,
+                                        as_stream(stream)));
+}
+
+MOE_API int moe_coselect_counts(const int32_t* topk_idx, int64_t tokens, int n_experts,
+                                int top_k, int32_t* coselect, void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if (tokens == 0) return MOE_OK;
+  if (!topk_idx || !coselect) return MOE_EINVAL;
+  return hip_status(moe::launch_coselect(topk_idx, tokens, n_experts, top_k, coselect,
+                                         as_stream(stream)));
+}

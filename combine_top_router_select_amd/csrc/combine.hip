@@ -1,0 +1,143 @@
+// A5 - combine: weighted sum of the rows that served each token, back in
+// token order.
+//
+// Sources: "Expert Coupling in MoE Pretraining" (summary), "The Communication
+// Bottleneck": under expert parallelism each MoE layer dispatches rows to the
+// experts and combines their outputs back.  "DODOCO" dataset card,
+// "send_matrices.csv columns": combine moves the dispatch volumes in reverse.
+//
+// Design: one wave per (token, row chunk).  Lanes j < k read slot_row[t][j]
+// and the row weight; a slot whose row already appeared in an earlier slot is
+// dropped (dedup rows serve several slots), negative rows are skipped.  The
+// wave then issues the loads of every used row's chunk before any arithmetic
+// (KMAX rows x NV 16-byte vectors in flight per lane), accumulates in fp32
+// with fused multiply-adds in slot order starting from -0.0, and converts to
+// bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+#include "common.hpp"
+
+namespace moe {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  const bf16x2 b = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+template <int NV, int KMAX>
+__global__ void __launch_bounds__(256)
+combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
+               const int32_t* __restrict__ slot_row, int64_t T, int row_bytes, int k, int cpr,
+               uint8_t* __restrict__ out) {
+  const int lane = lane_id();
+  const int64_t wid = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t t = wid / cpr;
+  const int c = int(wid - t * cpr);
+  if (t >= T) return;  // whole wave
+  const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
+  int r = -1;
+  if (lane < k) r = slot_row[t * k + lane];
+  bool use = lane < k && r >= 0;
+  for (int i = 0; i < k; ++i) {
+    const int ri = bcast(r, i);
+    if (i < lane && ri == r) use = false;
+  }
+  float wr = 1.0f;
+  if (use && w) wr = w[r];
+  uint64_t um = __ballot(use);
+  const int nrows = __popcll(um);
+
+  u32x4 y[KMAX][NV];
+  float wq[KMAX];
+#pragma unroll
+  for (int q = 0; q < KMAX; ++q) {
+    wq[q] = 0.0f;
+    if (q < nrows) {
+      const int j = __ffsll((unsigned long long)um) - 1;
+      um &= um - 1;
+      const int p = bcast(r, j);
+      wq[q] = bcastf(wr, j);
+      const uint8_t* src = rows + int64_t(p) * row_bytes + chunk0;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int64_t off = int64_t(i * kWave + lane) * 16;
+        if (chunk0 + off < row_bytes) y[q][i] = load16(src + off);
+      }
+    }
+  }
+  float acc[NV][8];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int h = 0; h < 8; ++h) acc[i][h] = -0.0f;
+#pragma unroll
+  for (int q = 0; q < KMAX; ++q) {
+    if (q < nrows) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t u = y[q][i][h];
+          acc[i][2 * h] = __builtin_fmaf(wq[q], __uint_as_float(u << 16), acc[i][2 * h]);
+          acc[i][2 * h + 1] =
+              __builtin_fmaf(wq[q], __uint_as_float(u & 0xFFFF0000u), acc[i][2 * h + 1]);
+        }
+      }
+    }
+  }
+  uint8_t* dst = out + t * row_bytes + chunk0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t off = int64_t(i * kWave + lane) * 16;
+    if (chunk0 + off < row_bytes) {
+      u32x4 o;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(acc[i][2 * h], acc[i][2 * h + 1]);
+      store16(dst + off, o);
+    }
+  }
+}
+
+template <int NV, int KMAX>
+static hipError_t launch_combine_t(const void* rows, const float* w, const int32_t* slot_row,
+                                   int64_t T, int row_bytes, int k, void* out,
+                                   hipStream_t stream) {
+  const int chunk = NV * kWave * 16;
+  const int cpr = (row_bytes + chunk - 1) / chunk;
+  const int64_t blocks = (T * cpr + 3) / 4;
+  hipLaunchKernelGGL((combine_kernel<NV, KMAX>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(rows), w, slot_row, T, row_bytes, k, cpr,
+                     static_cast<uint8_t*>(out));
+  return hipGetLastError();
+}
+
+template <int KMAX>
+static hipError_t launch_combine_k(const void* rows, const float* w, const int32_t* slot_row,
+                                   int64_t T, int row_bytes, int k, void* out,
+                                   hipStream_t stream) {
+  // keep KMAX * NV <= 32 vectors (128 VGPRs) in flight per lane
+  const int vr = row_bytes / 16;
+  constexpr int NVMAX = (32 / KMAX) < 4 ? (32 / KMAX) : 4;
+  if (NVMAX >= 4 && vr >= 4 * kWave)
+    return launch_combine_t<(NVMAX >= 4 ? 4 : 1), KMAX>(rows, w, slot_row, T, row_bytes, k, out,
+                                                         stream);
+  if (NVMAX >= 2 && vr >= 2 * kWave)
+    return launch_combine_t<(NVMAX >= 2 ? 2 : 1), KMAX>(rows, w, slot_row, T, row_bytes, k, out,
+                                                         stream);
+  return launch_combine_t<1, KMAX>(rows, w, slot_row, T, row_bytes, k, out, stream);
+}
+
+hipError_t launch_combine(const void* rows, const float* w, const int32_t* slot_row, int64_t T,
+                          int row_bytes, int k, void* out, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  if (k <= 1) return launch_combine_k<1>(rows, w, slot_row, T, row_bytes, k, out, stream);
+  if (k <= 2) return launch_combine_k<2>(rows, w, slot_row, T, row_bytes, k, out, stream);
+  if (k <= 4) return launch_combine_k<4>(rows, w, slot_row, T, row_bytes, k, out, stream);
+  if (k <= 6) return launch_combine_k<6>(rows, w, slot_row, T, row_bytes, k, out, stream);
+  if (k <= 8) return launch_combine_k<8>(rows, w, slot_row, T, row_bytes, k, out, stream);
+  return launch_combine_k<16>(rows, w, slot_row, T, row_bytes, k, out, stream);
+}
+
+}  // namespace moe

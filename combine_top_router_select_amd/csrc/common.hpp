@@ -1,0 +1,75 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels: wave64 lane masks,
+// broadcasts, 16-byte vector loads/stores and the plan layout that
+// moe_send_counts leaves in the workspace for the dispatch kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kTile = 64;          // tokens per counting tile (one lane per token)
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = __lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Wave-uniform value of `v` held by lane `src` (src must be wave-uniform).
+__device__ __forceinline__ int bcast(int v, int src) {
+  return __builtin_amdgcn_readlane(v, src);
+}
+__device__ __forceinline__ float bcastf(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ void store16_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// Plan written by moe_send_counts, read by the dispatch kernels.
+//   header[0]  total rows (N, or D in dedup mode)
+//   base[B][C] absolute first row of column c inside tile b, C = E (+ R in
+//              dedup mode: columns E..E+R-1 are ranks)
+//   lrank[T][k] uint8: rank of (t, j) among the tile's earlier tokens that use
+//              the same column (expert, or rank in dedup mode)
+struct PlanLayout {
+  int64_t tiles;      // B = ceil(T / 64)
+  int cols;           // C
+  size_t base_off;    // byte offsets inside the workspace
+  size_t lrank_off;
+  size_t bytes;
+};
+
+__host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+__host__ __device__ inline PlanLayout plan_layout(int64_t tokens, int n_experts, int top_k,
+                                                  int n_ranks, int dedup) {
+  PlanLayout p;
+  p.tiles = (tokens + kTile - 1) / kTile;
+  p.cols = n_experts + (dedup ? n_ranks : 0);
+  p.base_off = 256;
+  p.lrank_off = align256(p.base_off + size_t(p.tiles) * size_t(p.cols) * 4);
+  p.bytes = align256(p.lrank_off + size_t(tokens) * size_t(top_k));
+  return p;
+}
+
+}  // namespace moe

@@ -1,0 +1,226 @@
+// A4a / A4b - dispatch permute into a rank-contiguous send buffer.
+//
+// Source: "Expert Coupling in MoE Pretraining" (summary), "Method 1: Correlated
+// Expert Placement + Deduplicating Dispatcher": the conventional dispatcher
+// sends one copy of a token's hidden state per (token, expert); the
+// deduplicating one sends one row per distinct (token, destination rank) with
+// the ids and routing probabilities of the rank's selected experts as
+// metadata.  "DODOCO" dataset card, "Reading the counts": a token routed to
+// several experts on one rank is counted (and sent) once per expert by the
+// conventional dispatcher.
+//
+// Design: one wave per (token, row chunk).  Lanes j < k first resolve slot j's
+// destination row from the plan (base[tile][column] + lrank), then the wave
+// reads its chunk of x[t] once into registers (16-byte loads, 1 KiB per wave
+// instruction) and writes it to each destination row.  Every access is a full,
+// contiguous row segment, so reads and writes are perfectly coalesced; nothing
+// is re-read, so there is no cross-workgroup reuse for an XCD-aware order to
+// exploit.  Chunk 0 of each token also writes the row metadata.
+#include "common.hpp"
+
+namespace moe {
+
+template <int NV>
+__device__ __forceinline__ void load_chunk(u32x4 (&v)[NV], const uint8_t* src, int64_t chunk0,
+                                           int row_bytes, int lane) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t off = int64_t(i * kWave + lane) * 16;
+    if (chunk0 + off < row_bytes) v[i] = load16(src + off);
+  }
+}
+
+template <int NV, bool NT>
+__device__ __forceinline__ void store_chunk(const u32x4 (&v)[NV], uint8_t* dst, int64_t chunk0,
+                                            int row_bytes, int lane) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t off = int64_t(i * kWave + lane) * 16;
+    if (chunk0 + off < row_bytes) {
+      if (NT)
+        store16_nt(dst + off, v[i]);
+      else
+        store16(dst + off, v[i]);
+    }
+  }
+}
+
+template <int NV, bool NT>
+__global__ void __launch_bounds__(256)
+dispatch_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
+                const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k, int cpr,
+                const int32_t* __restrict__ base, const uint8_t* __restrict__ lrank, int C,
+                uint8_t* __restrict__ send, int32_t* __restrict__ row_token,
+                int32_t* __restrict__ row_expert, float* __restrict__ row_weight,
+                int32_t* __restrict__ slot_row) {
+  const int lane = lane_id();
+  const int64_t wid = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t t = wid / cpr;
+  const int c = int(wid - t * cpr);
+  if (t >= T) return;  // whole wave
+  const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
+  int e = 0, lr = 0;
+  if (lane < k) {
+    e = clampi(idx[t * k + lane], 0, E - 1);
+    lr = lrank[t * k + lane];
+  }
+  u32x4 v[NV];
+  load_chunk<NV>(v, x + t * row_bytes + chunk0, chunk0, row_bytes, lane);
+  int pos = 0;
+  if (lane < k) pos = base[(t / kTile) * C + e] + lr;
+  if (c == 0 && lane < k) {
+    slot_row[t * k + lane] = pos;
+    row_token[pos] = int32_t(t);
+    row_expert[pos] = e;
+    row_weight[pos] = gate[t * k + lane];
+  }
+  for (int j = 0; j < k; ++j) {
+    const int p = bcast(pos, j);
+    store_chunk<NV, NT>(v, send + int64_t(p) * row_bytes + chunk0, chunk0, row_bytes, lane);
+  }
+}
+
+template <int NV, bool NT>
+__global__ void __launch_bounds__(256)
+dispatch_dedup_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
+                      const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k,
+                      int R, const int32_t* __restrict__ place, int m, int cpr,
+                      const int32_t* __restrict__ base, const uint8_t* __restrict__ lrank, int C,
+                      const int32_t* __restrict__ header, uint8_t* __restrict__ send,
+                      int32_t* __restrict__ row_token, int32_t* __restrict__ row_experts,
+                      float* __restrict__ row_gates, float* __restrict__ row_weight,
+                      int32_t* __restrict__ slot_row, int32_t* __restrict__ n_rows) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_rows = header[0];
+  const int lane = lane_id();
+  const int64_t wid = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t t = wid / cpr;
+  const int c = int(wid - t * cpr);
+  if (t >= T) return;  // whole wave
+  const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
+  int e = 0, r = -1, lr = 0;
+  float g = 0.0f;
+  if (lane < k) {
+    e = clampi(idx[t * k + lane], 0, E - 1);
+    r = place ? clampi(place[e], 0, R - 1) : e / m;
+    lr = lrank[t * k + lane];
+    g = gate[t * k + lane];
+  }
+  u32x4 v[NV];
+  load_chunk<NV>(v, x + t * row_bytes + chunk0, chunk0, row_bytes, lane);
+  int pos = 0;
+  if (lane < k) pos = base[(t / kTile) * C + E + r] + lr;
+  // Per slot: is it the first slot of its rank (the row's leader)?  Its column
+  // among the rank's experts (ascending id), the rank's slot count, and its
+  // position in the token's ascending expert order.
+  bool leader = lane < k;
+  int col = 0, cnt = 0, sidx = 0;
+  for (int i = 0; i < k; ++i) {
+    const int ri = bcast(r, i), ei = bcast(e, i);
+    if (ri == r) {
+      ++cnt;
+      if (ei < e) ++col;
+      if (i < lane) leader = false;
+    }
+    if (ei < e) ++sidx;
+  }
+  if (c == 0) {
+    if (lane < k) {
+      slot_row[t * k + lane] = pos;
+      row_experts[int64_t(pos) * k + col] = e;
+      row_gates[int64_t(pos) * k + col] = g;
+      if (leader) {
+        row_token[pos] = int32_t(t);
+        for (int cc = cnt; cc < k; ++cc) {
+          row_experts[int64_t(pos) * k + cc] = -1;
+          row_gates[int64_t(pos) * k + cc] = 0.0f;
+        }
+      }
+    }
+    // row weight: fp64 sum of the rank's gates in ascending expert order
+    double wsum = 0.0;
+    for (int s = 0; s < k; ++s) {
+      const uint64_t sm = __ballot(lane < k && sidx == s);
+      if (sm == 0ull) continue;  // only if topk_idx repeats an expert (precondition)
+      const int src = __ffsll((unsigned long long)sm) - 1;
+      const float gs = bcastf(g, src);
+      const int rs = bcast(r, src);
+      if (leader && rs == r) wsum += double(gs);
+    }
+    if (leader) row_weight[pos] = float(wsum);
+  }
+  const uint64_t lm = __ballot(leader);
+  for (int j = 0; j < k; ++j) {
+    if (!((lm >> j) & 1ull)) continue;
+    const int p = bcast(pos, j);
+    store_chunk<NV, NT>(v, send + int64_t(p) * row_bytes + chunk0, chunk0, row_bytes, lane);
+  }
+}
+
+#ifndef MOE_DISPATCH_NT
+#define MOE_DISPATCH_NT 0
+#endif
+
+// Vectors of 16 B per lane per wave: a 4 KiB chunk per wave for long rows.
+static int dispatch_nv(int row_bytes) {
+  const int vr = row_bytes / 16;
+  if (vr >= 4 * kWave) return 4;
+  if (vr >= 2 * kWave) return 2;
+  return 1;
+}
+
+template <int NV>
+static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const float* gate,
+                                     int64_t T, int row_bytes, int E, int k, int R,
+                                     const int32_t* place, const void* workspace, int dedup,
+                                     void* send, int32_t* row_token, int32_t* row_e,
+                                     float* row_gates, float* row_weight, int32_t* slot_row,
+                                     int32_t* n_rows, hipStream_t stream) {
+  const PlanLayout pl = plan_layout(T, E, k, R, dedup);
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  const int32_t* header = reinterpret_cast<const int32_t*>(ws);
+  const int32_t* base = reinterpret_cast<const int32_t*>(ws + pl.base_off);
+  const uint8_t* lrank = ws + pl.lrank_off;
+  const int chunk = NV * kWave * 16;
+  const int cpr = (row_bytes + chunk - 1) / chunk;
+  const int64_t waves = T * cpr;
+  int64_t blocks = (waves + 3) / 4;
+  if (blocks == 0) blocks = 1;  // dedup still reports n_rows
+  constexpr bool NT = MOE_DISPATCH_NT != 0;
+  if (!dedup) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL((dispatch_kernel<NV, NT>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, cpr, base,
+                       lrank, pl.cols, static_cast<uint8_t*>(send), row_token, row_e,
+                       row_weight, slot_row);
+  } else {
+    hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT>), dim3(unsigned(blocks)), dim3(256), 0,
+                       stream, static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, R,
+                       place, E / R, cpr, base, lrank, pl.cols, header,
+                       static_cast<uint8_t*>(send), row_token, row_e, row_gates, row_weight,
+                       slot_row, n_rows);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const void* x, const int32_t* idx, const float* gate, int64_t T,
+                           int row_bytes, int E, int k, int R, const int32_t* place,
+                           const void* workspace, int dedup, void* send, int32_t* row_token,
+                           int32_t* row_e, float* row_gates, float* row_weight,
+                           int32_t* slot_row, int32_t* n_rows, hipStream_t stream) {
+  switch (dispatch_nv(row_bytes)) {
+    case 4:
+      return launch_dispatch_nv<4>(x, idx, gate, T, row_bytes, E, k, R, place, workspace, dedup,
+                                   send, row_token, row_e, row_gates, row_weight, slot_row,
+                                   n_rows, stream);
+    case 2:
+      return launch_dispatch_nv<2>(x, idx, gate, T, row_bytes, E, k, R, place, workspace, dedup,
+                                   send, row_token, row_e, row_gates, row_weight, slot_row,
+                                   n_rows, stream);
+    default:
+      return launch_dispatch_nv<1>(x, idx, gate, T, row_bytes, E, k, R, place, workspace, dedup,
+                                   send, row_token, row_e, row_gates, row_weight, slot_row,
+                                   n_rows, stream);
+  }
+}
+
+}  // namespace moe

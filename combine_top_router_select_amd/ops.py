@@ -1,0 +1,202 @@
+"""Python binding of the C ABI (include/moe_route.h), entry point for entry point.
+
+Each function checks dtype/device/contiguity, allocates any output that was not
+passed in (torch is used for device memory and streams only), passes raw
+pointers and the current HIP stream to the library, and raises MoeError on a
+non-zero status.  No step of the computation runs here.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from ._lib import MoeError, check, lib, status_string  # noqa: F401
+
+__all__ = ["MoeError", "moe_status_string", "moe_workspace_bytes", "moe_route_topk",
+           "moe_send_counts", "moe_dispatch_permute", "moe_dispatch_permute_dedup",
+           "moe_combine", "moe_coselect_counts", "workspace"]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr() or None
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def moe_status_string(code: int) -> str:
+    return status_string(code)
+
+
+def moe_workspace_bytes(tokens: int, n_experts: int, top_k: int, n_ranks: int,
+                        dedup: bool) -> int:
+    return int(lib().moe_workspace_bytes(tokens, n_experts, top_k, n_ranks, int(bool(dedup))))
+
+
+def workspace(tokens, n_experts, top_k, n_ranks, dedup, device) -> torch.Tensor:
+    n = moe_workspace_bytes(tokens, n_experts, top_k, n_ranks, dedup)
+    if n == 0:
+        raise MoeError(1, "moe_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_route_topk(logits, top_k, topk_idx=None, topk_gate=None, stream=None):
+    _dev(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if topk_gate is None:
+        topk_gate = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    _dev(topk_idx, "topk_idx", torch.int32)
+    _dev(topk_gate, "topk_gate", torch.float32)
+    check(lib().moe_route_topk(_ptr(logits), T, E, top_k, _ptr(topk_idx), _ptr(topk_gate),
+                               _stream(stream)), "moe_route_topk")
+    return topk_idx, topk_gate
+
+
+def moe_send_counts(topk_idx, n_experts, n_ranks, placement=None, dedup=False, ws=None,
+                    out=None, stream=None):
+    """Returns a dict with expert_counts, rank_counts, rank_offsets, expert_offsets
+    (None in dedup mode) and the workspace `ws` that the dispatch call needs."""
+    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    if placement is not None:
+        _dev(placement, "placement", torch.int32, 1)
+    if ws is None:
+        ws = workspace(T, n_experts, k, n_ranks, dedup, dev)
+    o = dict(out or {})
+    ec = o.get("expert_counts")
+    ec = torch.empty(n_experts, dtype=torch.int32, device=dev) if ec is None else ec
+    rc = o.get("rank_counts")
+    rc = torch.empty(n_ranks, dtype=torch.int32, device=dev) if rc is None else rc
+    ro = o.get("rank_offsets")
+    ro = torch.empty(n_ranks + 1, dtype=torch.int32, device=dev) if ro is None else ro
+    eo = None
+    if not dedup:
+        eo = o.get("expert_offsets")
+        eo = torch.empty(n_experts, dtype=torch.int32, device=dev) if eo is None else eo
+    check(lib().moe_send_counts(_ptr(topk_idx), T, n_experts, k, n_ranks, _ptr(placement),
+                                int(bool(dedup)), _ptr(ec), _ptr(rc), _ptr(ro), _ptr(eo),
+                                _ptr(ws), ws.numel(), _stream(stream)), "moe_send_counts")
+    return {"expert_counts": ec, "rank_counts": rc, "rank_offsets": ro,
+            "expert_offsets": eo, "ws": ws}
+
+
+def _x_bpe(x):
+    _dev(x, "x", None, 2)
+    if x.element_size() not in (1, 2, 4):
+        raise TypeError("x must have 1-, 2- or 4-byte elements")
+    return x.element_size()
+
+
+def moe_dispatch_permute(x, topk_idx, topk_gate, n_experts, n_ranks, ws, placement=None,
+                         out=None, stream=None):
+    bpe = _x_bpe(x)
+    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    _dev(topk_gate, "topk_gate", torch.float32, 2)
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    o = dict(out or {})
+    N = T * k
+    send = o.get("send")
+    send = torch.empty((N, H), dtype=x.dtype, device=dev) if send is None else send
+    rt = o.get("row_token")
+    rt = torch.empty(N, dtype=torch.int32, device=dev) if rt is None else rt
+    re = o.get("row_expert")
+    re = torch.empty(N, dtype=torch.int32, device=dev) if re is None else re
+    rw = o.get("row_weight")
+    rw = torch.empty(N, dtype=torch.float32, device=dev) if rw is None else rw
+    sr = o.get("slot_row")
+    sr = torch.empty((T, k), dtype=torch.int32, device=dev) if sr is None else sr
+    if send.numel() < N * H or rt.numel() < N or re.numel() < N or rw.numel() < N:
+        raise ValueError("output buffers are smaller than tokens*top_k rows")
+    check(lib().moe_dispatch_permute(_ptr(x), _ptr(topk_idx), _ptr(topk_gate), T, H, n_experts,
+                                     k, n_ranks, _ptr(placement), bpe, _ptr(ws), ws.numel(),
+                                     _ptr(send), _ptr(rt), _ptr(re), _ptr(rw), _ptr(sr),
+                                     _stream(stream)), "moe_dispatch_permute")
+    return {"send": send, "row_token": rt, "row_expert": re, "row_weight": rw, "slot_row": sr}
+
+
+def moe_dispatch_permute_dedup(x, topk_idx, topk_gate, n_experts, n_ranks, ws, placement=None,
+                               out=None, stream=None):
+    bpe = _x_bpe(x)
+    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    _dev(topk_gate, "topk_gate", torch.float32, 2)
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    o = dict(out or {})
+    N = T * k
+    send = o.get("send")
+    send = torch.empty((N, H), dtype=x.dtype, device=dev) if send is None else send
+    rt = o.get("row_token")
+    rt = torch.empty(N, dtype=torch.int32, device=dev) if rt is None else rt
+    rx = o.get("row_experts")
+    rx = torch.empty((N, k), dtype=torch.int32, device=dev) if rx is None else rx
+    rg = o.get("row_gates")
+    rg = torch.empty((N, k), dtype=torch.float32, device=dev) if rg is None else rg
+    rw = o.get("row_weight")
+    rw = torch.empty(N, dtype=torch.float32, device=dev) if rw is None else rw
+    sr = o.get("slot_row")
+    sr = torch.empty((T, k), dtype=torch.int32, device=dev) if sr is None else sr
+    nr = o.get("n_rows")
+    nr = torch.empty(1, dtype=torch.int32, device=dev) if nr is None else nr
+    if send.numel() < N * H or rx.numel() < N * k or rg.numel() < N * k or rw.numel() < N:
+        raise ValueError("output buffers are smaller than tokens*top_k rows")
+    check(lib().moe_dispatch_permute_dedup(_ptr(x), _ptr(topk_idx), _ptr(topk_gate), T, H,
+                                           n_experts, k, n_ranks, _ptr(placement), bpe,
+                                           _ptr(ws), ws.numel(), _ptr(send), _ptr(rt),
+                                           _ptr(rx), _ptr(rg), _ptr(rw), _ptr(sr), _ptr(nr),
+                                           _stream(stream)), "moe_dispatch_permute_dedup")
+    return {"send": send, "row_token": rt, "row_experts": rx, "row_gates": rg,
+            "row_weight": rw, "slot_row": sr, "n_rows": nr}
+
+
+def moe_combine(rows, row_weight, slot_row, out=None, stream=None):
+    _dev(rows, "rows", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _dev(slot_row, "slot_row", torch.int32, 2)
+    if row_weight is not None:
+        _dev(row_weight, "row_weight", torch.float32)
+    T, k = slot_row.shape
+    H = rows.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=rows.dtype, device=rows.device)
+    _dev(out, "out", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    check(lib().moe_combine(_ptr(rows), _ptr(row_weight), _ptr(slot_row), T, H, k, 2,
+                            _ptr(out), _stream(stream)), "moe_combine")
+    return out
+
+
+def moe_coselect_counts(topk_idx, n_experts, tokens=None, coselect=None, stream=None):
+    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    T, k = topk_idx.shape
+    n = T if tokens is None else min(int(tokens), T)
+    if coselect is None:
+        coselect = torch.zeros((n_experts, n_experts), dtype=torch.int32,
+                               device=topk_idx.device)
+    _dev(coselect, "coselect", torch.int32, 2)
+    check(lib().moe_coselect_counts(_ptr(topk_idx), n, n_experts, k, _ptr(coselect),
+                                    _stream(stream)), "moe_coselect_counts")
+    return coselect

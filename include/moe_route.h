@@ -1,0 +1,213 @@
+/*
+ * moe_route.h - per-GPU MoE expert-parallel dispatch and combine on AMD
+ * Instinct MI355X (gfx950).  Plain C ABI over hand-written HIP kernels.
+ *
+ * What is computed (page title, then section):
+ *  [EC] "Expert Coupling in MoE Pretraining: Reducing All-to-All Overhead with
+ *       Correlated Placement and Token Shuffling" (summary page):
+ *       "Background" (top-k routing), "The Communication Bottleneck" (dispatch,
+ *       experts, combine under expert parallelism), "Method 1: Correlated Expert
+ *       Placement + Deduplicating Dispatcher" (one row per (token, expert) vs one
+ *       row per distinct (token, destination rank) with expert ids and routing
+ *       probabilities; co-selection graph W; E/EP experts per GPU).
+ *  [DD] "DODOCO: MoE AlltoAll Traffic Matrices on Real Text" (dataset card):
+ *       "Setup" (contiguous placement; per-destination input splits),
+ *       "Reading the counts" (one count per token-expert assignment, rows sum to
+ *       tokens x top-k, payload = count x hidden x bytes per element, expert
+ *       block sums = receive totals), "send_matrices.csv columns" (combine moves
+ *       the same volumes back).
+ *  [AD] "AllToAllDispatchScenario" (mlsysim API page), "Attributes": the
+ *       problem's inputs are the token count, device count, expert count, hidden
+ *       size and bytes per element; the argument names below follow them
+ *       (tokens, n_ranks, n_experts, hidden_dim, bytes_per_element).
+ *
+ * Destination ranks are logical: rank r's rows are the contiguous segment
+ * [rank_offsets[r], rank_offsets[r+1]) of one send buffer on this GPU.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is DEVICE memory (hipMalloc'd or a torch tensor's
+ *    data pointer) unless it is marked "host".  All buffers are caller-owned;
+ *    the library allocates nothing, keeps no state between calls and frees
+ *    nothing.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued asynchronously on it; the call returns once the launches are
+ *    queued.  Calls on one stream execute in order.
+ *  - Arrays are dense, row-major, with no padding: [T][k] means element (t, j)
+ *    is at t*k + j.  T = tokens, E = n_experts, k = top_k, R = n_ranks,
+ *    H = hidden_dim, N = T*k.
+ *  - Return value: MOE_OK, or an error code.  Argument checks run on the host
+ *    before anything is enqueued, so on an error nothing has been launched and
+ *    no output has been touched.  MOE_EHIP means a launch failed (outputs are
+ *    then undefined).  No C++ exception crosses the ABI.
+ *  - tokens == 0 is valid: nothing is launched except what is documented.
+ *  - Limits: 1 <= k <= 16, k <= E <= 1024, 1 <= R <= 64, E % R == 0,
+ *    T*k < 2^31.  Outside them: MOE_EUNSUPPORTED (or MOE_EINVAL for values
+ *    that can never be valid).
+ *  - Device-side contents are preconditions that the host cannot check without
+ *    synchronising: expert ids in topk_idx must lie in [0, E) and placement
+ *    values in [0, R).  Out-of-range values are clamped inside the kernels so
+ *    that no access leaves its buffer; the results are then unspecified.
+ *  - Concurrent calls are safe when they use distinct output and workspace
+ *    buffers.
+ */
+#ifndef MOE_ROUTE_H_
+#define MOE_ROUTE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL 1        /* an argument can never be valid (null pointer, k > E, ...) */
+#define MOE_EUNSUPPORTED 2  /* valid for the method but outside this library's limits */
+#define MOE_EWORKSPACE 3    /* workspace_bytes is smaller than moe_workspace_bytes() */
+#define MOE_EHIP 4          /* a HIP launch failed */
+
+#define MOE_MAX_TOP_K 16
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_RANKS 64
+
+/* Host.  A static, NUL-terminated description of a status code (never NULL). */
+const char* moe_status_string(int status);
+
+/* Host.  Bytes of workspace that moe_send_counts() fills and the dispatch call
+ * of the same (topk_idx, placement, dedup) then reads.  Returns 0 if the
+ * arguments are outside the limits above.  The workspace is opaque; it needs
+ * no initialisation and 256-byte alignment is enough. */
+size_t moe_workspace_bytes(int64_t tokens, int n_experts, int top_k, int n_ranks, int dedup);
+
+/* A1 - top-k routing ([EC] "Background"): each token is routed to its k experts
+ * with the largest router logits.
+ *   logits     [T][E] fp32, read only.
+ *   topk_idx   [T][k] int32 out: the selected expert ids in order of logit,
+ *              largest first; equal logits (IEEE equality, so -0.0 == +0.0) go
+ *              to the lower expert id first.  NaN logits are not supported.
+ *   topk_gate  [T][k] fp32 out: softmax over the k selected logits,
+ *              g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), evaluated in fp64 and
+ *              rounded once to fp32 (the pages name "routing probabilities" but
+ *              not their formula; this is the plainest reading).
+ * Errors: MOE_EINVAL for null pointers, tokens < 0, E < 1, k < 1, k > E. */
+int moe_route_topk(const float* logits, int64_t tokens, int n_experts, int top_k,
+                   int32_t* topk_idx, float* topk_gate, void* stream);
+
+/* A2 + A3 - send counts and their exclusive scan ([DD] "Setup", "Reading the
+ * counts"; [EC] "Method 1").
+ *   topk_idx       [T][k] int32, read only (expert ids in [0, E)).
+ *   placement      [E] int32 expert -> rank, values in [0, R), read only; NULL
+ *                  means contiguous: rank r holds experts r*E/R .. (r+1)*E/R-1.
+ *                  The pages' placements hold exactly E/R experts per rank; the
+ *                  kernels do not need that property.
+ *   dedup          0: one row per (token, expert) - rank_counts[r] counts the
+ *                  token-expert assignments whose expert lives on r (each row of
+ *                  the send matrix sums to T*k).  1: one row per distinct (token,
+ *                  rank) - rank_counts[r] counts the tokens with at least one
+ *                  selected expert on r.
+ *   expert_counts  [E] int32 out: #(t, j) with topk_idx[t][j] == e (both modes).
+ *   rank_counts    [R] int32 out, as above.
+ *   rank_offsets   [R+1] int32 out: exclusive scan of rank_counts; rank r's rows
+ *                  are [rank_offsets[r], rank_offsets[r+1]); rank_offsets[R] is
+ *                  the total number of rows (N, or D in dedup mode).
+ *   expert_offsets [E] int32 out, may be NULL; written only when dedup == 0:
+ *                  the first row of expert e's segment.  Inside a rank, experts
+ *                  are laid out in ascending id.
+ *   workspace      device buffer of at least moe_workspace_bytes(...) bytes; it
+ *                  receives the per-tile plan that the dispatch call consumes.
+ * Errors: MOE_EINVAL (null required pointer, bad sizes, E % R != 0),
+ *         MOE_EUNSUPPORTED (limits), MOE_EWORKSPACE. */
+int moe_send_counts(const int32_t* topk_idx, int64_t tokens, int n_experts, int top_k,
+                    int n_ranks, const int32_t* placement, int dedup,
+                    int32_t* expert_counts, int32_t* rank_counts, int32_t* rank_offsets,
+                    int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* A4a - dispatch permute, one row per (token, expert) ([EC] "Method 1",
+ * conventional dispatch; [DD] "Reading the counts").
+ * Must follow moe_send_counts(dedup = 0) on the same stream with the same
+ * topk_idx, placement and workspace (the workspace carries the plan).
+ *   x            [T][H] elements of bytes_per_element bytes (bf16: 2), read only;
+ *                rows are copied bit for bit.  H * bytes_per_element must be a
+ *                multiple of 16.
+ *   topk_gate    [T][k] fp32, read only.
+ *   send         [N][H] out.  Row order: rank ascending; inside a rank, expert id
+ *                ascending; inside an expert, token ascending.
+ *   row_token    [N] int32 out: source token of each row.
+ *   row_expert   [N] int32 out: expert of each row.
+ *   row_weight   [N] fp32 out: the gate of that (token, expert).
+ *   slot_row     [T][k] int32 out: the row that carries slot j of token t.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (bytes_per_element not 1/2/4, row bytes
+ *         not a multiple of 16, limits), MOE_EWORKSPACE. */
+int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* topk_gate,
+                         int64_t tokens, int hidden_dim, int n_experts, int top_k,
+                         int n_ranks, const int32_t* placement, int bytes_per_element,
+                         const void* workspace, size_t workspace_bytes, void* send,
+                         int32_t* row_token, int32_t* row_expert, float* row_weight,
+                         int32_t* slot_row, void* stream);
+
+/* A4b - deduplicating dispatch, one row per distinct (token, destination rank)
+ * ([EC] "Method 1", deduplicating dispatcher).
+ * Must follow moe_send_counts(dedup = 1) on the same stream with the same
+ * topk_idx, placement and workspace.  Capacity is N = T*k rows for every
+ * output so that no host synchronisation is needed; the number of rows written,
+ * D, is stored in *n_rows (and equals rank_offsets[R] of the counts call).
+ *   send         [capacity N][H] out; rows [0, D) written.  Row order: rank
+ *                ascending; inside a rank, token ascending.
+ *   row_token    [N] int32 out.
+ *   row_experts  [N][k] int32 out: the ids of the token's selected experts that
+ *                live on the row's rank, ascending, padded with -1.
+ *   row_gates    [N][k] fp32 out: their gates, aligned with row_experts, padded
+ *                with 0.
+ *   row_weight   [N] fp32 out: the sum of those gates (fp64, ascending expert
+ *                order, rounded once), i.e. the combine weight of the row when
+ *                the experts return their inputs unchanged.
+ *   slot_row     [T][k] int32 out: the row that carries slot j of token t
+ *                (slots whose experts share a rank share a row).
+ *   n_rows       [1] int32 out: D.
+ * Errors: as moe_dispatch_permute. */
+int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx, const float* topk_gate,
+                               int64_t tokens, int hidden_dim, int n_experts, int top_k,
+                               int n_ranks, const int32_t* placement, int bytes_per_element,
+                               const void* workspace, size_t workspace_bytes, void* send,
+                               int32_t* row_token, int32_t* row_experts, float* row_gates,
+                               float* row_weight, int32_t* slot_row, int32_t* n_rows,
+                               void* stream);
+
+/* A5 - combine ([EC] "The Communication Bottleneck"; [DD] "send_matrices.csv
+ * columns": combine moves the dispatch volumes back): each token's output is the
+ * weighted sum of the rows that served it.
+ *   rows         [*][H] bf16, read only: the rows returned by the experts, in the
+ *                send-buffer layout of the dispatch call.
+ *   row_weight   [*] fp32 or NULL (= 1 for every row).
+ *   slot_row     [T][k] int32: rows of each token; negative entries are skipped
+ *                and a row listed by several slots is added once.
+ *   out          [T][H] bf16 out: out[t][h] = bf16(sum over the token's distinct
+ *                rows r, in slot order, of row_weight[r] * rows[r][h]), summed in
+ *                fp32 with fused multiply-adds from -0.0 and rounded once to bf16
+ *                (nearest, ties to even).  Within 1 bf16 ulp of the exactly
+ *                rounded sum when the terms do not cancel.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (bytes_per_element != 2, H*2 not a
+ *         multiple of 16, k > 16). */
+int moe_combine(const void* rows, const float* row_weight, const int32_t* slot_row,
+                int64_t tokens, int hidden_dim, int top_k, int bytes_per_element,
+                void* out, void* stream);
+
+/* A6 - expert co-selection counts ([EC] "Method 1": the correlation graph
+ * counts the tokens that select both experts; "Correlation Formation and
+ * Stability": about 4096 tokens suffice to fit it).
+ *   topk_idx     [T][k] int32; the first `tokens` rows are used.
+ *   coselect     [E][E] int32, ACCUMULATED: for every used token, +1 at
+ *                [a][b] for each ordered pair of distinct selected experts and
+ *                +1 at [a][a] for each selected expert.  Zero it before the
+ *                first call.  Calls that accumulate into the same matrix must
+ *                not run concurrently.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED. */
+int moe_coselect_counts(const int32_t* topk_idx, int64_t tokens, int n_experts, int top_k,
+                        int32_t* coselect, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H_ */

@@ -1,0 +1,60 @@
+"""Helpers for the GPU parity tests (host-side comparisons only)."""
+import sys
+
+import numpy as np
+import torch
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dtype=None):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(dev())
+
+
+def bf16_dev(bits):
+    """uint16 numpy bf16 bits -> torch.bfloat16 on the GPU."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(dev())
+
+
+def bf16_host(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def ordered(bits_u16):
+    """bf16 bit patterns -> integers whose difference counts bf16 ulps."""
+    b = bits_u16.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def bf16_ulp_diff(a, b):
+    return np.abs(ordered(a) - ordered(b))
+
+
+def f32_ulp_diff(a, b):
+    a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    a = np.where(a < 0, -(a & 0x7FFFFFFF), a)
+    b = np.where(b < 0, -(b & 0x7FFFFFFF), b)
+    return np.abs(a - b)
+
+
+def bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,161 @@
+"""The C-ABI library loads without a GPU, exports what include/moe_route.h
+declares, and rejects invalid arguments on the host with the documented codes.
+
+Only argument checks that return before any launch are exercised here (no
+compute call is made without a GPU).  Fake non-null pointers are never
+dereferenced because every case below fails a host check first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_top_router_select_amd import _lib as L
+from combine_top_router_select_amd.build import LIB
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced in these tests
+
+EINVAL, EUNSUP, EWS = L.MOE_EINVAL, L.MOE_EUNSUPPORTED, L.MOE_EWORKSPACE
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} is not built: run python -m combine_top_router_select_amd.build")
+    return L.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(L.SYMBOLS)
+    raw = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = L.status_string(code)
+        assert s and isinstance(s, str)
+    assert "unknown" in L.status_string(99)
+
+
+def test_workspace_bytes(lib):
+    f = lib.moe_workspace_bytes
+    # 4096 tokens, 64 experts, top-6, 16 ranks: 64 tiles x 64 columns int32 plus
+    # one byte per (token, slot), 256-byte sections.
+    n = f(4096, 64, 6, 16, 0)
+    assert n >= 64 * 64 * 4 + 4096 * 6 and n % 256 == 0
+    assert f(4096, 64, 6, 16, 1) > n               # rank columns in dedup mode
+    assert f(0, 64, 6, 16, 0) > 0
+    assert f(10, 64, 6, 5, 0) == 0                 # E % R != 0
+    assert f(10, 64, 65, 16, 0) == 0               # k > E
+    assert f(10, 2048, 6, 16, 0) == 0              # E > 1024
+    assert f(-1, 64, 6, 16, 0) == 0
+
+
+def test_route_errors(lib):
+    f = lib.moe_route_topk
+    assert f(None, 10, 8, 2, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, -1, 8, 2, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 10, 8, 0, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 10, 8, 9, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 10, 0, 1, FAKE, FAKE, None) == EINVAL
+    assert f(FAKE, 10, 64, 17, FAKE, FAKE, None) == EUNSUP
+    assert f(FAKE, 10, 2000, 2, FAKE, FAKE, None) == EUNSUP
+    assert f(FAKE, 2 ** 30, 64, 6, FAKE, FAKE, None) == EUNSUP   # T*k >= 2^31
+    assert f(None, 0, 8, 2, None, None, None) == L.MOE_OK      # empty: nothing launched
+
+
+def test_send_counts_errors(lib):
+    f = lib.moe_send_counts
+    ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)
+    ok = (FAKE, 100, 8, 2, 4, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["idx", "T", "E", "k", "R", "place", "dedup", "ec", "rc", "ro", "eo", "ws",
+                 "wsb", "stream"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return f(*a)
+
+    assert call(R=3) == EINVAL
+    assert call(R=0) == EINVAL
+    assert call(E=128, R=128) == EUNSUP
+    assert call(idx=None) == EINVAL
+    assert call(ec=None) == EINVAL
+    assert call(ws=None) == EINVAL
+    assert call(wsb=ws - 1) == EWS
+    # dedup needs the rank columns too (sizes chosen so that they differ)
+    wsn = lib.moe_workspace_bytes(6400, 8, 2, 4, 0)
+    assert lib.moe_workspace_bytes(6400, 8, 2, 4, 1) > wsn
+    assert call(T=6400, dedup=1, wsb=wsn) == EWS
+
+
+def test_dispatch_errors(lib):
+    f = lib.moe_dispatch_permute
+    ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)
+    base = [FAKE, FAKE, FAKE, 100, 128, 8, 2, 4, None, 2, FAKE, ws, FAKE, FAKE, FAKE, FAKE,
+            FAKE, None]
+    names = ["x", "idx", "gate", "T", "H", "E", "k", "R", "place", "bpe", "ws", "wsb", "send",
+             "rt", "re", "rw", "sr", "stream"]
+
+    def call(**kw):
+        a = list(base)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return f(*a)
+
+    assert call(bpe=3) == EUNSUP
+    assert call(bpe=0) == EINVAL
+    assert call(H=4) == EUNSUP                     # 8 bytes per row: not a multiple of 16
+    assert call(H=0) == EINVAL
+    assert call(wsb=ws - 1) == EWS
+    assert call(send=None) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(ws=None) == EINVAL
+    g = lib.moe_dispatch_permute_dedup
+    wsn = lib.moe_workspace_bytes(6400, 8, 2, 4, 0)
+    wsd = lib.moe_workspace_bytes(6400, 8, 2, 4, 1)
+    assert wsd > wsn
+    args = [FAKE, FAKE, FAKE, 6400, 128, 8, 2, 4, None, 2, FAKE, wsd, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, None, None]
+    assert g(*args) == EINVAL                      # n_rows is NULL
+    args[18] = FAKE
+    args[11] = wsn                                 # non-dedup size is too small for dedup
+    assert g(*args) == EWS
+
+
+def test_combine_and_coselect_errors(lib):
+    c = lib.moe_combine
+    assert c(FAKE, None, FAKE, 10, 128, 2, 4, FAKE, None) == EUNSUP   # only bf16
+    assert c(FAKE, None, FAKE, 10, 4, 2, 2, FAKE, None) == EUNSUP     # 8-byte rows
+    assert c(None, None, FAKE, 10, 128, 2, 2, FAKE, None) == EINVAL
+    assert c(FAKE, None, FAKE, 10, 128, 17, 2, FAKE, None) == EUNSUP
+    assert c(FAKE, None, FAKE, -5, 128, 2, 2, FAKE, None) == EINVAL
+    s = lib.moe_coselect_counts
+    assert s(None, 10, 8, 2, FAKE, None) == EINVAL
+    assert s(FAKE, 10, 8, 9, FAKE, None) == EINVAL
+    assert s(FAKE, 10, 8, 2, None, None) == EINVAL
+
+
+def test_product_path_does_not_touch_oracle():
+    """The package sources never import, load or name the oracle."""
+    pkg = os.path.join(ROOT, "combine_top_router_select_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, fn)).read()
+                for pat in (r"^\s*(from|import)\s+oracle", r"liboracle", r"oracle\.c\b",
+                            r"oracle_[a-z_]+\("):
+                    assert not re.search(pat, txt, flags=re.M), (fn, pat)
