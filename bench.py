@@ -104,6 +104,7 @@ class BufferSet:
             self.disp["row_expert"] = torch.empty(N, dtype=i32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.W = torch.zeros((E, E), dtype=i32, device=dev)
+        self.cws = ops.coselect_workspace(w.coselect_tokens, E, dev)
 
     def nbytes(self):
         tot = 0
@@ -131,7 +132,7 @@ def gpu_step(ops, b, w, dedup, ev=None):
     ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b.out)
     if ev:
         ev[3].record()
-    ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W)
+    ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W, ws=b.cws)
 
 
 def cpu_baseline(inp, w, dedup, seconds):

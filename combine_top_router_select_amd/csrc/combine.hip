@@ -37,34 +37,50 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
   const int c = int(wid - t * cpr);
   if (t >= T) return;  // whole wave
   const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
-  int r = -1;
-  if (lane < k) r = slot_row[t * k + lane];
-  bool use = lane < k && r >= 0;
+  // All loads are unconditional from clamped, in-bounds addresses (a load under
+  // a branch is followed by a wait for it); only arithmetic and stores are
+  // predicated.
+  const int jl = lane < k ? lane : k - 1;
+  const int r_raw = slot_row[t * k + jl];
+  const int r = lane < k ? r_raw : -1;
+  bool use = r >= 0;
   for (int i = 0; i < k; ++i) {
     const int ri = bcast(r, i);
     if (i < lane && ri == r) use = false;
   }
-  float wr = 1.0f;
-  if (use && w) wr = w[r];
   uint64_t um = __ballot(use);
   const int nrows = __popcll(um);
+  uint8_t* dst = out + t * row_bytes;
+  if (nrows == 0) {  // no row serves this token: the empty sum, -0.0
+    const u32x4 nz = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
+      if (off < row_bytes) store16(dst + off, nz);
+    }
+    return;
+  }
+  const int j0 = __ffsll((unsigned long long)um) - 1;
+  const int rr = use ? r : bcast(r, j0);  // every lane names a valid row
+  const float wr = w ? w[rr] : 1.0f;
 
   u32x4 y[KMAX][NV];
   float wq[KMAX];
 #pragma unroll
   for (int q = 0; q < KMAX; ++q) {
-    wq[q] = 0.0f;
+    int j = j0;
     if (q < nrows) {
-      const int j = __ffsll((unsigned long long)um) - 1;
+      j = __ffsll((unsigned long long)um) - 1;
       um &= um - 1;
-      const int p = bcast(r, j);
-      wq[q] = bcastf(wr, j);
-      const uint8_t* src = rows + int64_t(p) * row_bytes + chunk0;
+    }
+    const int p = bcast(rr, j);
+    wq[q] = bcastf(wr, j);
+    const uint8_t* src = rows + int64_t(p) * row_bytes;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int64_t off = int64_t(i * kWave + lane) * 16;
-        if (chunk0 + off < row_bytes) y[q][i] = load16(src + off);
-      }
+    for (int i = 0; i < NV; ++i) {
+      int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
+      off = off < row_bytes ? off : row_bytes - 16;
+      y[q][i] = load16(src + off);
     }
   }
   float acc[NV][8];
@@ -87,11 +103,10 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
       }
     }
   }
-  uint8_t* dst = out + t * row_bytes + chunk0;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int64_t off = int64_t(i * kWave + lane) * 16;
-    if (chunk0 + off < row_bytes) {
+    const int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
+    if (off < row_bytes) {
       u32x4 o;
 #pragma unroll
       for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(acc[i][2 * h], acc[i][2 * h + 1]);

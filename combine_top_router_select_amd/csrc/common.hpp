@@ -46,16 +46,20 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) {
 }
 
 // Plan written by moe_send_counts, read by the dispatch kernels.
-//   header[0]  total rows (N, or D in dedup mode)
-//   base[B][C] absolute first row of column c inside tile b, C = E (+ R in
-//              dedup mode: columns E..E+R-1 are ranks)
-//   lrank[T][k] uint8: rank of (t, j) among the tile's earlier tokens that use
-//              the same column (expert, or rank in dedup mode)
+//   header[0]        total rows (N, or D in dedup mode)
+//   base[B][CP]      int32: absolute first row, inside tile b, of position
+//                    column c (the expert in plain mode, the rank in dedup mode)
+//   tcnt[B][C]       uint8: tokens of tile b that use column c (experts, then
+//                    ranks in dedup mode); at most 64, the tile size
+//   lslot[T][k]      uint32: (position column << 8) | rank of (t, j) among the
+//                    tile's earlier tokens that use the same position column
 struct PlanLayout {
   int64_t tiles;      // B = ceil(T / 64)
-  int cols;           // C
+  int cols;           // C: columns counted per tile (experts, + ranks in dedup mode)
+  int pos_cols;       // CP: position columns (experts, or ranks in dedup mode)
   size_t base_off;    // byte offsets inside the workspace
-  size_t lrank_off;
+  size_t tcnt_off;
+  size_t lslot_off;
   size_t bytes;
 };
 
@@ -66,10 +70,20 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t tokens, int n_experts,
   PlanLayout p;
   p.tiles = (tokens + kTile - 1) / kTile;
   p.cols = n_experts + (dedup ? n_ranks : 0);
+  p.pos_cols = dedup ? n_ranks : n_experts;
   p.base_off = 256;
-  p.lrank_off = align256(p.base_off + size_t(p.tiles) * size_t(p.cols) * 4);
-  p.bytes = align256(p.lrank_off + size_t(tokens) * size_t(top_k));
+  p.tcnt_off = align256(p.base_off + size_t(p.tiles) * size_t(p.pos_cols) * 4);
+  // +16: the scan reads the counts in 16-byte vectors
+  p.lslot_off = align256(p.tcnt_off + size_t(p.tiles) * size_t(p.cols) + 16);
+  p.bytes = align256(p.lslot_off + size_t(tokens) * size_t(top_k) * 4);
   return p;
+}
+
+// Keeps the compiler from moving LDS accesses of one wave across this point;
+// a wave's own LDS operations are executed in program order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
 }  // namespace moe

@@ -10,7 +10,8 @@
 // conventional dispatcher.
 //
 // Design: one wave per (token, row chunk).  Lanes j < k first resolve slot j's
-// destination row from the plan (base[tile][column] + lrank), then the wave
+// destination row from the plan (base[tile][column] + the slot's rank inside
+// the tile), then the wave
 // reads its chunk of x[t] once into registers (16-byte loads, 1 KiB per wave
 // instruction) and writes it to each destination row.  Every access is a full,
 // contiguous row segment, so reads and writes are perfectly coalesced; nothing
@@ -20,13 +21,17 @@
 
 namespace moe {
 
+// Loads are issued unconditionally from addresses clamped into the row, so a
+// wave's loads go out back to back (a load under a lane-divergent branch is
+// followed by a wait for it); only the stores are predicated.
 template <int NV>
-__device__ __forceinline__ void load_chunk(u32x4 (&v)[NV], const uint8_t* src, int64_t chunk0,
+__device__ __forceinline__ void load_chunk(u32x4 (&v)[NV], const uint8_t* row, int64_t chunk0,
                                            int row_bytes, int lane) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int64_t off = int64_t(i * kWave + lane) * 16;
-    if (chunk0 + off < row_bytes) v[i] = load16(src + off);
+    int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
+    off = off < row_bytes ? off : row_bytes - 16;
+    v[i] = load16(row + off);
   }
 }
 
@@ -49,8 +54,8 @@ template <int NV, bool NT>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
                 const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k, int cpr,
-                const int32_t* __restrict__ base, const uint8_t* __restrict__ lrank, int C,
-                uint8_t* __restrict__ send, int32_t* __restrict__ row_token,
+                const int32_t* __restrict__ base, const uint32_t* __restrict__ lslot, int stride,
+                int col_off, uint8_t* __restrict__ send, int32_t* __restrict__ row_token,
                 int32_t* __restrict__ row_expert, float* __restrict__ row_weight,
                 int32_t* __restrict__ slot_row) {
   const int lane = lane_id();
@@ -59,24 +64,25 @@ dispatch_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
   const int c = int(wid - t * cpr);
   if (t >= T) return;  // whole wave
   const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
-  int e = 0, lr = 0;
-  if (lane < k) {
-    e = clampi(idx[t * k + lane], 0, E - 1);
-    lr = lrank[t * k + lane];
-  }
+  // lanes j < k own slot j; the other lanes load slot k-1's data and ignore it
+  const int jl = lane < k ? lane : k - 1;
+  const uint32_t code = lslot[t * k + jl];  // (expert << 8) | rank inside the tile
+  const float g = gate[t * k + jl];
   u32x4 v[NV];
-  load_chunk<NV>(v, x + t * row_bytes + chunk0, chunk0, row_bytes, lane);
-  int pos = 0;
-  if (lane < k) pos = base[(t / kTile) * C + e] + lr;
+  load_chunk<NV>(v, x + t * row_bytes, chunk0, row_bytes, lane);
+  const int e = int(code >> 8);
+  const int pos = base[(t / kTile) * stride + col_off + e] + int(code & 255u);
+  for (int j = 0; j < k; ++j) {
+    const int p = bcast(pos, j);
+    store_chunk<NV, NT>(v, send + int64_t(p) * row_bytes + chunk0, chunk0, row_bytes, lane);
+  }
+  // metadata last: stores count against the same wait counter as loads, so
+  // stores issued before the row stores would hold them up
   if (c == 0 && lane < k) {
     slot_row[t * k + lane] = pos;
     row_token[pos] = int32_t(t);
     row_expert[pos] = e;
-    row_weight[pos] = gate[t * k + lane];
-  }
-  for (int j = 0; j < k; ++j) {
-    const int p = bcast(pos, j);
-    store_chunk<NV, NT>(v, send + int64_t(p) * row_bytes + chunk0, chunk0, row_bytes, lane);
+    row_weight[pos] = g;
   }
 }
 
@@ -85,8 +91,8 @@ __global__ void __launch_bounds__(256)
 dispatch_dedup_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
                       const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k,
                       int R, const int32_t* __restrict__ place, int m, int cpr,
-                      const int32_t* __restrict__ base, const uint8_t* __restrict__ lrank, int C,
-                      const int32_t* __restrict__ header, uint8_t* __restrict__ send,
+                      const int32_t* __restrict__ base, const uint32_t* __restrict__ lslot,
+                      int stride, int col_off, const int32_t* __restrict__ header, uint8_t* __restrict__ send,
                       int32_t* __restrict__ row_token, int32_t* __restrict__ row_experts,
                       float* __restrict__ row_gates, float* __restrict__ row_weight,
                       int32_t* __restrict__ slot_row, int32_t* __restrict__ n_rows) {
@@ -97,18 +103,15 @@ dispatch_dedup_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__
   const int c = int(wid - t * cpr);
   if (t >= T) return;  // whole wave
   const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
-  int e = 0, r = -1, lr = 0;
-  float g = 0.0f;
-  if (lane < k) {
-    e = clampi(idx[t * k + lane], 0, E - 1);
-    r = place ? clampi(place[e], 0, R - 1) : e / m;
-    lr = lrank[t * k + lane];
-    g = gate[t * k + lane];
-  }
+  const int jl = lane < k ? lane : k - 1;
+  const int e = clampi(idx[t * k + jl], 0, E - 1);
+  const uint32_t code = lslot[t * k + jl];  // (rank << 8) | rank inside the tile
+  const float g = gate[t * k + jl];
   u32x4 v[NV];
-  load_chunk<NV>(v, x + t * row_bytes + chunk0, chunk0, row_bytes, lane);
-  int pos = 0;
-  if (lane < k) pos = base[(t / kTile) * C + E + r] + lr;
+  load_chunk<NV>(v, x + t * row_bytes, chunk0, row_bytes, lane);
+  const int r_own = int(code >> 8);
+  const int pos = base[(t / kTile) * stride + col_off + r_own] + int(code & 255u);
+  const int r = lane < k ? r_own : -1;  // lanes >= k match no slot below
   // Per slot: is it the first slot of its rank (the row's leader)?  Its column
   // among the rank's experts (ascending id), the rank's slot count, and its
   // position in the token's ascending expert order.
@@ -123,6 +126,13 @@ dispatch_dedup_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__
     }
     if (ei < e) ++sidx;
   }
+  const uint64_t lm = __ballot(leader);
+  for (int j = 0; j < k; ++j) {
+    if (!((lm >> j) & 1ull)) continue;
+    const int p = bcast(pos, j);
+    store_chunk<NV, NT>(v, send + int64_t(p) * row_bytes + chunk0, chunk0, row_bytes, lane);
+  }
+  // metadata after the row stores (see the plain kernel)
   if (c == 0) {
     if (lane < k) {
       slot_row[t * k + lane] = pos;
@@ -147,12 +157,6 @@ dispatch_dedup_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__
       if (leader && rs == r) wsum += double(gs);
     }
     if (leader) row_weight[pos] = float(wsum);
-  }
-  const uint64_t lm = __ballot(leader);
-  for (int j = 0; j < k; ++j) {
-    if (!((lm >> j) & 1ull)) continue;
-    const int p = bcast(pos, j);
-    store_chunk<NV, NT>(v, send + int64_t(p) * row_bytes + chunk0, chunk0, row_bytes, lane);
   }
 }
 
@@ -179,7 +183,7 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
   const int32_t* header = reinterpret_cast<const int32_t*>(ws);
   const int32_t* base = reinterpret_cast<const int32_t*>(ws + pl.base_off);
-  const uint8_t* lrank = ws + pl.lrank_off;
+  const uint32_t* lslot = reinterpret_cast<const uint32_t*>(ws + pl.lslot_off);
   const int chunk = NV * kWave * 16;
   const int cpr = (row_bytes + chunk - 1) / chunk;
   const int64_t waves = T * cpr;
@@ -190,12 +194,12 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
     if (T == 0) return hipSuccess;
     hipLaunchKernelGGL((dispatch_kernel<NV, NT>), dim3(unsigned(blocks)), dim3(256), 0, stream,
                        static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, cpr, base,
-                       lrank, pl.cols, static_cast<uint8_t*>(send), row_token, row_e,
+                       lslot, pl.pos_cols, 0, static_cast<uint8_t*>(send), row_token, row_e,
                        row_weight, slot_row);
   } else {
     hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT>), dim3(unsigned(blocks)), dim3(256), 0,
                        stream, static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, R,
-                       place, E / R, cpr, base, lrank, pl.cols, header,
+                       place, E / R, cpr, base, lslot, pl.pos_cols, 0, header,
                        static_cast<uint8_t*>(send), row_token, row_e, row_gates, row_weight,
                        slot_row, n_rows);
   }

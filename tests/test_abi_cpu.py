@@ -53,9 +53,13 @@ def test_workspace_bytes(lib):
     f = lib.moe_workspace_bytes
     # 4096 tokens, 64 experts, top-6, 16 ranks: 64 tiles x 64 columns int32 plus
     # one byte per (token, slot), 256-byte sections.
+    # plain: bases for 64 tiles x 64 experts (int32), one count byte per tile
+    # and expert, one 4-byte slot code per (token, slot); 256-byte sections
     n = f(4096, 64, 6, 16, 0)
-    assert n >= 64 * 64 * 4 + 4096 * 6 and n % 256 == 0
-    assert f(4096, 64, 6, 16, 1) > n               # rank columns in dedup mode
+    assert n >= 64 * 64 * 4 + 64 * 64 + 4096 * 6 * 4 and n % 256 == 0
+    # dedup: bases only for the 16 rank columns, counts for experts and ranks
+    nd = f(4096, 64, 6, 16, 1)
+    assert nd >= 64 * 16 * 4 + 64 * 80 + 4096 * 6 * 4 and nd % 256 == 0
     assert f(0, 64, 6, 16, 0) > 0
     assert f(10, 64, 6, 5, 0) == 0                 # E % R != 0
     assert f(10, 64, 65, 16, 0) == 0               # k > E
@@ -96,10 +100,8 @@ def test_send_counts_errors(lib):
     assert call(ec=None) == EINVAL
     assert call(ws=None) == EINVAL
     assert call(wsb=ws - 1) == EWS
-    # dedup needs the rank columns too (sizes chosen so that they differ)
-    wsn = lib.moe_workspace_bytes(6400, 8, 2, 4, 0)
-    assert lib.moe_workspace_bytes(6400, 8, 2, 4, 1) > wsn
-    assert call(T=6400, dedup=1, wsb=wsn) == EWS
+    wsd = lib.moe_workspace_bytes(6400, 8, 2, 4, 1)
+    assert call(T=6400, dedup=1, wsb=wsd - 1) == EWS
 
 
 def test_dispatch_errors(lib):
@@ -125,14 +127,12 @@ def test_dispatch_errors(lib):
     assert call(x=None) == EINVAL
     assert call(ws=None) == EINVAL
     g = lib.moe_dispatch_permute_dedup
-    wsn = lib.moe_workspace_bytes(6400, 8, 2, 4, 0)
     wsd = lib.moe_workspace_bytes(6400, 8, 2, 4, 1)
-    assert wsd > wsn
     args = [FAKE, FAKE, FAKE, 6400, 128, 8, 2, 4, None, 2, FAKE, wsd, FAKE, FAKE, FAKE, FAKE,
             FAKE, FAKE, None, None]
     assert g(*args) == EINVAL                      # n_rows is NULL
     args[18] = FAKE
-    args[11] = wsn                                 # non-dedup size is too small for dedup
+    args[11] = wsd - 1                             # one byte short
     assert g(*args) == EWS
 
 
@@ -144,9 +144,15 @@ def test_combine_and_coselect_errors(lib):
     assert c(FAKE, None, FAKE, 10, 128, 17, 2, FAKE, None) == EUNSUP
     assert c(FAKE, None, FAKE, -5, 128, 2, 2, FAKE, None) == EINVAL
     s = lib.moe_coselect_counts
-    assert s(None, 10, 8, 2, FAKE, None) == EINVAL
-    assert s(FAKE, 10, 8, 9, FAKE, None) == EINVAL
-    assert s(FAKE, 10, 8, 2, None, None) == EINVAL
+    wsb = lib.moe_coselect_workspace_bytes(10, 8)
+    assert wsb >= 8 * 8 and wsb % 256 == 0
+    assert lib.moe_coselect_workspace_bytes(4096, 128) == 128 * 64 * 8
+    assert lib.moe_coselect_workspace_bytes(10, 0) == 0
+    assert s(None, 10, 8, 2, FAKE, FAKE, wsb, None) == EINVAL
+    assert s(FAKE, 10, 8, 9, FAKE, FAKE, wsb, None) == EINVAL
+    assert s(FAKE, 10, 8, 2, None, FAKE, wsb, None) == EINVAL
+    assert s(FAKE, 10, 8, 2, FAKE, None, wsb, None) == EINVAL
+    assert s(FAKE, 10, 8, 2, FAKE, FAKE, wsb - 1, None) == EWS
 
 
 def test_product_path_does_not_touch_oracle():

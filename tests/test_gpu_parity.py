@@ -128,6 +128,18 @@ def test_dispatch_parity_small(oracle_mod, T, H, E, k, R, dedup, pl):
                         explicit_place=(pl == "explicit"))
 
 
+@pytest.mark.parametrize("dedup", [False, True])
+def test_dispatch_parity_large_plan(oracle_mod, dedup):
+    """70000 tokens: the per-tile plan no longer fits one workgroup's LDS, so
+    the counts take the two-kernel path (tile counts, then a scan)."""
+    T, H, E, k, R = 70000, 32, 64, 4, 16
+    say(f"[dispatch] large plan T={T} dedup={dedup}")
+    inp = WL.make_custom_inputs(T, H, E, seed=99)
+    idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+    placement = WL.random_placement(E, R, seed=5)
+    run_dispatch_parity(oracle_mod, inp["x_bits"], idx_o, gate_o, E, R, placement, dedup)
+
+
 def test_dispatch_empty_ranks(oracle_mod):
     """Tokens that only ever pick experts of ranks 0 and 2: ranks 1 and 3 are
     empty segments."""
