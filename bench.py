@@ -6,7 +6,9 @@
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input, with inputs resident in HBM: top-k routing -> send counts and
 offsets -> dispatch permute -> combine (identity experts: the combine reads the
-send buffer) -> co-selection counts.  The workload defaults to 4096 tokens,
+send buffer), and the co-selection counts of the routed tokens.  Everything
+runs on one stream; --overlap forks the co-selection counts (which depend only
+on the routing) onto a second stream and joins them before the step ends.  The workload defaults to 4096 tokens,
 hidden 2048 bf16, 64 experts, top-6, 16 logical ranks, contiguous placement
 (DeepSeek-MoE-16B-shaped), plain (one row per token-expert) dispatch.
 
@@ -44,6 +46,8 @@ def parse():
     p.add_argument("--workload", default="deepseek_moe_16b")
     p.add_argument("--dedup", action="store_true")
     p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    p.add_argument("--overlap", action="store_true",
+                   help="run the co-selection counts on a second stream")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--footprint-gib", type=float, default=2.0,
@@ -105,6 +109,8 @@ class BufferSet:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.W = torch.zeros((E, E), dtype=i32, device=dev)
         self.cws = ops.coselect_workspace(w.coselect_tokens, E, dev)
+        self.ev_routed = torch.cuda.Event()
+        self.ev_coselected = torch.cuda.Event()
 
     def nbytes(self):
         tot = 0
@@ -116,11 +122,20 @@ class BufferSet:
         return tot
 
 
-def gpu_step(ops, b, w, dedup, ev=None):
-    """One pass of the hot path.  ev = (e0, e1, e2, e3) events bracketing the
-    dispatch and the combine kernels, recorded on the current stream."""
+def gpu_step(torch, ops, b, w, dedup, side=None, ev=None):
+    """One pass of the hot path.  With a side stream, the co-selection counts run
+    there, after the routing and concurrently with the rest.  ev = (e0, e1, e2,
+    e3) events bracketing the dispatch and the combine kernels, recorded on the
+    stream they run on."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
+    main = torch.cuda.current_stream()
     ops.moe_route_topk(b.logits, k, b.idx, b.gate)
+    if side is not None:
+        b.ev_routed.record(main)
+        side.wait_event(b.ev_routed)
+        ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W, ws=b.cws,
+                                stream=side)
+        b.ev_coselected.record(side)
     c = ops.moe_send_counts(b.idx, E, R, b.place, dedup, ws=b.ws, out=b.cnt)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
     if ev:
@@ -132,7 +147,10 @@ def gpu_step(ops, b, w, dedup, ev=None):
     ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b.out)
     if ev:
         ev[3].record()
-    ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W, ws=b.cws)
+    if side is not None:
+        main.wait_event(b.ev_coselected)
+    else:
+        ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W, ws=b.cws)
 
 
 def cpu_baseline(inp, w, dedup, seconds):
@@ -185,6 +203,7 @@ def main():
     sets = [first] + [BufferSet(torch, ops, inp, w, dedup, dev) for _ in range(nsets - 1)]
     torch.cuda.synchronize()
 
+    side = torch.cuda.Stream() if a.overlap else None
     graphs = None
     if a.graph:
         graphs = []
@@ -192,13 +211,13 @@ def main():
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for b in sets:       # warm the code paths once outside capture
-                gpu_step(ops, b, w, dedup)
+                gpu_step(torch, ops, b, w, dedup, side)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         for b in sets:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                gpu_step(ops, b, w, dedup)
+                gpu_step(torch, ops, b, w, dedup, side)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -206,7 +225,7 @@ def main():
         if graphs is not None:
             graphs[i % nsets].replay()
         else:
-            gpu_step(ops, sets[i % nsets], w, dedup, ev)
+            gpu_step(torch, ops, sets[i % nsets], w, dedup, side, ev)
 
     for i in range(a.warmup):
         step(i)
@@ -224,7 +243,7 @@ def main():
     K2 = min(a.steps, 100)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K2)]
     for i in range(K2):
-        gpu_step(ops, sets[(a.warmup + a.steps + i) % nsets], w, dedup, evs[i])
+        gpu_step(torch, ops, sets[(a.warmup + a.steps + i) % nsets], w, dedup, side, evs[i])
     torch.cuda.synchronize()
     t_disp = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
     t_comb = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e-3
@@ -259,6 +278,7 @@ def main():
                    "top_k": k, "n_ranks": R, "placement": w.placement,
                    "dispatch": "dedup" if dedup else "nondedup",
                    "bytes_per_element": 2, "graph": bool(a.graph),
+                   "coselect_stream": "side" if a.overlap else "main",
                    "buffer_sets": nsets, "footprint_MiB": round(nsets * per_set / 2 ** 20)},
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",

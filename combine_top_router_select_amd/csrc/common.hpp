@@ -45,16 +45,19 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
-// Plan written by moe_send_counts, read by the dispatch kernels.
+// Plan written by moe_send_counts, read by the dispatch kernels.  Per-column
+// arrays are column-major with the tile index padded to Bp = roundup(B, 16), so
+// that one thread can stream a column with 16-byte accesses.
 //   header[0]        total rows (N, or D in dedup mode)
-//   base[B][CP]      int32: absolute first row, inside tile b, of position
+//   base[CP][Bp]     int32: absolute first row, inside tile b, of position
 //                    column c (the expert in plain mode, the rank in dedup mode)
-//   tcnt[B][C]       uint8: tokens of tile b that use column c (experts, then
+//   tcnt[C][Bp]      uint8: tokens of tile b that use column c (experts, then
 //                    ranks in dedup mode); at most 64, the tile size
 //   lslot[T][k]      uint32: (position column << 8) | rank of (t, j) among the
 //                    tile's earlier tokens that use the same position column
 struct PlanLayout {
   int64_t tiles;      // B = ceil(T / 64)
+  int64_t tiles_pad;  // Bp = roundup(B, 16)
   int cols;           // C: columns counted per tile (experts, + ranks in dedup mode)
   int pos_cols;       // CP: position columns (experts, or ranks in dedup mode)
   size_t base_off;    // byte offsets inside the workspace
@@ -69,14 +72,27 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t tokens, int n_experts,
                                                   int n_ranks, int dedup) {
   PlanLayout p;
   p.tiles = (tokens + kTile - 1) / kTile;
+  p.tiles_pad = (p.tiles + 15) / 16 * 16;
   p.cols = n_experts + (dedup ? n_ranks : 0);
   p.pos_cols = dedup ? n_ranks : n_experts;
   p.base_off = 256;
-  p.tcnt_off = align256(p.base_off + size_t(p.tiles) * size_t(p.pos_cols) * 4);
-  // +16: the scan reads the counts in 16-byte vectors
-  p.lslot_off = align256(p.tcnt_off + size_t(p.tiles) * size_t(p.cols) + 16);
+  p.tcnt_off = align256(p.base_off + size_t(p.pos_cols) * size_t(p.tiles_pad) * 4);
+  p.lslot_off = align256(p.tcnt_off + size_t(p.cols) * size_t(p.tiles_pad));
   p.bytes = align256(p.lslot_off + size_t(tokens) * size_t(top_k) * 4);
   return p;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and row
+// broadcasts (the gfx9 family has row_bcast:15/31): no LDS round trips.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  int v = x + __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);         // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, x, 0x113, 0xF, 0xF, true);         // row_shr:3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xE, false);        // row_shr:4, lanes 4..15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xC, false);        // row_shr:8, lanes 8..15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);        // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);        // row_bcast:31 -> rows 2, 3
+  return v;
 }
 
 // Keeps the compiler from moving LDS accesses of one wave across this point;

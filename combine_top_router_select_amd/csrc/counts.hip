@@ -14,13 +14,15 @@
 // the bits below a lane is the token's rank among the tile's earlier users of
 // the column; popcount of the whole bitmap is the tile's count.  The tile
 // counts are then scanned over tiles, per column, into the absolute first row
-// of each tile in each column.  A row's position is base[tile][column] + rank,
+// of each tile in each column.  A row's position is base[column][tile] + rank,
 // which makes the send buffer order (rank, expert, token) - or (rank, token) -
 // stable and deterministic.  No global atomics anywhere.
 //
 // Two kernels: tile_counts (one wave per tile, so the per-assignment work and
 // its memory traffic spread over many CUs) and plan_scan (one workgroup, which
-// only reads the per-tile counts, one byte each, and writes the bases).
+// only reads the per-tile counts, one byte each, and writes the bases).  Both
+// per-tile arrays are column-major, so a scan thread streams a run of one
+// column's tiles with 16-byte loads and stores.
 //
 // All global loads are issued unconditionally from clamped, in-bounds
 // addresses and only stores are predicated: a load under a branch is followed
@@ -101,7 +103,7 @@ __device__ __forceinline__ void count_tile(const int (&raw)[KMAX], int64_t f0, i
 template <bool DEDUP, int KMAX>
 __global__ void __launch_bounds__(kWave)
 tile_counts_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k, int R,
-                   const int32_t* __restrict__ place, int m, uint32_t kmul,
+                   const int32_t* __restrict__ place, int m, uint32_t kmul, int64_t Bp,
                    uint8_t* __restrict__ tcnt, uint32_t* __restrict__ lslot) {
   extern __shared__ uint64_t s_tdyn[];
   const int C = E + (DEDUP ? R : 0);
@@ -121,7 +123,7 @@ tile_counts_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k, int
   wave_lds_sync();
   count_tile<DEDUP, KMAX>(raw, f0, nf, k, kmul, E, has_rank ? s_rank : nullptr, m, bits, lslot,
                           lane);
-  for (int c = lane; c < C; c += kWave) tcnt[b * C + c] = uint8_t(__popcll(bits[c]));
+  for (int c = lane; c < C; c += kWave) tcnt[c * Bp + b] = uint8_t(__popcll(bits[c]));
 }
 
 // ------------------------------------------------------------------- scan --
@@ -129,42 +131,64 @@ tile_counts_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k, int
 constexpr int kScanThreads = 1024;
 constexpr int kScanWaves = kScanThreads / kWave;
 constexpr int kMaxCols = MOE_MAX_EXPERTS + MOE_MAX_RANKS;
-constexpr int kScanMaxStaged = 32 * 1024;  // tile-count bytes staged in LDS
-constexpr int kMaxQ = 16;                   // tile chunks per column
+constexpr int kMaxQ = 16;  // tile chunks per column
+constexpr int kKeep = 8;   // 16-tile vectors a scan thread keeps in registers
 
-// Tile counts are read from LDS (STAGED) or straight from global memory.
-template <bool STAGED>
-__device__ __forceinline__ int tc_at(const uint8_t* __restrict__ g, const uint8_t* s, size_t i) {
-  return STAGED ? int(s[i]) : int(g[i]);
+// Sum of the 16 bytes of v (v_sad_u8 against zero adds four bytes at a time).
+__device__ __forceinline__ int byte_sum(const u32x4& v) {
+  uint32_t s = __builtin_amdgcn_sad_u8(v.x, 0u, 0u);
+  s = __builtin_amdgcn_sad_u8(v.y, 0u, s);
+  s = __builtin_amdgcn_sad_u8(v.z, 0u, s);
+  s = __builtin_amdgcn_sad_u8(v.w, 0u, s);
+  return int(s);
 }
 
-// Inclusive scan over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
+// Keeps the first n bytes of v and zeroes the rest (n <= 0: all zero).  The
+// padding tiles B..Bp-1 of a column are never written by tile_counts.
+__device__ __forceinline__ u32x4 keep_bytes(u32x4 v, int n) {
+  u32x4 r;
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(v, off, kWave);
-    v += lane >= off ? o : 0;
+  for (int i = 0; i < 4; ++i) {
+    const int nb = clampi(n - 4 * i, 0, 4);
+    const uint32_t mk = nb >= 4 ? ~0u : ((1u << (8 * nb)) - 1u);
+    r[i] = v[i] & mk;
   }
-  return v;
+  return r;
 }
 
-// One workgroup: per column, the sum of each chunk of tiles, the chunk's
-// prefix and the column total; experts are ordered by (rank, id) with a
-// counting sort and one block-wide scan; then every (tile, position column)
-// gets its absolute first row.  Loops are short and their loads independent,
-// so no phase waits on a chain of LDS round trips.
-template <bool DEDUP, bool STAGED>
+// Writes the running first row of 16 consecutive tiles of one position column.
+__device__ __forceinline__ void put_bases(const u32x4& v, int32_t& run, int32_t* dst) {
+  int32_t o[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    o[i] = run;
+    run += int32_t((v[i / 4] >> (8 * (i % 4))) & 255u);
+  }
+  u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    d4[i] = u32x4{uint32_t(o[4 * i]), uint32_t(o[4 * i + 1]), uint32_t(o[4 * i + 2]),
+                  uint32_t(o[4 * i + 3])};
+}
+
+// One workgroup.  Each column's Bp/16 tile vectors are split into Q chunks,
+// one (column, chunk) unit per thread: chunk sums, then per chunk the sum of
+// the column's earlier chunks and the column total; experts are ordered by
+// (rank, id) with a counting sort and one block-wide scan; then every unit of
+// a position column writes the absolute first row of each of its tiles.
+// KEEP: each thread owns at most one unit of at most kKeep vectors and keeps
+// them in registers between the two passes; otherwise units loop and the
+// second pass loads its vectors again (large inputs only).
+template <bool DEDUP, bool KEEP>
 __global__ void __launch_bounds__(kScanThreads)
-plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int E, int R,
+plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, int E, int R,
                  const int32_t* __restrict__ place, int m, int32_t* __restrict__ expert_counts,
                  int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
                  int32_t* __restrict__ expert_offsets, int32_t* __restrict__ header,
                  int32_t* __restrict__ base) {
-  extern __shared__ u32x4 s_tc4[];
-  __shared__ int32_t s_part[kMaxCols];       // [q][c] chunk sums
-  __shared__ int32_t s_pre[kMaxCols];        // [q][c] chunk prefixes
-  __shared__ int32_t s_tot[kMaxCols];        // column totals
+  __shared__ int32_t s_part[kMaxCols];  // [c][q] chunk sums
+  __shared__ int32_t s_pre[kMaxCols];   // [c][q] sums of the column's earlier chunks
+  __shared__ int32_t s_tot[kMaxCols];   // column totals
   __shared__ int32_t s_colbase[MOE_MAX_EXPERTS];
   __shared__ int32_t s_sorted[MOE_MAX_EXPERTS];
   __shared__ uint64_t s_rmask[MOE_MAX_RANKS][MOE_MAX_EXPERTS / kWave];
@@ -172,70 +196,76 @@ plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int E, int R,
   __shared__ int32_t s_rstart[MOE_MAX_RANKS + 1];
   __shared__ int32_t s_ro[MOE_MAX_RANKS + 1];
   __shared__ int32_t s_wsum[kScanWaves];
-  const uint8_t* s_tc = reinterpret_cast<const uint8_t*>(s_tc4);
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = tid / kWave;
   const int C = E + (DEDUP ? R : 0);
-  const int CP = DEDUP ? R : E;
   const int cbase = DEDUP ? E : 0;  // first position column among the counted ones
-  int Q = kScanThreads / C;
-  Q = Q < 1 ? 1 : (Q > kMaxQ ? kMaxQ : Q);
+  const int nvec = Bp / 16;         // 16-tile vectors per column
   const int units = C * Q;
   const int EW = (E + kWave - 1) / kWave;  // 64-expert words
   const bool sorted_by_id = DEDUP || place == nullptr;  // (rank, id) order == id order
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);
 
-  // 0. stage the tile counts (16-byte vectors, all loads before any LDS store)
-  if (STAGED) {
-    const int nvec = (B * C + 15) / 16;
-    const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);
-    for (int v0 = 0; v0 < nvec; v0 += 4 * kScanThreads) {
-      u32x4 tmp[4];
+  // 1. chunk sums (the loads go out first, before anything else)
+  u32x4 keep[KEEP ? kKeep : 1];
+  int kv0 = 0, kv1 = 0;
+  if (KEEP) {
+    if (tid < units) {
+      const int c = tid / Q, q = tid - (tid / Q) * Q;
+      kv0 = int(int64_t(nvec) * q / Q);
+      kv1 = int(int64_t(nvec) * (q + 1) / Q);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int v = v0 + u * kScanThreads + tid;
-        tmp[u] = g4[v < nvec ? v : nvec - 1];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int v = v0 + u * kScanThreads + tid;
-        if (v < nvec) s_tc4[v] = tmp[u];
+      for (int i = 0; i < kKeep; ++i) {
+        const int vi = kv0 + i < kv1 ? kv0 + i : kv1 - 1;  // every unit has a vector
+        keep[i] = g4[size_t(c) * nvec + vi];
       }
     }
   }
-  // rank of the experts this thread owns (place is wave-uniform: scalar branch)
-  int my_rank = 0;
+  int my_rank = 0;  // rank of the expert this thread owns (place is wave-uniform)
   if (tid < E) my_rank = place ? clampi(place[tid], 0, R - 1) : tid / m;
   if (tid < MOE_MAX_RANKS) s_rcnt[tid] = 0;
   for (int i = tid; i < MOE_MAX_RANKS * (MOE_MAX_EXPERTS / kWave); i += kScanThreads)
     (&s_rmask[0][0])[i] = 0ull;
-  __syncthreads();
-
-  // 1. chunk sums per (column, chunk); rank membership of each expert
-  for (int u = tid; u < units; u += kScanThreads) {
-    const int c = u % C, q = u / C;
-    const int b0 = int(int64_t(B) * q / Q), b1 = int(int64_t(B) * (q + 1) / Q);
-    int32_t sum = 0;
-#pragma unroll 8
-    for (int b = b0; b < b1; ++b) sum += tc_at<STAGED>(tcnt, s_tc, size_t(b) * C + c);
-    s_part[u] = sum;
+  if (KEEP) {
+    if (tid < units) {
+      int sum = 0;
+#pragma unroll
+      for (int i = 0; i < kKeep; ++i) {
+        keep[i] = keep_bytes(keep[i], kv0 + i < kv1 ? B - 16 * (kv0 + i) : 0);
+        sum += byte_sum(keep[i]);
+      }
+      s_part[tid] = sum;
+    }
+  } else {
+    for (int u = tid; u < units; u += kScanThreads) {
+      const int c = u / Q, q = u - (u / Q) * Q;
+      const int v0 = int(int64_t(nvec) * q / Q), v1 = int(int64_t(nvec) * (q + 1) / Q);
+      int sum = 0;
+      for (int vi = v0; vi < v1; ++vi)
+        sum += byte_sum(keep_bytes(g4[size_t(c) * nvec + vi], B - 16 * vi));
+      s_part[u] = sum;
+    }
   }
+  __syncthreads();
   if (!sorted_by_id && tid < E) {
     atomicOr(reinterpret_cast<unsigned long long*>(&s_rmask[my_rank][tid / kWave]),
              1ull << (tid % kWave));
     atomicAdd(&s_rcnt[my_rank], 1);
   }
-  __syncthreads();
 
-  // 2. chunk prefixes and column totals; start of each rank in the expert order
+  // 2. chunk prefixes and column totals
   for (int u = tid; u < units; u += kScanThreads) {
-    const int c = u % C, q = u / C;
+    const int c = u / Q, q = u - (u / Q) * Q;
+    const int32_t* part = s_part + c * Q;
     int32_t pre = 0;
 #pragma unroll
-    for (int qq = 0; qq < kMaxQ; ++qq) pre += qq < q ? s_part[(qq < Q ? qq : 0) * C + c] : 0;
+    for (int qq = 0; qq < kMaxQ; ++qq) pre += qq < q ? part[qq < Q ? qq : 0] : 0;
     s_pre[u] = pre;
-    if (q == Q - 1) s_tot[c] = pre + s_part[u];
+    if (q == Q - 1) s_tot[c] = pre + part[q];
   }
+  __syncthreads();
+  // start of each rank in the (rank, id) expert order
   if (!sorted_by_id && w == 0) {
     const int v = lane < R ? s_rcnt[lane] : 0;
     const int incl = wave_incl_scan(v);
@@ -258,10 +288,11 @@ plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int E, int R,
 
   // 4. exclusive scan in that order (experts, or ranks in dedup mode)
   const int nscan = DEDUP ? R : E;
+  const int nsw = (nscan + kWave - 1) / kWave;
   int v = 0;
   if (tid < nscan) v = DEDUP ? s_tot[E + tid] : s_sorted[tid];
   int incl = 0;
-  if (w < (nscan + kWave - 1) / kWave) {
+  if (w < nsw) {
     incl = wave_incl_scan(v);
     if (lane == kWave - 1) s_wsum[w] = incl;
   }
@@ -274,7 +305,7 @@ plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int E, int R,
   if (tid == 0) {
     int total = 0;
 #pragma unroll
-    for (int q = 0; q < kScanWaves; ++q) total += q < (nscan + kWave - 1) / kWave ? s_wsum[q] : 0;
+    for (int q = 0; q < kScanWaves; ++q) total += q < nsw ? s_wsum[q] : 0;
     s_ro[R] = total;
     header[0] = total;
   }
@@ -301,15 +332,26 @@ plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int E, int R,
   if (tid < R) rank_counts[tid] = s_ro[tid + 1] - s_ro[tid];
   if (tid <= R) rank_offsets[tid] = s_ro[tid];
 
-  // 6. absolute first row of every (tile, position column)
-  for (int u = tid; u < CP * Q; u += kScanThreads) {
-    const int cp = u % CP, q = u / CP;
-    const int c = cbase + cp;
-    const int b0 = int(int64_t(B) * q / Q), b1 = int(int64_t(B) * (q + 1) / Q);
-    int32_t run = s_colbase[cp] + s_pre[q * C + c];
-    for (int b = b0; b < b1; ++b) {
-      base[size_t(b) * CP + cp] = run;
-      run += tc_at<STAGED>(tcnt, s_tc, size_t(b) * C + c);
+  // 6. absolute first row of every (position column, tile)
+  if (KEEP) {
+    if (tid < units && tid >= cbase * Q) {
+      const int c = tid / Q;
+      const int cp = c - cbase;
+      int32_t run = s_colbase[cp] + s_pre[tid];
+      int32_t* col = base + size_t(cp) * Bp;
+#pragma unroll
+      for (int i = 0; i < kKeep; ++i)
+        if (kv0 + i < kv1) put_bases(keep[i], run, col + 16 * (kv0 + i));
+    }
+  } else {
+    for (int u = cbase * Q + tid; u < units; u += kScanThreads) {
+      const int c = u / Q, q = u - (u / Q) * Q;
+      const int cp = c - cbase;
+      const int v0 = int(int64_t(nvec) * q / Q), v1 = int(int64_t(nvec) * (q + 1) / Q);
+      int32_t run = s_colbase[cp] + s_pre[u];
+      int32_t* col = base + size_t(cp) * Bp;
+      for (int vi = v0; vi < v1; ++vi)
+        put_bases(keep_bytes(g4[size_t(c) * nvec + vi], B - 16 * vi), run, col + 16 * vi);
     }
   }
 }
@@ -331,26 +373,32 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
     const uint32_t kmul = kdiv_mul(k);
     if (dedup)
       hipLaunchKernelGGL((tile_counts_kernel<true, KMAX>), dim3(unsigned(pl.tiles)), dim3(kWave),
-                         lds, stream, idx, T, E, k, R, place, m, kmul, tcnt, lslot);
+                         lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad, tcnt,
+                         lslot);
     else
       hipLaunchKernelGGL((tile_counts_kernel<false, KMAX>), dim3(unsigned(pl.tiles)),
-                         dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, tcnt, lslot);
+                         dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
+                         tcnt, lslot);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   const int B = int(pl.tiles);
-  const size_t staged = size_t(B) * pl.cols;
-  const bool fits = staged <= size_t(kScanMaxStaged);
-  const size_t lds = fits ? ((staged + 15) / 16) * 16 : 0;
-#define MOE_SCAN_LAUNCH(D, S)                                                                   \
-  hipLaunchKernelGGL((plan_scan_kernel<D, S>), dim3(1), dim3(kScanThreads), lds, stream, tcnt, B, \
-                     E, R, place, m, expert_counts, rank_counts, rank_offsets, expert_offsets,    \
-                     header, base)
+  const int Bp = int(pl.tiles_pad);
+  const int nvec = Bp / 16;
+  int Q = kScanThreads / pl.cols;
+  Q = Q < 1 ? 1 : (Q > kMaxQ ? kMaxQ : Q);
+  Q = Q < nvec ? Q : (nvec > 0 ? nvec : 1);
+  // one unit per thread, each of at most kKeep vectors
+  const bool keep = nvec > 0 && pl.cols * Q <= kScanThreads && (nvec + Q - 1) / Q <= kKeep;
+#define MOE_SCAN_LAUNCH(D, K)                                                                   \
+  hipLaunchKernelGGL((plan_scan_kernel<D, K>), dim3(1), dim3(kScanThreads), 0, stream, tcnt, B,  \
+                     Bp, Q, E, R, place, m, expert_counts, rank_counts, rank_offsets,            \
+                     expert_offsets, header, base)
   if (dedup) {
-    if (fits) MOE_SCAN_LAUNCH(true, true);
+    if (keep) MOE_SCAN_LAUNCH(true, true);
     else MOE_SCAN_LAUNCH(true, false);
   } else {
-    if (fits) MOE_SCAN_LAUNCH(false, true);
+    if (keep) MOE_SCAN_LAUNCH(false, true);
     else MOE_SCAN_LAUNCH(false, false);
   }
 #undef MOE_SCAN_LAUNCH

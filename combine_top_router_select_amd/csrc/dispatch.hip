@@ -10,7 +10,7 @@
 // conventional dispatcher.
 //
 // Design: one wave per (token, row chunk).  Lanes j < k first resolve slot j's
-// destination row from the plan (base[tile][column] + the slot's rank inside
+// destination row from the plan (base[column][tile] + the slot's rank inside
 // the tile), then the wave
 // reads its chunk of x[t] once into registers (16-byte loads, 1 KiB per wave
 // instruction) and writes it to each destination row.  Every access is a full,
@@ -54,8 +54,8 @@ template <int NV, bool NT>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
                 const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k, int cpr,
-                const int32_t* __restrict__ base, const uint32_t* __restrict__ lslot, int stride,
-                int col_off, uint8_t* __restrict__ send, int32_t* __restrict__ row_token,
+                const int32_t* __restrict__ base, const uint32_t* __restrict__ lslot, int64_t Bp,
+                uint8_t* __restrict__ send, int32_t* __restrict__ row_token,
                 int32_t* __restrict__ row_expert, float* __restrict__ row_weight,
                 int32_t* __restrict__ slot_row) {
   const int lane = lane_id();
@@ -71,7 +71,7 @@ dispatch_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
   u32x4 v[NV];
   load_chunk<NV>(v, x + t * row_bytes, chunk0, row_bytes, lane);
   const int e = int(code >> 8);
-  const int pos = base[(t / kTile) * stride + col_off + e] + int(code & 255u);
+  const int pos = base[e * Bp + t / kTile] + int(code & 255u);
   for (int j = 0; j < k; ++j) {
     const int p = bcast(pos, j);
     store_chunk<NV, NT>(v, send + int64_t(p) * row_bytes + chunk0, chunk0, row_bytes, lane);
@@ -92,7 +92,7 @@ dispatch_dedup_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__
                       const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k,
                       int R, const int32_t* __restrict__ place, int m, int cpr,
                       const int32_t* __restrict__ base, const uint32_t* __restrict__ lslot,
-                      int stride, int col_off, const int32_t* __restrict__ header, uint8_t* __restrict__ send,
+                      int64_t Bp, const int32_t* __restrict__ header, uint8_t* __restrict__ send,
                       int32_t* __restrict__ row_token, int32_t* __restrict__ row_experts,
                       float* __restrict__ row_gates, float* __restrict__ row_weight,
                       int32_t* __restrict__ slot_row, int32_t* __restrict__ n_rows) {
@@ -110,7 +110,7 @@ dispatch_dedup_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__
   u32x4 v[NV];
   load_chunk<NV>(v, x + t * row_bytes, chunk0, row_bytes, lane);
   const int r_own = int(code >> 8);
-  const int pos = base[(t / kTile) * stride + col_off + r_own] + int(code & 255u);
+  const int pos = base[r_own * Bp + t / kTile] + int(code & 255u);
   const int r = lane < k ? r_own : -1;  // lanes >= k match no slot below
   // Per slot: is it the first slot of its rank (the row's leader)?  Its column
   // among the rank's experts (ascending id), the rank's slot count, and its
@@ -194,12 +194,12 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
     if (T == 0) return hipSuccess;
     hipLaunchKernelGGL((dispatch_kernel<NV, NT>), dim3(unsigned(blocks)), dim3(256), 0, stream,
                        static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, cpr, base,
-                       lslot, pl.pos_cols, 0, static_cast<uint8_t*>(send), row_token, row_e,
+                       lslot, pl.tiles_pad, static_cast<uint8_t*>(send), row_token, row_e,
                        row_weight, slot_row);
   } else {
     hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT>), dim3(unsigned(blocks)), dim3(256), 0,
                        stream, static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, R,
-                       place, E / R, cpr, base, lslot, pl.pos_cols, 0, header,
+                       place, E / R, cpr, base, lslot, pl.tiles_pad, header,
                        static_cast<uint8_t*>(send), row_token, row_e, row_gates, row_weight,
                        slot_row, n_rows);
   }
