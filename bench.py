@@ -108,7 +108,6 @@ class BufferSet:
             self.disp["row_expert"] = torch.empty(N, dtype=i32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.W = torch.zeros((E, E), dtype=i32, device=dev)
-        self.cws = ops.coselect_workspace(w.coselect_tokens, E, dev)
         self.ev_routed = torch.cuda.Event()
         self.ev_coselected = torch.cuda.Event()
 
@@ -122,35 +121,26 @@ class BufferSet:
         return tot
 
 
-def gpu_step(torch, ops, b, w, dedup, side=None, ev=None):
+def gpu_step(torch, ops, b, w, dedup, side=None):
     """One pass of the hot path.  With a side stream, the co-selection counts run
-    there, after the routing and concurrently with the rest.  ev = (e0, e1, e2,
-    e3) events bracketing the dispatch and the combine kernels, recorded on the
-    stream they run on."""
+    there, after the routing and concurrently with the rest."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
     main = torch.cuda.current_stream()
     ops.moe_route_topk(b.logits, k, b.idx, b.gate)
     if side is not None:
         b.ev_routed.record(main)
         side.wait_event(b.ev_routed)
-        ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W, ws=b.cws,
+        ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W,
                                 stream=side)
         b.ev_coselected.record(side)
     c = ops.moe_send_counts(b.idx, E, R, b.place, dedup, ws=b.ws, out=b.cnt)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-    if ev:
-        ev[0].record()
     d = f(b.x, b.idx, b.gate, E, R, c["ws"], b.place, out=b.disp)
-    if ev:
-        ev[1].record()
-        ev[2].record()
     ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b.out)
-    if ev:
-        ev[3].record()
     if side is not None:
         main.wait_event(b.ev_coselected)
     else:
-        ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W, ws=b.cws)
+        ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W)
 
 
 def cpu_baseline(inp, w, dedup, seconds):
@@ -221,11 +211,11 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    def step(i):
         if graphs is not None:
             graphs[i % nsets].replay()
         else:
-            gpu_step(torch, ops, sets[i % nsets], w, dedup, side, ev)
+            gpu_step(torch, ops, sets[i % nsets], w, dedup, side)
 
     for i in range(a.warmup):
         step(i)
@@ -238,15 +228,47 @@ def main():
     t1 = time.perf_counter()
     elapsed = t1 - t0
 
-    # per-kernel durations with HIP events on the stream the kernels run on
-    # (eager launches of the same step, same rotation)
+    # Per-kernel mean durations with HIP events on the stream the kernels run
+    # on: each event pair brackets a run of back-to-back launches of that one
+    # kernel over the rotated buffer sets (each set holds the plan and the send
+    # buffer of its last step), so neither event overhead nor other kernels
+    # enter the figure.
     K2 = min(a.steps, 100)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K2)]
-    for i in range(K2):
-        gpu_step(torch, ops, sets[(a.warmup + a.steps + i) % nsets], w, dedup, side, evs[i])
+    order = [sets[(a.warmup + a.steps + i) % nsets] for i in range(K2)]
+    L, st = ops.lib(), torch.cuda.current_stream().cuda_stream
+    disp_calls, comb_calls = [], []
+    for b in order:
+        d = b.disp
+        if dedup:
+            disp_calls.append((L.moe_dispatch_permute_dedup, (
+                b.x.data_ptr(), b.idx.data_ptr(), b.gate.data_ptr(), T, H, E, k, R,
+                b.place.data_ptr() if b.place is not None else None, 2, b.ws.data_ptr(),
+                b.ws.numel(), d["send"].data_ptr(), d["row_token"].data_ptr(),
+                d["row_experts"].data_ptr(), d["row_gates"].data_ptr(),
+                d["row_weight"].data_ptr(), d["slot_row"].data_ptr(), d["n_rows"].data_ptr(), st)))
+        else:
+            disp_calls.append((L.moe_dispatch_permute, (
+                b.x.data_ptr(), b.idx.data_ptr(), b.gate.data_ptr(), T, H, E, k, R,
+                b.place.data_ptr() if b.place is not None else None, 2, b.ws.data_ptr(),
+                b.ws.numel(), d["send"].data_ptr(), d["row_token"].data_ptr(),
+                d["row_expert"].data_ptr(), d["row_weight"].data_ptr(),
+                d["slot_row"].data_ptr(), st)))
+        comb_calls.append((L.moe_combine, (
+            d["send"].data_ptr(), d["row_weight"].data_ptr(), d["slot_row"].data_ptr(), T, H, k,
+            2, b.out.data_ptr(), st)))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for calls, e0, e1 in ((disp_calls, ev[0], ev[1]), (comb_calls, ev[2], ev[3])):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)  # the GPU waits while the launches queue up
+        e0.record()
+        for fn, args in calls:
+            rc = fn(*args)
+            if rc != 0:
+                raise ops.MoeError(rc, fn.__name__)
+        e1.record()
     torch.cuda.synchronize()
-    t_disp = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
-    t_comb = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e-3
+    t_disp = ev[0].elapsed_time(ev[1]) * 1e-3 / K2
+    t_comb = ev[2].elapsed_time(ev[3]) * 1e-3 / K2
 
     # rows actually written (N, or D for dedup)
     b = sets[0]

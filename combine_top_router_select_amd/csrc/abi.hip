@@ -17,8 +17,7 @@ hipError_t launch_dispatch(const void*, const int32_t*, const float*, int64_t, i
                            float*, float*, int32_t*, int32_t*, hipStream_t);
 hipError_t launch_combine(const void*, const float*, const int32_t*, int64_t, int, int, void*,
                           hipStream_t);
-hipError_t launch_coselect(const int32_t*, int64_t, int, int, int32_t*, void*, hipStream_t);
-size_t coselect_workspace(int64_t, int);
+hipError_t launch_coselect(const int32_t*, int64_t, int, int, int32_t*, hipStream_t);
 }  // namespace moe
 
 namespace {
@@ -163,19 +162,12 @@ MOE_API int moe_combine(const void* rows, const float* row_weight, const int32_t
                                         as_stream(stream)));
 }
 
-MOE_API size_t moe_coselect_workspace_bytes(int64_t tokens, int n_experts) {
-  if (check_tek(tokens, n_experts, 1) != MOE_OK) return 0;
-  return moe::coselect_workspace(tokens, n_experts);
-}
-
 MOE_API int moe_coselect_counts(const int32_t* topk_idx, int64_t tokens, int n_experts,
-                                int top_k, int32_t* coselect, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                int top_k, int32_t* coselect, void* stream) {
   int st = check_tek(tokens, n_experts, top_k);
   if (st != MOE_OK) return st;
   if (tokens == 0) return MOE_OK;
-  if (!topk_idx || !coselect || !workspace) return MOE_EINVAL;
-  if (workspace_bytes < moe_coselect_workspace_bytes(tokens, n_experts)) return MOE_EWORKSPACE;
-  return hip_status(moe::launch_coselect(topk_idx, tokens, n_experts, top_k, coselect, workspace,
+  if (!topk_idx || !coselect) return MOE_EINVAL;
+  return hip_status(moe::launch_coselect(topk_idx, tokens, n_experts, top_k, coselect,
                                          as_stream(stream)));
 }

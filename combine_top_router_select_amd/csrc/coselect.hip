@@ -8,17 +8,23 @@
 // change any placement objective).
 //
 // Design: with S_e the set of tokens that select e, W[a][b] = |S_a & S_b|.
-//  1. coselect_bits: one wave per 64-token word.  Lane l takes the word's top-k
-//     ids at flat positions l, l + 64, ... (coalesced loads), sets the token's
-//     bit in its expert's LDS bitset word (ds_or_b64, order independent) and the
-//     wave writes the E words to S[E][words] in the workspace.  Spread over
-//     many CUs, so no CU streams all the ids.
-//  2. coselect_pairs: one 1024-thread workgroup per 16 x 16 tile of W in the
-//     upper triangle.  It stages its 32 experts' bitset rows in LDS (16 KiB per
-//     4096 tokens), sums popcount(S_a & S_b) for each cell with four threads per
-//     cell, and adds the total to the cell and its mirror.  Each cell belongs to
-//     exactly one thread: no atomics touch global memory and the counts are
-//     exact integers, so the output is deterministic.
+// One kernel.  A workgroup of 1024 threads takes one 16 x 16 tile of W in the
+// upper triangle and one slice of the tokens, in rounds of 1024 tokens:
+//  1. the round's top-k ids are loaded coalesced (all loads issued before any
+//     use) and turned into row codes of the tile's (up to) 32 experts, staged
+//     in LDS as bytes;
+//  2. one wave per 64-token word, one lane per token: the lane ORs its slots'
+//     row bits into a 32-bit mask, and a 5-stage bit-matrix transpose across
+//     lanes (ds_swizzle exchanges) turns the 64 masks into the 32 experts'
+//     64-bit token bitsets.  No LDS atomics (measured: ds_or_b64 with many
+//     lanes is several times slower than this);
+//  3. popcount(S_a & S_b) over the round's 16 words for each cell, four
+//     threads per cell.
+// The cell's owner adds the slice's count to the cell and its mirror with an
+// integer atomic add: integer sums are exact in any order, so the result is
+// deterministic.  Slicing the tokens puts several workgroups on each tile (the
+// E = 64 case has only 10 tiles); there is no intermediate buffer in global
+// memory.
 #include "common.hpp"
 
 namespace moe {
@@ -27,50 +33,35 @@ constexpr int kCsT = 16;                             // experts per tile side
 constexpr int kCsThreads = 1024;
 constexpr int kCsCells = kCsT * kCsT;                // 256
 constexpr int kCsParts = kCsThreads / kCsCells;      // 4 partial sums per cell
-constexpr int kCsWords = 64;                         // bitset words staged per round
-constexpr int kCsWordsPerPart = kCsWords / kCsParts; // 16
+constexpr int kCsWords = kCsThreads / kWave;         // 16 words of 64 tokens per round
+constexpr int kCsRound = kCsWords * 64;              // 1024 tokens per round
+constexpr int kCsStride = kCsWords + 1;              // padded LDS row: rows start in different banks
+constexpr int kCsWordsPerPart = kCsWords / kCsParts; // 4
+constexpr int kCsTargetBlocks = 256;
+constexpr uint8_t kCsNoRow = 0xFF;
 
-__host__ __device__ inline int64_t cs_words(int64_t n) { return (n + kWave - 1) / kWave; }
-
-template <int KMAX>
-__global__ void __launch_bounds__(kWave)
-coselect_bits_kernel(const int32_t* __restrict__ idx, int64_t n, int E, int k, uint32_t kmul,
-                     uint64_t* __restrict__ S, int64_t nw) {
-  extern __shared__ uint64_t s_word[];  // [E]
-  const int lane = lane_id();
-  const int64_t wd = blockIdx.x;
-  const int64_t f0 = wd * kWave * k;
-  const int64_t total = n * k;
-  const int nf = int(total - f0 < int64_t(kWave) * k ? total - f0 : int64_t(kWave) * k);
-  int raw[KMAX];
-#pragma unroll
-  for (int r = 0; r < KMAX; ++r) {
-    const int64_t f = f0 + lane + kWave * r;
-    raw[r] = idx[f < total ? f : total - 1];
-  }
-  for (int e = lane; e < E; e += kWave) s_word[e] = 0ull;
-  wave_lds_sync();
-#pragma unroll
-  for (int r = 0; r < KMAX; ++r) {
-    const int f = lane + kWave * r;
-    if (f < nf) {
-      const int t = k == 1 ? f : int(__umulhi(uint32_t(f), kmul));  // token inside the word
-      atomicOr(reinterpret_cast<unsigned long long*>(&s_word[clampi(raw[r], 0, E - 1)]),
-               1ull << t);
-    }
-  }
-  wave_lds_sync();
-  for (int e = lane; e < E; e += kWave) S[int64_t(e) * nw + wd] = s_word[e];
+// One stage of the lane transpose of a 32 x 32 bit matrix (lane l holds row
+// l; afterwards lane c holds column c): lanes l and l ^ J swap the
+// off-diagonal J x J blocks of their 2J x 2J block.  ds_swizzle in bit-mask
+// mode reads lane l ^ J inside each 32-lane half.
+template <int J, uint32_t MASK>
+__device__ __forceinline__ uint32_t transpose_stage(uint32_t x, int lane) {
+  const uint32_t xp = uint32_t(__builtin_amdgcn_ds_swizzle(int(x), (J << 10) | 0x1F));
+  const bool up = (lane & J) != 0;
+  const uint32_t t = ((up ? xp : x) ^ ((up ? x : xp) << J)) & MASK;
+  return x ^ (up ? (t >> J) : t);
 }
 
+template <int KMAX>
 __global__ void __launch_bounds__(kCsThreads)
-coselect_pairs_kernel(const uint64_t* __restrict__ S, int64_t nw, int E,
-                      int32_t* __restrict__ W) {
-  __shared__ u32x4 s_rows4[kCsT * kCsWords];  // [32 experts][64 words] as 16-byte pairs, 16 KiB
+coselect_kernel(const int32_t* __restrict__ idx, int64_t n, int E, int k, int n_slices,
+                int64_t slice_tokens, int32_t* __restrict__ W) {
+  __shared__ uint8_t s_rows[kCsRound * KMAX];  // row code per id of the round
+  __shared__ uint64_t s_bits[2 * kCsT * kCsStride];    // [32 experts][17 words]
   __shared__ uint32_t s_red[kCsParts][kCsCells];
-  const uint64_t* s_rows = reinterpret_cast<const uint64_t*>(s_rows4);
   const int nt = (E + kCsT - 1) / kCsT;
-  int p = blockIdx.x, ta = 0;
+  const int slice = int(blockIdx.x % unsigned(n_slices));
+  int p = int(blockIdx.x / unsigned(n_slices)), ta = 0;
   while (p >= nt - ta) {
     p -= nt - ta;
     ++ta;
@@ -79,30 +70,57 @@ coselect_pairs_kernel(const uint64_t* __restrict__ S, int64_t nw, int E,
   const bool diag = ta == tb;
   const int a0 = ta * kCsT, b0 = tb * kCsT;
   const int tid = threadIdx.x;
+  const int lane = lane_id(), wv = tid / kWave;
   const int cell = tid % kCsCells, part = tid / kCsCells;
   const int i = cell / kCsT, j = cell % kCsT;
-  // staging: thread tid moves words 2 spair, 2 spair + 1 of staged row srow
-  const int srow = tid / (kCsWords / 2), spair = tid % (kCsWords / 2);
-  const int sexp = srow < kCsT ? a0 + srow : b0 + (srow - kCsT);
-  const bool svalid = sexp < E;
-  const int64_t row = int64_t(svalid ? sexp : 0) * nw;
-  const uint64_t* ra = s_rows + i * kCsWords;
-  const uint64_t* rb = s_rows + (diag ? j : kCsT + j) * kCsWords;
+  const int ca = a0 + i, cb = b0 + j;
+  const uint64_t* ra = s_bits + i * kCsStride;
+  const uint64_t* rb = s_bits + (diag ? j : kCsT + j) * kCsStride;
+  const int64_t s0 = int64_t(slice) * slice_tokens;
+  const int64_t s1 = s0 + slice_tokens < n ? s0 + slice_tokens : n;
   uint32_t acc = 0;
-  for (int64_t w0 = 0; w0 < nw; w0 += kCsWords) {
-    const int64_t wa = w0 + 2 * spair;  // words past the end or of experts >= E count as 0
-    const uint64_t x0 = S[row + (wa < nw ? wa : nw - 1)];
-    const uint64_t x1 = S[row + (wa + 1 < nw ? wa + 1 : nw - 1)];
-    u32x4 v;
-    v[0] = uint32_t(x0);
-    v[1] = uint32_t(x0 >> 32);
-    v[2] = uint32_t(x1);
-    v[3] = uint32_t(x1 >> 32);
-    if (!svalid || wa >= nw) v[0] = v[1] = 0u;
-    if (!svalid || wa + 1 >= nw) v[2] = v[3] = 0u;
-    __syncthreads();  // the previous round's popcounts are done
-    s_rows4[tid] = v;
+  for (int64_t t0 = s0; t0 < s1; t0 += kCsRound) {
+    const int32_t* ids = idx + t0 * k;  // this round's ids, flat
+    const int ntok = int(s1 - t0 < kCsRound ? s1 - t0 : kCsRound);
+    const int nf = ntok * k;            // at most 1024 * k: at most KMAX ids per thread
+    // 1. loads first (32-bit offsets clamped into the round, no branch)
+    int raw[KMAX];
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      uint32_t f = uint32_t(tid + kCsThreads * r);
+      f = f < uint32_t(nf) ? f : uint32_t(nf - 1);
+      raw[r] = ids[f];
+    }
+    __syncthreads();  // the previous round is done with s_rows and s_bits
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      const int f = tid + kCsThreads * r;
+      const int e = raw[r];
+      uint8_t row = kCsNoRow;
+      if (e >= a0 && e < a0 + kCsT) row = uint8_t(e - a0);
+      else if (!diag && e >= b0 && e < b0 + kCsT) row = uint8_t(kCsT + (e - b0));
+      if (f < nf) s_rows[f] = row;
+    }
     __syncthreads();
+    // 2. the token of this lane: its experts' row bits, then the transpose
+    const int tok = wv * kWave + lane;
+    uint32_t m = 0;
+    if (tok < ntok) {
+      for (int q = 0; q < k; ++q) {
+        const uint32_t row = s_rows[tok * k + q];
+        m |= row < 32u ? (1u << row) : 0u;
+      }
+    }
+    m = transpose_stage<16, 0xFFFF0000u>(m, lane);
+    m = transpose_stage<8, 0xFF00FF00u>(m, lane);
+    m = transpose_stage<4, 0xF0F0F0F0u>(m, lane);
+    m = transpose_stage<2, 0xCCCCCCCCu>(m, lane);
+    m = transpose_stage<1, 0xAAAAAAAAu>(m, lane);
+    // lane c < 32: tokens 0..31 of row c; lane 32 + c: tokens 32..63
+    const uint32_t hi = uint32_t(__shfl_xor(int(m), 32));
+    if (lane < 2 * kCsT) s_bits[lane * kCsStride + wv] = (uint64_t(hi) << 32) | m;
+    __syncthreads();
+    // 3. popcounts
 #pragma unroll
     for (int q = 0; q < kCsWordsPerPart; ++q) {
       const int wq = part * kCsWordsPerPart + q;
@@ -111,45 +129,43 @@ coselect_pairs_kernel(const uint64_t* __restrict__ S, int64_t nw, int E,
   }
   s_red[part][cell] = acc;
   __syncthreads();
-  if (tid < kCsCells) {
-    const int a = a0 + i, b = b0 + j;
-    if (a < E && b < E) {
-      uint32_t tot = 0;
+  if (part == 0 && ca < E && cb < E) {
+    uint32_t tot = 0;
 #pragma unroll
-      for (int q = 0; q < kCsParts; ++q) tot += s_red[q][cell];
-      W[int64_t(a) * E + b] += int32_t(tot);
-      if (!diag) W[int64_t(b) * E + a] += int32_t(tot);
+    for (int q = 0; q < kCsParts; ++q) tot += s_red[q][cell];
+    if (tot != 0) {
+      atomicAdd(&W[int64_t(ca) * E + cb], int32_t(tot));
+      if (!diag) atomicAdd(&W[int64_t(cb) * E + ca], int32_t(tot));
     }
   }
 }
 
-size_t coselect_workspace(int64_t n, int E) {
-  return align256(size_t(E) * size_t(cs_words(n)) * sizeof(uint64_t));
-}
-
-template <int KMAX>
-static hipError_t launch_coselect_k(const int32_t* idx, int64_t n, int E, int k, int32_t* W,
-                                    void* workspace, hipStream_t stream) {
-  const int64_t nw = cs_words(n);
-  const uint32_t kmul = k <= 1 ? 0u : uint32_t(((1ull << 32) + uint64_t(k) - 1) / uint64_t(k));
-  uint64_t* S = static_cast<uint64_t*>(workspace);
-  hipLaunchKernelGGL((coselect_bits_kernel<KMAX>), dim3(unsigned(nw)), dim3(kWave),
-                     size_t(E) * sizeof(uint64_t), stream, idx, n, E, k, kmul, S, nw);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int nt = (E + kCsT - 1) / kCsT;
-  hipLaunchKernelGGL(coselect_pairs_kernel, dim3(nt * (nt + 1) / 2), dim3(kCsThreads), 0, stream,
-                     S, nw, E, W);
-  return hipGetLastError();
-}
-
 hipError_t launch_coselect(const int32_t* idx, int64_t n, int E, int k, int32_t* W,
-                           void* workspace, hipStream_t stream) {
+                           hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  if (k <= 2) return launch_coselect_k<2>(idx, n, E, k, W, workspace, stream);
-  if (k <= 4) return launch_coselect_k<4>(idx, n, E, k, W, workspace, stream);
-  if (k <= 8) return launch_coselect_k<8>(idx, n, E, k, W, workspace, stream);
-  return launch_coselect_k<16>(idx, n, E, k, W, workspace, stream);
+  const int nt = (E + kCsT - 1) / kCsT;
+  const int tiles = nt * (nt + 1) / 2;
+  // slices of whole rounds, enough of them to put about kCsTargetBlocks
+  // workgroups in flight
+  const int64_t rounds = (n + kCsRound - 1) / kCsRound;
+  int64_t ns = (kCsTargetBlocks + tiles - 1) / tiles;
+  ns = ns < rounds ? ns : rounds;
+  const int64_t per = (rounds + ns - 1) / ns;  // rounds per slice
+  ns = (rounds + per - 1) / per;               // no empty slice
+  const dim3 grid(unsigned(tiles * ns));
+  if (k <= 2)
+    hipLaunchKernelGGL((coselect_kernel<2>), grid, dim3(kCsThreads), 0, stream, idx, n, E, k,
+                       int(ns), per * kCsRound, W);
+  else if (k <= 4)
+    hipLaunchKernelGGL((coselect_kernel<4>), grid, dim3(kCsThreads), 0, stream, idx, n, E, k,
+                       int(ns), per * kCsRound, W);
+  else if (k <= 8)
+    hipLaunchKernelGGL((coselect_kernel<8>), grid, dim3(kCsThreads), 0, stream, idx, n, E, k,
+                       int(ns), per * kCsRound, W);
+  else
+    hipLaunchKernelGGL((coselect_kernel<16>), grid, dim3(kCsThreads), 0, stream, idx, n, E, k,
+                       int(ns), per * kCsRound, W);
+  return hipGetLastError();
 }
 
 }  // namespace moe

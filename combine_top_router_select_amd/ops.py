@@ -15,8 +15,7 @@ from ._lib import MoeError, check, lib, status_string  # noqa: F401
 
 __all__ = ["MoeError", "moe_status_string", "moe_workspace_bytes", "moe_route_topk",
            "moe_send_counts", "moe_dispatch_permute", "moe_dispatch_permute_dedup",
-           "moe_combine", "moe_coselect_workspace_bytes", "moe_coselect_counts", "workspace",
-           "coselect_workspace"]
+           "moe_combine", "moe_coselect_counts", "workspace"]
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -190,18 +189,7 @@ def moe_combine(rows, row_weight, slot_row, out=None, stream=None):
     return out
 
 
-def moe_coselect_workspace_bytes(tokens: int, n_experts: int) -> int:
-    return int(lib().moe_coselect_workspace_bytes(tokens, n_experts))
-
-
-def coselect_workspace(tokens, n_experts, device) -> torch.Tensor:
-    n = moe_coselect_workspace_bytes(tokens, n_experts)
-    if n == 0:
-        raise MoeError(1, "moe_coselect_workspace_bytes")
-    return torch.empty(n, dtype=torch.uint8, device=device)
-
-
-def moe_coselect_counts(topk_idx, n_experts, tokens=None, coselect=None, ws=None, stream=None):
+def moe_coselect_counts(topk_idx, n_experts, tokens=None, coselect=None, stream=None):
     _dev(topk_idx, "topk_idx", torch.int32, 2)
     T, k = topk_idx.shape
     n = T if tokens is None else min(int(tokens), T)
@@ -211,8 +199,6 @@ def moe_coselect_counts(topk_idx, n_experts, tokens=None, coselect=None, ws=None
     _dev(coselect, "coselect", torch.int32, 2)
     if n == 0:
         return coselect
-    if ws is None:
-        ws = coselect_workspace(n, n_experts, topk_idx.device)
-    check(lib().moe_coselect_counts(_ptr(topk_idx), n, n_experts, k, _ptr(coselect), _ptr(ws),
-                                    ws.numel(), _stream(stream)), "moe_coselect_counts")
+    check(lib().moe_coselect_counts(_ptr(topk_idx), n, n_experts, k, _ptr(coselect),
+                                    _stream(stream)), "moe_coselect_counts")
     return coselect

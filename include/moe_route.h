@@ -193,11 +193,6 @@ int moe_combine(const void* rows, const float* row_weight, const int32_t* slot_r
                 int64_t tokens, int hidden_dim, int top_k, int bytes_per_element,
                 void* out, void* stream);
 
-/* Host.  Bytes of workspace moe_coselect_counts() needs for `tokens` tokens:
- * one bitset of the tokens selecting each expert, 8 * n_experts *
- * ceil(tokens / 64) bytes rounded up to 256.  Returns 0 outside the limits. */
-size_t moe_coselect_workspace_bytes(int64_t tokens, int n_experts);
-
 /* A6 - expert co-selection counts ([EC] "Method 1": the correlation graph
  * counts the tokens that select both experts; "Correlation Formation and
  * Stability": about 4096 tokens suffice to fit it).
@@ -207,14 +202,9 @@ size_t moe_coselect_workspace_bytes(int64_t tokens, int n_experts);
  *                +1 at [a][a] for each selected expert.  Zero it before the
  *                first call.  Calls that accumulate into the same matrix must
  *                not run concurrently.
- *   workspace    device scratch of at least moe_coselect_workspace_bytes(tokens,
- *                n_experts) bytes, 16-byte aligned; its contents on entry do
- *                not matter and on return are unspecified.
- * Errors: MOE_EINVAL (null pointers, bad sizes), MOE_EUNSUPPORTED,
- *         MOE_EWORKSPACE. */
+ * Errors: MOE_EINVAL (null pointers, bad sizes), MOE_EUNSUPPORTED. */
 int moe_coselect_counts(const int32_t* topk_idx, int64_t tokens, int n_experts, int top_k,
-                        int32_t* coselect, void* workspace, size_t workspace_bytes,
-                        void* stream);
+                        int32_t* coselect, void* stream);
 
 #ifdef __cplusplus
 }

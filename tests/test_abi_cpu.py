@@ -144,15 +144,12 @@ def test_combine_and_coselect_errors(lib):
     assert c(FAKE, None, FAKE, 10, 128, 17, 2, FAKE, None) == EUNSUP
     assert c(FAKE, None, FAKE, -5, 128, 2, 2, FAKE, None) == EINVAL
     s = lib.moe_coselect_counts
-    wsb = lib.moe_coselect_workspace_bytes(10, 8)
-    assert wsb >= 8 * 8 and wsb % 256 == 0
-    assert lib.moe_coselect_workspace_bytes(4096, 128) == 128 * 64 * 8
-    assert lib.moe_coselect_workspace_bytes(10, 0) == 0
-    assert s(None, 10, 8, 2, FAKE, FAKE, wsb, None) == EINVAL
-    assert s(FAKE, 10, 8, 9, FAKE, FAKE, wsb, None) == EINVAL
-    assert s(FAKE, 10, 8, 2, None, FAKE, wsb, None) == EINVAL
-    assert s(FAKE, 10, 8, 2, FAKE, None, wsb, None) == EINVAL
-    assert s(FAKE, 10, 8, 2, FAKE, FAKE, wsb - 1, None) == EWS
+    assert s(None, 10, 8, 2, FAKE, None) == EINVAL
+    assert s(FAKE, 10, 8, 9, FAKE, None) == EINVAL                  # k > E
+    assert s(FAKE, 10, 8, 2, None, None) == EINVAL
+    assert s(FAKE, -1, 8, 2, FAKE, None) == EINVAL
+    assert s(FAKE, 10, 2048, 2, FAKE, None) == EUNSUP               # E > 1024
+    assert s(None, 0, 8, 2, None, None) == 0                        # no tokens: no-op
 
 
 def test_product_path_does_not_touch_oracle():

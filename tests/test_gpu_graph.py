@@ -30,8 +30,7 @@ def _buffers(w, dedup, dev):
                   "row_weight": torch.empty(N, dtype=f32, device=dev),
                   "slot_row": torch.empty((T, k), dtype=i32, device=dev)},
          "out": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
-         "W": torch.zeros((E, E), dtype=i32, device=dev),
-         "cws": ops.coselect_workspace(w.coselect_tokens, E, dev)}
+         "W": torch.zeros((E, E), dtype=i32, device=dev)}
     if dedup:
         b["disp"].update(row_experts=torch.empty((N, k), dtype=i32, device=dev),
                          row_gates=torch.empty((N, k), dtype=f32, device=dev),
@@ -49,7 +48,7 @@ def _step(w, dedup, logits, x, place, b):
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
     d = f(x, b["idx"], b["gate"], E, R, c["ws"], place, out=b["disp"])
     ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b["out"])
-    ops.moe_coselect_counts(b["idx"], E, tokens=w.coselect_tokens, coselect=b["W"], ws=b["cws"])
+    ops.moe_coselect_counts(b["idx"], E, tokens=w.coselect_tokens, coselect=b["W"])
 
 
 def _snapshot(b):

@@ -222,7 +222,8 @@ def test_combine_random_rows(oracle_mod, dedup):
 @pytest.mark.parametrize("T,E,k,n", [(4096, 64, 6, 4096), (16384, 128, 6, 4096),
                                      (16384, 128, 2, 16384), (300, 8, 8, 300),
                                      (1000, 256, 8, 1000), (20000, 128, 4, 20000),
-                                     (5, 3, 3, 5)])
+                                     (5, 3, 3, 5), (600, 1024, 16, 600),
+                                     (4100, 64, 16, 4100), (64, 17, 1, 64)])
 def test_coselect_parity(oracle_mod, T, E, k, n):
     say(f"[coselect] T={T} E={E} k={k} n={n}")
     inp = WL.make_custom_inputs(T, 1, E, seed=E + k + n)
