@@ -1,24 +1,31 @@
 """Benchmark of the per-GPU MoE dispatch/combine hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
-                    [--graph] [--no-cpu-baseline] [--calib-copy]
+                    [--graph] [--overlap] [--no-cpu-baseline] [--calib-copy]
 
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input, with inputs resident in HBM: top-k routing -> send counts and
 offsets -> dispatch permute -> combine (identity experts: the combine reads the
 send buffer), and the co-selection counts of the routed tokens.  Everything
 runs on one stream; --overlap forks the co-selection counts (which depend only
-on the routing) onto a second stream and joins them before the step ends.  The workload defaults to 4096 tokens,
-hidden 2048 bf16, 64 experts, top-6, 16 logical ranks, contiguous placement
-(DeepSeek-MoE-16B-shaped), plain (one row per token-expert) dispatch.
+on the routing) onto a second stream and joins them before the step ends.  The
+workload defaults to 4096 tokens, hidden 2048 bf16, 64 experts, top-6, 16
+logical ranks, contiguous placement (DeepSeek-MoE-16B-shaped), plain (one row
+per token-expert) dispatch.
 
 To keep the last-level (Infinity) cache from serving the data, steps rotate
 over enough independent buffer sets to exceed it several times over, so each
 step's inputs and outputs were last touched many hundreds of MB earlier.
 
 Prints one JSON line.  `roofline` reports the dominant kernel's algorithmic HBM
-bytes per launch divided by its mean duration (HIP events on the stream the
-kernels run on); `cpu_baseline` times the CPU oracle on the same workload.
+bytes per launch divided by its mean launch duration, measured with HIP events
+on the stream the kernels run on around a run of back-to-back launches of that
+kernel alone (queued behind a short GPU sleep so that host launch overhead
+stays out); `traffic` is the HBM bytes per launch that rocprofv3's FETCH_SIZE
+and WRITE_SIZE counters measured for that kernel (profiles/hbm_traffic_*.md,
+scaled by a plain-copy calibration), or null when there is no such record for
+the workload or the kernel's sources changed since.  `cpu_baseline` times the
+CPU oracle on the same workload.
 """
 from __future__ import annotations
 
@@ -35,6 +42,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+PKG = os.path.join(ROOT, "combine_top_router_select_amd")
+KERNEL_SOURCES = {"moe_dispatch_permute": "csrc/dispatch.hip",
+                  "moe_dispatch_permute_dedup": "csrc/dispatch.hip",
+                  "moe_combine": "csrc/combine.hip"}
 METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak)"
 
 
@@ -141,6 +152,30 @@ def gpu_step(torch, ops, b, w, dedup, side=None):
         main.wait_event(b.ev_coselected)
     else:
         ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W)
+
+
+def counter_traffic(kernel, workload, mode):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summaries (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy
+    calibration), or None when there is none for this workload or the kernel's
+    sources have changed since the counters were taken."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "csrc/common.hpp", "build.py"):
+        with open(os.path.join(PKG, f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()[:16]
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic_*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                if not line.startswith("traffic "):
+                    continue
+                kv = dict(t.split("=", 1) for t in line.split()[1:])
+                if (kv.get("kernel"), kv.get("workload"), kv.get("dispatch")) == (kernel, workload,
+                                                                                   mode):
+                    return int(kv["bytes"]) if kv.get("sources_sha256") == digest else None
+    return None
 
 
 def cpu_baseline(inp, w, dedup, seconds):
@@ -304,7 +339,9 @@ def main():
                    "buffer_sets": nsets, "footprint_MiB": round(nsets * per_set / 2 ** 20)},
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": counter_traffic(dom[0], w.name, "dedup" if dedup else "nondedup"),
+                     "algorithmic_bytes": dom[2]},
         "dispatch_us": round(t_disp * 1e6, 2),
         "combine_us": round(t_comb * 1e6, 2),
         "dispatch_combine_tokens_per_s": T / (t_disp + t_comb),
