@@ -356,6 +356,111 @@ plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, int E, 
   }
 }
 
+// Inclusive scan inside aligned segments of Q consecutive lanes (Q a power of
+// two <= 16, so a segment never leaves its 16-lane DPP row).
+__device__ __forceinline__ int segment_incl_scan(int v, int Q, int lane) {
+  const int ls = lane & (Q - 1);
+  int t = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += ls >= 1 ? t : 0;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);      // row_shr:2
+  v += (Q > 2 && ls >= 2) ? t : 0;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);      // row_shr:4
+  v += (Q > 4 && ls >= 4) ? t : 0;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);      // row_shr:8
+  v += (Q > 8 && ls >= 8) ? t : 0;
+  return v;
+}
+
+// The common cases in one pass with two barriers: plain mode with contiguous
+// placement (the scan order is the expert id order) and dedup mode (the scan
+// order is the rank order).  One (column, chunk) unit per thread, Q chunks per
+// column (a power of two) on consecutive lanes, each of at most KV vectors; the
+// workgroup has just enough waves for the units.
+// A unit's byte sum is scanned inside its column's lane segment (DPP); the
+// segment's last lane carries the column total into one block-wide scan over
+// all units, whose exclusive value at any unit of a column is the column's
+// first row; each unit then writes its tiles' bases from the vectors it kept.
+template <bool DEDUP, int KV>
+__global__ void __launch_bounds__(kScanThreads)
+plan_scan_fast_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, int E, int R, int m,
+                      int32_t* __restrict__ expert_counts, int32_t* __restrict__ rank_counts,
+                      int32_t* __restrict__ rank_offsets, int32_t* __restrict__ expert_offsets,
+                      int32_t* __restrict__ header, int32_t* __restrict__ base) {
+  __shared__ int32_t s_wsum[kScanWaves];
+  __shared__ int32_t s_ro[MOE_MAX_RANKS + 1];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int C = E + (DEDUP ? R : 0);
+  const int cbase = DEDUP ? E : 0;
+  const int nvec = Bp / 16;
+  const int units = C * Q;
+  const bool active = tid < units;
+  const int c = tid / Q, q = tid & (Q - 1);
+  const int v0 = int(int64_t(nvec) * q / Q), v1 = int(int64_t(nvec) * (q + 1) / Q);
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);
+  u32x4 keep[KV];
+#pragma unroll
+  for (int i = 0; i < KV; ++i) {
+    const int vi = v0 + i < v1 ? v0 + i : v1 - 1;  // every unit has a vector
+    keep[i] = g4[size_t(active ? c : 0) * nvec + vi];
+  }
+  int part = 0;
+#pragma unroll
+  for (int i = 0; i < KV; ++i) {
+    keep[i] = keep_bytes(keep[i], v0 + i < v1 ? B - 16 * (v0 + i) : 0);
+    part += byte_sum(keep[i]);
+  }
+  part = active ? part : 0;
+  const int incl_c = segment_incl_scan(part, Q, lane);
+  const int tot = __shfl(incl_c, (lane & ~(Q - 1)) + Q - 1, kWave);  // column total
+  const int pre = incl_c - part;                                      // earlier chunks
+  const bool pos = active && c >= cbase;
+  const int v = (pos && q == Q - 1) ? tot : 0;
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) s_wsum[w] = incl;
+  __syncthreads();
+  int carry = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kScanWaves; ++i) {
+    const int x = i < nwaves ? s_wsum[i < nwaves ? i : 0] : 0;
+    carry += i < w ? x : 0;
+    total += x;
+  }
+  const int colbase = carry + incl - v;  // first row of this unit's column
+  if (active && q == 0) {
+    if (c < E) expert_counts[c] = tot;
+    if (DEDUP && c >= E) {
+      rank_counts[c - E] = tot;
+      rank_offsets[c - E] = colbase;
+    }
+    if (!DEDUP) {
+      if (expert_offsets) expert_offsets[c] = colbase;
+      if (c % m == 0) s_ro[c / m] = colbase;
+    }
+  }
+  if (tid == 0) {
+    header[0] = total;
+    rank_offsets[R] = total;
+    if (!DEDUP) s_ro[R] = total;
+  }
+  if (pos) {
+    int32_t run = colbase + pre;
+    int32_t* col = base + size_t(c - cbase) * Bp;
+#pragma unroll
+    for (int i = 0; i < KV; ++i)
+      if (v0 + i < v1) put_bases(keep[i], run, col + 16 * (v0 + i));
+  }
+  if (!DEDUP) {
+    __syncthreads();
+    if (tid < R) {
+      rank_offsets[tid] = s_ro[tid];
+      rank_counts[tid] = s_ro[tid + 1] - s_ro[tid];
+    }
+  }
+}
+
 template <int KMAX>
 static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, int R,
                                   const int32_t* place, int dedup, int32_t* expert_counts,
@@ -385,6 +490,33 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
   const int B = int(pl.tiles);
   const int Bp = int(pl.tiles_pad);
   const int nvec = Bp / 16;
+  // fast path: chunks per column a power of two, one unit per thread, at most
+  // kKeep vectors per unit; plain mode only with contiguous placement
+  if (nvec > 0 && (dedup || place == nullptr)) {
+    int Qf = kMaxQ;
+    while (Qf > 1 && (pl.cols * Qf > kScanThreads || Qf > nvec)) Qf >>= 1;
+    const int kv = (nvec + Qf - 1) / Qf;
+    if (pl.cols * Qf <= kScanThreads && kv <= kKeep) {
+      const int threads = (pl.cols * Qf + kWave - 1) / kWave * kWave;
+#define MOE_FAST_SCAN(D, KV)                                                                     \
+  hipLaunchKernelGGL((plan_scan_fast_kernel<D, KV>), dim3(1), dim3(threads), 0, stream, tcnt, B, \
+                     Bp, Qf, E, R, m, expert_counts, rank_counts, rank_offsets, expert_offsets,   \
+                     header, base)
+#define MOE_FAST_SCAN_KV(D)       \
+  if (kv <= 1) MOE_FAST_SCAN(D, 1); \
+  else if (kv <= 2) MOE_FAST_SCAN(D, 2); \
+  else if (kv <= 4) MOE_FAST_SCAN(D, 4); \
+  else MOE_FAST_SCAN(D, 8);
+      if (dedup) {
+        MOE_FAST_SCAN_KV(true)
+      } else {
+        MOE_FAST_SCAN_KV(false)
+      }
+#undef MOE_FAST_SCAN_KV
+#undef MOE_FAST_SCAN
+      return hipGetLastError();
+    }
+  }
   int Q = kScanThreads / pl.cols;
   Q = Q < 1 ? 1 : (Q > kMaxQ ? kMaxQ : Q);
   Q = Q < nvec ? Q : (nvec > 0 ? nvec : 1);
