@@ -11,6 +11,10 @@ available here):
 * DeepSeek-MoE-16B and Qwen3-30B-A3B rows of the DODOCO model table (E, top-k,
   hidden size); 4096 routed tokens per rank, expert parallelism 16 and
   contiguous placement from its "Setup" section.
+* Two further rows of the DODOCO model table as plain shapes: 256 experts,
+  top-8, hidden 2048, and 128 experts, top-6, hidden 2688 (the hybrid
+  Mamba-2 + attention row), with the same 4096 tokens, EP16 and contiguous
+  placement.
 * Zyphra's expert-coupling summary, "Model Configuration" (d_model 4096, 128
   experts, top-2/top-6, sequence length 8192), "Hardware"/"Measured A2A share"
   (EP8, EP32) and "Within-layer correlation" (42% of tokens on 64 pairs, 14
@@ -56,6 +60,10 @@ WORKLOADS: Dict[str, Workload] = {
                                  "contiguous", "pair_bias", ("nondedup", "dedup"), 4096),
     "qwen3_30b_a3b": Workload("qwen3_30b_a3b", 4096, 2048, 128, 8, 16, "contiguous",
                               "zipf", ("nondedup", "dedup"), 4096),
+    "e256_top8_h2048": Workload("e256_top8_h2048", 4096, 2048, 256, 8, 16, "contiguous",
+                                "zipf", ("nondedup", "dedup"), 4096),
+    "e128_top6_h2688": Workload("e128_top6_h2688", 4096, 2688, 128, 6, 16, "contiguous",
+                                "plain", ("nondedup", "dedup"), 4096),
     "zyphra_top2_ep8": Workload("zyphra_top2_ep8", 16384, 4096, 128, 2, 8, "correlated",
                                 "zyphra", ("dedup",), 4096),
     "zyphra_top6_ep32": Workload("zyphra_top6_ep32", 16384, 4096, 128, 6, 32, "correlated",

@@ -95,3 +95,19 @@ def test_zyphra_planted_pairs(oracle_mod, name):
     else:
         # at top-6 every planted token still selects its pair
         assert on_pairs / T >= 0.42
+
+
+def test_dodoco_shaped_workloads_match_the_model_table():
+    """Every 4096-token, EP16, contiguous workload takes (experts, top-k, hidden)
+    from a row of the DODOCO "Models" table (fixture with its citation)."""
+    import os
+    golden = os.path.join(os.path.dirname(__file__), "golden", "dodoco_models.txt")
+    with open(golden) as f:
+        rows = {tuple(int(v) for v in l.split()[1:]) for l in f
+                if l.strip() and not l.startswith("#")}
+    shaped = [w for w in (WL.get(n) for n in WL.ORDER)
+              if w.tokens == 4096 and w.n_ranks == 16]
+    assert len(shaped) == 4
+    for w in shaped:
+        assert (w.n_experts, w.top_k, w.hidden_dim) in rows, w.name
+        assert w.placement == "contiguous"
