@@ -220,6 +220,65 @@ int oracle_dispatch_dedup(const uint8_t* x, const int32_t* idx, const float* gat
     return 0;
 }
 
+/* ---------------------------------------------- receive-side expansion --- */
+
+/* [EC] "Method 1": a deduplicated row carries the ids and routing
+ * probabilities of every selected expert on its destination rank, so the
+ * receiving rank hands the row to each of those experts.  Expansion lays the
+ * received rows out per expert: for every row p < n_rows and every listed
+ * expert e (ids >= 0; -1 is padding), one copy of row p.  Order: rank
+ * ascending, expert id ascending within a rank, row ascending within an
+ * expert (the order of the conventional dispatcher's buffer).
+ * expert_counts[e] = number of rows listing e; rank_counts[r] = the sum over the
+ * experts on r; rank_offsets = its exclusive scan; expert_offsets[e] = start of
+ * e's segment.  Per expanded row q: exp_row[q] = source row, exp_expert[q] =
+ * expert, exp_gate[q] = that expert's gate on the row.  row_slot[p][c] = the
+ * expanded row of (p, listed column c); -1 for padding and for every row
+ * p >= n_rows up to `capacity`. */
+int oracle_expand_dedup(const uint8_t* rows, const int32_t* row_experts,
+                        const float* row_gates, int64_t n_rows, int64_t capacity,
+                        int row_bytes, int n_experts, int top_k, int n_ranks,
+                        const int32_t* place, int32_t* expert_counts, int32_t* rank_counts,
+                        int32_t* rank_offsets, int32_t* expert_offsets, uint8_t* expanded,
+                        int32_t* exp_row, int32_t* exp_expert, float* exp_gate,
+                        int32_t* row_slot) {
+    for (int e = 0; e < n_experts; ++e) expert_counts[e] = 0;
+    for (int r = 0; r < n_ranks; ++r) rank_counts[r] = 0;
+    for (int64_t p = 0; p < n_rows; ++p)
+        for (int c = 0; c < top_k; ++c) {
+            const int32_t e = row_experts[p * top_k + c];
+            if (e >= 0) expert_counts[e] += 1;
+        }
+    for (int e = 0; e < n_experts; ++e) rank_counts[place[e]] += expert_counts[e];
+    rank_offsets[0] = 0;
+    for (int r = 0; r < n_ranks; ++r) rank_offsets[r + 1] = rank_offsets[r] + rank_counts[r];
+    for (int e = 0; e < n_experts; ++e) {
+        int32_t off = rank_offsets[place[e]];
+        for (int e2 = 0; e2 < e; ++e2)
+            if (place[e2] == place[e]) off += expert_counts[e2];
+        expert_offsets[e] = off;
+    }
+    int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_experts);
+    if (!cursor) return 2;
+    for (int e = 0; e < n_experts; ++e) cursor[e] = expert_offsets[e];
+    for (int64_t i = 0; i < capacity * top_k; ++i) row_slot[i] = -1;
+    for (int64_t p = 0; p < n_rows; ++p) {
+        for (int c = 0; c < top_k; ++c) {
+            const int32_t e = row_experts[p * top_k + c];
+            if (e < 0) continue;
+            const int32_t q = cursor[e]++;
+            if (expanded)
+                memcpy(expanded + (int64_t)q * row_bytes, rows + p * row_bytes, (size_t)row_bytes);
+            exp_row[q] = (int32_t)p;
+            exp_expert[q] = e;
+            exp_gate[q] = row_gates[p * top_k + c];
+            row_slot[p * top_k + c] = q;
+        }
+    }
+    free(cursor);
+    return 0;
+}
+
 /* -------------------------------------------------------------- combine --- */
 
 /* bf16 value nearest to d, ties to even (IEEE round to nearest even), as bits.

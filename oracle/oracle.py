@@ -47,12 +47,15 @@ def lib():
         L.oracle_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_dispatch_dedup.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P,
                                             P, P, P, P, P, P, P]
+        L.oracle_expand_dedup.argtypes = [P, P, P, i64, i64, i32, i32, i32, i32, P, P, P, P,
+                                          P, P, P, P, P, P]
         L.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
         L.oracle_coselect.argtypes = [P, i64, i32, i32, P]
         L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
         L.oracle_bf16_from_double.restype = ctypes.c_uint16
         for f in ("oracle_route_topk", "oracle_send_counts", "oracle_dispatch",
-                  "oracle_dispatch_dedup", "oracle_combine", "oracle_coselect"):
+                  "oracle_dispatch_dedup", "oracle_expand_dedup", "oracle_combine",
+                  "oracle_coselect"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -144,6 +147,47 @@ def dispatch_dedup(x_bits, idx, gate, n_experts, n_ranks, placement=None, with_r
     return dict(cnt, send=send, row_token=row_token, row_experts=row_experts,
                 row_gates=row_gates, row_weight=row_weight, slot_row=slot_row,
                 n_rows=int(n_rows[0]))
+
+
+def expand_dedup(rows_bits, row_experts, row_gates, n_rows, n_experts, n_ranks,
+                 placement=None, capacity=None, with_rows=True):
+    """Receive-side expansion of deduplicated rows into per-expert segments.
+    rows_bits: [>= n_rows][H] of any 1/2/4-byte dtype (copied bitwise) or None."""
+    row_experts = _c(row_experts, np.int32)
+    row_gates = _c(row_gates, np.float32)
+    k = row_experts.shape[1]
+    cap = row_experts.shape[0] if capacity is None else int(capacity)
+    assert n_rows <= cap <= row_experts.shape[0]
+    place = contiguous(n_experts, n_ranks) if placement is None else _c(placement, np.int32)
+    ec = np.empty(n_experts, np.int32)
+    rc = np.empty(n_ranks, np.int32)
+    ro = np.empty(n_ranks + 1, np.int32)
+    eo = np.empty(n_experts, np.int32)
+    n_exp = int((row_experts[:n_rows] >= 0).sum())
+    if rows_bits is not None and with_rows:
+        x = np.ascontiguousarray(rows_bits)
+        row_bytes = x.shape[1] * x.itemsize
+        expanded = np.empty((n_exp,) + x.shape[1:], x.dtype)
+    else:
+        x, row_bytes, expanded = None, 0, None
+    exp_row = np.empty(n_exp, np.int32)
+    exp_expert = np.empty(n_exp, np.int32)
+    exp_gate = np.empty(n_exp, np.float32)
+    row_slot = np.empty((cap, k), np.int32)
+    _check(lib().oracle_expand_dedup(_p(x), _p(row_experts), _p(row_gates), int(n_rows), cap,
+                                     row_bytes, n_experts, k, n_ranks, _p(place), _p(ec),
+                                     _p(rc), _p(ro), _p(eo), _p(expanded), _p(exp_row),
+                                     _p(exp_expert), _p(exp_gate), _p(row_slot)),
+           "expand_dedup")
+    return {"expert_counts": ec, "rank_counts": rc, "rank_offsets": ro, "expert_offsets": eo,
+            "expanded": expanded, "exp_row": exp_row, "exp_expert": exp_expert,
+            "exp_gate": exp_gate, "row_slot": row_slot, "n_expanded": n_exp}
+
+
+def reduce_rows(expert_out_bits, exp_gate, row_slot, n_rows):
+    """Receive-side reduction: row p < n_rows becomes the gate-weighted sum of
+    its experts' outputs (the combine definition over the received rows)."""
+    return combine(expert_out_bits, exp_gate, _c(row_slot, np.int32)[:n_rows])
 
 
 def combine(rows_bits, row_weight, slot_row):

@@ -126,3 +126,11 @@ def softmax_desc(values):
     ex = [math.exp(v - m) for v in values]
     s = math.fsum(ex)
     return sorted((e / s for e in ex), reverse=True)
+
+
+def expand_layout(row_experts, n_rows, place):
+    """Receive-side expansion: position of every listed (row p, column c), by a
+    full sort of the (rank, expert, row) keys of the non-padding entries."""
+    keys = sorted((place[e], e, p, c) for p in range(n_rows)
+                  for c, e in enumerate(row_experts[p]) if e >= 0)
+    return {(p, c): q for q, (_, e, p, c) in enumerate(keys)}

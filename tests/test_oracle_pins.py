@@ -376,3 +376,99 @@ def test_coselect_invariants(oracle_mod, name):
     # accumulation: a second call adds the same counts again
     W2 = oracle_mod.coselect(idx, w.n_experts, tokens=n, W=W.copy())
     assert (W2 == 2 * W).all()
+
+
+# ------------------------------------------------ receive-side expansion --
+
+@pytest.mark.parametrize("T,E,k,R", TINY)
+@pytest.mark.parametrize("placement_kind", ["contiguous", "random"])
+def test_bruteforce_expand(oracle_mod, T, E, k, R, placement_kind):
+    """Expanded positions = index in the sorted (rank, expert, row) key list of
+    the listed entries; padding and rows past n_rows map to -1."""
+    inp = _tiny_logits(T, E, 11 + T * E + k, tied=True)
+    place = (WL.contiguous_placement(E, R) if placement_kind == "contiguous"
+             else WL.random_placement(E, R, seed=T + 2 * E))
+    idx, gate = oracle_mod.route_topk(inp["logits"], k)
+    dd = oracle_mod.dispatch_dedup(inp["x_bits"], idx, gate, E, R, place)
+    D = dd["n_rows"]
+    cap = D + 5   # rows past n_rows hold garbage ids that must be ignored
+    rx = np.concatenate([dd["row_experts"], np.full((5, k), 3 % E, np.int32)])
+    rg = np.concatenate([dd["row_gates"], np.ones((5, k), np.float32)])
+    rows = np.concatenate([dd["send"], np.zeros((5, 4), np.uint16)])
+    ex = oracle_mod.expand_dedup(rows, rx, rg, D, E, R, place, capacity=cap)
+    pos = BF.expand_layout(rx.tolist(), D, place.tolist())
+    assert ex["n_expanded"] == len(pos) == T * k
+    for (p, c), q in pos.items():
+        assert ex["row_slot"][p, c] == q
+        assert ex["exp_row"][q] == p and ex["exp_expert"][q] == rx[p, c]
+        assert ex["exp_gate"][q] == rg[p, c]
+        assert (ex["expanded"][q] == rows[p]).all()
+    listed = {pc for pc in pos}
+    for p in range(cap):
+        for c in range(k):
+            if (p, c) not in listed:
+                assert ex["row_slot"][p, c] == -1
+    assert ex["expert_counts"].tolist() == np.bincount(idx.ravel(), minlength=E).tolist()
+
+
+@pytest.mark.parametrize("name", [n for n in WL.ORDER if "dedup" in WL.get(n).dispatch])
+def test_expand_of_dedup_rows_is_the_plain_dispatch(oracle_mod, name):
+    """Expert Coupling, Method 1: the deduplicating dispatcher delivers the same
+    (token, expert) work as the conventional one.  Expanding the dedup rows per
+    expert must give back the conventional dispatcher's buffer exactly: same
+    rows, same segment offsets, same experts and gates per row."""
+    w = WL.get(name)
+    inp = WL.make_inputs(w, with_x=False)
+    T = min(w.tokens, 2048)
+    logits = inp["logits"][:T]
+    x = WL.make_custom_inputs(T, 16, 1, seed=5)["x_bits"]
+    idx, gate = oracle_mod.route_topk(logits, w.top_k)
+    place = inp["placement"]
+    E, R = w.n_experts, w.n_ranks
+    dd = oracle_mod.dispatch_dedup(x, idx, gate, E, R, place)
+    pl = oracle_mod.dispatch(x, idx, gate, E, R, place)
+    ex = oracle_mod.expand_dedup(dd["send"], dd["row_experts"], dd["row_gates"], dd["n_rows"],
+                                 E, R, place)
+    assert ex["n_expanded"] == pl["n_rows"] == T * w.top_k
+    assert (ex["expanded"] == pl["send"]).all()
+    assert (ex["expert_offsets"] == pl["expert_offsets"]).all()
+    assert (ex["rank_offsets"] == pl["rank_offsets"]).all()
+    assert (ex["exp_expert"] == pl["row_expert"]).all()
+    assert (ex["exp_gate"].view(np.uint32) == pl["row_weight"].view(np.uint32)).all()
+    assert (dd["row_token"][ex["exp_row"]] == pl["row_token"]).all()
+    # every expanded row is reached from exactly one (row, column)
+    rs = ex["row_slot"][: dd["n_rows"]]
+    got = np.sort(rs[rs >= 0])
+    assert (got == np.arange(T * w.top_k)).all()
+
+
+@pytest.mark.parametrize("name", ["deepseek_moe_16b", "zyphra_top2_ep8", "zyphra_top6_ep32"])
+def test_receive_round_trip_with_identity_experts(oracle_mod, name):
+    """Identity experts: each received row reduces to (sum of its gates) * x,
+    and combining those rows with weight 1 returns x (gates sum to 1), up to
+    the two bf16 roundings: within 2 bf16 ulps of x, and exactly x where the
+    token's experts all live on one rank (half the tokens of the top-2 EP8
+    workload)."""
+    w = WL.get(name)
+    inp = WL.make_inputs(w, with_x=False)
+    T = 1024
+    x = WL.make_custom_inputs(T, 64, 1, seed=9)["x_bits"]
+    idx, gate = oracle_mod.route_topk(inp["logits"][:T], w.top_k)
+    E, R, place = w.n_experts, w.n_ranks, inp["placement"]
+    dd = oracle_mod.dispatch_dedup(x, idx, gate, E, R, place)
+    ex = oracle_mod.expand_dedup(dd["send"], dd["row_experts"], dd["row_gates"], dd["n_rows"],
+                                 E, R, place)
+    red = oracle_mod.reduce_rows(ex["expanded"], ex["exp_gate"], ex["row_slot"], dd["n_rows"])
+    out = oracle_mod.combine(red, None, dd["slot_row"])
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    of = (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ulp = np.maximum(np.abs(xf), 2.0 ** -126) * 2.0 ** -7
+    assert (np.abs(of - xf) <= 2 * ulp).all()
+    pl = inp["placement_array"]
+    one_rank = np.array([len({int(pl[e]) for e in row}) == 1 for row in idx])
+    # one rank: x * sum(g) with |sum(g) - 1| <= k 2^-24 rounds back to x, and a
+    # weight-1 combine of one row is exact
+    if one_rank.any():
+        g1 = gate[one_rank].astype(np.float64).sum(1)
+        assert np.abs(g1 - 1).max() <= w.top_k * 2.0 ** -24
+        assert (out[one_rank] == x[one_rank]).all()
