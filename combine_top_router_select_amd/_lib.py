@@ -11,8 +11,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_rout
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 
-SYMBOLS = ("moe_status_string", "moe_workspace_bytes", "moe_route_topk", "moe_send_counts", "moe_dispatch_permute",
-           "moe_dispatch_permute_dedup", "moe_combine", "moe_coselect_counts")
+SYMBOLS = ("moe_status_string", "moe_workspace_bytes", "moe_expand_workspace_bytes",
+           "moe_route_topk", "moe_send_counts", "moe_dispatch_permute",
+           "moe_dispatch_permute_dedup", "moe_combine", "moe_coselect_counts",
+           "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce")
 
 _lib = None
 
@@ -44,7 +46,13 @@ def lib():
                                                  sz, P, P, P, P, P, P, P, P]
         L.moe_combine.argtypes = [P, P, P, i64, i32, i32, i32, P, P]
         L.moe_coselect_counts.argtypes = [P, i64, i32, i32, P, P]
-        for s in SYMBOLS[2:]:
+        L.moe_expand_workspace_bytes.argtypes = [i64, i32, i32, i32]
+        L.moe_expand_workspace_bytes.restype = sz
+        L.moe_expand_counts.argtypes = [P, P, i64, i32, i32, i32, P, P, P, P, P, P, sz, P]
+        L.moe_expand_permute.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, P, sz, P, i64,
+                                         P, P, P, P, P]
+        L.moe_expand_reduce.argtypes = [P, P, P, P, i64, i32, i32, i32, P, P]
+        for s in SYMBOLS[3:]:
             getattr(L, s).restype = i32
         _lib = L
     return _lib

@@ -15,8 +15,14 @@ hipError_t launch_send_counts(const int32_t*, int64_t, int, int, int, const int3
 hipError_t launch_dispatch(const void*, const int32_t*, const float*, int64_t, int, int, int,
                            int, const int32_t*, const void*, int, void*, int32_t*, int32_t*,
                            float*, float*, int32_t*, int32_t*, hipStream_t);
-hipError_t launch_combine(const void*, const float*, const int32_t*, int64_t, int, int, void*,
-                          hipStream_t);
+hipError_t launch_combine(const void*, const float*, const int32_t*, int64_t, int, int,
+                          const int32_t*, void*, hipStream_t);
+hipError_t launch_expand_counts(const int32_t*, int64_t, int, int, int, const int32_t*,
+                                const int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, void*,
+                                hipStream_t);
+hipError_t launch_expand(const void*, const float*, const int32_t*, int64_t, int, int, int, int,
+                         const void*, void*, int64_t, int32_t*, int32_t*, float*, int32_t*,
+                         hipStream_t);
 hipError_t launch_coselect(const int32_t*, int64_t, int, int, int32_t*, hipStream_t);
 }  // namespace moe
 
@@ -158,8 +164,75 @@ MOE_API int moe_combine(const void* rows, const float* row_weight, const int32_t
   if (rb % 16 != 0 || rb > INT_MAX / 2) return MOE_EUNSUPPORTED;
   if (tokens == 0) return MOE_OK;
   if (!rows || !slot_row || !out) return MOE_EINVAL;
-  return hip_status(moe::launch_combine(rows, row_weight, slot_row, tokens, int(rb), top_k, out,
-                                        as_stream(stream)));
+  return hip_status(moe::launch_combine(rows, row_weight, slot_row, tokens, int(rb), top_k,
+                                        nullptr, out, as_stream(stream)));
+}
+
+MOE_API size_t moe_expand_workspace_bytes(int64_t capacity, int n_experts, int top_k,
+                                          int n_ranks) {
+  return moe_workspace_bytes(capacity, n_experts, top_k, n_ranks, 0);
+}
+
+MOE_API int moe_expand_counts(const int32_t* row_experts, const int32_t* n_rows,
+                              int64_t capacity, int n_experts, int top_k, int n_ranks,
+                              const int32_t* placement, int32_t* expert_counts,
+                              int32_t* rank_counts, int32_t* rank_offsets,
+                              int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  int st = check_tek(capacity, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if ((capacity > 0 && !row_experts) || !n_rows || !expert_counts || !rank_counts ||
+      !rank_offsets || !workspace)
+    return MOE_EINVAL;
+  if (workspace_bytes < moe_expand_workspace_bytes(capacity, n_experts, top_k, n_ranks))
+    return MOE_EWORKSPACE;
+  return hip_status(moe::launch_expand_counts(row_experts, capacity, n_experts, top_k, n_ranks,
+                                              placement, n_rows, expert_counts, rank_counts,
+                                              rank_offsets, expert_offsets, workspace,
+                                              as_stream(stream)));
+}
+
+MOE_API int moe_expand_permute(const void* rows, const int32_t* row_experts,
+                               const float* row_gates, const int32_t* n_rows, int64_t capacity,
+                               int hidden_dim, int n_experts, int top_k, int n_ranks,
+                               int bytes_per_element, const void* workspace,
+                               size_t workspace_bytes, void* expanded, int64_t expanded_capacity,
+                               int32_t* exp_row, int32_t* exp_expert, float* exp_gate,
+                               int32_t* row_slot, void* stream) {
+  int st = check_tek(capacity, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if ((st = check_rows(hidden_dim, bytes_per_element)) != MOE_OK) return st;
+  if (expanded_capacity < 0 || !n_rows || !workspace) return MOE_EINVAL;
+  if (expanded_capacity > int64_t(INT_MAX)) return MOE_EUNSUPPORTED;
+  if (workspace_bytes < moe_expand_workspace_bytes(capacity, n_experts, top_k, n_ranks))
+    return MOE_EWORKSPACE;
+  if (capacity == 0) return MOE_OK;
+  if (!rows || !row_experts || !row_gates || !row_slot ||
+      (expanded_capacity > 0 && (!expanded || !exp_row || !exp_expert || !exp_gate)))
+    return MOE_EINVAL;
+  (void)row_experts;  // the plan in the workspace already encodes them
+  return hip_status(moe::launch_expand(rows, row_gates, n_rows, capacity,
+                                       hidden_dim * bytes_per_element, n_experts, top_k, n_ranks,
+                                       workspace, expanded, expanded_capacity, exp_row,
+                                       exp_expert, exp_gate, row_slot, as_stream(stream)));
+}
+
+MOE_API int moe_expand_reduce(const void* expert_out, const float* exp_gate,
+                              const int32_t* row_slot, const int32_t* n_rows, int64_t capacity,
+                              int hidden_dim, int top_k, int bytes_per_element, void* out,
+                              void* stream) {
+  if (capacity < 0 || top_k < 1 || hidden_dim < 1 || bytes_per_element < 1) return MOE_EINVAL;
+  if (top_k > MOE_MAX_TOP_K || bytes_per_element != 2) return MOE_EUNSUPPORTED;
+  if (capacity > int64_t(INT_MAX) / top_k) return MOE_EUNSUPPORTED;
+  const int64_t rb = int64_t(hidden_dim) * 2;
+  if (rb % 16 != 0 || rb > INT_MAX / 2) return MOE_EUNSUPPORTED;
+  if (!n_rows) return MOE_EINVAL;
+  if (capacity == 0) return MOE_OK;
+  if (!expert_out || !row_slot || !out) return MOE_EINVAL;
+  return hip_status(moe::launch_combine(expert_out, exp_gate, row_slot, capacity, int(rb), top_k,
+                                        n_rows, out, as_stream(stream)));
 }
 
 MOE_API int moe_coselect_counts(const int32_t* topk_idx, int64_t tokens, int n_experts,

@@ -36,12 +36,13 @@ template <int NV, int KMAX>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
                const int32_t* __restrict__ slot_row, int64_t T, int row_bytes, int k, int cpr,
-               uint8_t* __restrict__ out) {
+               const int32_t* __restrict__ n_valid, uint8_t* __restrict__ out) {
   const int lane = lane_id();
   const int64_t wid = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
   const int64_t t = wid / cpr;
   const int c = int(wid - t * cpr);
   if (t >= T) return;  // whole wave
+  if (n_valid && t >= *n_valid) return;  // whole wave: only the first *n_valid outputs
   const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
   // All loads are unconditional from clamped, in-bounds addresses (a load under
   // a branch is followed by a wait for it); only arithmetic and stores are
@@ -123,42 +124,45 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
 
 template <int NV, int KMAX>
 static hipError_t launch_combine_t(const void* rows, const float* w, const int32_t* slot_row,
-                                   int64_t T, int row_bytes, int k, void* out,
-                                   hipStream_t stream) {
+                                   int64_t T, int row_bytes, int k, const int32_t* n_valid,
+                                   void* out, hipStream_t stream) {
   const int chunk = NV * kWave * 16;
   const int cpr = (row_bytes + chunk - 1) / chunk;
   const int64_t blocks = (T * cpr + 3) / 4;
   hipLaunchKernelGGL((combine_kernel<NV, KMAX>), dim3(unsigned(blocks)), dim3(256), 0, stream,
                      static_cast<const uint8_t*>(rows), w, slot_row, T, row_bytes, k, cpr,
-                     static_cast<uint8_t*>(out));
+                     n_valid, static_cast<uint8_t*>(out));
   return hipGetLastError();
 }
 
 template <int KMAX>
 static hipError_t launch_combine_k(const void* rows, const float* w, const int32_t* slot_row,
-                                   int64_t T, int row_bytes, int k, void* out,
-                                   hipStream_t stream) {
+                                   int64_t T, int row_bytes, int k, const int32_t* n_valid,
+                                   void* out, hipStream_t stream) {
   // keep KMAX * NV <= 32 vectors (128 VGPRs) in flight per lane
   const int vr = row_bytes / 16;
   constexpr int NVMAX = (32 / KMAX) < 4 ? (32 / KMAX) : 4;
   if (NVMAX >= 4 && vr >= 4 * kWave)
-    return launch_combine_t<(NVMAX >= 4 ? 4 : 1), KMAX>(rows, w, slot_row, T, row_bytes, k, out,
-                                                         stream);
+    return launch_combine_t<(NVMAX >= 4 ? 4 : 1), KMAX>(rows, w, slot_row, T, row_bytes, k,
+                                                         n_valid, out, stream);
   if (NVMAX >= 2 && vr >= 2 * kWave)
-    return launch_combine_t<(NVMAX >= 2 ? 2 : 1), KMAX>(rows, w, slot_row, T, row_bytes, k, out,
-                                                         stream);
-  return launch_combine_t<1, KMAX>(rows, w, slot_row, T, row_bytes, k, out, stream);
+    return launch_combine_t<(NVMAX >= 2 ? 2 : 1), KMAX>(rows, w, slot_row, T, row_bytes, k,
+                                                         n_valid, out, stream);
+  return launch_combine_t<1, KMAX>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
 }
 
+// n_valid (device, may be null): only outputs t < *n_valid are computed and
+// written (the receive-side reduction over the received rows).
 hipError_t launch_combine(const void* rows, const float* w, const int32_t* slot_row, int64_t T,
-                          int row_bytes, int k, void* out, hipStream_t stream) {
+                          int row_bytes, int k, const int32_t* n_valid, void* out,
+                          hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if (k <= 1) return launch_combine_k<1>(rows, w, slot_row, T, row_bytes, k, out, stream);
-  if (k <= 2) return launch_combine_k<2>(rows, w, slot_row, T, row_bytes, k, out, stream);
-  if (k <= 4) return launch_combine_k<4>(rows, w, slot_row, T, row_bytes, k, out, stream);
-  if (k <= 6) return launch_combine_k<6>(rows, w, slot_row, T, row_bytes, k, out, stream);
-  if (k <= 8) return launch_combine_k<8>(rows, w, slot_row, T, row_bytes, k, out, stream);
-  return launch_combine_k<16>(rows, w, slot_row, T, row_bytes, k, out, stream);
+  if (k <= 1) return launch_combine_k<1>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  if (k <= 2) return launch_combine_k<2>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  if (k <= 4) return launch_combine_k<4>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  if (k <= 6) return launch_combine_k<6>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  if (k <= 8) return launch_combine_k<8>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  return launch_combine_k<16>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
 }
 
 }  // namespace moe

@@ -10,6 +10,7 @@ namespace moe {
 
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kTile = 64;          // tokens per counting tile (one lane per token)
+constexpr uint32_t kNoSlot = 0xFFFFFFFFu;  // plan code of an empty slot (received rows)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

@@ -63,11 +63,13 @@ __device__ __forceinline__ void load_tile_ids(int (&raw)[KMAX], const int32_t* _
 // same positions, so loads and stores stay coalesced.  In dedup mode every id
 // also sets its token's bit in its rank's bitmap (setting it twice is harmless).
 // `s_rank` maps expert -> rank (LDS) or is null for contiguous placement.
-template <bool DEDUP, int KMAX>
+// PAD (received rows): negative ids are empty slots and only the first
+// `tvalid` rows of the tile are counted; empty entries get the code kNoSlot.
+template <bool DEDUP, bool PAD, int KMAX>
 __device__ __forceinline__ void count_tile(const int (&raw)[KMAX], int64_t f0, int nf, int k,
                                            uint32_t kmul, int E, const int32_t* s_rank, int m,
-                                           uint64_t* bits, uint32_t* __restrict__ lslot,
-                                           int lane) {
+                                           int tvalid, uint64_t* bits,
+                                           uint32_t* __restrict__ lslot, int lane) {
   int e[KMAX], col[KMAX], tl[KMAX];
 #pragma unroll
   for (int r = 0; r < KMAX; ++r) {
@@ -77,9 +79,13 @@ __device__ __forceinline__ void count_tile(const int (&raw)[KMAX], int64_t f0, i
     tl[r] = tl[r] < kTile ? tl[r] : kTile - 1;  // positions past the tile are never used
     col[r] = DEDUP ? (s_rank ? s_rank[e[r]] : e[r] / m) : e[r];
   }
+  bool ok[KMAX];
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r)
+    ok[r] = lane + kWave * r < nf && (!PAD || (raw[r] >= 0 && tl[r] < tvalid));
 #pragma unroll
   for (int r = 0; r < KMAX; ++r) {
-    if (lane + kWave * r < nf) {
+    if (ok[r]) {
       const unsigned long long bit = 1ull << tl[r];
       atomicOr(reinterpret_cast<unsigned long long*>(&bits[e[r]]), bit);
       if (DEDUP) atomicOr(reinterpret_cast<unsigned long long*>(&bits[E + col[r]]), bit);
@@ -92,6 +98,7 @@ __device__ __forceinline__ void count_tile(const int (&raw)[KMAX], int64_t f0, i
     const uint64_t mb = bits[DEDUP ? E + col[r] : col[r]];
     const uint64_t below = tl[r] == 0 ? 0ull : (~0ull >> (kWave - tl[r]));
     code[r] = (uint32_t(col[r]) << 8) | uint32_t(__popcll(mb & below));
+    if (PAD && !ok[r]) code[r] = kNoSlot;
   }
 #pragma unroll
   for (int r = 0; r < KMAX; ++r)
@@ -100,11 +107,12 @@ __device__ __forceinline__ void count_tile(const int (&raw)[KMAX], int64_t f0, i
 
 // ----------------------------------------------------------- tile counts --
 
-template <bool DEDUP, int KMAX>
+template <bool DEDUP, bool PAD, int KMAX>
 __global__ void __launch_bounds__(kWave)
 tile_counts_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k, int R,
                    const int32_t* __restrict__ place, int m, uint32_t kmul, int64_t Bp,
-                   uint8_t* __restrict__ tcnt, uint32_t* __restrict__ lslot) {
+                   const int32_t* __restrict__ n_valid, uint8_t* __restrict__ tcnt,
+                   uint32_t* __restrict__ lslot) {
   extern __shared__ uint64_t s_tdyn[];
   const int C = E + (DEDUP ? R : 0);
   uint64_t* bits = s_tdyn;                                        // [C]
@@ -116,13 +124,18 @@ tile_counts_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k, int
   const int nf = int(total - f0 < int64_t(kTile) * k ? total - f0 : int64_t(kTile) * k);
   int raw[KMAX];
   load_tile_ids<KMAX>(raw, idx, f0, total, lane);
+  int tvalid = kTile;  // rows of this tile that count (PAD: rows below *n_valid)
+  if (PAD) {
+    const int64_t nv = *n_valid;
+    tvalid = int(nv - b * kTile < 0 ? 0 : (nv - b * kTile > kTile ? kTile : nv - b * kTile));
+  }
   for (int c = lane; c < C; c += kWave) bits[c] = 0ull;
   const bool has_rank = DEDUP && place;
   if (has_rank)
     for (int e = lane; e < E; e += kWave) s_rank[e] = clampi(place[e], 0, R - 1);
   wave_lds_sync();
-  count_tile<DEDUP, KMAX>(raw, f0, nf, k, kmul, E, has_rank ? s_rank : nullptr, m, bits, lslot,
-                          lane);
+  count_tile<DEDUP, PAD, KMAX>(raw, f0, nf, k, kmul, E, has_rank ? s_rank : nullptr, m, tvalid,
+                               bits, lslot, lane);
   for (int c = lane; c < C; c += kWave) tcnt[c * Bp + b] = uint8_t(__popcll(bits[c]));
 }
 
@@ -461,11 +474,12 @@ plan_scan_fast_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, in
   }
 }
 
-template <int KMAX>
+template <bool PAD, int KMAX>
 static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, int R,
-                                  const int32_t* place, int dedup, int32_t* expert_counts,
-                                  int32_t* rank_counts, int32_t* rank_offsets,
-                                  int32_t* expert_offsets, void* workspace, hipStream_t stream) {
+                                  const int32_t* place, int dedup, const int32_t* n_valid,
+                                  int32_t* expert_counts, int32_t* rank_counts,
+                                  int32_t* rank_offsets, int32_t* expert_offsets,
+                                  void* workspace, hipStream_t stream) {
   const PlanLayout pl = plan_layout(T, E, k, R, dedup);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int32_t* header = reinterpret_cast<int32_t*>(ws);
@@ -477,13 +491,13 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
     const size_t lds = size_t(pl.cols) * sizeof(uint64_t) + size_t(E) * sizeof(int32_t);
     const uint32_t kmul = kdiv_mul(k);
     if (dedup)
-      hipLaunchKernelGGL((tile_counts_kernel<true, KMAX>), dim3(unsigned(pl.tiles)), dim3(kWave),
-                         lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad, tcnt,
-                         lslot);
-    else
-      hipLaunchKernelGGL((tile_counts_kernel<false, KMAX>), dim3(unsigned(pl.tiles)),
+      hipLaunchKernelGGL((tile_counts_kernel<true, false, KMAX>), dim3(unsigned(pl.tiles)),
                          dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
-                         tcnt, lslot);
+                         n_valid, tcnt, lslot);
+    else
+      hipLaunchKernelGGL((tile_counts_kernel<false, PAD, KMAX>), dim3(unsigned(pl.tiles)),
+                         dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
+                         n_valid, tcnt, lslot);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -542,16 +556,43 @@ hipError_t launch_send_counts(const int32_t* idx, int64_t T, int E, int k, int R
                               int32_t* rank_counts, int32_t* rank_offsets,
                               int32_t* expert_offsets, void* workspace, hipStream_t stream) {
   if (k <= 2)
-    return launch_counts_k<2>(idx, T, E, k, R, place, dedup, expert_counts, rank_counts,
-                              rank_offsets, expert_offsets, workspace, stream);
+    return launch_counts_k<false, 2>(idx, T, E, k, R, place, dedup, nullptr, expert_counts,
+                                     rank_counts, rank_offsets, expert_offsets, workspace,
+                                     stream);
   if (k <= 4)
-    return launch_counts_k<4>(idx, T, E, k, R, place, dedup, expert_counts, rank_counts,
-                              rank_offsets, expert_offsets, workspace, stream);
+    return launch_counts_k<false, 4>(idx, T, E, k, R, place, dedup, nullptr, expert_counts,
+                                     rank_counts, rank_offsets, expert_offsets, workspace,
+                                     stream);
   if (k <= 8)
-    return launch_counts_k<8>(idx, T, E, k, R, place, dedup, expert_counts, rank_counts,
-                              rank_offsets, expert_offsets, workspace, stream);
-  return launch_counts_k<16>(idx, T, E, k, R, place, dedup, expert_counts, rank_counts,
-                             rank_offsets, expert_offsets, workspace, stream);
+    return launch_counts_k<false, 8>(idx, T, E, k, R, place, dedup, nullptr, expert_counts,
+                                     rank_counts, rank_offsets, expert_offsets, workspace,
+                                     stream);
+  return launch_counts_k<false, 16>(idx, T, E, k, R, place, dedup, nullptr, expert_counts,
+                                    rank_counts, rank_offsets, expert_offsets, workspace, stream);
+}
+
+// Receive side: the plan of the per-expert expansion of `cap` received rows, of
+// which the first *n_rows count; negative ids are empty slots.  Same plan as
+// the plain dispatch (rows play the part of tokens).
+hipError_t launch_expand_counts(const int32_t* row_experts, int64_t cap, int E, int k, int R,
+                                const int32_t* place, const int32_t* n_rows,
+                                int32_t* expert_counts, int32_t* rank_counts,
+                                int32_t* rank_offsets, int32_t* expert_offsets, void* workspace,
+                                hipStream_t stream) {
+  if (k <= 2)
+    return launch_counts_k<true, 2>(row_experts, cap, E, k, R, place, 0, n_rows, expert_counts,
+                                    rank_counts, rank_offsets, expert_offsets, workspace,
+                                    stream);
+  if (k <= 4)
+    return launch_counts_k<true, 4>(row_experts, cap, E, k, R, place, 0, n_rows, expert_counts,
+                                    rank_counts, rank_offsets, expert_offsets, workspace,
+                                    stream);
+  if (k <= 8)
+    return launch_counts_k<true, 8>(row_experts, cap, E, k, R, place, 0, n_rows, expert_counts,
+                                    rank_counts, rank_offsets, expert_offsets, workspace,
+                                    stream);
+  return launch_counts_k<true, 16>(row_experts, cap, E, k, R, place, 0, n_rows, expert_counts,
+                                   rank_counts, rank_offsets, expert_offsets, workspace, stream);
 }
 
 }  // namespace moe

@@ -50,19 +50,26 @@ __device__ __forceinline__ void store_chunk(const u32x4 (&v)[NV], uint8_t* dst, 
   }
 }
 
-template <int NV, bool NT>
+// PAD: the receive-side expansion, where a "token" is a received row, slots
+// with the code kNoSlot are empty, only rows below *n_valid are expanded, and
+// no row is written at or past out_cap (such slots get slot_row = -1).
+template <int NV, bool NT, bool PAD>
 __global__ void __launch_bounds__(256)
-dispatch_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
-                const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k, int cpr,
-                const int32_t* __restrict__ base, const uint32_t* __restrict__ lslot, int64_t Bp,
-                uint8_t* __restrict__ send, int32_t* __restrict__ row_token,
-                int32_t* __restrict__ row_expert, float* __restrict__ row_weight,
-                int32_t* __restrict__ slot_row) {
+dispatch_kernel(const uint8_t* __restrict__ x, const float* __restrict__ gate, int64_t T,
+                int row_bytes, int k, int cpr, const int32_t* __restrict__ base,
+                const uint32_t* __restrict__ lslot, int64_t Bp, uint8_t* __restrict__ send,
+                int32_t* __restrict__ row_token, int32_t* __restrict__ row_expert,
+                float* __restrict__ row_weight, int32_t* __restrict__ slot_row,
+                const int32_t* __restrict__ n_valid, int64_t out_cap) {
   const int lane = lane_id();
   const int64_t wid = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
   const int64_t t = wid / cpr;
   const int c = int(wid - t * cpr);
   if (t >= T) return;  // whole wave
+  if (PAD && t >= *n_valid) {  // whole wave: a row past the received ones
+    if (c == 0 && lane < k) slot_row[t * k + lane] = -1;
+    return;
+  }
   const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
   // lanes j < k own slot j; the other lanes load slot k-1's data and ignore it
   const int jl = lane < k ? lane : k - 1;
@@ -70,19 +77,25 @@ dispatch_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
   const float g = gate[t * k + jl];
   u32x4 v[NV];
   load_chunk<NV>(v, x + t * row_bytes, chunk0, row_bytes, lane);
-  const int e = int(code >> 8);
+  const bool has = !PAD || code != kNoSlot;
+  const int e = has ? int(code >> 8) : 0;
   const int pos = base[e * Bp + t / kTile] + int(code & 255u);
+  const bool ok = has && (!PAD || pos < out_cap);
+  const uint64_t okm = __ballot(lane < k && ok);
   for (int j = 0; j < k; ++j) {
+    if (PAD && !((okm >> j) & 1ull)) continue;
     const int p = bcast(pos, j);
     store_chunk<NV, NT>(v, send + int64_t(p) * row_bytes + chunk0, chunk0, row_bytes, lane);
   }
   // metadata last: stores count against the same wait counter as loads, so
   // stores issued before the row stores would hold them up
   if (c == 0 && lane < k) {
-    slot_row[t * k + lane] = pos;
-    row_token[pos] = int32_t(t);
-    row_expert[pos] = e;
-    row_weight[pos] = g;
+    slot_row[t * k + lane] = ok ? pos : -1;
+    if (ok) {
+      row_token[pos] = int32_t(t);
+      row_expert[pos] = e;
+      row_weight[pos] = g;
+    }
   }
 }
 
@@ -192,10 +205,10 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
   constexpr bool NT = MOE_DISPATCH_NT != 0;
   if (!dedup) {
     if (T == 0) return hipSuccess;
-    hipLaunchKernelGGL((dispatch_kernel<NV, NT>), dim3(unsigned(blocks)), dim3(256), 0, stream,
-                       static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, cpr, base,
+    hipLaunchKernelGGL((dispatch_kernel<NV, NT, false>), dim3(unsigned(blocks)), dim3(256), 0,
+                       stream, static_cast<const uint8_t*>(x), gate, T, row_bytes, k, cpr, base,
                        lslot, pl.tiles_pad, static_cast<uint8_t*>(send), row_token, row_e,
-                       row_weight, slot_row);
+                       row_weight, slot_row, nullptr, int64_t(0));
   } else {
     hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT>), dim3(unsigned(blocks)), dim3(256), 0,
                        stream, static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, R,
@@ -224,6 +237,49 @@ hipError_t launch_dispatch(const void* x, const int32_t* idx, const float* gate,
       return launch_dispatch_nv<1>(x, idx, gate, T, row_bytes, E, k, R, place, workspace, dedup,
                                    send, row_token, row_e, row_gates, row_weight, slot_row,
                                    n_rows, stream);
+  }
+}
+
+
+template <int NV>
+static hipError_t launch_expand_nv(const void* rows, const float* row_gates,
+                                   const int32_t* n_rows, int64_t cap, int row_bytes, int E,
+                                   int k, int R, const void* workspace, void* expanded,
+                                   int64_t out_cap, int32_t* exp_row, int32_t* exp_expert,
+                                   float* exp_gate, int32_t* row_slot, hipStream_t stream) {
+  const PlanLayout pl = plan_layout(cap, E, k, R, 0);
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  const int32_t* base = reinterpret_cast<const int32_t*>(ws + pl.base_off);
+  const uint32_t* lslot = reinterpret_cast<const uint32_t*>(ws + pl.lslot_off);
+  const int chunk = NV * kWave * 16;
+  const int cpr = (row_bytes + chunk - 1) / chunk;
+  const int64_t blocks = (cap * cpr + 3) / 4;
+  constexpr bool NT = MOE_DISPATCH_NT != 0;
+  hipLaunchKernelGGL((dispatch_kernel<NV, NT, true>), dim3(unsigned(blocks)), dim3(256), 0,
+                     stream, static_cast<const uint8_t*>(rows), row_gates, cap, row_bytes, k, cpr,
+                     base, lslot, pl.tiles_pad, static_cast<uint8_t*>(expanded), exp_row,
+                     exp_expert, exp_gate, row_slot, n_rows, out_cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand(const void* rows, const float* row_gates, const int32_t* n_rows,
+                         int64_t cap, int row_bytes, int E, int k, int R, const void* workspace,
+                         void* expanded, int64_t out_cap, int32_t* exp_row, int32_t* exp_expert,
+                         float* exp_gate, int32_t* row_slot, hipStream_t stream) {
+  if (cap == 0) return hipSuccess;
+  switch (dispatch_nv(row_bytes)) {
+    case 4:
+      return launch_expand_nv<4>(rows, row_gates, n_rows, cap, row_bytes, E, k, R, workspace,
+                                 expanded, out_cap, exp_row, exp_expert, exp_gate, row_slot,
+                                 stream);
+    case 2:
+      return launch_expand_nv<2>(rows, row_gates, n_rows, cap, row_bytes, E, k, R, workspace,
+                                 expanded, out_cap, exp_row, exp_expert, exp_gate, row_slot,
+                                 stream);
+    default:
+      return launch_expand_nv<1>(rows, row_gates, n_rows, cap, row_bytes, E, k, R, workspace,
+                                 expanded, out_cap, exp_row, exp_expert, exp_gate, row_slot,
+                                 stream);
   }
 }
 

@@ -15,7 +15,8 @@ from ._lib import MoeError, check, lib, status_string  # noqa: F401
 
 __all__ = ["MoeError", "moe_status_string", "moe_workspace_bytes", "moe_route_topk",
            "moe_send_counts", "moe_dispatch_permute", "moe_dispatch_permute_dedup",
-           "moe_combine", "moe_coselect_counts", "workspace"]
+           "moe_combine", "moe_coselect_counts", "workspace", "moe_expand_workspace_bytes",
+           "expand_workspace", "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce"]
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -202,3 +203,99 @@ def moe_coselect_counts(topk_idx, n_experts, tokens=None, coselect=None, stream=
     check(lib().moe_coselect_counts(_ptr(topk_idx), n, n_experts, k, _ptr(coselect),
                                     _stream(stream)), "moe_coselect_counts")
     return coselect
+
+
+# ------------------------------------------------------------- receive side --
+
+def moe_expand_workspace_bytes(capacity: int, n_experts: int, top_k: int, n_ranks: int) -> int:
+    return int(lib().moe_expand_workspace_bytes(capacity, n_experts, top_k, n_ranks))
+
+
+def expand_workspace(capacity, n_experts, top_k, n_ranks, device) -> torch.Tensor:
+    n = moe_expand_workspace_bytes(capacity, n_experts, top_k, n_ranks)
+    if n == 0:
+        raise MoeError(1, "moe_expand_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def moe_expand_counts(row_experts, n_rows, n_experts, n_ranks, placement=None, ws=None,
+                      out=None, stream=None):
+    """Receive-side counts and plan for received dedup rows.  `row_experts`
+    [C][k] int32, `n_rows` a 1-element device int32 tensor.  Returns a dict with
+    expert_counts, rank_counts, rank_offsets, expert_offsets and `ws`."""
+    _dev(row_experts, "row_experts", torch.int32, 2)
+    _dev(n_rows, "n_rows", torch.int32)
+    C, k = row_experts.shape
+    dev = row_experts.device
+    if placement is not None:
+        _dev(placement, "placement", torch.int32, 1)
+    if ws is None:
+        ws = expand_workspace(C, n_experts, k, n_ranks, dev)
+    o = dict(out or {})
+    i32 = torch.int32
+    ec = o.get("expert_counts")
+    ec = torch.empty(n_experts, dtype=i32, device=dev) if ec is None else ec
+    rc = o.get("rank_counts")
+    rc = torch.empty(n_ranks, dtype=i32, device=dev) if rc is None else rc
+    ro = o.get("rank_offsets")
+    ro = torch.empty(n_ranks + 1, dtype=i32, device=dev) if ro is None else ro
+    eo = o.get("expert_offsets")
+    eo = torch.empty(n_experts, dtype=i32, device=dev) if eo is None else eo
+    check(lib().moe_expand_counts(_ptr(row_experts), _ptr(n_rows), C, n_experts, k, n_ranks,
+                                  _ptr(placement), _ptr(ec), _ptr(rc), _ptr(ro), _ptr(eo),
+                                  _ptr(ws), ws.numel(), _stream(stream)), "moe_expand_counts")
+    return {"expert_counts": ec, "rank_counts": rc, "rank_offsets": ro, "expert_offsets": eo,
+            "ws": ws}
+
+
+def moe_expand_permute(rows, row_experts, row_gates, n_rows, n_experts, n_ranks, ws,
+                       expanded_capacity=None, out=None, stream=None):
+    """Receive-side expansion.  expanded_capacity defaults to C rows, which
+    holds every entry when the received buffers have the dedup dispatch's
+    capacity T*k (the expansion has exactly T*k rows).  Returns expanded,
+    exp_row, exp_expert, exp_gate, row_slot."""
+    bpe = _x_bpe(rows)
+    _dev(row_experts, "row_experts", torch.int32, 2)
+    _dev(row_gates, "row_gates", torch.float32, 2)
+    _dev(n_rows, "n_rows", torch.int32)
+    C, H = rows.shape
+    k = row_experts.shape[1]
+    dev = rows.device
+    cap = C if expanded_capacity is None else int(expanded_capacity)
+    o = dict(out or {})
+    ex = o.get("expanded")
+    ex = torch.empty((cap, H), dtype=rows.dtype, device=dev) if ex is None else ex
+    er = o.get("exp_row")
+    er = torch.empty(cap, dtype=torch.int32, device=dev) if er is None else er
+    ee = o.get("exp_expert")
+    ee = torch.empty(cap, dtype=torch.int32, device=dev) if ee is None else ee
+    eg = o.get("exp_gate")
+    eg = torch.empty(cap, dtype=torch.float32, device=dev) if eg is None else eg
+    rs = o.get("row_slot")
+    rs = torch.empty((C, k), dtype=torch.int32, device=dev) if rs is None else rs
+    if ex.numel() < cap * H or er.numel() < cap or ee.numel() < cap or eg.numel() < cap:
+        raise ValueError("expanded buffers are smaller than expanded_capacity rows")
+    check(lib().moe_expand_permute(_ptr(rows), _ptr(row_experts), _ptr(row_gates), _ptr(n_rows),
+                                   C, H, n_experts, k, n_ranks, bpe, _ptr(ws), ws.numel(),
+                                   _ptr(ex), cap, _ptr(er), _ptr(ee), _ptr(eg), _ptr(rs),
+                                   _stream(stream)), "moe_expand_permute")
+    return {"expanded": ex, "exp_row": er, "exp_expert": ee, "exp_gate": eg, "row_slot": rs}
+
+
+def moe_expand_reduce(expert_out, exp_gate, row_slot, n_rows, out=None, stream=None):
+    """Receive-side reduction of the experts' outputs back to one row per
+    received row (rows past n_rows are not written)."""
+    _dev(expert_out, "expert_out", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _dev(row_slot, "row_slot", torch.int32, 2)
+    _dev(n_rows, "n_rows", torch.int32)
+    if exp_gate is not None:
+        _dev(exp_gate, "exp_gate", torch.float32)
+    C, k = row_slot.shape
+    H = expert_out.shape[1]
+    if out is None:
+        out = torch.empty((C, H), dtype=expert_out.dtype, device=expert_out.device)
+    _dev(out, "out", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    check(lib().moe_expand_reduce(_ptr(expert_out), _ptr(exp_gate), _ptr(row_slot),
+                                  _ptr(n_rows), C, H, k, 2, _ptr(out), _stream(stream)),
+          "moe_expand_reduce")
+    return out

@@ -206,6 +206,84 @@ int moe_combine(const void* rows, const float* row_weight, const int32_t* slot_r
 int moe_coselect_counts(const int32_t* topk_idx, int64_t tokens, int n_experts, int top_k,
                         int32_t* coselect, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Receive side of the deduplicating dispatcher ([EC] "Method 1": a dedup row
+ * carries the ids and routing probabilities of every selected expert on its
+ * destination rank, so the receiving rank hands the row to each of them and
+ * weights their outputs by those probabilities).
+ *
+ * The received rows are laid out as moe_dispatch_permute_dedup() writes them:
+ * rows [C][H], row_experts [C][k] (ids ascending, -1 = empty column),
+ * row_gates [C][k], and a device row count *n_rows <= C, where C = `capacity`
+ * (host).  Rows at or past *n_rows are ignored, whatever they hold.
+ * Expansion writes, for every received row p and every listed expert e, one
+ * copy of row p into an expanded buffer ordered by (rank of e, e, p): the
+ * layout of the conventional dispatcher, one contiguous segment per expert
+ * (the input of a grouped expert GEMM).  After the experts ran, the reduction
+ * turns each received row back into one row: the gate-weighted sum of its
+ * experts' outputs.
+ * ------------------------------------------------------------------------ */
+
+/* Host.  Bytes of workspace moe_expand_counts() fills and moe_expand_permute()
+ * then reads, for `capacity` received rows.  0 outside the limits. */
+size_t moe_expand_workspace_bytes(int64_t capacity, int n_experts, int top_k, int n_ranks);
+
+/* Receive-side counts and the expansion plan.
+ *   row_experts    [C][k] int32, as above (ids in [0, E) or negative = empty).
+ *   n_rows         device int32[1]: the number of received rows (<= C).
+ *   capacity       host: C, the rows the buffers hold.
+ *   placement      [E] or NULL = contiguous (as moe_send_counts()).
+ *   expert_counts  [E] out: rows listing each expert (the per-expert receive
+ *                  counts).
+ *   rank_counts    [R] out: sum of expert_counts over each rank's experts.
+ *   rank_offsets   [R+1] out: exclusive scan; rank_offsets[R] = the number of
+ *                  expanded rows.
+ *   expert_offsets [E] out or NULL: first expanded row of each expert; experts
+ *                  ordered by (rank, id).
+ *   workspace      >= moe_expand_workspace_bytes(C, E, k, R) bytes.
+ * Errors: as moe_send_counts(); n_rows must not be NULL. */
+int moe_expand_counts(const int32_t* row_experts, const int32_t* n_rows, int64_t capacity,
+                      int n_experts, int top_k, int n_ranks, const int32_t* placement,
+                      int32_t* expert_counts, int32_t* rank_counts, int32_t* rank_offsets,
+                      int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Receive-side expansion: copies every listed (row, expert) into its place.
+ *   rows           [C][H] elements of bytes_per_element bytes (copied bitwise).
+ *   row_gates      [C][k] fp32, aligned with row_experts.
+ *   workspace      as filled by moe_expand_counts() for the same arguments.
+ *   expanded       [expanded_capacity][H] out: expanded row q = rows[exp_row[q]].
+ *   exp_row, exp_expert [expanded_capacity] int32 out; exp_gate
+ *                  [expanded_capacity] fp32 out: source row, expert and that
+ *                  expert's gate of each expanded row.
+ *   row_slot       [C][k] int32 out: expanded row of (row p, column c); -1 for
+ *                  empty columns, for rows at or past *n_rows, and for entries
+ *                  that would land at or past expanded_capacity (those are not
+ *                  written; rank_offsets[R] from moe_expand_counts() tells the
+ *                  caller how many rows the expansion needs).
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (as moe_dispatch_permute()),
+ *         MOE_EWORKSPACE. */
+int moe_expand_permute(const void* rows, const int32_t* row_experts, const float* row_gates,
+                       const int32_t* n_rows, int64_t capacity, int hidden_dim, int n_experts,
+                       int top_k, int n_ranks, int bytes_per_element, const void* workspace,
+                       size_t workspace_bytes, void* expanded, int64_t expanded_capacity,
+                       int32_t* exp_row, int32_t* exp_expert, float* exp_gate,
+                       int32_t* row_slot, void* stream);
+
+/* Receive-side reduction: for every received row p < *n_rows,
+ * out[p][h] = bf16(sum over the distinct expanded rows q in row_slot[p][.]
+ * (q >= 0), in column order, of exp_gate[q] * expert_out[q][h]), with the
+ * arithmetic of moe_combine() (fp32 fused multiply-adds from -0.0, one
+ * round-to-nearest-even).  exp_gate NULL = weight 1.  Rows p >= *n_rows of out
+ * are not written.
+ *   expert_out     [expanded rows][H] bf16: the experts' outputs in the
+ *                  expanded layout.
+ *   out            [C][H] bf16.
+ * Errors: as moe_combine(); n_rows must not be NULL. */
+int moe_expand_reduce(const void* expert_out, const float* exp_gate, const int32_t* row_slot,
+                      const int32_t* n_rows, int64_t capacity, int hidden_dim, int top_k,
+                      int bytes_per_element, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,6 +152,52 @@ def test_combine_and_coselect_errors(lib):
     assert s(None, 0, 8, 2, None, None) == 0                        # no tokens: no-op
 
 
+def test_receive_side_errors(lib):
+    assert lib.moe_expand_workspace_bytes(100, 8, 2, 4) == lib.moe_workspace_bytes(100, 8, 2, 4, 0)
+    assert lib.moe_expand_workspace_bytes(100, 8, 9, 4) == 0
+    ws = lib.moe_expand_workspace_bytes(100, 8, 2, 4)
+    f = lib.moe_expand_counts
+    base = [FAKE, FAKE, 100, 8, 2, 4, None, FAKE, FAKE, FAKE, None, FAKE, ws, None]
+    names = ["rx", "n", "C", "E", "k", "R", "place", "ec", "rc", "ro", "eo", "ws", "wsb", "st"]
+
+    def call(fn, base, names, **kw):
+        a = list(base)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return fn(*a)
+
+    assert call(f, base, names, n=None) == EINVAL      # the device row count is required
+    assert call(f, base, names, rx=None) == EINVAL
+    assert call(f, base, names, C=-1) == EINVAL
+    assert call(f, base, names, R=3) == EINVAL         # E % R != 0
+    assert call(f, base, names, k=17, E=32) == EUNSUP
+    assert call(f, base, names, wsb=ws - 1) == EWS
+    g = lib.moe_expand_permute
+    gb = [FAKE, FAKE, FAKE, FAKE, 100, 128, 8, 2, 4, 2, FAKE, ws, FAKE, 200, FAKE, FAKE, FAKE,
+          FAKE, None]
+    gn = ["rows", "rx", "rg", "n", "C", "H", "E", "k", "R", "bpe", "ws", "wsb", "ex", "excap",
+          "er", "ee", "eg", "rs", "st"]
+    assert call(g, gb, gn, n=None) == EINVAL
+    assert call(g, gb, gn, excap=-1) == EINVAL
+    assert call(g, gb, gn, excap=1 << 40) == EUNSUP
+    assert call(g, gb, gn, bpe=3) == EUNSUP
+    assert call(g, gb, gn, H=4) == EUNSUP
+    assert call(g, gb, gn, wsb=ws - 1) == EWS
+    assert call(g, gb, gn, rs=None) == EINVAL
+    assert call(g, gb, gn, ex=None) == EINVAL
+    assert call(g, gb, gn, C=0, wsb=lib.moe_expand_workspace_bytes(0, 8, 2, 4)) == 0  # no-op
+    r = lib.moe_expand_reduce
+    rb = [FAKE, None, FAKE, FAKE, 100, 128, 2, 2, FAKE, None]
+    rn = ["y", "w", "rs", "n", "C", "H", "k", "bpe", "out", "st"]
+    assert call(r, rb, rn, n=None) == EINVAL
+    assert call(r, rb, rn, bpe=4) == EUNSUP
+    assert call(r, rb, rn, k=17) == EUNSUP
+    assert call(r, rb, rn, H=4) == EUNSUP
+    assert call(r, rb, rn, out=None) == EINVAL
+    assert call(r, rb, rn, C=-2) == EINVAL
+    assert call(r, rb, rn, C=0) == 0                    # no-op
+
+
 def test_product_path_does_not_touch_oracle():
     """The package sources never import, load or name the oracle."""
     pkg = os.path.join(ROOT, "combine_top_router_select_amd")
