@@ -1,7 +1,7 @@
 """Benchmark of the per-GPU MoE dispatch/combine hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
-                    [--graph] [--overlap] [--no-cpu-baseline] [--calib-copy]
+                    [--receive] [--graph] [--overlap] [--no-cpu-baseline] [--calib-copy]
 
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input, with inputs resident in HBM: top-k routing -> send counts and
@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="deepseek_moe_16b")
     p.add_argument("--dedup", action="store_true")
+    p.add_argument("--receive", action="store_true",
+                   help="dedup mode: also run the receive side (per-expert expansion, identity "
+                        "experts, reduction) and combine the reduced rows with weight 1")
     p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     p.add_argument("--overlap", action="store_true",
                    help="run the co-selection counts on a second stream")
@@ -91,7 +94,7 @@ def calib_copy():
 class BufferSet:
     """Device buffers for one step (inputs resident, outputs preallocated)."""
 
-    def __init__(self, torch, ops, inp, w, dedup, dev):
+    def __init__(self, torch, ops, inp, w, dedup, dev, receive=False):
         T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
         N = T * k
         self.logits = torch.from_numpy(inp["logits"]).to(dev)
@@ -119,6 +122,18 @@ class BufferSet:
             self.disp["row_expert"] = torch.empty(N, dtype=i32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.W = torch.zeros((E, E), dtype=i32, device=dev)
+        if receive:  # the received rows are this set's dedup send buffer (capacity N)
+            self.ews = ops.expand_workspace(N, E, k, R, dev)
+            self.ecnt = {"expert_counts": torch.empty(E, dtype=i32, device=dev),
+                         "rank_counts": torch.empty(R, dtype=i32, device=dev),
+                         "rank_offsets": torch.empty(R + 1, dtype=i32, device=dev),
+                         "expert_offsets": torch.empty(E, dtype=i32, device=dev)}
+            self.exp = {"expanded": torch.empty((N, H), dtype=torch.bfloat16, device=dev),
+                        "exp_row": torch.empty(N, dtype=i32, device=dev),
+                        "exp_expert": torch.empty(N, dtype=i32, device=dev),
+                        "exp_gate": torch.empty(N, dtype=f32, device=dev),
+                        "row_slot": torch.empty((N, k), dtype=i32, device=dev)}
+            self.red = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
         self.ev_routed = torch.cuda.Event()
         self.ev_coselected = torch.cuda.Event()
 
@@ -132,9 +147,12 @@ class BufferSet:
         return tot
 
 
-def gpu_step(torch, ops, b, w, dedup, side=None):
+def gpu_step(torch, ops, b, w, dedup, side=None, receive=False):
     """One pass of the hot path.  With a side stream, the co-selection counts run
-    there, after the routing and concurrently with the rest."""
+    there, after the routing and concurrently with the rest.  With `receive`
+    (dedup mode), the dedup rows are expanded per expert, passed through
+    identity experts, reduced back to one row per received row, and those rows
+    are combined with weight 1."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
     main = torch.cuda.current_stream()
     ops.moe_route_topk(b.logits, k, b.idx, b.gate)
@@ -147,7 +165,15 @@ def gpu_step(torch, ops, b, w, dedup, side=None):
     c = ops.moe_send_counts(b.idx, E, R, b.place, dedup, ws=b.ws, out=b.cnt)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
     d = f(b.x, b.idx, b.gate, E, R, c["ws"], b.place, out=b.disp)
-    ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b.out)
+    if receive:
+        ops.moe_expand_counts(d["row_experts"], d["n_rows"], E, R, b.place, ws=b.ews, out=b.ecnt)
+        ex = ops.moe_expand_permute(d["send"], d["row_experts"], d["row_gates"], d["n_rows"], E,
+                                    R, b.ews, out=b.exp)
+        red = ops.moe_expand_reduce(ex["expanded"], ex["exp_gate"], ex["row_slot"], d["n_rows"],
+                                    out=b.red)
+        ops.moe_combine(red, None, d["slot_row"], out=b.out)
+    else:
+        ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b.out)
     if side is not None:
         main.wait_event(b.ev_coselected)
     else:
@@ -178,7 +204,7 @@ def counter_traffic(kernel, workload, mode):
     return None
 
 
-def cpu_baseline(inp, w, dedup, seconds):
+def cpu_baseline(inp, w, dedup, seconds, receive=False):
     """The CPU oracle as it stands (single host thread), on whole steps of the
     same workload, repeated until `seconds` have elapsed."""
     from oracle import oracle as O
@@ -189,7 +215,13 @@ def cpu_baseline(inp, w, dedup, seconds):
         idx, gate = O.route_topk(inp["logits"], w.top_k)
         f = O.dispatch_dedup if dedup else O.dispatch
         d = f(inp["x_bits"], idx, gate, w.n_experts, w.n_ranks, inp["placement"])
-        O.combine(d["send"], d["row_weight"], d["slot_row"])
+        if receive:
+            ex = O.expand_dedup(d["send"], d["row_experts"], d["row_gates"], d["n_rows"],
+                                w.n_experts, w.n_ranks, inp["placement"])
+            red = O.reduce_rows(ex["expanded"], ex["exp_gate"], ex["row_slot"], d["n_rows"])
+            O.combine(red, None, d["slot_row"])
+        else:
+            O.combine(d["send"], d["row_weight"], d["slot_row"])
         O.coselect(idx, w.n_experts, tokens=w.coselect_tokens)
         steps += 1
         el = time.perf_counter() - t0
@@ -216,16 +248,22 @@ def main():
     ops.lib()
     w = WL.get(a.workload)
     dedup = bool(a.dedup)
+    receive = bool(a.receive)
+    if receive and not dedup:
+        print("--receive needs --dedup (the receive side expands deduplicated rows)",
+              file=sys.stderr)
+        sys.exit(2)
     if dedup and "dedup" not in w.dispatch:
         print(f"warning: {w.name} is not normally run with dedup dispatch", file=sys.stderr)
     dev = torch.device("cuda:0")
     inp = WL.make_inputs(w)
     T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
 
-    first = BufferSet(torch, ops, inp, w, dedup, dev)
+    first = BufferSet(torch, ops, inp, w, dedup, dev, receive)
     per_set = first.nbytes()
     nsets = max(2, int(np.ceil(a.footprint_gib * 2 ** 30 / per_set)))
-    sets = [first] + [BufferSet(torch, ops, inp, w, dedup, dev) for _ in range(nsets - 1)]
+    sets = [first] + [BufferSet(torch, ops, inp, w, dedup, dev, receive)
+                      for _ in range(nsets - 1)]
     torch.cuda.synchronize()
 
     side = torch.cuda.Stream() if a.overlap else None
@@ -236,13 +274,13 @@ def main():
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for b in sets:       # warm the code paths once outside capture
-                gpu_step(torch, ops, b, w, dedup, side)
+                gpu_step(torch, ops, b, w, dedup, side, receive)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         for b in sets:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                gpu_step(torch, ops, b, w, dedup, side)
+                gpu_step(torch, ops, b, w, dedup, side, receive)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -250,7 +288,7 @@ def main():
         if graphs is not None:
             graphs[i % nsets].replay()
         else:
-            gpu_step(torch, ops, sets[i % nsets], w, dedup, side)
+            gpu_step(torch, ops, sets[i % nsets], w, dedup, side, receive)
 
     for i in range(a.warmup):
         step(i)
@@ -291,8 +329,24 @@ def main():
         comb_calls.append((L.moe_combine, (
             d["send"].data_ptr(), d["row_weight"].data_ptr(), d["slot_row"].data_ptr(), T, H, k,
             2, b.out.data_ptr(), st)))
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    for calls, e0, e1 in ((disp_calls, ev[0], ev[1]), (comb_calls, ev[2], ev[3])):
+    exp_calls, red_calls = [], []
+    if receive:
+        N = T * k
+        for b in order:
+            d, x = b.disp, b.exp
+            exp_calls.append((L.moe_expand_permute, (
+                d["send"].data_ptr(), d["row_experts"].data_ptr(), d["row_gates"].data_ptr(),
+                d["n_rows"].data_ptr(), N, H, E, k, R, 2, b.ews.data_ptr(), b.ews.numel(),
+                x["expanded"].data_ptr(), N, x["exp_row"].data_ptr(), x["exp_expert"].data_ptr(),
+                x["exp_gate"].data_ptr(), x["row_slot"].data_ptr(), st)))
+            red_calls.append((L.moe_expand_reduce, (
+                x["expanded"].data_ptr(), x["exp_gate"].data_ptr(), x["row_slot"].data_ptr(),
+                d["n_rows"].data_ptr(), N, H, k, 2, b.red.data_ptr(), st)))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    runs = [(disp_calls, ev[0], ev[1]), (comb_calls, ev[2], ev[3])]
+    if receive:
+        runs += [(exp_calls, ev[4], ev[5]), (red_calls, ev[6], ev[7])]
+    for calls, e0, e1 in runs:
         torch.cuda.synchronize()
         torch.cuda._sleep(20_000_000)  # the GPU waits while the launches queue up
         e0.record()
@@ -304,6 +358,8 @@ def main():
     torch.cuda.synchronize()
     t_disp = ev[0].elapsed_time(ev[1]) * 1e-3 / K2
     t_comb = ev[2].elapsed_time(ev[3]) * 1e-3 / K2
+    t_exp = ev[4].elapsed_time(ev[5]) * 1e-3 / K2 if receive else None
+    t_red = ev[6].elapsed_time(ev[7]) * 1e-3 / K2 if receive else None
 
     # rows actually written (N, or D for dedup)
     b = sets[0]
@@ -317,6 +373,16 @@ def main():
         dom = ("moe_combine", t_comb, comb_bytes)
     achieved = dom[2] / dom[1] / 1e9
     dc_gbps = (disp_bytes + comb_bytes) / (t_disp + t_comb) / 1e9
+    recv = None
+    if receive:
+        n_exp = int(b.ecnt["rank_offsets"][R].item())
+        exp_bytes = row_bytes * (n_rows + n_exp)  # read each received row once, write each copy
+        red_bytes = row_bytes * (n_exp + n_rows)  # read each expert output once, write each row
+        recv = {"expanded_rows": n_exp,
+                "expand_us": round(t_exp * 1e6, 2), "reduce_us": round(t_red * 1e6, 2),
+                "expand_GBps": round(exp_bytes / t_exp / 1e9, 1),
+                "reduce_GBps": round(red_bytes / t_red / 1e9, 1),
+                "algorithmic_bytes": {"expand": exp_bytes, "reduce": red_bytes}}
 
     res = {
         "metric": METRIC,
@@ -333,7 +399,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "hidden_dim": H, "n_experts": E,
                    "top_k": k, "n_ranks": R, "placement": w.placement,
-                   "dispatch": "dedup" if dedup else "nondedup",
+                   "dispatch": "dedup" if dedup else "nondedup", "receive_side": receive,
                    "bytes_per_element": 2, "graph": bool(a.graph),
                    "coselect_stream": "side" if a.overlap else "main",
                    "buffer_sets": nsets, "footprint_MiB": round(nsets * per_set / 2 ** 20)},
@@ -352,8 +418,10 @@ def main():
                               "metadata": meta_bytes},
         "device": torch.cuda.get_device_name(0),
     }
+    if recv is not None:
+        res["receive"] = recv
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, w, dedup, a.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(inp, w, dedup, a.cpu_seconds, receive)
     print(json.dumps(res), flush=True)
 
 

@@ -32,6 +32,65 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// The weighted sum of a token's rows for one chunk: NQ >= nrows rows are
+// loaded (all loads before any arithmetic; rows past nrows repeat the first
+// one and are not added), accumulated in fp32 from -0.0 in slot order, and
+// stored as bf16.
+template <int NQ, int NV>
+__device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int row_bytes,
+                                         int64_t chunk0, uint64_t um, int j0, int nrows, int rr,
+                                         float wr, int lane, uint8_t* __restrict__ dst) {
+  u32x4 y[NQ][NV];
+  float wq[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    int j = j0;
+    if (q < nrows) {
+      j = __ffsll((unsigned long long)um) - 1;
+      um &= um - 1;
+    }
+    const int p = bcast(rr, j);
+    wq[q] = bcastf(wr, j);
+    const uint8_t* src = rows + int64_t(p) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
+      off = off < row_bytes ? off : row_bytes - 16;
+      y[q][i] = MOE_COMBINE_NT ? load16_nt(src + off) : load16(src + off);
+    }
+  }
+  float acc[NV][8];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int h = 0; h < 8; ++h) acc[i][h] = -0.0f;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    if (q < nrows) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t u = y[q][i][h];
+          acc[i][2 * h] = __builtin_fmaf(wq[q], __uint_as_float(u << 16), acc[i][2 * h]);
+          acc[i][2 * h + 1] =
+              __builtin_fmaf(wq[q], __uint_as_float(u & 0xFFFF0000u), acc[i][2 * h + 1]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
+    if (off < row_bytes) {
+      u32x4 o;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(acc[i][2 * h], acc[i][2 * h + 1]);
+      store16(dst + off, o);
+    }
+  }
+}
+
 template <int NV, int KMAX>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
@@ -70,56 +129,22 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
   const int j0 = __ffsll((unsigned long long)um) - 1;
   const int rr = use ? r : bcast(r, j0);  // every lane names a valid row
   const float wr = w ? w[rr] : 1.0f;
-
-  u32x4 y[KMAX][NV];
-  float wq[KMAX];
-#pragma unroll
-  for (int q = 0; q < KMAX; ++q) {
-    int j = j0;
-    if (q < nrows) {
-      j = __ffsll((unsigned long long)um) - 1;
-      um &= um - 1;
-    }
-    const int p = bcast(rr, j);
-    wq[q] = bcastf(wr, j);
-    const uint8_t* src = rows + int64_t(p) * row_bytes;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
-      off = off < row_bytes ? off : row_bytes - 16;
-      y[q][i] = MOE_COMBINE_NT ? load16_nt(src + off) : load16(src + off);
-    }
+  // as few row loads as the token needs (nrows is wave-uniform): a token served
+  // by one or two rows - most received rows in the reduction - does not load
+  // KMAX rows
+  if constexpr (KMAX >= 1) {
+    if (nrows <= 1)
+      return sum_rows<1, NV>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
   }
-  float acc[NV][8];
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-#pragma unroll
-    for (int h = 0; h < 8; ++h) acc[i][h] = -0.0f;
-#pragma unroll
-  for (int q = 0; q < KMAX; ++q) {
-    if (q < nrows) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint32_t u = y[q][i][h];
-          acc[i][2 * h] = __builtin_fmaf(wq[q], __uint_as_float(u << 16), acc[i][2 * h]);
-          acc[i][2 * h + 1] =
-              __builtin_fmaf(wq[q], __uint_as_float(u & 0xFFFF0000u), acc[i][2 * h + 1]);
-        }
-      }
-    }
+  if constexpr (KMAX >= 2) {
+    if (nrows <= 2)
+      return sum_rows<2, NV>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
   }
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
-    if (off < row_bytes) {
-      u32x4 o;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(acc[i][2 * h], acc[i][2 * h + 1]);
-      store16(dst + off, o);
-    }
+  if constexpr (KMAX > 4) {
+    if (nrows <= 4)
+      return sum_rows<4, NV>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
   }
+  sum_rows<KMAX, NV>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
 }
 
 template <int NV, int KMAX>

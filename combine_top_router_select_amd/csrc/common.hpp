@@ -46,21 +46,47 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// Sum of the 16 bytes of v (v_sad_u8 against zero adds four bytes at a time).
+__device__ __forceinline__ int byte_sum(const u32x4& v) {
+  uint32_t s = __builtin_amdgcn_sad_u8(v.x, 0u, 0u);
+  s = __builtin_amdgcn_sad_u8(v.y, 0u, s);
+  s = __builtin_amdgcn_sad_u8(v.z, 0u, s);
+  s = __builtin_amdgcn_sad_u8(v.w, 0u, s);
+  return int(s);
+}
+
+// Keeps the first n bytes of v and zeroes the rest (n <= 0: all zero).
+__device__ __forceinline__ u32x4 keep_bytes(u32x4 v, int n) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int nb = clampi(n - 4 * i, 0, 4);
+    const uint32_t mk = nb >= 4 ? ~0u : ((1u << (8 * nb)) - 1u);
+    r[i] = v[i] & mk;
+  }
+  return r;
+}
+
 // Plan written by moe_send_counts, read by the dispatch kernels.  Per-column
 // arrays are column-major with the tile index padded to Bp = roundup(B, 16), so
-// that one thread can stream a column with 16-byte accesses.
+// that a column's tile counts come in 16-byte vectors of 16 tiles.
 //   header[0]        total rows (N, or D in dedup mode)
-//   base[CP][Bp]     int32: absolute first row, inside tile b, of position
-//                    column c (the expert in plain mode, the rank in dedup mode)
+//   gbase[CP][Bp/16] int32: first row, in the send buffer, of each group of 16
+//                    tiles of position column c (the expert in plain mode, the
+//                    rank in dedup mode)
 //   tcnt[C][Bp]      uint8: tokens of tile b that use column c (experts, then
 //                    ranks in dedup mode); at most 64, the tile size
 //   lslot[T][k]      uint32: (position column << 8) | rank of (t, j) among the
 //                    tile's earlier tokens that use the same position column
+// The row of (t, j) is gbase[c][b / 16] + (counts of tiles 16 (b / 16) .. b - 1
+// in column c) + rank, with b = t / 64.
 struct PlanLayout {
   int64_t tiles;      // B = ceil(T / 64)
   int64_t tiles_pad;  // Bp = roundup(B, 16)
+  int64_t groups;     // Bp / 16
   int cols;           // C: columns counted per tile (experts, + ranks in dedup mode)
   int pos_cols;       // CP: position columns (experts, or ranks in dedup mode)
+  int cbase;          // tcnt column of position column 0 (E in dedup mode, else 0)
   size_t base_off;    // byte offsets inside the workspace
   size_t tcnt_off;
   size_t lslot_off;
@@ -74,10 +100,12 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t tokens, int n_experts,
   PlanLayout p;
   p.tiles = (tokens + kTile - 1) / kTile;
   p.tiles_pad = (p.tiles + 15) / 16 * 16;
+  p.groups = p.tiles_pad / 16;
   p.cols = n_experts + (dedup ? n_ranks : 0);
   p.pos_cols = dedup ? n_ranks : n_experts;
+  p.cbase = dedup ? n_experts : 0;
   p.base_off = 256;
-  p.tcnt_off = align256(p.base_off + size_t(p.pos_cols) * size_t(p.tiles_pad) * 4);
+  p.tcnt_off = align256(p.base_off + size_t(p.pos_cols) * size_t(p.groups) * 4);
   p.lslot_off = align256(p.tcnt_off + size_t(p.cols) * size_t(p.tiles_pad));
   p.bytes = align256(p.lslot_off + size_t(tokens) * size_t(top_k) * 4);
   return p;

@@ -14,7 +14,9 @@
 // the bits below a lane is the token's rank among the tile's earlier users of
 // the column; popcount of the whole bitmap is the tile's count.  The tile
 // counts are then scanned over tiles, per column, into the absolute first row
-// of each tile in each column.  A row's position is base[column][tile] + rank,
+// of each tile in each column.  A row's position is the first row of the
+// tile's 16-tile group in its column (written by the scan) + the counts of the
+// group's earlier tiles (summed by the dispatch kernel) + rank,
 // which makes the send buffer order (rank, expert, token) - or (rank, token) -
 // stable and deterministic.  No global atomics anywhere.
 //
@@ -144,230 +146,9 @@ tile_counts_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k, int
 constexpr int kScanThreads = 1024;
 constexpr int kScanWaves = kScanThreads / kWave;
 constexpr int kMaxCols = MOE_MAX_EXPERTS + MOE_MAX_RANKS;
-constexpr int kMaxQ = 16;  // tile chunks per column
-constexpr int kKeep = 8;   // 16-tile vectors a scan thread keeps in registers
-
-// Sum of the 16 bytes of v (v_sad_u8 against zero adds four bytes at a time).
-__device__ __forceinline__ int byte_sum(const u32x4& v) {
-  uint32_t s = __builtin_amdgcn_sad_u8(v.x, 0u, 0u);
-  s = __builtin_amdgcn_sad_u8(v.y, 0u, s);
-  s = __builtin_amdgcn_sad_u8(v.z, 0u, s);
-  s = __builtin_amdgcn_sad_u8(v.w, 0u, s);
-  return int(s);
-}
-
-// Keeps the first n bytes of v and zeroes the rest (n <= 0: all zero).  The
-// padding tiles B..Bp-1 of a column are never written by tile_counts.
-__device__ __forceinline__ u32x4 keep_bytes(u32x4 v, int n) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nb = clampi(n - 4 * i, 0, 4);
-    const uint32_t mk = nb >= 4 ? ~0u : ((1u << (8 * nb)) - 1u);
-    r[i] = v[i] & mk;
-  }
-  return r;
-}
-
-// Writes the running first row of 16 consecutive tiles of one position column.
-__device__ __forceinline__ void put_bases(const u32x4& v, int32_t& run, int32_t* dst) {
-  int32_t o[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    o[i] = run;
-    run += int32_t((v[i / 4] >> (8 * (i % 4))) & 255u);
-  }
-  u32x4* d4 = reinterpret_cast<u32x4*>(dst);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    d4[i] = u32x4{uint32_t(o[4 * i]), uint32_t(o[4 * i + 1]), uint32_t(o[4 * i + 2]),
-                  uint32_t(o[4 * i + 3])};
-}
-
-// One workgroup.  Each column's Bp/16 tile vectors are split into Q chunks,
-// one (column, chunk) unit per thread: chunk sums, then per chunk the sum of
-// the column's earlier chunks and the column total; experts are ordered by
-// (rank, id) with a counting sort and one block-wide scan; then every unit of
-// a position column writes the absolute first row of each of its tiles.
-// KEEP: each thread owns at most one unit of at most kKeep vectors and keeps
-// them in registers between the two passes; otherwise units loop and the
-// second pass loads its vectors again (large inputs only).
-template <bool DEDUP, bool KEEP>
-__global__ void __launch_bounds__(kScanThreads)
-plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, int E, int R,
-                 const int32_t* __restrict__ place, int m, int32_t* __restrict__ expert_counts,
-                 int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
-                 int32_t* __restrict__ expert_offsets, int32_t* __restrict__ header,
-                 int32_t* __restrict__ base) {
-  __shared__ int32_t s_part[kMaxCols];  // [c][q] chunk sums
-  __shared__ int32_t s_pre[kMaxCols];   // [c][q] sums of the column's earlier chunks
-  __shared__ int32_t s_tot[kMaxCols];   // column totals
-  __shared__ int32_t s_colbase[MOE_MAX_EXPERTS];
-  __shared__ int32_t s_sorted[MOE_MAX_EXPERTS];
-  __shared__ uint64_t s_rmask[MOE_MAX_RANKS][MOE_MAX_EXPERTS / kWave];
-  __shared__ int32_t s_rcnt[MOE_MAX_RANKS];
-  __shared__ int32_t s_rstart[MOE_MAX_RANKS + 1];
-  __shared__ int32_t s_ro[MOE_MAX_RANKS + 1];
-  __shared__ int32_t s_wsum[kScanWaves];
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int w = tid / kWave;
-  const int C = E + (DEDUP ? R : 0);
-  const int cbase = DEDUP ? E : 0;  // first position column among the counted ones
-  const int nvec = Bp / 16;         // 16-tile vectors per column
-  const int units = C * Q;
-  const int EW = (E + kWave - 1) / kWave;  // 64-expert words
-  const bool sorted_by_id = DEDUP || place == nullptr;  // (rank, id) order == id order
-  const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);
-
-  // 1. chunk sums (the loads go out first, before anything else)
-  u32x4 keep[KEEP ? kKeep : 1];
-  int kv0 = 0, kv1 = 0;
-  if (KEEP) {
-    if (tid < units) {
-      const int c = tid / Q, q = tid - (tid / Q) * Q;
-      kv0 = int(int64_t(nvec) * q / Q);
-      kv1 = int(int64_t(nvec) * (q + 1) / Q);
-#pragma unroll
-      for (int i = 0; i < kKeep; ++i) {
-        const int vi = kv0 + i < kv1 ? kv0 + i : kv1 - 1;  // every unit has a vector
-        keep[i] = g4[size_t(c) * nvec + vi];
-      }
-    }
-  }
-  int my_rank = 0;  // rank of the expert this thread owns (place is wave-uniform)
-  if (tid < E) my_rank = place ? clampi(place[tid], 0, R - 1) : tid / m;
-  if (tid < MOE_MAX_RANKS) s_rcnt[tid] = 0;
-  for (int i = tid; i < MOE_MAX_RANKS * (MOE_MAX_EXPERTS / kWave); i += kScanThreads)
-    (&s_rmask[0][0])[i] = 0ull;
-  if (KEEP) {
-    if (tid < units) {
-      int sum = 0;
-#pragma unroll
-      for (int i = 0; i < kKeep; ++i) {
-        keep[i] = keep_bytes(keep[i], kv0 + i < kv1 ? B - 16 * (kv0 + i) : 0);
-        sum += byte_sum(keep[i]);
-      }
-      s_part[tid] = sum;
-    }
-  } else {
-    for (int u = tid; u < units; u += kScanThreads) {
-      const int c = u / Q, q = u - (u / Q) * Q;
-      const int v0 = int(int64_t(nvec) * q / Q), v1 = int(int64_t(nvec) * (q + 1) / Q);
-      int sum = 0;
-      for (int vi = v0; vi < v1; ++vi)
-        sum += byte_sum(keep_bytes(g4[size_t(c) * nvec + vi], B - 16 * vi));
-      s_part[u] = sum;
-    }
-  }
-  __syncthreads();
-  if (!sorted_by_id && tid < E) {
-    atomicOr(reinterpret_cast<unsigned long long*>(&s_rmask[my_rank][tid / kWave]),
-             1ull << (tid % kWave));
-    atomicAdd(&s_rcnt[my_rank], 1);
-  }
-
-  // 2. chunk prefixes and column totals
-  for (int u = tid; u < units; u += kScanThreads) {
-    const int c = u / Q, q = u - (u / Q) * Q;
-    const int32_t* part = s_part + c * Q;
-    int32_t pre = 0;
-#pragma unroll
-    for (int qq = 0; qq < kMaxQ; ++qq) pre += qq < q ? part[qq < Q ? qq : 0] : 0;
-    s_pre[u] = pre;
-    if (q == Q - 1) s_tot[c] = pre + part[q];
-  }
-  __syncthreads();
-  // start of each rank in the (rank, id) expert order
-  if (!sorted_by_id && w == 0) {
-    const int v = lane < R ? s_rcnt[lane] : 0;
-    const int incl = wave_incl_scan(v);
-    if (lane < R) s_rstart[lane] = incl - v;
-  }
-  __syncthreads();
-
-  // 3. the expert order: expert e goes to slot `key` of the (rank, id) order
-  int key = tid;
-  if (!sorted_by_id && tid < E) {
-    const uint64_t* mk = s_rmask[my_rank];
-    const int wi = tid / kWave;
-    int below = __popcll(mk[wi] & lanemask_lt());
-#pragma unroll
-    for (int q = 0; q < MOE_MAX_EXPERTS / kWave; ++q) below += q < wi ? __popcll(mk[q]) : 0;
-    key = s_rstart[my_rank] + below;
-  }
-  if (!DEDUP && tid < E) s_sorted[key] = s_tot[tid];
-  __syncthreads();
-
-  // 4. exclusive scan in that order (experts, or ranks in dedup mode)
-  const int nscan = DEDUP ? R : E;
-  const int nsw = (nscan + kWave - 1) / kWave;
-  int v = 0;
-  if (tid < nscan) v = DEDUP ? s_tot[E + tid] : s_sorted[tid];
-  int incl = 0;
-  if (w < nsw) {
-    incl = wave_incl_scan(v);
-    if (lane == kWave - 1) s_wsum[w] = incl;
-  }
-  __syncthreads();
-  int carry = 0;
-#pragma unroll
-  for (int q = 0; q < kScanWaves; ++q) carry += q < w ? s_wsum[q < EW ? q : 0] : 0;
-  const int excl = carry + incl - v;
-  if (tid < nscan) s_sorted[tid] = excl;  // scanned value of slot tid
-  if (tid == 0) {
-    int total = 0;
-#pragma unroll
-    for (int q = 0; q < kScanWaves; ++q) total += q < nsw ? s_wsum[q] : 0;
-    s_ro[R] = total;
-    header[0] = total;
-  }
-  __syncthreads();
-
-  // 5. counts, offsets and column bases
-  if (tid < E) expert_counts[tid] = s_tot[tid];
-  if (!DEDUP) {
-    if (tid < E) {
-      const int off = s_sorted[key];
-      s_colbase[tid] = off;
-      if (expert_offsets) expert_offsets[tid] = off;
-    }
-    if (tid < R) {
-      // the first expert of rank r in the (rank, id) order
-      const int first = sorted_by_id ? tid * m : s_rstart[tid];
-      s_ro[tid] = first < E ? s_sorted[first] : s_ro[R];
-    }
-  } else if (tid < R) {
-    s_ro[tid] = s_sorted[tid];
-    s_colbase[tid] = s_sorted[tid];
-  }
-  __syncthreads();
-  if (tid < R) rank_counts[tid] = s_ro[tid + 1] - s_ro[tid];
-  if (tid <= R) rank_offsets[tid] = s_ro[tid];
-
-  // 6. absolute first row of every (position column, tile)
-  if (KEEP) {
-    if (tid < units && tid >= cbase * Q) {
-      const int c = tid / Q;
-      const int cp = c - cbase;
-      int32_t run = s_colbase[cp] + s_pre[tid];
-      int32_t* col = base + size_t(cp) * Bp;
-#pragma unroll
-      for (int i = 0; i < kKeep; ++i)
-        if (kv0 + i < kv1) put_bases(keep[i], run, col + 16 * (kv0 + i));
-    }
-  } else {
-    for (int u = cbase * Q + tid; u < units; u += kScanThreads) {
-      const int c = u / Q, q = u - (u / Q) * Q;
-      const int cp = c - cbase;
-      const int v0 = int(int64_t(nvec) * q / Q), v1 = int(int64_t(nvec) * (q + 1) / Q);
-      int32_t run = s_colbase[cp] + s_pre[u];
-      int32_t* col = base + size_t(cp) * Bp;
-      for (int vi = v0; vi < v1; ++vi)
-        put_bases(keep_bytes(g4[size_t(c) * nvec + vi], B - 16 * vi), run, col + 16 * vi);
-    }
-  }
-}
+constexpr int kMaxQ = 16;  // lanes per column (one DPP row at most)
+constexpr int kMaxKV = 16; // tile vectors per lane held in registers
+constexpr int kBatch = 8;  // vectors loaded together by the looping variant
 
 // Inclusive scan inside aligned segments of Q consecutive lanes (Q a power of
 // two <= 16, so a segment never leaves its 16-lane DPP row).
@@ -384,54 +165,120 @@ __device__ __forceinline__ int segment_incl_scan(int v, int Q, int lane) {
   return v;
 }
 
-// The common cases in one pass with two barriers: plain mode with contiguous
-// placement (the scan order is the expert id order) and dedup mode (the scan
-// order is the rank order).  One (column, chunk) unit per thread, Q chunks per
-// column (a power of two) on consecutive lanes, each of at most KV vectors; the
-// workgroup has just enough waves for the units.
-// A unit's byte sum is scanned inside its column's lane segment (DPP); the
-// segment's last lane carries the column total into one block-wide scan over
-// all units, whose exclusive value at any unit of a column is the column's
-// first row; each unit then writes its tiles' bases from the vectors it kept.
-template <bool DEDUP, int KV>
+// One workgroup turns the per-tile counts into the plan's group bases: for
+// every position column and every group of 16 tiles (one 16-byte vector of
+// tile counts), the first row of that group in the send buffer.
+//  A. Column sums.  KV > 0: a column's vectors are dealt round-robin to Q
+//     consecutive lanes (lane q takes vectors q, q + Q, ...: each load
+//     instruction covers Q x 16 contiguous bytes of the column); per round a
+//     segmented DPP scan gives each vector the sum of the column's earlier
+//     vectors.  KV = 0 (very large plans): one lane per column, looping.
+//  B. The columns in scan order - expert id (plain, contiguous placement),
+//     rank (dedup), or (rank, id) for plain dispatch with an explicit
+//     placement (RANKED: a counting sort with rank bitmasks) - and one
+//     block-wide exclusive scan (DPP wave scans) give each column's first row.
+//  C. Group bases = column first row + earlier vectors; counts and offsets.
+// No global atomics: the plan is a pure function of the counts.
+template <bool DEDUP, bool RANKED, int KV>
 __global__ void __launch_bounds__(kScanThreads)
-plan_scan_fast_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, int E, int R, int m,
-                      int32_t* __restrict__ expert_counts, int32_t* __restrict__ rank_counts,
-                      int32_t* __restrict__ rank_offsets, int32_t* __restrict__ expert_offsets,
-                      int32_t* __restrict__ header, int32_t* __restrict__ base) {
+plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, int E, int R,
+                 const int32_t* __restrict__ place, int m, int32_t* __restrict__ expert_counts,
+                 int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
+                 int32_t* __restrict__ expert_offsets, int32_t* __restrict__ header,
+                 int32_t* __restrict__ vbase) {
+  __shared__ int32_t s_tot[kMaxCols];           // column totals
+  __shared__ int32_t s_colbase[MOE_MAX_EXPERTS];  // first row of each position column
+  __shared__ int32_t s_scan[MOE_MAX_EXPERTS];     // exclusive scan by scan slot
   __shared__ int32_t s_wsum[kScanWaves];
-  __shared__ int32_t s_ro[MOE_MAX_RANKS + 1];
+  __shared__ uint64_t s_rmask[RANKED ? MOE_MAX_RANKS : 1][MOE_MAX_EXPERTS / kWave];
+  __shared__ int32_t s_rcnt[MOE_MAX_RANKS];
+  __shared__ int32_t s_rstart[MOE_MAX_RANKS];
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = tid / kWave;
-  const int nwaves = blockDim.x / kWave;
+  const int nthreads = blockDim.x;
+  const int nwaves = nthreads / kWave;
   const int C = E + (DEDUP ? R : 0);
-  const int cbase = DEDUP ? E : 0;
-  const int nvec = Bp / 16;
-  const int units = C * Q;
-  const bool active = tid < units;
-  const int c = tid / Q, q = tid & (Q - 1);
-  const int v0 = int(int64_t(nvec) * q / Q), v1 = int(int64_t(nvec) * (q + 1) / Q);
+  const int cbase = DEDUP ? E : 0;  // first position column among the counted ones
+  const int CP = DEDUP ? R : E;     // position columns = scan slots
+  const int nvec = Bp / 16;         // 16-tile vectors per column
   const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);
-  u32x4 keep[KV];
+
+  // A. column sums; the loads go out first
+  constexpr int NK = KV > 0 ? KV : 1;
+  const int units = C * Q;
+  const bool active = KV > 0 && tid < units;
+  const int c = tid / Q, q = tid & (Q - 1);
+  int pre[NK];
+  if (KV > 0) {
+    u32x4 v[NK];
 #pragma unroll
-  for (int i = 0; i < KV; ++i) {
-    const int vi = v0 + i < v1 ? v0 + i : v1 - 1;  // every unit has a vector
-    keep[i] = g4[size_t(active ? c : 0) * nvec + vi];
-  }
-  int part = 0;
+    for (int i = 0; i < NK; ++i) {
+      const int vi = q + Q * i;
+      v[i] = g4[size_t(active ? c : 0) * nvec + (vi < nvec ? vi : nvec - 1)];
+    }
+    int run = 0;
 #pragma unroll
-  for (int i = 0; i < KV; ++i) {
-    keep[i] = keep_bytes(keep[i], v0 + i < v1 ? B - 16 * (v0 + i) : 0);
-    part += byte_sum(keep[i]);
+    for (int i = 0; i < NK; ++i) {
+      const int vi = q + Q * i;
+      const int vs = (active && vi < nvec) ? byte_sum(keep_bytes(v[i], B - 16 * vi)) : 0;
+      const int incl = segment_incl_scan(vs, Q, lane);
+      pre[i] = run + incl - vs;
+      run += __shfl(incl, (lane & ~(Q - 1)) + Q - 1, kWave);  // the round's column total
+    }
+    if (active && q == 0) s_tot[c] = run;
+  } else {
+    for (int cc = tid; cc < C; cc += nthreads) {
+      int sum = 0;
+      for (int b0 = 0; b0 < nvec; b0 += kBatch) {
+        u32x4 t[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          t[i] = g4[size_t(cc) * nvec + (b0 + i < nvec ? b0 + i : nvec - 1)];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          sum += b0 + i < nvec ? byte_sum(keep_bytes(t[i], B - 16 * (b0 + i))) : 0;
+      }
+      s_tot[cc] = sum;
+    }
   }
-  part = active ? part : 0;
-  const int incl_c = segment_incl_scan(part, Q, lane);
-  const int tot = __shfl(incl_c, (lane & ~(Q - 1)) + Q - 1, kWave);  // column total
-  const int pre = incl_c - part;                                      // earlier chunks
-  const bool pos = active && c >= cbase;
-  const int v = (pos && q == Q - 1) ? tot : 0;
-  const int incl = wave_incl_scan(v);
+  int my_rank = 0;
+  if (RANKED) {
+    if (tid < E) my_rank = clampi(place[tid], 0, R - 1);
+    if (tid < MOE_MAX_RANKS) s_rcnt[tid] = 0;
+    for (int i = tid; i < MOE_MAX_RANKS * (MOE_MAX_EXPERTS / kWave); i += nthreads)
+      (&s_rmask[0][0])[i] = 0ull;
+  }
+  __syncthreads();
+
+  // B. scan order and the block-wide scan
+  int key = tid;  // scan slot of expert tid (RANKED), else slot tid = column cbase + tid
+  if (RANKED) {
+    if (tid < E) {
+      atomicOr(reinterpret_cast<unsigned long long*>(&s_rmask[my_rank][tid / kWave]),
+               1ull << (tid % kWave));
+      atomicAdd(&s_rcnt[my_rank], 1);
+    }
+    __syncthreads();
+    if (w == 0) {
+      const int v = lane < R ? s_rcnt[lane] : 0;
+      const int incl = wave_incl_scan(v);
+      if (lane < R) s_rstart[lane] = incl - v;
+    }
+    __syncthreads();
+    if (tid < E) {
+      const uint64_t* mk = s_rmask[my_rank];
+      const int wi = tid / kWave;
+      int below = __popcll(mk[wi] & lanemask_lt());
+#pragma unroll
+      for (int qq = 0; qq < MOE_MAX_EXPERTS / kWave; ++qq) below += qq < wi ? __popcll(mk[qq]) : 0;
+      key = s_rstart[my_rank] + below;
+      s_scan[key] = s_tot[tid];
+    }
+    __syncthreads();
+  }
+  const int sv = tid < CP ? (RANKED ? s_scan[tid] : s_tot[cbase + tid]) : 0;
+  const int incl = wave_incl_scan(sv);
   if (lane == kWave - 1) s_wsum[w] = incl;
   __syncthreads();
   int carry = 0, total = 0;
@@ -441,35 +288,67 @@ plan_scan_fast_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, in
     carry += i < w ? x : 0;
     total += x;
   }
-  const int colbase = carry + incl - v;  // first row of this unit's column
-  if (active && q == 0) {
-    if (c < E) expert_counts[c] = tot;
-    if (DEDUP && c >= E) {
-      rank_counts[c - E] = tot;
-      rank_offsets[c - E] = colbase;
+  const int excl = carry + incl - sv;  // first row of scan slot tid
+  if (RANKED) {
+    __syncthreads();  // every s_scan read above is done
+    if (tid < CP) s_scan[tid] = excl;
+    __syncthreads();
+    if (tid < E) s_colbase[tid] = s_scan[key];
+  } else if (tid < CP) {
+    s_colbase[tid] = excl;
+  }
+  __syncthreads();
+
+  // C. outputs
+  if (tid < E) expert_counts[tid] = s_tot[tid];
+  if (!DEDUP && expert_offsets && tid < E) expert_offsets[tid] = s_colbase[tid];
+  if (tid < R) {
+    int start, next;
+    if (DEDUP) {
+      start = s_colbase[tid];
+      next = start + s_tot[E + tid];
+    } else if (RANKED) {
+      const int s0 = s_rstart[tid], s1 = tid + 1 < R ? s_rstart[tid + 1] : E;
+      start = s0 < E ? s_scan[s0] : total;
+      next = s1 < E ? s_scan[s1] : total;
+    } else {
+      start = s_colbase[tid * m];
+      next = tid + 1 < R ? s_colbase[(tid + 1) * m] : total;
     }
-    if (!DEDUP) {
-      if (expert_offsets) expert_offsets[c] = colbase;
-      if (c % m == 0) s_ro[c / m] = colbase;
-    }
+    rank_offsets[tid] = start;
+    rank_counts[tid] = next - start;
   }
   if (tid == 0) {
-    header[0] = total;
     rank_offsets[R] = total;
-    if (!DEDUP) s_ro[R] = total;
+    header[0] = total;
   }
-  if (pos) {
-    int32_t run = colbase + pre;
-    int32_t* col = base + size_t(c - cbase) * Bp;
+  if (KV > 0) {
+    if (active && c >= cbase) {
+      const int cb = s_colbase[c - cbase];
+      int32_t* col = vbase + size_t(c - cbase) * nvec;
 #pragma unroll
-    for (int i = 0; i < KV; ++i)
-      if (v0 + i < v1) put_bases(keep[i], run, col + 16 * (v0 + i));
-  }
-  if (!DEDUP) {
-    __syncthreads();
-    if (tid < R) {
-      rank_offsets[tid] = s_ro[tid];
-      rank_counts[tid] = s_ro[tid + 1] - s_ro[tid];
+      for (int i = 0; i < NK; ++i) {
+        const int vi = q + Q * i;
+        if (vi < nvec) col[vi] = cb + pre[i];
+      }
+    }
+  } else {
+    for (int cc = cbase + tid; cc < C; cc += nthreads) {
+      int run = s_colbase[cc - cbase];
+      int32_t* col = vbase + size_t(cc - cbase) * nvec;
+      for (int b0 = 0; b0 < nvec; b0 += kBatch) {
+        u32x4 t[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          t[i] = g4[size_t(cc) * nvec + (b0 + i < nvec ? b0 + i : nvec - 1)];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          if (b0 + i < nvec) {
+            col[b0 + i] = run;
+            run += byte_sum(keep_bytes(t[i], B - 16 * (b0 + i)));
+          }
+        }
+      }
     }
   }
 }
@@ -483,7 +362,7 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
   const PlanLayout pl = plan_layout(T, E, k, R, dedup);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int32_t* header = reinterpret_cast<int32_t*>(ws);
-  int32_t* base = reinterpret_cast<int32_t*>(ws + pl.base_off);
+  int32_t* vbase = reinterpret_cast<int32_t*>(ws + pl.base_off);
   uint8_t* tcnt = ws + pl.tcnt_off;
   uint32_t* lslot = reinterpret_cast<uint32_t*>(ws + pl.lslot_off);
   const int m = E / R;
@@ -504,49 +383,44 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
   const int B = int(pl.tiles);
   const int Bp = int(pl.tiles_pad);
   const int nvec = Bp / 16;
-  // fast path: chunks per column a power of two, one unit per thread, at most
-  // kKeep vectors per unit; plain mode only with contiguous placement
-  if (nvec > 0 && (dedup || place == nullptr)) {
-    int Qf = kMaxQ;
-    while (Qf > 1 && (pl.cols * Qf > kScanThreads || Qf > nvec)) Qf >>= 1;
-    const int kv = (nvec + Qf - 1) / Qf;
-    if (pl.cols * Qf <= kScanThreads && kv <= kKeep) {
-      const int threads = (pl.cols * Qf + kWave - 1) / kWave * kWave;
-#define MOE_FAST_SCAN(D, KV)                                                                     \
-  hipLaunchKernelGGL((plan_scan_fast_kernel<D, KV>), dim3(1), dim3(threads), 0, stream, tcnt, B, \
-                     Bp, Qf, E, R, m, expert_counts, rank_counts, rank_offsets, expert_offsets,   \
-                     header, base)
-#define MOE_FAST_SCAN_KV(D)       \
-  if (kv <= 1) MOE_FAST_SCAN(D, 1); \
-  else if (kv <= 2) MOE_FAST_SCAN(D, 2); \
-  else if (kv <= 4) MOE_FAST_SCAN(D, 4); \
-  else MOE_FAST_SCAN(D, 8);
-      if (dedup) {
-        MOE_FAST_SCAN_KV(true)
-      } else {
-        MOE_FAST_SCAN_KV(false)
-      }
-#undef MOE_FAST_SCAN_KV
-#undef MOE_FAST_SCAN
-      return hipGetLastError();
-    }
+  const int CP = pl.pos_cols;
+  const bool ranked = !dedup && place != nullptr;
+  // lanes per column: a power of two <= 16 with every column's lanes in one
+  // workgroup; then vectors per lane
+  int Q = kMaxQ;
+  while (Q > 1 && (pl.cols * Q > kScanThreads || Q > nvec)) Q >>= 1;
+  const int kv = nvec > 0 ? (nvec + Q - 1) / Q : 1;
+  int KV = kv <= 1 ? 1 : kv <= 2 ? 2 : kv <= 4 ? 4 : kv <= 8 ? 8 : kv <= kMaxKV ? 16 : 0;
+  if (pl.cols * Q > kScanThreads || nvec == 0) KV = 0;  // no tiles: nothing to load
+  if (KV == 0) Q = 1;
+  int threads = kScanThreads;
+  if (KV > 0) {
+    int need = pl.cols * Q;
+    need = need > CP ? need : CP;
+    if (ranked) need = need > E ? need : E;
+    threads = (need + kWave - 1) / kWave * kWave;
   }
-  int Q = kScanThreads / pl.cols;
-  Q = Q < 1 ? 1 : (Q > kMaxQ ? kMaxQ : Q);
-  Q = Q < nvec ? Q : (nvec > 0 ? nvec : 1);
-  // one unit per thread, each of at most kKeep vectors
-  const bool keep = nvec > 0 && pl.cols * Q <= kScanThreads && (nvec + Q - 1) / Q <= kKeep;
-#define MOE_SCAN_LAUNCH(D, K)                                                                   \
-  hipLaunchKernelGGL((plan_scan_kernel<D, K>), dim3(1), dim3(kScanThreads), 0, stream, tcnt, B,  \
+#define MOE_SCAN_LAUNCH(D, RK, K)                                                               \
+  hipLaunchKernelGGL((plan_scan_kernel<D, RK, K>), dim3(1), dim3(threads), 0, stream, tcnt, B,   \
                      Bp, Q, E, R, place, m, expert_counts, rank_counts, rank_offsets,            \
-                     expert_offsets, header, base)
-  if (dedup) {
-    if (keep) MOE_SCAN_LAUNCH(true, true);
-    else MOE_SCAN_LAUNCH(true, false);
-  } else {
-    if (keep) MOE_SCAN_LAUNCH(false, true);
-    else MOE_SCAN_LAUNCH(false, false);
+                     expert_offsets, header, vbase)
+#define MOE_SCAN_KV(D, RK)                      \
+  switch (KV) {                                 \
+    case 0: MOE_SCAN_LAUNCH(D, RK, 0); break;   \
+    case 1: MOE_SCAN_LAUNCH(D, RK, 1); break;   \
+    case 2: MOE_SCAN_LAUNCH(D, RK, 2); break;   \
+    case 4: MOE_SCAN_LAUNCH(D, RK, 4); break;   \
+    case 8: MOE_SCAN_LAUNCH(D, RK, 8); break;   \
+    default: MOE_SCAN_LAUNCH(D, RK, 16); break; \
   }
+  if (dedup) {
+    MOE_SCAN_KV(true, false)
+  } else if (ranked) {
+    MOE_SCAN_KV(false, true)
+  } else {
+    MOE_SCAN_KV(false, false)
+  }
+#undef MOE_SCAN_KV
 #undef MOE_SCAN_LAUNCH
   return hipGetLastError();
 }

@@ -10,8 +10,8 @@
 // conventional dispatcher.
 //
 // Design: one wave per (token, row chunk).  Lanes j < k first resolve slot j's
-// destination row from the plan (base[column][tile] + the slot's rank inside
-// the tile), then the wave
+// destination row from the plan (the tile's first row in the slot's column +
+// the slot's rank inside the tile), then the wave
 // reads its chunk of x[t] once into registers (16-byte loads, 1 KiB per wave
 // instruction) and writes it to each destination row.  Every access is a full,
 // contiguous row segment, so reads and writes are perfectly coalesced; nothing
@@ -35,6 +35,17 @@ __device__ __forceinline__ void load_chunk(u32x4 (&v)[NV], const uint8_t* row, i
   }
 }
 
+// First row of position column `col` in tile b: the scan's base of the tile's
+// 16-tile group plus the counts of the group's earlier tiles (one 16-byte load
+// of the column's tile counts).
+__device__ __forceinline__ int tile_first_row(const int32_t* __restrict__ gbase,
+                                              const uint8_t* __restrict__ tcnt, int64_t Bp,
+                                              int64_t G, int tcol, int col, int64_t b) {
+  const int g = int(gbase[col * G + (b >> 4)]);
+  const u32x4 tv = load16(tcnt + tcol * Bp + (b & ~int64_t(15)));
+  return g + byte_sum(keep_bytes(tv, int(b & 15)));
+}
+
 template <int NV, bool NT>
 __device__ __forceinline__ void store_chunk(const u32x4 (&v)[NV], uint8_t* dst, int64_t chunk0,
                                             int row_bytes, int lane) {
@@ -56,8 +67,9 @@ __device__ __forceinline__ void store_chunk(const u32x4 (&v)[NV], uint8_t* dst, 
 template <int NV, bool NT, bool PAD>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint8_t* __restrict__ x, const float* __restrict__ gate, int64_t T,
-                int row_bytes, int k, int cpr, const int32_t* __restrict__ base,
-                const uint32_t* __restrict__ lslot, int64_t Bp, uint8_t* __restrict__ send,
+                int row_bytes, int k, int cpr, const int32_t* __restrict__ gbase,
+                const uint8_t* __restrict__ tcnt, const uint32_t* __restrict__ lslot, int64_t Bp,
+                int64_t G, uint8_t* __restrict__ send,
                 int32_t* __restrict__ row_token, int32_t* __restrict__ row_expert,
                 float* __restrict__ row_weight, int32_t* __restrict__ slot_row,
                 const int32_t* __restrict__ n_valid, int64_t out_cap) {
@@ -79,7 +91,7 @@ dispatch_kernel(const uint8_t* __restrict__ x, const float* __restrict__ gate, i
   load_chunk<NV>(v, x + t * row_bytes, chunk0, row_bytes, lane);
   const bool has = !PAD || code != kNoSlot;
   const int e = has ? int(code >> 8) : 0;
-  const int pos = base[e * Bp + t / kTile] + int(code & 255u);
+  const int pos = tile_first_row(gbase, tcnt, Bp, G, e, e, t / kTile) + int(code & 255u);
   const bool ok = has && (!PAD || pos < out_cap);
   const uint64_t okm = __ballot(lane < k && ok);
   for (int j = 0; j < k; ++j) {
@@ -104,8 +116,9 @@ __global__ void __launch_bounds__(256)
 dispatch_dedup_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
                       const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k,
                       int R, const int32_t* __restrict__ place, int m, int cpr,
-                      const int32_t* __restrict__ base, const uint32_t* __restrict__ lslot,
-                      int64_t Bp, const int32_t* __restrict__ header, uint8_t* __restrict__ send,
+                      const int32_t* __restrict__ gbase, const uint8_t* __restrict__ tcnt,
+                      const uint32_t* __restrict__ lslot, int64_t Bp, int64_t G,
+                      const int32_t* __restrict__ header, uint8_t* __restrict__ send,
                       int32_t* __restrict__ row_token, int32_t* __restrict__ row_experts,
                       float* __restrict__ row_gates, float* __restrict__ row_weight,
                       int32_t* __restrict__ slot_row, int32_t* __restrict__ n_rows) {
@@ -123,7 +136,8 @@ dispatch_dedup_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__
   u32x4 v[NV];
   load_chunk<NV>(v, x + t * row_bytes, chunk0, row_bytes, lane);
   const int r_own = int(code >> 8);
-  const int pos = base[r_own * Bp + t / kTile] + int(code & 255u);
+  const int pos = tile_first_row(gbase, tcnt, Bp, G, E + r_own, r_own, t / kTile) +
+                  int(code & 255u);
   const int r = lane < k ? r_own : -1;  // lanes >= k match no slot below
   // Per slot: is it the first slot of its rank (the row's leader)?  Its column
   // among the rank's experts (ascending id), the rank's slot count, and its
@@ -195,7 +209,8 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
   const PlanLayout pl = plan_layout(T, E, k, R, dedup);
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
   const int32_t* header = reinterpret_cast<const int32_t*>(ws);
-  const int32_t* base = reinterpret_cast<const int32_t*>(ws + pl.base_off);
+  const int32_t* gbase = reinterpret_cast<const int32_t*>(ws + pl.base_off);
+  const uint8_t* tcnt = ws + pl.tcnt_off;
   const uint32_t* lslot = reinterpret_cast<const uint32_t*>(ws + pl.lslot_off);
   const int chunk = NV * kWave * 16;
   const int cpr = (row_bytes + chunk - 1) / chunk;
@@ -206,13 +221,13 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
   if (!dedup) {
     if (T == 0) return hipSuccess;
     hipLaunchKernelGGL((dispatch_kernel<NV, NT, false>), dim3(unsigned(blocks)), dim3(256), 0,
-                       stream, static_cast<const uint8_t*>(x), gate, T, row_bytes, k, cpr, base,
-                       lslot, pl.tiles_pad, static_cast<uint8_t*>(send), row_token, row_e,
-                       row_weight, slot_row, nullptr, int64_t(0));
+                       stream, static_cast<const uint8_t*>(x), gate, T, row_bytes, k, cpr, gbase,
+                       tcnt, lslot, pl.tiles_pad, pl.groups, static_cast<uint8_t*>(send),
+                       row_token, row_e, row_weight, slot_row, nullptr, int64_t(0));
   } else {
     hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT>), dim3(unsigned(blocks)), dim3(256), 0,
                        stream, static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, R,
-                       place, E / R, cpr, base, lslot, pl.tiles_pad, header,
+                       place, E / R, cpr, gbase, tcnt, lslot, pl.tiles_pad, pl.groups, header,
                        static_cast<uint8_t*>(send), row_token, row_e, row_gates, row_weight,
                        slot_row, n_rows);
   }
@@ -249,7 +264,8 @@ static hipError_t launch_expand_nv(const void* rows, const float* row_gates,
                                    float* exp_gate, int32_t* row_slot, hipStream_t stream) {
   const PlanLayout pl = plan_layout(cap, E, k, R, 0);
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
-  const int32_t* base = reinterpret_cast<const int32_t*>(ws + pl.base_off);
+  const int32_t* gbase = reinterpret_cast<const int32_t*>(ws + pl.base_off);
+  const uint8_t* tcnt = ws + pl.tcnt_off;
   const uint32_t* lslot = reinterpret_cast<const uint32_t*>(ws + pl.lslot_off);
   const int chunk = NV * kWave * 16;
   const int cpr = (row_bytes + chunk - 1) / chunk;
@@ -257,8 +273,9 @@ static hipError_t launch_expand_nv(const void* rows, const float* row_gates,
   constexpr bool NT = MOE_DISPATCH_NT != 0;
   hipLaunchKernelGGL((dispatch_kernel<NV, NT, true>), dim3(unsigned(blocks)), dim3(256), 0,
                      stream, static_cast<const uint8_t*>(rows), row_gates, cap, row_bytes, k, cpr,
-                     base, lslot, pl.tiles_pad, static_cast<uint8_t*>(expanded), exp_row,
-                     exp_expert, exp_gate, row_slot, n_rows, out_cap);
+                     gbase, tcnt, lslot, pl.tiles_pad, pl.groups,
+                     static_cast<uint8_t*>(expanded), exp_row, exp_expert, exp_gate, row_slot,
+                     n_rows, out_cap);
   return hipGetLastError();
 }
 

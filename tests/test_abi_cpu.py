@@ -51,15 +51,15 @@ def test_status_strings(lib):
 
 def test_workspace_bytes(lib):
     f = lib.moe_workspace_bytes
-    # 4096 tokens, 64 experts, top-6, 16 ranks: 64 tiles x 64 columns int32 plus
-    # one byte per (token, slot), 256-byte sections.
-    # plain: bases for 64 tiles x 64 experts (int32), one count byte per tile
-    # and expert, one 4-byte slot code per (token, slot); 256-byte sections
+    # 4096 tokens, 64 experts, top-6, 16 ranks; 256-byte sections.
+    # plain: one int32 base per 16-tile group (4 groups) per expert, one count
+    # byte per tile (64) and expert, one 4-byte slot code per (token, slot)
     n = f(4096, 64, 6, 16, 0)
-    assert n >= 64 * 64 * 4 + 64 * 64 + 4096 * 6 * 4 and n % 256 == 0
+    assert n >= 4 * 64 * 4 + 64 * 64 + 4096 * 6 * 4 and n % 256 == 0
     # dedup: bases only for the 16 rank columns, counts for experts and ranks
     nd = f(4096, 64, 6, 16, 1)
-    assert nd >= 64 * 16 * 4 + 64 * 80 + 4096 * 6 * 4 and nd % 256 == 0
+    assert nd >= 4 * 16 * 4 + 64 * 80 + 4096 * 6 * 4 and nd % 256 == 0
+    assert nd > n                                  # the rank count columns
     assert f(0, 64, 6, 16, 0) > 0
     assert f(10, 64, 6, 5, 0) == 0                 # E % R != 0
     assert f(10, 64, 65, 16, 0) == 0               # k > E
