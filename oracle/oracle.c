@@ -371,3 +371,61 @@ int oracle_coselect(const int32_t* idx, int64_t tokens, int n_experts, int top_k
     }
     return 0;
 }
+
+/* ------------------------------------------------- placement search --- */
+
+/* [EC] "Method 1", correlated placement: starting from a placement (contiguous
+ * unless given), swap experts between ranks to raise the co-location objective
+ *   O(place) = sum over ordered pairs x != y with place[x] == place[y] of W[x][y]
+ * while every rank keeps its E/R experts.  The page names a Kernighan-Lin-style
+ * local search without printing it; this is the plainest reading: repeatedly
+ * apply the swap (e, f), place[e] != place[f], e < f, with the largest gain,
+ * ties to the lowest e then the lowest f, until no swap gains or max_swaps
+ * swaps were made.
+ * Gain of swapping e (rank a) and f (rank b), with
+ *   A(x, r) = sum over y on r, y != x, of W[x][y] + W[y][x]:
+ *   A(e, b) + A(f, a) - A(e, a) - A(f, b) - 2 (W[e][f] + W[f][e]).
+ * Every A is summed afresh with plain loops for every candidate. */
+static int64_t oracle_attach(const int32_t* W, int n, const int32_t* place, int x, int r) {
+    int64_t s = 0;
+    for (int y = 0; y < n; ++y)
+        if (y != x && place[y] == r) s += (int64_t)W[(int64_t)x * n + y] + W[(int64_t)y * n + x];
+    return s;
+}
+
+int64_t oracle_placement_objective(const int32_t* W, int n_experts, const int32_t* place) {
+    int64_t o = 0;
+    for (int x = 0; x < n_experts; ++x)
+        for (int y = 0; y < n_experts; ++y)
+            if (x != y && place[x] == place[y]) o += W[(int64_t)x * n_experts + y];
+    return o;
+}
+
+int oracle_placement_search(const int32_t* W, int n_experts, int n_ranks, const int32_t* initial,
+                            int max_swaps, int32_t* place, int64_t* objective, int* swaps) {
+    const int n = n_experts;
+    for (int e = 0; e < n; ++e) place[e] = initial ? initial[e] : e / (n / n_ranks);
+    int done = 0;
+    while (done < max_swaps) {
+        int64_t best = 0;
+        int be = -1, bf = -1;
+        for (int e = 0; e < n; ++e) {
+            for (int f = e + 1; f < n; ++f) {
+                const int a = place[e], b = place[f];
+                if (a == b) continue;
+                const int64_t g = oracle_attach(W, n, place, e, b) + oracle_attach(W, n, place, f, a)
+                                - oracle_attach(W, n, place, e, a) - oracle_attach(W, n, place, f, b)
+                                - 2 * ((int64_t)W[(int64_t)e * n + f] + W[(int64_t)f * n + e]);
+                if (g > best) { best = g; be = e; bf = f; }
+            }
+        }
+        if (be < 0) break;
+        const int t = place[be];
+        place[be] = place[bf];
+        place[bf] = t;
+        ++done;
+    }
+    if (objective) *objective = oracle_placement_objective(W, n, place);
+    if (swaps) *swaps = done;
+    return 0;
+}

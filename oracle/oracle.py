@@ -51,6 +51,10 @@ def lib():
                                           P, P, P, P, P, P]
         L.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
         L.oracle_coselect.argtypes = [P, i64, i32, i32, P]
+        L.oracle_placement_search.argtypes = [P, i32, i32, P, i32, P, P, P]
+        L.oracle_placement_search.restype = ctypes.c_int
+        L.oracle_placement_objective.argtypes = [P, i32, P]
+        L.oracle_placement_objective.restype = ctypes.c_int64
         L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
         L.oracle_bf16_from_double.restype = ctypes.c_uint16
         for f in ("oracle_route_topk", "oracle_send_counts", "oracle_dispatch",
@@ -215,3 +219,24 @@ def coselect(idx, n_experts, tokens=None, W=None):
 
 def bf16_from_double(d: float) -> int:
     return int(lib().oracle_bf16_from_double(float(d)))
+
+
+def placement_objective(W, placement):
+    W = _c(W, np.int32)
+    place = _c(placement, np.int32)
+    return int(lib().oracle_placement_objective(_p(W), W.shape[0], _p(place)))
+
+
+def placement_search(W, n_ranks, initial=None, max_swaps=None):
+    """Best-gain swap search from `initial` (contiguous if None).  Returns
+    (placement, objective, swaps)."""
+    W = _c(W, np.int32)
+    E = W.shape[0]
+    init = None if initial is None else _c(initial, np.int32)
+    place = np.empty(E, np.int32)
+    obj = np.zeros(1, np.int64)
+    sw = np.zeros(1, np.int32)
+    ms = E * E if max_swaps is None else int(max_swaps)
+    _check(lib().oracle_placement_search(_p(W), E, n_ranks, _p(init), ms, _p(place), _p(obj),
+                                         _p(sw)), "placement_search")
+    return place, int(obj[0]), int(sw[0])

@@ -472,3 +472,77 @@ def test_receive_round_trip_with_identity_experts(oracle_mod, name):
         g1 = gate[one_rank].astype(np.float64).sum(1)
         assert np.abs(g1 - 1).max() <= w.top_k * 2.0 ** -24
         assert (out[one_rank] == x[one_rank]).all()
+
+
+# -------------------------------------------------------- placement search --
+
+def _objective(W, place):
+    """Co-location objective by brute force: sum of W[x][y] over ordered pairs
+    x != y on one rank (Expert Coupling, Method 1)."""
+    same = place[:, None] == place[None, :]
+    np.fill_diagonal(same, False)
+    return int((W.astype(np.int64) * same).sum())
+
+
+def _swapped(place, e, f):
+    p = place.copy()
+    p[e], p[f] = place[f], place[e]
+    return p
+
+
+@pytest.mark.parametrize("E,R,sym", [(8, 2, True), (8, 4, False), (12, 3, True), (16, 8, True),
+                                     (16, 4, False)])
+def test_placement_search_bruteforce(oracle_mod, E, R, sym):
+    """Every step takes the best swap (ties to the lowest pair) found by
+    recomputing the objective for every swap; the end is a local optimum; the
+    objective never decreases; every rank keeps E/R experts."""
+    rng = np.random.default_rng(E * 7 + R)
+    W = rng.integers(0, 9, (E, E)).astype(np.int32)
+    if sym:
+        W = (W + W.T).astype(np.int32)
+    place = WL.contiguous_placement(E, R)
+    prev = _objective(W, place)
+    for step in range(1, 40):
+        got, obj, sw = oracle_mod.placement_search(W, R, max_swaps=step)
+        assert obj == _objective(W, got)
+        assert (np.bincount(got, minlength=R) == E // R).all()
+        # the expected next swap from the previous placement, by brute force
+        best, pair = 0, None
+        for e in range(E):
+            for f in range(e + 1, E):
+                if place[e] != place[f]:
+                    d = _objective(W, _swapped(place, e, f)) - prev
+                    if d > best:
+                        best, pair = d, (e, f)
+        if pair is None:
+            assert sw == step - 1 and (got == place).all()
+            break
+        assert sw == step and (got == _swapped(place, *pair)).all()
+        assert obj == prev + best
+        place, prev = got, obj
+    else:
+        pytest.fail("no local optimum within 40 swaps")
+    # local optimum: no single swap improves
+    for e in range(E):
+        for f in range(e + 1, E):
+            if place[e] != place[f]:
+                assert _objective(W, _swapped(place, e, f)) <= prev
+
+
+def test_placement_search_recovers_planted_pairs(oracle_mod):
+    """A co-selection matrix made of strongly coupled expert pairs (plus weak
+    noise): the search puts every pair on one rank."""
+    E, R = 64, 16
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(E)
+    W = rng.integers(0, 3, (E, E)).astype(np.int32)
+    W = W + W.T
+    for i in range(0, E, 2):
+        a, b = perm[i], perm[i + 1]
+        W[a, b] += 100
+        W[b, a] += 100
+    np.fill_diagonal(W, 0)
+    place, obj, _ = oracle_mod.placement_search(W, R)
+    for i in range(0, E, 2):
+        assert place[perm[i]] == place[perm[i + 1]]
+    assert obj >= _objective(W, WL.contiguous_placement(E, R))
