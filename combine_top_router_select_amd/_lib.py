@@ -14,7 +14,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 SYMBOLS = ("moe_status_string", "moe_workspace_bytes", "moe_expand_workspace_bytes",
            "moe_route_topk", "moe_send_counts", "moe_dispatch_permute",
            "moe_dispatch_permute_dedup", "moe_combine", "moe_coselect_counts",
-           "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce")
+           "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
+           "moe_placement_search")
 
 _lib = None
 
@@ -52,6 +53,7 @@ def lib():
         L.moe_expand_permute.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, P, sz, P, i64,
                                          P, P, P, P, P]
         L.moe_expand_reduce.argtypes = [P, P, P, P, i64, i32, i32, i32, P, P]
+        L.moe_placement_search.argtypes = [P, i32, i32, P, i32, P, P, P]
         for s in SYMBOLS[3:]:
             getattr(L, s).restype = i32
         _lib = L

@@ -23,6 +23,7 @@ hipError_t launch_expand_counts(const int32_t*, int64_t, int, int, int, const in
 hipError_t launch_expand(const void*, const float*, const int32_t*, int64_t, int, int, int, int,
                          const void*, void*, int64_t, int32_t*, int32_t*, float*, int32_t*,
                          hipStream_t);
+int placement_search(const int32_t*, int, int, const int32_t*, int, int32_t*, int64_t*, int*);
 hipError_t launch_coselect(const int32_t*, int64_t, int, int, int32_t*, hipStream_t);
 }  // namespace moe
 
@@ -243,4 +244,25 @@ MOE_API int moe_coselect_counts(const int32_t* topk_idx, int64_t tokens, int n_e
   if (!topk_idx || !coselect) return MOE_EINVAL;
   return hip_status(moe::launch_coselect(topk_idx, tokens, n_experts, top_k, coselect,
                                          as_stream(stream)));
+}
+
+MOE_API int moe_placement_search(const int32_t* coselect, int n_experts, int n_ranks,
+                                 const int32_t* initial, int max_swaps, int32_t* placement,
+                                 int64_t* objective, int* swaps) {
+  if (n_experts < 1) return MOE_EINVAL;
+  if (n_experts > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+  int st = check_ranks(n_experts, n_ranks);
+  if (st != MOE_OK) return st;
+  if (!coselect || !placement || max_swaps < 0) return MOE_EINVAL;
+  if (initial) {
+    int per[MOE_MAX_RANKS] = {0};
+    for (int e = 0; e < n_experts; ++e) {
+      if (initial[e] < 0 || initial[e] >= n_ranks) return MOE_EINVAL;
+      ++per[initial[e]];
+    }
+    for (int r = 0; r < n_ranks; ++r)
+      if (per[r] != n_experts / n_ranks) return MOE_EINVAL;
+  }
+  return moe::placement_search(coselect, n_experts, n_ranks, initial, max_swaps, placement,
+                               objective, swaps);
 }

@@ -16,7 +16,8 @@ from ._lib import MoeError, check, lib, status_string  # noqa: F401
 __all__ = ["MoeError", "moe_status_string", "moe_workspace_bytes", "moe_route_topk",
            "moe_send_counts", "moe_dispatch_permute", "moe_dispatch_permute_dedup",
            "moe_combine", "moe_coselect_counts", "workspace", "moe_expand_workspace_bytes",
-           "expand_workspace", "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce"]
+           "expand_workspace", "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
+           "moe_placement_search"]
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -299,3 +300,31 @@ def moe_expand_reduce(expert_out, exp_gate, row_slot, n_rows, out=None, stream=N
                                   _ptr(n_rows), C, H, k, 2, _ptr(out), _stream(stream)),
           "moe_expand_reduce")
     return out
+
+
+# -------------------------------------------------------- placement search --
+
+def moe_placement_search(coselect, n_ranks, initial=None, max_swaps=None):
+    """Correlated placement from a co-selection matrix (host computation).
+    `coselect` [E][E] int32 (a GPU tensor is copied to the host first),
+    `initial` [E] int32 or None (contiguous).  Returns (placement, objective,
+    swaps) with placement a host int32 tensor."""
+    import ctypes
+    W = coselect.detach().to("cpu", torch.int32).contiguous()
+    if W.dim() != 2 or W.shape[0] != W.shape[1]:
+        raise ValueError("coselect must be [E][E]")
+    E = W.shape[0]
+    init = None
+    if initial is not None:
+        init = initial.detach().to("cpu", torch.int32).contiguous()
+        if init.numel() != E:
+            raise ValueError("initial must have E entries")
+    place = torch.empty(E, dtype=torch.int32)
+    obj = ctypes.c_int64(0)
+    sw = ctypes.c_int(0)
+    ms = E * E if max_swaps is None else int(max_swaps)
+    check(lib().moe_placement_search(W.data_ptr(), E, n_ranks,
+                                     None if init is None else init.data_ptr(), ms,
+                                     place.data_ptr(), ctypes.byref(obj), ctypes.byref(sw)),
+          "moe_placement_search")
+    return place, int(obj.value), int(sw.value)

@@ -284,6 +284,29 @@ int moe_expand_reduce(const void* expert_out, const float* exp_gate, const int32
                       const int32_t* n_rows, int64_t capacity, int hidden_dim, int top_k,
                       int bytes_per_element, void* out, void* stream);
 
+/* Host.  Correlated expert placement ([EC] "Method 1": a Kernighan-Lin-style
+ * local search starts from the contiguous placement and swaps experts between
+ * ranks to maximise the co-selection weight of the pairs that share a rank;
+ * each rank keeps E/R experts).  The search itself is not printed on the page;
+ * this is the plainest reading: repeatedly apply the swap of two experts on
+ * different ranks with the largest gain in
+ *   O = sum over ordered pairs x != y on one rank of coselect[x][y],
+ * ties to the lowest (e, f) with e < f, until no swap gains or `max_swaps`
+ * swaps were made.  Synchronous, host memory only, deterministic.
+ *   coselect   host [E][E] int32: W, e.g. moe_coselect_counts() copied back.
+ *   initial    host [E] int32 or NULL (= contiguous): the starting placement;
+ *              every rank must hold exactly E/R experts.
+ *   max_swaps  >= 0.
+ *   placement  host [E] int32 out: the expert -> rank table found.
+ *   objective  host int64 out or NULL: O of the result.
+ *   swaps      host int out or NULL: swaps made.
+ * Errors: MOE_EINVAL (null pointers, E % R != 0, max_swaps < 0, an initial
+ *         placement with a value outside [0, R) or not E/R experts per rank),
+ *         MOE_EUNSUPPORTED (E > 1024, R > 64). */
+int moe_placement_search(const int32_t* coselect, int n_experts, int n_ranks,
+                         const int32_t* initial, int max_swaps, int32_t* placement,
+                         int64_t* objective, int* swaps);
+
 #ifdef __cplusplus
 }
 #endif
