@@ -1,7 +1,8 @@
 """Benchmark of the per-GPU MoE dispatch/combine hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
-                    [--receive] [--graph] [--overlap] [--no-cpu-baseline] [--calib-copy]
+                    [--receive] [--search] [--graph] [--overlap] [--no-cpu-baseline]
+                    [--calib-copy]
 
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input, with inputs resident in HBM: top-k routing -> send counts and
@@ -59,6 +60,9 @@ def parse():
     p.add_argument("--receive", action="store_true",
                    help="dedup mode: also run the receive side (per-expert expansion, identity "
                         "experts, reduction) and combine the reduced rows with weight 1")
+    p.add_argument("--search", action="store_true",
+                   help="also fit a correlated placement to the co-selection counts of the "
+                        "workload's first tokens and report the dedup rows it gives")
     p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     p.add_argument("--overlap", action="store_true",
                    help="run the co-selection counts on a second stream")
@@ -202,6 +206,34 @@ def counter_traffic(kernel, workload, mode):
                                                                                    mode):
                     return int(kv["bytes"]) if kv.get("sources_sha256") == digest else None
     return None
+
+
+def placement_leg(torch, ops, b, w):
+    """Correlated placement from this workload's co-selection counts (first
+    coselect_tokens tokens, counted on the GPU), then the dedup rows of all
+    tokens under the contiguous, the workload's own and the searched placement
+    (counted on the GPU).  Not part of the timed step."""
+    E, k, R, T = w.n_experts, w.top_k, w.n_ranks, w.tokens
+    dev = b.idx.device
+    W = torch.zeros((E, E), dtype=torch.int32, device=dev)
+    ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=W)
+    torch.cuda.synchronize()
+    Wh = W.cpu()
+    t0 = time.perf_counter()
+    place, obj, swaps = ops.moe_placement_search(Wh, R)
+    search_ms = (time.perf_counter() - t0) * 1e3
+    contiguous = (torch.arange(E, dtype=torch.int32) // (E // R))
+    cands = {"contiguous": contiguous, "searched": place}
+    if b.place is not None:
+        cands["workload"] = b.place.cpu()
+    rows, objective = {}, {}
+    for name, pl in cands.items():
+        c = ops.moe_send_counts(b.idx, E, R, pl.to(dev), dedup=True)
+        rows[name] = int(c["rank_offsets"][R].item())
+        objective[name] = ops.moe_placement_search(Wh, R, initial=pl, max_swaps=0)[1]
+    return {"fit_tokens": w.coselect_tokens, "search_ms": round(search_ms, 2), "swaps": swaps,
+            "objective": objective, "dedup_rows": rows,
+            "rows_removed_pct": {n: round(100.0 * (1 - r / (T * k)), 2) for n, r in rows.items()}}
 
 
 def cpu_baseline(inp, w, dedup, seconds, receive=False):
@@ -420,6 +452,8 @@ def main():
     }
     if recv is not None:
         res["receive"] = recv
+    if a.search:
+        res["placement_search"] = placement_leg(torch, ops, sets[0], w)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, w, dedup, a.cpu_seconds, receive)
     print(json.dumps(res), flush=True)
