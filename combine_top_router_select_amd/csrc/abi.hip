@@ -15,7 +15,7 @@ hipError_t launch_send_counts(const int32_t*, int64_t, int, int, int, const int3
 hipError_t launch_dispatch(const void*, const int32_t*, const float*, int64_t, int, int, int,
                            int, const int32_t*, const void*, int, void*, int32_t*, int32_t*,
                            float*, float*, int32_t*, int32_t*, hipStream_t);
-hipError_t launch_combine(const void*, const float*, const int32_t*, int64_t, int, int,
+hipError_t launch_combine(const void*, const float*, const int32_t*, int64_t, int, int, int,
                           const int32_t*, void*, hipStream_t);
 hipError_t launch_expand_counts(const int32_t*, int64_t, int, int, int, const int32_t*,
                                 const int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, void*,
@@ -155,18 +155,27 @@ MOE_API int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx,
                                          as_stream(stream)));
 }
 
+// Rows of bf16 (2 bytes) or fp8 E4M3 (1 byte); the output is bf16.
+static int check_combine(int64_t tokens, int hidden_dim, int top_k, int bytes_per_element) {
+  if (tokens < 0 || top_k < 1 || hidden_dim < 1 || bytes_per_element < 1) return MOE_EINVAL;
+  if (top_k > MOE_MAX_TOP_K || (bytes_per_element != 2 && bytes_per_element != 1))
+    return MOE_EUNSUPPORTED;
+  if (tokens > int64_t(INT_MAX) / top_k) return MOE_EUNSUPPORTED;
+  const int64_t rb = int64_t(hidden_dim) * bytes_per_element;
+  if (rb % 16 != 0 || int64_t(hidden_dim) * 2 > INT_MAX / 2) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
 MOE_API int moe_combine(const void* rows, const float* row_weight, const int32_t* slot_row,
                         int64_t tokens, int hidden_dim, int top_k, int bytes_per_element,
                         void* out, void* stream) {
-  if (tokens < 0 || top_k < 1 || hidden_dim < 1 || bytes_per_element < 1) return MOE_EINVAL;
-  if (top_k > MOE_MAX_TOP_K || bytes_per_element != 2) return MOE_EUNSUPPORTED;
-  if (tokens > int64_t(INT_MAX) / top_k) return MOE_EUNSUPPORTED;
-  const int64_t rb = int64_t(hidden_dim) * 2;
-  if (rb % 16 != 0 || rb > INT_MAX / 2) return MOE_EUNSUPPORTED;
+  const int st = check_combine(tokens, hidden_dim, top_k, bytes_per_element);
+  if (st != MOE_OK) return st;
   if (tokens == 0) return MOE_OK;
   if (!rows || !slot_row || !out) return MOE_EINVAL;
-  return hip_status(moe::launch_combine(rows, row_weight, slot_row, tokens, int(rb), top_k,
-                                        nullptr, out, as_stream(stream)));
+  return hip_status(moe::launch_combine(rows, row_weight, slot_row, tokens,
+                                        hidden_dim * bytes_per_element, top_k,
+                                        bytes_per_element == 1, nullptr, out, as_stream(stream)));
 }
 
 MOE_API size_t moe_expand_workspace_bytes(int64_t capacity, int n_experts, int top_k,
@@ -224,16 +233,14 @@ MOE_API int moe_expand_reduce(const void* expert_out, const float* exp_gate,
                               const int32_t* row_slot, const int32_t* n_rows, int64_t capacity,
                               int hidden_dim, int top_k, int bytes_per_element, void* out,
                               void* stream) {
-  if (capacity < 0 || top_k < 1 || hidden_dim < 1 || bytes_per_element < 1) return MOE_EINVAL;
-  if (top_k > MOE_MAX_TOP_K || bytes_per_element != 2) return MOE_EUNSUPPORTED;
-  if (capacity > int64_t(INT_MAX) / top_k) return MOE_EUNSUPPORTED;
-  const int64_t rb = int64_t(hidden_dim) * 2;
-  if (rb % 16 != 0 || rb > INT_MAX / 2) return MOE_EUNSUPPORTED;
+  const int st = check_combine(capacity, hidden_dim, top_k, bytes_per_element);
+  if (st != MOE_OK) return st;
   if (!n_rows) return MOE_EINVAL;
   if (capacity == 0) return MOE_OK;
   if (!expert_out || !row_slot || !out) return MOE_EINVAL;
-  return hip_status(moe::launch_combine(expert_out, exp_gate, row_slot, capacity, int(rb), top_k,
-                                        n_rows, out, as_stream(stream)));
+  return hip_status(moe::launch_combine(expert_out, exp_gate, row_slot, capacity,
+                                        hidden_dim * bytes_per_element, top_k,
+                                        bytes_per_element == 1, n_rows, out, as_stream(stream)));
 }
 
 MOE_API int moe_coselect_counts(const int32_t* topk_idx, int64_t tokens, int n_experts,

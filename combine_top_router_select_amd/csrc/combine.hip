@@ -4,17 +4,21 @@
 // Sources: "Expert Coupling in MoE Pretraining" (summary), "The Communication
 // Bottleneck": under expert parallelism each MoE layer dispatches rows to the
 // experts and combines their outputs back.  "DODOCO" dataset card,
-// "send_matrices.csv columns": combine moves the dispatch volumes in reverse.
+// "send_matrices.csv columns": combine moves the dispatch volumes in reverse;
+// "Reading the counts": the payload is count x hidden x bytes per element of
+// the dispatch precision (rows here are bf16, or fp8 E4M3 with bf16 output).
 //
 // Design: one wave per (token, row chunk).  Lanes j < k read slot_row[t][j]
 // and the row weight; a slot whose row already appeared in an earlier slot is
 // dropped (dedup rows serve several slots), negative rows are skipped.  The
 // wave then issues the loads of every used row's chunk before any arithmetic
-// (KMAX rows x NV 16-byte vectors in flight per lane), accumulates in fp32
+// (up to KMAX rows x NV 16-byte vectors in flight per lane), accumulates in fp32
 // with fused multiply-adds in slot order starting from -0.0, and converts to
-// bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).  Row loads are
-// nontemporal: each row is read once, so it should not displace cached data
-// (measured: about 2 us less per 4096-token, top-6, hidden-2048 step).
+// bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).  fp8 rows (OCP
+// E4M3) are decoded with v_cvt_pk_f32_fp8, exact for every byte value.  Row
+// loads are nontemporal: each row is read once, so it should not displace
+// cached data (measured: about 2 us less per 4096-token, top-6, hidden-2048
+// step).
 #include "common.hpp"
 
 #ifndef MOE_COMBINE_NT
@@ -32,14 +36,50 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// Values in one 16-byte input vector: 8 bf16, or 16 fp8 (IN8).
+template <bool IN8>
+constexpr int kVals = IN8 ? 16 : 8;
+
+template <bool IN8>
+__device__ __forceinline__ void decode16(const u32x4& v, float (&f)[kVals<IN8>]) {
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    if constexpr (IN8) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(v[h]), false);  // bytes 0, 1
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(v[h]), true);   // bytes 2, 3
+      f[4 * h] = lo.x;
+      f[4 * h + 1] = lo.y;
+      f[4 * h + 2] = hi.x;
+      f[4 * h + 3] = hi.y;
+    } else {
+      f[2 * h] = __uint_as_float(v[h] << 16);
+      f[2 * h + 1] = __uint_as_float(v[h] & 0xFFFF0000u);
+    }
+  }
+}
+
+// bf16 output of the kVals values of one input vector: 16 or 32 bytes at dst.
+template <bool IN8>
+__device__ __forceinline__ void store_out(uint8_t* dst, const float (&a)[kVals<IN8>]) {
+#pragma unroll
+  for (int s = 0; s < kVals<IN8> / 8; ++s) {
+    u32x4 o;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(a[8 * s + 2 * h], a[8 * s + 2 * h + 1]);
+    store16(dst + 16 * s, o);
+  }
+}
+
 // The weighted sum of a token's rows for one chunk: NQ >= nrows rows are
 // loaded (all loads before any arithmetic; rows past nrows repeat the first
 // one and are not added), accumulated in fp32 from -0.0 in slot order, and
-// stored as bf16.
-template <int NQ, int NV>
+// stored as bf16.  Offsets are in input bytes; output offsets are twice that
+// for fp8 input.
+template <int NQ, int NV, bool IN8>
 __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int row_bytes,
                                          int64_t chunk0, uint64_t um, int j0, int nrows, int rr,
                                          float wr, int lane, uint8_t* __restrict__ dst) {
+  constexpr int OS = IN8 ? 2 : 1;  // output bytes per input byte
   u32x4 y[NQ][NV];
   float wq[NQ];
 #pragma unroll
@@ -59,43 +99,36 @@ __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int r
       y[q][i] = MOE_COMBINE_NT ? load16_nt(src + off) : load16(src + off);
     }
   }
-  float acc[NV][8];
+  float acc[NV][kVals<IN8>];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
-    for (int h = 0; h < 8; ++h) acc[i][h] = -0.0f;
+    for (int h = 0; h < kVals<IN8>; ++h) acc[i][h] = -0.0f;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     if (q < nrows) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
+        float f[kVals<IN8>];
+        decode16<IN8>(y[q][i], f);
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint32_t u = y[q][i][h];
-          acc[i][2 * h] = __builtin_fmaf(wq[q], __uint_as_float(u << 16), acc[i][2 * h]);
-          acc[i][2 * h + 1] =
-              __builtin_fmaf(wq[q], __uint_as_float(u & 0xFFFF0000u), acc[i][2 * h + 1]);
-        }
+        for (int h = 0; h < kVals<IN8>; ++h) acc[i][h] = __builtin_fmaf(wq[q], f[h], acc[i][h]);
       }
     }
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
-    if (off < row_bytes) {
-      u32x4 o;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(acc[i][2 * h], acc[i][2 * h + 1]);
-      store16(dst + off, o);
-    }
+    if (off < row_bytes) store_out<IN8>(dst + OS * off, acc[i]);
   }
 }
 
-template <int NV, int KMAX>
+template <int NV, int KMAX, bool IN8>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
                const int32_t* __restrict__ slot_row, int64_t T, int row_bytes, int k, int cpr,
                const int32_t* __restrict__ n_valid, uint8_t* __restrict__ out) {
+  constexpr int OS = IN8 ? 2 : 1;
   const int lane = lane_id();
   const int64_t wid = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
   const int64_t t = wid / cpr;
@@ -116,13 +149,15 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
   }
   uint64_t um = __ballot(use);
   const int nrows = __popcll(um);
-  uint8_t* dst = out + t * row_bytes;
+  uint8_t* dst = out + t * int64_t(row_bytes) * OS;
   if (nrows == 0) {  // no row serves this token: the empty sum, -0.0
     const u32x4 nz = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
-      if (off < row_bytes) store16(dst + off, nz);
+      if (off < row_bytes)
+#pragma unroll
+        for (int s = 0; s < OS; ++s) store16(dst + OS * off + 16 * s, nz);
     }
     return;
   }
@@ -134,60 +169,78 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
   // KMAX rows
   if constexpr (KMAX >= 1) {
     if (nrows <= 1)
-      return sum_rows<1, NV>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+      return sum_rows<1, NV, IN8>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
   }
   if constexpr (KMAX >= 2) {
     if (nrows <= 2)
-      return sum_rows<2, NV>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+      return sum_rows<2, NV, IN8>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
   }
   if constexpr (KMAX > 4) {
     if (nrows <= 4)
-      return sum_rows<4, NV>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+      return sum_rows<4, NV, IN8>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
   }
-  sum_rows<KMAX, NV>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+  sum_rows<KMAX, NV, IN8>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
 }
 
-template <int NV, int KMAX>
+template <int NV, int KMAX, bool IN8>
 static hipError_t launch_combine_t(const void* rows, const float* w, const int32_t* slot_row,
                                    int64_t T, int row_bytes, int k, const int32_t* n_valid,
                                    void* out, hipStream_t stream) {
   const int chunk = NV * kWave * 16;
   const int cpr = (row_bytes + chunk - 1) / chunk;
   const int64_t blocks = (T * cpr + 3) / 4;
-  hipLaunchKernelGGL((combine_kernel<NV, KMAX>), dim3(unsigned(blocks)), dim3(256), 0, stream,
-                     static_cast<const uint8_t*>(rows), w, slot_row, T, row_bytes, k, cpr,
+  hipLaunchKernelGGL((combine_kernel<NV, KMAX, IN8>), dim3(unsigned(blocks)), dim3(256), 0,
+                     stream, static_cast<const uint8_t*>(rows), w, slot_row, T, row_bytes, k, cpr,
                      n_valid, static_cast<uint8_t*>(out));
   return hipGetLastError();
 }
 
-template <int KMAX>
+template <int KMAX, bool IN8>
 static hipError_t launch_combine_k(const void* rows, const float* w, const int32_t* slot_row,
                                    int64_t T, int row_bytes, int k, const int32_t* n_valid,
                                    void* out, hipStream_t stream) {
-  // keep KMAX * NV <= 32 vectors (128 VGPRs) in flight per lane
+  // keep KMAX * NV <= 32 input vectors (128 VGPRs) in flight per lane, and the
+  // fp8 accumulators (16 per vector) to two vectors
   const int vr = row_bytes / 16;
-  constexpr int NVMAX = (32 / KMAX) < 4 ? (32 / KMAX) : 4;
+  constexpr int NVCAP = IN8 ? 2 : 4;
+  constexpr int NVMAX = (32 / KMAX) < NVCAP ? (32 / KMAX) : NVCAP;
   if (NVMAX >= 4 && vr >= 4 * kWave)
-    return launch_combine_t<(NVMAX >= 4 ? 4 : 1), KMAX>(rows, w, slot_row, T, row_bytes, k,
-                                                         n_valid, out, stream);
+    return launch_combine_t<(NVMAX >= 4 ? 4 : 1), KMAX, IN8>(rows, w, slot_row, T, row_bytes, k,
+                                                              n_valid, out, stream);
   if (NVMAX >= 2 && vr >= 2 * kWave)
-    return launch_combine_t<(NVMAX >= 2 ? 2 : 1), KMAX>(rows, w, slot_row, T, row_bytes, k,
-                                                         n_valid, out, stream);
-  return launch_combine_t<1, KMAX>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+    return launch_combine_t<(NVMAX >= 2 ? 2 : 1), KMAX, IN8>(rows, w, slot_row, T, row_bytes, k,
+                                                              n_valid, out, stream);
+  return launch_combine_t<1, KMAX, IN8>(rows, w, slot_row, T, row_bytes, k, n_valid, out,
+                                        stream);
 }
 
-// n_valid (device, may be null): only outputs t < *n_valid are computed and
-// written (the receive-side reduction over the received rows).
+template <bool IN8>
+static hipError_t launch_combine_f(const void* rows, const float* w, const int32_t* slot_row,
+                                   int64_t T, int row_bytes, int k, const int32_t* n_valid,
+                                   void* out, hipStream_t stream) {
+  if (k <= 1)
+    return launch_combine_k<1, IN8>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  if (k <= 2)
+    return launch_combine_k<2, IN8>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  if (k <= 4)
+    return launch_combine_k<4, IN8>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  if (k <= 6)
+    return launch_combine_k<6, IN8>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  if (k <= 8)
+    return launch_combine_k<8, IN8>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  return launch_combine_k<16, IN8>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+}
+
+// row_bytes: bytes of one input row (H * 2 for bf16, H for fp8); the output
+// rows are bf16 either way.  n_valid (device, may be null): only outputs
+// t < *n_valid are computed and written (the receive-side reduction).
 hipError_t launch_combine(const void* rows, const float* w, const int32_t* slot_row, int64_t T,
-                          int row_bytes, int k, const int32_t* n_valid, void* out,
+                          int row_bytes, int k, int in_fp8, const int32_t* n_valid, void* out,
                           hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if (k <= 1) return launch_combine_k<1>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
-  if (k <= 2) return launch_combine_k<2>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
-  if (k <= 4) return launch_combine_k<4>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
-  if (k <= 6) return launch_combine_k<6>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
-  if (k <= 8) return launch_combine_k<8>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
-  return launch_combine_k<16>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  if (in_fp8)
+    return launch_combine_f<true>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
+  return launch_combine_f<false>(rows, w, slot_row, T, row_bytes, k, n_valid, out, stream);
 }
 
 }  // namespace moe

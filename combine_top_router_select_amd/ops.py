@@ -176,17 +176,28 @@ def moe_dispatch_permute_dedup(x, topk_idx, topk_gate, n_experts, n_ranks, ws, p
             "row_weight": rw, "slot_row": sr, "n_rows": nr}
 
 
+_FP8 = tuple(t for t in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if t is not None)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _row_bpe(rows, name):
+    """Row element size: bf16 (2 bytes) or fp8 E4M3 (1 byte)."""
+    _dev(rows, name, _BF16 + _FP8, 2)
+    return 1 if rows.dtype in _FP8 else 2
+
+
 def moe_combine(rows, row_weight, slot_row, out=None, stream=None):
-    _dev(rows, "rows", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    """out[T][H] bf16; rows bf16, or fp8 E4M3 (torch.float8_e4m3fn or uint8)."""
+    bpe = _row_bpe(rows, "rows")
     _dev(slot_row, "slot_row", torch.int32, 2)
     if row_weight is not None:
         _dev(row_weight, "row_weight", torch.float32)
     T, k = slot_row.shape
     H = rows.shape[1]
     if out is None:
-        out = torch.empty((T, H), dtype=rows.dtype, device=rows.device)
-    _dev(out, "out", (torch.bfloat16, torch.int16, torch.uint16), 2)
-    check(lib().moe_combine(_ptr(rows), _ptr(row_weight), _ptr(slot_row), T, H, k, 2,
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=rows.device)
+    _dev(out, "out", _BF16, 2)
+    check(lib().moe_combine(_ptr(rows), _ptr(row_weight), _ptr(slot_row), T, H, k, bpe,
                             _ptr(out), _stream(stream)), "moe_combine")
     return out
 
@@ -284,9 +295,9 @@ def moe_expand_permute(rows, row_experts, row_gates, n_rows, n_experts, n_ranks,
 
 
 def moe_expand_reduce(expert_out, exp_gate, row_slot, n_rows, out=None, stream=None):
-    """Receive-side reduction of the experts' outputs back to one row per
-    received row (rows past n_rows are not written)."""
-    _dev(expert_out, "expert_out", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    """Receive-side reduction of the experts' outputs (bf16, or fp8 E4M3) back
+    to one bf16 row per received row (rows past n_rows are not written)."""
+    bpe = _row_bpe(expert_out, "expert_out")
     _dev(row_slot, "row_slot", torch.int32, 2)
     _dev(n_rows, "n_rows", torch.int32)
     if exp_gate is not None:
@@ -294,10 +305,10 @@ def moe_expand_reduce(expert_out, exp_gate, row_slot, n_rows, out=None, stream=N
     C, k = row_slot.shape
     H = expert_out.shape[1]
     if out is None:
-        out = torch.empty((C, H), dtype=expert_out.dtype, device=expert_out.device)
-    _dev(out, "out", (torch.bfloat16, torch.int16, torch.uint16), 2)
+        out = torch.empty((C, H), dtype=torch.bfloat16, device=expert_out.device)
+    _dev(out, "out", _BF16, 2)
     check(lib().moe_expand_reduce(_ptr(expert_out), _ptr(exp_gate), _ptr(row_slot),
-                                  _ptr(n_rows), C, H, k, 2, _ptr(out), _stream(stream)),
+                                  _ptr(n_rows), C, H, k, bpe, _ptr(out), _stream(stream)),
           "moe_expand_reduce")
     return out
 

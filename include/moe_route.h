@@ -177,8 +177,12 @@ int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx, const flo
 /* A5 - combine ([EC] "The Communication Bottleneck"; [DD] "send_matrices.csv
  * columns": combine moves the dispatch volumes back): each token's output is the
  * weighted sum of the rows that served it.
- *   rows         [*][H] bf16, read only: the rows returned by the experts, in the
- *                send-buffer layout of the dispatch call.
+ *   rows         [*][H] read only: the rows returned by the experts, in the
+ *                send-buffer layout of the dispatch call; bf16 when
+ *                bytes_per_element is 2, fp8 E4M3 (OCP: 1 sign, 4 exponent bits
+ *                with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN)
+ *                when it is 1 ([DD] "Reading the counts": the payload is count x
+ *                hidden x bytes per element of the dispatch precision).
  *   row_weight   [*] fp32 or NULL (= 1 for every row).
  *   slot_row     [T][k] int32: rows of each token; negative entries are skipped
  *                and a row listed by several slots is added once.
@@ -187,8 +191,9 @@ int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx, const flo
  *                fp32 with fused multiply-adds from -0.0 and rounded once to bf16
  *                (nearest, ties to even).  Within 1 bf16 ulp of the exactly
  *                rounded sum when the terms do not cancel.
- * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (bytes_per_element != 2, H*2 not a
- *         multiple of 16, k > 16). */
+ *                Every fp8 value is decoded exactly.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (bytes_per_element not 1 or 2, H *
+ *         bytes_per_element not a multiple of 16, k > 16). */
 int moe_combine(const void* rows, const float* row_weight, const int32_t* slot_row,
                 int64_t tokens, int hidden_dim, int top_k, int bytes_per_element,
                 void* out, void* stream);
@@ -276,8 +281,8 @@ int moe_expand_permute(const void* rows, const int32_t* row_experts, const float
  * arithmetic of moe_combine() (fp32 fused multiply-adds from -0.0, one
  * round-to-nearest-even).  exp_gate NULL = weight 1.  Rows p >= *n_rows of out
  * are not written.
- *   expert_out     [expanded rows][H] bf16: the experts' outputs in the
- *                  expanded layout.
+ *   expert_out     [expanded rows][H] bf16 (bytes_per_element 2) or fp8 E4M3
+ *                  (1): the experts' outputs in the expanded layout.
  *   out            [C][H] bf16.
  * Errors: as moe_combine(); n_rows must not be NULL. */
 int moe_expand_reduce(const void* expert_out, const float* exp_gate, const int32_t* row_slot,

@@ -311,6 +311,18 @@ static double oracle_bf16_to_double(uint16_t b) {
     return (double)f;
 }
 
+/* fp8 E4M3 in the OCP 8-bit floating point format: sign, 4 exponent bits
+ * (bias 7), 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6;
+ * no infinities; S.1111.111 is NaN.  Decoded exactly into a double. */
+double oracle_e4m3_to_double(uint8_t b) {
+    const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
 /* [EC] "The Communication Bottleneck" (dispatch, experts, combine) and [DD]
  * "send_matrices.csv columns" (combine is the reverse exchange): each token's
  * output is the weighted sum of the rows that served it.
@@ -319,8 +331,8 @@ static double oracle_bf16_to_double(uint16_t b) {
  * (each product of an fp32 and a bf16 is exact in fp64), rounded once.
  * w == NULL means weight 1 for every row.  Rows are visited in ascending index
  * order; the sum starts at -0.0 so that an all-(-0) input stays -0. */
-int oracle_combine(const uint16_t* rows, const float* w, const int32_t* slot_row,
-                   int64_t tokens, int hidden_dim, int top_k, uint16_t* out) {
+static int oracle_combine_rows(const void* rows, int fp8, const float* w, const int32_t* slot_row,
+                               int64_t tokens, int hidden_dim, int top_k, uint16_t* out) {
     int32_t* rs = (int32_t*)malloc(sizeof(int32_t) * (size_t)top_k);
     if (!rs) return 2;
     for (int64_t t = 0; t < tokens; ++t) {
@@ -343,13 +355,28 @@ int oracle_combine(const uint16_t* rows, const float* w, const int32_t* slot_row
             double acc = -0.0;
             for (int i = 0; i < nr; ++i) {
                 const double wr = w ? (double)w[rs[i]] : 1.0;
-                acc += wr * oracle_bf16_to_double(rows[(int64_t)rs[i] * hidden_dim + h]);
+                const int64_t at = (int64_t)rs[i] * hidden_dim + h;
+                const double y = fp8 ? oracle_e4m3_to_double(((const uint8_t*)rows)[at])
+                                     : oracle_bf16_to_double(((const uint16_t*)rows)[at]);
+                acc += wr * y;
             }
             out[t * hidden_dim + h] = oracle_bf16_from_double(acc);
         }
     }
     free(rs);
     return 0;
+}
+
+int oracle_combine(const uint16_t* rows, const float* w, const int32_t* slot_row,
+                   int64_t tokens, int hidden_dim, int top_k, uint16_t* out) {
+    return oracle_combine_rows(rows, 0, w, slot_row, tokens, hidden_dim, top_k, out);
+}
+
+/* The same sum over rows of fp8 E4M3 values (the dispatch precision may be
+ * one byte per element: [DD] "Reading the counts"); output bf16. */
+int oracle_combine_fp8(const uint8_t* rows, const float* w, const int32_t* slot_row,
+                       int64_t tokens, int hidden_dim, int top_k, uint16_t* out) {
+    return oracle_combine_rows(rows, 1, w, slot_row, tokens, hidden_dim, top_k, out);
 }
 
 /* --------------------------------------------------------- co-selection --- */

@@ -50,6 +50,9 @@ def lib():
         L.oracle_expand_dedup.argtypes = [P, P, P, i64, i64, i32, i32, i32, i32, P, P, P, P,
                                           P, P, P, P, P, P]
         L.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
+        L.oracle_combine_fp8.argtypes = [P, P, P, i64, i32, i32, P]
+        L.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_to_double.restype = ctypes.c_double
         L.oracle_coselect.argtypes = [P, i64, i32, i32, P]
         L.oracle_placement_search.argtypes = [P, i32, i32, P, i32, P, P, P]
         L.oracle_placement_search.restype = ctypes.c_int
@@ -59,7 +62,7 @@ def lib():
         L.oracle_bf16_from_double.restype = ctypes.c_uint16
         for f in ("oracle_route_topk", "oracle_send_counts", "oracle_dispatch",
                   "oracle_dispatch_dedup", "oracle_expand_dedup", "oracle_combine",
-                  "oracle_coselect"):
+                  "oracle_combine_fp8", "oracle_coselect"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -192,6 +195,23 @@ def reduce_rows(expert_out_bits, exp_gate, row_slot, n_rows):
     """Receive-side reduction: row p < n_rows becomes the gate-weighted sum of
     its experts' outputs (the combine definition over the received rows)."""
     return combine(expert_out_bits, exp_gate, _c(row_slot, np.int32)[:n_rows])
+
+
+def e4m3_to_double(b: int) -> float:
+    return float(lib().oracle_e4m3_to_double(int(b) & 0xFF))
+
+
+def combine_fp8(rows_u8, row_weight, slot_row):
+    """Combine of fp8 E4M3 rows (uint8 bit patterns) into bf16 bits."""
+    rows = _c(rows_u8, np.uint8)
+    slot_row = _c(slot_row, np.int32)
+    T, k = slot_row.shape
+    H = rows.shape[1]
+    w = None if row_weight is None else _c(row_weight, np.float32)
+    out = np.empty((T, H), np.uint16)
+    _check(lib().oracle_combine_fp8(_p(rows), _p(w), _p(slot_row), T, H, k, _p(out)),
+           "combine_fp8")
+    return out
 
 
 def combine(rows_bits, row_weight, slot_row):

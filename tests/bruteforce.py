@@ -86,8 +86,18 @@ def nearest_bf16(q: Fraction, negative_zero=False):
     return sign | b
 
 
-def combine(rows_bits, weights, slot_row):
-    """Exact rational weighted sum of the distinct rows of each token."""
+def e4m3_to_fraction(b):
+    """fp8 E4M3 (OCP) value of byte b as an exact fraction (NaN excluded)."""
+    b = int(b) & 0xFF
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    assert not (e == 15 and m == 7), "NaN"
+    v = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -v if s else v
+
+
+def combine(rows_bits, weights, slot_row, fp8=False):
+    """Exact rational weighted sum of the distinct rows of each token; rows are
+    bf16 bit patterns, or fp8 E4M3 bytes with fp8=True."""
     T, k = len(slot_row), len(slot_row[0])
     H = len(rows_bits[0])
     out = []
@@ -99,10 +109,11 @@ def combine(rows_bits, weights, slot_row):
             all_neg_zero = True
             for r in rs:
                 w = Fraction(1) if weights is None else Fraction(float(weights[r]))
-                v = bf16_to_fraction(rows_bits[r][h])
+                v = e4m3_to_fraction(rows_bits[r][h]) if fp8 else bf16_to_fraction(rows_bits[r][h])
                 acc += w * v
                 b = int(rows_bits[r][h])
-                if not (b == 0x8000 and (weights is None or float(weights[r]) > 0)):
+                neg_zero = b == (0x80 if fp8 else 0x8000)
+                if not (neg_zero and (weights is None or float(weights[r]) > 0)):
                     all_neg_zero = False
             # the sum starts at -0.0: it stays -0 only if every term is -0 (or none)
             o.append(nearest_bf16(acc, negative_zero=(acc == 0 and all_neg_zero)))

@@ -138,7 +138,9 @@ def test_dispatch_errors(lib):
 
 def test_combine_and_coselect_errors(lib):
     c = lib.moe_combine
-    assert c(FAKE, None, FAKE, 10, 128, 2, 4, FAKE, None) == EUNSUP   # only bf16
+    assert c(FAKE, None, FAKE, 10, 128, 2, 4, FAKE, None) == EUNSUP   # bf16 or fp8 rows only
+    assert c(FAKE, None, FAKE, 10, 128, 2, 3, FAKE, None) == EUNSUP
+    assert c(FAKE, None, FAKE, 10, 8, 2, 1, FAKE, None) == EUNSUP     # 8-byte fp8 rows
     assert c(FAKE, None, FAKE, 10, 4, 2, 2, FAKE, None) == EUNSUP     # 8-byte rows
     assert c(None, None, FAKE, 10, 128, 2, 2, FAKE, None) == EINVAL
     assert c(FAKE, None, FAKE, 10, 128, 17, 2, FAKE, None) == EUNSUP

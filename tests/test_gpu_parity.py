@@ -431,3 +431,95 @@ def test_k_equals_e_and_k1(oracle_mod):
             out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"])
             sync()
             assert (bf16_host(out) == inp["x_bits"]).all()
+
+
+# ------------------------------------------------------------- fp8 rows --
+
+def _fp8_dev(u8):
+    return torch.from_numpy(np.ascontiguousarray(u8)).to("cuda:0").view(torch.float8_e4m3fn)
+
+
+def _bound_ok(got, ref, Y_f64, w, slot, k):
+    n = Y_f64.shape[0]
+    wv = np.ones(n) if w is None else w.astype(np.float64)
+    absum = np.zeros((slot.shape[0], Y_f64.shape[1]))
+    for t in range(slot.shape[0]):
+        for r in sorted({int(v) for v in slot[t] if v >= 0}):
+            absum[t] += np.abs(wv[r] * Y_f64[r])
+    gam = k * 2.0 ** -24 / (1 - k * 2.0 ** -24)
+    g64, r64 = bf16_to_f64(got), bf16_to_f64(ref)
+    ulp = np.maximum(np.maximum(np.abs(r64), np.abs(g64)) * 2.0 ** -7, 2.0 ** -133)
+    return bool((np.abs(g64 - r64) <= ulp + gam * absum).all())
+
+
+@pytest.mark.parametrize("dedup", [False, True])
+@pytest.mark.parametrize("H", [1024, 2048, 4096, 272])
+def test_combine_fp8_rows(oracle_mod, dedup, H):
+    """fp8 E4M3 rows (random bytes, no NaN, some -0) into bf16, for gate, NULL
+    and signed weights, against the oracle's exact decode and sum."""
+    T, E, k, R = 600, 64, 6, 8
+    say(f"[combine fp8] H={H} dedup={dedup}")
+    inp = WL.make_custom_inputs(T, 8, E, seed=H + dedup)
+    idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+    o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(
+        inp["x_bits"], idx_o, gate_o, E, R)
+    n = o["n_rows"]
+    rng = np.random.default_rng(H)
+    Y = rng.integers(0, 256, (n, H)).astype(np.uint8)
+    Y[(Y & 0x7F) == 0x7F] = 0x80
+    Yf = torch.from_numpy(Y).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    slot = o["slot_row"]
+    for w in (o["row_weight"], None, rng.standard_normal(n).astype(np.float32)):
+        ref = oracle_mod.combine_fp8(Y, w, slot)
+        got = bf16_host(ops.moe_combine(_fp8_dev(Y), to_dev(w), to_dev(slot)))
+        sync()
+        assert _bound_ok(got, ref, Yf, w, slot, k)
+
+
+def test_fp8_dispatch_combine_chain(oracle_mod):
+    """x in fp8: dispatch moves the bytes bit for bit (bytes_per_element 1),
+    combine decodes them; identity experts with gates summing to 1 return x
+    converted to bf16 within the fp32 rounding of the gate sum (1 bf16 ulp)."""
+    T, H, E, k, R = 1000, 2048, 64, 6, 16
+    inp = WL.make_custom_inputs(T, H, E, seed=8)
+    xf = torch.from_numpy(inp["x_bits"].view(np.int16)).view(torch.bfloat16).float()
+    x8 = xf.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+    for dedup in (False, True):
+        idx, gate = to_dev(idx_o), to_dev(gate_o)
+        c = ops.moe_send_counts(idx, E, R, None, dedup=dedup)
+        f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+        d = f(_fp8_dev(x8), idx, gate, E, R, c["ws"])
+        o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(x8, idx_o, gate_o, E, R)
+        n = o["n_rows"]
+        sync()
+        assert (host(d["send"][:n].view(torch.uint8)) == o["send"]).all()
+        out = bf16_host(ops.moe_combine(d["send"], d["row_weight"], d["slot_row"]))
+        ref = oracle_mod.combine_fp8(o["send"], o["row_weight"], o["slot_row"])
+        sync()
+        assert bf16_ulp_diff(out, ref).max() <= 1
+        x_bf = (torch.from_numpy(x8).view(torch.float8_e4m3fn).to(torch.bfloat16)
+                .view(torch.int16).numpy().view(np.uint16))
+        assert bf16_ulp_diff(out, x_bf).max() <= 1
+
+
+def test_fp8_reduce(oracle_mod):
+    """The receive-side reduction with fp8 expert outputs."""
+    T, H, E, k, R = 500, 512, 32, 4, 8
+    inp = WL.make_custom_inputs(T, H, E, seed=12)
+    idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+    o = oracle_mod.dispatch_dedup(inp["x_bits"], idx_o, gate_o, E, R)
+    D = o["n_rows"]
+    ref_ex = oracle_mod.expand_dedup(None, o["row_experts"], o["row_gates"], D, E, R,
+                                     with_rows=False)
+    n = ref_ex["n_expanded"]
+    rng = np.random.default_rng(4)
+    Y = rng.integers(0, 256, (n, H)).astype(np.uint8)
+    Y[(Y & 0x7F) == 0x7F] = 0x00
+    nr = torch.tensor([D], dtype=torch.int32, device="cuda:0")
+    out = ops.moe_expand_reduce(_fp8_dev(Y), to_dev(ref_ex["exp_gate"]),
+                                to_dev(ref_ex["row_slot"]), nr)
+    ref = oracle_mod.combine_fp8(Y, ref_ex["exp_gate"], ref_ex["row_slot"][:D])
+    sync()
+    Yf = torch.from_numpy(Y).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert _bound_ok(bf16_host(out[:D]), ref, Yf, ref_ex["exp_gate"], ref_ex["row_slot"][:D], k)

@@ -546,3 +546,49 @@ def test_placement_search_recovers_planted_pairs(oracle_mod):
     for i in range(0, E, 2):
         assert place[perm[i]] == place[perm[i + 1]]
     assert obj >= _objective(W, WL.contiguous_placement(E, R))
+
+
+# ------------------------------------------------------------ fp8 rows --
+
+def test_e4m3_decode_matches_torch(oracle_mod):
+    """The oracle's E4M3 decode equals torch's float8_e4m3fn -> float32 cast for
+    all 256 byte values (NaN for S.1111.111), and the brute-force decode."""
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    got = np.array([oracle_mod.e4m3_to_double(int(v)) for v in b])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all() and nan.sum() == 2
+    assert (got[~nan] == ref[~nan].astype(np.float64)).all()
+    assert (np.signbit(got[~nan]) == np.signbit(ref[~nan])).all()
+    for v in b[~nan]:
+        assert float(BF.e4m3_to_fraction(v)) == got[v]
+
+
+@pytest.mark.parametrize("T,E,k,R", TINY[:5])
+def test_bruteforce_combine_fp8_rows(oracle_mod, T, E, k, R):
+    """fp8 rows (random bytes, NaN excluded, some -0): the oracle equals the
+    exactly rounded rational sum, for NULL, gate and signed weights."""
+    rng = np.random.default_rng(T * 13 + k)
+    H = 5
+    inp = _tiny_logits(T, E, 5 + T, tied=False)
+    idx, gate = oracle_mod.route_topk(inp["logits"], k)
+    d = oracle_mod.dispatch(inp["x_bits"][:, :1], idx, gate, E, R)
+    n = d["n_rows"]
+    Y = rng.integers(0, 256, (n, H)).astype(np.uint8)
+    Y[(Y & 0x7F) == 0x7F] = 0x80                  # no NaN; those become -0
+    for w in (None, d["row_weight"], rng.standard_normal(n).astype(np.float32)):
+        out = oracle_mod.combine_fp8(Y, w, d["slot_row"])
+        ref = BF.combine(Y.tolist(), None if w is None else w.tolist(), d["slot_row"].tolist(),
+                         fp8=True)
+        assert out.tolist() == ref
+
+
+def test_fp8_single_row_is_exact(oracle_mod):
+    """k = 1, weight 1: every E4M3 value is a bf16 value, so the output is the
+    row itself converted exactly (torch's cast as the reference)."""
+    b = np.arange(256, dtype=np.uint8)
+    b = b[(b & 0x7F) != 0x7F].reshape(1, -1)
+    out = oracle_mod.combine_fp8(b, None, np.zeros((1, 1), np.int32))
+    ref = (torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float32)
+           .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    assert (out == ref).all()
