@@ -14,6 +14,11 @@ workload defaults to 4096 tokens, hidden 2048 bf16, 64 experts, top-6, 16
 logical ranks, contiguous placement (DeepSeek-MoE-16B-shaped), plain (one row
 per token-expert) dispatch.
 
+The timed steps call the C ABI directly with arguments marshalled once per
+buffer set (the Python binding's per-call checks would otherwise cost about
+10 us of host time per call and make short steps host-bound); the first
+warm-up step goes through the binding.
+
 To keep the last-level (Infinity) cache from serving the data, steps rotate
 over enough independent buffer sets to exceed it several times over, so each
 step's inputs and outputs were last touched many hundreds of MB earlier.
@@ -57,6 +62,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="deepseek_moe_16b")
     p.add_argument("--dedup", action="store_true")
+    p.add_argument("--fp8", action="store_true",
+                   help="rows in fp8 E4M3 (activations quantised on the host): dispatch moves one "
+                        "byte per element, combine decodes to bf16")
     p.add_argument("--receive", action="store_true",
                    help="dedup mode: also run the receive side (per-expert expansion, identity "
                         "experts, reduction) and combine the reduced rows with weight 1")
@@ -98,11 +106,15 @@ def calib_copy():
 class BufferSet:
     """Device buffers for one step (inputs resident, outputs preallocated)."""
 
-    def __init__(self, torch, ops, inp, w, dedup, dev, receive=False):
+    def __init__(self, torch, ops, inp, w, dedup, dev, receive=False, fp8=False):
         T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
         N = T * k
+        rdt = torch.float8_e4m3fn if fp8 else torch.bfloat16  # row type of x, send, expanded
         self.logits = torch.from_numpy(inp["logits"]).to(dev)
-        self.x = torch.from_numpy(inp["x_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        if fp8:
+            self.x = torch.from_numpy(inp["x_fp8"]).view(torch.float8_e4m3fn).to(dev)
+        else:
+            self.x = torch.from_numpy(inp["x_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
         self.place = (torch.from_numpy(inp["placement"]).to(dev)
                       if inp["placement"] is not None else None)
         i32, f32 = torch.int32, torch.float32
@@ -114,7 +126,7 @@ class BufferSet:
                     "rank_offsets": torch.empty(R + 1, dtype=i32, device=dev)}
         if not dedup:
             self.cnt["expert_offsets"] = torch.empty(E, dtype=i32, device=dev)
-        self.disp = {"send": torch.empty((N, H), dtype=torch.bfloat16, device=dev),
+        self.disp = {"send": torch.empty((N, H), dtype=rdt, device=dev),
                      "row_token": torch.empty(N, dtype=i32, device=dev),
                      "row_weight": torch.empty(N, dtype=f32, device=dev),
                      "slot_row": torch.empty((T, k), dtype=i32, device=dev)}
@@ -132,7 +144,7 @@ class BufferSet:
                          "rank_counts": torch.empty(R, dtype=i32, device=dev),
                          "rank_offsets": torch.empty(R + 1, dtype=i32, device=dev),
                          "expert_offsets": torch.empty(E, dtype=i32, device=dev)}
-            self.exp = {"expanded": torch.empty((N, H), dtype=torch.bfloat16, device=dev),
+            self.exp = {"expanded": torch.empty((N, H), dtype=rdt, device=dev),
                         "exp_row": torch.empty(N, dtype=i32, device=dev),
                         "exp_expert": torch.empty(N, dtype=i32, device=dev),
                         "exp_gate": torch.empty(N, dtype=f32, device=dev),
@@ -208,6 +220,52 @@ def counter_traffic(kernel, workload, mode):
     return None
 
 
+def raw_step_calls(torch, ops, b, w, dedup, receive, bpe):
+    """The C-ABI calls of one step on buffer set b, with every argument
+    marshalled once: the timed loop then costs a few microseconds of host time
+    per step instead of the Python binding's checks."""
+    L = ops.lib()
+    T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
+    N = T * k
+    st = torch.cuda.current_stream().cuda_stream
+    p = lambda t: None if t is None else t.data_ptr()
+    c, d = b.cnt, b.disp
+    calls = [(L.moe_route_topk, (p(b.logits), T, E, k, p(b.idx), p(b.gate), st)),
+             (L.moe_send_counts, (p(b.idx), T, E, k, R, p(b.place), int(dedup),
+                                  p(c["expert_counts"]), p(c["rank_counts"]),
+                                  p(c["rank_offsets"]), p(c.get("expert_offsets")), p(b.ws),
+                                  b.ws.numel(), st))]
+    if dedup:
+        calls.append((L.moe_dispatch_permute_dedup, (
+            p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, p(b.place), bpe, p(b.ws), b.ws.numel(),
+            p(d["send"]), p(d["row_token"]), p(d["row_experts"]), p(d["row_gates"]),
+            p(d["row_weight"]), p(d["slot_row"]), p(d["n_rows"]), st)))
+    else:
+        calls.append((L.moe_dispatch_permute, (
+            p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, p(b.place), bpe, p(b.ws), b.ws.numel(),
+            p(d["send"]), p(d["row_token"]), p(d["row_expert"]), p(d["row_weight"]),
+            p(d["slot_row"]), st)))
+    if receive:
+        ec, x = b.ecnt, b.exp
+        calls += [
+            (L.moe_expand_counts, (p(d["row_experts"]), p(d["n_rows"]), N, E, k, R, p(b.place),
+                                   p(ec["expert_counts"]), p(ec["rank_counts"]),
+                                   p(ec["rank_offsets"]), p(ec["expert_offsets"]), p(b.ews),
+                                   b.ews.numel(), st)),
+            (L.moe_expand_permute, (p(d["send"]), p(d["row_experts"]), p(d["row_gates"]),
+                                    p(d["n_rows"]), N, H, E, k, R, bpe, p(b.ews), b.ews.numel(),
+                                    p(x["expanded"]), N, p(x["exp_row"]), p(x["exp_expert"]),
+                                    p(x["exp_gate"]), p(x["row_slot"]), st)),
+            (L.moe_expand_reduce, (p(x["expanded"]), p(x["exp_gate"]), p(x["row_slot"]),
+                                   p(d["n_rows"]), N, H, k, bpe, p(b.red), st)),
+            (L.moe_combine, (p(b.red), None, p(d["slot_row"]), T, H, k, 2, p(b.out), st))]
+    else:
+        calls.append((L.moe_combine, (p(d["send"]), p(d["row_weight"]), p(d["slot_row"]), T, H,
+                                      k, bpe, p(b.out), st)))
+    calls.append((L.moe_coselect_counts, (p(b.idx), w.coselect_tokens, E, k, p(b.W), st)))
+    return calls
+
+
 def placement_leg(torch, ops, b, w):
     """Correlated placement from this workload's co-selection counts (first
     coselect_tokens tokens, counted on the GPU), then the dedup rows of all
@@ -236,7 +294,7 @@ def placement_leg(torch, ops, b, w):
             "rows_removed_pct": {n: round(100.0 * (1 - r / (T * k)), 2) for n, r in rows.items()}}
 
 
-def cpu_baseline(inp, w, dedup, seconds, receive=False):
+def cpu_baseline(inp, w, dedup, seconds, receive=False, fp8=False):
     """The CPU oracle as it stands (single host thread), on whole steps of the
     same workload, repeated until `seconds` have elapsed."""
     from oracle import oracle as O
@@ -246,14 +304,16 @@ def cpu_baseline(inp, w, dedup, seconds, receive=False):
     while True:
         idx, gate = O.route_topk(inp["logits"], w.top_k)
         f = O.dispatch_dedup if dedup else O.dispatch
-        d = f(inp["x_bits"], idx, gate, w.n_experts, w.n_ranks, inp["placement"])
+        x = inp["x_fp8"] if fp8 else inp["x_bits"]
+        comb = O.combine_fp8 if fp8 else O.combine
+        d = f(x, idx, gate, w.n_experts, w.n_ranks, inp["placement"])
         if receive:
             ex = O.expand_dedup(d["send"], d["row_experts"], d["row_gates"], d["n_rows"],
                                 w.n_experts, w.n_ranks, inp["placement"])
-            red = O.reduce_rows(ex["expanded"], ex["exp_gate"], ex["row_slot"], d["n_rows"])
+            red = comb(ex["expanded"], ex["exp_gate"], ex["row_slot"][:d["n_rows"]])
             O.combine(red, None, d["slot_row"])
         else:
-            O.combine(d["send"], d["row_weight"], d["slot_row"])
+            comb(d["send"], d["row_weight"], d["slot_row"])
         O.coselect(idx, w.n_experts, tokens=w.coselect_tokens)
         steps += 1
         el = time.perf_counter() - t0
@@ -289,12 +349,17 @@ def main():
         print(f"warning: {w.name} is not normally run with dedup dispatch", file=sys.stderr)
     dev = torch.device("cuda:0")
     inp = WL.make_inputs(w)
+    fp8 = bool(a.fp8)
+    bpe = 1 if fp8 else 2
+    if fp8:  # synthetic fp8 activations: the bf16 ones rounded to E4M3 on the host
+        xb = torch.from_numpy(inp["x_bits"].view(np.int16)).view(torch.bfloat16)
+        inp["x_fp8"] = xb.float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
 
-    first = BufferSet(torch, ops, inp, w, dedup, dev, receive)
+    first = BufferSet(torch, ops, inp, w, dedup, dev, receive, fp8)
     per_set = first.nbytes()
     nsets = max(2, int(np.ceil(a.footprint_gib * 2 ** 30 / per_set)))
-    sets = [first] + [BufferSet(torch, ops, inp, w, dedup, dev, receive)
+    sets = [first] + [BufferSet(torch, ops, inp, w, dedup, dev, receive, fp8)
                       for _ in range(nsets - 1)]
     torch.cuda.synchronize()
 
@@ -316,14 +381,26 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
 
+    raw = None
+    if graphs is None and side is None:
+        raw = [raw_step_calls(torch, ops, b, w, dedup, receive, bpe) for b in sets]
+
     def step(i):
         if graphs is not None:
             graphs[i % nsets].replay()
+        elif raw is not None:
+            for fn, args in raw[i % nsets]:
+                rc = fn(*args)
+                if rc != 0:
+                    raise ops.MoeError(rc, fn.__name__)
         else:
             gpu_step(torch, ops, sets[i % nsets], w, dedup, side, receive)
 
     for i in range(a.warmup):
-        step(i)
+        if i == 0 and graphs is None:   # once through the Python binding, with its checks
+            gpu_step(torch, ops, sets[0], w, dedup, side, receive)
+        else:
+            step(i)
     torch.cuda.synchronize()
     # timed region: exactly K steps, synchronised on both sides
     t0 = time.perf_counter()
@@ -347,20 +424,20 @@ def main():
         if dedup:
             disp_calls.append((L.moe_dispatch_permute_dedup, (
                 b.x.data_ptr(), b.idx.data_ptr(), b.gate.data_ptr(), T, H, E, k, R,
-                b.place.data_ptr() if b.place is not None else None, 2, b.ws.data_ptr(),
+                b.place.data_ptr() if b.place is not None else None, bpe, b.ws.data_ptr(),
                 b.ws.numel(), d["send"].data_ptr(), d["row_token"].data_ptr(),
                 d["row_experts"].data_ptr(), d["row_gates"].data_ptr(),
                 d["row_weight"].data_ptr(), d["slot_row"].data_ptr(), d["n_rows"].data_ptr(), st)))
         else:
             disp_calls.append((L.moe_dispatch_permute, (
                 b.x.data_ptr(), b.idx.data_ptr(), b.gate.data_ptr(), T, H, E, k, R,
-                b.place.data_ptr() if b.place is not None else None, 2, b.ws.data_ptr(),
+                b.place.data_ptr() if b.place is not None else None, bpe, b.ws.data_ptr(),
                 b.ws.numel(), d["send"].data_ptr(), d["row_token"].data_ptr(),
                 d["row_expert"].data_ptr(), d["row_weight"].data_ptr(),
                 d["slot_row"].data_ptr(), st)))
         comb_calls.append((L.moe_combine, (
             d["send"].data_ptr(), d["row_weight"].data_ptr(), d["slot_row"].data_ptr(), T, H, k,
-            2, b.out.data_ptr(), st)))
+            bpe, b.out.data_ptr(), st)))
     exp_calls, red_calls = [], []
     if receive:
         N = T * k
@@ -368,12 +445,12 @@ def main():
             d, x = b.disp, b.exp
             exp_calls.append((L.moe_expand_permute, (
                 d["send"].data_ptr(), d["row_experts"].data_ptr(), d["row_gates"].data_ptr(),
-                d["n_rows"].data_ptr(), N, H, E, k, R, 2, b.ews.data_ptr(), b.ews.numel(),
+                d["n_rows"].data_ptr(), N, H, E, k, R, bpe, b.ews.data_ptr(), b.ews.numel(),
                 x["expanded"].data_ptr(), N, x["exp_row"].data_ptr(), x["exp_expert"].data_ptr(),
                 x["exp_gate"].data_ptr(), x["row_slot"].data_ptr(), st)))
             red_calls.append((L.moe_expand_reduce, (
                 x["expanded"].data_ptr(), x["exp_gate"].data_ptr(), x["row_slot"].data_ptr(),
-                d["n_rows"].data_ptr(), N, H, k, 2, b.red.data_ptr(), st)))
+                d["n_rows"].data_ptr(), N, H, k, bpe, b.red.data_ptr(), st)))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
     runs = [(disp_calls, ev[0], ev[1]), (comb_calls, ev[2], ev[3])]
     if receive:
@@ -396,9 +473,10 @@ def main():
     # rows actually written (N, or D for dedup)
     b = sets[0]
     n_rows = int(b.cnt["rank_offsets"][R].item())
-    row_bytes = H * 2
+    row_bytes = H * bpe                     # rows of x, send and expanded
+    out_bytes = H * 2                       # bf16 outputs of combine and reduce
     disp_bytes = row_bytes * (T + n_rows)   # read x once, write each row once
-    comb_bytes = row_bytes * (n_rows + T)   # read each row once, write out once
+    comb_bytes = row_bytes * n_rows + out_bytes * T  # read each row once, write out once
     meta_bytes = n_rows * (12 if not dedup else 8 + 8 * k) + T * k * 4
     dom = ("moe_dispatch_permute" + ("_dedup" if dedup else ""), t_disp, disp_bytes)
     if t_comb > t_disp:
@@ -409,7 +487,7 @@ def main():
     if receive:
         n_exp = int(b.ecnt["rank_offsets"][R].item())
         exp_bytes = row_bytes * (n_rows + n_exp)  # read each received row once, write each copy
-        red_bytes = row_bytes * (n_exp + n_rows)  # read each expert output once, write each row
+        red_bytes = row_bytes * n_exp + out_bytes * n_rows  # read each output once, write each row
         recv = {"expanded_rows": n_exp,
                 "expand_us": round(t_exp * 1e6, 2), "reduce_us": round(t_red * 1e6, 2),
                 "expand_GBps": round(exp_bytes / t_exp / 1e9, 1),
@@ -427,18 +505,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "hidden_dim": H, "n_experts": E,
                    "top_k": k, "n_ranks": R, "placement": w.placement,
                    "dispatch": "dedup" if dedup else "nondedup", "receive_side": receive,
-                   "bytes_per_element": 2, "graph": bool(a.graph),
+                   "bytes_per_element": bpe, "graph": bool(a.graph),
                    "coselect_stream": "side" if a.overlap else "main",
                    "buffer_sets": nsets, "footprint_MiB": round(nsets * per_set / 2 ** 20)},
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": counter_traffic(dom[0], w.name, "dedup" if dedup else "nondedup"),
+                     "traffic": (counter_traffic(dom[0], w.name, "dedup" if dedup else "nondedup")
+                                 if not fp8 else None),
                      "algorithmic_bytes": dom[2]},
         "dispatch_us": round(t_disp * 1e6, 2),
         "combine_us": round(t_comb * 1e6, 2),
@@ -455,7 +534,7 @@ def main():
     if a.search:
         res["placement_search"] = placement_leg(torch, ops, sets[0], w)
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, w, dedup, a.cpu_seconds, receive)
+        res["cpu_baseline"] = cpu_baseline(inp, w, dedup, a.cpu_seconds, receive, fp8)
     print(json.dumps(res), flush=True)
 
 
