@@ -1,8 +1,10 @@
 """The hot path captured in a HIP graph replays correctly.
 
-The chain (route -> counts -> dispatch -> combine -> co-selection) is captured
-once, then replayed several times with eager GPU work and synchronisations in
-between; every replay must reproduce the eager result bit for bit.
+The chain (route -> counts -> dispatch -> combine -> co-selection; in dedup
+mode also the receive side: expansion -> reduction -> weight-1 combine) is
+captured once, then replayed several times with eager GPU work and
+synchronisations in between; every replay must reproduce the eager result bit
+for bit.
 """
 import numpy as np
 import pytest
@@ -35,6 +37,18 @@ def _buffers(w, dedup, dev):
         b["disp"].update(row_experts=torch.empty((N, k), dtype=i32, device=dev),
                          row_gates=torch.empty((N, k), dtype=f32, device=dev),
                          n_rows=torch.empty(1, dtype=i32, device=dev))
+        b["ews"] = ops.expand_workspace(N, E, k, R, dev)
+        b["ecnt"] = {"expert_counts": torch.empty(E, dtype=i32, device=dev),
+                     "rank_counts": torch.empty(R, dtype=i32, device=dev),
+                     "rank_offsets": torch.empty(R + 1, dtype=i32, device=dev),
+                     "expert_offsets": torch.empty(E, dtype=i32, device=dev)}
+        b["exp"] = {"expanded": torch.empty((N, H), dtype=torch.bfloat16, device=dev),
+                    "exp_row": torch.empty(N, dtype=i32, device=dev),
+                    "exp_expert": torch.empty(N, dtype=i32, device=dev),
+                    "exp_gate": torch.empty(N, dtype=f32, device=dev),
+                    "row_slot": torch.empty((N, k), dtype=i32, device=dev)}
+        b["red"] = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+        b["out2"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     else:
         b["cnt"]["expert_offsets"] = torch.empty(E, dtype=i32, device=dev)
         b["disp"]["row_expert"] = torch.empty(N, dtype=i32, device=dev)
@@ -48,12 +62,31 @@ def _step(w, dedup, logits, x, place, b):
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
     d = f(x, b["idx"], b["gate"], E, R, c["ws"], place, out=b["disp"])
     ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b["out"])
+    if dedup:
+        ops.moe_expand_counts(d["row_experts"], d["n_rows"], E, R, place, ws=b["ews"],
+                              out=b["ecnt"])
+        ex = ops.moe_expand_permute(d["send"], d["row_experts"], d["row_gates"], d["n_rows"], E,
+                                    R, b["ews"], out=b["exp"])
+        red = ops.moe_expand_reduce(ex["expanded"], ex["exp_gate"], ex["row_slot"], d["n_rows"],
+                                    out=b["red"])
+        ops.moe_combine(red, None, d["slot_row"], out=b["out2"])
     ops.moe_coselect_counts(b["idx"], E, tokens=w.coselect_tokens, coselect=b["W"])
 
 
 def _snapshot(b):
     snap = {"idx": host(b["idx"]), "gate": host(b["gate"]).view(np.uint32),
             "out": bf16_host(b["out"]), "W": host(b["W"])}
+    if "ecnt" in b:
+        for key, v in b["ecnt"].items():
+            snap["e_" + key] = host(v)
+        ne = int(snap["e_rank_offsets"][-1])
+        D = int(host(b["disp"]["n_rows"])[0])
+        snap["expanded"] = bf16_host(b["exp"]["expanded"][:ne])
+        for key in ("exp_row", "exp_expert", "exp_gate"):
+            snap[key] = host(b["exp"][key][:ne]).copy()
+        snap["row_slot"] = host(b["exp"]["row_slot"][:D]).copy()
+        snap["red"] = bf16_host(b["red"][:D])
+        snap["out2"] = bf16_host(b["out2"])
     for key, v in b["cnt"].items():
         snap[key] = host(v)
     n = int(snap["rank_offsets"][-1])
@@ -98,6 +131,11 @@ def test_graph_replays_match_eager(name, dedup):
         for v in list(gb["cnt"].values()) + list(gb["disp"].values()):
             v.view(torch.uint8).fill_(0xA5)
         gb["out"].view(torch.uint8).fill_(0x5A)
+        if dedup:
+            for v in list(gb["ecnt"].values()) + list(gb["exp"].values()):
+                v.view(torch.uint8).fill_(0xA5)
+            gb["red"].view(torch.uint8).fill_(0x5A)
+            gb["out2"].view(torch.uint8).fill_(0x5A)
         gb["idx"].fill_(-1)
         gb["W"].zero_()
         torch.cuda.synchronize()

@@ -130,13 +130,25 @@ def test_dispatch_parity_small(oracle_mod, T, H, E, k, R, dedup, pl):
 
 @pytest.mark.parametrize("dedup", [False, True])
 def test_dispatch_parity_large_plan(oracle_mod, dedup):
-    """70000 tokens: the per-tile plan no longer fits one workgroup's LDS, so
-    the counts take the two-kernel path (tile counts, then a scan)."""
+    """70000 tokens, explicit placement: 1094 tiles, 69 tile-count vectors per
+    column dealt to 16 lanes each (5 per lane) in the scan."""
     T, H, E, k, R = 70000, 32, 64, 4, 16
     say(f"[dispatch] large plan T={T} dedup={dedup}")
     inp = WL.make_custom_inputs(T, H, E, seed=99)
     idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
     placement = WL.random_placement(E, R, seed=5)
+    run_dispatch_parity(oracle_mod, inp["x_bits"], idx_o, gate_o, E, R, placement, dedup)
+
+
+@pytest.mark.parametrize("dedup,pl", [(False, "contiguous"), (False, "random"), (True, "random")])
+def test_dispatch_parity_huge_plan(oracle_mod, dedup, pl):
+    """300000 tokens: 4688 tiles, 293 vectors per column, more than the scan
+    keeps in registers, so it takes the looping variant (one lane per column)."""
+    T, H, E, k, R = 300000, 16, 8, 2, 4
+    say(f"[dispatch] huge plan T={T} dedup={dedup} placement={pl}")
+    inp = WL.make_custom_inputs(T, H, E, seed=101)
+    idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+    placement = None if pl == "contiguous" else WL.random_placement(E, R, seed=6)
     run_dispatch_parity(oracle_mod, inp["x_bits"], idx_o, gate_o, E, R, placement, dedup)
 
 
