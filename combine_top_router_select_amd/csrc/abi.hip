@@ -9,7 +9,7 @@
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
 namespace moe {
-hipError_t launch_route_topk(const float*, int64_t, int, int, int32_t*, float*, hipStream_t);
+hipError_t launch_route_topk(const float*, int64_t, int, int, int, int32_t*, float*, hipStream_t);
 hipError_t launch_send_counts(const int32_t*, int64_t, int, int, int, const int32_t*, int,
                               int32_t*, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
 hipError_t launch_dispatch(const void*, const int32_t*, const float*, int64_t, int, int, int,
@@ -82,7 +82,18 @@ MOE_API int moe_route_topk(const float* logits, int64_t tokens, int n_experts, i
   if (st != MOE_OK) return st;
   if (tokens == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_gate) return MOE_EINVAL;
-  return hip_status(moe::launch_route_topk(logits, tokens, n_experts, top_k, topk_idx,
+  return hip_status(moe::launch_route_topk(logits, tokens, n_experts, top_k, 0, topk_idx,
+                                           topk_gate, as_stream(stream)));
+}
+
+MOE_API int moe_route_topk_softmax_all(const float* logits, int64_t tokens, int n_experts,
+                                       int top_k, int32_t* topk_idx, float* topk_gate,
+                                       void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if (tokens == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_gate) return MOE_EINVAL;
+  return hip_status(moe::launch_route_topk(logits, tokens, n_experts, top_k, 1, topk_idx,
                                            topk_gate, as_stream(stream)));
 }
 

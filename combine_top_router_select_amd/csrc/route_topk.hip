@@ -16,6 +16,8 @@
 // no LDS round trip), and retires the winning key.  Lane j of the group keeps
 // the round-j winner.  Gates are computed in fp64 (exp of the logit minus the
 // largest one, divided by their DPP-summed total) and rounded once to fp32.
+// FULL: the total runs over all E logits instead of the k selected ones
+// (softmax over every expert, not renormalised over the selection).
 #include <math.h>
 
 #include "common.hpp"
@@ -82,7 +84,7 @@ __device__ __forceinline__ double group_sum(double v) {
   return v;
 }
 
-template <int L, int V>
+template <int L, int V, bool FULL>
 __global__ void __launch_bounds__(256)
 route_topk_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k,
                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
@@ -126,7 +128,14 @@ route_topk_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k
       }
     }
     const double d = (li < k) ? exp(double(my_f) - double(l0)) : 0.0;
-    const double s = group_sum<L>(d);
+    double part = d;
+    if (FULL) {
+      part = 0.0;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        part += (li + L * v < E) ? exp(double(f[v]) - double(l0)) : 0.0;
+    }
+    const double s = group_sum<L>(part);
     if (tok_ok && li < k) {
       topk_idx[t * k + li] = my_e;
       topk_gate[t * k + li] = float(d / s);
@@ -134,31 +143,40 @@ route_topk_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k
   }
 }
 
-template <int L, int V>
+template <int L, int V, bool FULL>
 static hipError_t launch_route(const float* logits, int64_t tokens, int E, int k, int32_t* idx,
                                float* gate, hipStream_t stream) {
   constexpr int G = kWave / L;
   const int64_t per_block = 4 * G;
   int64_t blocks = (tokens + per_block - 1) / per_block;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((route_topk_kernel<L, V>), dim3(unsigned(blocks)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((route_topk_kernel<L, V, FULL>), dim3(unsigned(blocks)), dim3(256), 0, stream,
                      logits, tokens, E, k, idx, gate);
   return hipGetLastError();
 }
 
-hipError_t launch_route_topk(const float* logits, int64_t tokens, int E, int k, int32_t* idx,
-                             float* gate, hipStream_t stream) {
-  if (E <= 1) return launch_route<1, 1>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 2) return launch_route<2, 1>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 4) return launch_route<4, 1>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 8) return launch_route<8, 1>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 16) return launch_route<16, 1>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 32) return launch_route<16, 2>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 64) return launch_route<16, 4>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 128) return launch_route<16, 8>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 256) return launch_route<16, 16>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 512) return launch_route<16, 32>(logits, tokens, E, k, idx, gate, stream);
-  return launch_route<16, 64>(logits, tokens, E, k, idx, gate, stream);
+template <bool FULL>
+static hipError_t launch_route_e(const float* logits, int64_t tokens, int E, int k, int32_t* idx,
+                                 float* gate, hipStream_t stream) {
+  if (E <= 1) return launch_route<1, 1, FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E <= 2) return launch_route<2, 1, FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E <= 4) return launch_route<4, 1, FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E <= 8) return launch_route<8, 1, FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E <= 16) return launch_route<16, 1, FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E <= 32) return launch_route<16, 2, FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E <= 64) return launch_route<16, 4, FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E <= 128) return launch_route<16, 8, FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E <= 256) return launch_route<16, 16, FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E <= 512) return launch_route<16, 32, FULL>(logits, tokens, E, k, idx, gate, stream);
+  return launch_route<16, 64, FULL>(logits, tokens, E, k, idx, gate, stream);
+}
+
+// full_softmax: gates are the softmax over all E logits at the selected
+// experts; otherwise the softmax over the k selected logits.
+hipError_t launch_route_topk(const float* logits, int64_t tokens, int E, int k, int full_softmax,
+                             int32_t* idx, float* gate, hipStream_t stream) {
+  if (full_softmax) return launch_route_e<true>(logits, tokens, E, k, idx, gate, stream);
+  return launch_route_e<false>(logits, tokens, E, k, idx, gate, stream);
 }
 
 }  // namespace moe

@@ -62,7 +62,11 @@ def workspace(tokens, n_experts, top_k, n_ranks, dedup, device) -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def moe_route_topk(logits, top_k, topk_idx=None, topk_gate=None, stream=None):
+def moe_route_topk(logits, top_k, topk_idx=None, topk_gate=None, stream=None,
+                   softmax_all=False):
+    """Top-k experts per token and their gates: softmax over the k selected
+    logits, or (softmax_all) the softmax over all E logits at the selected
+    experts (moe_route_topk_softmax_all)."""
     _dev(logits, "logits", torch.float32, 2)
     T, E = logits.shape
     if topk_idx is None:
@@ -71,8 +75,9 @@ def moe_route_topk(logits, top_k, topk_idx=None, topk_gate=None, stream=None):
         topk_gate = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
     _dev(topk_idx, "topk_idx", torch.int32)
     _dev(topk_gate, "topk_gate", torch.float32)
-    check(lib().moe_route_topk(_ptr(logits), T, E, top_k, _ptr(topk_idx), _ptr(topk_gate),
-                               _stream(stream)), "moe_route_topk")
+    fn = lib().moe_route_topk_softmax_all if softmax_all else lib().moe_route_topk
+    check(fn(_ptr(logits), T, E, top_k, _ptr(topk_idx), _ptr(topk_gate), _stream(stream)),
+          "moe_route_topk_softmax_all" if softmax_all else "moe_route_topk")
     return topk_idx, topk_gate
 
 

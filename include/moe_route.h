@@ -93,6 +93,16 @@ size_t moe_workspace_bytes(int64_t tokens, int n_experts, int top_k, int n_ranks
 int moe_route_topk(const float* logits, int64_t tokens, int n_experts, int top_k,
                    int32_t* topk_idx, float* topk_gate, void* stream);
 
+/* A1, gating variant: the same expert selection as moe_route_topk(), with
+ * topk_gate[t][j] = exp(l_j - l_0) / (sum over all E experts e of
+ * exp(l_e - l_0)), i.e. the softmax over every expert's logit taken at the
+ * selected ones, not renormalised over the selection (the pages speak of
+ * routing probabilities without fixing the normalisation; this is the other
+ * common reading).  fp64 inside, one rounding to fp32.  Arguments and errors
+ * as moe_route_topk(). */
+int moe_route_topk_softmax_all(const float* logits, int64_t tokens, int n_experts, int top_k,
+                               int32_t* topk_idx, float* topk_gate, void* stream);
+
 /* A2 + A3 - send counts and their exclusive scan ([DD] "Setup", "Reading the
  * counts"; [EC] "Method 1").
  *   topk_idx       [T][k] int32, read only (expert ids in [0, E)).

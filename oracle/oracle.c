@@ -93,6 +93,25 @@ int oracle_route_topk(const float* logits, int64_t tokens, int n_experts, int to
     return 0;
 }
 
+/* The same selection; gate[t][j] = exp(l_j - l_0) / sum over all E experts e
+ * of exp(l_e - l_0): the softmax over every logit, taken at the selected
+ * experts and not renormalised (the other reading of "routing
+ * probabilities").  fp64, summed in expert order, rounded once. */
+int oracle_route_topk_softmax_all(const float* logits, int64_t tokens, int n_experts, int top_k,
+                                  int32_t* idx, float* gate) {
+    int rc = oracle_route_topk(logits, tokens, n_experts, top_k, idx, gate);
+    if (rc) return rc;
+    for (int64_t t = 0; t < tokens; ++t) {
+        const float* row = logits + t * n_experts;
+        const double l0 = (double)row[idx[t * top_k]];
+        double s = 0.0;
+        for (int e = 0; e < n_experts; ++e) s += exp((double)row[e] - l0);
+        for (int j = 0; j < top_k; ++j)
+            gate[t * top_k + j] = (float)(exp((double)row[idx[t * top_k + j]] - l0) / s);
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------- counts, offsets --- */
 
 /* [DD] "Reading the counts" and [EC] "Method 1".

@@ -43,6 +43,7 @@ def lib():
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int
         L.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
+        L.oracle_route_topk_softmax_all.argtypes = [P, i64, i32, i32, P, P]
         L.oracle_send_counts.argtypes = [P, i64, i32, i32, i32, P, i32, P, P, P, P]
         L.oracle_dispatch.argtypes = [P, P, P, i64, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_dispatch_dedup.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P,
@@ -60,7 +61,8 @@ def lib():
         L.oracle_placement_objective.restype = ctypes.c_int64
         L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
         L.oracle_bf16_from_double.restype = ctypes.c_uint16
-        for f in ("oracle_route_topk", "oracle_send_counts", "oracle_dispatch",
+        for f in ("oracle_route_topk", "oracle_route_topk_softmax_all", "oracle_send_counts",
+                  "oracle_dispatch",
                   "oracle_dispatch_dedup", "oracle_expand_dedup", "oracle_combine",
                   "oracle_combine_fp8", "oracle_coselect"):
             getattr(L, f).restype = ctypes.c_int
@@ -91,6 +93,16 @@ def route_topk(logits, top_k):
     idx = np.empty((T, top_k), np.int32)
     gate = np.empty((T, top_k), np.float32)
     _check(lib().oracle_route_topk(_p(logits), T, E, top_k, _p(idx), _p(gate)), "route")
+    return idx, gate
+
+
+def route_topk_softmax_all(logits, top_k):
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, top_k), np.int32)
+    gate = np.empty((T, top_k), np.float32)
+    _check(lib().oracle_route_topk_softmax_all(_p(logits), T, E, top_k, _p(idx), _p(gate)),
+           "route_softmax_all")
     return idx, gate
 
 

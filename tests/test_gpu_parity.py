@@ -535,3 +535,15 @@ def test_fp8_reduce(oracle_mod):
     sync()
     Yf = torch.from_numpy(Y).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     assert _bound_ok(bf16_host(out[:D]), ref, Yf, ref_ex["exp_gate"], ref_ex["row_slot"][:D], k)
+
+
+@pytest.mark.parametrize("T,E,k", [(1000, 64, 6), (777, 128, 8), (300, 8, 8), (130, 1024, 16),
+                                   (129, 1, 1), (257, 3, 2)])
+def test_route_softmax_all_parity(oracle_mod, T, E, k):
+    say(f"[route softmax_all] T={T} E={E} k={k}")
+    inp = WL.make_custom_inputs(T, 8, E, seed=T + 5 * E + k)
+    idx_o, gate_o = oracle_mod.route_topk_softmax_all(inp["logits"], k)
+    idx, gate = ops.moe_route_topk(to_dev(inp["logits"]), k, softmax_all=True)
+    sync()
+    assert (host(idx) == idx_o).all()
+    assert f32_ulp_diff(host(gate), gate_o).max() <= 1

@@ -592,3 +592,22 @@ def test_fp8_single_row_is_exact(oracle_mod):
     ref = (torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float32)
            .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
     assert (out == ref).all()
+
+
+# ------------------------------------------------- softmax over all experts --
+
+def test_softmax_all_gates(oracle_mod):
+    """Same selection as the k-softmax; gates equal torch's float64 softmax over
+    all logits at the selected experts (within 1 fp32 ulp: summation order);
+    at k = E they are the k-softmax gates."""
+    for T, E, k in ((300, 64, 6), (200, 128, 8), (50, 8, 8), (40, 3, 1)):
+        inp = WL.make_custom_inputs(T, 1, E, seed=T + E)
+        idx, gate = oracle_mod.route_topk_softmax_all(inp["logits"], k)
+        idx_k, gate_k = oracle_mod.route_topk(inp["logits"], k)
+        assert (idx == idx_k).all()
+        p = torch.softmax(torch.from_numpy(inp["logits"]).double(), dim=1).numpy()
+        ref = np.take_along_axis(p, idx.astype(np.int64), axis=1).astype(np.float32)
+        assert f32_ulp_diff(gate, ref).max() <= 1
+        assert (gate.astype(np.float64).sum(1) <= 1 + k * 2.0 ** -24).all()
+        if k == E:
+            assert f32_ulp_diff(gate, gate_k).max() <= 1
