@@ -525,9 +525,14 @@ def main():
         "dispatch_combine_GBps": round(dc_gbps, 1),
         "dispatch_combine_hbm_frac": round(dc_gbps / HBM_PEAK_GBPS, 4),
         "rows": n_rows,
+        "rows_removed_by_dedup_pct": round(100.0 * (1 - n_rows / (T * k)), 2) if dedup else 0.0,
+        # rows that stay on source rank 0 (the diagonal of the send matrix)
+        "self_rank_share": round(int(b.cnt["rank_counts"][0].item()) / n_rows, 4),
         "algorithmic_bytes": {"dispatch": disp_bytes, "combine": comb_bytes,
                               "metadata": meta_bytes},
         "device": torch.cuda.get_device_name(0),
+        "hip_version": getattr(torch.version, "hip", None),
+        "host_cores_available": len(os.sched_getaffinity(0)),
     }
     if recv is not None:
         res["receive"] = recv

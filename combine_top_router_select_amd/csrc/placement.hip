@@ -14,6 +14,7 @@
 //   A[e][b] + A[f][a] - A[e][a] - A[f][b] - 2 S(e, f).
 // A is kept up to date in O(E) per swap, so a pass over all pairs is O(E^2).
 // Runs on the host: E <= 1024, and the search is sequential by nature.
+#include <stddef.h>
 #include <stdint.h>
 
 #include <vector>
