@@ -33,7 +33,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "make_custom_inputs",
-           "bf16_bits_from_f32", "contiguous_placement"]
+           "bf16_bits_from_f32", "contiguous_placement", "make_layer_logits", "random_placement"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -202,6 +202,35 @@ def make_custom_inputs(tokens: int, hidden_dim: int, n_experts: int, seed: int =
         vals = np.asarray(logit_values, dtype=np.float32)
         logits = vals[gl.integers(0, len(vals), size=(tokens, n_experts))]
     return {"x_bits": x, "logits": np.ascontiguousarray(logits, dtype=np.float32)}
+
+
+def make_layer_logits(w: Workload, n_layers: int = 3, seed: int = 1,
+                      path_share: float = 0.6, boost: float = 4.0) -> List[np.ndarray]:
+    """Router logits of `n_layers` consecutive MoE layers with cross-layer
+    correlation (Expert Coupling summary, "Key Theoretical Insight": the
+    experts a token selects at one layer predict its experts at the next).
+
+    E seeded expert paths are drawn, one expert per layer each, every expert on
+    exactly one path at every layer (a permutation per layer); a `path_share` of
+    the tokens each follows one path, uniformly chosen, and gets `boost` added
+    to its path's expert at every layer.  The correlation comes from the shared
+    latent path only: nothing here routes tokens."""
+    ss = np.random.SeedSequence([w.seed, seed])
+    s_paths, s_tok, *s_layers = ss.spawn(2 + n_layers)
+    T, E = w.tokens, w.n_experts
+    gp = np.random.Generator(np.random.PCG64(s_paths))
+    paths = np.stack([gp.permutation(E) for _ in range(n_layers)], axis=1)
+    gt = np.random.Generator(np.random.PCG64(s_tok))
+    follows = gt.random(T) < path_share
+    which = gt.integers(0, E, size=T)
+    out = []
+    for layer in range(n_layers):
+        g = np.random.Generator(np.random.PCG64(s_layers[layer]))
+        lg = g.standard_normal((T, E), dtype=np.float32)
+        toks = np.nonzero(follows)[0]
+        lg[toks, paths[which[toks], layer]] += np.float32(boost)
+        out.append(lg)
+    return out
 
 
 def random_placement(n_experts: int, n_ranks: int, seed: int) -> np.ndarray:

@@ -475,3 +475,115 @@ int oracle_placement_search(const int32_t* W, int n_experts, int n_ranks, const 
     if (swaps) *swaps = done;
     return 0;
 }
+
+/* ------------------------------------------------ token shuffle planner --- */
+
+/* [EC] "Method 2: Token Shuffling", prediction: a token's owner rank at layer
+ * l+1 is predicted from the experts it selected at the two preceding MoE
+ * layers (l-1 and l), by a pair lookup with a single-expert fallback when the
+ * pair was seen too rarely.  Reading (the page prints no formula): on a
+ * calibration batch, for every token, every expert c it selects at l+1 (rank
+ * r = place_next[c]) and every pair (a, b) of its experts at l-1 and l,
+ *   pair[a][b][r] += 1;   and for every b at l:  single[b][r] += 1.
+ * Both tables accumulate (caller-zeroed int32). */
+int oracle_shuffle_fit(const int32_t* prev, const int32_t* cur, const int32_t* next,
+                       int64_t tokens, int n_experts, int top_k, int n_ranks,
+                       const int32_t* place_next, int32_t* pair, int32_t* single) {
+    const int E = n_experts, k = top_k, R = n_ranks;
+    for (int64_t t = 0; t < tokens; ++t) {
+        for (int jc = 0; jc < k; ++jc) {
+            const int r = place_next[next[t * k + jc]];
+            for (int ja = 0; ja < k; ++ja)
+                for (int jb = 0; jb < k; ++jb) {
+                    const int a = prev[t * k + ja], b = cur[t * k + jb];
+                    pair[((int64_t)a * E + b) * R + r] += 1;
+                }
+            for (int jb = 0; jb < k; ++jb) single[(int64_t)cur[t * k + jb] * R + r] += 1;
+        }
+    }
+    return 0;
+}
+
+/* Scores of every rank for every token: the sum over the token's (a, b) pairs,
+ * in slot order (a's slot, then b's), of the pair's rank distribution
+ * pair[a][b][r] / sum_r pair[a][b][r] when that sum is at least min_obs, else
+ * of b's distribution single[b][r] / sum_r single[b][r] (nothing when b was
+ * never seen).  fp64, one rounding to fp32 per score. */
+int oracle_shuffle_predict(const int32_t* prev, const int32_t* cur, int64_t tokens,
+                           int n_experts, int top_k, int n_ranks, const int32_t* pair,
+                           const int32_t* single, int min_obs, float* scores) {
+    const int E = n_experts, k = top_k, R = n_ranks;
+    double* sc = (double*)malloc(sizeof(double) * (size_t)R);
+    if (!sc) return 2;
+    for (int64_t t = 0; t < tokens; ++t) {
+        for (int r = 0; r < R; ++r) sc[r] = 0.0;
+        for (int ja = 0; ja < k; ++ja) {
+            for (int jb = 0; jb < k; ++jb) {
+                const int a = prev[t * k + ja], b = cur[t * k + jb];
+                const int32_t* pr = pair + ((int64_t)a * E + b) * R;
+                int64_t n = 0;
+                for (int r = 0; r < R; ++r) n += pr[r];
+                if (n >= min_obs && n > 0) {
+                    for (int r = 0; r < R; ++r) sc[r] += (double)pr[r] / (double)n;
+                } else {
+                    const int32_t* sr = single + (int64_t)b * R;
+                    int64_t m = 0;
+                    for (int r = 0; r < R; ++r) m += sr[r];
+                    if (m > 0)
+                        for (int r = 0; r < R; ++r) sc[r] += (double)sr[r] / (double)m;
+                }
+            }
+        }
+        for (int r = 0; r < R; ++r) scores[t * R + r] = (float)sc[r];
+    }
+    free(sc);
+    return 0;
+}
+
+/* "Capacity Constraint": every rank owns exactly T/R tokens (T % R == 0);
+ * tokens are taken in decreasing confidence = (largest score) / (sum of
+ * scores) (0 for an all-zero row; computed in fp64 from the fp32 scores; ties
+ * to the lower token index) and each goes to its highest-scoring rank that
+ * still has room (ties to the lower rank). */
+typedef struct { double conf; int64_t t; } oracle_conf;
+
+static int oracle_conf_cmp(const void* pa, const void* pb) {
+    const oracle_conf* a = (const oracle_conf*)pa;
+    const oracle_conf* b = (const oracle_conf*)pb;
+    if (a->conf > b->conf) return -1;
+    if (a->conf < b->conf) return 1;
+    return (a->t > b->t) - (a->t < b->t);
+}
+
+int oracle_shuffle_assign(const float* scores, int64_t tokens, int n_ranks, int32_t* owner) {
+    const int R = n_ranks;
+    if (tokens % R != 0) return 1;
+    oracle_conf* c = (oracle_conf*)malloc(sizeof(oracle_conf) * (size_t)(tokens > 0 ? tokens : 1));
+    int64_t* room = (int64_t*)malloc(sizeof(int64_t) * (size_t)R);
+    if (!c || !room) { free(c); free(room); return 2; }
+    for (int64_t t = 0; t < tokens; ++t) {
+        double mx = 0.0, sum = 0.0;
+        for (int r = 0; r < R; ++r) {
+            const double v = (double)scores[t * R + r];
+            sum += v;
+            if (v > mx) mx = v;
+        }
+        c[t].conf = sum > 0.0 ? mx / sum : 0.0;
+        c[t].t = t;
+    }
+    qsort(c, (size_t)tokens, sizeof(oracle_conf), oracle_conf_cmp);
+    for (int r = 0; r < R; ++r) room[r] = tokens / R;
+    for (int64_t i = 0; i < tokens; ++i) {
+        const int64_t t = c[i].t;
+        int best = -1;
+        for (int r = 0; r < R; ++r) {
+            if (room[r] == 0) continue;
+            if (best < 0 || scores[t * R + r] > scores[t * R + best]) best = r;
+        }
+        owner[t] = best;
+        room[best] -= 1;
+    }
+    free(c);
+    free(room);
+    return 0;
+}

@@ -59,6 +59,11 @@ def lib():
         L.oracle_placement_search.restype = ctypes.c_int
         L.oracle_placement_objective.argtypes = [P, i32, P]
         L.oracle_placement_objective.restype = ctypes.c_int64
+        L.oracle_shuffle_fit.argtypes = [P, P, P, i64, i32, i32, i32, P, P, P]
+        L.oracle_shuffle_predict.argtypes = [P, P, i64, i32, i32, i32, P, P, i32, P]
+        L.oracle_shuffle_assign.argtypes = [P, i64, i32, P]
+        for f in ("oracle_shuffle_fit", "oracle_shuffle_predict", "oracle_shuffle_assign"):
+            getattr(L, f).restype = ctypes.c_int
         L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
         L.oracle_bf16_from_double.restype = ctypes.c_uint16
         for f in ("oracle_route_topk", "oracle_route_topk_softmax_all", "oracle_send_counts",
@@ -272,3 +277,36 @@ def placement_search(W, n_ranks, initial=None, max_swaps=None):
     _check(lib().oracle_placement_search(_p(W), E, n_ranks, _p(init), ms, _p(place), _p(obj),
                                          _p(sw)), "placement_search")
     return place, int(obj[0]), int(sw[0])
+
+
+def shuffle_fit(prev, cur, nxt, n_experts, n_ranks, place_next=None, pair=None, single=None):
+    prev, cur, nxt = (_c(a, np.int32) for a in (prev, cur, nxt))
+    T, k = cur.shape
+    E, R = n_experts, n_ranks
+    place = contiguous(E, R) if place_next is None else _c(place_next, np.int32)
+    if pair is None:
+        pair = np.zeros((E, E, R), np.int32)
+    if single is None:
+        single = np.zeros((E, R), np.int32)
+    _check(lib().oracle_shuffle_fit(_p(prev), _p(cur), _p(nxt), T, E, k, R, _p(place),
+                                    _p(pair), _p(single)), "shuffle_fit")
+    return pair, single
+
+
+def shuffle_predict(prev, cur, pair, single, min_obs):
+    prev, cur = _c(prev, np.int32), _c(cur, np.int32)
+    pair, single = _c(pair, np.int32), _c(single, np.int32)
+    T, k = cur.shape
+    E, R = single.shape
+    scores = np.empty((T, R), np.float32)
+    _check(lib().oracle_shuffle_predict(_p(prev), _p(cur), T, E, k, R, _p(pair), _p(single),
+                                        int(min_obs), _p(scores)), "shuffle_predict")
+    return scores
+
+
+def shuffle_assign(scores):
+    scores = _c(scores, np.float32)
+    T, R = scores.shape
+    owner = np.empty(T, np.int32)
+    _check(lib().oracle_shuffle_assign(_p(scores), T, R, _p(owner)), "shuffle_assign")
+    return owner

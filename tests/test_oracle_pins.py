@@ -611,3 +611,77 @@ def test_softmax_all_gates(oracle_mod):
         assert (gate.astype(np.float64).sum(1) <= 1 + k * 2.0 ** -24).all()
         if k == E:
             assert f32_ulp_diff(gate, gate_k).max() <= 1
+
+
+# ---------------------------------------------------- token shuffle planner --
+
+def _routes(rng, T, E, k, n=3):
+    return [np.array([rng.choice(E, k, replace=False) for _ in range(T)], np.int32)
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("T,E,k,R", [(40, 8, 2, 4), (33, 6, 3, 3), (64, 16, 1, 8), (20, 4, 4, 2)])
+def test_shuffle_fit_counts(oracle_mod, T, E, k, R):
+    """Fit tables by enumeration: every (a at l-1, b at l, rank of c at l+1)
+    triple counted once per token; single[b][r] = sum over a of pair / k."""
+    from collections import Counter
+    rng = np.random.default_rng(T + E)
+    prev, cur, nxt = _routes(rng, T, E, k)
+    place = WL.random_placement(E, R, seed=T)
+    pair, single = oracle_mod.shuffle_fit(prev, cur, nxt, E, R, place)
+    cnt = Counter((a, b, int(place[c])) for t in range(T) for a in prev[t] for b in cur[t]
+                  for c in nxt[t])
+    ref = np.zeros((E, E, R), np.int64)
+    for (a, b, r), v in cnt.items():
+        ref[a, b, r] = v
+    assert (pair == ref).all()
+    assert (pair.sum(axis=0) == k * single).all()
+    assert pair.sum() == T * k ** 3 and single.sum() == T * k ** 2
+
+
+def test_shuffle_predict_properties(oracle_mod):
+    """Each (a, b) pair adds one probability distribution: scores sum to k^2
+    when every pair or its fallback was seen; with min_obs above every count
+    the scores are the single-expert fallback alone; a rank that took every
+    calibration token of a pair is that pair's only rank."""
+    T, E, k, R = 200, 8, 2, 4
+    rng = np.random.default_rng(1)
+    prev, cur, nxt = _routes(rng, T, E, k)
+    pair, single = oracle_mod.shuffle_fit(prev, cur, nxt, E, R)
+    s = oracle_mod.shuffle_predict(prev, cur, pair, single, 1)
+    assert np.abs(s.astype(np.float64).sum(1) - k * k).max() < 1e-5
+    fb = oracle_mod.shuffle_predict(prev, cur, pair, single, 10 ** 9)
+    sd = single / single.sum(1, keepdims=True)
+    ref = np.stack([k * sd[cur[t]].sum(0) for t in range(T)])
+    assert np.abs(fb - ref).max() < 1e-5
+    # a planted route: every calibration token goes to rank 3 at l+1
+    place = np.full(E, 3, np.int32)
+    place[:6] = [0, 0, 1, 1, 2, 2]
+    nxt3 = np.tile(np.array([6, 7], np.int32), (T, 1))
+    pair3, single3 = oracle_mod.shuffle_fit(prev, cur, nxt3, E, R, np.array(place))
+    s3 = oracle_mod.shuffle_predict(prev, cur, pair3, single3, 1)
+    assert (s3.argmax(1) == 3).all() and (s3[:, :3] == 0).all()
+
+
+def test_shuffle_assign_properties(oracle_mod):
+    """Every rank owns exactly T/R tokens; when each rank is the top choice of
+    exactly T/R tokens every token gets its top choice; a token never gets a
+    lower-scoring rank while a higher-scoring one of its ranks had room when
+    it was placed (checked by replaying the confidence order)."""
+    rng = np.random.default_rng(2)
+    T, R = 96, 4
+    s = rng.random((T, R)).astype(np.float32)
+    own = oracle_mod.shuffle_assign(s)
+    assert (np.bincount(own, minlength=R) == T // R).all()
+    top = np.repeat(np.arange(R), T // R)
+    rng.shuffle(top)
+    s2 = rng.random((T, R)).astype(np.float32) * 0.5
+    s2[np.arange(T), top] = 1.0
+    assert (oracle_mod.shuffle_assign(s2) == top).all()
+    conf = s.astype(np.float64).max(1) / s.astype(np.float64).sum(1)
+    order = sorted(range(T), key=lambda t: (-conf[t], t))
+    room = [T // R] * R
+    for t in order:
+        better = [r for r in range(R) if s[t, r] > s[t, own[t]]]
+        assert all(room[r] == 0 for r in better)
+        room[own[t]] -= 1

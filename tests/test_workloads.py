@@ -111,3 +111,25 @@ def test_dodoco_shaped_workloads_match_the_model_table():
     for w in shaped:
         assert (w.n_experts, w.top_k, w.hidden_dim) in rows, w.name
         assert w.placement == "contiguous"
+
+
+def test_layer_logits_cross_layer_correlation(oracle_mod):
+    """The multi-layer generator gives the cross-layer statistic the Expert
+    Coupling summary reports ("Key Theoretical Insight": most layer-l experts
+    send >= 30% of their tokens to one layer-(l+1) expert, median share 48%),
+    measured on the top-1 choices; reported, asserted only loosely."""
+    w = WL.get("zyphra_top2_ep8")
+    L = WL.make_layer_logits(w)
+    assert len(L) == 3 and all(l.shape == (w.tokens, w.n_experts) for l in L)
+    a = oracle_mod.route_topk(L[1][:8192], w.top_k)[0][:, 0]
+    b = oracle_mod.route_topk(L[2][:8192], w.top_k)[0][:, 0]
+    share = []
+    for e in range(w.n_experts):
+        m = a == e
+        if m.any():
+            share.append(np.bincount(b[m], minlength=w.n_experts).max() / m.sum())
+    share = np.array(share)
+    assert 0.35 <= np.median(share) <= 0.65
+    assert (share >= 0.3).sum() >= 100
+    again = WL.make_layer_logits(w)
+    assert all((x == y).all() for x, y in zip(L, again))
