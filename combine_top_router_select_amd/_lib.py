@@ -15,7 +15,8 @@ SYMBOLS = ("moe_status_string", "moe_workspace_bytes", "moe_expand_workspace_byt
            "moe_route_topk", "moe_send_counts", "moe_dispatch_permute",
            "moe_dispatch_permute_dedup", "moe_combine", "moe_coselect_counts",
            "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
-           "moe_placement_search", "moe_route_topk_softmax_all")
+           "moe_placement_search", "moe_route_topk_softmax_all", "moe_shuffle_fit",
+           "moe_shuffle_predict", "moe_shuffle_assign")
 
 _lib = None
 
@@ -55,6 +56,9 @@ def lib():
                                          P, P, P, P, P]
         L.moe_expand_reduce.argtypes = [P, P, P, P, i64, i32, i32, i32, P, P]
         L.moe_placement_search.argtypes = [P, i32, i32, P, i32, P, P, P]
+        L.moe_shuffle_fit.argtypes = [P, P, P, i64, i32, i32, i32, P, P, P, P]
+        L.moe_shuffle_predict.argtypes = [P, P, i64, i32, i32, i32, P, P, i32, P, P]
+        L.moe_shuffle_assign.argtypes = [P, i64, i32, P]
         for s in SYMBOLS[3:]:
             getattr(L, s).restype = i32
         _lib = L

@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "route_topk.hip", "counts.hip", "dispatch.hip", "combine.hip",
-           "coselect.hip", "placement.hip"]
+           "coselect.hip", "placement.hip", "shuffle.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

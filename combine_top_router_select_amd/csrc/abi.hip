@@ -24,6 +24,11 @@ hipError_t launch_expand(const void*, const float*, const int32_t*, int64_t, int
                          const void*, void*, int64_t, int32_t*, int32_t*, float*, int32_t*,
                          hipStream_t);
 int placement_search(const int32_t*, int, int, const int32_t*, int, int32_t*, int64_t*, int*);
+hipError_t launch_shuffle_fit(const int32_t*, const int32_t*, const int32_t*, int64_t, int, int,
+                              int, const int32_t*, int32_t*, int32_t*, hipStream_t);
+hipError_t launch_shuffle_predict(const int32_t*, const int32_t*, int64_t, int, int, int,
+                                  const int32_t*, const int32_t*, int, float*, hipStream_t);
+int shuffle_assign(const float*, int64_t, int, int32_t*);
 hipError_t launch_coselect(const int32_t*, int64_t, int, int, int32_t*, hipStream_t);
 }  // namespace moe
 
@@ -283,4 +288,44 @@ MOE_API int moe_placement_search(const int32_t* coselect, int n_experts, int n_r
   }
   return moe::placement_search(coselect, n_experts, n_ranks, initial, max_swaps, placement,
                                objective, swaps);
+}
+
+MOE_API int moe_shuffle_fit(const int32_t* prev_idx, const int32_t* cur_idx,
+                            const int32_t* next_idx, int64_t tokens, int n_experts, int top_k,
+                            int n_ranks, const int32_t* placement_next, int32_t* pair_counts,
+                            int32_t* single_counts, void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if (!pair_counts || !single_counts) return MOE_EINVAL;
+  if (tokens == 0) return MOE_OK;
+  if (!prev_idx || !cur_idx || !next_idx) return MOE_EINVAL;
+  return hip_status(moe::launch_shuffle_fit(prev_idx, cur_idx, next_idx, tokens, n_experts, top_k,
+                                            n_ranks, placement_next, pair_counts, single_counts,
+                                            as_stream(stream)));
+}
+
+MOE_API int moe_shuffle_predict(const int32_t* prev_idx, const int32_t* cur_idx, int64_t tokens,
+                                int n_experts, int top_k, int n_ranks, const int32_t* pair_counts,
+                                const int32_t* single_counts, int min_obs, float* scores,
+                                void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if (min_obs < 0) return MOE_EINVAL;
+  if (tokens > int64_t(INT_MAX) / n_ranks) return MOE_EUNSUPPORTED;
+  if (tokens == 0) return MOE_OK;
+  if (!prev_idx || !cur_idx || !pair_counts || !single_counts || !scores) return MOE_EINVAL;
+  return hip_status(moe::launch_shuffle_predict(prev_idx, cur_idx, tokens, n_experts, top_k,
+                                                n_ranks, pair_counts, single_counts, min_obs,
+                                                scores, as_stream(stream)));
+}
+
+MOE_API int moe_shuffle_assign(const float* scores, int64_t tokens, int n_ranks, int32_t* owner) {
+  if (tokens < 0 || n_ranks < 1) return MOE_EINVAL;
+  if (n_ranks > MOE_MAX_RANKS) return MOE_EUNSUPPORTED;
+  if (tokens % n_ranks != 0) return MOE_EINVAL;
+  if (tokens == 0) return MOE_OK;
+  if (!scores || !owner) return MOE_EINVAL;
+  return moe::shuffle_assign(scores, tokens, n_ranks, owner);
 }

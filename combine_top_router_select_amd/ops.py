@@ -17,7 +17,8 @@ __all__ = ["MoeError", "moe_status_string", "moe_workspace_bytes", "moe_route_to
            "moe_send_counts", "moe_dispatch_permute", "moe_dispatch_permute_dedup",
            "moe_combine", "moe_coselect_counts", "workspace", "moe_expand_workspace_bytes",
            "expand_workspace", "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
-           "moe_placement_search"]
+           "moe_placement_search", "moe_shuffle_fit", "moe_shuffle_predict",
+           "moe_shuffle_assign"]
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -344,3 +345,54 @@ def moe_placement_search(coselect, n_ranks, initial=None, max_swaps=None):
                                      place.data_ptr(), ctypes.byref(obj), ctypes.byref(sw)),
           "moe_placement_search")
     return place, int(obj.value), int(sw.value)
+
+
+# ---------------------------------------------------- token shuffle planner --
+
+def moe_shuffle_fit(prev_idx, cur_idx, next_idx, n_experts, n_ranks, placement_next=None,
+                    pair_counts=None, single_counts=None, stream=None):
+    """Accumulate the planner's count tables from one calibration batch."""
+    for name, t in (("prev_idx", prev_idx), ("cur_idx", cur_idx), ("next_idx", next_idx)):
+        _dev(t, name, torch.int32, 2)
+    T, k = cur_idx.shape
+    dev = cur_idx.device
+    if placement_next is not None:
+        _dev(placement_next, "placement_next", torch.int32, 1)
+    if pair_counts is None:
+        pair_counts = torch.zeros((n_experts, n_experts, n_ranks), dtype=torch.int32, device=dev)
+    if single_counts is None:
+        single_counts = torch.zeros((n_experts, n_ranks), dtype=torch.int32, device=dev)
+    _dev(pair_counts, "pair_counts", torch.int32, 3)
+    _dev(single_counts, "single_counts", torch.int32, 2)
+    check(lib().moe_shuffle_fit(_ptr(prev_idx), _ptr(cur_idx), _ptr(next_idx), T, n_experts, k,
+                                n_ranks, _ptr(placement_next), _ptr(pair_counts),
+                                _ptr(single_counts), _stream(stream)), "moe_shuffle_fit")
+    return pair_counts, single_counts
+
+
+def moe_shuffle_predict(prev_idx, cur_idx, pair_counts, single_counts, min_obs, scores=None,
+                        stream=None):
+    _dev(prev_idx, "prev_idx", torch.int32, 2)
+    _dev(cur_idx, "cur_idx", torch.int32, 2)
+    _dev(pair_counts, "pair_counts", torch.int32, 3)
+    _dev(single_counts, "single_counts", torch.int32, 2)
+    T, k = cur_idx.shape
+    E, R = single_counts.shape
+    if scores is None:
+        scores = torch.empty((T, R), dtype=torch.float32, device=cur_idx.device)
+    _dev(scores, "scores", torch.float32, 2)
+    check(lib().moe_shuffle_predict(_ptr(prev_idx), _ptr(cur_idx), T, E, k, R, _ptr(pair_counts),
+                                    _ptr(single_counts), int(min_obs), _ptr(scores),
+                                    _stream(stream)), "moe_shuffle_predict")
+    return scores
+
+
+def moe_shuffle_assign(scores):
+    """Host assignment of owner ranks from [T][R] scores (a GPU tensor is
+    copied to the host first).  Returns a host int32 tensor [T]."""
+    S = scores.detach().to("cpu", torch.float32).contiguous()
+    T, R = S.shape
+    owner = torch.empty(T, dtype=torch.int32)
+    check(lib().moe_shuffle_assign(S.data_ptr() if T else None, T, R,
+                                   owner.data_ptr() if T else None), "moe_shuffle_assign")
+    return owner

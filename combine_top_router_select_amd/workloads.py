@@ -214,9 +214,13 @@ def make_layer_logits(w: Workload, n_layers: int = 3, seed: int = 1,
     exactly one path at every layer (a permutation per layer); a `path_share` of
     the tokens each follows one path, uniformly chosen, and gets `boost` added
     to its path's expert at every layer.  The correlation comes from the shared
-    latent path only: nothing here routes tokens."""
-    ss = np.random.SeedSequence([w.seed, seed])
-    s_paths, s_tok, *s_layers = ss.spawn(2 + n_layers)
+    latent path only: nothing here routes tokens.  The paths depend on the
+    workload only; `seed` picks the batch (which tokens follow which path, and
+    the noise), so a calibration batch and an evaluation batch share them."""
+    # the paths are the model's (fixed by the workload's seed); the tokens and
+    # the noise are the batch's (`seed`), so two batches share the structure
+    s_paths = np.random.SeedSequence([w.seed, 0x9A7E])
+    s_tok, *s_layers = np.random.SeedSequence([w.seed, seed]).spawn(1 + n_layers)
     T, E = w.tokens, w.n_experts
     gp = np.random.Generator(np.random.PCG64(s_paths))
     paths = np.stack([gp.permutation(E) for _ in range(n_layers)], axis=1)

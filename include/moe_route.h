@@ -322,6 +322,50 @@ int moe_placement_search(const int32_t* coselect, int n_experts, int n_ranks,
                          const int32_t* initial, int max_swaps, int32_t* placement,
                          int64_t* objective, int* swaps);
 
+/* ------------------------------------------------------------------------
+ * Token-shuffle planner ([EC] "Method 2: Token Shuffling": a token's owner
+ * rank at layer l+1 is predicted from the experts it selected at the two
+ * preceding MoE layers, by a pair lookup with a single-expert fallback for
+ * sparse observations; every rank owns exactly T/EP tokens, so tokens are
+ * assigned in decreasing confidence to their most preferred rank with room
+ * left).  The page prints no formula; the readings are stated per call.  The
+ * fused reduce-scatter that moves the tokens is not part of this library.
+ * ------------------------------------------------------------------------ */
+
+/* Fit, on a calibration batch: for every token, every expert c it selects at
+ * layer l+1 (on rank r = placement_next[c], contiguous when NULL) and every
+ * pair (a, b) of its experts at layers l-1 (prev_idx) and l (cur_idx):
+ *   pair_counts[a][b][r] += 1;  and for every b:  single_counts[b][r] += 1.
+ *   prev_idx, cur_idx, next_idx  [T][k] int32 (ids in [0, E)).
+ *   pair_counts    [E][E][R] int32, ACCUMULATED (zero it first).
+ *   single_counts  [E][R] int32, ACCUMULATED.
+ * Integer atomics: the result does not depend on their order.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (as moe_send_counts()). */
+int moe_shuffle_fit(const int32_t* prev_idx, const int32_t* cur_idx, const int32_t* next_idx,
+                    int64_t tokens, int n_experts, int top_k, int n_ranks,
+                    const int32_t* placement_next, int32_t* pair_counts, int32_t* single_counts,
+                    void* stream);
+
+/* Prediction: scores[t][r] = sum over the token's pairs (a, b), a's slot then
+ * b's, of pair_counts[a][b][r] / n_ab when n_ab = sum_r pair_counts[a][b][r]
+ * is at least min_obs (and positive), else of single_counts[b][r] / n_b (n_b
+ * = sum_r single_counts[b][r]; nothing when n_b = 0).  fp64 in that order,
+ * one rounding to fp32 per score.
+ *   scores  [T][R] fp32 out.
+ * Errors: MOE_EINVAL (min_obs < 0, null pointers), MOE_EUNSUPPORTED. */
+int moe_shuffle_predict(const int32_t* prev_idx, const int32_t* cur_idx, int64_t tokens,
+                        int n_experts, int top_k, int n_ranks, const int32_t* pair_counts,
+                        const int32_t* single_counts, int min_obs, float* scores, void* stream);
+
+/* Host.  Assignment: every rank owns exactly T/R tokens (T % R == 0).  Tokens
+ * are taken in decreasing confidence = (largest score) / (sum of scores) (0
+ * for an all-zero row; fp64 from the fp32 scores; ties to the lower token
+ * index), each to its highest-scoring rank that still has room (ties to the
+ * lower rank).  Synchronous; host memory only.
+ *   scores  host [T][R] fp32;  owner  host [T] int32 out.
+ * Errors: MOE_EINVAL (T % R != 0, null pointers), MOE_EUNSUPPORTED (R > 64). */
+int moe_shuffle_assign(const float* scores, int64_t tokens, int n_ranks, int32_t* owner);
+
 #ifdef __cplusplus
 }
 #endif

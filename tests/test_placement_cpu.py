@@ -54,3 +54,28 @@ def test_search_errors():
         ops.moe_placement_search(W, 2, max_swaps=-1)
     with pytest.raises(MoeError):
         ops.moe_placement_search(torch.zeros((2048, 2048), dtype=torch.int32), 2)
+
+
+# ------------------------------------------------------ shuffle assignment --
+
+@pytest.mark.parametrize("T,R,ties", [(96, 4, False), (96, 4, True), (16384, 8, False),
+                                      (4096, 32, True), (64, 64, False), (10, 1, False)])
+def test_shuffle_assign_matches_oracle(oracle_mod, T, R, ties):
+    rng = np.random.default_rng(T + R)
+    s = rng.random((T, R)).astype(np.float32)
+    if ties:   # many equal scores and equal confidences
+        s = (rng.integers(0, 3, (T, R)) / 2).astype(np.float32)
+        s[rng.random(T) < 0.1] = 0.0
+    own_o = oracle_mod.shuffle_assign(s)
+    own = ops.moe_shuffle_assign(torch.from_numpy(s))
+    assert (own.numpy() == own_o).all()
+    assert (np.bincount(own_o, minlength=R) == T // R).all()
+
+
+def test_shuffle_assign_errors():
+    from combine_top_router_select_amd._lib import MoeError
+    with pytest.raises(MoeError):
+        ops.moe_shuffle_assign(torch.zeros((10, 3)))          # 10 % 3 != 0
+    with pytest.raises(MoeError):
+        ops.moe_shuffle_assign(torch.zeros((130, 65)))        # R > 64
+    assert ops.moe_shuffle_assign(torch.zeros((0, 4))).numel() == 0
