@@ -1,7 +1,8 @@
 """Benchmark of the per-GPU MoE dispatch/combine hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
-                    [--receive] [--search] [--graph] [--overlap] [--no-cpu-baseline]
+                    [--receive] [--search] [--shuffle] [--fp8] [--graph] [--overlap]
+                    [--no-cpu-baseline]
                     [--calib-copy]
 
 A step is one pass of the whole path over one batch of the workload's seeded
@@ -71,6 +72,12 @@ def parse():
     p.add_argument("--search", action="store_true",
                    help="also fit a correlated placement to the co-selection counts of the "
                         "workload's first tokens and report the dedup rows it gives")
+    p.add_argument("--shuffle", action="store_true",
+                   help="also fit the token-shuffle planner on one batch of correlated "
+                        "three-layer routing and plan another, reporting times and locality")
+    p.add_argument("--separate", action="store_true",
+                   help="route and count with moe_route_topk + moe_send_counts instead of the "
+                        "fused moe_route_plan (one kernel more)")
     p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     p.add_argument("--overlap", action="store_true",
                    help="run the co-selection counts on a second stream")
@@ -163,7 +170,7 @@ class BufferSet:
         return tot
 
 
-def gpu_step(torch, ops, b, w, dedup, side=None, receive=False):
+def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True):
     """One pass of the hot path.  With a side stream, the co-selection counts run
     there, after the routing and concurrently with the rest.  With `receive`
     (dedup mode), the dedup rows are expanded per expert, passed through
@@ -171,14 +178,20 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False):
     are combined with weight 1."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
     main = torch.cuda.current_stream()
-    ops.moe_route_topk(b.logits, k, b.idx, b.gate)
+    if fused:   # co-selection counts folded in unless they run on the side stream
+        c = ops.moe_route_plan(b.logits, k, R, b.place, dedup, topk_idx=b.idx, topk_gate=b.gate,
+                               ws=b.ws, out=b.cnt, coselect=None if side is not None else b.W,
+                               coselect_tokens=w.coselect_tokens)[2]
+    else:
+        ops.moe_route_topk(b.logits, k, b.idx, b.gate)
     if side is not None:
         b.ev_routed.record(main)
         side.wait_event(b.ev_routed)
         ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W,
                                 stream=side)
         b.ev_coselected.record(side)
-    c = ops.moe_send_counts(b.idx, E, R, b.place, dedup, ws=b.ws, out=b.cnt)
+    if not fused:
+        c = ops.moe_send_counts(b.idx, E, R, b.place, dedup, ws=b.ws, out=b.cnt)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
     d = f(b.x, b.idx, b.gate, E, R, c["ws"], b.place, out=b.disp)
     if receive:
@@ -192,7 +205,7 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False):
         ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b.out)
     if side is not None:
         main.wait_event(b.ev_coselected)
-    else:
+    elif not fused:
         ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W)
 
 
@@ -220,21 +233,43 @@ def counter_traffic(kernel, workload, mode):
     return None
 
 
-def raw_step_calls(torch, ops, b, w, dedup, receive, bpe):
+def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True):
     """The C-ABI calls of one step on buffer set b, with every argument
     marshalled once: the timed loop then costs a few microseconds of host time
-    per step instead of the Python binding's checks."""
+    per step instead of the Python binding's checks.  With a side stream the
+    co-selection counts run there, forked after the routing and joined at the
+    end of the step (event record and wait entries return 0)."""
     L = ops.lib()
     T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
     N = T * k
     st = torch.cuda.current_stream().cuda_stream
     p = lambda t: None if t is None else t.data_ptr()
     c, d = b.cnt, b.disp
-    calls = [(L.moe_route_topk, (p(b.logits), T, E, k, p(b.idx), p(b.gate), st)),
-             (L.moe_send_counts, (p(b.idx), T, E, k, R, p(b.place), int(dedup),
-                                  p(c["expert_counts"]), p(c["rank_counts"]),
-                                  p(c["rank_offsets"]), p(c.get("expert_offsets")), p(b.ws),
-                                  b.ws.numel(), st))]
+    cargs = (int(dedup), p(c["expert_counts"]), p(c["rank_counts"]), p(c["rank_offsets"]),
+             p(c.get("expert_offsets")))
+    wsargs = (p(b.ws), b.ws.numel(), st)
+    ncs = w.coselect_tokens if side is None else 0
+    if fused:
+        calls = [(L.moe_route_plan, (p(b.logits), T, E, k, 0, R, p(b.place), *cargs[:1],
+                                     p(b.idx), p(b.gate), *cargs[1:], ncs,
+                                     p(b.W) if ncs else None, *wsargs))]
+    else:
+        calls = [(L.moe_route_topk, (p(b.logits), T, E, k, p(b.idx), p(b.gate), st))]
+    if side is not None:
+        main = torch.cuda.current_stream()
+
+        def fork():
+            b.ev_routed.record(main)
+            side.wait_event(b.ev_routed)
+            return L.moe_coselect_counts(p(b.idx), w.coselect_tokens, E, k, p(b.W),
+                                         side.cuda_stream) or b.ev_coselected.record(side) or 0
+
+        def join():
+            main.wait_event(b.ev_coselected)
+            return 0
+        calls.append((fork, ()))
+    if not fused:
+        calls.append((L.moe_send_counts, (p(b.idx), T, E, k, R, p(b.place), *cargs, *wsargs)))
     if dedup:
         calls.append((L.moe_dispatch_permute_dedup, (
             p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, p(b.place), bpe, p(b.ws), b.ws.numel(),
@@ -262,7 +297,10 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe):
     else:
         calls.append((L.moe_combine, (p(d["send"]), p(d["row_weight"]), p(d["slot_row"]), T, H,
                                       k, bpe, p(b.out), st)))
-    calls.append((L.moe_coselect_counts, (p(b.idx), w.coselect_tokens, E, k, p(b.W), st)))
+    if side is not None:
+        calls.append((join, ()))
+    elif not fused:
+        calls.append((L.moe_coselect_counts, (p(b.idx), w.coselect_tokens, E, k, p(b.W), st)))
     return calls
 
 
@@ -292,6 +330,47 @@ def placement_leg(torch, ops, b, w):
     return {"fit_tokens": w.coselect_tokens, "search_ms": round(search_ms, 2), "swaps": swaps,
             "objective": objective, "dedup_rows": rows,
             "rows_removed_pct": {n: round(100.0 * (1 - r / (T * k)), 2) for n, r in rows.items()}}
+
+
+def shuffle_leg(torch, ops, WL, w):
+    """Token-shuffle planner: fit on a calibration batch of three consecutive
+    layers (l-1, l, l+1) under the contiguous expert placement, plan an
+    evaluation batch, and report the share of layer l+1 token-expert
+    assignments served on the token's own rank: contiguous token ownership vs
+    the planned owners.  Not part of the timed step; GPU times are HIP events
+    around single launches (host launch latency included)."""
+    E, k, R, T = w.n_experts, w.top_k, w.n_ranks, w.tokens
+    dev = torch.device("cuda:0")
+
+    def routes(seed):
+        return [ops.moe_route_topk(torch.from_numpy(l).to(dev), k)[0]
+                for l in WL.make_layer_logits(w, seed=seed)]
+
+    cal, ev = routes(1), routes(2)
+    pair = torch.zeros((E, E, R), dtype=torch.int32, device=dev)
+    single = torch.zeros((E, R), dtype=torch.int32, device=dev)
+    pl = torch.from_numpy(WL.contiguous_placement(E, R)).to(dev)
+    ops.moe_shuffle_predict(ev[0], ev[1],                      # untimed first launches
+                            *ops.moe_shuffle_fit(cal[0], cal[1], cal[2], E, R, pl), 8)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    torch.cuda.synchronize()
+    e[0].record()
+    ops.moe_shuffle_fit(cal[0], cal[1], cal[2], E, R, pl, pair, single)
+    e[1].record()
+    e[2].record()
+    scores = ops.moe_shuffle_predict(ev[0], ev[1], pair, single, 8)
+    e[3].record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    owner = ops.moe_shuffle_assign(scores)
+    assign_ms = (time.perf_counter() - t0) * 1e3
+    served = pl.cpu()[ev[2].cpu().long()]                     # rank of each l+1 assignment
+    base = (torch.arange(T) * R // T)[:, None]
+    return {"fit_us": round(e[0].elapsed_time(e[1]) * 1e3, 2),
+            "predict_us": round(e[2].elapsed_time(e[3]) * 1e3, 2),
+            "assign_ms": round(assign_ms, 2),
+            "locality_contiguous": round(float((served == base).float().mean()), 4),
+            "locality_planned": round(float((served == owner[:, None]).float().mean()), 4)}
 
 
 def cpu_baseline(inp, w, dedup, seconds, receive=False, fp8=False):
@@ -341,6 +420,7 @@ def main():
     w = WL.get(a.workload)
     dedup = bool(a.dedup)
     receive = bool(a.receive)
+    fused = not a.separate
     if receive and not dedup:
         print("--receive needs --dedup (the receive side expands deduplicated rows)",
               file=sys.stderr)
@@ -371,19 +451,20 @@ def main():
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for b in sets:       # warm the code paths once outside capture
-                gpu_step(torch, ops, b, w, dedup, side, receive)
+                gpu_step(torch, ops, b, w, dedup, side, receive, fused)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         for b in sets:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                gpu_step(torch, ops, b, w, dedup, side, receive)
+                gpu_step(torch, ops, b, w, dedup, side, receive, fused)
             graphs.append(g)
         torch.cuda.synchronize()
 
     raw = None
-    if graphs is None and side is None:
-        raw = [raw_step_calls(torch, ops, b, w, dedup, receive, bpe) for b in sets]
+    if graphs is None:
+        raw = [raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side, fused)
+               for b in sets]
 
     def step(i):
         if graphs is not None:
@@ -394,11 +475,11 @@ def main():
                 if rc != 0:
                     raise ops.MoeError(rc, fn.__name__)
         else:
-            gpu_step(torch, ops, sets[i % nsets], w, dedup, side, receive)
+            gpu_step(torch, ops, sets[i % nsets], w, dedup, side, receive, fused)
 
     for i in range(a.warmup):
         if i == 0 and graphs is None:   # once through the Python binding, with its checks
-            gpu_step(torch, ops, sets[0], w, dedup, side, receive)
+            gpu_step(torch, ops, sets[0], w, dedup, side, receive, fused)
         else:
             step(i)
     torch.cuda.synchronize()
@@ -510,6 +591,7 @@ def main():
         "config": {"workload": w.name, "tokens": T, "hidden_dim": H, "n_experts": E,
                    "top_k": k, "n_ranks": R, "placement": w.placement,
                    "dispatch": "dedup" if dedup else "nondedup", "receive_side": receive,
+                   "routing": "fused" if fused else "separate",
                    "bytes_per_element": bpe, "graph": bool(a.graph),
                    "coselect_stream": "side" if a.overlap else "main",
                    "buffer_sets": nsets, "footprint_MiB": round(nsets * per_set / 2 ** 20)},
@@ -538,6 +620,8 @@ def main():
         res["receive"] = recv
     if a.search:
         res["placement_search"] = placement_leg(torch, ops, sets[0], w)
+    if a.shuffle:
+        res["token_shuffle"] = shuffle_leg(torch, ops, WL, w)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, w, dedup, a.cpu_seconds, receive, fp8)
     print(json.dumps(res), flush=True)

@@ -16,7 +16,7 @@ SYMBOLS = ("moe_status_string", "moe_workspace_bytes", "moe_expand_workspace_byt
            "moe_dispatch_permute_dedup", "moe_combine", "moe_coselect_counts",
            "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
            "moe_placement_search", "moe_route_topk_softmax_all", "moe_shuffle_fit",
-           "moe_shuffle_predict", "moe_shuffle_assign")
+           "moe_shuffle_predict", "moe_shuffle_assign", "moe_route_plan")
 
 _lib = None
 
@@ -43,6 +43,8 @@ def lib():
         L.moe_route_topk.argtypes = [P, i64, i32, i32, P, P, P]
         L.moe_route_topk_softmax_all.argtypes = [P, i64, i32, i32, P, P, P]
         L.moe_send_counts.argtypes = [P, i64, i32, i32, i32, P, i32, P, P, P, P, P, sz, P]
+        L.moe_route_plan.argtypes = [P, i64, i32, i32, i32, i32, P, i32, P, P, P, P, P, P, i64,
+                                     P, P, sz, P]
         L.moe_dispatch_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i32, P, sz, P,
                                            P, P, P, P, P]
         L.moe_dispatch_permute_dedup.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i32, P,

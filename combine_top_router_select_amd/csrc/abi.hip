@@ -30,6 +30,9 @@ hipError_t launch_shuffle_predict(const int32_t*, const int32_t*, int64_t, int, 
                                   const int32_t*, const int32_t*, int, float*, hipStream_t);
 int shuffle_assign(const float*, int64_t, int, int32_t*);
 hipError_t launch_coselect(const int32_t*, int64_t, int, int, int32_t*, hipStream_t);
+hipError_t launch_route_plan(const float*, int64_t, int, int, int, int, const int32_t*, int,
+                             int32_t*, float*, int32_t*, int32_t*, int32_t*, int32_t*, int64_t,
+                             int32_t*, void*, hipStream_t);
 }  // namespace moe
 
 namespace {
@@ -119,6 +122,30 @@ MOE_API int moe_send_counts(const int32_t* topk_idx, int64_t tokens, int n_exper
                                             rank_counts, rank_offsets,
                                             dedup ? nullptr : expert_offsets, workspace,
                                             as_stream(stream)));
+}
+
+MOE_API int moe_route_plan(const float* logits, int64_t tokens, int n_experts, int top_k,
+                           int gating, int n_ranks, const int32_t* placement, int dedup,
+                           int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+                           int32_t* rank_counts, int32_t* rank_offsets, int32_t* expert_offsets,
+                           int64_t coselect_tokens, int32_t* coselect, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if (gating != 0 && gating != 1) return MOE_EINVAL;
+  if (coselect_tokens < 0 || coselect_tokens > tokens || (coselect_tokens > 0 && !coselect))
+    return MOE_EINVAL;
+  if ((tokens > 0 && (!logits || !topk_idx || !topk_gate)) || !expert_counts || !rank_counts ||
+      !rank_offsets || !workspace)
+    return MOE_EINVAL;
+  if (workspace_bytes < moe_workspace_bytes(tokens, n_experts, top_k, n_ranks, dedup))
+    return MOE_EWORKSPACE;
+  return hip_status(moe::launch_route_plan(logits, tokens, n_experts, top_k, gating, n_ranks,
+                                           placement, dedup ? 1 : 0, topk_idx, topk_gate,
+                                           expert_counts, rank_counts, rank_offsets,
+                                           dedup ? nullptr : expert_offsets, coselect_tokens,
+                                           coselect, workspace, as_stream(stream)));
 }
 
 MOE_API int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* topk_gate,

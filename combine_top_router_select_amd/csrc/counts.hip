@@ -353,33 +353,17 @@ plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, int E, 
   }
 }
 
-template <bool PAD, int KMAX>
-static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, int R,
-                                  const int32_t* place, int dedup, const int32_t* n_valid,
-                                  int32_t* expert_counts, int32_t* rank_counts,
-                                  int32_t* rank_offsets, int32_t* expert_offsets,
-                                  void* workspace, hipStream_t stream) {
+// The scan of a plan whose tile counts (tcnt) are already in the workspace:
+// launched after tile_counts_kernel, or after the fused routing kernel.
+hipError_t launch_plan_scan(int64_t T, int E, int k, int R, const int32_t* place, int dedup,
+                            int32_t* expert_counts, int32_t* rank_counts, int32_t* rank_offsets,
+                            int32_t* expert_offsets, void* workspace, hipStream_t stream) {
   const PlanLayout pl = plan_layout(T, E, k, R, dedup);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int32_t* header = reinterpret_cast<int32_t*>(ws);
   int32_t* vbase = reinterpret_cast<int32_t*>(ws + pl.base_off);
-  uint8_t* tcnt = ws + pl.tcnt_off;
-  uint32_t* lslot = reinterpret_cast<uint32_t*>(ws + pl.lslot_off);
+  const uint8_t* tcnt = ws + pl.tcnt_off;
   const int m = E / R;
-  if (T > 0) {
-    const size_t lds = size_t(pl.cols) * sizeof(uint64_t) + size_t(E) * sizeof(int32_t);
-    const uint32_t kmul = kdiv_mul(k);
-    if (dedup)
-      hipLaunchKernelGGL((tile_counts_kernel<true, false, KMAX>), dim3(unsigned(pl.tiles)),
-                         dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
-                         n_valid, tcnt, lslot);
-    else
-      hipLaunchKernelGGL((tile_counts_kernel<false, PAD, KMAX>), dim3(unsigned(pl.tiles)),
-                         dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
-                         n_valid, tcnt, lslot);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
   const int B = int(pl.tiles);
   const int Bp = int(pl.tiles_pad);
   const int nvec = Bp / 16;
@@ -423,6 +407,35 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
 #undef MOE_SCAN_KV
 #undef MOE_SCAN_LAUNCH
   return hipGetLastError();
+}
+
+template <bool PAD, int KMAX>
+static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, int R,
+                                  const int32_t* place, int dedup, const int32_t* n_valid,
+                                  int32_t* expert_counts, int32_t* rank_counts,
+                                  int32_t* rank_offsets, int32_t* expert_offsets,
+                                  void* workspace, hipStream_t stream) {
+  const PlanLayout pl = plan_layout(T, E, k, R, dedup);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* tcnt = ws + pl.tcnt_off;
+  uint32_t* lslot = reinterpret_cast<uint32_t*>(ws + pl.lslot_off);
+  const int m = E / R;
+  if (T > 0) {
+    const size_t lds = size_t(pl.cols) * sizeof(uint64_t) + size_t(E) * sizeof(int32_t);
+    const uint32_t kmul = kdiv_mul(k);
+    if (dedup)
+      hipLaunchKernelGGL((tile_counts_kernel<true, false, KMAX>), dim3(unsigned(pl.tiles)),
+                         dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
+                         n_valid, tcnt, lslot);
+    else
+      hipLaunchKernelGGL((tile_counts_kernel<false, PAD, KMAX>), dim3(unsigned(pl.tiles)),
+                         dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
+                         n_valid, tcnt, lslot);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return launch_plan_scan(T, E, k, R, place, dedup, expert_counts, rank_counts, rank_offsets,
+                          expert_offsets, workspace, stream);
 }
 
 hipError_t launch_send_counts(const int32_t* idx, int64_t T, int E, int k, int R,

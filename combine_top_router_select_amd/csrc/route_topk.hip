@@ -84,6 +84,55 @@ __device__ __forceinline__ double group_sum(double v) {
   return v;
 }
 
+// Routes token t (one L-lane group; li = lane within the group).  Lane j < k of
+// the group gets the round-j winner in `my_e` and its unrounded gate numerator
+// and the group's denominator; other lanes' outputs are unused.  tok_ok false:
+// the loads stay in bounds (token tokens - 1) and the results are unused.
+template <int L, int V, bool FULL>
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int64_t tokens,
+                                            int E, int k, int64_t t, bool tok_ok, int li,
+                                            int& my_e, double& num, double& den) {
+  const int64_t tc = tok_ok ? t : tokens - 1;  // loads stay in bounds and unconditional
+  float f[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = li + L * v;
+    f[v] = logits[tc * E + (e < E ? e : E - 1)];
+  }
+  uint64_t key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = li + L * v;
+    key[v] = (tok_ok && e < E)
+                 ? (uint64_t(order_key(f[v])) << 32) | uint64_t(~uint32_t(e))
+                 : 0ull;  // below every real key
+  }
+  float my_f = 0.0f, l0 = 0.0f;
+  my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int v = 1; v < V; ++v) best = key[v] > best ? key[v] : best;
+    best = group_max<L>(best);
+#pragma unroll
+    for (int v = 0; v < V; ++v) key[v] = key[v] == best ? 0ull : key[v];
+    const float fb = key_value(uint32_t(best >> 32));
+    if (j == 0) l0 = fb;
+    if (li == j) {
+      my_e = int(~uint32_t(best));
+      my_f = fb;
+    }
+  }
+  num = (li < k) ? exp(double(my_f) - double(l0)) : 0.0;
+  double part = num;
+  if (FULL) {
+    part = 0.0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) part += (li + L * v < E) ? exp(double(f[v]) - double(l0)) : 0.0;
+  }
+  den = group_sum<L>(part);
+}
+
 template <int L, int V, bool FULL>
 __global__ void __launch_bounds__(256)
 route_topk_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k,
@@ -96,49 +145,77 @@ route_topk_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k
   for (int64_t t0 = wave * G; t0 < tokens; t0 += nwaves * G) {
     const int64_t t = t0 + lane / L;
     const bool tok_ok = t < tokens;
-    const int64_t tc = tok_ok ? t : tokens - 1;  // loads stay in bounds and unconditional
-    float f[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int e = li + L * v;
-      f[v] = logits[tc * E + (e < E ? e : E - 1)];
-    }
-    uint64_t key[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int e = li + L * v;
-      key[v] = (tok_ok && e < E)
-                   ? (uint64_t(order_key(f[v])) << 32) | uint64_t(~uint32_t(e))
-                   : 0ull;  // below every real key
-    }
-    int my_e = 0;
-    float my_f = 0.0f, l0 = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int v = 1; v < V; ++v) best = key[v] > best ? key[v] : best;
-      best = group_max<L>(best);
-#pragma unroll
-      for (int v = 0; v < V; ++v) key[v] = key[v] == best ? 0ull : key[v];
-      const float f = key_value(uint32_t(best >> 32));
-      if (j == 0) l0 = f;
-      if (li == j) {
-        my_e = int(~uint32_t(best));
-        my_f = f;
-      }
-    }
-    const double d = (li < k) ? exp(double(my_f) - double(l0)) : 0.0;
-    double part = d;
-    if (FULL) {
-      part = 0.0;
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        part += (li + L * v < E) ? exp(double(f[v]) - double(l0)) : 0.0;
-    }
-    const double s = group_sum<L>(part);
+    int my_e;
+    double num, den;
+    route_token<L, V, FULL>(logits, tokens, E, k, t, tok_ok, li, my_e, num, den);
     if (tok_ok && li < k) {
       topk_idx[t * k + li] = my_e;
-      topk_gate[t * k + li] = float(d / s);
+      topk_gate[t * k + li] = float(num / den);
+    }
+  }
+}
+
+// Routing fused with the per-tile counts of the dispatch plan: one workgroup
+// per 64-token tile, L lanes per token (64 L threads).  Each selected expert
+// sets its token's bit in an LDS bitmap of its column (the expert; in dedup
+// mode also its rank), after which the popcount of the bits below the token is
+// its rank in the tile and the popcount of the whole bitmap is the tile's
+// count - the same plan entries as the separate counting kernel writes from
+// topk_idx.  Saves that kernel's launch and its reread of the ids.
+// With W, the tile's tokens below cs_tokens also
+// add their co-selection counts: the tokens selecting both a and b are the set
+// bits of bits[a] & bits[b] (a == b: the tokens selecting a), so each ordered
+// pair takes one popcount and at most one global atomic add per tile.
+template <int L, int V, bool FULL, bool DEDUP>
+__global__ void __launch_bounds__(kTile * L)
+route_tile_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k, int R,
+                  const int32_t* __restrict__ place, int m, int64_t Bp,
+                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+                  uint8_t* __restrict__ tcnt, uint32_t* __restrict__ lslot, int64_t cs_tokens,
+                  int32_t* __restrict__ W) {
+  extern __shared__ uint64_t s_rdyn[];
+  const int C = E + (DEDUP ? R : 0);
+  uint64_t* bits = s_rdyn;                                       // [C]
+  int32_t* s_rank = reinterpret_cast<int32_t*>(s_rdyn + C);     // [E] (dedup, explicit placement)
+  const int tid = threadIdx.x;
+  const int nthreads = kTile * L;
+  const int64_t b = blockIdx.x;
+  const int li = lane_id() & (L - 1);
+  const int tl = tid / L;  // token within the tile
+  const int64_t t = b * kTile + tl;
+  const bool tok_ok = t < tokens;
+  for (int c = tid; c < C; c += nthreads) bits[c] = 0ull;
+  const bool has_rank = DEDUP && place;
+  if (has_rank)
+    for (int e = tid; e < E; e += nthreads) s_rank[e] = clampi(place[e], 0, R - 1);
+  int my_e;
+  double num, den;
+  route_token<L, V, FULL>(logits, tokens, E, k, t, tok_ok, li, my_e, num, den);
+  __syncthreads();  // bitmaps cleared, ranks loaded
+  const bool mine = tok_ok && li < k;
+  const int e = mine ? my_e : 0;  // lanes without a selection keep an in-range id
+  const int col = DEDUP ? (has_rank ? s_rank[e] : e / m) : e;
+  const unsigned long long bit = 1ull << tl;
+  if (mine) {
+    topk_idx[t * k + li] = e;
+    topk_gate[t * k + li] = float(num / den);
+    atomicOr(reinterpret_cast<unsigned long long*>(&bits[e]), bit);
+    if (DEDUP) atomicOr(reinterpret_cast<unsigned long long*>(&bits[E + col]), bit);
+  }
+  __syncthreads();
+  if (mine) {
+    const uint64_t mb = bits[DEDUP ? E + col : col];
+    const uint64_t below = tl == 0 ? 0ull : (~0ull >> (kWave - tl));
+    lslot[t * k + li] = (uint32_t(col) << 8) | uint32_t(__popcll(mb & below));
+  }
+  for (int c = tid; c < C; c += nthreads) tcnt[c * Bp + b] = uint8_t(__popcll(bits[c]));
+  const int64_t ncs = cs_tokens - b * kTile;  // tokens of this tile in the co-selection counts
+  if (W != nullptr && ncs > 0) {
+    const uint64_t cm = ncs >= kTile ? ~0ull : ((1ull << ncs) - 1ull);
+    const int pairs = E * E;
+    for (int q = tid; q < pairs; q += nthreads) {
+      const int n = __popcll(bits[q / E] & bits[q % E] & cm);
+      if (n) atomicAdd(&W[q], n);
     }
   }
 }
@@ -177,6 +254,93 @@ hipError_t launch_route_topk(const float* logits, int64_t tokens, int E, int k, 
                              int32_t* idx, float* gate, hipStream_t stream) {
   if (full_softmax) return launch_route_e<true>(logits, tokens, E, k, idx, gate, stream);
   return launch_route_e<false>(logits, tokens, E, k, idx, gate, stream);
+}
+
+hipError_t launch_plan_scan(int64_t T, int E, int k, int R, const int32_t* place, int dedup,
+                            int32_t* expert_counts, int32_t* rank_counts, int32_t* rank_offsets,
+                            int32_t* expert_offsets, void* workspace, hipStream_t stream);
+hipError_t launch_send_counts(const int32_t* idx, int64_t T, int E, int k, int R,
+                              const int32_t* place, int dedup, int32_t* expert_counts,
+                              int32_t* rank_counts, int32_t* rank_offsets,
+                              int32_t* expert_offsets, void* workspace, hipStream_t stream);
+
+// Largest expert count and token count routed by the fused kernel; beyond them
+// the routing, the counting and the co-selection counts run as separate kernels
+// (same results).  The fused kernel has one workgroup per 64-token tile, so it
+// runs 4 waves per SIMD on a quarter of the CUs that the routing kernel fills:
+// at E = 256 its selection rounds cost more than the launch it saves.  Its
+// co-selection counts take E * E popcounts per tile.
+constexpr int kFusedMaxExperts = 128;
+constexpr int64_t kFusedMaxTokens = int64_t(1) << 24;
+
+template <int L, int V, bool FULL>
+static hipError_t launch_route_tile(const float* logits, int64_t T, int E, int k, int R,
+                                    const int32_t* place, int dedup, int32_t* idx, float* gate,
+                                    int64_t cs_tokens, int32_t* W, void* workspace,
+                                    hipStream_t stream) {
+  const PlanLayout pl = plan_layout(T, E, k, R, dedup);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* tcnt = ws + pl.tcnt_off;
+  uint32_t* lslot = reinterpret_cast<uint32_t*>(ws + pl.lslot_off);
+  const size_t lds = size_t(pl.cols) * sizeof(uint64_t) + size_t(E) * sizeof(int32_t);
+  if (dedup)
+    hipLaunchKernelGGL((route_tile_kernel<L, V, FULL, true>), dim3(unsigned(pl.tiles)),
+                       dim3(kTile * L), lds, stream, logits, T, E, k, R, place, E / R,
+                       pl.tiles_pad, idx, gate, tcnt, lslot, cs_tokens, W);
+  else
+    hipLaunchKernelGGL((route_tile_kernel<L, V, FULL, false>), dim3(unsigned(pl.tiles)),
+                       dim3(kTile * L), lds, stream, logits, T, E, k, R, place, E / R,
+                       pl.tiles_pad, idx, gate, tcnt, lslot, cs_tokens, W);
+  return hipGetLastError();
+}
+
+template <bool FULL>
+static hipError_t launch_route_tile_e(const float* logits, int64_t T, int E, int k, int R,
+                                      const int32_t* place, int dedup, int32_t* idx, float* gate,
+                                      int64_t cs, int32_t* W, void* ws, hipStream_t st) {
+#define MOE_RT(LL, VV) \
+  launch_route_tile<LL, VV, FULL>(logits, T, E, k, R, place, dedup, idx, gate, cs, W, ws, st)
+  if (E <= 1) return MOE_RT(1, 1);
+  if (E <= 2) return MOE_RT(2, 1);
+  if (E <= 4) return MOE_RT(4, 1);
+  if (E <= 8) return MOE_RT(8, 1);
+  if (E <= 16) return MOE_RT(16, 1);
+  if (E <= 32) return MOE_RT(16, 2);
+  if (E <= 64) return MOE_RT(16, 4);
+  return MOE_RT(16, 8);
+#undef MOE_RT
+}
+
+hipError_t launch_coselect(const int32_t* idx, int64_t n, int E, int k, int32_t* W,
+                           hipStream_t stream);
+
+// Routing, the dispatch plan and (W non-null) the co-selection counts of the
+// first cs_tokens tokens: the fused kernel then the scan, or (large E or T)
+// the separate kernels.
+hipError_t launch_route_plan(const float* logits, int64_t T, int E, int k, int full_softmax,
+                             int R, const int32_t* place, int dedup, int32_t* idx, float* gate,
+                             int32_t* expert_counts, int32_t* rank_counts, int32_t* rank_offsets,
+                             int32_t* expert_offsets, int64_t cs_tokens, int32_t* W,
+                             void* workspace, hipStream_t stream) {
+  hipError_t err;
+  if (cs_tokens <= 0) W = nullptr;
+  if (E > kFusedMaxExperts || T > kFusedMaxTokens) {
+    err = launch_route_topk(logits, T, E, k, full_softmax, idx, gate, stream);
+    if (err != hipSuccess) return err;
+    err = launch_send_counts(idx, T, E, k, R, place, dedup, expert_counts, rank_counts,
+                             rank_offsets, expert_offsets, workspace, stream);
+    if (err != hipSuccess || W == nullptr) return err;
+    return launch_coselect(idx, cs_tokens, E, k, W, stream);
+  }
+  if (T > 0) {
+    err = full_softmax ? launch_route_tile_e<true>(logits, T, E, k, R, place, dedup, idx, gate,
+                                                   cs_tokens, W, workspace, stream)
+                       : launch_route_tile_e<false>(logits, T, E, k, R, place, dedup, idx, gate,
+                                                    cs_tokens, W, workspace, stream);
+    if (err != hipSuccess) return err;
+  }
+  return launch_plan_scan(T, E, k, R, place, dedup, expert_counts, rank_counts, rank_offsets,
+                          expert_offsets, workspace, stream);
 }
 
 }  // namespace moe

@@ -111,6 +111,50 @@ def moe_send_counts(topk_idx, n_experts, n_ranks, placement=None, dedup=False, w
             "expert_offsets": eo, "ws": ws}
 
 
+def moe_route_plan(logits, top_k, n_ranks, placement=None, dedup=False, softmax_all=False,
+                   topk_idx=None, topk_gate=None, ws=None, out=None, coselect=None,
+                   coselect_tokens=None, stream=None):
+    """moe_route_topk, moe_send_counts and (with `coselect`, an [E][E] int32
+    matrix that is accumulated into) moe_coselect_counts over the first
+    `coselect_tokens` tokens (default all) in one call.  Returns (topk_idx,
+    topk_gate, counts) with counts as moe_send_counts returns them."""
+    _dev(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    if topk_gate is None:
+        topk_gate = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    _dev(topk_idx, "topk_idx", torch.int32)
+    _dev(topk_gate, "topk_gate", torch.float32)
+    if placement is not None:
+        _dev(placement, "placement", torch.int32, 1)
+    if ws is None:
+        ws = workspace(T, E, top_k, n_ranks, dedup, dev)
+    o = dict(out or {})
+    ec = o.get("expert_counts")
+    ec = torch.empty(E, dtype=torch.int32, device=dev) if ec is None else ec
+    rc = o.get("rank_counts")
+    rc = torch.empty(n_ranks, dtype=torch.int32, device=dev) if rc is None else rc
+    ro = o.get("rank_offsets")
+    ro = torch.empty(n_ranks + 1, dtype=torch.int32, device=dev) if ro is None else ro
+    eo = None
+    if not dedup:
+        eo = o.get("expert_offsets")
+        eo = torch.empty(E, dtype=torch.int32, device=dev) if eo is None else eo
+    ncs = 0
+    if coselect is not None:
+        _dev(coselect, "coselect", torch.int32, 2)
+        ncs = T if coselect_tokens is None else int(coselect_tokens)
+    check(lib().moe_route_plan(_ptr(logits), T, E, top_k, int(bool(softmax_all)), n_ranks,
+                               _ptr(placement), int(bool(dedup)), _ptr(topk_idx),
+                               _ptr(topk_gate), _ptr(ec), _ptr(rc), _ptr(ro), _ptr(eo), ncs,
+                               _ptr(coselect), _ptr(ws), ws.numel(), _stream(stream)),
+          "moe_route_plan")
+    return topk_idx, topk_gate, {"expert_counts": ec, "rank_counts": rc, "rank_offsets": ro,
+                                 "expert_offsets": eo, "ws": ws}
+
+
 def _x_bpe(x):
     _dev(x, "x", None, 2)
     if x.element_size() not in (1, 2, 4):

@@ -133,6 +133,33 @@ int moe_send_counts(const int32_t* topk_idx, int64_t tokens, int n_experts, int 
                     int32_t* expert_offsets, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* A1 + A2 + A3 (+ A6) in one call: moe_route_topk() (gating 0) or
+ * moe_route_topk_softmax_all() (gating 1), then moe_send_counts() on the ids
+ * it produced, then (coselect_tokens > 0) moe_coselect_counts() on the first
+ * coselect_tokens of them - the same outputs bit for bit and the same plan left
+ * in the workspace ([EC] "Background", "Method 1", "Correlation Formation and
+ * Stability"; [DD] "Setup", "Reading the counts").  For E <= 128 one kernel
+ * routes each 64-token tile, counts it and adds its co-selection counts, which
+ * saves the counting and co-selection kernels' launches and their rereads of
+ * topk_idx; larger E (or T > 2^24) run the separate kernels.
+ *   logits, topk_idx, topk_gate   as moe_route_topk() (may be NULL when
+ *                                 tokens == 0).
+ *   gating                        0 or 1, as above.
+ *   n_ranks ... expert_offsets    as moe_send_counts().
+ *   coselect_tokens               0 <= coselect_tokens <= tokens; 0: no
+ *                                 co-selection counts.
+ *   coselect                      [E][E] int32, ACCUMULATED as by
+ *                                 moe_coselect_counts(); may be NULL when
+ *                                 coselect_tokens == 0.
+ *   workspace, workspace_bytes    as moe_send_counts().
+ * Errors: those of moe_route_topk() and moe_send_counts(); MOE_EINVAL for a
+ *         gating value other than 0 or 1 or a bad coselect_tokens. */
+int moe_route_plan(const float* logits, int64_t tokens, int n_experts, int top_k, int gating,
+                   int n_ranks, const int32_t* placement, int dedup, int32_t* topk_idx,
+                   float* topk_gate, int32_t* expert_counts, int32_t* rank_counts,
+                   int32_t* rank_offsets, int32_t* expert_offsets, int64_t coselect_tokens,
+                   int32_t* coselect, void* workspace, size_t workspace_bytes, void* stream);
+
 /* A4a - dispatch permute, one row per (token, expert) ([EC] "Method 1",
  * conventional dispatch; [DD] "Reading the counts").
  * Must follow moe_send_counts(dedup = 0) on the same stream with the same

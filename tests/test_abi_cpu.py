@@ -104,6 +104,39 @@ def test_send_counts_errors(lib):
     assert call(T=6400, dedup=1, wsb=wsd - 1) == EWS
 
 
+def test_route_plan_errors(lib):
+    f = lib.moe_route_plan
+    ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)
+    names = ["logits", "T", "E", "k", "gating", "R", "place", "dedup", "idx", "gate", "ec", "rc",
+             "ro", "eo", "ncs", "W", "ws", "wsb", "stream"]
+    ok = (FAKE, 100, 8, 2, 0, 4, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, ws,
+          None)
+
+    def call(**kw):
+        a = list(ok)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return f(*a)
+
+    assert call(gating=2) == EINVAL
+    assert call(gating=-1) == EINVAL
+    assert call(ncs=-1, W=FAKE) == EINVAL
+    assert call(ncs=101, W=FAKE) == EINVAL                # more than tokens
+    assert call(ncs=10, W=None) == EINVAL
+    assert call(logits=None) == EINVAL
+    assert call(idx=None) == EINVAL
+    assert call(gate=None) == EINVAL
+    assert call(ec=None) == EINVAL
+    assert call(ws=None) == EINVAL
+    assert call(R=3) == EINVAL
+    assert call(k=9) == EINVAL
+    assert call(k=17, E=64) == EUNSUP
+    assert call(E=128, R=128) == EUNSUP
+    assert call(wsb=ws - 1) == EWS
+    wsd = lib.moe_workspace_bytes(6400, 8, 2, 4, 1)
+    assert call(T=6400, dedup=1, wsb=wsd - 1) == EWS
+
+
 def test_dispatch_errors(lib):
     f = lib.moe_dispatch_permute
     ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)

@@ -68,6 +68,84 @@ def test_route_parity_workloads(oracle_mod, name):
     assert d.max() <= 1
 
 
+# ------------------------------------------------ fused routing + plan --
+
+ROUTE_PLAN_CASES = [  # T, E, k, R
+    (1, 8, 2, 4), (63, 8, 2, 4), (64, 64, 6, 16), (1000, 64, 6, 16), (777, 128, 8, 16),
+    (300, 8, 8, 8), (257, 3, 1, 1), (129, 1, 1, 1), (500, 256, 8, 32), (200, 100, 16, 4),
+    (4100, 16, 4, 16), (130, 512, 16, 64), (70, 1024, 3, 8),
+]
+
+
+@pytest.mark.parametrize("T,E,k,R", ROUTE_PLAN_CASES)
+@pytest.mark.parametrize("dedup", [False, True])
+@pytest.mark.parametrize("pl", ["contiguous", "random"])
+@pytest.mark.parametrize("softmax_all", [False, True])
+def test_route_plan_parity(oracle_mod, T, E, k, R, dedup, pl, softmax_all):
+    """moe_route_plan against the oracle (ids, gates, counts, offsets,
+    co-selection counts accumulated onto a nonzero matrix) and against
+    moe_route_topk + moe_send_counts (every byte of the plan, and the dispatch
+    that consumes it).  E > 128 takes the unfused path."""
+    say(f"[route_plan] T={T} E={E} k={k} R={R} dedup={dedup} placement={pl} "
+        f"softmax_all={softmax_all}")
+    inp = WL.make_custom_inputs(T, 64, E, seed=T * 5 + E + k + R)
+    route = oracle_mod.route_topk_softmax_all if softmax_all else oracle_mod.route_topk
+    idx_o, gate_o = route(inp["logits"], k)
+    placement = WL.random_placement(E, R, seed=T) if pl == "random" else None
+    place_dev = to_dev(placement) if placement is not None else None
+    logits = to_dev(inp["logits"])
+    rng = np.random.default_rng(T + E)
+    W0 = rng.integers(0, 1000, size=(E, E)).astype(np.int32)
+    cs = T if dedup else (T * 2) // 3          # all tokens, or a prefix ending inside a tile
+    W = to_dev(W0.copy())
+    idx, gate, c = ops.moe_route_plan(logits, k, R, place_dev, dedup, softmax_all, coselect=W,
+                                      coselect_tokens=cs)
+    idx2, gate2 = ops.moe_route_topk(logits, k, softmax_all=softmax_all)
+    c2 = ops.moe_send_counts(idx2, E, R, place_dev, dedup=dedup)
+    sync()
+    assert (host(idx) == idx_o).all()
+    assert f32_ulp_diff(host(gate), gate_o).max() <= 1
+    assert (host(gate).view(np.uint32) == host(gate2).view(np.uint32)).all()
+    co = oracle_mod.send_counts(idx_o, E, R, placement, dedup)
+    _check_counts(c, co, dedup)
+    W_o = oracle_mod.coselect(idx_o, E, tokens=cs, W=W0.copy())
+    assert (host(W) == W_o).all()
+    # the plan in the workspace: header, group bases, tile counts, slot codes
+    assert _plan_equal(c["ws"], c2["ws"], T, E, k, R, dedup)
+    f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+    x = bf16_dev(inp["x_bits"])
+    d = f(x, idx, gate, E, R, c["ws"], place_dev)
+    o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(inp["x_bits"], idx_o, gate_o,
+                                                                     E, R, placement)
+    sync()
+    assert (host(d["slot_row"]) == o["slot_row"]).all()
+    assert (bf16_host(d["send"][:o["n_rows"]]) == o["send"]).all()
+
+
+def _plan_equal(ws_a, ws_b, T, E, k, R, dedup):
+    """Plan regions compared field by field (the tile-count padding bytes past
+    the last tile are never read and may differ)."""
+    tiles = (T + 63) // 64
+    tp = (tiles + 15) // 16 * 16
+    groups = tp // 16
+    cols = E + (R if dedup else 0)
+    pos = R if dedup else E
+    al = lambda v: (v + 255) // 256 * 256
+    base_off = 256
+    tcnt_off = al(base_off + pos * groups * 4)
+    lslot_off = al(tcnt_off + cols * tp)
+    a, b = host(ws_a), host(ws_b)
+    if not (a[:4] == b[:4]).all():
+        return False
+    if not (a[base_off:base_off + pos * groups * 4] == b[base_off:base_off + pos * groups * 4]).all():
+        return False
+    ta = a[tcnt_off:tcnt_off + cols * tp].reshape(cols, tp)[:, :tiles]
+    tb = b[tcnt_off:tcnt_off + cols * tp].reshape(cols, tp)[:, :tiles]
+    if not (ta == tb).all():
+        return False
+    return bool((a[lslot_off:lslot_off + T * k * 4] == b[lslot_off:lslot_off + T * k * 4]).all())
+
+
 # ------------------------------------------------------ counts + dispatch --
 
 def _check_counts(c, co, dedup):
