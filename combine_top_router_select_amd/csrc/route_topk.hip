@@ -74,6 +74,25 @@ __device__ __forceinline__ uint64_t group_max(uint64_t v) {
   return v;
 }
 
+// Maximum / minimum of 32-bit values over the L-lane group; every lane gets it.
+template <int L>
+__device__ __forceinline__ uint32_t group_max32(uint32_t v) {
+  if (L >= 2) v = max(v, dpp32<kDppXor1>(v));
+  if (L >= 4) v = max(v, dpp32<kDppXor2>(v));
+  if (L >= 8) v = max(v, dpp32<kDppHalfMirror>(v));
+  if (L >= 16) v = max(v, dpp32<kDppMirror>(v));
+  return v;
+}
+
+template <int L>
+__device__ __forceinline__ uint32_t group_min32(uint32_t v) {
+  if (L >= 2) v = min(v, dpp32<kDppXor1>(v));
+  if (L >= 4) v = min(v, dpp32<kDppXor2>(v));
+  if (L >= 8) v = min(v, dpp32<kDppHalfMirror>(v));
+  if (L >= 16) v = min(v, dpp32<kDppMirror>(v));
+  return v;
+}
+
 // Sum over the L-lane group in a fixed order; every lane gets it.
 template <int L>
 __device__ __forceinline__ double group_sum(double v) {
@@ -88,6 +107,14 @@ __device__ __forceinline__ double group_sum(double v) {
 // the group gets the round-j winner in `my_e` and its unrounded gate numerator
 // and the group's denominator; other lanes' outputs are unused.  tok_ok false:
 // the loads stay in bounds (token tokens - 1) and the results are unused.
+//
+// Selection with 32-bit operations only: candidate keys are the order keys of
+// the logits, raised to at least 1 so that 0 can mark retired and absent
+// candidates (only the NaN pattern 0xFFFFFFFF has order key 0, and NaN logits
+// are outside the contract).  A round takes the group maximum of the keys, then
+// the group minimum of the expert ids that hold it (the lowest id wins a tie),
+// and retires that one candidate.  Each group reduction is four DPP max or min
+// steps on 32-bit values.
 template <int L, int V, bool FULL>
 __device__ __forceinline__ void route_token(const float* __restrict__ logits, int64_t tokens,
                                             int E, int k, int64_t t, bool tok_ok, int li,
@@ -99,31 +126,33 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
     const int e = li + L * v;
     f[v] = logits[tc * E + (e < E ? e : E - 1)];
   }
-  uint64_t key[V];
+  uint32_t key[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const int e = li + L * v;
-    key[v] = (tok_ok && e < E)
-                 ? (uint64_t(order_key(f[v])) << 32) | uint64_t(~uint32_t(e))
-                 : 0ull;  // below every real key
+    const uint32_t ok = order_key(f[v]);
+    key[v] = (tok_ok && li + L * v < E) ? (ok > 1u ? ok : 1u) : 0u;
   }
-  float my_f = 0.0f, l0 = 0.0f;
+  uint32_t my_key = 0u, key0 = 0u;
   my_e = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    uint32_t m = key[0];
 #pragma unroll
-    for (int v = 1; v < V; ++v) best = key[v] > best ? key[v] : best;
-    best = group_max<L>(best);
+    for (int v = 1; v < V; ++v) m = key[v] > m ? key[v] : m;
+    const uint32_t best = group_max32<L>(m);
+    uint32_t cand = 0xFFFFFFFFu;  // lowest expert id of this lane holding the maximum
 #pragma unroll
-    for (int v = 0; v < V; ++v) key[v] = key[v] == best ? 0ull : key[v];
-    const float fb = key_value(uint32_t(best >> 32));
-    if (j == 0) l0 = fb;
+    for (int v = V - 1; v >= 0; --v) cand = key[v] == best ? uint32_t(li + L * v) : cand;
+    const uint32_t win = group_min32<L>(cand);
+#pragma unroll
+    for (int v = 0; v < V; ++v) key[v] = uint32_t(li + L * v) == win ? 0u : key[v];
+    if (j == 0) key0 = best;
     if (li == j) {
-      my_e = int(~uint32_t(best));
-      my_f = fb;
+      my_e = int(win);
+      my_key = best;
     }
   }
-  num = (li < k) ? exp(double(my_f) - double(l0)) : 0.0;
+  const float l0 = key_value(key0);
+  num = (li < k) ? exp(double(key_value(my_key)) - double(l0)) : 0.0;
   double part = num;
   if (FULL) {
     part = 0.0;
