@@ -81,6 +81,9 @@ def parse():
     p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     p.add_argument("--overlap", action="store_true",
                    help="run the co-selection counts on a second stream")
+    p.add_argument("--step-events", action="store_true",
+                   help="also record HIP events around the dispatch and combine launches of every "
+                        "timed step (their in-step durations)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--footprint-gib", type=float, default=2.0,
@@ -466,14 +469,27 @@ def main():
         raw = [raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side, fused)
                for b in sets]
 
-    def step(i):
+    timed_kernels = ("moe_dispatch_permute", "moe_dispatch_permute_dedup", "moe_combine",
+                     "moe_expand_permute", "moe_expand_reduce")
+    step_ev = {}   # (step, entry point) -> (start event, end event)
+    ev_pool = ([torch.cuda.Event(enable_timing=True) for _ in range(8 * a.steps + 8)]
+               if a.step_events else [])
+
+    def step(i, events=False):
         if graphs is not None:
             graphs[i % nsets].replay()
         elif raw is not None:
             for fn, args in raw[i % nsets]:
+                name = getattr(fn, "__name__", "")
+                ev = None
+                if events and name in timed_kernels:
+                    ev = step_ev[(i, name)] = (ev_pool.pop(), ev_pool.pop())
+                    ev[0].record()
                 rc = fn(*args)
+                if ev is not None:
+                    ev[1].record()
                 if rc != 0:
-                    raise ops.MoeError(rc, fn.__name__)
+                    raise ops.MoeError(rc, name)
         else:
             gpu_step(torch, ops, sets[i % nsets], w, dedup, side, receive, fused)
 
@@ -486,10 +502,14 @@ def main():
     # timed region: exactly K steps, synchronised on both sides
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(a.warmup + i)
+        step(a.warmup + i, a.step_events)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    in_step = {}
+    for (i, name), (e0, e1) in step_ev.items():
+        in_step.setdefault(name, []).append(e0.elapsed_time(e1) * 1e-3)
+    in_step = {n: round(float(np.mean(v)) * 1e6, 2) for n, v in in_step.items()}
 
     # Per-kernel mean durations with HIP events on the stream the kernels run
     # on: each event pair brackets a run of back-to-back launches of that one
@@ -602,6 +622,7 @@ def main():
                                  if not fp8 else None),
                      "algorithmic_bytes": dom[2]},
         "dispatch_us": round(t_disp * 1e6, 2),
+        "in_step_event_us": in_step or None,
         "combine_us": round(t_comb * 1e6, 2),
         "dispatch_combine_tokens_per_s": T / (t_disp + t_comb),
         "dispatch_combine_GBps": round(dc_gbps, 1),

@@ -103,66 +103,111 @@ __device__ __forceinline__ double group_sum(double v) {
   return v;
 }
 
-// Routes token t (one L-lane group; li = lane within the group).  Lane j < k of
-// the group gets the round-j winner in `my_e` and its unrounded gate numerator
-// and the group's denominator; other lanes' outputs are unused.  tok_ok false:
-// the loads stay in bounds (token tokens - 1) and the results are unused.
+constexpr int kMaxTopK = 16;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Expert held by lane li of a group in its v-th register: VEC consecutive
+// experts per lane and chunk, chunks of L * VEC experts.  Ascending v is
+// ascending expert id within a lane.
+template <int L, int VEC>
+__device__ __forceinline__ int expert_of(int li, int v) {
+  return (v / VEC) * (L * VEC) + li * VEC + (v % VEC);
+}
+
+// Winner slots kept by one lane: rounds li, li + L, li + 2L, ... of its group.
+template <int L>
+struct RouteSlots {
+  static constexpr int N = (kMaxTopK + L - 1) / L;
+  int e[N];          // expert id of round li + L s
+  double num[N];     // its gate numerator exp(l - l_max), fp64
+  double den;        // the group's gate denominator
+};
+
+// Routes token t with one group of L lanes (li = lane within the group); V
+// logits per lane (VEC = 4: 16-byte loads, E % 4 == 0).  tok_ok false: loads
+// stay in bounds (token tokens - 1) and the results are unused.
 //
 // Selection with 32-bit operations only: candidate keys are the order keys of
-// the logits, raised to at least 1 so that 0 can mark retired and absent
+// the logits, raised to at least 1 so that 0 marks retired and absent
 // candidates (only the NaN pattern 0xFFFFFFFF has order key 0, and NaN logits
-// are outside the contract).  A round takes the group maximum of the keys, then
-// the group minimum of the expert ids that hold it (the lowest id wins a tie),
-// and retires that one candidate.  Each group reduction is four DPP max or min
-// steps on 32-bit values.
-template <int L, int V, bool FULL>
+// are outside the contract).  A round takes the group maximum of the keys,
+// then the group minimum of the expert ids holding it (the lowest id wins a
+// tie), and retires that candidate; each group reduction is log2(L) DPP
+// max/min steps.  Every lane of the group sees every round's winner; lane li
+// keeps rounds li + L s.  The rounds are unrolled, so slot indices are static.
+template <int L, int V, int VEC, bool FULL>
 __device__ __forceinline__ void route_token(const float* __restrict__ logits, int64_t tokens,
                                             int E, int k, int64_t t, bool tok_ok, int li,
-                                            int& my_e, double& num, double& den) {
+                                            RouteSlots<L>& out) {
   const int64_t tc = tok_ok ? t : tokens - 1;  // loads stay in bounds and unconditional
+  const float* row = logits + tc * E;
   float f[V];
+  if (VEC == 4) {
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int e = li + L * v;
-    f[v] = logits[tc * E + (e < E ? e : E - 1)];
+    for (int c = 0; c < V / 4; ++c) {
+      const int base = c * L * 4 + li * 4;
+      const f32x4 q = *reinterpret_cast<const f32x4*>(row + (base <= E - 4 ? base : E - 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[4 * c + i] = q[i];
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = expert_of<L, VEC>(li, v);
+      f[v] = row[e < E ? e : E - 1];
+    }
   }
   uint32_t key[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const uint32_t ok = order_key(f[v]);
-    key[v] = (tok_ok && li + L * v < E) ? (ok > 1u ? ok : 1u) : 0u;
+    key[v] = (tok_ok && expert_of<L, VEC>(li, v) < E) ? (ok > 1u ? ok : 1u) : 0u;
   }
-  uint32_t my_key = 0u, key0 = 0u;
-  my_e = 0;
-  for (int j = 0; j < k; ++j) {
+  uint32_t my_key[RouteSlots<L>::N];
+  uint32_t key0 = 0u;
+#pragma unroll
+  for (int s = 0; s < RouteSlots<L>::N; ++s) {
+    out.e[s] = 0;
+    my_key[s] = 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= k) continue;  // uniform; every round is its own unrolled copy
     uint32_t m = key[0];
 #pragma unroll
     for (int v = 1; v < V; ++v) m = key[v] > m ? key[v] : m;
     const uint32_t best = group_max32<L>(m);
     uint32_t cand = 0xFFFFFFFFu;  // lowest expert id of this lane holding the maximum
 #pragma unroll
-    for (int v = V - 1; v >= 0; --v) cand = key[v] == best ? uint32_t(li + L * v) : cand;
+    for (int v = V - 1; v >= 0; --v)
+      cand = key[v] == best ? uint32_t(expert_of<L, VEC>(li, v)) : cand;
     const uint32_t win = group_min32<L>(cand);
 #pragma unroll
-    for (int v = 0; v < V; ++v) key[v] = uint32_t(li + L * v) == win ? 0u : key[v];
+    for (int v = 0; v < V; ++v) key[v] = uint32_t(expert_of<L, VEC>(li, v)) == win ? 0u : key[v];
     if (j == 0) key0 = best;
-    if (li == j) {
-      my_e = int(win);
-      my_key = best;
+    if (li == j % L) {
+      out.e[j / L] = int(win);
+      my_key[j / L] = best;
     }
   }
-  const float l0 = key_value(key0);
-  num = (li < k) ? exp(double(key_value(my_key)) - double(l0)) : 0.0;
-  double part = num;
+  const double l0 = double(key_value(key0));
+  double part = 0.0;
+#pragma unroll
+  for (int s = 0; s < RouteSlots<L>::N; ++s) {
+    out.num[s] = li + L * s < k ? exp(double(key_value(my_key[s])) - l0) : 0.0;
+    part += out.num[s];
+  }
   if (FULL) {
     part = 0.0;
 #pragma unroll
-    for (int v = 0; v < V; ++v) part += (li + L * v < E) ? exp(double(f[v]) - double(l0)) : 0.0;
+    for (int v = 0; v < V; ++v)
+      part += expert_of<L, VEC>(li, v) < E ? exp(double(f[v]) - l0) : 0.0;
   }
-  den = group_sum<L>(part);
+  out.den = group_sum<L>(part);
 }
 
-template <int L, int V, bool FULL>
+template <int L, int V, int VEC, bool FULL>
 __global__ void __launch_bounds__(256)
 route_topk_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k,
                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
@@ -174,12 +219,15 @@ route_topk_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k
   for (int64_t t0 = wave * G; t0 < tokens; t0 += nwaves * G) {
     const int64_t t = t0 + lane / L;
     const bool tok_ok = t < tokens;
-    int my_e;
-    double num, den;
-    route_token<L, V, FULL>(logits, tokens, E, k, t, tok_ok, li, my_e, num, den);
-    if (tok_ok && li < k) {
-      topk_idx[t * k + li] = my_e;
-      topk_gate[t * k + li] = float(num / den);
+    RouteSlots<L> r;
+    route_token<L, V, VEC, FULL>(logits, tokens, E, k, t, tok_ok, li, r);
+#pragma unroll
+    for (int s = 0; s < RouteSlots<L>::N; ++s) {
+      const int j = li + L * s;
+      if (tok_ok && j < k) {
+        topk_idx[t * k + j] = r.e[s];
+        topk_gate[t * k + j] = float(r.num[s] / r.den);
+      }
     }
   }
 }
@@ -191,11 +239,11 @@ route_topk_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k
 // its rank in the tile and the popcount of the whole bitmap is the tile's
 // count - the same plan entries as the separate counting kernel writes from
 // topk_idx.  Saves that kernel's launch and its reread of the ids.
-// With W, the tile's tokens below cs_tokens also
-// add their co-selection counts: the tokens selecting both a and b are the set
-// bits of bits[a] & bits[b] (a == b: the tokens selecting a), so each ordered
-// pair takes one popcount and at most one global atomic add per tile.
-template <int L, int V, bool FULL, bool DEDUP>
+// With W, the tile's tokens below cs_tokens also add their co-selection
+// counts: the tokens selecting both a and b are the set bits of
+// bits[a] & bits[b] (a == b: the tokens selecting a), so each ordered pair
+// takes one popcount and at most one global atomic add per tile.
+template <int L, int V, int VEC, bool FULL, bool DEDUP>
 __global__ void __launch_bounds__(kTile * L)
 route_tile_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k, int R,
                   const int32_t* __restrict__ place, int m, int64_t Bp,
@@ -203,6 +251,7 @@ route_tile_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k
                   uint8_t* __restrict__ tcnt, uint32_t* __restrict__ lslot, int64_t cs_tokens,
                   int32_t* __restrict__ W) {
   extern __shared__ uint64_t s_rdyn[];
+  constexpr int NS = RouteSlots<L>::N;
   const int C = E + (DEDUP ? R : 0);
   uint64_t* bits = s_rdyn;                                       // [C]
   int32_t* s_rank = reinterpret_cast<int32_t*>(s_rdyn + C);     // [E] (dedup, explicit placement)
@@ -217,64 +266,97 @@ route_tile_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k
   const bool has_rank = DEDUP && place;
   if (has_rank)
     for (int e = tid; e < E; e += nthreads) s_rank[e] = clampi(place[e], 0, R - 1);
-  int my_e;
-  double num, den;
-  route_token<L, V, FULL>(logits, tokens, E, k, t, tok_ok, li, my_e, num, den);
+  RouteSlots<L> r;
+  route_token<L, V, VEC, FULL>(logits, tokens, E, k, t, tok_ok, li, r);
   __syncthreads();  // bitmaps cleared, ranks loaded
-  const bool mine = tok_ok && li < k;
-  const int e = mine ? my_e : 0;  // lanes without a selection keep an in-range id
-  const int col = DEDUP ? (has_rank ? s_rank[e] : e / m) : e;
   const unsigned long long bit = 1ull << tl;
-  if (mine) {
-    topk_idx[t * k + li] = e;
-    topk_gate[t * k + li] = float(num / den);
-    atomicOr(reinterpret_cast<unsigned long long*>(&bits[e]), bit);
-    if (DEDUP) atomicOr(reinterpret_cast<unsigned long long*>(&bits[E + col]), bit);
+  int col[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j = li + L * s;
+    const bool mine = tok_ok && j < k;
+    const int e = mine ? r.e[s] : 0;  // slots without a selection keep an in-range id
+    col[s] = DEDUP ? (has_rank ? s_rank[e] : e / m) : e;
+    if (mine) {
+      topk_idx[t * k + j] = e;
+      topk_gate[t * k + j] = float(r.num[s] / r.den);
+      atomicOr(reinterpret_cast<unsigned long long*>(&bits[e]), bit);
+      if (DEDUP) atomicOr(reinterpret_cast<unsigned long long*>(&bits[E + col[s]]), bit);
+    }
   }
   __syncthreads();
-  if (mine) {
-    const uint64_t mb = bits[DEDUP ? E + col : col];
-    const uint64_t below = tl == 0 ? 0ull : (~0ull >> (kWave - tl));
-    lslot[t * k + li] = (uint32_t(col) << 8) | uint32_t(__popcll(mb & below));
+  const uint64_t below = tl == 0 ? 0ull : (~0ull >> (kWave - tl));
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j = li + L * s;
+    if (tok_ok && j < k) {
+      const uint64_t mb = bits[DEDUP ? E + col[s] : col[s]];
+      lslot[t * k + j] = (uint32_t(col[s]) << 8) | uint32_t(__popcll(mb & below));
+    }
   }
   for (int c = tid; c < C; c += nthreads) tcnt[c * Bp + b] = uint8_t(__popcll(bits[c]));
   const int64_t ncs = cs_tokens - b * kTile;  // tokens of this tile in the co-selection counts
   if (W != nullptr && ncs > 0) {
     const uint64_t cm = ncs >= kTile ? ~0ull : ((1ull << ncs) - 1ull);
-    const int pairs = E * E;
-    for (int q = tid; q < pairs; q += nthreads) {
-      const int n = __popcll(bits[q / E] & bits[q % E] & cm);
-      if (n) atomicAdd(&W[q], n);
+    if (nthreads % E == 0) {  // a fixed column per thread, rows stepping by nthreads / E
+      const int cb = tid % E;
+      const uint64_t mcol = bits[cb] & cm;
+      for (int a = tid / E; a < E; a += nthreads / E) {
+        const int n = __popcll(bits[a] & mcol);
+        if (n) atomicAdd(&W[a * E + cb], n);
+      }
+    } else {
+      for (int q = tid; q < E * E; q += nthreads) {
+        const int n = __popcll(bits[q / E] & bits[q % E] & cm);
+        if (n) atomicAdd(&W[q], n);
+      }
     }
   }
 }
 
-template <int L, int V, bool FULL>
+template <int L, int V, int VEC, bool FULL>
 static hipError_t launch_route(const float* logits, int64_t tokens, int E, int k, int32_t* idx,
                                float* gate, hipStream_t stream) {
   constexpr int G = kWave / L;
   const int64_t per_block = 4 * G;
   int64_t blocks = (tokens + per_block - 1) / per_block;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((route_topk_kernel<L, V, FULL>), dim3(unsigned(blocks)), dim3(256), 0, stream,
-                     logits, tokens, E, k, idx, gate);
+  hipLaunchKernelGGL((route_topk_kernel<L, V, VEC, FULL>), dim3(unsigned(blocks)), dim3(256), 0,
+                     stream, logits, tokens, E, k, idx, gate);
   return hipGetLastError();
+}
+
+// Lanes per token L = min(16, E rounded up to a power of two) and logits per
+// lane V = ceil(E / L).  (Four lanes with 16 logits each were measured slower
+// at E = 64: one wave per SIMD then leaves the round's dependent chain
+// unhidden.)  VEC = 4 needs V % 4 == 0.
+template <bool FULL, int VEC>
+static hipError_t launch_route_v(const float* logits, int64_t tokens, int E, int k, int32_t* idx,
+                                 float* gate, hipStream_t st) {
+  if (E <= 64) return launch_route<16, 4, VEC, FULL>(logits, tokens, E, k, idx, gate, st);
+  if (E <= 128) return launch_route<16, 8, VEC, FULL>(logits, tokens, E, k, idx, gate, st);
+  if (E <= 256) return launch_route<16, 16, VEC, FULL>(logits, tokens, E, k, idx, gate, st);
+  if (E <= 512) return launch_route<16, 32, VEC, FULL>(logits, tokens, E, k, idx, gate, st);
+  return launch_route<16, 64, VEC, FULL>(logits, tokens, E, k, idx, gate, st);
+}
+
+template <bool FULL>
+static hipError_t launch_route_small(const float* logits, int64_t tokens, int E, int k,
+                                     int32_t* idx, float* gate, hipStream_t st) {
+  if (E <= 1) return launch_route<1, 1, 1, FULL>(logits, tokens, E, k, idx, gate, st);
+  if (E <= 2) return launch_route<2, 1, 1, FULL>(logits, tokens, E, k, idx, gate, st);
+  if (E <= 4) return launch_route<4, 1, 1, FULL>(logits, tokens, E, k, idx, gate, st);
+  if (E <= 8) return launch_route<8, 1, 1, FULL>(logits, tokens, E, k, idx, gate, st);
+  if (E <= 16) return launch_route<16, 1, 1, FULL>(logits, tokens, E, k, idx, gate, st);
+  return launch_route<16, 2, 1, FULL>(logits, tokens, E, k, idx, gate, st);
 }
 
 template <bool FULL>
 static hipError_t launch_route_e(const float* logits, int64_t tokens, int E, int k, int32_t* idx,
                                  float* gate, hipStream_t stream) {
-  if (E <= 1) return launch_route<1, 1, FULL>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 2) return launch_route<2, 1, FULL>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 4) return launch_route<4, 1, FULL>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 8) return launch_route<8, 1, FULL>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 16) return launch_route<16, 1, FULL>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 32) return launch_route<16, 2, FULL>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 64) return launch_route<16, 4, FULL>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 128) return launch_route<16, 8, FULL>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 256) return launch_route<16, 16, FULL>(logits, tokens, E, k, idx, gate, stream);
-  if (E <= 512) return launch_route<16, 32, FULL>(logits, tokens, E, k, idx, gate, stream);
-  return launch_route<16, 64, FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E <= 32) return launch_route_small<FULL>(logits, tokens, E, k, idx, gate, stream);
+  if (E % 4 == 0) return launch_route_v<FULL, 4>(logits, tokens, E, k, idx, gate, stream);
+  return launch_route_v<FULL, 1>(logits, tokens, E, k, idx, gate, stream);
 }
 
 // full_softmax: gates are the softmax over all E logits at the selected
@@ -295,14 +377,13 @@ hipError_t launch_send_counts(const int32_t* idx, int64_t T, int E, int k, int R
 
 // Largest expert count and token count routed by the fused kernel; beyond them
 // the routing, the counting and the co-selection counts run as separate kernels
-// (same results).  The fused kernel has one workgroup per 64-token tile, so it
-// runs 4 waves per SIMD on a quarter of the CUs that the routing kernel fills:
-// at E = 256 its selection rounds cost more than the launch it saves.  Its
-// co-selection counts take E * E popcounts per tile.
+// (same results).  The fused kernel has one workgroup per 64-token tile; its
+// co-selection counts take E * E popcounts per tile, which at E = 256 cost
+// more than the separate co-selection kernel.
 constexpr int kFusedMaxExperts = 128;
 constexpr int64_t kFusedMaxTokens = int64_t(1) << 24;
 
-template <int L, int V, bool FULL>
+template <int L, int V, int VEC, bool FULL>
 static hipError_t launch_route_tile(const float* logits, int64_t T, int E, int k, int R,
                                     const int32_t* place, int dedup, int32_t* idx, float* gate,
                                     int64_t cs_tokens, int32_t* W, void* workspace,
@@ -313,30 +394,31 @@ static hipError_t launch_route_tile(const float* logits, int64_t T, int E, int k
   uint32_t* lslot = reinterpret_cast<uint32_t*>(ws + pl.lslot_off);
   const size_t lds = size_t(pl.cols) * sizeof(uint64_t) + size_t(E) * sizeof(int32_t);
   if (dedup)
-    hipLaunchKernelGGL((route_tile_kernel<L, V, FULL, true>), dim3(unsigned(pl.tiles)),
+    hipLaunchKernelGGL((route_tile_kernel<L, V, VEC, FULL, true>), dim3(unsigned(pl.tiles)),
                        dim3(kTile * L), lds, stream, logits, T, E, k, R, place, E / R,
                        pl.tiles_pad, idx, gate, tcnt, lslot, cs_tokens, W);
   else
-    hipLaunchKernelGGL((route_tile_kernel<L, V, FULL, false>), dim3(unsigned(pl.tiles)),
+    hipLaunchKernelGGL((route_tile_kernel<L, V, VEC, FULL, false>), dim3(unsigned(pl.tiles)),
                        dim3(kTile * L), lds, stream, logits, T, E, k, R, place, E / R,
                        pl.tiles_pad, idx, gate, tcnt, lslot, cs_tokens, W);
   return hipGetLastError();
 }
 
-template <bool FULL>
+template <bool FULL, int VEC>
 static hipError_t launch_route_tile_e(const float* logits, int64_t T, int E, int k, int R,
                                       const int32_t* place, int dedup, int32_t* idx, float* gate,
                                       int64_t cs, int32_t* W, void* ws, hipStream_t st) {
-#define MOE_RT(LL, VV) \
-  launch_route_tile<LL, VV, FULL>(logits, T, E, k, R, place, dedup, idx, gate, cs, W, ws, st)
-  if (E <= 1) return MOE_RT(1, 1);
-  if (E <= 2) return MOE_RT(2, 1);
-  if (E <= 4) return MOE_RT(4, 1);
-  if (E <= 8) return MOE_RT(8, 1);
-  if (E <= 16) return MOE_RT(16, 1);
-  if (E <= 32) return MOE_RT(16, 2);
-  if (E <= 64) return MOE_RT(16, 4);
-  return MOE_RT(16, 8);
+#define MOE_RT(LL, VV, VC)                                                                    \
+  launch_route_tile<LL, VV, VC, FULL>(logits, T, E, k, R, place, dedup, idx, gate, cs, W, ws, \
+                                      st)
+  if (E <= 1) return MOE_RT(1, 1, 1);
+  if (E <= 2) return MOE_RT(2, 1, 1);
+  if (E <= 4) return MOE_RT(4, 1, 1);
+  if (E <= 8) return MOE_RT(8, 1, 1);
+  if (E <= 16) return MOE_RT(16, 1, 1);
+  if (E <= 32) return MOE_RT(16, 2, 1);
+  if (E <= 64) return MOE_RT(16, 4, VEC);
+  return MOE_RT(16, 8, VEC);
 #undef MOE_RT
 }
 
@@ -362,10 +444,13 @@ hipError_t launch_route_plan(const float* logits, int64_t T, int E, int k, int f
     return launch_coselect(idx, cs_tokens, E, k, W, stream);
   }
   if (T > 0) {
-    err = full_softmax ? launch_route_tile_e<true>(logits, T, E, k, R, place, dedup, idx, gate,
-                                                   cs_tokens, W, workspace, stream)
-                       : launch_route_tile_e<false>(logits, T, E, k, R, place, dedup, idx, gate,
-                                                    cs_tokens, W, workspace, stream);
+    const bool v4 = E % 4 == 0;
+#define MOE_RTE(FU, VC)                                                                \
+  launch_route_tile_e<FU, VC>(logits, T, E, k, R, place, dedup, idx, gate, cs_tokens, W, \
+                              workspace, stream)
+    err = full_softmax ? (v4 ? MOE_RTE(true, 4) : MOE_RTE(true, 1))
+                       : (v4 ? MOE_RTE(false, 4) : MOE_RTE(false, 1));
+#undef MOE_RTE
     if (err != hipSuccess) return err;
   }
   return launch_plan_scan(T, E, k, R, place, dedup, expert_counts, rank_counts, rank_offsets,
