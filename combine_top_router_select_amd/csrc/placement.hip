@@ -14,9 +14,16 @@
 //   A[e][b] + A[f][a] - A[e][a] - A[f][b] - 2 S(e, f).
 // A is kept up to date in O(E) per swap, so a pass over all pairs is O(E^2).
 // Runs on the host: E <= 1024, and the search is sequential by nature.
+//
+// Also the token-shuffle planner's assignment ("Expert Coupling in MoE
+// Pretraining" (summary), "Method 2: Token Shuffling": greedy in decreasing
+// confidence under a per-rank capacity): tokens sorted by confidence = largest
+// score / sum of scores (ties to the lower token), each to its highest-scoring
+// rank with room left of T/R (ties to the lower rank).  Sequential, host.
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <vector>
 
 namespace moe {
@@ -74,6 +81,38 @@ int placement_search(const int32_t* W, int E, int R, const int32_t* initial, int
     *objective = o2 / 2;
   }
   if (swaps) *swaps = done;
+  return 0;
+}
+
+// Host: confidence order, then each token to its best rank with room.
+int shuffle_assign(const float* scores, int64_t T, int R, int32_t* owner) {
+  std::vector<double> conf(static_cast<size_t>(T));
+  for (int64_t t = 0; t < T; ++t) {
+    double mx = 0.0, sum = 0.0;
+    for (int r = 0; r < R; ++r) {
+      const double v = double(scores[t * R + r]);
+      sum += v;
+      if (v > mx) mx = v;
+    }
+    conf[size_t(t)] = sum > 0.0 ? mx / sum : 0.0;
+  }
+  std::vector<int64_t> order(static_cast<size_t>(T));
+  for (int64_t t = 0; t < T; ++t) order[size_t(t)] = t;
+  std::sort(order.begin(), order.end(), [&](int64_t x, int64_t y) {
+    if (conf[size_t(x)] != conf[size_t(y)]) return conf[size_t(x)] > conf[size_t(y)];
+    return x < y;
+  });
+  std::vector<int64_t> room(static_cast<size_t>(R), T / R);
+  for (int64_t t : order) {
+    const float* s = scores + t * R;
+    int best = -1;
+    for (int r = 0; r < R; ++r) {
+      if (room[size_t(r)] == 0) continue;
+      if (best < 0 || s[r] > s[best]) best = r;
+    }
+    owner[t] = best;
+    --room[size_t(best)];
+  }
   return 0;
 }
 

@@ -1,5 +1,5 @@
-// Token-shuffle planner: fit, prediction (GPU) and capacity-constrained
-// assignment (host).
+// Token-shuffle planner: fit and prediction (GPU).  The capacity-constrained
+// assignment that follows is host code, in placement.hip.
 //
 // Source: "Expert Coupling in MoE Pretraining" (summary), "Method 2: Token
 // Shuffling": the planner predicts each token's owner rank at layer l+1 from
@@ -21,9 +21,6 @@
 // bit for bit and the assignment's decisions are the same.
 #include <stddef.h>
 #include <stdint.h>
-
-#include <algorithm>
-#include <vector>
 
 #include "common.hpp"
 #include "moe_route.h"
@@ -121,38 +118,6 @@ hipError_t launch_shuffle_predict(const int32_t* prev, const int32_t* cur, int64
   hipLaunchKernelGGL(shuffle_predict_kernel, dim3(unsigned((T + 3) / 4)), dim3(256), 0, stream,
                      prev, cur, T, E, k, R, pair, single, min_obs, scores);
   return hipGetLastError();
-}
-
-// Host: confidence order, then each token to its best rank with room.
-int shuffle_assign(const float* scores, int64_t T, int R, int32_t* owner) {
-  std::vector<double> conf(static_cast<size_t>(T));
-  for (int64_t t = 0; t < T; ++t) {
-    double mx = 0.0, sum = 0.0;
-    for (int r = 0; r < R; ++r) {
-      const double v = double(scores[t * R + r]);
-      sum += v;
-      if (v > mx) mx = v;
-    }
-    conf[size_t(t)] = sum > 0.0 ? mx / sum : 0.0;
-  }
-  std::vector<int64_t> order(static_cast<size_t>(T));
-  for (int64_t t = 0; t < T; ++t) order[size_t(t)] = t;
-  std::sort(order.begin(), order.end(), [&](int64_t x, int64_t y) {
-    if (conf[size_t(x)] != conf[size_t(y)]) return conf[size_t(x)] > conf[size_t(y)];
-    return x < y;
-  });
-  std::vector<int64_t> room(static_cast<size_t>(R), T / R);
-  for (int64_t t : order) {
-    const float* s = scores + t * R;
-    int best = -1;
-    for (int r = 0; r < R; ++r) {
-      if (room[size_t(r)] == 0) continue;
-      if (best < 0 || s[r] > s[best]) best = r;
-    }
-    owner[t] = best;
-    --room[size_t(best)];
-  }
-  return 0;
 }
 
 }  // namespace moe

@@ -1,10 +1,12 @@
 // Host-only driver run under AddressSanitizer and UndefinedBehaviorSanitizer
 // by tests/test_sanitizers.py: exercises every oracle entry point and the
-// library's host placement search on small and edge-case shapes.  Exits 0
+// library's host planners (placement search, token-shuffle assignment) on
+// small and edge-case shapes, and checks the planners against the oracle.  Exits 0
 // when the sanitizers report nothing (they abort otherwise).
 #include <stdint.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <random>
 #include <vector>
 
@@ -27,9 +29,15 @@ int oracle_combine_fp8(const uint8_t*, const float*, const int32_t*, int64_t, in
 int oracle_coselect(const int32_t*, int64_t, int, int, int32_t*);
 int oracle_placement_search(const int32_t*, int, int, const int32_t*, int, int32_t*, int64_t*,
                             int*);
+int oracle_shuffle_fit(const int32_t*, const int32_t*, const int32_t*, int64_t, int, int, int,
+                       const int32_t*, int32_t*, int32_t*);
+int oracle_shuffle_predict(const int32_t*, const int32_t*, int64_t, int, int, int,
+                           const int32_t*, const int32_t*, int, float*);
+int oracle_shuffle_assign(const float*, int64_t, int, int32_t*);
 }
 namespace moe {
 int placement_search(const int32_t*, int, int, const int32_t*, int, int32_t*, int64_t*, int*);
+int shuffle_assign(const float*, int64_t, int, int32_t*);
 }
 
 static int run(int T, int E, int k, int R, int H, unsigned seed) {
@@ -88,6 +96,25 @@ static int run(int T, int E, int k, int R, int H, unsigned seed) {
   if (oracle_placement_search(W.data(), E, R, nullptr, E * E, p1.data(), &o1, &s1)) return 1;
   if (moe::placement_search(W.data(), E, R, nullptr, E * E, p2.data(), &o2, &s2)) return 1;
   if (p1 != p2 || o1 != o2 || s1 != s2) return 2;
+  // token-shuffle planner: the three layers are the routing above and two
+  // shuffled copies of it; T rounded down to a multiple of R for the assignment
+  std::vector<int32_t> prev(idx), next(idx);
+  std::shuffle(prev.begin(), prev.end(), g);
+  std::shuffle(next.begin(), next.end(), g);
+  std::vector<int32_t> pair(size_t(E) * E * R, 0), single(size_t(E) * R, 0);
+  if (oracle_shuffle_fit(prev.data(), idx.data(), next.data(), T, E, k, R, place.data(),
+                         pair.data(), single.data()))
+    return 1;
+  std::vector<float> sc(size_t(T) * R);
+  for (int min_obs : {0, 1, 3, 1 << 30})
+    if (oracle_shuffle_predict(prev.data(), idx.data(), T, E, k, R, pair.data(), single.data(),
+                               min_obs, sc.data()))
+      return 1;
+  const int Ta = T / R * R;
+  std::vector<int32_t> o_or(size_t(Ta) + 1), o_lib(size_t(Ta) + 1);
+  if (oracle_shuffle_assign(sc.data(), Ta, R, o_or.data())) return 1;
+  if (moe::shuffle_assign(sc.data(), Ta, R, o_lib.data())) return 1;
+  if (o_or != o_lib) return 3;
   return 0;
 }
 
