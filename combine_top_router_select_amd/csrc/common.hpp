@@ -78,6 +78,9 @@ __device__ __forceinline__ u32x4 keep_bytes(u32x4 v, int n) {
 //                    ranks in dedup mode); at most 64, the tile size
 //   lslot[T][k]      uint32: (position column << 8) | rank of (t, j) among the
 //                    tile's earlier tokens that use the same position column
+//   bm[B][E]         uint64: bit i set when token i of the tile selects expert e
+//                    (written by the separate counting kernel; the co-selection
+//                    counts of the combined routing call read it)
 // The row of (t, j) is gbase[c][b / 16] + (counts of tiles 16 (b / 16) .. b - 1
 // in column c) + rank, with b = t / 64.
 struct PlanLayout {
@@ -90,6 +93,7 @@ struct PlanLayout {
   size_t base_off;    // byte offsets inside the workspace
   size_t tcnt_off;
   size_t lslot_off;
+  size_t bm_off;
   size_t bytes;
 };
 
@@ -107,7 +111,8 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t tokens, int n_experts,
   p.base_off = 256;
   p.tcnt_off = align256(p.base_off + size_t(p.pos_cols) * size_t(p.groups) * 4);
   p.lslot_off = align256(p.tcnt_off + size_t(p.cols) * size_t(p.tiles_pad));
-  p.bytes = align256(p.lslot_off + size_t(tokens) * size_t(top_k) * 4);
+  p.bm_off = align256(p.lslot_off + size_t(tokens) * size_t(top_k) * 4);
+  p.bytes = align256(p.bm_off + size_t(p.tiles) * size_t(n_experts) * 8);
   return p;
 }
 

@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(kWave)
 tile_counts_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k, int R,
                    const int32_t* __restrict__ place, int m, uint32_t kmul, int64_t Bp,
                    const int32_t* __restrict__ n_valid, uint8_t* __restrict__ tcnt,
-                   uint32_t* __restrict__ lslot) {
+                   uint32_t* __restrict__ lslot, uint64_t* __restrict__ bm) {
   extern __shared__ uint64_t s_tdyn[];
   const int C = E + (DEDUP ? R : 0);
   uint64_t* bits = s_tdyn;                                        // [C]
@@ -139,6 +139,8 @@ tile_counts_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k, int
   count_tile<DEDUP, PAD, KMAX>(raw, f0, nf, k, kmul, E, has_rank ? s_rank : nullptr, m, tvalid,
                                bits, lslot, lane);
   for (int c = lane; c < C; c += kWave) tcnt[c * Bp + b] = uint8_t(__popcll(bits[c]));
+  if (bm)  // the tile's expert bitmaps, for the co-selection counts
+    for (int e = lane; e < E; e += kWave) bm[b * E + e] = bits[e];
 }
 
 // ------------------------------------------------------------------- scan --
@@ -419,6 +421,7 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* tcnt = ws + pl.tcnt_off;
   uint32_t* lslot = reinterpret_cast<uint32_t*>(ws + pl.lslot_off);
+  uint64_t* bm = PAD ? nullptr : reinterpret_cast<uint64_t*>(ws + pl.bm_off);
   const int m = E / R;
   if (T > 0) {
     const size_t lds = size_t(pl.cols) * sizeof(uint64_t) + size_t(E) * sizeof(int32_t);
@@ -426,11 +429,11 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
     if (dedup)
       hipLaunchKernelGGL((tile_counts_kernel<true, false, KMAX>), dim3(unsigned(pl.tiles)),
                          dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
-                         n_valid, tcnt, lslot);
+                         n_valid, tcnt, lslot, bm);
     else
       hipLaunchKernelGGL((tile_counts_kernel<false, PAD, KMAX>), dim3(unsigned(pl.tiles)),
                          dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
-                         n_valid, tcnt, lslot);
+                         n_valid, tcnt, lslot, bm);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

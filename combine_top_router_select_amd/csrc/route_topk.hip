@@ -378,8 +378,8 @@ hipError_t launch_send_counts(const int32_t* idx, int64_t T, int E, int k, int R
 // Largest expert count and token count routed by the fused kernel; beyond them
 // the routing, the counting and the co-selection counts run as separate kernels
 // (same results).  The fused kernel has one workgroup per 64-token tile; its
-// co-selection counts take E * E popcounts per tile, which at E = 256 cost
-// more than the separate co-selection kernel.
+// co-selection counts take E * E popcounts and up to E * E atomics per tile,
+// which at E = 256 cost more than a separate pass over the tile bitmaps.
 constexpr int kFusedMaxExperts = 128;
 constexpr int64_t kFusedMaxTokens = int64_t(1) << 24;
 
@@ -422,12 +422,13 @@ static hipError_t launch_route_tile_e(const float* logits, int64_t T, int E, int
 #undef MOE_RT
 }
 
-hipError_t launch_coselect(const int32_t* idx, int64_t n, int E, int k, int32_t* W,
-                           hipStream_t stream);
+hipError_t launch_coselect_bm(const uint64_t* bm, int64_t cs_tokens, int E, int32_t* W,
+                              hipStream_t stream);
 
 // Routing, the dispatch plan and (W non-null) the co-selection counts of the
 // first cs_tokens tokens: the fused kernel then the scan, or (large E or T)
-// the separate kernels.
+// the routing kernel, the counting kernel and the scan, then the co-selection
+// counts from the per-tile expert bitmaps the counting kernel left behind.
 hipError_t launch_route_plan(const float* logits, int64_t T, int E, int k, int full_softmax,
                              int R, const int32_t* place, int dedup, int32_t* idx, float* gate,
                              int32_t* expert_counts, int32_t* rank_counts, int32_t* rank_offsets,
@@ -441,7 +442,11 @@ hipError_t launch_route_plan(const float* logits, int64_t T, int E, int k, int f
     err = launch_send_counts(idx, T, E, k, R, place, dedup, expert_counts, rank_counts,
                              rank_offsets, expert_offsets, workspace, stream);
     if (err != hipSuccess || W == nullptr) return err;
-    return launch_coselect(idx, cs_tokens, E, k, W, stream);
+    // the counting kernel left every tile's expert bitmaps in the workspace
+    const PlanLayout pl = plan_layout(T, E, k, R, dedup);
+    const uint64_t* bm =
+        reinterpret_cast<const uint64_t*>(static_cast<const uint8_t*>(workspace) + pl.bm_off);
+    return launch_coselect_bm(bm, cs_tokens, E, W, stream);
   }
   if (T > 0) {
     const bool v4 = E % 4 == 0;
