@@ -113,6 +113,33 @@ def calib_copy():
                       "ms": ms, "GBps_rw": 2 * n / ms / 1e6}), flush=True)
 
 
+def copy_reference(torch, nbytes, launches=100):
+    """Device-to-device copies moving `nbytes` per launch (half read, half
+    written), timed like the kernels: back-to-back launches over rotated
+    buffers (about 1.5 GB, beyond the 256 MB Infinity Cache) queued behind a GPU
+    sleep, bracketed by HIP events on the current stream."""
+    half = max(1, nbytes // 2)
+    pairs = max(2, int(np.ceil(1.5e9 / (2 * half))))
+    bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda:0"),
+             torch.empty(half, dtype=torch.uint8, device="cuda:0")) for _ in range(pairs)]
+    for a, b in bufs:
+        a.fill_(1)
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)
+    e0.record()
+    for i in range(launches):
+        a, b = bufs[i % pairs]
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / launches
+    del bufs
+    return {"bytes_per_copy": 2 * half, "us": round(t * 1e6, 2),
+            "GBps": round(2 * half / t / 1e9, 1)}
+
+
 class BufferSet:
     """Device buffers for one step (inputs resident, outputs preallocated)."""
 
@@ -633,6 +660,7 @@ def main():
         "self_rank_share": round(int(b.cnt["rank_counts"][0].item()) / n_rows, 4),
         "algorithmic_bytes": {"dispatch": disp_bytes, "combine": comb_bytes,
                               "metadata": meta_bytes},
+        "copy_reference": copy_reference(torch, dom[2]),
         "device": torch.cuda.get_device_name(0),
         "hip_version": getattr(torch.version, "hip", None),
         "host_cores_available": len(os.sched_getaffinity(0)),
