@@ -24,6 +24,10 @@
 #ifndef MOE_COMBINE_NT
 #define MOE_COMBINE_NT 1
 #endif
+// Input vectors in flight per lane (KMAX rows x NV vectors) at most.
+#ifndef MOE_COMBINE_VECS
+#define MOE_COMBINE_VECS 24
+#endif
 
 namespace moe {
 
@@ -199,11 +203,12 @@ template <int KMAX, bool IN8>
 static hipError_t launch_combine_k(const void* rows, const float* w, const int32_t* slot_row,
                                    int64_t T, int row_bytes, int k, const int32_t* n_valid,
                                    void* out, hipStream_t stream) {
-  // keep KMAX * NV <= 32 input vectors (128 VGPRs) in flight per lane, and the
-  // fp8 accumulators (16 per vector) to two vectors
+  // keep KMAX * NV <= MOE_COMBINE_VECS input vectors in flight per lane, and
+  // the fp8 accumulators (16 per vector) to two vectors
   const int vr = row_bytes / 16;
   constexpr int NVCAP = IN8 ? 2 : 4;
-  constexpr int NVMAX = (32 / KMAX) < NVCAP ? (32 / KMAX) : NVCAP;
+  constexpr int NVB = MOE_COMBINE_VECS / KMAX > 0 ? MOE_COMBINE_VECS / KMAX : 1;
+  constexpr int NVMAX = NVB < NVCAP ? NVB : NVCAP;
   if (NVMAX >= 4 && vr >= 4 * kWave)
     return launch_combine_t<(NVMAX >= 4 ? 4 : 1), KMAX, IN8>(rows, w, slot_row, T, row_bytes, k,
                                                               n_valid, out, stream);
