@@ -55,10 +55,15 @@ def _buffers(w, dedup, dev):
     return b
 
 
-def _step(w, dedup, logits, x, place, b):
+def _step(w, dedup, logits, x, place, b, fused=False):
     E, k, R = w.n_experts, w.top_k, w.n_ranks
-    ops.moe_route_topk(logits, k, b["idx"], b["gate"])
-    c = ops.moe_send_counts(b["idx"], E, R, place, dedup, ws=b["ws"], out=b["cnt"])
+    if fused:   # routing, plan and co-selection counts in one call
+        c = ops.moe_route_plan(logits, k, R, place, dedup, topk_idx=b["idx"], topk_gate=b["gate"],
+                               ws=b["ws"], out=b["cnt"], coselect=b["W"],
+                               coselect_tokens=w.coselect_tokens)[2]
+    else:
+        ops.moe_route_topk(logits, k, b["idx"], b["gate"])
+        c = ops.moe_send_counts(b["idx"], E, R, place, dedup, ws=b["ws"], out=b["cnt"])
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
     d = f(x, b["idx"], b["gate"], E, R, c["ws"], place, out=b["disp"])
     ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b["out"])
@@ -70,7 +75,8 @@ def _step(w, dedup, logits, x, place, b):
         red = ops.moe_expand_reduce(ex["expanded"], ex["exp_gate"], ex["row_slot"], d["n_rows"],
                                     out=b["red"])
         ops.moe_combine(red, None, d["slot_row"], out=b["out2"])
-    ops.moe_coselect_counts(b["idx"], E, tokens=w.coselect_tokens, coselect=b["W"])
+    if not fused:
+        ops.moe_coselect_counts(b["idx"], E, tokens=w.coselect_tokens, coselect=b["W"])
 
 
 def _snapshot(b):
@@ -100,10 +106,17 @@ def _snapshot(b):
     return snap
 
 
-@pytest.mark.parametrize("name,dedup", [("deepseek_moe_16b", False), ("zyphra_top6_ep32", True)])
-def test_graph_replays_match_eager(name, dedup):
+@pytest.mark.parametrize("name,dedup,fused", [
+    ("deepseek_moe_16b", False, False), ("zyphra_top6_ep32", True, False),
+    ("deepseek_moe_16b", False, True), ("e256_top8_h2048", False, True),
+    ("zyphra_top2_ep8", True, True)])
+def test_graph_replays_match_eager(name, dedup, fused):
+    """fused: moe_route_plan in place of the routing, counting and co-selection
+    calls (the fused kernel up to 128 experts, the tile-bitmap co-selection
+    above); the eager reference uses the separate calls, so the replays also
+    check the two paths against each other."""
     w = WL.get(name)
-    say(f"[graph] {name} dedup={dedup}")
+    say(f"[graph] {name} dedup={dedup} fused={fused}")
     dev = torch.device("cuda:0")
     inp = WL.make_inputs(w)
     logits = to_dev(inp["logits"])
@@ -119,12 +132,12 @@ def test_graph_replays_match_eager(name, dedup):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        _step(w, dedup, logits, x, place, gb)   # warm up outside capture
+        _step(w, dedup, logits, x, place, gb, fused)   # warm up outside capture
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _step(w, dedup, logits, x, place, gb)
+        _step(w, dedup, logits, x, place, gb, fused)
     torch.cuda.synchronize()
     for rep in range(4):
         # scramble the outputs with eager work, then replay
@@ -137,6 +150,7 @@ def test_graph_replays_match_eager(name, dedup):
             gb["red"].view(torch.uint8).fill_(0x5A)
             gb["out2"].view(torch.uint8).fill_(0x5A)
         gb["idx"].fill_(-1)
+        gb["ws"].fill_(0xA5)   # the plan is rebuilt by every replay
         gb["W"].zero_()
         torch.cuda.synchronize()
         g.replay()
