@@ -74,6 +74,7 @@ ROUTE_PLAN_CASES = [  # T, E, k, R
     (1, 8, 2, 4), (63, 8, 2, 4), (64, 64, 6, 16), (1000, 64, 6, 16), (777, 128, 8, 16),
     (300, 8, 8, 8), (257, 3, 1, 1), (129, 1, 1, 1), (500, 256, 8, 32), (200, 100, 16, 4),
     (4100, 16, 4, 16), (130, 512, 16, 64), (70, 1024, 3, 8),
+    (5000, 256, 8, 16),   # tile bitmaps of 79 tiles: two chunks, atomic adds into W
 ]
 
 
@@ -504,6 +505,13 @@ def test_zero_tokens():
                           torch.empty((0, k), dtype=torch.int32, device=dv))
     sync()
     assert out.shape == (0, H)
+    for dedup in (False, True):    # the combined routing call: zeros, W untouched
+        W = torch.full((E, E), 3, dtype=torch.int32, device=dv)
+        _, _, c = ops.moe_route_plan(torch.empty((0, E), dtype=torch.float32, device=dv), k, R,
+                                     None, dedup, coselect=W)
+        sync()
+        assert (host(c["rank_counts"]) == 0).all() and (host(c["rank_offsets"]) == 0).all()
+        assert (host(c["expert_counts"]) == 0).all() and (host(W) == 3).all()
 
 
 def test_k_equals_e_and_k1(oracle_mod):
