@@ -368,7 +368,7 @@ def shuffle_leg(torch, ops, WL, w):
     evaluation batch, and report the share of layer l+1 token-expert
     assignments served on the token's own rank: contiguous token ownership vs
     the planned owners.  Not part of the timed step; GPU times are HIP events
-    around single launches (host launch latency included)."""
+    around single launches queued behind a GPU sleep (no host time inside)."""
     E, k, R, T = w.n_experts, w.top_k, w.n_ranks, w.tokens
     dev = torch.device("cuda:0")
 
@@ -384,9 +384,12 @@ def shuffle_leg(torch, ops, WL, w):
                             *ops.moe_shuffle_fit(cal[0], cal[1], cal[2], E, R, pl), 8)
     e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
+    torch.cuda._sleep(5_000_000)   # the launches queue up behind it
     e[0].record()
     ops.moe_shuffle_fit(cal[0], cal[1], cal[2], E, R, pl, pair, single)
     e[1].record()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(5_000_000)
     e[2].record()
     scores = ops.moe_shuffle_predict(ev[0], ev[1], pair, single, 8)
     e[3].record()

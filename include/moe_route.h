@@ -366,7 +366,8 @@ int moe_placement_search(const int32_t* coselect, int n_experts, int n_ranks,
  *   prev_idx, cur_idx, next_idx  [T][k] int32 (ids in [0, E)).
  *   pair_counts    [E][E][R] int32, ACCUMULATED (zero it first).
  *   single_counts  [E][R] int32, ACCUMULATED.
- * Integer atomics: the result does not depend on their order.
+ * Integer sums: the result does not depend on their order.  Calls that
+ * accumulate into the same tables must not run concurrently.
  * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (as moe_send_counts()). */
 int moe_shuffle_fit(const int32_t* prev_idx, const int32_t* cur_idx, const int32_t* next_idx,
                     int64_t tokens, int n_experts, int top_k, int n_ranks,

@@ -35,7 +35,8 @@ def _check(oracle_mod, prev, cur, nxt, E, R, place, min_obs):
 
 @pytest.mark.parametrize("T,E,k,R,min_obs", [(200, 8, 2, 4, 1), (333, 16, 3, 8, 4),
                                              (1000, 64, 6, 16, 8), (64, 128, 16, 64, 2),
-                                             (100, 4, 1, 2, 0), (257, 32, 4, 32, 1000)])
+                                             (100, 4, 1, 2, 0), (257, 32, 4, 32, 1000),
+                                             (50, 6, 2, 1, 1), (70, 12, 3, 3, 1)])
 def test_shuffle_fit_predict_parity(oracle_mod, T, E, k, R, min_obs):
     say(f"[shuffle] T={T} E={E} k={k} R={R} min_obs={min_obs}")
     rng = np.random.default_rng(T * 3 + k)
