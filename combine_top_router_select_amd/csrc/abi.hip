@@ -223,7 +223,11 @@ MOE_API int moe_combine(const void* rows, const float* row_weight, const int32_t
 
 MOE_API size_t moe_expand_workspace_bytes(int64_t capacity, int n_experts, int top_k,
                                           int n_ranks) {
-  return moe_workspace_bytes(capacity, n_experts, top_k, n_ranks, 0);
+  if (check_tek(capacity, n_experts, top_k) != MOE_OK) return 0;
+  if (check_ranks(n_experts, n_ranks) != MOE_OK) return 0;
+  // the plan of the plain layout without its last region, the tile expert
+  // bitmaps (only the co-selection counts of the routing call read them)
+  return moe::plan_layout(capacity, n_experts, top_k, n_ranks, 0).bm_off;
 }
 
 MOE_API int moe_expand_counts(const int32_t* row_experts, const int32_t* n_rows,
