@@ -1,19 +1,27 @@
 """Benchmark of the per-GPU MoE dispatch/combine hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
-                    [--receive] [--search] [--shuffle] [--fp8] [--graph] [--overlap]
-                    [--no-cpu-baseline]
+                    [--receive] [--fp8] [--search] [--shuffle] [--streams {1,2}]
+                    [--separate] [--graph] [--overlap] [--step-events]
+                    [--no-cpu-baseline] [--cpu-seconds S] [--footprint-gib G]
                     [--calib-copy]
 
 A step is one pass of the whole path over one batch of the workload's seeded
-synthetic input, with inputs resident in HBM: top-k routing -> send counts and
-offsets -> dispatch permute -> combine (identity experts: the combine reads the
-send buffer), and the co-selection counts of the routed tokens.  Everything
-runs on one stream; --overlap forks the co-selection counts (which depend only
-on the routing) onto a second stream and joins them before the step ends.  The
-workload defaults to 4096 tokens, hidden 2048 bf16, 64 experts, top-6, 16
-logical ranks, contiguous placement (DeepSeek-MoE-16B-shaped), plain (one row
-per token-expert) dispatch.
+synthetic input, with inputs resident in HBM: top-k routing, send counts,
+offsets and the co-selection counts of the routed tokens (one combined call;
+--separate uses their three entry points) -> dispatch permute -> combine
+(identity experts: the combine reads the send buffer).  With --receive (dedup)
+the receive side runs between dispatch and combine.  The workload defaults to
+4096 tokens, hidden 2048 bf16, 64 experts, top-6, 16 logical ranks, contiguous
+placement (DeepSeek-MoE-16B-shaped), plain (one row per token-expert) dispatch.
+
+Steps are independent batches.  By default consecutive steps alternate between
+two streams with no waits between them (the way a server overlaps two
+micro-batches), so one batch's latency-bound kernels can run beside the other
+batch's copies; each step's own kernels stay in order on its stream.  The same
+K steps are then timed on the other setting and reported as `other_streams`
+(--streams 1 swaps the two).  --overlap instead forks only the co-selection
+counts onto a second stream inside each step.
 
 The timed steps call the C ABI directly with arguments marshalled once per
 buffer set (the Python binding's per-call checks would otherwise cost about
@@ -31,8 +39,9 @@ kernel alone (queued behind a short GPU sleep so that host launch overhead
 stays out); `traffic` is the HBM bytes per launch that rocprofv3's FETCH_SIZE
 and WRITE_SIZE counters measured for that kernel (profiles/hbm_traffic_*.md,
 scaled by a plain-copy calibration), or null when there is no such record for
-the workload or the kernel's sources changed since.  `cpu_baseline` times the
-CPU oracle on the same workload.
+the workload or the kernel's sources changed since.  `copy_reference` times a
+plain device copy of the same bytes the same way.  `cpu_baseline` times the CPU
+oracle on the same workload.
 """
 from __future__ import annotations
 
@@ -75,6 +84,12 @@ def parse():
     p.add_argument("--shuffle", action="store_true",
                    help="also fit the token-shuffle planner on one batch of correlated "
                         "three-layer routing and plan another, reporting times and locality")
+    p.add_argument("--streams", type=int, default=2, choices=(1, 2),
+                   help="2 (default): alternate the rotated buffer sets, i.e. consecutive "
+                        "independent batches, between two streams so that one batch's "
+                        "latency-bound kernels overlap the other's copies (no cross-stream "
+                        "waits); 1: every step on one stream.  The other setting is timed too "
+                        "and reported as other_streams")
     p.add_argument("--separate", action="store_true",
                    help="route and count with moe_route_topk + moe_send_counts instead of the "
                         "fused moe_route_plan (one kernel more)")
@@ -263,7 +278,7 @@ def counter_traffic(kernel, workload, mode):
     return None
 
 
-def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True):
+def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True, stream=None):
     """The C-ABI calls of one step on buffer set b, with every argument
     marshalled once: the timed loop then costs a few microseconds of host time
     per step instead of the Python binding's checks.  With a side stream the
@@ -272,7 +287,7 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True)
     L = ops.lib()
     T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
     N = T * k
-    st = torch.cuda.current_stream().cuda_stream
+    st = (stream or torch.cuda.current_stream()).cuda_stream
     p = lambda t: None if t is None else t.data_ptr()
     c, d = b.cnt, b.disp
     cargs = (int(dedup), p(c["expert_counts"]), p(c["rank_counts"]), p(c["rank_offsets"]),
@@ -494,10 +509,17 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
 
-    raw = None
+    raw = raw_other = None
+    n_streams = a.streams if (side is None and not a.step_events and graphs is None) else 1
     if graphs is None:
-        raw = [raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side, fused)
-               for b in sets]
+        streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+
+        def raw_sets(ns):
+            return [raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side, fused,
+                                   streams[i % ns]) for i, b in enumerate(sets)]
+        raw = raw_sets(n_streams)
+        if side is None and not a.step_events:
+            raw_other = raw_sets(3 - n_streams)
 
     timed_kernels = ("moe_dispatch_permute", "moe_dispatch_permute_dedup", "moe_combine",
                      "moe_expand_permute", "moe_expand_reduce")
@@ -536,6 +558,19 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    other = None
+    if raw_other is not None:   # the same K steps with the other stream setting
+        raw, raw_main = raw_other, raw
+        for i in range(a.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        u0 = time.perf_counter()
+        for i in range(a.steps):
+            step(a.warmup + i)
+        torch.cuda.synchronize()
+        other = {"streams": 3 - n_streams,
+                 "ms_per_step": (time.perf_counter() - u0) / a.steps * 1e3}
+        raw = raw_main
     in_step = {}
     for (i, name), (e0, e1) in step_ev.items():
         in_step.setdefault(name, []).append(e0.elapsed_time(e1) * 1e-3)
@@ -609,16 +644,19 @@ def main():
     disp_bytes = row_bytes * (T + n_rows)   # read x once, write each row once
     comb_bytes = row_bytes * n_rows + out_bytes * T  # read each row once, write out once
     meta_bytes = n_rows * (12 if not dedup else 8 + 8 * k) + T * k * 4
+    route_bytes = T * E * 4 + T * k * 8        # logits in, ids and gates out
     dom = ("moe_dispatch_permute" + ("_dedup" if dedup else ""), t_disp, disp_bytes)
     if t_comb > t_disp:
         dom = ("moe_combine", t_comb, comb_bytes)
     achieved = dom[2] / dom[1] / 1e9
     dc_gbps = (disp_bytes + comb_bytes) / (t_disp + t_comb) / 1e9
     recv = None
+    job_bytes = disp_bytes + comb_bytes + meta_bytes + route_bytes
     if receive:
         n_exp = int(b.ecnt["rank_offsets"][R].item())
         exp_bytes = row_bytes * (n_rows + n_exp)  # read each received row once, write each copy
         red_bytes = row_bytes * n_exp + out_bytes * n_rows  # read each output once, write each row
+        job_bytes += exp_bytes + red_bytes
         recv = {"expanded_rows": n_exp,
                 "expand_us": round(t_exp * 1e6, 2), "reduce_us": round(t_red * 1e6, 2),
                 "expand_GBps": round(exp_bytes / t_exp / 1e9, 1),
@@ -644,6 +682,7 @@ def main():
                    "routing": "fused" if fused else "separate",
                    "bytes_per_element": bpe, "graph": bool(a.graph),
                    "coselect_stream": "side" if a.overlap else "main",
+                   "streams": n_streams,
                    "buffer_sets": nsets, "footprint_MiB": round(nsets * per_set / 2 ** 20)},
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -653,9 +692,14 @@ def main():
                      "algorithmic_bytes": dom[2]},
         "dispatch_us": round(t_disp * 1e6, 2),
         "in_step_event_us": in_step or None,
+        "other_streams": other,
         "combine_us": round(t_comb * 1e6, 2),
         "dispatch_combine_tokens_per_s": T / (t_disp + t_comb),
         "dispatch_combine_GBps": round(dc_gbps, 1),
+        # whole job: every algorithmic byte of a step (logits, ids, rows, metadata,
+        # and with --receive the receive side) over the measured step time
+        "job_GBps": round(job_bytes / (elapsed / a.steps) / 1e9, 1),
+        "job_hbm_frac": round(job_bytes / (elapsed / a.steps) / 1e9 / HBM_PEAK_GBPS, 4),
         "dispatch_combine_hbm_frac": round(dc_gbps / HBM_PEAK_GBPS, 4),
         "rows": n_rows,
         "rows_removed_by_dedup_pct": round(100.0 * (1 - n_rows / (T * k)), 2) if dedup else 0.0,
