@@ -84,7 +84,7 @@ def parse():
     p.add_argument("--shuffle", action="store_true",
                    help="also fit the token-shuffle planner on one batch of correlated "
                         "three-layer routing and plan another, reporting times and locality")
-    p.add_argument("--streams", type=int, default=2, choices=(1, 2),
+    p.add_argument("--streams", type=int, default=2, choices=(1, 2, 3, 4),
                    help="2 (default): alternate the rotated buffer sets, i.e. consecutive "
                         "independent batches, between two streams so that one batch's "
                         "latency-bound kernels overlap the other's copies (no cross-stream "
@@ -512,14 +512,14 @@ def main():
     raw = raw_other = None
     n_streams = a.streams if (side is None and not a.step_events and graphs is None) else 1
     if graphs is None:
-        streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+        streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(3)]
 
         def raw_sets(ns):
             return [raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side, fused,
                                    streams[i % ns]) for i, b in enumerate(sets)]
         raw = raw_sets(n_streams)
         if side is None and not a.step_events:
-            raw_other = raw_sets(3 - n_streams)
+            raw_other = raw_sets(1 if n_streams > 1 else 2)
 
     timed_kernels = ("moe_dispatch_permute", "moe_dispatch_permute_dedup", "moe_combine",
                      "moe_expand_permute", "moe_expand_reduce")
@@ -568,7 +568,7 @@ def main():
         for i in range(a.steps):
             step(a.warmup + i)
         torch.cuda.synchronize()
-        other = {"streams": 3 - n_streams,
+        other = {"streams": 1 if n_streams > 1 else 2,
                  "ms_per_step": (time.perf_counter() - u0) / a.steps * 1e3}
         raw = raw_main
     in_step = {}
