@@ -331,37 +331,48 @@ def test_coselect_parity(oracle_mod, T, E, k, n):
 
 # ------------------------------------------------------- full workloads --
 
-def gpu_chain(inp, w, dedup, stream=None):
-    """The whole hot path on the GPU, through the C ABI."""
+def gpu_chain(inp, w, dedup, stream=None, fused=False):
+    """The whole hot path on the GPU, through the C ABI: the separate routing,
+    counting and co-selection calls, or (fused) the combined routing call the
+    benchmark times."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
     place = to_dev(inp["placement"]) if inp["placement"] is not None else None
     logits = to_dev(inp["logits"])
     x = bf16_dev(inp["x_bits"])
-    idx, gate = ops.moe_route_topk(logits, k, stream=stream)
-    c = ops.moe_send_counts(idx, E, R, place, dedup=dedup, stream=stream)
+    if fused:
+        W = torch.zeros((E, E), dtype=torch.int32, device=logits.device)
+        idx, gate, c = ops.moe_route_plan(logits, k, R, place, dedup, coselect=W,
+                                          coselect_tokens=w.coselect_tokens, stream=stream)
+    else:
+        idx, gate = ops.moe_route_topk(logits, k, stream=stream)
+        c = ops.moe_send_counts(idx, E, R, place, dedup=dedup, stream=stream)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
     d = f(x, idx, gate, E, R, c["ws"], place, stream=stream)
     out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], stream=stream)
-    W = ops.moe_coselect_counts(idx, E, tokens=w.coselect_tokens, stream=stream)
+    if not fused:
+        W = ops.moe_coselect_counts(idx, E, tokens=w.coselect_tokens, stream=stream)
     return idx, gate, c, d, out, W
 
 
 def _cases():
     for name in WL.ORDER:
         for mode in WL.get(name).dispatch:
-            yield name, mode == "dedup"
+            yield name, mode == "dedup", True
+    yield "deepseek_moe_16b", False, False
+    yield "zyphra_top6_ep32", True, False
 
 
-@pytest.mark.parametrize("name,dedup", list(_cases()))
-def test_workload_end_to_end(oracle_mod, name, dedup):
-    """Full sizes, the launch configuration the benchmark times: logits -> route
-    -> counts -> dispatch -> combine (identity experts) -> co-selection, all on
+@pytest.mark.parametrize("name,dedup,fused", list(_cases()))
+def test_workload_end_to_end(oracle_mod, name, dedup, fused):
+    """Full sizes, the launch configuration the benchmark times (fused: the
+    combined routing call; two cases also with the separate calls): logits ->
+    route, counts, co-selection -> dispatch -> combine (identity experts), all on
     the GPU, against the oracle chain on the same inputs."""
     w = WL.get(name)
-    say(f"[e2e] {name} dedup={dedup} T={w.tokens} H={w.hidden_dim} E={w.n_experts} "
-        f"k={w.top_k} R={w.n_ranks}")
+    say(f"[e2e] {name} dedup={dedup} fused={fused} T={w.tokens} H={w.hidden_dim} "
+        f"E={w.n_experts} k={w.top_k} R={w.n_ranks}")
     inp = WL.make_inputs(w)
-    idx, gate, c, d, out, W = gpu_chain(inp, w, dedup)
+    idx, gate, c, d, out, W = gpu_chain(inp, w, dedup, fused=fused)
     sync()
     idx_o, gate_o = oracle_mod.route_topk(inp["logits"], w.top_k)
     assert (host(idx) == idx_o).all()
@@ -403,12 +414,13 @@ def test_workload_end_to_end(oracle_mod, name, dedup):
 def test_determinism_and_nondefault_stream():
     w = WL.get("qwen3_30b_a3b")
     inp = WL.make_inputs(w)
-    say("[determinism] qwen3_30b_a3b dedup, default stream vs side stream")
+    say("[determinism] qwen3_30b_a3b dedup, separate calls on the default stream vs the "
+        "combined routing call on a side stream")
     a = gpu_chain(inp, w, True)
     sync()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        b = gpu_chain(inp, w, True, stream=s)
+        b = gpu_chain(inp, w, True, stream=s, fused=True)
     s.synchronize()
     n = int(host(a[3]["n_rows"])[0])
     assert (host(a[0]) == host(b[0])).all()
