@@ -13,8 +13,8 @@ hipError_t launch_route_topk(const float*, int64_t, int, int, int, int32_t*, flo
 hipError_t launch_send_counts(const int32_t*, int64_t, int, int, int, const int32_t*, int,
                               int32_t*, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
 hipError_t launch_dispatch(const void*, const int32_t*, const float*, int64_t, int, int, int,
-                           int, const int32_t*, const void*, int, void*, int32_t*, int32_t*,
-                           float*, float*, int32_t*, int32_t*, hipStream_t);
+                           int, const void*, int, void*, int32_t*, int32_t*, float*, float*,
+                           int32_t*, int32_t*, hipStream_t);
 hipError_t launch_combine(const void*, const float*, const int32_t*, int64_t, int, int, int,
                           const int32_t*, void*, hipStream_t);
 hipError_t launch_expand_counts(const int32_t*, int64_t, int, int, int, const int32_t*,
@@ -168,7 +168,7 @@ MOE_API int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const f
   (void)placement;  // the plan in the workspace already encodes it
   return hip_status(moe::launch_dispatch(x, topk_idx, topk_gate, tokens,
                                          hidden_dim * bytes_per_element, n_experts, top_k,
-                                         n_ranks, placement, workspace, 0, send, row_token,
+                                         n_ranks, workspace, 0, send, row_token,
                                          row_expert, nullptr, row_weight, slot_row, nullptr,
                                          as_stream(stream)));
 }
@@ -191,9 +191,10 @@ MOE_API int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx,
   if (tokens > 0 && (!x || !topk_idx || !topk_gate || !send || !row_token || !row_experts ||
                      !row_gates || !row_weight || !slot_row))
     return MOE_EINVAL;
+  (void)placement;  // the plan in the workspace already encodes it
   return hip_status(moe::launch_dispatch(x, topk_idx, topk_gate, tokens,
                                          hidden_dim * bytes_per_element, n_experts, top_k,
-                                         n_ranks, placement, workspace, 1, send, row_token,
+                                         n_ranks, workspace, 1, send, row_token,
                                          row_experts, row_gates, row_weight, slot_row, n_rows,
                                          as_stream(stream)));
 }

@@ -115,8 +115,7 @@ template <int NV, bool NT>
 __global__ void __launch_bounds__(256)
 dispatch_dedup_kernel(const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
                       const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k,
-                      int R, const int32_t* __restrict__ place, int m, int cpr,
-                      const int32_t* __restrict__ gbase, const uint8_t* __restrict__ tcnt,
+                      int cpr, const int32_t* __restrict__ gbase, const uint8_t* __restrict__ tcnt,
                       const uint32_t* __restrict__ lslot, int64_t Bp, int64_t G,
                       const int32_t* __restrict__ header, uint8_t* __restrict__ send,
                       int32_t* __restrict__ row_token, int32_t* __restrict__ row_experts,
@@ -202,7 +201,7 @@ static int dispatch_nv(int row_bytes) {
 template <int NV>
 static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const float* gate,
                                      int64_t T, int row_bytes, int E, int k, int R,
-                                     const int32_t* place, const void* workspace, int dedup,
+                                     const void* workspace, int dedup,
                                      void* send, int32_t* row_token, int32_t* row_e,
                                      float* row_gates, float* row_weight, int32_t* slot_row,
                                      int32_t* n_rows, hipStream_t stream) {
@@ -226,8 +225,8 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
                        row_token, row_e, row_weight, slot_row, nullptr, int64_t(0));
   } else {
     hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT>), dim3(unsigned(blocks)), dim3(256), 0,
-                       stream, static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, R,
-                       place, E / R, cpr, gbase, tcnt, lslot, pl.tiles_pad, pl.groups, header,
+                       stream, static_cast<const uint8_t*>(x), idx, gate, T, row_bytes, E, k, cpr,
+                       gbase, tcnt, lslot, pl.tiles_pad, pl.groups, header,
                        static_cast<uint8_t*>(send), row_token, row_e, row_gates, row_weight,
                        slot_row, n_rows);
   }
@@ -235,21 +234,21 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
 }
 
 hipError_t launch_dispatch(const void* x, const int32_t* idx, const float* gate, int64_t T,
-                           int row_bytes, int E, int k, int R, const int32_t* place,
-                           const void* workspace, int dedup, void* send, int32_t* row_token,
+                           int row_bytes, int E, int k, int R, const void* workspace, int dedup,
+                           void* send, int32_t* row_token,
                            int32_t* row_e, float* row_gates, float* row_weight,
                            int32_t* slot_row, int32_t* n_rows, hipStream_t stream) {
   switch (dispatch_nv(row_bytes)) {
     case 4:
-      return launch_dispatch_nv<4>(x, idx, gate, T, row_bytes, E, k, R, place, workspace, dedup,
+      return launch_dispatch_nv<4>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
                                    send, row_token, row_e, row_gates, row_weight, slot_row,
                                    n_rows, stream);
     case 2:
-      return launch_dispatch_nv<2>(x, idx, gate, T, row_bytes, E, k, R, place, workspace, dedup,
+      return launch_dispatch_nv<2>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
                                    send, row_token, row_e, row_gates, row_weight, slot_row,
                                    n_rows, stream);
     default:
-      return launch_dispatch_nv<1>(x, idx, gate, T, row_bytes, E, k, R, place, workspace, dedup,
+      return launch_dispatch_nv<1>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
                                    send, row_token, row_e, row_gates, row_weight, slot_row,
                                    n_rows, stream);
   }
