@@ -59,6 +59,25 @@ def build(defines=(), out=LIB, verbose=False) -> str:
     return out
 
 
+DEMO_SRC = os.path.join(ROOT, "tests", "abi_demo.c")
+DEMO = os.path.join(ROOT, "tests", "abi_demo")
+
+
+def build_abi_demo(out=DEMO) -> str:
+    """The plain-C user of the C ABI (tests/abi_demo.c), compiled with gcc as
+    C11 against include/moe_route.h and HIP's C runtime API, linked against the
+    in-tree library (found through its rpath)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           f"-I{rocm}/include", f"-I{INCLUDE}", DEMO_SRC, "-o", out, f"-L{PKG}", "-lmoe_route",
+           f"-L{rocm}/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/../combine_top_router_select_amd",
+           f"-Wl,-rpath,{rocm}/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"abi demo build failed:\n{r.stdout}\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     defs = []
     args = sys.argv[1:]
