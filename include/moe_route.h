@@ -73,10 +73,10 @@ extern "C" {
 /* Host.  A static, NUL-terminated description of a status code (never NULL). */
 const char* moe_status_string(int status);
 
-/* Host.  Bytes of workspace that moe_send_counts() fills and the dispatch call
- * of the same (topk_idx, placement, dedup) then reads.  Returns 0 if the
- * arguments are outside the limits above.  The workspace is opaque; it needs
- * no initialisation and 256-byte alignment is enough. */
+/* Host.  Bytes of workspace that moe_send_counts() or moe_route_plan() fills
+ * and the dispatch call of the same (topk_idx, placement, dedup) then reads.
+ * Returns 0 if the arguments are outside the limits above.  The workspace is
+ * opaque; it needs no initialisation and 256-byte alignment is enough. */
 size_t moe_workspace_bytes(int64_t tokens, int n_experts, int top_k, int n_ranks, int dedup);
 
 /* A1 - top-k routing ([EC] "Background"): each token is routed to its k experts
@@ -162,8 +162,9 @@ int moe_route_plan(const float* logits, int64_t tokens, int n_experts, int top_k
 
 /* A4a - dispatch permute, one row per (token, expert) ([EC] "Method 1",
  * conventional dispatch; [DD] "Reading the counts").
- * Must follow moe_send_counts(dedup = 0) on the same stream with the same
- * topk_idx, placement and workspace (the workspace carries the plan).
+ * Must follow moe_send_counts(dedup = 0), or moe_route_plan(dedup = 0), on the
+ * same stream with the same topk_idx, placement and workspace (the workspace
+ * carries the plan).
  *   x            [T][H] elements of bytes_per_element bytes (bf16: 2), read only;
  *                rows are copied bit for bit.  H * bytes_per_element must be a
  *                multiple of 16.
@@ -185,8 +186,9 @@ int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* to
 
 /* A4b - deduplicating dispatch, one row per distinct (token, destination rank)
  * ([EC] "Method 1", deduplicating dispatcher).
- * Must follow moe_send_counts(dedup = 1) on the same stream with the same
- * topk_idx, placement and workspace.  Capacity is N = T*k rows for every
+ * Must follow moe_send_counts(dedup = 1), or moe_route_plan(dedup = 1), on the
+ * same stream with the same topk_idx, placement and workspace.  Capacity is
+ * N = T*k rows for every
  * output so that no host synchronisation is needed; the number of rows written,
  * D, is stored in *n_rows (and equals rank_offsets[R] of the counts call).
  *   send         [capacity N][H] out; rows [0, D) written.  Row order: rank
