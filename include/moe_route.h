@@ -188,9 +188,9 @@ int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* to
  * ([EC] "Method 1", deduplicating dispatcher).
  * Must follow moe_send_counts(dedup = 1), or moe_route_plan(dedup = 1), on the
  * same stream with the same topk_idx, placement and workspace.  Capacity is
- * N = T*k rows for every
- * output so that no host synchronisation is needed; the number of rows written,
- * D, is stored in *n_rows (and equals rank_offsets[R] of the counts call).
+ * N = T*k rows for every output so that no host synchronisation is needed; the
+ * number of rows written, D, is stored in *n_rows (and equals rank_offsets[R]
+ * of the counts call).
  *   send         [capacity N][H] out; rows [0, D) written.  Row order: rank
  *                ascending; inside a rank, token ascending.
  *   row_token    [N] int32 out.
