@@ -15,12 +15,13 @@ the receive side runs between dispatch and combine.  The workload defaults to
 4096 tokens, hidden 2048 bf16, 64 experts, top-6, 16 logical ranks, contiguous
 placement (DeepSeek-MoE-16B-shaped), plain (one row per token-expert) dispatch.
 
-Steps are independent batches.  By default consecutive steps alternate between
-two streams with no waits between them (the way a server overlaps two
-micro-batches), so one batch's latency-bound kernels can run beside the other
-batch's copies; each step's own kernels stay in order on its stream.  The same
-K steps are then timed on the other setting and reported as `other_streams`
-(--streams 1 swaps the two).  --overlap instead forks only the co-selection
+Steps are independent batches.  By default, when a batch's activations are
+under 64 MiB, consecutive steps alternate between two streams with no waits
+between them (the way a server overlaps two micro-batches), so one batch's
+latency-bound kernels can run beside the other batch's copies; each step's own
+kernels stay in order on its stream.  Larger batches run on one stream.  The
+same K steps are then timed on the other setting and reported as
+`other_streams`; --streams n fixes the setting.  --overlap instead forks only the co-selection
 counts onto a second stream inside each step.
 
 The timed steps call the C ABI directly with arguments marshalled once per
@@ -84,12 +85,15 @@ def parse():
     p.add_argument("--shuffle", action="store_true",
                    help="also fit the token-shuffle planner on one batch of correlated "
                         "three-layer routing and plan another, reporting times and locality")
-    p.add_argument("--streams", type=int, default=2, choices=(1, 2, 3, 4),
-                   help="2 (default): alternate the rotated buffer sets, i.e. consecutive "
-                        "independent batches, between two streams so that one batch's "
-                        "latency-bound kernels overlap the other's copies (no cross-stream "
-                        "waits); 1: every step on one stream.  The other setting is timed too "
-                        "and reported as other_streams")
+    p.add_argument("--streams", type=int, default=0, choices=(0, 1, 2, 3, 4),
+                   help="n > 1: alternate the rotated buffer sets, i.e. consecutive "
+                        "independent batches, between n streams so that one batch's "
+                        "latency-bound kernels overlap another's copies (no cross-stream "
+                        "waits); 1: every step on one stream; 0 (default): 2 when a batch's "
+                        "activations are under 64 MiB, else 1 (measured: large batches have "
+                        "nothing latency-bound to hide and their concurrent working sets "
+                        "overflow the Infinity Cache).  The other setting (1, or 2 after 1) is "
+                        "timed too and reported as other_streams")
     p.add_argument("--separate", action="store_true",
                    help="route and count with moe_route_topk + moe_send_counts instead of the "
                         "fused moe_route_plan (one kernel more)")
@@ -510,7 +514,8 @@ def main():
         torch.cuda.synchronize()
 
     raw = raw_other = None
-    n_streams = a.streams if (side is None and not a.step_events and graphs is None) else 1
+    want = a.streams if a.streams else (2 if T * H * bpe < 64 * 2 ** 20 else 1)
+    n_streams = want if (side is None and not a.step_events and graphs is None) else 1
     if graphs is None:
         streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(3)]
 
