@@ -411,6 +411,43 @@ def test_workload_end_to_end(oracle_mod, name, dedup, fused):
 
 # ------------------------------------------------ determinism, streams, edges --
 
+@pytest.mark.parametrize("name", ["deepseek_moe_16b", "qwen3_30b_a3b"])
+def test_two_streams_of_batches(oracle_mod, name):
+    """The benchmark's launch configuration: independent batches alternate
+    between two streams with no waits between them (four batches, two per
+    stream, each on its own buffers and workspace), every call through the
+    combined routing call, dispatch and combine; every batch matches the
+    oracle."""
+    w = WL.get(name)
+    E, k, R = w.n_experts, w.top_k, w.n_ranks
+    say(f"[two streams] {name}: 4 batches")
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    batches = [WL.make_inputs(w, seed=s) for s in (0, 1, 2, 3)]
+    sync()
+    res = []
+    for i, inp in enumerate(batches):
+        st = streams[i % 2]
+        with torch.cuda.stream(st):
+            logits = to_dev(inp["logits"])
+            x = bf16_dev(inp["x_bits"])
+            W = torch.zeros((E, E), dtype=torch.int32, device=logits.device)
+            idx, gate, c = ops.moe_route_plan(logits, k, R, None, False, coselect=W,
+                                              coselect_tokens=w.coselect_tokens, stream=st)
+            d = ops.moe_dispatch_permute(x, idx, gate, E, R, c["ws"], stream=st)
+            out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], stream=st)
+        res.append((idx, gate, c, d, out, W))
+    sync()
+    for inp, (idx, gate, c, d, out, W) in zip(batches, res):
+        idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+        assert (host(idx) == idx_o).all()
+        assert f32_ulp_diff(host(gate), gate_o).max() <= 1
+        o = oracle_mod.dispatch(inp["x_bits"], idx_o, host(gate), E, R)
+        _check_counts(c, o, False)
+        assert (host(d["slot_row"]) == o["slot_row"]).all()
+        assert (bf16_host(d["send"]) == o["send"]).all()
+        assert (bf16_host(out) == inp["x_bits"]).all()
+        assert (host(W) == oracle_mod.coselect(idx_o, E, tokens=w.coselect_tokens)).all()
+
 def test_determinism_and_nondefault_stream():
     w = WL.get("qwen3_30b_a3b")
     inp = WL.make_inputs(w)
