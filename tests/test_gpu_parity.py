@@ -75,6 +75,8 @@ ROUTE_PLAN_CASES = [  # T, E, k, R
     (300, 8, 8, 8), (257, 3, 1, 1), (129, 1, 1, 1), (500, 256, 8, 32), (200, 100, 16, 4),
     (4100, 16, 4, 16), (130, 512, 16, 64), (70, 1024, 3, 8),
     (5000, 256, 8, 16),   # tile bitmaps of 79 tiles: two chunks, atomic adds into W
+    (100, 33, 5, 11),     # scalar logit loads (E % 4 != 0) in the fused kernel
+    (90, 96, 7, 12),      # 16-byte loads with a partial last chunk
 ]
 
 
