@@ -233,6 +233,27 @@ def test_dispatch_parity_huge_plan(oracle_mod, dedup, pl):
     run_dispatch_parity(oracle_mod, inp["x_bits"], idx_o, gate_o, E, R, placement, dedup)
 
 
+@pytest.mark.parametrize("dedup", [False, True])
+def test_route_plan_huge(oracle_mod, dedup):
+    """The combined routing call at 300000 tokens (4688 tiles: the looping scan)
+    against the oracle's ids, counts and co-selection counts, and its plan
+    against the separate calls byte for byte."""
+    T, E, k, R = 300000, 64, 6, 16
+    say(f"[route_plan] huge T={T} E={E} k={k} R={R} dedup={dedup}")
+    inp = WL.make_custom_inputs(T, 16, E, seed=303)
+    logits = to_dev(inp["logits"])
+    W = torch.zeros((E, E), dtype=torch.int32, device=logits.device)
+    idx, gate, c = ops.moe_route_plan(logits, k, R, None, dedup, coselect=W)
+    idx2, _ = ops.moe_route_topk(logits, k)
+    c2 = ops.moe_send_counts(idx2, E, R, None, dedup=dedup)
+    sync()
+    idx_o, _ = oracle_mod.route_topk(inp["logits"], k)
+    assert (host(idx) == idx_o).all()
+    _check_counts(c, oracle_mod.send_counts(idx_o, E, R, None, dedup), dedup)
+    assert (host(W) == oracle_mod.coselect(idx_o, E)).all()
+    assert _plan_equal(c["ws"], c2["ws"], T, E, k, R, dedup)
+
+
 def test_dispatch_empty_ranks(oracle_mod):
     """Tokens that only ever pick experts of ranks 0 and 2: ranks 1 and 3 are
     empty segments."""
