@@ -254,6 +254,54 @@ def test_route_plan_huge(oracle_mod, dedup):
     assert _plan_equal(c["ws"], c2["ws"], T, E, k, R, dedup)
 
 
+def _random_case(i):
+    """Seeded shape draw for the randomized parity sweep (same cases every run)."""
+    rng = np.random.default_rng(1000 + i)
+    R = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 64]))
+    m = int(rng.choice([1, 2, 3, 4, 8]))
+    E = min(R * m, 1024)
+    k = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.integers(1, 3000))
+    H = int(rng.choice([8, 16, 24, 64, 200, 1024, 2056]))
+    dedup = bool(rng.integers(0, 2))
+    pl = str(rng.choice(["contiguous", "random"]))
+    ties = bool(rng.integers(0, 4) == 0)
+    return T, H, E, k, R, dedup, pl, ties
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_shapes(oracle_mod, i):
+    """Forty seeded random shapes (T, H, E, k, R, mode, placement, tied
+    logits) through the combined routing call, dispatch and combine, against
+    the oracle."""
+    T, H, E, k, R, dedup, pl, ties = _random_case(i)
+    say(f"[random {i}] T={T} H={H} E={E} k={k} R={R} dedup={dedup} placement={pl} ties={ties}")
+    inp = WL.make_custom_inputs(T, H, E, seed=i,
+                                logit_values=[-1.0, -0.0, 0.0, 1.0] if ties else None)
+    placement = WL.random_placement(E, R, seed=i) if pl == "random" else None
+    place_dev = to_dev(placement) if placement is not None else None
+    W = torch.zeros((E, E), dtype=torch.int32, device=torch.device("cuda:0"))
+    idx, gate, c = ops.moe_route_plan(to_dev(inp["logits"]), k, R, place_dev, dedup, coselect=W)
+    f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+    d = f(bf16_dev(inp["x_bits"]), idx, gate, E, R, c["ws"], place_dev)
+    out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"])
+    sync()
+    idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+    assert (host(idx) == idx_o).all()
+    assert f32_ulp_diff(host(gate), gate_o).max() <= 1
+    gate_h = host(gate)
+    o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(
+        inp["x_bits"], idx_o, gate_h, E, R, placement)
+    _check_counts(c, o, dedup)
+    n = o["n_rows"]
+    assert (host(d["slot_row"]) == o["slot_row"]).all()
+    assert (bf16_host(d["send"][:n]) == o["send"]).all()
+    assert (host(d["row_weight"][:n]).view(np.uint32) == o["row_weight"].view(np.uint32)).all()
+    ref = oracle_mod.combine(o["send"], o["row_weight"], o["slot_row"])
+    assert bf16_ulp_diff(bf16_host(out), ref).max() <= 1
+    assert (host(W) == oracle_mod.coselect(idx_o, E)).all()
+
+
 def test_dispatch_empty_ranks(oracle_mod):
     """Tokens that only ever pick experts of ranks 0 and 2: ranks 1 and 3 are
     empty segments."""
