@@ -219,3 +219,38 @@ def test_receive_chain_workload(oracle_mod, name):
     xf, of = bf16_to_f64(inp["x_bits"]), bf16_to_f64(got)
     ulp = np.maximum(np.abs(xf), 2.0 ** -126) * 2.0 ** -7
     assert (np.abs(of - xf) <= 2 * ulp).all()
+
+
+def _random_receive_case(i):
+    rng = np.random.default_rng(2000 + i)
+    R = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    m = int(rng.choice([1, 2, 3, 4, 8]))
+    E = R * m
+    k = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.integers(1, 2000))
+    H = int(rng.choice([8, 24, 64, 256, 2056]))
+    pl = bool(rng.integers(0, 2))
+    return T, H, E, k, R, pl
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_receive(oracle_mod, i):
+    """Twenty seeded random shapes through the receive side (garbage past the
+    received rows): expansion bit-exact, gate-weighted reduction of random
+    expert outputs within the bound."""
+    T, H, E, k, R, pl = _random_receive_case(i)
+    placement = WL.random_placement(E, R, seed=i) if pl else None
+    say(f"[receive random {i}] T={T} H={H} E={E} k={k} R={R} random placement={pl}")
+    inp = WL.make_custom_inputs(T, H, E, seed=50 + i)
+    _, _, d, o = received(oracle_mod, inp["x_bits"], inp["logits"], k, E, R, placement)
+    ec, ex, ref = check_expand(oracle_mod, d, o, E, R, placement, k)
+    D, n = o["n_rows"], ref["n_expanded"]
+    C = T * k
+    rng = np.random.default_rng(i)
+    Y = WL.bf16_bits_from_f32(rng.standard_normal((max(n, 1), H)).astype(np.float32))[:n]
+    Yd = torch.zeros((C, H), dtype=torch.bfloat16, device="cuda:0")
+    Yd[:n] = bf16_dev(Y)
+    out = ops.moe_expand_reduce(Yd, ex["exp_gate"], ex["row_slot"], d["n_rows"])
+    rr = oracle_mod.reduce_rows(Y, ref["exp_gate"], ref["row_slot"], D)
+    sync()
+    assert _reduce_bound_ok(bf16_host(out[:D]), rr, Y, ref["exp_gate"], ref["row_slot"][:D], k)
