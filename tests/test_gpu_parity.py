@@ -753,3 +753,39 @@ def test_route_softmax_all_parity(oracle_mod, T, E, k):
     sync()
     assert (host(idx) == idx_o).all()
     assert f32_ulp_diff(host(gate), gate_o).max() <= 1
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_fp8_chain(oracle_mod, i):
+    """Twelve seeded random shapes with fp8 rows: the combined routing call,
+    dispatch of E4M3 bytes (bit for bit) and the decoding combine against the
+    oracle's exact decode and sum."""
+    rng = np.random.default_rng(3000 + i)
+    R = int(rng.choice([1, 2, 4, 8, 16]))
+    E = R * int(rng.choice([1, 2, 4, 8]))
+    k = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.integers(1, 2000))
+    H = int(rng.choice([16, 48, 272, 1024, 4096]))
+    dedup = bool(rng.integers(0, 2))
+    say(f"[fp8 random {i}] T={T} H={H} E={E} k={k} R={R} dedup={dedup}")
+    inp = WL.make_custom_inputs(T, H, E, seed=70 + i)
+    x8 = rng.integers(0, 256, (T, H)).astype(np.uint8)
+    x8[(x8 & 0x7F) == 0x7F] = 0x80                 # no NaN; those become -0
+    idx, gate, c = ops.moe_route_plan(to_dev(inp["logits"]), k, R, None, dedup)
+    f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+    d = f(_fp8_dev(x8), idx, gate, E, R, c["ws"])
+    out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"])
+    sync()
+    idx_o, _ = oracle_mod.route_topk(inp["logits"], k)
+    assert (host(idx) == idx_o).all()
+    o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(x8, idx_o, host(gate), E, R)
+    n = o["n_rows"]
+    assert (host(d["send"][:n].view(torch.uint8)) == o["send"]).all()
+    ref = oracle_mod.combine_fp8(o["send"], o["row_weight"], o["slot_row"])
+    Y = np.array([[oracle_mod.e4m3_to_double(int(b)) for b in row] for row in o["send"]]) \
+        if n * H <= 200000 else None
+    got = bf16_host(out)
+    if Y is not None:
+        assert _bound_ok(got, ref, Y, o["row_weight"], o["slot_row"], k)
+    else:
+        assert bf16_ulp_diff(got, ref).max() <= 1
