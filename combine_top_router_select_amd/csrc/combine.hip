@@ -85,7 +85,7 @@ __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int r
                                          float wr, int lane, uint8_t* __restrict__ dst) {
   constexpr int OS = IN8 ? 2 : 1;  // output bytes per input byte
   u32x4 y[NQ][NV];
-  float wq[NQ];
+  int jq[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     int j = j0;
@@ -93,8 +93,8 @@ __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int r
       j = __ffsll((unsigned long long)um) - 1;
       um &= um - 1;
     }
+    jq[q] = j;
     const int p = bcast(rr, j);
-    wq[q] = bcastf(wr, j);
     const uint8_t* src = rows + int64_t(p) * row_bytes;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -103,6 +103,13 @@ __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int r
       y[q][i] = MOE_COMBINE_NT ? load16_nt(src + off) : load16(src + off);
     }
   }
+  // the weights are broadcast only once every row load is out: reading the
+  // weight register waits for its load, which would hold back the row loads
+  // issued after it
+  __builtin_amdgcn_sched_barrier(0);
+  float wq[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) wq[q] = bcastf(wr, jq[q]);
   float acc[NV][kVals<IN8>];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
