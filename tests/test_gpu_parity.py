@@ -302,6 +302,38 @@ def test_random_shapes(oracle_mod, i):
     assert (host(W) == oracle_mod.coselect(idx_o, E)).all()
 
 
+@pytest.mark.parametrize("T", [2044, 2048, 2049, 4097])
+@pytest.mark.parametrize("dedup", [False, True])
+def test_dispatch_metadata_order_boundary(oracle_mod, T, dedup):
+    """Token counts around the grid size (512 workgroups of four one-chunk
+    tokens) from which each token's metadata is written in the XCD-contiguous
+    order, on grids padded to a multiple of 8 workgroups: 511, 512, 513 and
+    1025 workgroups.  Rows, metadata and slots against the oracle."""
+    H, E, k, R = 64, 64, 6, 16
+    say(f"[metadata order] T={T} dedup={dedup}")
+    inp = WL.make_custom_inputs(T, H, E, seed=T)
+    placement = WL.random_placement(E, R, seed=T)
+    place_dev = to_dev(placement)
+    idx, gate, c = ops.moe_route_plan(to_dev(inp["logits"]), k, R, place_dev, dedup)
+    f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+    d = f(bf16_dev(inp["x_bits"]), idx, gate, E, R, c["ws"], place_dev)
+    sync()
+    idx_h, gate_h = host(idx), host(gate)
+    o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(
+        inp["x_bits"], idx_h, gate_h, E, R, placement)
+    n = o["n_rows"]
+    assert (host(d["slot_row"]) == o["slot_row"]).all()
+    assert (bf16_host(d["send"][:n]) == o["send"]).all()
+    assert (host(d["row_token"][:n]) == o["row_token"]).all()
+    assert (host(d["row_weight"][:n]).view(np.uint32) == o["row_weight"].view(np.uint32)).all()
+    if dedup:
+        assert int(host(d["n_rows"])[0]) == n
+        assert (host(d["row_experts"][:n]) == o["row_experts"]).all()
+        assert (host(d["row_gates"][:n]).view(np.uint32) == o["row_gates"].view(np.uint32)).all()
+    else:
+        assert (host(d["row_expert"][:n]) == o["row_expert"]).all()
+
+
 def test_dispatch_empty_ranks(oracle_mod):
     """Tokens that only ever pick experts of ranks 0 and 2: ranks 1 and 3 are
     empty segments."""
