@@ -134,6 +134,24 @@ __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int r
   }
 }
 
+// Whether an earlier lane of the 16-lane DPP row holds the same value: lane j
+// compares its value with lanes j-1 .. j-(KMAX-1), moved in with row_shr
+// (lanes shifted in from before the row read a value no row index takes).
+// Slots sit in lanes 0 .. k-1 <= KMAX-1 of row 0, so this finds a slot whose
+// row an earlier slot already names, without a readlane per slot.
+template <int S>
+__device__ __forceinline__ int row_shr(int v) {
+  return __builtin_amdgcn_update_dpp(int(0x80000000u), v, 0x110 + S, 0xF, 0xF, false);
+}
+template <int KMAX, int S = 1>
+__device__ __forceinline__ bool repeats_earlier(int v) {
+  if constexpr (S >= KMAX || S > 15) {
+    return false;
+  } else {
+    return (row_shr<S>(v) == v) | repeats_earlier<KMAX, S + 1>(v);
+  }
+}
+
 template <int NV, int KMAX, bool IN8>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
@@ -153,11 +171,7 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
   const int jl = lane < k ? lane : k - 1;
   const int r_raw = slot_row[t * k + jl];
   const int r = lane < k ? r_raw : -1;
-  bool use = r >= 0;
-  for (int i = 0; i < k; ++i) {
-    const int ri = bcast(r, i);
-    if (i < lane && ri == r) use = false;
-  }
+  const bool use = (r >= 0) & !repeats_earlier<KMAX>(r);
   uint64_t um = __ballot(use);
   const int nrows = __popcll(um);
   uint8_t* dst = out + t * int64_t(row_bytes) * OS;
