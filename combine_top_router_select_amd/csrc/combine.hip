@@ -18,7 +18,8 @@
 // E4M3) are decoded with v_cvt_pk_f32_fp8, exact for every byte value.  Row
 // loads are nontemporal: each row is read once, so it should not displace
 // cached data (measured: about 2 us less per 4096-token, top-6, hidden-2048
-// step).
+// step).  So are the output stores of the combine proper with bf16 rows
+// (launch_combine_t gives the cases).
 #include "common.hpp"
 
 #ifndef MOE_COMBINE_NT
@@ -63,14 +64,18 @@ __device__ __forceinline__ void decode16(const u32x4& v, float (&f)[kVals<IN8>])
 }
 
 // bf16 output of the kVals values of one input vector: 16 or 32 bytes at dst.
-template <bool IN8>
+// NTS: nontemporal stores.
+template <bool IN8, bool NTS>
 __device__ __forceinline__ void store_out(uint8_t* dst, const float (&a)[kVals<IN8>]) {
 #pragma unroll
   for (int s = 0; s < kVals<IN8> / 8; ++s) {
     u32x4 o;
 #pragma unroll
     for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(a[8 * s + 2 * h], a[8 * s + 2 * h + 1]);
-    store16(dst + 16 * s, o);
+    if (NTS)
+      store16_nt(dst + 16 * s, o);
+    else
+      store16(dst + 16 * s, o);
   }
 }
 
@@ -79,7 +84,7 @@ __device__ __forceinline__ void store_out(uint8_t* dst, const float (&a)[kVals<I
 // one and are not added), accumulated in fp32 from -0.0 in slot order, and
 // stored as bf16.  Offsets are in input bytes; output offsets are twice that
 // for fp8 input.
-template <int NQ, int NV, bool IN8>
+template <int NQ, int NV, bool IN8, bool NTS>
 __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int row_bytes,
                                          int64_t chunk0, uint64_t um, int j0, int nrows, int rr,
                                          float wr, int lane, uint8_t* __restrict__ dst) {
@@ -130,7 +135,7 @@ __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int r
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
-    if (off < row_bytes) store_out<IN8>(dst + OS * off, acc[i]);
+    if (off < row_bytes) store_out<IN8, NTS>(dst + OS * off, acc[i]);
   }
 }
 
@@ -152,7 +157,7 @@ __device__ __forceinline__ bool repeats_earlier(int v) {
   }
 }
 
-template <int NV, int KMAX, bool IN8>
+template <int NV, int KMAX, bool IN8, bool NTS>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
                const int32_t* __restrict__ slot_row, int64_t T, int row_bytes, int k, int cpr,
@@ -194,17 +199,17 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
   // KMAX rows
   if constexpr (KMAX >= 1) {
     if (nrows <= 1)
-      return sum_rows<1, NV, IN8>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+      return sum_rows<1, NV, IN8, NTS>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
   }
   if constexpr (KMAX >= 2) {
     if (nrows <= 2)
-      return sum_rows<2, NV, IN8>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+      return sum_rows<2, NV, IN8, NTS>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
   }
   if constexpr (KMAX > 4) {
     if (nrows <= 4)
-      return sum_rows<4, NV, IN8>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+      return sum_rows<4, NV, IN8, NTS>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
   }
-  sum_rows<KMAX, NV, IN8>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+  sum_rows<KMAX, NV, IN8, NTS>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
 }
 
 template <int NV, int KMAX, bool IN8>
@@ -214,9 +219,22 @@ static hipError_t launch_combine_t(const void* rows, const float* w, const int32
   const int chunk = NV * kWave * 16;
   const int cpr = (row_bytes + chunk - 1) / chunk;
   const int64_t blocks = (T * cpr + 3) / 4;
-  hipLaunchKernelGGL((combine_kernel<NV, KMAX, IN8>), dim3(unsigned(blocks)), dim3(256), 0,
-                     stream, static_cast<const uint8_t*>(rows), w, slot_row, T, row_bytes, k, cpr,
-                     n_valid, static_cast<uint8_t*>(out));
+  const uint8_t* rb = static_cast<const uint8_t*>(rows);
+  uint8_t* ob = static_cast<uint8_t*>(out);
+  // Nontemporal output stores for the combine proper with bf16 rows: nothing in
+  // the step reads its output again, and keeping it out of the caches leaves
+  // the Infinity Cache to the rows the next batch's kernels read (a 4096-token,
+  // top-6, hidden-2048 step 42.0 -> 40.6 us).  Not for the receive-side
+  // reduction (n_valid set), whose rows the combine reads next (16384-token
+  // top-2 receive step 271 -> 282 us with them), nor for fp8 rows, whose
+  // 32-byte outputs per lane go out as two half-line stores (combine
+  // 13.5 -> 14.7 us with them).
+  if (!IN8 && n_valid == nullptr)
+    hipLaunchKernelGGL((combine_kernel<NV, KMAX, IN8, !IN8>), dim3(unsigned(blocks)), dim3(256),
+                       0, stream, rb, w, slot_row, T, row_bytes, k, cpr, n_valid, ob);
+  else
+    hipLaunchKernelGGL((combine_kernel<NV, KMAX, IN8, false>), dim3(unsigned(blocks)), dim3(256),
+                       0, stream, rb, w, slot_row, T, row_bytes, k, cpr, n_valid, ob);
   return hipGetLastError();
 }
 
