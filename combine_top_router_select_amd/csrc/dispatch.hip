@@ -23,20 +23,21 @@ namespace moe {
 
 // Loads are issued unconditionally from addresses clamped into the row, so a
 // wave's loads go out back to back (a load under a lane-divergent branch is
-// followed by a wait for it); only the stores are predicated.  NTL: the loads
-// are nontemporal (the receive-side expansion: its received rows are read
-// once, and keeping them out of the caches leaves the Infinity Cache to the
-// expanded rows the next kernel reads - 287 -> 270 us per 16384-token, top-2,
-// 8-rank receive step; in the send-side dispatch the same loads gained 1.5% on
-// two streams and lost 2.7% on one, so it keeps ordinary loads).
-template <int NV, bool NTL>
+// followed by a wait for it); only the stores are predicated.  They are
+// nontemporal: a call reads each row once, and keeping those reads out of the
+// caches leaves the Infinity Cache to the rows just written, which the combine
+// (or, on the receive side, the reduction) reads next.  Whole steps 1-6%
+// faster (16384-token top-2 receive step 287 -> 270 us, 4096-token top-8 step
+// at 256 experts 53.1 -> 51.8 us), though a 4096-token top-6 dispatch timed
+// alone, back to back, is 1.6% slower.
+template <int NV>
 __device__ __forceinline__ void load_chunk(u32x4 (&v)[NV], const uint8_t* row, int64_t chunk0,
                                            int row_bytes, int lane) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
     off = off < row_bytes ? off : row_bytes - 16;
-    v[i] = NTL ? load16_nt(row + off) : load16(row + off);
+    v[i] = load16_nt(row + off);
   }
 }
 
@@ -140,7 +141,7 @@ dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
   const uint32_t code_m = META ? lslot[tml * k + jl] : code;
   const float g_m = gate[tml * k + jl];
   u32x4 v[NV];
-  load_chunk<NV, PAD>(v, x + tl * row_bytes, chunk0, row_bytes, lane);
+  load_chunk<NV>(v, x + tl * row_bytes, chunk0, row_bytes, lane);
   issue_fence();
   const bool has = !PAD || code != kNoSlot;
   const int e = has ? int(code >> 8) : 0;
@@ -203,7 +204,7 @@ dispatch_dedup_kernel(const uint8_t* x, const int32_t* __restrict__ idx,
   const int e_m = clampi(idx[tml * k + jl], 0, E - 1);
   const float g_m = gate[tml * k + jl];
   u32x4 v[NV];
-  load_chunk<NV, false>(v, x + tl * row_bytes, chunk0, row_bytes, lane);
+  load_chunk<NV>(v, x + tl * row_bytes, chunk0, row_bytes, lane);
   issue_fence();
   const int r_own = int(code >> 8);
   const int pos = tile_first_row(gbase, tcnt, Bp, G, E + r_own, r_own, tl / kTile) +
