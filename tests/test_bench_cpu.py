@@ -1,0 +1,85 @@
+"""Host-side checks of bench.py that need no GPU: the one-GPU guard, the
+argument checks that run before any device work, and the lookup of counter
+traffic in the committed rocprofv3 summaries (keyed on the kernel's sources)."""
+import hashlib
+import importlib.util
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench_module():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=300, cwd=ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _run("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""  # no JSON line
+
+
+def test_receive_without_dedup_is_refused():
+    r = _run("--receive")
+    assert r.returncode == 2
+    assert "--receive needs --dedup" in r.stderr
+
+
+def _digest(bench, kernel, pkg):
+    h = hashlib.sha256()
+    for f in (bench.KERNEL_SOURCES[kernel], "csrc/common.hpp", "build.py"):
+        with open(os.path.join(pkg, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def test_counter_traffic_follows_the_sources(tmp_path, monkeypatch):
+    """A traffic line counts only while the SHA-256 of the kernel's sources
+    matches the one recorded with it; other workloads and modes are not
+    confused with it."""
+    bench = _bench_module()
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    kernel = "moe_dispatch_permute"
+    good = _digest(bench, kernel, bench.PKG)
+    (prof / "hbm_traffic_x.md").write_text(
+        "# summary\n\n```\n"
+        f"traffic kernel={kernel} workload=wl_a dispatch=nondedup sources_sha256={good} "
+        "fetch_kib=1.0 fetch_factor=2.0 write_kib=1.0 write_factor=1.0 bytes=123456\n"
+        f"traffic kernel={kernel} workload=wl_b dispatch=nondedup sources_sha256=0000000000000000 "
+        "fetch_kib=1.0 fetch_factor=2.0 write_kib=1.0 write_factor=1.0 bytes=654321\n"
+        "```\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.counter_traffic(kernel, "wl_a", "nondedup") == 123456
+    assert bench.counter_traffic(kernel, "wl_b", "nondedup") is None   # stale sources
+    assert bench.counter_traffic(kernel, "wl_a", "dedup") is None      # other mode
+    assert bench.counter_traffic(kernel, "wl_c", "nondedup") is None   # no line
+
+
+@pytest.mark.parametrize("path", sorted(
+    os.path.join(ROOT, "profiles", f) for f in os.listdir(os.path.join(ROOT, "profiles"))
+    if f.startswith("hbm_traffic_")))
+def test_committed_traffic_lines_are_well_formed(path):
+    bench = _bench_module()
+    lines = [ln for ln in open(path) if ln.startswith("traffic ")]
+    assert lines, f"{path} has no traffic line"
+    for ln in lines:
+        kv = dict(t.split("=", 1) for t in ln.split()[1:])
+        assert kv["kernel"] in bench.KERNEL_SOURCES
+        assert len(kv["sources_sha256"]) == 16
+        fetch = float(kv["fetch_kib"]) * float(kv["fetch_factor"]) * 1024
+        write = float(kv["write_kib"]) * float(kv["write_factor"]) * 1024
+        # the factors are printed to 4 decimals, the bytes at full precision
+        assert abs(int(kv["bytes"]) - (fetch + write)) <= 1e-4 * (fetch + write)
