@@ -12,14 +12,14 @@
 // and the row weight; a slot whose row already appeared in an earlier slot is
 // dropped (dedup rows serve several slots), negative rows are skipped.  The
 // wave then issues the loads of every used row's chunk before any arithmetic
-// (up to KMAX rows x NV 16-byte vectors in flight per lane), accumulates in fp32
-// with fused multiply-adds in slot order starting from -0.0, and converts to
-// bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).  fp8 rows (OCP
-// E4M3) are decoded with v_cvt_pk_f32_fp8, exact for every byte value.  Row
-// loads are nontemporal: each row is read once, so it should not displace
-// cached data (measured: about 2 us less per 4096-token, top-6, hidden-2048
-// step).  So are the output stores of the combine proper with bf16 rows
-// (launch_combine_t gives the cases).
+// (up to KMAX rows x NV vectors of 8 values in flight per lane: 16 bytes of
+// bf16 or 8 bytes of fp8), accumulates in fp32 with fused multiply-adds in slot
+// order starting from -0.0, and converts to bf16 with round-to-nearest-even
+// (v_cvt_pk_bf16_f32 on gfx950).  fp8 rows (OCP E4M3) are decoded with
+// v_cvt_pk_f32_fp8, exact for every byte value.  Row loads are nontemporal:
+// each row is read once, so it should not displace cached data (measured:
+// about 2 us less per 4096-token, top-6, hidden-2048 step).  So are the output
+// stores of the combine proper (launch_combine_t gives the cases).
 #include "common.hpp"
 
 #ifndef MOE_COMBINE_NT
@@ -41,14 +41,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
-// Values in one 16-byte input vector: 8 bf16, or 16 fp8 (IN8).
+// One input vector per lane holds 8 values: 16 bytes of bf16, or 8 bytes of
+// fp8 (IN8), so that its 8 bf16 outputs are always one 16-byte store and a
+// wave instruction writes 1 KiB of contiguous output.
+constexpr int kVals = 8;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <bool IN8>
-constexpr int kVals = IN8 ? 16 : 8;
+struct InVec {
+  typedef u32x4 type;
+  static constexpr int kBytes = 16;
+};
+template <>
+struct InVec<true> {
+  typedef u32x2 type;
+  static constexpr int kBytes = 8;
+};
+
+template <bool IN8, bool NT>
+__device__ __forceinline__ typename InVec<IN8>::type load_in(const uint8_t* p) {
+  typedef typename InVec<IN8>::type V;
+  const V* q = reinterpret_cast<const V*>(p);
+  return NT ? __builtin_nontemporal_load(q) : *q;
+}
 
 template <bool IN8>
-__device__ __forceinline__ void decode16(const u32x4& v, float (&f)[kVals<IN8>]) {
+__device__ __forceinline__ void decode(const typename InVec<IN8>::type& v, float (&f)[kVals]) {
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
+  for (int h = 0; h < InVec<IN8>::kBytes / 4; ++h) {
     if constexpr (IN8) {
       const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(v[h]), false);  // bytes 0, 1
       const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(v[h]), true);   // bytes 2, 3
@@ -63,20 +82,17 @@ __device__ __forceinline__ void decode16(const u32x4& v, float (&f)[kVals<IN8>])
   }
 }
 
-// bf16 output of the kVals values of one input vector: 16 or 32 bytes at dst.
+// bf16 output of the kVals values of one input vector: 16 bytes at dst.
 // NTS: nontemporal stores.
-template <bool IN8, bool NTS>
-__device__ __forceinline__ void store_out(uint8_t* dst, const float (&a)[kVals<IN8>]) {
+template <bool NTS>
+__device__ __forceinline__ void store_out(uint8_t* dst, const float (&a)[kVals]) {
+  u32x4 o;
 #pragma unroll
-  for (int s = 0; s < kVals<IN8> / 8; ++s) {
-    u32x4 o;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(a[8 * s + 2 * h], a[8 * s + 2 * h + 1]);
-    if (NTS)
-      store16_nt(dst + 16 * s, o);
-    else
-      store16(dst + 16 * s, o);
-  }
+  for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(a[2 * h], a[2 * h + 1]);
+  if (NTS)
+    store16_nt(dst, o);
+  else
+    store16(dst, o);
 }
 
 // The weighted sum of a token's rows for one chunk: NQ >= nrows rows are
@@ -89,7 +105,8 @@ __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int r
                                          int64_t chunk0, uint64_t um, int j0, int nrows, int rr,
                                          float wr, int lane, uint8_t* __restrict__ dst) {
   constexpr int OS = IN8 ? 2 : 1;  // output bytes per input byte
-  u32x4 y[NQ][NV];
+  constexpr int IB = InVec<IN8>::kBytes;
+  typename InVec<IN8>::type y[NQ][NV];
   int jq[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -103,9 +120,9 @@ __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int r
     const uint8_t* src = rows + int64_t(p) * row_bytes;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
-      off = off < row_bytes ? off : row_bytes - 16;
-      y[q][i] = MOE_COMBINE_NT ? load16_nt(src + off) : load16(src + off);
+      int64_t off = chunk0 + int64_t(i * kWave + lane) * IB;
+      off = off < row_bytes ? off : row_bytes - IB;
+      y[q][i] = load_in<IN8, MOE_COMBINE_NT != 0>(src + off);
     }
   }
   // the weights are broadcast only once every row load is out: reading the
@@ -115,27 +132,27 @@ __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int r
   float wq[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) wq[q] = bcastf(wr, jq[q]);
-  float acc[NV][kVals<IN8>];
+  float acc[NV][kVals];
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
-    for (int h = 0; h < kVals<IN8>; ++h) acc[i][h] = -0.0f;
+    for (int h = 0; h < kVals; ++h) acc[i][h] = -0.0f;
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     if (q < nrows) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        float f[kVals<IN8>];
-        decode16<IN8>(y[q][i], f);
+        float f[kVals];
+        decode<IN8>(y[q][i], f);
 #pragma unroll
-        for (int h = 0; h < kVals<IN8>; ++h) acc[i][h] = __builtin_fmaf(wq[q], f[h], acc[i][h]);
+        for (int h = 0; h < kVals; ++h) acc[i][h] = __builtin_fmaf(wq[q], f[h], acc[i][h]);
       }
     }
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
-    if (off < row_bytes) store_out<IN8, NTS>(dst + OS * off, acc[i]);
+    const int64_t off = chunk0 + int64_t(i * kWave + lane) * IB;
+    if (off < row_bytes) store_out<NTS>(dst + OS * off, acc[i]);
   }
 }
 
@@ -169,7 +186,8 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
   const int c = int(wid - t * cpr);
   if (t >= T) return;  // whole wave
   if (n_valid && t >= *n_valid) return;  // whole wave: only the first *n_valid outputs
-  const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
+  constexpr int IB = InVec<IN8>::kBytes;
+  const int64_t chunk0 = int64_t(c) * (NV * kWave * IB);
   // All loads are unconditional from clamped, in-bounds addresses (a load under
   // a branch is followed by a wait for it); only arithmetic and stores are
   // predicated.
@@ -184,10 +202,8 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
     const u32x4 nz = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int64_t off = chunk0 + int64_t(i * kWave + lane) * 16;
-      if (off < row_bytes)
-#pragma unroll
-        for (int s = 0; s < OS; ++s) store16(dst + OS * off + 16 * s, nz);
+      const int64_t off = chunk0 + int64_t(i * kWave + lane) * IB;
+      if (off < row_bytes) store16(dst + OS * off, nz);
     }
     return;
   }
@@ -216,21 +232,19 @@ template <int NV, int KMAX, bool IN8>
 static hipError_t launch_combine_t(const void* rows, const float* w, const int32_t* slot_row,
                                    int64_t T, int row_bytes, int k, const int32_t* n_valid,
                                    void* out, hipStream_t stream) {
-  const int chunk = NV * kWave * 16;
+  const int chunk = NV * kWave * InVec<IN8>::kBytes;
   const int cpr = (row_bytes + chunk - 1) / chunk;
   const int64_t blocks = (T * cpr + 3) / 4;
   const uint8_t* rb = static_cast<const uint8_t*>(rows);
   uint8_t* ob = static_cast<uint8_t*>(out);
-  // Nontemporal output stores for the combine proper with bf16 rows: nothing in
-  // the step reads its output again, and keeping it out of the caches leaves
-  // the Infinity Cache to the rows the next batch's kernels read (a 4096-token,
+  // Nontemporal output stores for the combine proper: nothing in the step
+  // reads its output again, and keeping it out of the caches leaves the
+  // Infinity Cache to the rows the next batch's kernels read (a 4096-token,
   // top-6, hidden-2048 step 42.0 -> 40.6 us).  Not for the receive-side
   // reduction (n_valid set), whose rows the combine reads next (16384-token
-  // top-2 receive step 271 -> 282 us with them), nor for fp8 rows, whose
-  // 32-byte outputs per lane go out as two half-line stores (combine
-  // 13.5 -> 14.7 us with them).
-  if (!IN8 && n_valid == nullptr)
-    hipLaunchKernelGGL((combine_kernel<NV, KMAX, IN8, !IN8>), dim3(unsigned(blocks)), dim3(256),
+  // top-2 receive step 271 -> 282 us with them).
+  if (n_valid == nullptr)
+    hipLaunchKernelGGL((combine_kernel<NV, KMAX, IN8, true>), dim3(unsigned(blocks)), dim3(256),
                        0, stream, rb, w, slot_row, T, row_bytes, k, cpr, n_valid, ob);
   else
     hipLaunchKernelGGL((combine_kernel<NV, KMAX, IN8, false>), dim3(unsigned(blocks)), dim3(256),
@@ -242,10 +256,9 @@ template <int KMAX, bool IN8>
 static hipError_t launch_combine_k(const void* rows, const float* w, const int32_t* slot_row,
                                    int64_t T, int row_bytes, int k, const int32_t* n_valid,
                                    void* out, hipStream_t stream) {
-  // keep KMAX * NV <= MOE_COMBINE_VECS input vectors in flight per lane, and
-  // the fp8 accumulators (16 per vector) to two vectors
-  const int vr = row_bytes / 16;
-  constexpr int NVCAP = IN8 ? 2 : 4;
+  // keep KMAX * NV <= MOE_COMBINE_VECS input vectors in flight per lane
+  const int vr = row_bytes / InVec<IN8>::kBytes;
+  constexpr int NVCAP = 4;
   constexpr int NVB = MOE_COMBINE_VECS / KMAX > 0 ? MOE_COMBINE_VECS / KMAX : 1;
   constexpr int NVMAX = NVB < NVCAP ? NVB : NVCAP;
   if (NVMAX >= 4 && vr >= 4 * kWave)
