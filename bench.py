@@ -16,7 +16,7 @@ the receive side runs between dispatch and combine.  The workload defaults to
 placement (DeepSeek-MoE-16B-shaped), plain (one row per token-expert) dispatch.
 
 Steps are independent batches.  By default, when a batch's activations are
-under 64 MiB, consecutive steps alternate between two streams with no waits
+at most 64 MiB, consecutive steps alternate between two streams with no waits
 between them (the way a server overlaps two micro-batches), so one batch's
 latency-bound kernels can run beside the other batch's copies; each step's own
 kernels stay in order on its stream.  Larger batches run on one stream.  The
@@ -90,7 +90,7 @@ def parse():
                         "independent batches, between n streams so that one batch's "
                         "latency-bound kernels overlap another's copies (no cross-stream "
                         "waits); 1: every step on one stream; 0 (default): 2 when a batch's "
-                        "activations are under 64 MiB, else 1 (measured: large batches have "
+                        "activations are at most 64 MiB, else 1 (measured: large batches have "
                         "nothing latency-bound to hide and their concurrent working sets "
                         "overflow the Infinity Cache).  The other setting (1, or 2 after 1) is "
                         "timed too and reported as other_streams")
@@ -514,7 +514,7 @@ def main():
         torch.cuda.synchronize()
 
     raw = raw_other = None
-    want = a.streams if a.streams else (2 if T * H * bpe < 64 * 2 ** 20 else 1)
+    want = a.streams if a.streams else (2 if T * H * bpe <= 64 * 2 ** 20 else 1)
     n_streams = want if (side is None and not a.step_events and graphs is None) else 1
     if graphs is None:
         streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(3)]
