@@ -703,7 +703,7 @@ def _bound_ok(got, ref, Y_f64, w, slot, k):
 
 
 @pytest.mark.parametrize("dedup", [False, True])
-@pytest.mark.parametrize("H", [1024, 2048, 4096, 272])
+@pytest.mark.parametrize("H", [1024, 2048, 4096, 272, 2064, 16])
 def test_combine_fp8_rows(oracle_mod, dedup, H):
     """fp8 E4M3 rows (random bytes, no NaN, some -0) into bf16, for gate, NULL
     and signed weights, against the oracle's exact decode and sum."""
