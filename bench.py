@@ -258,6 +258,39 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True):
         ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W)
 
 
+def algorithmic_bytes(T, H, E, k, bpe, n_rows, dedup, n_exp=None):
+    """Bytes the method must move (each input read once, each output written
+    once) for one step of T tokens, hidden H, E experts, top-k, rows of bpe
+    bytes per element, n_rows rows sent (T*k, or D for dedup) and, on the
+    receive side, n_exp expanded rows (None: no receive side).
+      dispatch  read x once, write each sent row once
+      combine   the send-side combine: read each sent row once, write out once
+                (bf16)
+      metadata  per sent row its token, expert(s), gate(s) and weight; per
+                token-slot its row
+      route     logits in, ids and gates out
+      expand    read each received row once, write each expanded copy
+      reduce    read each expert output once, write one bf16 row per received
+                row
+      job       everything a step moves; with a receive side the step's combine
+                reads the reduced bf16 rows instead of the sent rows"""
+    row_bytes = H * bpe
+    out_bytes = H * 2
+    res = {"dispatch": row_bytes * (T + n_rows),
+           "combine": row_bytes * n_rows + out_bytes * T,
+           "metadata": n_rows * (12 if not dedup else 8 + 8 * k) + T * k * 4,
+           "route": T * E * 4 + T * k * 8}
+    if n_exp is None:
+        res["job"] = res["dispatch"] + res["combine"] + res["metadata"] + res["route"]
+        return res
+    res["expand"] = row_bytes * (n_rows + n_exp)
+    res["reduce"] = row_bytes * n_exp + out_bytes * n_rows
+    step_combine = out_bytes * n_rows + out_bytes * T
+    res["job"] = (res["dispatch"] + step_combine + res["metadata"] + res["route"] +
+                  res["expand"] + res["reduce"])
+    return res
+
+
 def counter_traffic(kernel, workload, mode):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summaries (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy
@@ -644,24 +677,19 @@ def main():
     # rows actually written (N, or D for dedup)
     b = sets[0]
     n_rows = int(b.cnt["rank_offsets"][R].item())
-    row_bytes = H * bpe                     # rows of x, send and expanded
-    out_bytes = H * 2                       # bf16 outputs of combine and reduce
-    disp_bytes = row_bytes * (T + n_rows)   # read x once, write each row once
-    comb_bytes = row_bytes * n_rows + out_bytes * T  # read each row once, write out once
-    meta_bytes = n_rows * (12 if not dedup else 8 + 8 * k) + T * k * 4
-    route_bytes = T * E * 4 + T * k * 8        # logits in, ids and gates out
+    n_exp = int(b.ecnt["rank_offsets"][R].item()) if receive else None
+    ab = algorithmic_bytes(T, H, E, k, bpe, n_rows, dedup, n_exp)
+    disp_bytes, comb_bytes = ab["dispatch"], ab["combine"]
+    meta_bytes = ab["metadata"]
     dom = ("moe_dispatch_permute" + ("_dedup" if dedup else ""), t_disp, disp_bytes)
     if t_comb > t_disp:
         dom = ("moe_combine", t_comb, comb_bytes)
     achieved = dom[2] / dom[1] / 1e9
     dc_gbps = (disp_bytes + comb_bytes) / (t_disp + t_comb) / 1e9
     recv = None
-    job_bytes = disp_bytes + comb_bytes + meta_bytes + route_bytes
+    job_bytes = ab["job"]
     if receive:
-        n_exp = int(b.ecnt["rank_offsets"][R].item())
-        exp_bytes = row_bytes * (n_rows + n_exp)  # read each received row once, write each copy
-        red_bytes = row_bytes * n_exp + out_bytes * n_rows  # read each output once, write each row
-        job_bytes += exp_bytes + red_bytes
+        exp_bytes, red_bytes = ab["expand"], ab["reduce"]
         recv = {"expanded_rows": n_exp,
                 "expand_us": round(t_exp * 1e6, 2), "reduce_us": round(t_red * 1e6, 2),
                 "expand_GBps": round(exp_bytes / t_exp / 1e9, 1),

@@ -83,3 +83,35 @@ def test_committed_traffic_lines_are_well_formed(path):
         write = float(kv["write_kib"]) * float(kv["write_factor"]) * 1024
         # the factors are printed to 4 decimals, the bytes at full precision
         assert abs(int(kv["bytes"]) - (fetch + write)) <= 1e-4 * (fetch + write)
+
+
+def test_algorithmic_bytes_c2():
+    """The 4096-token, top-6 of 64 experts, hidden-2048 workload: 4096-byte rows,
+    24576 sent rows - the per-launch figures the roofline divides by."""
+    bench = _bench_module()
+    ab = bench.algorithmic_bytes(4096, 2048, 64, 6, 2, 24576, False)
+    assert ab["dispatch"] == 4096 * (4096 + 24576) == 117_440_512
+    assert ab["combine"] == 4096 * 24576 + 4096 * 4096 == 117_440_512
+    assert ab["metadata"] == 24576 * 12 + 4096 * 6 * 4 == 393_216
+    assert ab["route"] == 4096 * 64 * 4 + 4096 * 6 * 8 == 1_245_184
+    assert ab["job"] == ab["dispatch"] + ab["combine"] + ab["metadata"] + ab["route"]
+    assert "expand" not in ab
+
+
+def test_algorithmic_bytes_receive_side():
+    """Dedup with the receive side: 21744 received rows expanded into 24576.
+    With fp8 rows the step's combine reads the reduced rows, which are bf16."""
+    bench = _bench_module()
+    ab = bench.algorithmic_bytes(4096, 2048, 64, 6, 2, 21744, True, 24576)
+    assert ab["expand"] == ab["reduce"] == 4096 * (21744 + 24576) == 189_726_720
+    assert ab["metadata"] == 21744 * (8 + 8 * 6) + 4096 * 6 * 4
+    assert ab["job"] == (ab["dispatch"] + ab["combine"] + ab["metadata"] + ab["route"] +
+                         ab["expand"] + ab["reduce"])  # bf16: reduced rows = sent rows in size
+    f8 = bench.algorithmic_bytes(4096, 2048, 64, 6, 1, 21744, True, 24576)
+    assert f8["dispatch"] == 2048 * (4096 + 21744)
+    assert f8["combine"] == 2048 * 21744 + 4096 * 4096          # the send-side combine kernel
+    assert f8["expand"] == 2048 * (21744 + 24576)
+    assert f8["reduce"] == 2048 * 24576 + 4096 * 21744
+    step_combine = 4096 * 21744 + 4096 * 4096                   # reads the bf16 reduced rows
+    assert f8["job"] == (f8["dispatch"] + step_combine + f8["metadata"] + f8["route"] +
+                         f8["expand"] + f8["reduce"])
