@@ -269,9 +269,9 @@ def _random_case(i):
     return T, H, E, k, R, dedup, pl, ties
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(100))
 def test_random_shapes(oracle_mod, i):
-    """Forty seeded random shapes (T, H, E, k, R, mode, placement, tied
+    """A hundred seeded random shapes (T, H, E, k, R, mode, placement, tied
     logits) through the combined routing call, dispatch and combine, against
     the oracle."""
     T, H, E, k, R, dedup, pl, ties = _random_case(i)
@@ -787,9 +787,9 @@ def test_route_softmax_all_parity(oracle_mod, T, E, k):
     assert f32_ulp_diff(host(gate), gate_o).max() <= 1
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(32))
 def test_random_fp8_chain(oracle_mod, i):
-    """Twelve seeded random shapes with fp8 rows: the combined routing call,
+    """Thirty-two seeded random shapes with fp8 rows: the combined routing call,
     dispatch of E4M3 bytes (bit for bit) and the decoding combine against the
     oracle's exact decode and sum."""
     rng = np.random.default_rng(3000 + i)

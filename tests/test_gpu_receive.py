@@ -233,9 +233,9 @@ def _random_receive_case(i):
     return T, H, E, k, R, pl
 
 
-@pytest.mark.parametrize("i", range(20))
+@pytest.mark.parametrize("i", range(50))
 def test_random_receive(oracle_mod, i):
-    """Twenty seeded random shapes through the receive side (garbage past the
+    """Fifty seeded random shapes through the receive side (garbage past the
     received rows): expansion bit-exact, gate-weighted reduction of random
     expert outputs within the bound."""
     T, H, E, k, R, pl = _random_receive_case(i)
