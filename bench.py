@@ -1,7 +1,7 @@
 """Benchmark of the per-GPU MoE dispatch/combine hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
-                    [--receive] [--fp8] [--search] [--shuffle] [--streams {1,2}]
+                    [--receive] [--fp8] [--search] [--shuffle] [--streams {0,1,2,3,4}]
                     [--separate] [--graph] [--overlap] [--step-events]
                     [--no-cpu-baseline] [--cpu-seconds S] [--footprint-gib G]
                     [--calib-copy]
