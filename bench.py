@@ -291,11 +291,12 @@ def algorithmic_bytes(T, H, E, k, bpe, n_rows, dedup, n_exp=None):
     return res
 
 
-def counter_traffic(kernel, workload, mode):
+def counter_traffic(kernel, workload, mode, dtype="bf16"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summaries (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy
-    calibration), or None when there is none for this workload or the kernel's
-    sources have changed since the counters were taken."""
+    calibration), or None when there is none for this workload, dispatch mode
+    and row type (a line without dtype= is bf16) or the kernel's sources have
+    changed since the counters were taken."""
     import glob
     import hashlib
     h = hashlib.sha256()
@@ -309,8 +310,8 @@ def counter_traffic(kernel, workload, mode):
                 if not line.startswith("traffic "):
                     continue
                 kv = dict(t.split("=", 1) for t in line.split()[1:])
-                if (kv.get("kernel"), kv.get("workload"), kv.get("dispatch")) == (kernel, workload,
-                                                                                   mode):
+                if (kv.get("kernel"), kv.get("workload"), kv.get("dispatch"),
+                        kv.get("dtype", "bf16")) == (kernel, workload, mode, dtype):
                     return int(kv["bytes"]) if kv.get("sources_sha256") == digest else None
     return None
 
@@ -720,8 +721,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": (counter_traffic(dom[0], w.name, "dedup" if dedup else "nondedup")
-                                 if not fp8 else None),
+                     "traffic": counter_traffic(dom[0], w.name, "dedup" if dedup else "nondedup",
+                                                "fp8" if fp8 else "bf16"),
                      "algorithmic_bytes": dom[2]},
         "dispatch_us": round(t_disp * 1e6, 2),
         "in_step_event_us": in_step or None,

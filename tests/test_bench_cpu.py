@@ -61,8 +61,15 @@ def test_counter_traffic_follows_the_sources(tmp_path, monkeypatch):
         f"traffic kernel={kernel} workload=wl_b dispatch=nondedup sources_sha256=0000000000000000 "
         "fetch_kib=1.0 fetch_factor=2.0 write_kib=1.0 write_factor=1.0 bytes=654321\n"
         "```\n")
+    # a second file: fp8 rows of the same workload
+    (prof / "hbm_traffic_y.md").write_text(
+        f"traffic kernel={kernel} workload=wl_a dispatch=nondedup dtype=fp8 sources_sha256={good} "
+        "fetch_kib=1.0 fetch_factor=2.0 write_kib=1.0 write_factor=1.0 bytes=777\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.counter_traffic(kernel, "wl_a", "nondedup") == 123456
+    assert bench.counter_traffic(kernel, "wl_a", "nondedup", "bf16") == 123456
+    assert bench.counter_traffic(kernel, "wl_a", "nondedup", "fp8") == 777
+    assert bench.counter_traffic(kernel, "wl_b", "nondedup", "fp8") is None
     assert bench.counter_traffic(kernel, "wl_b", "nondedup") is None   # stale sources
     assert bench.counter_traffic(kernel, "wl_a", "dedup") is None      # other mode
     assert bench.counter_traffic(kernel, "wl_c", "nondedup") is None   # no line
@@ -78,6 +85,7 @@ def test_committed_traffic_lines_are_well_formed(path):
     for ln in lines:
         kv = dict(t.split("=", 1) for t in ln.split()[1:])
         assert kv["kernel"] in bench.KERNEL_SOURCES
+        assert kv.get("dtype", "bf16") in ("bf16", "fp8")
         assert len(kv["sources_sha256"]) == 16
         fetch = float(kv["fetch_kib"]) * float(kv["fetch_factor"]) * 1024
         write = float(kv["write_kib"]) * float(kv["write_factor"]) * 1024
