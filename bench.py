@@ -242,11 +242,11 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True):
     if not fused:
         c = ops.moe_send_counts(b.idx, E, R, b.place, dedup, ws=b.ws, out=b.cnt)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-    d = f(b.x, b.idx, b.gate, E, R, c["ws"], b.place, out=b.disp)
+    d = f(b.x, b.idx, b.gate, E, R, c["ws"], out=b.disp)
     if receive:
         ops.moe_expand_counts(d["row_experts"], d["n_rows"], E, R, b.place, ws=b.ews, out=b.ecnt)
-        ex = ops.moe_expand_permute(d["send"], d["row_experts"], d["row_gates"], d["n_rows"], E,
-                                    R, b.ews, out=b.exp)
+        ex = ops.moe_expand_permute(d["send"], d["row_gates"], d["n_rows"], E, R, b.ews,
+                                    out=b.exp)
         red = ops.moe_expand_reduce(ex["expanded"], ex["exp_gate"], ex["row_slot"], d["n_rows"],
                                     out=b.red)
         ops.moe_combine(red, None, d["slot_row"], out=b.out)
@@ -355,12 +355,12 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
         calls.append((L.moe_send_counts, (p(b.idx), T, E, k, R, p(b.place), *cargs, *wsargs)))
     if dedup:
         calls.append((L.moe_dispatch_permute_dedup, (
-            p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, p(b.place), bpe, p(b.ws), b.ws.numel(),
+            p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, bpe, p(b.ws), b.ws.numel(),
             p(d["send"]), p(d["row_token"]), p(d["row_experts"]), p(d["row_gates"]),
             p(d["row_weight"]), p(d["slot_row"]), p(d["n_rows"]), st)))
     else:
         calls.append((L.moe_dispatch_permute, (
-            p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, p(b.place), bpe, p(b.ws), b.ws.numel(),
+            p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, bpe, p(b.ws), b.ws.numel(),
             p(d["send"]), p(d["row_token"]), p(d["row_expert"]), p(d["row_weight"]),
             p(d["slot_row"]), st)))
     if receive:
@@ -370,7 +370,7 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
                                    p(ec["expert_counts"]), p(ec["rank_counts"]),
                                    p(ec["rank_offsets"]), p(ec["expert_offsets"]), p(b.ews),
                                    b.ews.numel(), st)),
-            (L.moe_expand_permute, (p(d["send"]), p(d["row_experts"]), p(d["row_gates"]),
+            (L.moe_expand_permute, (p(d["send"]), p(d["row_gates"]),
                                     p(d["n_rows"]), N, H, E, k, R, bpe, p(b.ews), b.ews.numel(),
                                     p(x["expanded"]), N, p(x["exp_row"]), p(x["exp_expert"]),
                                     p(x["exp_gate"]), p(x["row_slot"]), st)),
@@ -628,16 +628,14 @@ def main():
         d = b.disp
         if dedup:
             disp_calls.append((L.moe_dispatch_permute_dedup, (
-                b.x.data_ptr(), b.idx.data_ptr(), b.gate.data_ptr(), T, H, E, k, R,
-                b.place.data_ptr() if b.place is not None else None, bpe, b.ws.data_ptr(),
-                b.ws.numel(), d["send"].data_ptr(), d["row_token"].data_ptr(),
+                b.x.data_ptr(), b.idx.data_ptr(), b.gate.data_ptr(), T, H, E, k, R, bpe,
+                b.ws.data_ptr(), b.ws.numel(), d["send"].data_ptr(), d["row_token"].data_ptr(),
                 d["row_experts"].data_ptr(), d["row_gates"].data_ptr(),
                 d["row_weight"].data_ptr(), d["slot_row"].data_ptr(), d["n_rows"].data_ptr(), st)))
         else:
             disp_calls.append((L.moe_dispatch_permute, (
-                b.x.data_ptr(), b.idx.data_ptr(), b.gate.data_ptr(), T, H, E, k, R,
-                b.place.data_ptr() if b.place is not None else None, bpe, b.ws.data_ptr(),
-                b.ws.numel(), d["send"].data_ptr(), d["row_token"].data_ptr(),
+                b.x.data_ptr(), b.idx.data_ptr(), b.gate.data_ptr(), T, H, E, k, R, bpe,
+                b.ws.data_ptr(), b.ws.numel(), d["send"].data_ptr(), d["row_token"].data_ptr(),
                 d["row_expert"].data_ptr(), d["row_weight"].data_ptr(),
                 d["slot_row"].data_ptr(), st)))
         comb_calls.append((L.moe_combine, (
@@ -649,7 +647,7 @@ def main():
         for b in order:
             d, x = b.disp, b.exp
             exp_calls.append((L.moe_expand_permute, (
-                d["send"].data_ptr(), d["row_experts"].data_ptr(), d["row_gates"].data_ptr(),
+                d["send"].data_ptr(), d["row_gates"].data_ptr(),
                 d["n_rows"].data_ptr(), N, H, E, k, R, bpe, b.ews.data_ptr(), b.ews.numel(),
                 x["expanded"].data_ptr(), N, x["exp_row"].data_ptr(), x["exp_expert"].data_ptr(),
                 x["exp_gate"].data_ptr(), x["row_slot"].data_ptr(), st)))

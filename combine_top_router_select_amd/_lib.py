@@ -45,16 +45,16 @@ def lib():
         L.moe_send_counts.argtypes = [P, i64, i32, i32, i32, P, i32, P, P, P, P, P, sz, P]
         L.moe_route_plan.argtypes = [P, i64, i32, i32, i32, i32, P, i32, P, P, P, P, P, P, i64,
                                      P, P, sz, P]
-        L.moe_dispatch_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i32, P, sz, P,
-                                           P, P, P, P, P]
-        L.moe_dispatch_permute_dedup.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i32, P,
-                                                 sz, P, P, P, P, P, P, P, P]
+        L.moe_dispatch_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, sz, P, P,
+                                           P, P, P, P]
+        L.moe_dispatch_permute_dedup.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, sz,
+                                                 P, P, P, P, P, P, P, P]
         L.moe_combine.argtypes = [P, P, P, i64, i32, i32, i32, P, P]
         L.moe_coselect_counts.argtypes = [P, i64, i32, i32, P, P]
         L.moe_expand_workspace_bytes.argtypes = [i64, i32, i32, i32]
         L.moe_expand_workspace_bytes.restype = sz
         L.moe_expand_counts.argtypes = [P, P, i64, i32, i32, i32, P, P, P, P, P, P, sz, P]
-        L.moe_expand_permute.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, P, sz, P, i64,
+        L.moe_expand_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, sz, P, i64,
                                          P, P, P, P, P]
         L.moe_expand_reduce.argtypes = [P, P, P, P, i64, i32, i32, i32, P, P]
         L.moe_placement_search.argtypes = [P, i32, i32, P, i32, P, P, P]

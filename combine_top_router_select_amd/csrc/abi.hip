@@ -150,10 +150,10 @@ MOE_API int moe_route_plan(const float* logits, int64_t tokens, int n_experts, i
 
 MOE_API int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* topk_gate,
                                  int64_t tokens, int hidden_dim, int n_experts, int top_k,
-                                 int n_ranks, const int32_t* placement, int bytes_per_element,
-                                 const void* workspace, size_t workspace_bytes, void* send,
-                                 int32_t* row_token, int32_t* row_expert, float* row_weight,
-                                 int32_t* slot_row, void* stream) {
+                                 int n_ranks, int bytes_per_element, const void* workspace,
+                                 size_t workspace_bytes, void* send, int32_t* row_token,
+                                 int32_t* row_expert, float* row_weight, int32_t* slot_row,
+                                 void* stream) {
   int st = check_tek(tokens, n_experts, top_k);
   if (st != MOE_OK) return st;
   if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
@@ -165,7 +165,6 @@ MOE_API int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const f
   if (!x || !topk_idx || !topk_gate || !send || !row_token || !row_expert || !row_weight ||
       !slot_row)
     return MOE_EINVAL;
-  (void)placement;  // the plan in the workspace already encodes it
   return hip_status(moe::launch_dispatch(x, topk_idx, topk_gate, tokens,
                                          hidden_dim * bytes_per_element, n_experts, top_k,
                                          n_ranks, workspace, 0, send, row_token,
@@ -176,11 +175,11 @@ MOE_API int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const f
 MOE_API int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx,
                                        const float* topk_gate, int64_t tokens, int hidden_dim,
                                        int n_experts, int top_k, int n_ranks,
-                                       const int32_t* placement, int bytes_per_element,
-                                       const void* workspace, size_t workspace_bytes,
-                                       void* send, int32_t* row_token, int32_t* row_experts,
-                                       float* row_gates, float* row_weight, int32_t* slot_row,
-                                       int32_t* n_rows, void* stream) {
+                                       int bytes_per_element, const void* workspace,
+                                       size_t workspace_bytes, void* send, int32_t* row_token,
+                                       int32_t* row_experts, float* row_gates,
+                                       float* row_weight, int32_t* slot_row, int32_t* n_rows,
+                                       void* stream) {
   int st = check_tek(tokens, n_experts, top_k);
   if (st != MOE_OK) return st;
   if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
@@ -191,7 +190,6 @@ MOE_API int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx,
   if (tokens > 0 && (!x || !topk_idx || !topk_gate || !send || !row_token || !row_experts ||
                      !row_gates || !row_weight || !slot_row))
     return MOE_EINVAL;
-  (void)placement;  // the plan in the workspace already encodes it
   return hip_status(moe::launch_dispatch(x, topk_idx, topk_gate, tokens,
                                          hidden_dim * bytes_per_element, n_experts, top_k,
                                          n_ranks, workspace, 1, send, row_token,
@@ -251,10 +249,9 @@ MOE_API int moe_expand_counts(const int32_t* row_experts, const int32_t* n_rows,
                                               as_stream(stream)));
 }
 
-MOE_API int moe_expand_permute(const void* rows, const int32_t* row_experts,
-                               const float* row_gates, const int32_t* n_rows, int64_t capacity,
-                               int hidden_dim, int n_experts, int top_k, int n_ranks,
-                               int bytes_per_element, const void* workspace,
+MOE_API int moe_expand_permute(const void* rows, const float* row_gates, const int32_t* n_rows,
+                               int64_t capacity, int hidden_dim, int n_experts, int top_k,
+                               int n_ranks, int bytes_per_element, const void* workspace,
                                size_t workspace_bytes, void* expanded, int64_t expanded_capacity,
                                int32_t* exp_row, int32_t* exp_expert, float* exp_gate,
                                int32_t* row_slot, void* stream) {
@@ -267,10 +264,9 @@ MOE_API int moe_expand_permute(const void* rows, const int32_t* row_experts,
   if (workspace_bytes < moe_expand_workspace_bytes(capacity, n_experts, top_k, n_ranks))
     return MOE_EWORKSPACE;
   if (capacity == 0) return MOE_OK;
-  if (!rows || !row_experts || !row_gates || !row_slot ||
+  if (!rows || !row_gates || !row_slot ||
       (expanded_capacity > 0 && (!expanded || !exp_row || !exp_expert || !exp_gate)))
     return MOE_EINVAL;
-  (void)row_experts;  // the plan in the workspace already encodes them
   return hip_status(moe::launch_expand(rows, row_gates, n_rows, capacity,
                                        hidden_dim * bytes_per_element, n_experts, top_k, n_ranks,
                                        workspace, expanded, expanded_capacity, exp_row,

@@ -10,13 +10,17 @@
 //
 // Design: one wave per (token, row chunk).  Lanes j < k read slot_row[t][j]
 // and the row weight; a slot whose row already appeared in an earlier slot is
-// dropped (dedup rows serve several slots), negative rows are skipped.  The
-// wave then issues the loads of every used row's chunk before any arithmetic
-// (up to KMAX rows x NV vectors of 8 values in flight per lane: 16 bytes of
-// bf16 or 8 bytes of fp8), accumulates in fp32 with fused multiply-adds in slot
-// order starting from -0.0, and converts to bf16 with round-to-nearest-even
-// (v_cvt_pk_bf16_f32 on gfx950).  fp8 rows (OCP E4M3) are decoded with
-// v_cvt_pk_f32_fp8, exact for every byte value.  Row loads are nontemporal:
+// dropped (dedup rows serve several slots), negative rows are skipped, and each
+// remaining lane learns the rank of its row among the token's distinct rows
+// (DPP row shifts inside the 16-lane row that holds the slots).  The wave then
+// issues the loads of every used row's chunk before any arithmetic (up to KMAX
+// rows x NV vectors of 8 values in flight per lane: 16 bytes of bf16 or 8 bytes
+// of fp8), accumulates in fp32 with fused multiply-adds over the rows in
+// ascending row index starting from -0.0, and converts to bf16 with
+// round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).  The order is fixed so
+// that every output is a pure function of its inputs, bit for bit.  fp8 rows
+// (OCP E4M3) are decoded with v_cvt_pk_f32_fp8, exact for every byte value.
+// Row loads are nontemporal:
 // each row is read once, so it should not displace cached data (measured:
 // about 2 us less per 4096-token, top-6, hidden-2048 step).  So are the output
 // stores of the combine proper (launch_combine_t gives the cases).
@@ -97,12 +101,13 @@ __device__ __forceinline__ void store_out(uint8_t* dst, const float (&a)[kVals])
 
 // The weighted sum of a token's rows for one chunk: NQ >= nrows rows are
 // loaded (all loads before any arithmetic; rows past nrows repeat the first
-// one and are not added), accumulated in fp32 from -0.0 in slot order, and
-// stored as bf16.  Offsets are in input bytes; output offsets are twice that
-// for fp8 input.
+// one and are not added), accumulated in fp32 from -0.0 in ascending row
+// order, and stored as bf16.  `ord` is the lane's rank among the token's
+// distinct rows (lanes without a row hold kNoOrder).  Offsets are in input
+// bytes; output offsets are twice that for fp8 input.
 template <int NQ, int NV, bool IN8, bool NTS>
 __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int row_bytes,
-                                         int64_t chunk0, uint64_t um, int j0, int nrows, int rr,
+                                         int64_t chunk0, int ord, int j0, int nrows, int rr,
                                          float wr, int lane, uint8_t* __restrict__ dst) {
   constexpr int OS = IN8 ? 2 : 1;  // output bytes per input byte
   constexpr int IB = InVec<IN8>::kBytes;
@@ -110,11 +115,8 @@ __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ rows, int r
   int jq[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    int j = j0;
-    if (q < nrows) {
-      j = __ffsll((unsigned long long)um) - 1;
-      um &= um - 1;
-    }
+    // the lane holding the q-th smallest row (q = 0: j0)
+    const int j = (q > 0 && q < nrows) ? __ffsll((unsigned long long)__ballot(ord == q)) - 1 : j0;
     jq[q] = j;
     const int p = bcast(rr, j);
     const uint8_t* src = rows + int64_t(p) * row_bytes;
@@ -174,6 +176,30 @@ __device__ __forceinline__ bool repeats_earlier(int v) {
   }
 }
 
+// Rank of lane j's key among the keys of lanes 0 .. KMAX-1 of its DPP row:
+// the number of them that are smaller, counted over the lanes S below
+// (row_shr) and S above (row_shl) for S = 1 .. KMAX-1.  Lanes shifted in from
+// outside the row read INT_MAX, which is never smaller.  Keys are distinct
+// except INT_MAX (lanes without a row), so the used lanes get ranks 0, 1, ...
+// in ascending key order.
+constexpr int kNoOrder = 64;
+template <int S>
+__device__ __forceinline__ int row_shr_max(int v) {
+  return __builtin_amdgcn_update_dpp(0x7FFFFFFF, v, 0x110 + S, 0xF, 0xF, false);
+}
+template <int S>
+__device__ __forceinline__ int row_shl_max(int v) {
+  return __builtin_amdgcn_update_dpp(0x7FFFFFFF, v, 0x100 + S, 0xF, 0xF, false);
+}
+template <int KMAX, int S = 1>
+__device__ __forceinline__ int rank_in_row(int v) {
+  if constexpr (S >= KMAX || S > 15) {
+    return 0;
+  } else {
+    return int(row_shr_max<S>(v) < v) + int(row_shl_max<S>(v) < v) + rank_in_row<KMAX, S + 1>(v);
+  }
+}
+
 template <int NV, int KMAX, bool IN8, bool NTS>
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
@@ -195,8 +221,13 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
   const int r_raw = slot_row[t * k + jl];
   const int r = lane < k ? r_raw : -1;
   const bool use = (r >= 0) & !repeats_earlier<KMAX>(r);
-  uint64_t um = __ballot(use);
+  const uint64_t um = __ballot(use);
   const int nrows = __popcll(um);
+  // rank of this lane's row among the token's distinct rows: rows are added in
+  // ascending row index
+  const int key = use ? r : 0x7FFFFFFF;  // every lane takes part in the DPP moves
+  const int rk = rank_in_row<KMAX>(key);
+  const int ord = use ? rk : kNoOrder;
   uint8_t* dst = out + t * int64_t(row_bytes) * OS;
   if (nrows == 0) {  // no row serves this token: the empty sum, -0.0
     const u32x4 nz = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
@@ -207,7 +238,7 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
     }
     return;
   }
-  const int j0 = __ffsll((unsigned long long)um) - 1;
+  const int j0 = __ffsll((unsigned long long)__ballot(ord == 0)) - 1;  // the smallest row
   const int rr = use ? r : bcast(r, j0);  // every lane names a valid row
   const float wr = w ? w[rr] : 1.0f;
   // as few row loads as the token needs (nrows is wave-uniform): a token served
@@ -215,17 +246,17 @@ combine_kernel(const uint8_t* __restrict__ rows, const float* __restrict__ w,
   // KMAX rows
   if constexpr (KMAX >= 1) {
     if (nrows <= 1)
-      return sum_rows<1, NV, IN8, NTS>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+      return sum_rows<1, NV, IN8, NTS>(rows, row_bytes, chunk0, ord, j0, nrows, rr, wr, lane, dst);
   }
   if constexpr (KMAX >= 2) {
     if (nrows <= 2)
-      return sum_rows<2, NV, IN8, NTS>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+      return sum_rows<2, NV, IN8, NTS>(rows, row_bytes, chunk0, ord, j0, nrows, rr, wr, lane, dst);
   }
   if constexpr (KMAX > 4) {
     if (nrows <= 4)
-      return sum_rows<4, NV, IN8, NTS>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+      return sum_rows<4, NV, IN8, NTS>(rows, row_bytes, chunk0, ord, j0, nrows, rr, wr, lane, dst);
   }
-  sum_rows<KMAX, NV, IN8, NTS>(rows, row_bytes, chunk0, um, j0, nrows, rr, wr, lane, dst);
+  sum_rows<KMAX, NV, IN8, NTS>(rows, row_bytes, chunk0, ord, j0, nrows, rr, wr, lane, dst);
 }
 
 template <int NV, int KMAX, bool IN8>

@@ -363,6 +363,7 @@ static hipError_t launch_route_e(const float* logits, int64_t tokens, int E, int
 // experts; otherwise the softmax over the k selected logits.
 hipError_t launch_route_topk(const float* logits, int64_t tokens, int E, int k, int full_softmax,
                              int32_t* idx, float* gate, hipStream_t stream) {
+  if (tokens == 0) return hipSuccess;  // no grid to launch
   if (full_softmax) return launch_route_e<true>(logits, tokens, E, k, idx, gate, stream);
   return launch_route_e<false>(logits, tokens, E, k, idx, gate, stream);
 }

@@ -1,9 +1,14 @@
 """Python binding of the C ABI (include/moe_route.h), entry point for entry point.
 
-Each function checks dtype/device/contiguity, allocates any output that was not
-passed in (torch is used for device memory and streams only), passes raw
-pointers and the current HIP stream to the library, and raises MoeError on a
-non-zero status.  No step of the computation runs here.
+Each function checks the dtype, shape, device and contiguity of every tensor
+argument, outputs passed in included, and that the sizes agree with each other
+(so that no kernel can write past a buffer the binding was handed), allocates
+any output that was not passed in (torch is used for device memory and streams
+only), passes raw pointers and the current HIP stream to the library, and
+raises MoeError on a non-zero status.  No step of the computation runs here.
+Device-side contents (expert ids in range, placement values, slot_row entries
+below the row count) are preconditions the kernels clamp but do not check;
+check_placement() checks a placement table on the host, on request.
 """
 from __future__ import annotations
 
@@ -13,7 +18,8 @@ import torch
 
 from ._lib import MoeError, check, lib, status_string  # noqa: F401
 
-__all__ = ["MoeError", "moe_status_string", "moe_workspace_bytes", "moe_route_topk",
+__all__ = ["MoeError", "check_placement", "moe_status_string", "moe_workspace_bytes",
+           "moe_route_topk", "moe_route_plan",
            "moe_send_counts", "moe_dispatch_permute", "moe_dispatch_permute_dedup",
            "moe_combine", "moe_coselect_counts", "workspace", "moe_expand_workspace_bytes",
            "expand_workspace", "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
@@ -27,18 +33,70 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr() or None
 
 
-def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> torch.Tensor:
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None, shape=None, itemsize=None,
+         device=None) -> torch.Tensor:
+    """Checks that `t` is a contiguous GPU tensor with the given dtype (or one of
+    a tuple), number of dimensions, exact shape, element size and device."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other arguments on {device}")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if itemsize is not None and t.element_size() != itemsize:
+        raise TypeError(f"{name} must have {itemsize}-byte elements, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _out(o: dict, key: str, shape, dtype, device, itemsize=None) -> torch.Tensor:
+    """The caller's output buffer `o[key]`, checked against the exact shape and
+    type the library will write, or a new one."""
+    t = o.get(key)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if itemsize is not None:
+        return _dev(t, key, shape=shape, itemsize=itemsize, device=device)
+    return _dev(t, key, dtype, shape=shape, device=device)
+
+
+def _ws(ws, device) -> torch.Tensor:
+    """A workspace: a contiguous 1-D byte tensor on the device (the library
+    checks its size)."""
+    return _dev(ws, "ws", torch.uint8, ndim=1, device=device)
+
+
+def _placement(placement, n_experts, device):
+    if placement is None:
+        return None
+    return _dev(placement, "placement", torch.int32, shape=(n_experts,), device=device)
+
+
+def check_placement(placement, n_experts: int, n_ranks: int) -> None:
+    """Opt-in debug helper: checks on the host that an expert -> rank table has
+    n_experts entries in [0, n_ranks) and gives every rank exactly
+    n_experts / n_ranks experts (each GPU holds E/EP experts), which the
+    kernels take as a precondition and do not check.  A GPU tensor is copied
+    to the host, so the call synchronises.  Raises ValueError."""
+    if n_ranks < 1 or n_experts % n_ranks != 0:
+        raise ValueError(f"n_experts {n_experts} is not a multiple of n_ranks {n_ranks}")
+    p = torch.as_tensor(placement).detach().to("cpu", torch.int64).reshape(-1)
+    if p.numel() != n_experts:
+        raise ValueError(f"placement has {p.numel()} entries, expected {n_experts}")
+    if p.numel() and (int(p.min()) < 0 or int(p.max()) >= n_ranks):
+        raise ValueError(f"placement values must lie in [0, {n_ranks})")
+    per = torch.bincount(p, minlength=n_ranks)
+    bad = (per != n_experts // n_ranks).nonzero().reshape(-1).tolist()
+    if bad:
+        raise ValueError(f"ranks {bad[:8]} do not hold exactly {n_experts // n_ranks} experts "
+                         f"(counts {per[bad[:8]].tolist()})")
 
 
 def _stream(stream) -> int:
@@ -70,16 +128,22 @@ def moe_route_topk(logits, top_k, topk_idx=None, topk_gate=None, stream=None,
     experts (moe_route_topk_softmax_all)."""
     _dev(logits, "logits", torch.float32, 2)
     T, E = logits.shape
-    if topk_idx is None:
-        topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
-    if topk_gate is None:
-        topk_gate = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
-    _dev(topk_idx, "topk_idx", torch.int32)
-    _dev(topk_gate, "topk_gate", torch.float32)
+    dev = logits.device
+    o = {"topk_idx": topk_idx, "topk_gate": topk_gate}
+    topk_idx = _out(o, "topk_idx", (T, top_k), torch.int32, dev)
+    topk_gate = _out(o, "topk_gate", (T, top_k), torch.float32, dev)
     fn = lib().moe_route_topk_softmax_all if softmax_all else lib().moe_route_topk
     check(fn(_ptr(logits), T, E, top_k, _ptr(topk_idx), _ptr(topk_gate), _stream(stream)),
           "moe_route_topk_softmax_all" if softmax_all else "moe_route_topk")
     return topk_idx, topk_gate
+
+
+def _count_outputs(o, E, R, dedup, dev):
+    ec = _out(o, "expert_counts", (E,), torch.int32, dev)
+    rc = _out(o, "rank_counts", (R,), torch.int32, dev)
+    ro = _out(o, "rank_offsets", (R + 1,), torch.int32, dev)
+    eo = None if dedup else _out(o, "expert_offsets", (E,), torch.int32, dev)
+    return ec, rc, ro, eo
 
 
 def moe_send_counts(topk_idx, n_experts, n_ranks, placement=None, dedup=False, ws=None,
@@ -89,21 +153,9 @@ def moe_send_counts(topk_idx, n_experts, n_ranks, placement=None, dedup=False, w
     _dev(topk_idx, "topk_idx", torch.int32, 2)
     T, k = topk_idx.shape
     dev = topk_idx.device
-    if placement is not None:
-        _dev(placement, "placement", torch.int32, 1)
-    if ws is None:
-        ws = workspace(T, n_experts, k, n_ranks, dedup, dev)
-    o = dict(out or {})
-    ec = o.get("expert_counts")
-    ec = torch.empty(n_experts, dtype=torch.int32, device=dev) if ec is None else ec
-    rc = o.get("rank_counts")
-    rc = torch.empty(n_ranks, dtype=torch.int32, device=dev) if rc is None else rc
-    ro = o.get("rank_offsets")
-    ro = torch.empty(n_ranks + 1, dtype=torch.int32, device=dev) if ro is None else ro
-    eo = None
-    if not dedup:
-        eo = o.get("expert_offsets")
-        eo = torch.empty(n_experts, dtype=torch.int32, device=dev) if eo is None else eo
+    placement = _placement(placement, n_experts, dev)
+    ws = workspace(T, n_experts, k, n_ranks, dedup, dev) if ws is None else _ws(ws, dev)
+    ec, rc, ro, eo = _count_outputs(dict(out or {}), n_experts, n_ranks, dedup, dev)
     check(lib().moe_send_counts(_ptr(topk_idx), T, n_experts, k, n_ranks, _ptr(placement),
                                 int(bool(dedup)), _ptr(ec), _ptr(rc), _ptr(ro), _ptr(eo),
                                 _ptr(ws), ws.numel(), _stream(stream)), "moe_send_counts")
@@ -121,30 +173,15 @@ def moe_route_plan(logits, top_k, n_ranks, placement=None, dedup=False, softmax_
     _dev(logits, "logits", torch.float32, 2)
     T, E = logits.shape
     dev = logits.device
-    if topk_idx is None:
-        topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
-    if topk_gate is None:
-        topk_gate = torch.empty((T, top_k), dtype=torch.float32, device=dev)
-    _dev(topk_idx, "topk_idx", torch.int32)
-    _dev(topk_gate, "topk_gate", torch.float32)
-    if placement is not None:
-        _dev(placement, "placement", torch.int32, 1)
-    if ws is None:
-        ws = workspace(T, E, top_k, n_ranks, dedup, dev)
-    o = dict(out or {})
-    ec = o.get("expert_counts")
-    ec = torch.empty(E, dtype=torch.int32, device=dev) if ec is None else ec
-    rc = o.get("rank_counts")
-    rc = torch.empty(n_ranks, dtype=torch.int32, device=dev) if rc is None else rc
-    ro = o.get("rank_offsets")
-    ro = torch.empty(n_ranks + 1, dtype=torch.int32, device=dev) if ro is None else ro
-    eo = None
-    if not dedup:
-        eo = o.get("expert_offsets")
-        eo = torch.empty(E, dtype=torch.int32, device=dev) if eo is None else eo
+    o = {"topk_idx": topk_idx, "topk_gate": topk_gate}
+    topk_idx = _out(o, "topk_idx", (T, top_k), torch.int32, dev)
+    topk_gate = _out(o, "topk_gate", (T, top_k), torch.float32, dev)
+    placement = _placement(placement, E, dev)
+    ws = workspace(T, E, top_k, n_ranks, dedup, dev) if ws is None else _ws(ws, dev)
+    ec, rc, ro, eo = _count_outputs(dict(out or {}), E, n_ranks, dedup, dev)
     ncs = 0
     if coselect is not None:
-        _dev(coselect, "coselect", torch.int32, 2)
+        _dev(coselect, "coselect", torch.int32, shape=(E, E), device=dev)
         ncs = T if coselect_tokens is None else int(coselect_tokens)
     check(lib().moe_route_plan(_ptr(logits), T, E, top_k, int(bool(softmax_all)), n_ranks,
                                _ptr(placement), int(bool(dedup)), _ptr(topk_idx),
@@ -155,73 +192,66 @@ def moe_route_plan(logits, top_k, n_ranks, placement=None, dedup=False, softmax_
                                  "expert_offsets": eo, "ws": ws}
 
 
-def _x_bpe(x):
-    _dev(x, "x", None, 2)
+def _x_bpe(x, name="x"):
+    _dev(x, name, None, 2)
     if x.element_size() not in (1, 2, 4):
-        raise TypeError("x must have 1-, 2- or 4-byte elements")
+        raise TypeError(f"{name} must have 1-, 2- or 4-byte elements")
     return x.element_size()
 
 
-def moe_dispatch_permute(x, topk_idx, topk_gate, n_experts, n_ranks, ws, placement=None,
-                         out=None, stream=None):
+def _routed(x, topk_idx, topk_gate):
+    """Checks the dispatch inputs against each other: ids and gates [T][k] for
+    the T rows of x, on x's device.  Returns (T, H, k, bpe, device)."""
     bpe = _x_bpe(x)
-    _dev(topk_idx, "topk_idx", torch.int32, 2)
-    _dev(topk_gate, "topk_gate", torch.float32, 2)
     T, H = x.shape
-    k = topk_idx.shape[1]
     dev = x.device
+    _dev(topk_idx, "topk_idx", torch.int32, 2, device=dev)
+    if topk_idx.shape[0] != T:
+        raise ValueError(f"topk_idx has {topk_idx.shape[0]} rows, x has {T}")
+    k = topk_idx.shape[1]
+    _dev(topk_gate, "topk_gate", torch.float32, shape=(T, k), device=dev)
+    return T, H, k, bpe, dev
+
+
+def moe_dispatch_permute(x, topk_idx, topk_gate, n_experts, n_ranks, ws, out=None, stream=None):
+    """Plain dispatch of the plan in `ws` (from moe_send_counts or
+    moe_route_plan with dedup False, same topk_idx)."""
+    T, H, k, bpe, dev = _routed(x, topk_idx, topk_gate)
+    _ws(ws, dev)
     o = dict(out or {})
     N = T * k
-    send = o.get("send")
-    send = torch.empty((N, H), dtype=x.dtype, device=dev) if send is None else send
-    rt = o.get("row_token")
-    rt = torch.empty(N, dtype=torch.int32, device=dev) if rt is None else rt
-    re = o.get("row_expert")
-    re = torch.empty(N, dtype=torch.int32, device=dev) if re is None else re
-    rw = o.get("row_weight")
-    rw = torch.empty(N, dtype=torch.float32, device=dev) if rw is None else rw
-    sr = o.get("slot_row")
-    sr = torch.empty((T, k), dtype=torch.int32, device=dev) if sr is None else sr
-    if send.numel() < N * H or rt.numel() < N or re.numel() < N or rw.numel() < N:
-        raise ValueError("output buffers are smaller than tokens*top_k rows")
+    send = _out(o, "send", (N, H), x.dtype, dev, itemsize=bpe)
+    rt = _out(o, "row_token", (N,), torch.int32, dev)
+    re = _out(o, "row_expert", (N,), torch.int32, dev)
+    rw = _out(o, "row_weight", (N,), torch.float32, dev)
+    sr = _out(o, "slot_row", (T, k), torch.int32, dev)
     check(lib().moe_dispatch_permute(_ptr(x), _ptr(topk_idx), _ptr(topk_gate), T, H, n_experts,
-                                     k, n_ranks, _ptr(placement), bpe, _ptr(ws), ws.numel(),
-                                     _ptr(send), _ptr(rt), _ptr(re), _ptr(rw), _ptr(sr),
-                                     _stream(stream)), "moe_dispatch_permute")
+                                     k, n_ranks, bpe, _ptr(ws), ws.numel(), _ptr(send),
+                                     _ptr(rt), _ptr(re), _ptr(rw), _ptr(sr), _stream(stream)),
+          "moe_dispatch_permute")
     return {"send": send, "row_token": rt, "row_expert": re, "row_weight": rw, "slot_row": sr}
 
 
-def moe_dispatch_permute_dedup(x, topk_idx, topk_gate, n_experts, n_ranks, ws, placement=None,
-                               out=None, stream=None):
-    bpe = _x_bpe(x)
-    _dev(topk_idx, "topk_idx", torch.int32, 2)
-    _dev(topk_gate, "topk_gate", torch.float32, 2)
-    T, H = x.shape
-    k = topk_idx.shape[1]
-    dev = x.device
+def moe_dispatch_permute_dedup(x, topk_idx, topk_gate, n_experts, n_ranks, ws, out=None,
+                               stream=None):
+    """Deduplicating dispatch of the plan in `ws` (from moe_send_counts or
+    moe_route_plan with dedup True, same topk_idx).  Buffers hold T*k rows."""
+    T, H, k, bpe, dev = _routed(x, topk_idx, topk_gate)
+    _ws(ws, dev)
     o = dict(out or {})
     N = T * k
-    send = o.get("send")
-    send = torch.empty((N, H), dtype=x.dtype, device=dev) if send is None else send
-    rt = o.get("row_token")
-    rt = torch.empty(N, dtype=torch.int32, device=dev) if rt is None else rt
-    rx = o.get("row_experts")
-    rx = torch.empty((N, k), dtype=torch.int32, device=dev) if rx is None else rx
-    rg = o.get("row_gates")
-    rg = torch.empty((N, k), dtype=torch.float32, device=dev) if rg is None else rg
-    rw = o.get("row_weight")
-    rw = torch.empty(N, dtype=torch.float32, device=dev) if rw is None else rw
-    sr = o.get("slot_row")
-    sr = torch.empty((T, k), dtype=torch.int32, device=dev) if sr is None else sr
-    nr = o.get("n_rows")
-    nr = torch.empty(1, dtype=torch.int32, device=dev) if nr is None else nr
-    if send.numel() < N * H or rx.numel() < N * k or rg.numel() < N * k or rw.numel() < N:
-        raise ValueError("output buffers are smaller than tokens*top_k rows")
+    send = _out(o, "send", (N, H), x.dtype, dev, itemsize=bpe)
+    rt = _out(o, "row_token", (N,), torch.int32, dev)
+    rx = _out(o, "row_experts", (N, k), torch.int32, dev)
+    rg = _out(o, "row_gates", (N, k), torch.float32, dev)
+    rw = _out(o, "row_weight", (N,), torch.float32, dev)
+    sr = _out(o, "slot_row", (T, k), torch.int32, dev)
+    nr = _out(o, "n_rows", (1,), torch.int32, dev)
     check(lib().moe_dispatch_permute_dedup(_ptr(x), _ptr(topk_idx), _ptr(topk_gate), T, H,
-                                           n_experts, k, n_ranks, _ptr(placement), bpe,
-                                           _ptr(ws), ws.numel(), _ptr(send), _ptr(rt),
-                                           _ptr(rx), _ptr(rg), _ptr(rw), _ptr(sr), _ptr(nr),
-                                           _stream(stream)), "moe_dispatch_permute_dedup")
+                                           n_experts, k, n_ranks, bpe, _ptr(ws), ws.numel(),
+                                           _ptr(send), _ptr(rt), _ptr(rx), _ptr(rg), _ptr(rw),
+                                           _ptr(sr), _ptr(nr), _stream(stream)),
+          "moe_dispatch_permute_dedup")
     return {"send": send, "row_token": rt, "row_experts": rx, "row_gates": rg,
             "row_weight": rw, "slot_row": sr, "n_rows": nr}
 
@@ -237,16 +267,17 @@ def _row_bpe(rows, name):
 
 
 def moe_combine(rows, row_weight, slot_row, out=None, stream=None):
-    """out[T][H] bf16; rows bf16, or fp8 E4M3 (torch.float8_e4m3fn or uint8)."""
+    """out[T][H] bf16; rows bf16, or fp8 E4M3 (torch.float8_e4m3fn or uint8).
+    row_weight: one fp32 weight per row of `rows`, or None (weight 1).  The
+    entries of slot_row must be below rows.shape[0] (a device precondition)."""
     bpe = _row_bpe(rows, "rows")
-    _dev(slot_row, "slot_row", torch.int32, 2)
+    dev = rows.device
+    n_rows, H = rows.shape
+    _dev(slot_row, "slot_row", torch.int32, 2, device=dev)
     if row_weight is not None:
-        _dev(row_weight, "row_weight", torch.float32)
+        _dev(row_weight, "row_weight", torch.float32, shape=(n_rows,), device=dev)
     T, k = slot_row.shape
-    H = rows.shape[1]
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=rows.device)
-    _dev(out, "out", _BF16, 2)
+    out = _out({"out": out}, "out", (T, H), torch.bfloat16, dev, itemsize=2)
     check(lib().moe_combine(_ptr(rows), _ptr(row_weight), _ptr(slot_row), T, H, k, bpe,
                             _ptr(out), _stream(stream)), "moe_combine")
     return out
@@ -255,11 +286,11 @@ def moe_combine(rows, row_weight, slot_row, out=None, stream=None):
 def moe_coselect_counts(topk_idx, n_experts, tokens=None, coselect=None, stream=None):
     _dev(topk_idx, "topk_idx", torch.int32, 2)
     T, k = topk_idx.shape
+    dev = topk_idx.device
     n = T if tokens is None else min(int(tokens), T)
     if coselect is None:
-        coselect = torch.zeros((n_experts, n_experts), dtype=torch.int32,
-                               device=topk_idx.device)
-    _dev(coselect, "coselect", torch.int32, 2)
+        coselect = torch.zeros((n_experts, n_experts), dtype=torch.int32, device=dev)
+    _dev(coselect, "coselect", torch.int32, shape=(n_experts, n_experts), device=dev)
     if n == 0:
         return coselect
     check(lib().moe_coselect_counts(_ptr(topk_idx), n, n_experts, k, _ptr(coselect),
@@ -280,29 +311,22 @@ def expand_workspace(capacity, n_experts, top_k, n_ranks, device) -> torch.Tenso
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _n_rows(n_rows, device):
+    return _dev(n_rows, "n_rows", torch.int32, shape=(1,), device=device)
+
+
 def moe_expand_counts(row_experts, n_rows, n_experts, n_ranks, placement=None, ws=None,
                       out=None, stream=None):
     """Receive-side counts and plan for received dedup rows.  `row_experts`
     [C][k] int32, `n_rows` a 1-element device int32 tensor.  Returns a dict with
     expert_counts, rank_counts, rank_offsets, expert_offsets and `ws`."""
     _dev(row_experts, "row_experts", torch.int32, 2)
-    _dev(n_rows, "n_rows", torch.int32)
     C, k = row_experts.shape
     dev = row_experts.device
-    if placement is not None:
-        _dev(placement, "placement", torch.int32, 1)
-    if ws is None:
-        ws = expand_workspace(C, n_experts, k, n_ranks, dev)
-    o = dict(out or {})
-    i32 = torch.int32
-    ec = o.get("expert_counts")
-    ec = torch.empty(n_experts, dtype=i32, device=dev) if ec is None else ec
-    rc = o.get("rank_counts")
-    rc = torch.empty(n_ranks, dtype=i32, device=dev) if rc is None else rc
-    ro = o.get("rank_offsets")
-    ro = torch.empty(n_ranks + 1, dtype=i32, device=dev) if ro is None else ro
-    eo = o.get("expert_offsets")
-    eo = torch.empty(n_experts, dtype=i32, device=dev) if eo is None else eo
+    _n_rows(n_rows, dev)
+    placement = _placement(placement, n_experts, dev)
+    ws = expand_workspace(C, n_experts, k, n_ranks, dev) if ws is None else _ws(ws, dev)
+    ec, rc, ro, eo = _count_outputs(dict(out or {}), n_experts, n_ranks, False, dev)
     check(lib().moe_expand_counts(_ptr(row_experts), _ptr(n_rows), C, n_experts, k, n_ranks,
                                   _ptr(placement), _ptr(ec), _ptr(rc), _ptr(ro), _ptr(eo),
                                   _ptr(ws), ws.numel(), _stream(stream)), "moe_expand_counts")
@@ -310,37 +334,33 @@ def moe_expand_counts(row_experts, n_rows, n_experts, n_ranks, placement=None, w
             "ws": ws}
 
 
-def moe_expand_permute(rows, row_experts, row_gates, n_rows, n_experts, n_ranks, ws,
+def moe_expand_permute(rows, row_gates, n_rows, n_experts, n_ranks, ws,
                        expanded_capacity=None, out=None, stream=None):
-    """Receive-side expansion.  expanded_capacity defaults to C rows, which
+    """Receive-side expansion of the plan in `ws` (from moe_expand_counts over
+    the same received rows).  expanded_capacity defaults to C rows, which
     holds every entry when the received buffers have the dedup dispatch's
     capacity T*k (the expansion has exactly T*k rows).  Returns expanded,
     exp_row, exp_expert, exp_gate, row_slot."""
-    bpe = _x_bpe(rows)
-    _dev(row_experts, "row_experts", torch.int32, 2)
-    _dev(row_gates, "row_gates", torch.float32, 2)
-    _dev(n_rows, "n_rows", torch.int32)
+    bpe = _x_bpe(rows, "rows")
     C, H = rows.shape
-    k = row_experts.shape[1]
     dev = rows.device
+    _dev(row_gates, "row_gates", torch.float32, 2, device=dev)
+    if row_gates.shape[0] != C:
+        raise ValueError(f"row_gates has {row_gates.shape[0]} rows, rows has {C}")
+    k = row_gates.shape[1]
+    _n_rows(n_rows, dev)
+    _ws(ws, dev)
     cap = C if expanded_capacity is None else int(expanded_capacity)
     o = dict(out or {})
-    ex = o.get("expanded")
-    ex = torch.empty((cap, H), dtype=rows.dtype, device=dev) if ex is None else ex
-    er = o.get("exp_row")
-    er = torch.empty(cap, dtype=torch.int32, device=dev) if er is None else er
-    ee = o.get("exp_expert")
-    ee = torch.empty(cap, dtype=torch.int32, device=dev) if ee is None else ee
-    eg = o.get("exp_gate")
-    eg = torch.empty(cap, dtype=torch.float32, device=dev) if eg is None else eg
-    rs = o.get("row_slot")
-    rs = torch.empty((C, k), dtype=torch.int32, device=dev) if rs is None else rs
-    if ex.numel() < cap * H or er.numel() < cap or ee.numel() < cap or eg.numel() < cap:
-        raise ValueError("expanded buffers are smaller than expanded_capacity rows")
-    check(lib().moe_expand_permute(_ptr(rows), _ptr(row_experts), _ptr(row_gates), _ptr(n_rows),
-                                   C, H, n_experts, k, n_ranks, bpe, _ptr(ws), ws.numel(),
-                                   _ptr(ex), cap, _ptr(er), _ptr(ee), _ptr(eg), _ptr(rs),
-                                   _stream(stream)), "moe_expand_permute")
+    ex = _out(o, "expanded", (cap, H), rows.dtype, dev, itemsize=bpe)
+    er = _out(o, "exp_row", (cap,), torch.int32, dev)
+    ee = _out(o, "exp_expert", (cap,), torch.int32, dev)
+    eg = _out(o, "exp_gate", (cap,), torch.float32, dev)
+    rs = _out(o, "row_slot", (C, k), torch.int32, dev)
+    check(lib().moe_expand_permute(_ptr(rows), _ptr(row_gates), _ptr(n_rows), C, H, n_experts,
+                                   k, n_ranks, bpe, _ptr(ws), ws.numel(), _ptr(ex), cap,
+                                   _ptr(er), _ptr(ee), _ptr(eg), _ptr(rs), _stream(stream)),
+          "moe_expand_permute")
     return {"expanded": ex, "exp_row": er, "exp_expert": ee, "exp_gate": eg, "row_slot": rs}
 
 
@@ -348,15 +368,14 @@ def moe_expand_reduce(expert_out, exp_gate, row_slot, n_rows, out=None, stream=N
     """Receive-side reduction of the experts' outputs (bf16, or fp8 E4M3) back
     to one bf16 row per received row (rows past n_rows are not written)."""
     bpe = _row_bpe(expert_out, "expert_out")
-    _dev(row_slot, "row_slot", torch.int32, 2)
-    _dev(n_rows, "n_rows", torch.int32)
+    dev = expert_out.device
+    n_exp, H = expert_out.shape
+    _dev(row_slot, "row_slot", torch.int32, 2, device=dev)
+    _n_rows(n_rows, dev)
     if exp_gate is not None:
-        _dev(exp_gate, "exp_gate", torch.float32)
+        _dev(exp_gate, "exp_gate", torch.float32, shape=(n_exp,), device=dev)
     C, k = row_slot.shape
-    H = expert_out.shape[1]
-    if out is None:
-        out = torch.empty((C, H), dtype=torch.bfloat16, device=expert_out.device)
-    _dev(out, "out", _BF16, 2)
+    out = _out({"out": out}, "out", (C, H), torch.bfloat16, dev, itemsize=2)
     check(lib().moe_expand_reduce(_ptr(expert_out), _ptr(exp_gate), _ptr(row_slot),
                                   _ptr(n_rows), C, H, k, bpe, _ptr(out), _stream(stream)),
           "moe_expand_reduce")
@@ -396,18 +415,19 @@ def moe_placement_search(coselect, n_ranks, initial=None, max_swaps=None):
 def moe_shuffle_fit(prev_idx, cur_idx, next_idx, n_experts, n_ranks, placement_next=None,
                     pair_counts=None, single_counts=None, stream=None):
     """Accumulate the planner's count tables from one calibration batch."""
-    for name, t in (("prev_idx", prev_idx), ("cur_idx", cur_idx), ("next_idx", next_idx)):
-        _dev(t, name, torch.int32, 2)
+    _dev(cur_idx, "cur_idx", torch.int32, 2)
     T, k = cur_idx.shape
     dev = cur_idx.device
-    if placement_next is not None:
-        _dev(placement_next, "placement_next", torch.int32, 1)
+    _dev(prev_idx, "prev_idx", torch.int32, shape=(T, k), device=dev)
+    _dev(next_idx, "next_idx", torch.int32, shape=(T, k), device=dev)
+    placement_next = _placement(placement_next, n_experts, dev)
+    E, R = n_experts, n_ranks
     if pair_counts is None:
-        pair_counts = torch.zeros((n_experts, n_experts, n_ranks), dtype=torch.int32, device=dev)
+        pair_counts = torch.zeros((E, E, R), dtype=torch.int32, device=dev)
     if single_counts is None:
-        single_counts = torch.zeros((n_experts, n_ranks), dtype=torch.int32, device=dev)
-    _dev(pair_counts, "pair_counts", torch.int32, 3)
-    _dev(single_counts, "single_counts", torch.int32, 2)
+        single_counts = torch.zeros((E, R), dtype=torch.int32, device=dev)
+    _dev(pair_counts, "pair_counts", torch.int32, shape=(E, E, R), device=dev)
+    _dev(single_counts, "single_counts", torch.int32, shape=(E, R), device=dev)
     check(lib().moe_shuffle_fit(_ptr(prev_idx), _ptr(cur_idx), _ptr(next_idx), T, n_experts, k,
                                 n_ranks, _ptr(placement_next), _ptr(pair_counts),
                                 _ptr(single_counts), _stream(stream)), "moe_shuffle_fit")
@@ -416,15 +436,14 @@ def moe_shuffle_fit(prev_idx, cur_idx, next_idx, n_experts, n_ranks, placement_n
 
 def moe_shuffle_predict(prev_idx, cur_idx, pair_counts, single_counts, min_obs, scores=None,
                         stream=None):
-    _dev(prev_idx, "prev_idx", torch.int32, 2)
     _dev(cur_idx, "cur_idx", torch.int32, 2)
-    _dev(pair_counts, "pair_counts", torch.int32, 3)
-    _dev(single_counts, "single_counts", torch.int32, 2)
     T, k = cur_idx.shape
+    dev = cur_idx.device
+    _dev(prev_idx, "prev_idx", torch.int32, shape=(T, k), device=dev)
+    _dev(single_counts, "single_counts", torch.int32, 2, device=dev)
     E, R = single_counts.shape
-    if scores is None:
-        scores = torch.empty((T, R), dtype=torch.float32, device=cur_idx.device)
-    _dev(scores, "scores", torch.float32, 2)
+    _dev(pair_counts, "pair_counts", torch.int32, shape=(E, E, R), device=dev)
+    scores = _out({"scores": scores}, "scores", (T, R), torch.float32, dev)
     check(lib().moe_shuffle_predict(_ptr(prev_idx), _ptr(cur_idx), T, E, k, R, _ptr(pair_counts),
                                     _ptr(single_counts), int(min_obs), _ptr(scores),
                                     _stream(stream)), "moe_shuffle_predict")

@@ -74,7 +74,7 @@ extern "C" {
 const char* moe_status_string(int status);
 
 /* Host.  Bytes of workspace that moe_send_counts() or moe_route_plan() fills
- * and the dispatch call of the same (topk_idx, placement, dedup) then reads.
+ * and the dispatch call of the same topk_idx and dedup mode then reads.
  * Returns 0 if the arguments are outside the limits above.  The workspace is
  * opaque; it needs no initialisation and 256-byte alignment is enough. */
 size_t moe_workspace_bytes(int64_t tokens, int n_experts, int top_k, int n_ranks, int dedup);
@@ -163,8 +163,9 @@ int moe_route_plan(const float* logits, int64_t tokens, int n_experts, int top_k
 /* A4a - dispatch permute, one row per (token, expert) ([EC] "Method 1",
  * conventional dispatch; [DD] "Reading the counts").
  * Must follow moe_send_counts(dedup = 0), or moe_route_plan(dedup = 0), on the
- * same stream with the same topk_idx, placement and workspace (the workspace
- * carries the plan).
+ * same stream with the same topk_idx and workspace.  The workspace carries the
+ * plan: every row position, and with it the placement and the expert and rank
+ * offsets of the counts call, so the dispatch calls take none of them.
  *   x            [T][H] elements of bytes_per_element bytes (bf16: 2), read only;
  *                rows are copied bit for bit.  H * bytes_per_element must be a
  *                multiple of 16.
@@ -179,15 +180,16 @@ int moe_route_plan(const float* logits, int64_t tokens, int n_experts, int top_k
  *         not a multiple of 16, limits), MOE_EWORKSPACE. */
 int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* topk_gate,
                          int64_t tokens, int hidden_dim, int n_experts, int top_k,
-                         int n_ranks, const int32_t* placement, int bytes_per_element,
-                         const void* workspace, size_t workspace_bytes, void* send,
-                         int32_t* row_token, int32_t* row_expert, float* row_weight,
-                         int32_t* slot_row, void* stream);
+                         int n_ranks, int bytes_per_element, const void* workspace,
+                         size_t workspace_bytes, void* send, int32_t* row_token,
+                         int32_t* row_expert, float* row_weight, int32_t* slot_row,
+                         void* stream);
 
 /* A4b - deduplicating dispatch, one row per distinct (token, destination rank)
  * ([EC] "Method 1", deduplicating dispatcher).
  * Must follow moe_send_counts(dedup = 1), or moe_route_plan(dedup = 1), on the
- * same stream with the same topk_idx, placement and workspace.  Capacity is
+ * same stream with the same topk_idx and workspace (which carries the plan,
+ * the placement included).  Capacity is
  * N = T*k rows for every output so that no host synchronisation is needed; the
  * number of rows written, D, is stored in *n_rows (and equals rank_offsets[R]
  * of the counts call).
@@ -207,11 +209,10 @@ int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* to
  * Errors: as moe_dispatch_permute. */
 int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx, const float* topk_gate,
                                int64_t tokens, int hidden_dim, int n_experts, int top_k,
-                               int n_ranks, const int32_t* placement, int bytes_per_element,
-                               const void* workspace, size_t workspace_bytes, void* send,
-                               int32_t* row_token, int32_t* row_experts, float* row_gates,
-                               float* row_weight, int32_t* slot_row, int32_t* n_rows,
-                               void* stream);
+                               int n_ranks, int bytes_per_element, const void* workspace,
+                               size_t workspace_bytes, void* send, int32_t* row_token,
+                               int32_t* row_experts, float* row_gates, float* row_weight,
+                               int32_t* slot_row, int32_t* n_rows, void* stream);
 
 /* A5 - combine ([EC] "The Communication Bottleneck"; [DD] "send_matrices.csv
  * columns": combine moves the dispatch volumes back): each token's output is the
@@ -226,11 +227,17 @@ int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx, const flo
  *   slot_row     [T][k] int32: rows of each token; negative entries are skipped
  *                and a row listed by several slots is added once.
  *   out          [T][H] bf16 out: out[t][h] = bf16(sum over the token's distinct
- *                rows r, in slot order, of row_weight[r] * rows[r][h]), summed in
- *                fp32 with fused multiply-adds from -0.0 and rounded once to bf16
- *                (nearest, ties to even).  Within 1 bf16 ulp of the exactly
- *                rounded sum when the terms do not cancel.
- *                Every fp8 value is decoded exactly.
+ *                rows r of row_weight[r] * rows[r][h]).  The pages fix neither
+ *                the order nor the precision of this sum; here it is, exactly:
+ *                acc = -0.0f, then for the distinct rows in ascending row index
+ *                acc = fmaf(row_weight[r], rows[r][h], acc) in fp32 (one
+ *                rounding per step, nearest-even, subnormals kept), then one
+ *                round-to-nearest-even of acc to bf16 (overflow to infinity).
+ *                Every fp8 value is decoded exactly.  The result is a pure
+ *                function of the inputs, bit for bit, for every finite or
+ *                infinite input; an output that the rule makes NaN (a NaN in a
+ *                row, inf - inf, 0 * inf) is some NaN whose sign and payload
+ *                are not specified.
  * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (bytes_per_element not 1 or 2, H *
  *         bytes_per_element not a multiple of 16, k > 16). */
 int moe_combine(const void* rows, const float* row_weight, const int32_t* slot_row,
@@ -293,8 +300,10 @@ int moe_expand_counts(const int32_t* row_experts, const int32_t* n_rows, int64_t
                       void* stream);
 
 /* Receive-side expansion: copies every listed (row, expert) into its place.
+ * The row_experts table is not an argument: moe_expand_counts() read it, and
+ * the plan it left in the workspace holds every entry's expert and position.
  *   rows           [C][H] elements of bytes_per_element bytes (copied bitwise).
- *   row_gates      [C][k] fp32, aligned with row_experts.
+ *   row_gates      [C][k] fp32, aligned with the row_experts table.
  *   workspace      as filled by moe_expand_counts() for the same arguments.
  *   expanded       [expanded_capacity][H] out: expanded row q = rows[exp_row[q]].
  *   exp_row, exp_expert [expanded_capacity] int32 out; exp_gate
@@ -307,19 +316,19 @@ int moe_expand_counts(const int32_t* row_experts, const int32_t* n_rows, int64_t
  *                  caller how many rows the expansion needs).
  * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (as moe_dispatch_permute()),
  *         MOE_EWORKSPACE. */
-int moe_expand_permute(const void* rows, const int32_t* row_experts, const float* row_gates,
-                       const int32_t* n_rows, int64_t capacity, int hidden_dim, int n_experts,
-                       int top_k, int n_ranks, int bytes_per_element, const void* workspace,
-                       size_t workspace_bytes, void* expanded, int64_t expanded_capacity,
-                       int32_t* exp_row, int32_t* exp_expert, float* exp_gate,
-                       int32_t* row_slot, void* stream);
+int moe_expand_permute(const void* rows, const float* row_gates, const int32_t* n_rows,
+                       int64_t capacity, int hidden_dim, int n_experts, int top_k, int n_ranks,
+                       int bytes_per_element, const void* workspace, size_t workspace_bytes,
+                       void* expanded, int64_t expanded_capacity, int32_t* exp_row,
+                       int32_t* exp_expert, float* exp_gate, int32_t* row_slot,
+                       void* stream);
 
 /* Receive-side reduction: for every received row p < *n_rows,
  * out[p][h] = bf16(sum over the distinct expanded rows q in row_slot[p][.]
- * (q >= 0), in column order, of exp_gate[q] * expert_out[q][h]), with the
- * arithmetic of moe_combine() (fp32 fused multiply-adds from -0.0, one
- * round-to-nearest-even).  exp_gate NULL = weight 1.  Rows p >= *n_rows of out
- * are not written.
+ * (q >= 0) of exp_gate[q] * expert_out[q][h]), with the arithmetic of
+ * moe_combine() (fp32 fused multiply-adds from -0.0 over the rows in ascending
+ * index, one round-to-nearest-even).  exp_gate NULL = weight 1.  Rows
+ * p >= *n_rows of out are not written.
  *   expert_out     [expanded rows][H] bf16 (bytes_per_element 2) or fp8 E4M3
  *                  (1): the experts' outputs in the expanded layout.
  *   out            [C][H] bf16.

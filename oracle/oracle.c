@@ -6,7 +6,9 @@
  * leg use it.  It shares no source with the HIP kernels.
  *
  * Plain, slow, single-threaded loops in the order the definitions are stated.
- * Floating point that the pages leave open is done in fp64 and rounded once.
+ * Floating point that the pages leave open is done in fp64 and rounded once,
+ * except the combine, which is a fixed chain of fp32 fused multiply-adds (see
+ * oracle_combine_rows).
  *
  * Sources (page title, then section):
  *  [EC]  "Expert Coupling in MoE Pretraining: Reducing All-to-All Overhead with
@@ -35,8 +37,9 @@
  *    rank ascending, then token (dedup);
  *  - dedup row weight: sum of that rank's gates in ascending expert order, fp64,
  *    rounded once to fp32;
- *  - combine: sum over the distinct rows serving a token of weight*row, exact
- *    products summed in fp64, rounded once to bf16 (round to nearest even);
+ *  - combine: sum over the distinct rows serving a token, in ascending row
+ *    index, of weight*row as a chain of fp32 fused multiply-adds starting from
+ *    -0.0, rounded once to bf16 (round to nearest even);
  *  - W's diagonal counts the tokens selecting e.
  */
 #include <math.h>
@@ -323,11 +326,24 @@ uint16_t oracle_bf16_from_double(double d) {
     return (uint16_t)(u >> 16);
 }
 
-static double oracle_bf16_to_double(uint16_t b) {
+/* The fp32 value of a bf16 bit pattern: bf16 is the top half of an fp32. */
+static float oracle_bf16_to_float(uint16_t b) {
     const uint32_t u = (uint32_t)b << 16;
     float f;
     memcpy(&f, &u, sizeof f);
-    return (double)f;
+    return f;
+}
+
+/* bf16 nearest to the fp32 value f, ties to even.  Every fp32 value is exact
+ * in fp64, so this is the rounding above; a NaN keeps its sign and the top of
+ * its payload and is made quiet. */
+uint16_t oracle_bf16_from_float(float f) {
+    if (isnan(f)) {
+        uint32_t u;
+        memcpy(&u, &f, sizeof u);
+        return (uint16_t)((u >> 16) | 0x0040u);
+    }
+    return oracle_bf16_from_double((double)f);
 }
 
 /* fp8 E4M3 in the OCP 8-bit floating point format: sign, 4 exponent bits
@@ -345,11 +361,14 @@ double oracle_e4m3_to_double(uint8_t b) {
 /* [EC] "The Communication Bottleneck" (dispatch, experts, combine) and [DD]
  * "send_matrices.csv columns" (combine is the reverse exchange): each token's
  * output is the weighted sum of the rows that served it.
- * out[t][h] = bf16( sum over distinct rows r in slot_row[t][.] (r >= 0) of
- *                   w[r] * rows[r][h] ), summed exactly enough in fp64
- * (each product of an fp32 and a bf16 is exact in fp64), rounded once.
- * w == NULL means weight 1 for every row.  Rows are visited in ascending index
- * order; the sum starts at -0.0 so that an all-(-0) input stays -0. */
+ * out[t][h] = bf16( sum over the distinct rows r in slot_row[t][.] (r >= 0)
+ *                   of w[r] * rows[r][h] ).
+ * The pages fix no order or precision for this sum; the reading taken: rows
+ * in ascending index, acc = -0.0f, then acc = fmaf(w[r], rows[r][h], acc) for
+ * each row (fp32, one rounding per step), and one round-to-nearest-even of acc
+ * to bf16.  -0.0 as the start keeps an all-(-0) sum at -0 and makes the empty
+ * sum -0.  w == NULL means weight 1 for every row.  Rows of fp8 E4M3 are
+ * decoded exactly (every E4M3 value is an fp32 value). */
 static int oracle_combine_rows(const void* rows, int fp8, const float* w, const int32_t* slot_row,
                                int64_t tokens, int hidden_dim, int top_k, uint16_t* out) {
     int32_t* rs = (int32_t*)malloc(sizeof(int32_t) * (size_t)top_k);
@@ -371,15 +390,15 @@ static int oracle_combine_rows(const void* rows, int fp8, const float* w, const 
             rs[b + 1] = v;
         }
         for (int h = 0; h < hidden_dim; ++h) {
-            double acc = -0.0;
+            float acc = -0.0f;
             for (int i = 0; i < nr; ++i) {
-                const double wr = w ? (double)w[rs[i]] : 1.0;
+                const float wr = w ? w[rs[i]] : 1.0f;
                 const int64_t at = (int64_t)rs[i] * hidden_dim + h;
-                const double y = fp8 ? oracle_e4m3_to_double(((const uint8_t*)rows)[at])
-                                     : oracle_bf16_to_double(((const uint16_t*)rows)[at]);
-                acc += wr * y;
+                const float y = fp8 ? (float)oracle_e4m3_to_double(((const uint8_t*)rows)[at])
+                                    : oracle_bf16_to_float(((const uint16_t*)rows)[at]);
+                acc = fmaf(wr, y, acc);
             }
-            out[t * hidden_dim + h] = oracle_bf16_from_double(acc);
+            out[t * hidden_dim + h] = oracle_bf16_from_float(acc);
         }
     }
     free(rs);

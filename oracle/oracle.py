@@ -66,6 +66,8 @@ def lib():
             getattr(L, f).restype = ctypes.c_int
         L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
         L.oracle_bf16_from_double.restype = ctypes.c_uint16
+        L.oracle_bf16_from_float.argtypes = [ctypes.c_float]
+        L.oracle_bf16_from_float.restype = ctypes.c_uint16
         for f in ("oracle_route_topk", "oracle_route_topk_softmax_all", "oracle_send_counts",
                   "oracle_dispatch",
                   "oracle_dispatch_dedup", "oracle_expand_dedup", "oracle_combine",
@@ -256,6 +258,11 @@ def coselect(idx, n_experts, tokens=None, W=None):
 
 def bf16_from_double(d: float) -> int:
     return int(lib().oracle_bf16_from_double(float(d)))
+
+
+def bf16_from_float(f) -> int:
+    """bf16 bits of the fp32 value f (round to nearest even)."""
+    return int(lib().oracle_bf16_from_float(ctypes.c_float(np.float32(f))))
 
 
 def placement_objective(W, placement):

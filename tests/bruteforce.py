@@ -3,7 +3,8 @@
 Written independently of oracle.c, from the same definitions but by other
 means: top-k membership by counting the experts strictly ahead, buffer
 positions by a full sort of (rank, expert, token) keys, dedup rows from a set,
-combine by exact rational arithmetic.
+combine by exact rational arithmetic (the exact sum, and the fp32 chain with
+every rounding step done by bisection over fp32 bit patterns).
 """
 from __future__ import annotations
 
@@ -117,6 +118,79 @@ def combine(rows_bits, weights, slot_row, fp8=False):
                     all_neg_zero = False
             # the sum starts at -0.0: it stays -0 only if every term is -0 (or none)
             o.append(nearest_bf16(acc, negative_zero=(acc == 0 and all_neg_zero)))
+        out.append(o)
+    return out
+
+
+def _f32_value(bits):
+    return struct.unpack("<f", struct.pack("<I", bits & 0xFFFFFFFF))[0]
+
+
+_F32_MAX = Fraction(_f32_value(0x7F7FFFFF))
+_F32_OVERFLOW = _F32_MAX + Fraction(2) ** 103     # halfway from the largest fp32 to 2^128
+
+
+def nearest_f32(q: Fraction):
+    """Nearest fp32 to an exact rational, ties to the even bit pattern, by
+    bisection over the finite non-negative fp32 patterns; magnitudes from the
+    halfway point above the largest fp32 on round to infinity.  Returns a
+    Python float (zero comes back as +0.0: callers fix its sign)."""
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    if a >= _F32_OVERFLOW:
+        return sign * math.inf
+    lo, hi = 0, 0x7F7FFFFF
+    while lo < hi:                      # smallest pattern with value >= a
+        mid = (lo + hi) // 2
+        if Fraction(_f32_value(mid)) >= a:
+            hi = mid
+        else:
+            lo = mid + 1
+    up = lo
+    if Fraction(_f32_value(up)) == a:
+        return sign * _f32_value(up)
+    down = up - 1
+    du = Fraction(_f32_value(up)) - a
+    dd = a - Fraction(_f32_value(down))
+    if du < dd or (du == dd and (up & 1) == 0):
+        return sign * _f32_value(up)
+    return sign * _f32_value(down)
+
+
+def fma_f32(w, y, acc):
+    """fp32 fused multiply-add of finite fp32 values: w*y + acc computed
+    exactly as rationals and rounded once.  An exact zero takes IEEE's sign:
+    -0 only when both w*y and acc are zeros of negative sign."""
+    p = Fraction(w) * Fraction(y)
+    s = p + Fraction(acc)
+    if s == 0:
+        p_neg = p == 0 and (math.copysign(1.0, w) * math.copysign(1.0, y)) < 0
+        acc_neg = acc == 0 and math.copysign(1.0, acc) < 0
+        return -0.0 if (p_neg and acc_neg) else 0.0
+    return nearest_f32(s)
+
+
+def combine_chain(rows_bits, weights, slot_row, fp8=False):
+    """The combine as its fp32 chain, emulated one rounding at a time with
+    exact rationals: distinct rows in ascending index, acc = -0.0, acc =
+    fma_f32(w, y, acc) per row, then bf16 round-to-nearest-even of acc.
+    Finite values only (no overflow to bf16 infinity)."""
+    T = len(slot_row)
+    H = len(rows_bits[0])
+    out = []
+    for t in range(T):
+        rs = sorted({r for r in slot_row[t] if r >= 0})
+        o = []
+        for h in range(H):
+            acc = -0.0
+            for r in rs:
+                w = 1.0 if weights is None else float(weights[r])
+                y = (float(e4m3_to_fraction(rows_bits[r][h])) if fp8
+                     else _bf16_value(int(rows_bits[r][h])))
+                acc = fma_f32(w, y, acc)
+            o.append(nearest_bf16(Fraction(acc), negative_zero=math.copysign(1.0, acc) < 0))
         out.append(o)
     return out
 

@@ -58,3 +58,26 @@ def f32_ulp_diff(a, b):
 
 def bf16_to_f64(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_isnan(bits):
+    b = np.asarray(bits, np.uint16)
+    return ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+
+
+def assert_bf16_equal(got, ref, what=""):
+    """Bit-for-bit equality of bf16 outputs; where the reference is NaN the
+    output must be a NaN too (sign and payload are not part of the contract).
+    On failure the message names the first differing element and the largest
+    difference in bf16 ulps."""
+    got = np.asarray(got, np.uint16)
+    ref = np.asarray(ref, np.uint16)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    gn, rn = bf16_isnan(got), bf16_isnan(ref)
+    bad = (gn != rn) | (~rn & (got != ref))
+    if bad.any():
+        first = tuple(int(v[0]) for v in np.nonzero(bad))
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} bf16 outputs differ; first at {first}: "
+            f"got {int(got[first]):#06x}, want {int(ref[first]):#06x}; max "
+            f"{int(bf16_ulp_diff(got[bad & ~gn & ~rn], ref[bad & ~gn & ~rn]).max(initial=0))} ulp")

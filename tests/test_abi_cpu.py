@@ -140,10 +140,10 @@ def test_route_plan_errors(lib):
 def test_dispatch_errors(lib):
     f = lib.moe_dispatch_permute
     ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)
-    base = [FAKE, FAKE, FAKE, 100, 128, 8, 2, 4, None, 2, FAKE, ws, FAKE, FAKE, FAKE, FAKE,
-            FAKE, None]
-    names = ["x", "idx", "gate", "T", "H", "E", "k", "R", "place", "bpe", "ws", "wsb", "send",
-             "rt", "re", "rw", "sr", "stream"]
+    base = [FAKE, FAKE, FAKE, 100, 128, 8, 2, 4, 2, FAKE, ws, FAKE, FAKE, FAKE, FAKE, FAKE,
+            None]
+    names = ["x", "idx", "gate", "T", "H", "E", "k", "R", "bpe", "ws", "wsb", "send", "rt", "re",
+             "rw", "sr", "stream"]
 
     def call(**kw):
         a = list(base)
@@ -161,11 +161,11 @@ def test_dispatch_errors(lib):
     assert call(ws=None) == EINVAL
     g = lib.moe_dispatch_permute_dedup
     wsd = lib.moe_workspace_bytes(6400, 8, 2, 4, 1)
-    args = [FAKE, FAKE, FAKE, 6400, 128, 8, 2, 4, None, 2, FAKE, wsd, FAKE, FAKE, FAKE, FAKE,
-            FAKE, FAKE, None, None]
+    args = [FAKE, FAKE, FAKE, 6400, 128, 8, 2, 4, 2, FAKE, wsd, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, None, None]
     assert g(*args) == EINVAL                      # n_rows is NULL
-    args[18] = FAKE
-    args[11] = wsd - 1                             # one byte short
+    args[17] = FAKE
+    args[10] = wsd - 1                             # one byte short
     assert g(*args) == EWS
 
 
@@ -210,10 +210,10 @@ def test_receive_side_errors(lib):
     assert call(f, base, names, k=17, E=32) == EUNSUP
     assert call(f, base, names, wsb=ws - 1) == EWS
     g = lib.moe_expand_permute
-    gb = [FAKE, FAKE, FAKE, FAKE, 100, 128, 8, 2, 4, 2, FAKE, ws, FAKE, 200, FAKE, FAKE, FAKE,
-          FAKE, None]
-    gn = ["rows", "rx", "rg", "n", "C", "H", "E", "k", "R", "bpe", "ws", "wsb", "ex", "excap",
-          "er", "ee", "eg", "rs", "st"]
+    gb = [FAKE, FAKE, FAKE, 100, 128, 8, 2, 4, 2, FAKE, ws, FAKE, 200, FAKE, FAKE, FAKE, FAKE,
+          None]
+    gn = ["rows", "rg", "n", "C", "H", "E", "k", "R", "bpe", "ws", "wsb", "ex", "excap", "er",
+          "ee", "eg", "rs", "st"]
     assert call(g, gb, gn, n=None) == EINVAL
     assert call(g, gb, gn, excap=-1) == EINVAL
     assert call(g, gb, gn, excap=1 << 40) == EUNSUP

@@ -65,13 +65,13 @@ def _step(w, dedup, logits, x, place, b, fused=False):
         ops.moe_route_topk(logits, k, b["idx"], b["gate"])
         c = ops.moe_send_counts(b["idx"], E, R, place, dedup, ws=b["ws"], out=b["cnt"])
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-    d = f(x, b["idx"], b["gate"], E, R, c["ws"], place, out=b["disp"])
+    d = f(x, b["idx"], b["gate"], E, R, c["ws"], out=b["disp"])
     ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b["out"])
     if dedup:
         ops.moe_expand_counts(d["row_experts"], d["n_rows"], E, R, place, ws=b["ews"],
                               out=b["ecnt"])
-        ex = ops.moe_expand_permute(d["send"], d["row_experts"], d["row_gates"], d["n_rows"], E,
-                                    R, b["ews"], out=b["exp"])
+        ex = ops.moe_expand_permute(d["send"], d["row_gates"], d["n_rows"], E, R, b["ews"],
+                                    out=b["exp"])
         red = ops.moe_expand_reduce(ex["expanded"], ex["exp_gate"], ex["row_slot"], d["n_rows"],
                                     out=b["red"])
         ops.moe_combine(red, None, d["slot_row"], out=b["out2"])

@@ -4,9 +4,10 @@ seeded inputs.
 Bars: bit-exact for indices, counts, offsets, row positions, copied rows and
 integer metadata; gates within 1 fp32 ulp (both sides evaluate the same fp64
 formula, only the exp implementations differ); dedup row weights bit-exact
-(same fp64 additions in the same order); combine within 1 bf16 ulp of the
-oracle's exactly rounded fp64 sum (plus the fp32 accumulation bound where the
-terms can cancel); co-selection counts bit-exact.
+(same fp64 additions in the same order); combine bit-exact (both sides take the
+same chain of fp32 fused multiply-adds over the rows in ascending index from
+-0.0 and one bf16 rounding; where the chain gives NaN, any NaN); co-selection
+counts bit-exact.
 """
 import numpy as np
 import pytest
@@ -14,8 +15,8 @@ import torch
 
 from combine_top_router_select_amd import ops
 from combine_top_router_select_amd import workloads as WL
-from gpu_util import (bf16_dev, bf16_host, bf16_to_f64, bf16_ulp_diff, f32_ulp_diff, host,
-                      say, to_dev)
+from gpu_util import (assert_bf16_equal, bf16_dev, bf16_host, bf16_ulp_diff, f32_ulp_diff,
+                      host, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,7 +118,7 @@ def test_route_plan_parity(oracle_mod, T, E, k, R, dedup, pl, softmax_all):
     assert _plan_equal(c["ws"], c2["ws"], T, E, k, R, dedup)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
     x = bf16_dev(inp["x_bits"])
-    d = f(x, idx, gate, E, R, c["ws"], place_dev)
+    d = f(x, idx, gate, E, R, c["ws"])
     o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(inp["x_bits"], idx_o, gate_o,
                                                                      E, R, placement)
     sync()
@@ -169,10 +170,10 @@ def run_dispatch_parity(oracle_mod, x_bits, idx_o, gate_o, E, R, placement, dedu
     x = bf16_dev(x_bits)
     c = ops.moe_send_counts(idx, E, R, place_dev, dedup=dedup)
     if dedup:
-        d = ops.moe_dispatch_permute_dedup(x, idx, gate, E, R, c["ws"], place_dev)
+        d = ops.moe_dispatch_permute_dedup(x, idx, gate, E, R, c["ws"])
         o = oracle_mod.dispatch_dedup(x_bits, idx_o, gate_o, E, R, placement)
     else:
-        d = ops.moe_dispatch_permute(x, idx, gate, E, R, c["ws"], place_dev)
+        d = ops.moe_dispatch_permute(x, idx, gate, E, R, c["ws"])
         o = oracle_mod.dispatch(x_bits, idx_o, gate_o, E, R, placement)
     sync()
     _check_counts(c, o, dedup)
@@ -283,7 +284,7 @@ def test_random_shapes(oracle_mod, i):
     W = torch.zeros((E, E), dtype=torch.int32, device=torch.device("cuda:0"))
     idx, gate, c = ops.moe_route_plan(to_dev(inp["logits"]), k, R, place_dev, dedup, coselect=W)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-    d = f(bf16_dev(inp["x_bits"]), idx, gate, E, R, c["ws"], place_dev)
+    d = f(bf16_dev(inp["x_bits"]), idx, gate, E, R, c["ws"])
     out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"])
     sync()
     idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
@@ -298,7 +299,7 @@ def test_random_shapes(oracle_mod, i):
     assert (bf16_host(d["send"][:n]) == o["send"]).all()
     assert (host(d["row_weight"][:n]).view(np.uint32) == o["row_weight"].view(np.uint32)).all()
     ref = oracle_mod.combine(o["send"], o["row_weight"], o["slot_row"])
-    assert bf16_ulp_diff(bf16_host(out), ref).max() <= 1
+    assert_bf16_equal(bf16_host(out), ref, f"random {i} combine")
     assert (host(W) == oracle_mod.coselect(idx_o, E)).all()
 
 
@@ -316,7 +317,7 @@ def test_dispatch_metadata_order_boundary(oracle_mod, T, dedup):
     place_dev = to_dev(placement)
     idx, gate, c = ops.moe_route_plan(to_dev(inp["logits"]), k, R, place_dev, dedup)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-    d = f(bf16_dev(inp["x_bits"]), idx, gate, E, R, c["ws"], place_dev)
+    d = f(bf16_dev(inp["x_bits"]), idx, gate, E, R, c["ws"])
     sync()
     idx_h, gate_h = host(idx), host(gate)
     o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(
@@ -377,7 +378,7 @@ def test_bytes_per_element_1_and_4(oracle_mod):
 @pytest.mark.parametrize("dedup", [False, True])
 def test_combine_random_rows(oracle_mod, dedup):
     """Non-identity experts: random signed rows, random weights (both signs),
-    NULL weights, and slots marked -1 (skipped)."""
+    NULL weights, and slots marked -1 (skipped); bit-exact against the oracle."""
     T, H, E, k, R = 1000, 512, 64, 8, 8
     say(f"[combine] random rows dedup={dedup}")
     inp = WL.make_custom_inputs(T, 8, E, seed=21)
@@ -394,21 +395,89 @@ def test_combine_random_rows(oracle_mod, dedup):
         ref = oracle_mod.combine(Y, w, slot)
         got = bf16_host(ops.moe_combine(bf16_dev(Y), to_dev(w), to_dev(slot)))
         sync()
-        # bound: 1 bf16 ulp + fp32 accumulation error gamma_k * sum |w*y|
-        yv = bf16_to_f64(Y)
-        wv = np.ones(n) if w is None else w.astype(np.float64)
-        absum = np.zeros((T, H))
-        for t in range(T):
-            for r in sorted({int(v) for v in slot[t] if v >= 0}):
-                absum[t] += np.abs(wv[r] * yv[r])
-        gam = k * 2.0 ** -24 / (1 - k * 2.0 ** -24)
-        g64, r64 = bf16_to_f64(got), bf16_to_f64(ref)
-        ulp = np.maximum(np.abs(r64), np.abs(g64)) * 2.0 ** -7
-        ulp = np.maximum(ulp, 2.0 ** -133)
-        ok = np.abs(g64 - r64) <= ulp + gam * absum
-        exact = (got == ref).mean()
-        say(f"  weights={wname}: bit-exact {exact:.6f}, max ulp {bf16_ulp_diff(got, ref).max()}")
-        assert ok.all()
+        assert_bf16_equal(got, ref, f"combine weights={wname}")
+
+
+def _chain_cases():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "combine_fp32_chain.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("H", [8, 2056])
+def test_combine_hand_cases(H):
+    """The hand-worked combine cases (ascending row order, fp32 accumulation,
+    fused multiply-adds, signed zeros, skipped and repeated slots, bf16 and
+    fp32 overflow, infinities, NaN, subnormal results and inputs) through the
+    kernel: every output element equals the worked value (any NaN for a NaN)."""
+    for c in _chain_cases():
+        Y = np.repeat(np.array([[int(b, 16)] for b in c["rows"]], np.uint16), H, axis=1)
+        w = None if c["weights"] is None else np.array(
+            [float.fromhex(v) for v in c["weights"]], np.float32)
+        slot = np.array([c["slot_row"]], np.int32)
+        got = bf16_host(ops.moe_combine(bf16_dev(Y), to_dev(w), to_dev(slot)))
+        sync()
+        if c["out"] == "nan":
+            assert (((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)).all(), c["name"]
+        else:
+            assert (got == int(c["out"], 16)).all(), (c["name"], hex(int(got[0, 0])))
+
+
+@pytest.mark.parametrize("kind", ["special", "tiny", "huge"])
+def test_combine_edge_values(oracle_mod, kind):
+    """Rows with edge values against the oracle, bit for bit (NaN for NaN):
+    'special' mixes +-inf, NaN and +-0 into ordinary rows; 'tiny' rows and
+    weights whose products and sums are subnormal in fp32 and in bf16; 'huge'
+    rows near the top of the bf16 range whose weighted sums overflow bf16 (and
+    fp32) or cancel."""
+    T, H, E, k, R = 700, 264, 32, 6, 8
+    say(f"[combine edge] {kind}")
+    inp = WL.make_custom_inputs(T, 8, E, seed=31)
+    idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+    o = oracle_mod.dispatch(inp["x_bits"], idx_o, gate_o, E, R)
+    n = o["n_rows"]
+    rng = np.random.default_rng({"special": 1, "tiny": 2, "huge": 3}[kind])
+    if kind == "special":
+        Y = WL.bf16_bits_from_f32(rng.standard_normal((n, H)).astype(np.float32))
+        m = rng.random((n, H))
+        Y[m < 0.02] = 0x7F80
+        Y[(m >= 0.02) & (m < 0.04)] = 0xFF80
+        Y[(m >= 0.04) & (m < 0.05)] = 0x7FC1
+        Y[(m >= 0.05) & (m < 0.07)] = 0x8000
+        Y[(m >= 0.07) & (m < 0.09)] = 0x0000
+        ws = [None, o["row_weight"], rng.standard_normal(n).astype(np.float32)]
+    elif kind == "tiny":
+        # |y| from 2^-133 (the smallest bf16 subnormal) to below 2^-118, weights
+        # from 2^-12 to 2: products and sums reach the fp32 and bf16 subnormal
+        # ranges, where both sides must keep subnormals
+        mag = rng.integers(0, 24, (n, H))
+        frac = rng.integers(0, 128, (n, H))
+        sign = rng.integers(0, 2, (n, H)) << 15
+        exp_field = np.maximum(mag - 16 + 1, 0)          # field 0: subnormal patterns
+        Y = (sign | (exp_field << 7) | frac).astype(np.uint16)
+        ws = [None, (2.0 ** rng.uniform(-12, 1, n)).astype(np.float32),
+              (rng.standard_normal(n) * 2.0 ** -6).astype(np.float32)]
+    else:
+        # exponents near the top of the range: sums of a few rows overflow bf16
+        # and fp32, and opposite signs cancel
+        e = rng.integers(250, 255, (n, H))
+        frac = rng.integers(0, 128, (n, H))
+        sign = rng.integers(0, 2, (n, H)) << 15
+        Y = (sign | (e << 7) | frac).astype(np.uint16)
+        ws = [None, o["row_weight"], rng.uniform(-2, 2, n).astype(np.float32)]
+    slot = o["slot_row"].copy()
+    slot[rng.random(slot.shape) < 0.05] = -1
+    for w in ws:
+        ref = oracle_mod.combine(Y, w, slot)
+        got = bf16_host(ops.moe_combine(bf16_dev(Y), to_dev(w), to_dev(slot)))
+        sync()
+        assert_bf16_equal(got, ref, f"combine edge {kind} weights={'none' if w is None else 'set'}")
+        isnan = ((ref & 0x7F80) == 0x7F80) & ((ref & 0x7F) != 0)
+        isinf = (ref & 0x7FFF) == 0x7F80
+        sub = ((ref & 0x7F80) == 0) & ((ref & 0x7F) != 0)
+        say(f"  outputs: {isnan.mean():.3f} NaN, {isinf.mean():.3f} inf, {sub.mean():.3f} "
+            f"subnormal")
 
 
 # -------------------------------------------------------------- co-selection --
@@ -450,7 +519,7 @@ def gpu_chain(inp, w, dedup, stream=None, fused=False):
         idx, gate = ops.moe_route_topk(logits, k, stream=stream)
         c = ops.moe_send_counts(idx, E, R, place, dedup=dedup, stream=stream)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-    d = f(x, idx, gate, E, R, c["ws"], place, stream=stream)
+    d = f(x, idx, gate, E, R, c["ws"], stream=stream)
     out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], stream=stream)
     if not fused:
         W = ops.moe_coselect_counts(idx, E, tokens=w.coselect_tokens, stream=stream)
@@ -503,9 +572,7 @@ def test_workload_end_to_end(oracle_mod, name, dedup, fused):
     del send_h
     out_h = bf16_host(out)
     ref = oracle_mod.combine(o["send"], o["row_weight"], o["slot_row"])
-    diff = bf16_ulp_diff(out_h, ref)
-    say(f"  combine max ulp {diff.max()}, non-exact {(diff > 0).mean():.2e}")
-    assert diff.max() <= 1
+    assert_bf16_equal(out_h, ref, f"{name} combine")
     # identity experts with gates summing to 1 return the input
     assert (out_h == inp["x_bits"]).all()
     W_o = oracle_mod.coselect(idx_o, w.n_experts, tokens=w.coselect_tokens)
@@ -620,7 +687,7 @@ def test_canary_padding_untouched(oracle_mod):
                 vv = vv.view(-1, k)
             views[kk] = vv
         f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-        d = f(bf16_dev(inp["x_bits"]), idx, gate, E, R, c["ws"], None, out=views)
+        d = f(bf16_dev(inp["x_bits"]), idx, gate, E, R, c["ws"], out=views)
         out_b = canary(T * H, torch.bfloat16)
         ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=out_b[:T * H].view(T, H))
         W_b = canary(E * E, torch.int32)
@@ -635,9 +702,13 @@ def test_canary_padding_untouched(oracle_mod):
         assert untouched(idx_b, T * k) and untouched(gate_b, T * k)
 
 
-def test_zero_tokens():
+@pytest.mark.parametrize("E", [16, 256])
+def test_zero_tokens(E):
+    """No tokens: every call succeeds, counts and offsets are zeros, the dedup
+    row count is 0 and W is untouched; E = 256 takes the unfused routing path
+    of the combined call."""
     dv = torch.device("cuda:0")
-    E, k, R, H = 16, 2, 4, 64
+    k, R, H = 2, 4, 64
     idx = torch.empty((0, k), dtype=torch.int32, device=dv)
     gate = torch.empty((0, k), dtype=torch.float32, device=dv)
     ops.moe_route_topk(torch.empty((0, E), dtype=torch.float32, device=dv), k, idx, gate)
@@ -689,24 +760,12 @@ def _fp8_dev(u8):
     return torch.from_numpy(np.ascontiguousarray(u8)).to("cuda:0").view(torch.float8_e4m3fn)
 
 
-def _bound_ok(got, ref, Y_f64, w, slot, k):
-    n = Y_f64.shape[0]
-    wv = np.ones(n) if w is None else w.astype(np.float64)
-    absum = np.zeros((slot.shape[0], Y_f64.shape[1]))
-    for t in range(slot.shape[0]):
-        for r in sorted({int(v) for v in slot[t] if v >= 0}):
-            absum[t] += np.abs(wv[r] * Y_f64[r])
-    gam = k * 2.0 ** -24 / (1 - k * 2.0 ** -24)
-    g64, r64 = bf16_to_f64(got), bf16_to_f64(ref)
-    ulp = np.maximum(np.maximum(np.abs(r64), np.abs(g64)) * 2.0 ** -7, 2.0 ** -133)
-    return bool((np.abs(g64 - r64) <= ulp + gam * absum).all())
-
-
 @pytest.mark.parametrize("dedup", [False, True])
 @pytest.mark.parametrize("H", [1024, 2048, 4096, 272, 2064, 16])
 def test_combine_fp8_rows(oracle_mod, dedup, H):
     """fp8 E4M3 rows (random bytes, no NaN, some -0) into bf16, for gate, NULL
-    and signed weights, against the oracle's exact decode and sum."""
+    and signed weights: bit-exact against the oracle (exact decode, the same
+    fp32 chain)."""
     T, E, k, R = 600, 64, 6, 8
     say(f"[combine fp8] H={H} dedup={dedup}")
     inp = WL.make_custom_inputs(T, 8, E, seed=H + dedup)
@@ -717,13 +776,12 @@ def test_combine_fp8_rows(oracle_mod, dedup, H):
     rng = np.random.default_rng(H)
     Y = rng.integers(0, 256, (n, H)).astype(np.uint8)
     Y[(Y & 0x7F) == 0x7F] = 0x80
-    Yf = torch.from_numpy(Y).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     slot = o["slot_row"]
     for w in (o["row_weight"], None, rng.standard_normal(n).astype(np.float32)):
         ref = oracle_mod.combine_fp8(Y, w, slot)
         got = bf16_host(ops.moe_combine(_fp8_dev(Y), to_dev(w), to_dev(slot)))
         sync()
-        assert _bound_ok(got, ref, Yf, w, slot, k)
+        assert_bf16_equal(got, ref, f"fp8 combine H={H}")
 
 
 def test_fp8_dispatch_combine_chain(oracle_mod):
@@ -747,7 +805,7 @@ def test_fp8_dispatch_combine_chain(oracle_mod):
         out = bf16_host(ops.moe_combine(d["send"], d["row_weight"], d["slot_row"]))
         ref = oracle_mod.combine_fp8(o["send"], o["row_weight"], o["slot_row"])
         sync()
-        assert bf16_ulp_diff(out, ref).max() <= 1
+        assert_bf16_equal(out, ref, f"fp8 chain dedup={dedup}")
         x_bf = (torch.from_numpy(x8).view(torch.float8_e4m3fn).to(torch.bfloat16)
                 .view(torch.int16).numpy().view(np.uint16))
         assert bf16_ulp_diff(out, x_bf).max() <= 1
@@ -771,8 +829,7 @@ def test_fp8_reduce(oracle_mod):
                                 to_dev(ref_ex["row_slot"]), nr)
     ref = oracle_mod.combine_fp8(Y, ref_ex["exp_gate"], ref_ex["row_slot"][:D])
     sync()
-    Yf = torch.from_numpy(Y).view(torch.float8_e4m3fn).to(torch.float64).numpy()
-    assert _bound_ok(bf16_host(out[:D]), ref, Yf, ref_ex["exp_gate"], ref_ex["row_slot"][:D], k)
+    assert_bf16_equal(bf16_host(out[:D]), ref, "fp8 reduce")
 
 
 @pytest.mark.parametrize("T,E,k", [(1000, 64, 6), (777, 128, 8), (300, 8, 8), (130, 1024, 16),
@@ -790,8 +847,8 @@ def test_route_softmax_all_parity(oracle_mod, T, E, k):
 @pytest.mark.parametrize("i", range(32))
 def test_random_fp8_chain(oracle_mod, i):
     """Thirty-two seeded random shapes with fp8 rows: the combined routing call,
-    dispatch of E4M3 bytes (bit for bit) and the decoding combine against the
-    oracle's exact decode and sum."""
+    dispatch of E4M3 bytes and the decoding combine, bit for bit against the
+    oracle."""
     rng = np.random.default_rng(3000 + i)
     R = int(rng.choice([1, 2, 4, 8, 16]))
     E = R * int(rng.choice([1, 2, 4, 8]))
@@ -814,10 +871,4 @@ def test_random_fp8_chain(oracle_mod, i):
     n = o["n_rows"]
     assert (host(d["send"][:n].view(torch.uint8)) == o["send"]).all()
     ref = oracle_mod.combine_fp8(o["send"], o["row_weight"], o["slot_row"])
-    Y = np.array([[oracle_mod.e4m3_to_double(int(b)) for b in row] for row in o["send"]]) \
-        if n * H <= 200000 else None
-    got = bf16_host(out)
-    if Y is not None:
-        assert _bound_ok(got, ref, Y, o["row_weight"], o["slot_row"], k)
-    else:
-        assert bf16_ulp_diff(got, ref).max() <= 1
+    assert_bf16_equal(bf16_host(out), ref, f"fp8 random {i}")

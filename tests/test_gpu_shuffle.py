@@ -69,3 +69,15 @@ def test_shuffle_plan_workload(oracle_mod, name):
     loc = (served == owner[:, None]).mean()
     say(f"  locality {loc_base:.3f} -> {loc:.3f}")
     assert loc > 2 * loc_base
+
+
+def test_shuffle_predict_hand_cases(oracle_mod):
+    """The hand-worked prediction fixture through the GPU: every score equals
+    the worked value exactly."""
+    from test_oracle_pins import load_shuffle_hand
+    h, pair, single, groups = load_shuffle_hand()
+    for prev, cur, want in groups:
+        s = host(ops.moe_shuffle_predict(to_dev(prev), to_dev(cur), to_dev(pair),
+                                         to_dev(single), h["min_obs"]))
+        torch.cuda.synchronize()
+        assert (s == want).all(), (prev.tolist(), cur.tolist(), s.tolist())

@@ -13,6 +13,8 @@ import math
 import os
 import struct
 
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -172,10 +174,40 @@ def test_bruteforce_layouts(oracle_mod, T, E, k, R, placement_kind):
     assert W.tolist() == BF.coselect(idx.tolist(), E, T)
 
 
+def _within_chain_bound(out_bits, rows_bits, weights, slot_row, fp8=False):
+    """The fp32 chain against the exact sum S: with n rows every fused
+    multiply-add rounds once, so the chain's fp32 result lies within
+    gamma_n * sum |w y| of S (gamma_n = n u / (1 - n u), u = 2^-24), and bf16
+    rounding is monotone, so the output lies between the bf16 roundings of the
+    two ends of that interval.  Returns the number of outputs checked."""
+    u = Fraction(1, 2 ** 24)
+    checked = 0
+    for t, slots in enumerate(slot_row):
+        rs = sorted({int(r) for r in slots if r >= 0})
+        n = len(rs)
+        gam = n * u / (1 - n * u)
+        for h in range(len(rows_bits[0])):
+            terms = []
+            for r in rs:
+                w = Fraction(1) if weights is None else Fraction(float(weights[r]))
+                y = (BF.e4m3_to_fraction(rows_bits[r][h]) if fp8
+                     else BF.bf16_to_fraction(rows_bits[r][h]))
+                terms.append(w * y)
+            S = sum(terms, Fraction(0))
+            B = gam * sum((abs(v) for v in terms), Fraction(0))
+            lo = BF._bf16_value(BF.nearest_bf16(S - B))
+            hi = BF._bf16_value(BF.nearest_bf16(S + B))
+            got = BF._bf16_value(int(out_bits[t][h]))
+            assert lo <= got <= hi, (t, h, lo, got, hi)
+            checked += 1
+    return checked
+
+
 @pytest.mark.parametrize("T,E,k,R", TINY)
 def test_bruteforce_combine_random_rows(oracle_mod, T, E, k, R):
-    """Random rows (signed, non-identity experts) and random weights: the oracle
-    equals the exactly rounded rational sum."""
+    """Random rows (signed, non-identity experts) and random weights: the
+    oracle equals the fp32 chain emulated step by step with exact rationals,
+    and lies within the chain's error bound of the exact rational sum."""
     rng = np.random.default_rng(T * 31 + k)
     H = 6
     inp = _tiny_logits(T, E, 3 + T, tied=False)
@@ -186,11 +218,85 @@ def test_bruteforce_combine_random_rows(oracle_mod, T, E, k, R):
         n = d["n_rows"]
         Y = WL.bf16_bits_from_f32(rng.standard_normal((n, H)).astype(np.float32) * 4)
         Y[rng.random((n, H)) < 0.1] = 0x8000      # some -0.0
+        slot = d["slot_row"].copy()
+        slot[rng.random(slot.shape) < 0.1] = -1   # some skipped slots
         for w in (None, d["row_weight"], rng.standard_normal(n).astype(np.float32)):
-            out = oracle_mod.combine(Y, w, d["slot_row"])
-            ref = BF.combine(Y.tolist(), None if w is None else w.tolist(),
-                             d["slot_row"].tolist())
-            assert out.tolist() == ref
+            out = oracle_mod.combine(Y, w, slot)
+            wl = None if w is None else w.tolist()
+            assert out.tolist() == BF.combine_chain(Y.tolist(), wl, slot.tolist())
+            assert _within_chain_bound(out.tolist(), Y.tolist(), wl, slot.tolist()) == T * H
+
+
+def test_combine_order_matters_and_is_ascending(oracle_mod):
+    """Rows whose fp32 sum depends on the order: the oracle takes the rows in
+    ascending index whatever the slot order, so permuting a token's slots
+    changes nothing, while renumbering the rows changes the result."""
+    one, big, nbig = 0x3F80, 0x4E80, 0xCE80            # 1, 2^30, -2^30
+    Y = np.array([[one], [big], [nbig]], np.uint16)
+    for perm in ([0, 1, 2], [2, 1, 0], [1, 2, 0], [2, 0, 1]):
+        out = oracle_mod.combine(Y, None, np.array([perm], np.int32))
+        assert int(out[0, 0]) == 0x0000, perm          # (1 + 2^30) - 2^30 = 0 in fp32
+    Y2 = np.array([[big], [nbig], [one]], np.uint16)    # same values, 1 added last
+    out = oracle_mod.combine(Y2, None, np.array([[2, 0, 1]], np.int32))
+    assert int(out[0, 0]) == 0x3F80
+
+
+def _hex_bits(v):
+    return int(v, 16)
+
+
+@pytest.fixture(scope="module")
+def chain_cases():
+    with open(os.path.join(GOLDEN, "combine_fp32_chain.json")) as f:
+        return json.load(f)["cases"]
+
+
+def test_hand_combine_fp32_chain(oracle_mod, chain_cases):
+    """Hand-worked cases of the combine reading (ascending rows, fp32 fused
+    multiply-adds from -0.0, one bf16 rounding): order, accumulation
+    precision, fusion, signed zeros, repeated and skipped slots, overflow,
+    infinities, NaN and subnormals."""
+    for c in chain_cases:
+        Y = np.array([[_hex_bits(b)] for b in c["rows"]], np.uint16)
+        w = None if c["weights"] is None else np.array(
+            [float.fromhex(v) for v in c["weights"]], np.float32)
+        if w is not None:   # the weights must be exact fp32 values
+            assert [float(v) for v in w] == [float.fromhex(v) for v in c["weights"]], c["name"]
+        out = int(oracle_mod.combine(Y, w, np.array([c["slot_row"]], np.int32))[0, 0])
+        if c["out"] == "nan":
+            assert (out & 0x7F80) == 0x7F80 and (out & 0x7F) != 0, c["name"]
+        else:
+            assert out == _hex_bits(c["out"]), (c["name"], hex(out))
+
+
+def test_hand_combine_fp32_chain_matches_bruteforce(chain_cases):
+    """The finite hand-worked cases, replayed through the step-by-step
+    rational emulation of the chain (a second, independent check of the hand
+    arithmetic)."""
+    for c in chain_cases:
+        if c["out"] == "nan" or c["out"] == "0x7F80":
+            continue
+        Y = [[_hex_bits(b)] for b in c["rows"]]
+        w = None if c["weights"] is None else [float.fromhex(v) for v in c["weights"]]
+        got = BF.combine_chain(Y, w, [c["slot_row"]])[0][0]
+        assert got == _hex_bits(c["out"]), (c["name"], hex(got))
+
+
+def test_bf16_from_float_nan_and_rounding(oracle_mod):
+    """fp32 -> bf16 of the combine output: torch's cast for finite values and
+    infinities; NaN stays NaN with its sign."""
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2 ** 32, size=5000, dtype=np.uint64).astype(np.uint32)
+    bits[:1000] = (bits[:1000] & 0xFFFF0000) | 0x8000
+    f = bits.view(np.float32)
+    f = f[~np.isnan(f)]
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle_mod.bf16_from_float(v) for v in f], np.uint16)
+    assert (got == ref).all()
+    for v in (float("nan"), -float("nan")):
+        b = oracle_mod.bf16_from_float(v)
+        assert (b & 0x7F80) == 0x7F80 and (b & 0x7F) != 0
+        assert bool(b & 0x8000) == bool(np.signbit(np.float32(v)))
 
 
 # ------------------------------------------------------------ library pins --
@@ -567,7 +673,9 @@ def test_e4m3_decode_matches_torch(oracle_mod):
 @pytest.mark.parametrize("T,E,k,R", TINY[:5])
 def test_bruteforce_combine_fp8_rows(oracle_mod, T, E, k, R):
     """fp8 rows (random bytes, NaN excluded, some -0): the oracle equals the
-    exactly rounded rational sum, for NULL, gate and signed weights."""
+    fp32 chain emulated with exact rationals over the exactly decoded bytes,
+    within the chain's bound of the exact sum, for NULL, gate and signed
+    weights."""
     rng = np.random.default_rng(T * 13 + k)
     H = 5
     inp = _tiny_logits(T, E, 5 + T, tied=False)
@@ -578,9 +686,9 @@ def test_bruteforce_combine_fp8_rows(oracle_mod, T, E, k, R):
     Y[(Y & 0x7F) == 0x7F] = 0x80                  # no NaN; those become -0
     for w in (None, d["row_weight"], rng.standard_normal(n).astype(np.float32)):
         out = oracle_mod.combine_fp8(Y, w, d["slot_row"])
-        ref = BF.combine(Y.tolist(), None if w is None else w.tolist(), d["slot_row"].tolist(),
-                         fp8=True)
-        assert out.tolist() == ref
+        wl = None if w is None else w.tolist()
+        assert out.tolist() == BF.combine_chain(Y.tolist(), wl, d["slot_row"].tolist(), fp8=True)
+        _within_chain_bound(out.tolist(), Y.tolist(), wl, d["slot_row"].tolist(), fp8=True)
 
 
 def test_fp8_single_row_is_exact(oracle_mod):
@@ -661,6 +769,37 @@ def test_shuffle_predict_properties(oracle_mod):
     pair3, single3 = oracle_mod.shuffle_fit(prev, cur, nxt3, E, R, np.array(place))
     s3 = oracle_mod.shuffle_predict(prev, cur, pair3, single3, 1)
     assert (s3.argmax(1) == 3).all() and (s3[:, :3] == 0).all()
+
+
+def load_shuffle_hand():
+    """The hand-worked prediction fixture as numpy tables and token groups."""
+    with open(os.path.join(GOLDEN, "shuffle_predict_hand.json")) as f:
+        h = json.load(f)
+    E, R = h["E"], h["R"]
+    pair = np.zeros((E, E, R), np.int32)
+    for p in h["pair"]:
+        pair[p["a"], p["b"]] = p["counts"]
+    single = np.array(h["single"], np.int32)
+    groups = []
+    for g in h["groups"]:
+        prev = np.array([t["prev"] for t in g["tokens"]], np.int32)
+        cur = np.array([t["cur"] for t in g["tokens"]], np.int32)
+        want = np.array([[float(Fraction(v)) for v in t["scores"]] for t in g["tokens"]],
+                        np.float32)
+        groups.append((prev, cur, want))
+    return h, pair, single, groups
+
+
+def test_shuffle_predict_hand(oracle_mod):
+    """Hand-worked scores: an asymmetric pair table (pair[a][b] != pair[b][a]),
+    a pair seen exactly min_obs times (used) and one seen min_obs - 1 times
+    (single-expert fallback), an expert never seen at layer l (no
+    contribution), and the sum over a token's k*k pairs at k = 2.  Reading
+    pair[b][a], or comparing with > instead of >=, changes these scores."""
+    h, pair, single, groups = load_shuffle_hand()
+    for prev, cur, want in groups:
+        got = oracle_mod.shuffle_predict(prev, cur, pair, single, h["min_obs"])
+        assert (got == want).all(), (prev.tolist(), cur.tolist(), got.tolist())
 
 
 def test_shuffle_assign_properties(oracle_mod):
