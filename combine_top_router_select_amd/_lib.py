@@ -16,7 +16,8 @@ SYMBOLS = ("moe_status_string", "moe_workspace_bytes", "moe_expand_workspace_byt
            "moe_dispatch_permute_dedup", "moe_combine", "moe_coselect_counts",
            "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
            "moe_placement_search", "moe_route_topk_softmax_all", "moe_shuffle_fit",
-           "moe_shuffle_predict", "moe_shuffle_assign", "moe_route_plan")
+           "moe_shuffle_predict", "moe_shuffle_assign", "moe_route_plan",
+           "moe_dispatch_permute_noalloc")
 
 _lib = None
 
@@ -49,6 +50,8 @@ def lib():
                                            P, P, P, P]
         L.moe_dispatch_permute_dedup.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, sz,
                                                  P, P, P, P, P, P, P, P]
+        L.moe_dispatch_permute_noalloc.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i32, P,
+                                                   P, P, P, P, P, P, P, P, P]
         L.moe_combine.argtypes = [P, P, P, i64, i32, i32, i32, P, P]
         L.moe_coselect_counts.argtypes = [P, i64, i32, i32, P, P]
         L.moe_expand_workspace_bytes.argtypes = [i64, i32, i32, i32]

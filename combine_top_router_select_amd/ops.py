@@ -21,6 +21,7 @@ from ._lib import MoeError, check, lib, status_string  # noqa: F401
 __all__ = ["MoeError", "check_placement", "moe_status_string", "moe_workspace_bytes",
            "moe_route_topk", "moe_route_plan",
            "moe_send_counts", "moe_dispatch_permute", "moe_dispatch_permute_dedup",
+           "moe_dispatch_permute_noalloc",
            "moe_combine", "moe_coselect_counts", "workspace", "moe_expand_workspace_bytes",
            "expand_workspace", "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
            "moe_placement_search", "moe_shuffle_fit", "moe_shuffle_predict",
@@ -254,6 +255,31 @@ def moe_dispatch_permute_dedup(x, topk_idx, topk_gate, n_experts, n_ranks, ws, o
           "moe_dispatch_permute_dedup")
     return {"send": send, "row_token": rt, "row_experts": rx, "row_gates": rg,
             "row_weight": rw, "slot_row": sr, "n_rows": nr}
+
+
+def moe_dispatch_permute_noalloc(x, topk_idx, topk_gate, n_experts, n_ranks, placement=None,
+                                 out=None, stream=None):
+    """moe_send_counts (plain) and moe_dispatch_permute in one call whose plan
+    lives in the library's static per-device scratch: the C entry point
+    allocates nothing (outputs not passed in are allocated here, by torch).
+    Returns the counts and the dispatch outputs in one dict."""
+    T, H, k, bpe, dev = _routed(x, topk_idx, topk_gate)
+    placement = _placement(placement, n_experts, dev)
+    o = dict(out or {})
+    ec, rc, ro, eo = _count_outputs(o, n_experts, n_ranks, False, dev)
+    N = T * k
+    send = _out(o, "send", (N, H), x.dtype, dev, itemsize=bpe)
+    rt = _out(o, "row_token", (N,), torch.int32, dev)
+    re = _out(o, "row_expert", (N,), torch.int32, dev)
+    rw = _out(o, "row_weight", (N,), torch.float32, dev)
+    sr = _out(o, "slot_row", (T, k), torch.int32, dev)
+    check(lib().moe_dispatch_permute_noalloc(_ptr(x), _ptr(topk_idx), _ptr(topk_gate), T, H,
+                                             n_experts, k, n_ranks, _ptr(placement), bpe,
+                                             _ptr(ec), _ptr(rc), _ptr(ro), _ptr(eo), _ptr(send),
+                                             _ptr(rt), _ptr(re), _ptr(rw), _ptr(sr),
+                                             _stream(stream)), "moe_dispatch_permute_noalloc")
+    return {"expert_counts": ec, "rank_counts": rc, "rank_offsets": ro, "expert_offsets": eo,
+            "send": send, "row_token": rt, "row_expert": re, "row_weight": rw, "slot_row": sr}
 
 
 _FP8 = tuple(t for t in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if t is not None)

@@ -185,6 +185,37 @@ int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* to
                          int32_t* row_expert, float* row_weight, int32_t* slot_row,
                          void* stream);
 
+/* Bytes of the per-device scratch array of moe_dispatch_permute_noalloc(). */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* A2 + A3 + A4a without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc.  The same as moe_send_counts(dedup = 0) followed by
+ * moe_dispatch_permute() on the same stream - the same outputs, bit for bit -
+ * except that the plan goes to a static scratch array of the library instead
+ * of a caller workspace: MOE_NOALLOC_SCRATCH_BYTES (8 MiB) of device memory
+ * that every GPU the library runs on holds from this call's first use on it
+ * until the process ends.  Nothing is allocated: no hipMalloc, hipFree or
+ * allocating library routine is called.
+ *   Arguments: those of moe_send_counts() (placement, the counts and offsets,
+ *   expert_offsets may be NULL) and moe_dispatch_permute() (x .. slot_row).
+ *   Every call on one GPU uses that GPU's one scratch array, which keeps the
+ *   last call's plan (nothing in it needs to start at zero): calls that can
+ *   overlap in time on one GPU - on streams not ordered with each other, or
+ *   from several host threads - race on it and must not be made.
+ * Errors: those of moe_send_counts() and moe_dispatch_permute();
+ *   MOE_EUNSUPPORTED when the plan, moe_workspace_bytes(tokens, n_experts,
+ *   top_k, n_ranks, 0) bytes, exceeds MOE_NOALLOC_SCRATCH_BYTES (about 34
+ *   bytes per token at 64 experts, top-6: some 250,000 tokens); MOE_EHIP when
+ *   the scratch's device address cannot be obtained or a launch fails. */
+int moe_dispatch_permute_noalloc(const void* x, const int32_t* topk_idx, const float* topk_gate,
+                                 int64_t tokens, int hidden_dim, int n_experts, int top_k,
+                                 int n_ranks, const int32_t* placement, int bytes_per_element,
+                                 int32_t* expert_counts, int32_t* rank_counts,
+                                 int32_t* rank_offsets, int32_t* expert_offsets, void* send,
+                                 int32_t* row_token, int32_t* row_expert, float* row_weight,
+                                 int32_t* slot_row, void* stream);
+
 /* A4b - deduplicating dispatch, one row per distinct (token, destination rank)
  * ([EC] "Method 1", deduplicating dispatcher).
  * Must follow moe_send_counts(dedup = 1), or moe_route_plan(dedup = 1), on the

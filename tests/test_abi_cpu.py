@@ -235,6 +235,36 @@ def test_receive_side_errors(lib):
     assert call(r, rb, rn, C=0) == 0                    # no-op
 
 
+def test_noalloc_errors(lib):
+    """The entry point that allocates nothing refuses, on the host, plans
+    larger than its scratch and the argument errors of the calls it stands for
+    (no HIP call is made in any of these cases)."""
+    f = lib.moe_dispatch_permute_noalloc
+    base = [FAKE, FAKE, FAKE, 4096, 2048, 64, 6, 16, None, 2, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+            FAKE, FAKE, FAKE, None]
+    names = ["x", "idx", "gate", "T", "H", "E", "k", "R", "place", "bpe", "ec", "rc", "ro", "eo",
+             "send", "rt", "re", "rw", "sr", "st"]
+
+    def call(**kw):
+        a = list(base)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return f(*a)
+
+    big = 300000                                  # plan of about 10 MB > 8 MiB of scratch
+    assert lib.moe_workspace_bytes(big, 64, 6, 16, 0) > (8 << 20)
+    assert lib.moe_workspace_bytes(200000, 64, 6, 16, 0) <= (8 << 20)
+    assert call(T=big) == EUNSUP
+    assert call(T=-1) == EINVAL
+    assert call(R=3) == EINVAL
+    assert call(k=17, E=64) == EUNSUP
+    assert call(bpe=3) == EUNSUP
+    assert call(H=4) == EUNSUP
+    assert call(ec=None) == EINVAL
+    assert call(send=None) == EINVAL
+    assert call(x=None) == EINVAL
+
+
 def test_product_path_does_not_touch_oracle():
     """The package sources never import, load or name the oracle."""
     pkg = os.path.join(ROOT, "combine_top_router_select_amd")
