@@ -41,8 +41,12 @@ stays out); `traffic` is the HBM bytes per launch that rocprofv3's FETCH_SIZE
 and WRITE_SIZE counters measured for that kernel (profiles/hbm_traffic_*.md,
 scaled by a plain-copy calibration), or null when there is no such record for
 the workload or the kernel's sources changed since.  `copy_reference` times a
-plain device copy of the same bytes the same way.  `cpu_baseline` times the CPU
-oracle on the same workload.
+plain device copy of the same bytes the same way; `hbm_ceiling` times
+hand-written reference kernels (pure read, pure write, copy, and the plain
+dispatch's own scatter without its plan and metadata) at the dispatch's sizes,
+the practical ceilings its rate is compared with.  `device` names the GPU
+(architecture, compute units, clocks).  `cpu_baseline` times the CPU oracle on
+the same workload.
 """
 from __future__ import annotations
 
@@ -157,6 +161,104 @@ def copy_reference(torch, nbytes, launches=100):
     del bufs
     return {"bytes_per_copy": 2 * half, "us": round(t * 1e6, 2),
             "GBps": round(2 * half / t / 1e9, 1)}
+
+
+def time_launches(torch, calls):
+    """Mean duration of one launch over a run of back-to-back launches (each a
+    (function, args) pair returning 0 on success), queued behind a GPU sleep
+    and bracketed by HIP events on the current stream."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)
+    e0.record()
+    for fn, args in calls:
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"{getattr(fn, '__name__', fn)} returned {rc}")
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / len(calls)
+
+
+def ceiling_lib():
+    import ctypes
+    from combine_top_router_select_amd.build import CEILING_LIB
+    L = ctypes.CDLL(CEILING_LIB)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.hbm_read.argtypes = [P, i64, P, P]
+    L.hbm_write.argtypes = [P, i64, P]
+    L.hbm_copy.argtypes = [P, P, i64, P]
+    L.hbm_scatter.argtypes = [P, P, i64, i32, i32, P, P]
+    L.hbm_device_info.argtypes = [P, P, P, P, ctypes.c_char_p, i32]
+    for f in ("hbm_read", "hbm_write", "hbm_copy", "hbm_scatter", "hbm_device_info"):
+        getattr(L, f).restype = i32
+    return L
+
+
+def device_info(torch):
+    """The GPU the run used: name, architecture, compute units, clocks."""
+    import ctypes
+    info = {"name": torch.cuda.get_device_name(0)}
+    try:
+        L = ceiling_lib()
+        cu, mclk, bus, clk = (ctypes.c_int(0) for _ in range(4))
+        arch = ctypes.create_string_buffer(64)
+        if L.hbm_device_info(ctypes.byref(cu), ctypes.byref(mclk), ctypes.byref(bus),
+                             ctypes.byref(clk), arch, 64) == 0:
+            info.update(arch=arch.value.decode(), compute_units=cu.value,
+                        mem_clock_MHz=round(mclk.value / 1e3), mem_bus_width_bits=bus.value,
+                        clock_MHz=round(clk.value / 1e3))
+    except OSError:
+        info["arch"] = getattr(torch.cuda.get_device_properties(0), "gcnArchName", None)
+    return info
+
+
+def hbm_ceiling(torch, sets, T, H, k, bpe, n_rows, dedup, launches=100):
+    """Practical HBM ceilings at the dispatch's sizes: hand-written reference
+    kernels (csrc/hbm_ceiling.hip) in the dispatch kernel's access pattern
+    (one wave per 4 KiB chunk, 16-byte accesses, nontemporal loads) without its
+    plan lookups and metadata, timed like the path's kernels (back-to-back
+    launches over rotated buffers, about 1.5 GB, so nothing is served from the
+    256 MB Infinity Cache):
+      read     a pure read of the dispatch's algorithmic bytes;
+      write    a pure write of them;
+      copy     half of them read and written elsewhere;
+      scatter  the plain dispatch's own data movement (each x row to its k
+               send rows, positions from the step's own slot_row), on the
+               bench's buffer sets (null for dedup, whose rows differ)."""
+    L = ceiling_lib()
+    st = torch.cuda.current_stream().cuda_stream
+    read_b, write_b = T * H * bpe, n_rows * H * bpe
+    total = (read_b + write_b) // 16 * 16
+    half = total // 2 // 16 * 16
+    nbuf = max(2, int(np.ceil(1.5e9 / total)))
+    bufs = [torch.empty(total, dtype=torch.uint8, device="cuda:0") for _ in range(nbuf)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda:0")
+    res = {}
+    t = time_launches(torch, [(L.hbm_read, (bufs[i % nbuf].data_ptr(), total, sink.data_ptr(),
+                                            st)) for i in range(launches)])
+    res["read"] = {"bytes": total, "us": round(t * 1e6, 2), "GBps": round(total / t / 1e9, 1)}
+    t = time_launches(torch, [(L.hbm_write, (bufs[i % nbuf].data_ptr(), total, st))
+                              for i in range(launches)])
+    res["write"] = {"bytes": total, "us": round(t * 1e6, 2), "GBps": round(total / t / 1e9, 1)}
+    t = time_launches(torch, [(L.hbm_copy, (bufs[i % nbuf].data_ptr(),
+                                            bufs[i % nbuf].data_ptr() + half, half, st))
+                              for i in range(launches)])
+    res["copy"] = {"bytes": 2 * half, "us": round(t * 1e6, 2),
+                   "GBps": round(2 * half / t / 1e9, 1)}
+    del bufs
+    if not dedup:
+        calls = [(L.hbm_scatter, (b.x.data_ptr(), b.disp["slot_row"].data_ptr(), T, H * bpe, k,
+                                  b.disp["send"].data_ptr(), st))
+                 for b in (sets[i % len(sets)] for i in range(launches))]
+        t = time_launches(torch, calls)
+        res["scatter"] = {"bytes": read_b + write_b, "us": round(t * 1e6, 2),
+                          "GBps": round((read_b + write_b) / t / 1e9, 1)}
+    else:
+        res["scatter"] = None
+    return res
 
 
 class BufferSet:
@@ -740,10 +842,16 @@ def main():
         "algorithmic_bytes": {"dispatch": disp_bytes, "combine": comb_bytes,
                               "metadata": meta_bytes},
         "copy_reference": copy_reference(torch, dom[2]),
-        "device": torch.cuda.get_device_name(0),
+        "device": device_info(torch),
         "hip_version": getattr(torch.version, "hip", None),
         "host_cores_available": len(os.sched_getaffinity(0)),
     }
+    ceil = hbm_ceiling(torch, sets, T, H, k, bpe, n_rows, dedup)
+    # the dispatch's achieved rate as a fraction of each reference rate
+    disp_gbps = disp_bytes / t_disp / 1e9
+    ceil["dispatch_frac_of"] = {name: round(disp_gbps / v["GBps"], 4)
+                                for name, v in ceil.items() if v is not None}
+    res["hbm_ceiling"] = ceil
     if recv is not None:
         res["receive"] = recv
     if a.search:

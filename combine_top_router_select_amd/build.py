@@ -1,4 +1,5 @@
-"""Build libmoe_route.so from csrc/*.hip for gfx950 with hipcc (in-tree).
+"""Build libmoe_route.so from csrc/*.hip for gfx950 with hipcc (in-tree), and
+libmoe_hbm_ceiling.so, the benchmark's reference kernels (bench.py only).
 
     python -m combine_top_router_select_amd.build [-D NAME=VALUE ...]
 
@@ -24,6 +25,8 @@ ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "route_topk.hip", "counts.hip", "dispatch.hip", "combine.hip",
            "coselect.hip", "placement.hip", "shuffle.hip", "noalloc.hip"]
+CEILING_SOURCES = ["hbm_ceiling.hip"]
+CEILING_LIB = os.path.join(PKG, "libmoe_hbm_ceiling.so")
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -35,6 +38,15 @@ COMMON_FLAGS = [
 
 
 def build(defines=(), out=LIB, verbose=False) -> str:
+    """Builds the library (and, for the in-tree library, the benchmark's
+    reference kernels next to it)."""
+    res = build_lib(SOURCES, out, defines, verbose)
+    if out == LIB:
+        build_lib(CEILING_SOURCES, CEILING_LIB, defines, verbose)
+    return res
+
+
+def build_lib(sources, out, defines=(), verbose=False) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     dflags = [f"-D{d}" for d in defines]
 
@@ -48,8 +60,8 @@ def build(defines=(), out=LIB, verbose=False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=min(len(sources), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(compile_one, sources))
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

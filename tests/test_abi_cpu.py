@@ -265,6 +265,24 @@ def test_noalloc_errors(lib):
     assert call(x=None) == EINVAL
 
 
+def test_ceiling_library_exports_and_checks():
+    """The benchmark's reference-kernel library loads without a GPU, exports
+    its entry points and rejects bad sizes before any launch."""
+    from combine_top_router_select_amd.build import CEILING_LIB
+    if not os.path.exists(CEILING_LIB):
+        pytest.fail(f"{CEILING_LIB} is not built")
+    raw = ctypes.CDLL(CEILING_LIB)
+    for n in ("hbm_read", "hbm_write", "hbm_copy", "hbm_scatter", "hbm_device_info"):
+        assert hasattr(raw, n), n
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    raw.hbm_copy.argtypes = [P, P, i64, P]
+    raw.hbm_scatter.argtypes = [P, P, i64, i32, i32, P, P]
+    assert raw.hbm_copy(FAKE, FAKE, 24, None) == 2       # not a multiple of 16
+    assert raw.hbm_copy(None, FAKE, 32, None) == 2
+    assert raw.hbm_scatter(FAKE, FAKE, 10, 24, 2, FAKE, None) == 2
+    assert raw.hbm_scatter(FAKE, FAKE, 10, 32, 0, FAKE, None) == 2
+
+
 def test_product_path_does_not_touch_oracle():
     """The package sources never import, load or name the oracle."""
     pkg = os.path.join(ROOT, "combine_top_router_select_amd")

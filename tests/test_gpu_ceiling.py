@@ -1,0 +1,69 @@
+"""The benchmark's reference kernels (libmoe_hbm_ceiling.so) move the data they
+are timed on: a copy is bit-identical, a scatter puts every row at its given
+positions, a write covers the whole range.  Not part of the method; checked so
+that the ceilings bench.py reports are real data movement."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bench
+    return bench.ceiling_lib()
+
+
+def test_copy_and_write(L):
+    n = (3 << 20) + 4096 + 48            # a ragged last chunk
+    st = torch.cuda.current_stream().cuda_stream
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.zeros(n + 4096, dtype=torch.uint8, device="cuda:0")
+    assert L.hbm_copy(src.data_ptr(), dst.data_ptr(), n, st) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src) and bool((dst[n:] == 0).all())
+    buf = torch.zeros(n + 4096, dtype=torch.uint8, device="cuda:0")
+    assert L.hbm_write(buf.data_ptr(), n, st) == 0
+    torch.cuda.synchronize()
+    words = host(buf[:n].view(torch.int32)).reshape(-1, 4)
+    lanes = np.arange(words.shape[0]) % 64
+    assert (words[:, 1] == lanes).all()       # every 16-byte vector written
+    assert bool((buf[n:] == 0).all())
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda:0")
+    assert L.hbm_read(src.data_ptr(), n, sink.data_ptr(), st) == 0
+    assert L.hbm_copy(src.data_ptr(), dst.data_ptr(), 8, st) == 2   # not a multiple of 16
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,row_bytes,k", [(100, 4096, 6), (37, 8192, 2), (64, 272, 8)])
+def test_scatter(L, T, row_bytes, k):
+    say(f"[ceiling scatter] T={T} row_bytes={row_bytes} k={k}")
+    rng = np.random.default_rng(T)
+    pos = rng.permutation(T * k).astype(np.int32).reshape(T, k)
+    x = torch.randint(0, 256, (T, row_bytes), dtype=torch.uint8, device="cuda:0")
+    dst = torch.zeros((T * k, row_bytes), dtype=torch.uint8, device="cuda:0")
+    p = torch.from_numpy(pos).to("cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    assert L.hbm_scatter(x.data_ptr(), p.data_ptr(), T, row_bytes, k, dst.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    xh, dh = host(x), host(dst)
+    for t in range(T):
+        for j in range(k):
+            assert (dh[pos[t, j]] == xh[t]).all()
+
+
+def test_device_info(L):
+    cu, mclk, bus, clk = (ctypes.c_int(0) for _ in range(4))
+    arch = ctypes.create_string_buffer(64)
+    assert L.hbm_device_info(ctypes.byref(cu), ctypes.byref(mclk), ctypes.byref(bus),
+                             ctypes.byref(clk), arch, 64) == 0
+    say(f"device: {arch.value.decode()} {cu.value} CUs, memory clock {mclk.value} kHz, "
+        f"bus {bus.value} bits, clock {clk.value} kHz")
+    assert arch.value.decode().startswith("gfx") and cu.value > 0
