@@ -78,6 +78,8 @@ __device__ __forceinline__ u32x4 keep_bytes(u32x4 v, int n) {
 //                    ranks in dedup mode); at most 64, the tile size
 //   lslot[T][k]      uint32: (position column << 8) | rank of (t, j) among the
 //                    tile's earlier tokens that use the same position column
+//   ctot[C]          int32: column totals (large plans, whose scan runs as two
+//                    many-workgroup kernels)
 //   bm[B][E]         uint64: bit i set when token i of the tile selects expert e
 //                    (written by the separate counting kernel; the co-selection
 //                    counts of the combined routing call read it)
@@ -93,6 +95,7 @@ struct PlanLayout {
   size_t base_off;    // byte offsets inside the workspace
   size_t tcnt_off;
   size_t lslot_off;
+  size_t ctot_off;
   size_t bm_off;
   size_t bytes;
 };
@@ -111,7 +114,8 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t tokens, int n_experts,
   p.base_off = 256;
   p.tcnt_off = align256(p.base_off + size_t(p.pos_cols) * size_t(p.groups) * 4);
   p.lslot_off = align256(p.tcnt_off + size_t(p.cols) * size_t(p.tiles_pad));
-  p.bm_off = align256(p.lslot_off + size_t(tokens) * size_t(top_k) * 4);
+  p.ctot_off = align256(p.lslot_off + size_t(tokens) * size_t(top_k) * 4);
+  p.bm_off = align256(p.ctot_off + size_t(p.cols) * 4);
   p.bytes = align256(p.bm_off + size_t(p.tiles) * size_t(n_experts) * 8);
   return p;
 }

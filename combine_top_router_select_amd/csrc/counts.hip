@@ -167,6 +167,123 @@ __device__ __forceinline__ int segment_incl_scan(int v, int Q, int lane) {
   return v;
 }
 
+// LDS of the column-order scan (order_columns), declared by its caller.
+template <bool RANKED>
+struct OrderLds {
+  int32_t scan[MOE_MAX_EXPERTS];  // exclusive scan by scan slot (RANKED)
+  int32_t wsum[kScanWaves];
+  uint64_t rmask[RANKED ? MOE_MAX_RANKS : 1][MOE_MAX_EXPERTS / kWave];
+  int32_t rcnt[MOE_MAX_RANKS];
+  int32_t rstart[MOE_MAX_RANKS];
+};
+
+// Clears the rank bitmaps and counts of L (RANKED); every thread calls it,
+// and a barrier must follow before order_columns.
+template <bool RANKED>
+__device__ __forceinline__ void order_init(OrderLds<RANKED>& L) {
+  if (!RANKED) return;
+  const int tid = threadIdx.x;
+  if (tid < MOE_MAX_RANKS) L.rcnt[tid] = 0;
+  for (int i = tid; i < MOE_MAX_RANKS * (MOE_MAX_EXPERTS / kWave); i += blockDim.x)
+    (&L.rmask[0][0])[i] = 0ull;
+}
+
+// The position columns in send-buffer order - expert id (plain, contiguous
+// placement), rank (dedup), or (rank, id) for plain dispatch with an explicit
+// placement (RANKED: a counting sort with rank bitmasks) - and one
+// block-wide exclusive scan (DPP wave scans) of their totals s_tot give each
+// position column's first row, s_colbase[0 .. CP).  With `outputs`, also the
+// counts, the offsets and the header.  Every thread of the workgroup calls it
+// after s_tot is complete and order_init's barrier; the workgroup has at least
+// max(CP, R) threads and, RANKED, at least E (my_rank: the rank of expert tid).
+// Returns the total number of rows.
+template <bool DEDUP, bool RANKED>
+__device__ int order_columns(const int32_t* s_tot, int32_t* s_colbase, OrderLds<RANKED>& L,
+                             int E, int R, int m, int my_rank, bool outputs,
+                             int32_t* __restrict__ expert_counts,
+                             int32_t* __restrict__ rank_counts,
+                             int32_t* __restrict__ rank_offsets,
+                             int32_t* __restrict__ expert_offsets,
+                             int32_t* __restrict__ header) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int cbase = DEDUP ? E : 0;  // first position column among the counted ones
+  const int CP = DEDUP ? R : E;     // position columns = scan slots
+  int key = tid;  // scan slot of expert tid (RANKED), else slot tid = column cbase + tid
+  if (RANKED) {
+    if (tid < E) {
+      atomicOr(reinterpret_cast<unsigned long long*>(&L.rmask[my_rank][tid / kWave]),
+               1ull << (tid % kWave));
+      atomicAdd(&L.rcnt[my_rank], 1);
+    }
+    __syncthreads();
+    if (w == 0) {
+      const int v = lane < R ? L.rcnt[lane] : 0;
+      const int incl = wave_incl_scan(v);
+      if (lane < R) L.rstart[lane] = incl - v;
+    }
+    __syncthreads();
+    if (tid < E) {
+      const uint64_t* mk = L.rmask[my_rank];
+      const int wi = tid / kWave;
+      int below = __popcll(mk[wi] & lanemask_lt());
+#pragma unroll
+      for (int qq = 0; qq < MOE_MAX_EXPERTS / kWave; ++qq) below += qq < wi ? __popcll(mk[qq]) : 0;
+      key = L.rstart[my_rank] + below;
+      L.scan[key] = s_tot[tid];
+    }
+    __syncthreads();
+  }
+  const int sv = tid < CP ? (RANKED ? L.scan[tid] : s_tot[cbase + tid]) : 0;
+  const int incl = wave_incl_scan(sv);
+  if (lane == kWave - 1) L.wsum[w] = incl;
+  __syncthreads();
+  int carry = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kScanWaves; ++i) {
+    const int x = i < nwaves ? L.wsum[i < nwaves ? i : 0] : 0;
+    carry += i < w ? x : 0;
+    total += x;
+  }
+  const int excl = carry + incl - sv;  // first row of scan slot tid
+  if (RANKED) {
+    __syncthreads();  // every L.scan read above is done
+    if (tid < CP) L.scan[tid] = excl;
+    __syncthreads();
+    if (tid < E) s_colbase[tid] = L.scan[key];
+  } else if (tid < CP) {
+    s_colbase[tid] = excl;
+  }
+  __syncthreads();
+  if (outputs) {
+    if (tid < E) expert_counts[tid] = s_tot[tid];
+    if (!DEDUP && expert_offsets && tid < E) expert_offsets[tid] = s_colbase[tid];
+    if (tid < R) {
+      int start, next;
+      if (DEDUP) {
+        start = s_colbase[tid];
+        next = start + s_tot[E + tid];
+      } else if (RANKED) {
+        const int s0 = L.rstart[tid], s1 = tid + 1 < R ? L.rstart[tid + 1] : E;
+        start = s0 < E ? L.scan[s0] : total;
+        next = s1 < E ? L.scan[s1] : total;
+      } else {
+        start = s_colbase[tid * m];
+        next = tid + 1 < R ? s_colbase[(tid + 1) * m] : total;
+      }
+      rank_offsets[tid] = start;
+      rank_counts[tid] = next - start;
+    }
+    if (tid == 0) {
+      rank_offsets[R] = total;
+      header[0] = total;
+    }
+  }
+  return total;
+}
+
 // One workgroup turns the per-tile counts into the plan's group bases: for
 // every position column and every group of 16 tiles (one 16-byte vector of
 // tile counts), the first row of that group in the send buffer.
@@ -190,19 +307,12 @@ plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, int E, 
                  int32_t* __restrict__ vbase) {
   __shared__ int32_t s_tot[kMaxCols];           // column totals
   __shared__ int32_t s_colbase[MOE_MAX_EXPERTS];  // first row of each position column
-  __shared__ int32_t s_scan[MOE_MAX_EXPERTS];     // exclusive scan by scan slot
-  __shared__ int32_t s_wsum[kScanWaves];
-  __shared__ uint64_t s_rmask[RANKED ? MOE_MAX_RANKS : 1][MOE_MAX_EXPERTS / kWave];
-  __shared__ int32_t s_rcnt[MOE_MAX_RANKS];
-  __shared__ int32_t s_rstart[MOE_MAX_RANKS];
+  __shared__ OrderLds<RANKED> s_ord;
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int w = tid / kWave;
   const int nthreads = blockDim.x;
-  const int nwaves = nthreads / kWave;
   const int C = E + (DEDUP ? R : 0);
   const int cbase = DEDUP ? E : 0;  // first position column among the counted ones
-  const int CP = DEDUP ? R : E;     // position columns = scan slots
   const int nvec = Bp / 16;         // 16-tile vectors per column
   const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);
 
@@ -245,85 +355,15 @@ plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, int E, 
     }
   }
   int my_rank = 0;
-  if (RANKED) {
-    if (tid < E) my_rank = clampi(place[tid], 0, R - 1);
-    if (tid < MOE_MAX_RANKS) s_rcnt[tid] = 0;
-    for (int i = tid; i < MOE_MAX_RANKS * (MOE_MAX_EXPERTS / kWave); i += nthreads)
-      (&s_rmask[0][0])[i] = 0ull;
-  }
+  if (RANKED && tid < E) my_rank = clampi(place[tid], 0, R - 1);
+  order_init<RANKED>(s_ord);
   __syncthreads();
 
-  // B. scan order and the block-wide scan
-  int key = tid;  // scan slot of expert tid (RANKED), else slot tid = column cbase + tid
-  if (RANKED) {
-    if (tid < E) {
-      atomicOr(reinterpret_cast<unsigned long long*>(&s_rmask[my_rank][tid / kWave]),
-               1ull << (tid % kWave));
-      atomicAdd(&s_rcnt[my_rank], 1);
-    }
-    __syncthreads();
-    if (w == 0) {
-      const int v = lane < R ? s_rcnt[lane] : 0;
-      const int incl = wave_incl_scan(v);
-      if (lane < R) s_rstart[lane] = incl - v;
-    }
-    __syncthreads();
-    if (tid < E) {
-      const uint64_t* mk = s_rmask[my_rank];
-      const int wi = tid / kWave;
-      int below = __popcll(mk[wi] & lanemask_lt());
-#pragma unroll
-      for (int qq = 0; qq < MOE_MAX_EXPERTS / kWave; ++qq) below += qq < wi ? __popcll(mk[qq]) : 0;
-      key = s_rstart[my_rank] + below;
-      s_scan[key] = s_tot[tid];
-    }
-    __syncthreads();
-  }
-  const int sv = tid < CP ? (RANKED ? s_scan[tid] : s_tot[cbase + tid]) : 0;
-  const int incl = wave_incl_scan(sv);
-  if (lane == kWave - 1) s_wsum[w] = incl;
-  __syncthreads();
-  int carry = 0, total = 0;
-#pragma unroll
-  for (int i = 0; i < kScanWaves; ++i) {
-    const int x = i < nwaves ? s_wsum[i < nwaves ? i : 0] : 0;
-    carry += i < w ? x : 0;
-    total += x;
-  }
-  const int excl = carry + incl - sv;  // first row of scan slot tid
-  if (RANKED) {
-    __syncthreads();  // every s_scan read above is done
-    if (tid < CP) s_scan[tid] = excl;
-    __syncthreads();
-    if (tid < E) s_colbase[tid] = s_scan[key];
-  } else if (tid < CP) {
-    s_colbase[tid] = excl;
-  }
-  __syncthreads();
+  // B. scan order, the block-wide scan, counts and offsets
+  order_columns<DEDUP, RANKED>(s_tot, s_colbase, s_ord, E, R, m, my_rank, true, expert_counts,
+                               rank_counts, rank_offsets, expert_offsets, header);
 
-  // C. outputs
-  if (tid < E) expert_counts[tid] = s_tot[tid];
-  if (!DEDUP && expert_offsets && tid < E) expert_offsets[tid] = s_colbase[tid];
-  if (tid < R) {
-    int start, next;
-    if (DEDUP) {
-      start = s_colbase[tid];
-      next = start + s_tot[E + tid];
-    } else if (RANKED) {
-      const int s0 = s_rstart[tid], s1 = tid + 1 < R ? s_rstart[tid + 1] : E;
-      start = s0 < E ? s_scan[s0] : total;
-      next = s1 < E ? s_scan[s1] : total;
-    } else {
-      start = s_colbase[tid * m];
-      next = tid + 1 < R ? s_colbase[(tid + 1) * m] : total;
-    }
-    rank_offsets[tid] = start;
-    rank_counts[tid] = next - start;
-  }
-  if (tid == 0) {
-    rank_offsets[R] = total;
-    header[0] = total;
-  }
+  // C. group bases
   if (KV > 0) {
     if (active && c >= cbase) {
       const int cb = s_colbase[c - cbase];
@@ -355,6 +395,116 @@ plan_scan_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int Q, int E, 
   }
 }
 
+// ----------------------------------------------- scan of large plans --
+//
+// Past kSplitVec vectors (16-tile groups) per column the one-workgroup scan
+// runs long (the receive-side plan of 98304 rows: 96 vectors in each of 128
+// columns).  There the scan runs as two kernels of many workgroups (measured
+// on that plan's 16384-token top-6 receive step: 844.8 -> 842.5 us; at 32
+// vectors, the 16384-token top-2 step, one workgroup stays faster, 265.3
+// against 266.8 us): the column totals
+// (one workgroup per column), then the bases (one workgroup per position
+// column): each of those orders the columns and scans their totals itself -
+// cheap, in LDS - and scans its own column's vectors; workgroup 0 also writes
+// the counts and offsets.  Same plan, bit for bit, still no global atomics.
+constexpr int kSplitVec = 32;
+constexpr int kColThreads = 256;
+
+// Sum over the workgroup (blockDim.x a multiple of 64, at most 1024); every
+// thread gets it.
+__device__ __forceinline__ int block_sum(int v, int32_t* s_w) {
+  const int lane = lane_id(), w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const int incl = wave_incl_scan(v);
+  __syncthreads();  // s_w may still be read by an earlier call
+  if (lane == kWave - 1) s_w[w] = incl;
+  __syncthreads();
+  int t = 0;
+  for (int i = 0; i < nw; ++i) t += s_w[i];
+  return t;
+}
+
+// Exclusive scan over the workgroup; *total gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int32_t* s_w, int* total) {
+  const int lane = lane_id(), w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const int incl = wave_incl_scan(v);
+  __syncthreads();
+  if (lane == kWave - 1) s_w[w] = incl;
+  __syncthreads();
+  int carry = 0, t = 0;
+  for (int i = 0; i < nw; ++i) {
+    carry += i < w ? s_w[i] : 0;
+    t += s_w[i];
+  }
+  *total = t;
+  return carry + incl - v;
+}
+
+// Column c = blockIdx.x: the sum of its tile counts.
+__global__ void __launch_bounds__(kColThreads)
+plan_colsum_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp,
+                   int32_t* __restrict__ ctot) {
+  __shared__ int32_t s_w[kColThreads / kWave];
+  const int c = blockIdx.x;
+  const int nvec = Bp / 16;
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt) + size_t(c) * nvec;
+  int sum = 0;
+  for (int v0 = 0; v0 < nvec; v0 += 4 * kColThreads) {
+    u32x4 t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = v0 + i * kColThreads + int(threadIdx.x);
+      t[i] = g4[v < nvec ? v : nvec - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = v0 + i * kColThreads + int(threadIdx.x);
+      sum += v < nvec ? byte_sum(keep_bytes(t[i], B - 16 * v)) : 0;
+    }
+  }
+  const int total = block_sum(sum, s_w);
+  if (threadIdx.x == 0) ctot[c] = total;
+}
+
+// Position column p = blockIdx.x: the first row of each of its 16-tile groups.
+template <bool DEDUP, bool RANKED>
+__global__ void __launch_bounds__(kScanThreads)
+plan_bases_kernel(const uint8_t* __restrict__ tcnt, int B, int Bp, int E, int R,
+                  const int32_t* __restrict__ place, int m, const int32_t* __restrict__ ctot,
+                  int32_t* __restrict__ expert_counts, int32_t* __restrict__ rank_counts,
+                  int32_t* __restrict__ rank_offsets, int32_t* __restrict__ expert_offsets,
+                  int32_t* __restrict__ header, int32_t* __restrict__ vbase) {
+  __shared__ int32_t s_tot[kMaxCols];
+  __shared__ int32_t s_colbase[MOE_MAX_EXPERTS];
+  __shared__ OrderLds<RANKED> s_ord;
+  __shared__ int32_t s_w[kScanWaves];
+  const int tid = threadIdx.x;
+  const int p = blockIdx.x;
+  const int C = E + (DEDUP ? R : 0);
+  const int cbase = DEDUP ? E : 0;
+  const int nvec = Bp / 16;
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt) + size_t(cbase + p) * nvec;
+  // this column's first vectors go out first
+  const u32x4 first = g4[tid < nvec ? tid : nvec - 1];
+  for (int c = tid; c < C; c += blockDim.x) s_tot[c] = ctot[c];
+  int my_rank = 0;
+  if (RANKED && tid < E) my_rank = clampi(place[tid], 0, R - 1);
+  order_init<RANKED>(s_ord);
+  __syncthreads();
+  order_columns<DEDUP, RANKED>(s_tot, s_colbase, s_ord, E, R, m, my_rank, p == 0,
+                               expert_counts, rank_counts, rank_offsets, expert_offsets, header);
+  int run = s_colbase[p];
+  int32_t* col = vbase + size_t(p) * nvec;
+  for (int v0 = 0; v0 < nvec; v0 += blockDim.x) {
+    const int v = v0 + tid;
+    const u32x4 t = v0 == 0 ? first : g4[v < nvec ? v : nvec - 1];
+    const int x = v < nvec ? byte_sum(keep_bytes(t, B - 16 * v)) : 0;
+    int total;
+    const int excl = block_excl_scan(x, s_w, &total);
+    if (v < nvec) col[v] = run + excl;
+    run += total;
+  }
+}
+
 // The scan of a plan whose tile counts (tcnt) are already in the workspace:
 // launched after tile_counts_kernel, or after the fused routing kernel.
 hipError_t launch_plan_scan(int64_t T, int E, int k, int R, const int32_t* place, int dedup,
@@ -371,6 +521,24 @@ hipError_t launch_plan_scan(int64_t T, int E, int k, int R, const int32_t* place
   const int nvec = Bp / 16;
   const int CP = pl.pos_cols;
   const bool ranked = !dedup && place != nullptr;
+  if (nvec > kSplitVec) {  // large plan: two kernels of many workgroups
+    int32_t* ctot = reinterpret_cast<int32_t*>(ws + pl.ctot_off);
+    hipLaunchKernelGGL(plan_colsum_kernel, dim3(unsigned(pl.cols)), dim3(kColThreads), 0, stream,
+                       tcnt, B, Bp, ctot);
+    int need = CP > R ? CP : R;
+    if (ranked) need = need > E ? need : E;
+    need = need > kColThreads ? need : kColThreads;
+    const int threads = (need + kWave - 1) / kWave * kWave;
+#define MOE_BASES(D, RK)                                                                      \
+  hipLaunchKernelGGL((plan_bases_kernel<D, RK>), dim3(unsigned(CP)), dim3(threads), 0, stream, \
+                     tcnt, B, Bp, E, R, place, m, ctot, expert_counts, rank_counts,            \
+                     rank_offsets, expert_offsets, header, vbase)
+    if (dedup) MOE_BASES(true, false);
+    else if (ranked) MOE_BASES(false, true);
+    else MOE_BASES(false, false);
+#undef MOE_BASES
+    return hipGetLastError();
+  }
   // lanes per column: a power of two <= 16 with every column's lanes in one
   // workgroup; then vectors per lane
   int Q = kMaxQ;
