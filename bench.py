@@ -3,8 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
                     [--receive] [--fp8] [--search] [--shuffle] [--streams {0,1,2,3,4}]
                     [--separate] [--graph] [--overlap] [--step-events]
-                    [--no-cpu-baseline] [--cpu-seconds S] [--footprint-gib G]
-                    [--calib-copy]
+                    [--no-cpu-baseline] [--no-reference] [--cpu-seconds S]
+                    [--footprint-gib G] [--calib-copy]
 
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input, with inputs resident in HBM: top-k routing, send counts,
@@ -66,7 +66,9 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 PKG = os.path.join(ROOT, "combine_top_router_select_amd")
 KERNEL_SOURCES = {"moe_dispatch_permute": "csrc/dispatch.hip",
                   "moe_dispatch_permute_dedup": "csrc/dispatch.hip",
-                  "moe_combine": "csrc/combine.hip"}
+                  "moe_combine": "csrc/combine.hip",
+                  "moe_expand_permute": "csrc/dispatch.hip",
+                  "moe_expand_reduce": "csrc/combine.hip"}
 METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak)"
 
 
@@ -108,6 +110,8 @@ def parse():
                    help="also record HIP events around the dispatch and combine launches of every "
                         "timed step (their in-step durations)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-reference", action="store_true",
+                   help="skip the copy_reference and hbm_ceiling legs (short profiler runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--footprint-gib", type=float, default=2.0,
                    help="total size of the rotated buffer sets")
@@ -413,8 +417,9 @@ def counter_traffic(kernel, workload, mode, dtype="bf16"):
                     continue
                 kv = dict(t.split("=", 1) for t in line.split()[1:])
                 if (kv.get("kernel"), kv.get("workload"), kv.get("dispatch"),
-                        kv.get("dtype", "bf16")) == (kernel, workload, mode, dtype):
-                    return int(kv["bytes"]) if kv.get("sources_sha256") == digest else None
+                        kv.get("dtype", "bf16"), kv.get("sources_sha256")) == \
+                        (kernel, workload, mode, dtype, digest):
+                    return int(kv["bytes"])
     return None
 
 
@@ -789,13 +794,16 @@ def main():
     dc_gbps = (disp_bytes + comb_bytes) / (t_disp + t_comb) / 1e9
     recv = None
     job_bytes = ab["job"]
+    mode, dt = ("dedup" if dedup else "nondedup"), ("fp8" if fp8 else "bf16")
     if receive:
         exp_bytes, red_bytes = ab["expand"], ab["reduce"]
         recv = {"expanded_rows": n_exp,
                 "expand_us": round(t_exp * 1e6, 2), "reduce_us": round(t_red * 1e6, 2),
                 "expand_GBps": round(exp_bytes / t_exp / 1e9, 1),
                 "reduce_GBps": round(red_bytes / t_red / 1e9, 1),
-                "algorithmic_bytes": {"expand": exp_bytes, "reduce": red_bytes}}
+                "algorithmic_bytes": {"expand": exp_bytes, "reduce": red_bytes},
+                "traffic": {"expand": counter_traffic("moe_expand_permute", w.name, mode, dt),
+                            "reduce": counter_traffic("moe_expand_reduce", w.name, mode, dt)}}
 
     res = {
         "metric": METRIC,
@@ -821,8 +829,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": counter_traffic(dom[0], w.name, "dedup" if dedup else "nondedup",
-                                                "fp8" if fp8 else "bf16"),
+                     "traffic": counter_traffic(dom[0], w.name, mode, dt),
                      "algorithmic_bytes": dom[2]},
         "dispatch_us": round(t_disp * 1e6, 2),
         "in_step_event_us": in_step or None,
@@ -841,17 +848,18 @@ def main():
         "self_rank_share": round(int(b.cnt["rank_counts"][0].item()) / n_rows, 4),
         "algorithmic_bytes": {"dispatch": disp_bytes, "combine": comb_bytes,
                               "metadata": meta_bytes},
-        "copy_reference": copy_reference(torch, dom[2]),
+        "copy_reference": None if a.no_reference else copy_reference(torch, dom[2]),
         "device": device_info(torch),
         "hip_version": getattr(torch.version, "hip", None),
         "host_cores_available": len(os.sched_getaffinity(0)),
     }
-    ceil = hbm_ceiling(torch, sets, T, H, k, bpe, n_rows, dedup)
-    # the dispatch's achieved rate as a fraction of each reference rate
-    disp_gbps = disp_bytes / t_disp / 1e9
-    ceil["dispatch_frac_of"] = {name: round(disp_gbps / v["GBps"], 4)
-                                for name, v in ceil.items() if v is not None}
-    res["hbm_ceiling"] = ceil
+    if not a.no_reference:
+        ceil = hbm_ceiling(torch, sets, T, H, k, bpe, n_rows, dedup)
+        # the dispatch's achieved rate as a fraction of each reference rate
+        disp_gbps = disp_bytes / t_disp / 1e9
+        ceil["dispatch_frac_of"] = {name: round(disp_gbps / v["GBps"], 4)
+                                    for name, v in ceil.items() if v is not None}
+        res["hbm_ceiling"] = ceil
     if recv is not None:
         res["receive"] = recv
     if a.search:
