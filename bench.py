@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
                     [--receive] [--fp8] [--search] [--shuffle] [--streams {0,1,2,3,4}]
-                    [--separate] [--graph] [--overlap] [--step-events]
+                    [--separate] [--graph] [--overlap] [--coselect-in {dispatch,route}]
+                    [--step-events]
                     [--no-cpu-baseline] [--no-reference] [--cpu-seconds S]
                     [--footprint-gib G] [--calib-copy]
 
@@ -23,6 +24,12 @@ kernels stay in order on its stream.  Larger batches run on one stream.  The
 same K steps are then timed on the other setting and reported as
 `other_streams`; --streams n fixes the setting.  --overlap instead forks only the co-selection
 counts onto a second stream inside each step.
+
+The co-selection counts (of the workload's first tokens) are taken by default
+in the dispatch launch, from the expert bitmaps of the plan, in workgroups that
+run beside the row copies; --coselect-in route takes them in the routing call
+instead (fused routing: one short kernel more; --separate: the stand-alone
+co-selection kernel at the end of the step).
 
 The timed steps call the C ABI directly with arguments marshalled once per
 buffer set (the Python binding's per-call checks would otherwise cost about
@@ -106,6 +113,8 @@ def parse():
     p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     p.add_argument("--overlap", action="store_true",
                    help="run the co-selection counts on a second stream")
+    p.add_argument("--coselect-in", choices=("dispatch", "route"), default="dispatch",
+                   help="the call that takes the co-selection counts (without --overlap)")
     p.add_argument("--step-events", action="store_true",
                    help="also record HIP events around the dispatch and combine launches of every "
                         "timed step (their in-step durations)")
@@ -325,17 +334,20 @@ class BufferSet:
         return tot
 
 
-def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True):
-    """One pass of the hot path.  With a side stream, the co-selection counts run
-    there, after the routing and concurrently with the rest.  With `receive`
-    (dedup mode), the dedup rows are expanded per expert, passed through
-    identity experts, reduced back to one row per received row, and those rows
-    are combined with weight 1."""
+def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True, cs_in="dispatch"):
+    """One pass of the hot path.  The co-selection counts go with the dispatch
+    (cs_in "dispatch") or the routing ("route") call, or with a side stream
+    they run there, after the routing and concurrently with the rest.  With
+    `receive` (dedup mode), the dedup rows are expanded per expert, passed
+    through identity experts, reduced back to one row per received row, and
+    those rows are combined with weight 1."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
     main = torch.cuda.current_stream()
-    if fused:   # co-selection counts folded in unless they run on the side stream
+    cs_route = side is None and cs_in == "route"
+    cs_disp = side is None and cs_in == "dispatch"
+    if fused:
         c = ops.moe_route_plan(b.logits, k, R, b.place, dedup, topk_idx=b.idx, topk_gate=b.gate,
-                               ws=b.ws, out=b.cnt, coselect=None if side is not None else b.W,
+                               ws=b.ws, out=b.cnt, coselect=b.W if cs_route else None,
                                coselect_tokens=w.coselect_tokens)[2]
     else:
         ops.moe_route_topk(b.logits, k, b.idx, b.gate)
@@ -348,7 +360,8 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True):
     if not fused:
         c = ops.moe_send_counts(b.idx, E, R, b.place, dedup, ws=b.ws, out=b.cnt)
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-    d = f(b.x, b.idx, b.gate, E, R, c["ws"], out=b.disp)
+    d = f(b.x, b.idx, b.gate, E, R, c["ws"], out=b.disp, coselect=b.W if cs_disp else None,
+          coselect_tokens=w.coselect_tokens)
     if receive:
         ops.moe_expand_counts(d["row_experts"], d["n_rows"], E, R, b.place, ws=b.ews, out=b.ecnt)
         ex = ops.moe_expand_permute(d["send"], d["row_gates"], d["n_rows"], E, R, b.ews,
@@ -360,7 +373,7 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True):
         ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b.out)
     if side is not None:
         main.wait_event(b.ev_coselected)
-    elif not fused:
+    elif cs_route and not fused:
         ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W)
 
 
@@ -423,7 +436,8 @@ def counter_traffic(kernel, workload, mode, dtype="bf16"):
     return None
 
 
-def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True, stream=None):
+def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True, stream=None,
+                   cs_in="dispatch"):
     """The C-ABI calls of one step on buffer set b, with every argument
     marshalled once: the timed loop then costs a few microseconds of host time
     per step instead of the Python binding's checks.  With a side stream the
@@ -438,7 +452,8 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
     cargs = (int(dedup), p(c["expert_counts"]), p(c["rank_counts"]), p(c["rank_offsets"]),
              p(c.get("expert_offsets")))
     wsargs = (p(b.ws), b.ws.numel(), st)
-    ncs = w.coselect_tokens if side is None else 0
+    ncs = w.coselect_tokens if side is None and cs_in == "route" else 0
+    dcs = w.coselect_tokens if side is None and cs_in == "dispatch" else 0
     if fused:
         calls = [(L.moe_route_plan, (p(b.logits), T, E, k, 0, R, p(b.place), *cargs[:1],
                                      p(b.idx), p(b.gate), *cargs[1:], ncs,
@@ -464,12 +479,13 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
         calls.append((L.moe_dispatch_permute_dedup, (
             p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, bpe, p(b.ws), b.ws.numel(),
             p(d["send"]), p(d["row_token"]), p(d["row_experts"]), p(d["row_gates"]),
-            p(d["row_weight"]), p(d["slot_row"]), p(d["n_rows"]), st)))
+            p(d["row_weight"]), p(d["slot_row"]), p(d["n_rows"]), dcs,
+            p(b.W) if dcs else None, st)))
     else:
         calls.append((L.moe_dispatch_permute, (
             p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, bpe, p(b.ws), b.ws.numel(),
             p(d["send"]), p(d["row_token"]), p(d["row_expert"]), p(d["row_weight"]),
-            p(d["slot_row"]), st)))
+            p(d["slot_row"]), dcs, p(b.W) if dcs else None, st)))
     if receive:
         ec, x = b.ecnt, b.exp
         calls += [
@@ -489,7 +505,7 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
                                       k, bpe, p(b.out), st)))
     if side is not None:
         calls.append((join, ()))
-    elif not fused:
+    elif not fused and ncs:
         calls.append((L.moe_coselect_counts, (p(b.idx), w.coselect_tokens, E, k, p(b.W), st)))
     return calls
 
@@ -644,13 +660,13 @@ def main():
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for b in sets:       # warm the code paths once outside capture
-                gpu_step(torch, ops, b, w, dedup, side, receive, fused)
+                gpu_step(torch, ops, b, w, dedup, side, receive, fused, a.coselect_in)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         for b in sets:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                gpu_step(torch, ops, b, w, dedup, side, receive, fused)
+                gpu_step(torch, ops, b, w, dedup, side, receive, fused, a.coselect_in)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -662,7 +678,7 @@ def main():
 
         def raw_sets(ns):
             return [raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side, fused,
-                                   streams[i % ns]) for i, b in enumerate(sets)]
+                                   streams[i % ns], a.coselect_in) for i, b in enumerate(sets)]
         raw = raw_sets(n_streams)
         if side is None and not a.step_events:
             raw_other = raw_sets(1 if n_streams > 1 else 2)
@@ -689,11 +705,11 @@ def main():
                 if rc != 0:
                     raise ops.MoeError(rc, name)
         else:
-            gpu_step(torch, ops, sets[i % nsets], w, dedup, side, receive, fused)
+            gpu_step(torch, ops, sets[i % nsets], w, dedup, side, receive, fused, a.coselect_in)
 
     for i in range(a.warmup):
         if i == 0 and graphs is None:   # once through the Python binding, with its checks
-            gpu_step(torch, ops, sets[0], w, dedup, side, receive, fused)
+            gpu_step(torch, ops, sets[0], w, dedup, side, receive, fused, a.coselect_in)
         else:
             step(i)
     torch.cuda.synchronize()
@@ -731,20 +747,23 @@ def main():
     order = [sets[(a.warmup + a.steps + i) % nsets] for i in range(K2)]
     L, st = ops.lib(), torch.cuda.current_stream().cuda_stream
     disp_calls, comb_calls = [], []
+    dcs = w.coselect_tokens if side is None and a.coselect_in == "dispatch" else 0
     for b in order:
         d = b.disp
+        wp = b.W.data_ptr() if dcs else None
         if dedup:
             disp_calls.append((L.moe_dispatch_permute_dedup, (
                 b.x.data_ptr(), b.idx.data_ptr(), b.gate.data_ptr(), T, H, E, k, R, bpe,
                 b.ws.data_ptr(), b.ws.numel(), d["send"].data_ptr(), d["row_token"].data_ptr(),
                 d["row_experts"].data_ptr(), d["row_gates"].data_ptr(),
-                d["row_weight"].data_ptr(), d["slot_row"].data_ptr(), d["n_rows"].data_ptr(), st)))
+                d["row_weight"].data_ptr(), d["slot_row"].data_ptr(), d["n_rows"].data_ptr(),
+                dcs, wp, st)))
         else:
             disp_calls.append((L.moe_dispatch_permute, (
                 b.x.data_ptr(), b.idx.data_ptr(), b.gate.data_ptr(), T, H, E, k, R, bpe,
                 b.ws.data_ptr(), b.ws.numel(), d["send"].data_ptr(), d["row_token"].data_ptr(),
                 d["row_expert"].data_ptr(), d["row_weight"].data_ptr(),
-                d["slot_row"].data_ptr(), st)))
+                d["slot_row"].data_ptr(), dcs, wp, st)))
         comb_calls.append((L.moe_combine, (
             d["send"].data_ptr(), d["row_weight"].data_ptr(), d["slot_row"].data_ptr(), T, H, k,
             bpe, b.out.data_ptr(), st)))
@@ -823,7 +842,7 @@ def main():
                    "dispatch": "dedup" if dedup else "nondedup", "receive_side": receive,
                    "routing": "fused" if fused else "separate",
                    "bytes_per_element": bpe, "graph": bool(a.graph),
-                   "coselect_stream": "side" if a.overlap else "main",
+                   "coselect": "side_stream" if a.overlap else a.coselect_in + "_call",
                    "streams": n_streams,
                    "buffer_sets": nsets, "footprint_MiB": round(nsets * per_set / 2 ** 20)},
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(achieved, 1),

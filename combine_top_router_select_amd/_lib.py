@@ -47,9 +47,9 @@ def lib():
         L.moe_route_plan.argtypes = [P, i64, i32, i32, i32, i32, P, i32, P, P, P, P, P, P, i64,
                                      P, P, sz, P]
         L.moe_dispatch_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, sz, P, P,
-                                           P, P, P, P]
+                                           P, P, P, i64, P, P]
         L.moe_dispatch_permute_dedup.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, sz,
-                                                 P, P, P, P, P, P, P, P]
+                                                 P, P, P, P, P, P, P, i64, P, P]
         L.moe_dispatch_permute_noalloc.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i32, P,
                                                    P, P, P, P, P, P, P, P, P]
         L.moe_combine.argtypes = [P, P, P, i64, i32, i32, i32, P, P]

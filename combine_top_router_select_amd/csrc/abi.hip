@@ -14,7 +14,7 @@ hipError_t launch_send_counts(const int32_t*, int64_t, int, int, int, const int3
                               int32_t*, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
 hipError_t launch_dispatch(const void*, const int32_t*, const float*, int64_t, int, int, int,
                            int, const void*, int, void*, int32_t*, int32_t*, float*, float*,
-                           int32_t*, int32_t*, hipStream_t);
+                           int32_t*, int32_t*, int64_t, int32_t*, hipStream_t);
 hipError_t launch_combine(const void*, const float*, const int32_t*, int64_t, int, int, int,
                           const int32_t*, void*, hipStream_t);
 hipError_t launch_expand_counts(const int32_t*, int64_t, int, int, int, const int32_t*,
@@ -153,12 +153,13 @@ MOE_API int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const f
                                  int n_ranks, int bytes_per_element, const void* workspace,
                                  size_t workspace_bytes, void* send, int32_t* row_token,
                                  int32_t* row_expert, float* row_weight, int32_t* slot_row,
-                                 void* stream) {
+                                 int64_t coselect_tokens, int32_t* coselect, void* stream) {
   int st = check_tek(tokens, n_experts, top_k);
   if (st != MOE_OK) return st;
   if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
   if ((st = check_rows(hidden_dim, bytes_per_element)) != MOE_OK) return st;
   if (!workspace) return MOE_EINVAL;
+  if (coselect && (coselect_tokens < 0 || coselect_tokens > tokens)) return MOE_EINVAL;
   if (workspace_bytes < moe_workspace_bytes(tokens, n_experts, top_k, n_ranks, 0))
     return MOE_EWORKSPACE;
   if (tokens == 0) return MOE_OK;
@@ -169,6 +170,7 @@ MOE_API int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const f
                                          hidden_dim * bytes_per_element, n_experts, top_k,
                                          n_ranks, workspace, 0, send, row_token,
                                          row_expert, nullptr, row_weight, slot_row, nullptr,
+                                         coselect ? coselect_tokens : 0, coselect,
                                          as_stream(stream)));
 }
 
@@ -179,12 +181,14 @@ MOE_API int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx,
                                        size_t workspace_bytes, void* send, int32_t* row_token,
                                        int32_t* row_experts, float* row_gates,
                                        float* row_weight, int32_t* slot_row, int32_t* n_rows,
+                                       int64_t coselect_tokens, int32_t* coselect,
                                        void* stream) {
   int st = check_tek(tokens, n_experts, top_k);
   if (st != MOE_OK) return st;
   if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
   if ((st = check_rows(hidden_dim, bytes_per_element)) != MOE_OK) return st;
   if (!workspace || !n_rows) return MOE_EINVAL;
+  if (coselect && (coselect_tokens < 0 || coselect_tokens > tokens)) return MOE_EINVAL;
   if (workspace_bytes < moe_workspace_bytes(tokens, n_experts, top_k, n_ranks, 1))
     return MOE_EWORKSPACE;
   if (tokens > 0 && (!x || !topk_idx || !topk_gate || !send || !row_token || !row_experts ||
@@ -194,6 +198,7 @@ MOE_API int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx,
                                          hidden_dim * bytes_per_element, n_experts, top_k,
                                          n_ranks, workspace, 1, send, row_token,
                                          row_experts, row_gates, row_weight, slot_row, n_rows,
+                                         coselect ? coselect_tokens : 0, coselect,
                                          as_stream(stream)));
 }
 

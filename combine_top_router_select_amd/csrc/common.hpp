@@ -9,7 +9,25 @@
 namespace moe {
 
 constexpr int kWave = 64;          // CDNA wavefront width
-constexpr int kTile = 64;          // tokens per counting tile (one lane per token)
+// Tokens per plan tile, one routing workgroup (16, 32 or 64 compile).  Measured
+// at 4096 tokens, top-6 of 64, one stream, per step: 16 -> 44.6 us, 32 -> 44.0,
+// 64 -> 44.75; with two streams 40.7, 40.0, 39.9.  Smaller tiles spread the
+// routing over more CUs (at 16: 3.26 us per call against 3.36 at 32 and 4.30
+// at 64) but give the dispatch 2x / 4x more plan entries to look up, which
+// costs it 0.15 / 0.5 us.
+constexpr int kTile = 32;
+constexpr int kWaveTile = 64;      // tokens per counting wave and per co-selection bitmap
+constexpr int kTilesPerWave = kWaveTile / kTile;
+static_assert(kTile == 16 || kTile == 32 || kTile == 64, "plan tiles of 16, 32 or 64 tokens");
+
+// A bitmap of one plan tile's tokens, and the piece of a 64-token co-selection
+// bitmap that one tile fills.
+template <int N> struct TileBits;
+template <> struct TileBits<16> { typedef uint32_t mask; typedef uint16_t piece; };
+template <> struct TileBits<32> { typedef uint32_t mask; typedef uint32_t piece; };
+template <> struct TileBits<64> { typedef uint64_t mask; typedef uint64_t piece; };
+typedef TileBits<kTile>::mask TileMask;
+typedef TileBits<kTile>::piece TilePiece;
 constexpr uint32_t kNoSlot = 0xFFFFFFFFu;  // plan code of an empty slot (received rows)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -67,9 +85,10 @@ __device__ __forceinline__ u32x4 keep_bytes(u32x4 v, int n) {
   return r;
 }
 
-// Plan written by moe_send_counts, read by the dispatch kernels.  Per-column
-// arrays are column-major with the tile index padded to Bp = roundup(B, 16), so
-// that a column's tile counts come in 16-byte vectors of 16 tiles.
+// Plan written by moe_send_counts, read by the dispatch kernels.  A plan tile
+// is kTile consecutive tokens.  Per-column arrays are column-major with the tile
+// index padded to Bp = roundup(B, 16), so that a column's tile counts come in
+// 16-byte vectors of 16 tiles.
 //   header[0]        total rows (N, or D in dedup mode)
 //   gbase[CP][Bp/16] int32: first row, in the send buffer, of each group of 16
 //                    tiles of position column c (the expert in plain mode, the
@@ -80,18 +99,19 @@ __device__ __forceinline__ u32x4 keep_bytes(u32x4 v, int n) {
 //                    tile's earlier tokens that use the same position column
 //   ctot[C]          int32: column totals (large plans, whose scan runs as two
 //                    many-workgroup kernels)
-//   bm[B][E]         uint64: bit i set when token i of the tile selects expert e
-//                    (written by the separate counting kernel; the co-selection
-//                    counts of the combined routing call read it)
+//   bm[BW][E]        uint64, BW = ceil(T / 64): bit i set when token i of the
+//                    64-token block selects expert e (written by both counting
+//                    paths, read by the co-selection counts)
 // The row of (t, j) is gbase[c][b / 16] + (counts of tiles 16 (b / 16) .. b - 1
-// in column c) + rank, with b = t / 64.
+// in column c) + rank, with b = t / kTile.
 struct PlanLayout {
-  int64_t tiles;      // B = ceil(T / 64)
+  int64_t tiles;      // B = ceil(T / kTile)
   int64_t tiles_pad;  // Bp = roundup(B, 16)
   int64_t groups;     // Bp / 16
   int cols;           // C: columns counted per tile (experts, + ranks in dedup mode)
   int pos_cols;       // CP: position columns (experts, or ranks in dedup mode)
   int cbase;          // tcnt column of position column 0 (E in dedup mode, else 0)
+  int64_t bm_tiles;   // BW = ceil(T / 64): 64-token blocks of the expert bitmaps
   size_t base_off;    // byte offsets inside the workspace
   size_t tcnt_off;
   size_t lslot_off;
@@ -111,12 +131,13 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t tokens, int n_experts,
   p.cols = n_experts + (dedup ? n_ranks : 0);
   p.pos_cols = dedup ? n_ranks : n_experts;
   p.cbase = dedup ? n_experts : 0;
+  p.bm_tiles = (tokens + kWaveTile - 1) / kWaveTile;
   p.base_off = 256;
   p.tcnt_off = align256(p.base_off + size_t(p.pos_cols) * size_t(p.groups) * 4);
   p.lslot_off = align256(p.tcnt_off + size_t(p.cols) * size_t(p.tiles_pad));
   p.ctot_off = align256(p.lslot_off + size_t(tokens) * size_t(top_k) * 4);
   p.bm_off = align256(p.ctot_off + size_t(p.cols) * 4);
-  p.bytes = align256(p.bm_off + size_t(p.tiles) * size_t(n_experts) * 8);
+  p.bytes = align256(p.bm_off + size_t(p.bm_tiles) * size_t(n_experts) * 8);
   return p;
 }
 

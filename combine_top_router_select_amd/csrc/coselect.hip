@@ -26,6 +26,7 @@
 // E = 64 case has only 10 tiles); there is no intermediate buffer in global
 // memory.
 #include "common.hpp"
+#include "coselect_bm.hpp"
 
 namespace moe {
 
@@ -168,74 +169,19 @@ hipError_t launch_coselect(const int32_t* idx, int64_t n, int E, int k, int32_t*
   return hipGetLastError();
 }
 
-// Co-selection counts from the per-tile expert bitmaps that the counting
-// kernel leaves in the plan workspace: W[a][b] += sum over the first `ntiles`
-// tiles of popcount(bm[t][a] & bm[t][b]), the last tile masked to the tokens
-// below cs_tokens.  A bit-matrix product with a short inner dimension: one
-// workgroup per 16 x 16 block of W and chunk of kBmChunk tiles stages the
-// block's 16 + 16 bitmap columns of the chunk in LDS (each bitmap is read by
-// E / 16 workgroups instead of E), then thread (a, b) of the block sums its
-// popcounts.  With one chunk every W entry has one owner and is added with a
-// plain read-modify-write; with several, with an integer atomic.
-constexpr int kBmBlk = 16;    // W block edge
-constexpr int kBmChunk = 64;  // tiles per workgroup
-
-__global__ void __launch_bounds__(256)
-coselect_bm_kernel(const uint64_t* __restrict__ bm, int64_t ntiles, uint64_t last_mask, int E,
-                   int nblk, int32_t* __restrict__ W) {
-  __shared__ uint64_t s_a[kBmChunk][kBmBlk];
-  __shared__ uint64_t s_b[kBmChunk][kBmBlk];
-  const int tid = threadIdx.x;
-  const int a0 = (int(blockIdx.x) / nblk) * kBmBlk;
-  const int b0 = (int(blockIdx.x) % nblk) * kBmBlk;
-  const int ai = tid / kBmBlk, bi = tid % kBmBlk;
-  uint32_t acc = 0;
-  for (int64_t t0 = int64_t(blockIdx.y) * kBmChunk; t0 < ntiles;
-       t0 += int64_t(gridDim.y) * kBmChunk) {
-    // stage: 64 tiles x 16 columns of each side, four 8-byte loads per thread
-    // per side (16 consecutive columns of one tile are 128 contiguous bytes)
-    uint64_t va[kBmChunk * kBmBlk / 256], vb[kBmChunk * kBmBlk / 256];
-#pragma unroll
-    for (int i = 0; i < kBmChunk * kBmBlk / 256; ++i) {
-      const int q = tid + 256 * i;
-      int64_t t = t0 + q / kBmBlk;
-      t = t < ntiles ? t : ntiles - 1;
-      const int ca = a0 + q % kBmBlk, cb = b0 + q % kBmBlk;
-      va[i] = bm[t * E + (ca < E ? ca : E - 1)];
-      vb[i] = bm[t * E + (cb < E ? cb : E - 1)];
-    }
-    __syncthreads();  // the previous chunk's reads of s_a / s_b are done
-#pragma unroll
-    for (int i = 0; i < kBmChunk * kBmBlk / 256; ++i) {
-      const int q = tid + 256 * i;
-      const int64_t t = t0 + q / kBmBlk;
-      const uint64_t m = t < ntiles - 1 ? ~0ull : (t == ntiles - 1 ? last_mask : 0ull);
-      s_a[q / kBmBlk][q % kBmBlk] = va[i] & m;
-      s_b[q / kBmBlk][q % kBmBlk] = vb[i];
-    }
-    __syncthreads();
-#pragma unroll 16
-    for (int t = 0; t < kBmChunk; ++t) acc += uint32_t(__popcll(s_a[t][ai] & s_b[t][bi]));
-  }
-  const int a = a0 + ai, b = b0 + bi;
-  if (a < E && b < E && acc != 0) {
-    int32_t* w = &W[int64_t(a) * E + b];
-    if (gridDim.y == 1) *w += int32_t(acc);  // the only owner of this entry
-    else atomicAdd(w, int32_t(acc));
-  }
+// Co-selection counts from the 64-token expert bitmaps of a plan (see
+// coselect_bm.hpp): one workgroup per 16 x 16 block of W and chunk of blocks.
+__global__ void __launch_bounds__(kBmThreads) coselect_bm_kernel(CoselectBm a) {
+  __shared__ uint64_t s_lds[kBmLdsBytes / sizeof(uint64_t)];
+  coselect_bm_block(a, blockIdx.x, s_lds);
 }
 
 hipError_t launch_coselect_bm(const uint64_t* bm, int64_t cs_tokens, int E, int32_t* W,
                               hipStream_t stream) {
   if (cs_tokens <= 0) return hipSuccess;
-  const int64_t ntiles = (cs_tokens + kTile - 1) / kTile;
-  const int rem = int(cs_tokens - (ntiles - 1) * kTile);  // tokens of the last tile, 1..64
-  const uint64_t last_mask = rem >= kTile ? ~0ull : ((1ull << rem) - 1ull);
-  const int nblk = (E + kBmBlk - 1) / kBmBlk;
-  int64_t chunks = (ntiles + kBmChunk - 1) / kBmChunk;
-  chunks = chunks < 65535 ? chunks : 65535;
-  hipLaunchKernelGGL(coselect_bm_kernel, dim3(unsigned(nblk * nblk), unsigned(chunks)), dim3(256),
-                     0, stream, bm, ntiles, last_mask, E, nblk, W);
+  const CoselectBm a = coselect_bm_args(bm, cs_tokens, E, W);
+  hipLaunchKernelGGL(coselect_bm_kernel, dim3(unsigned(a.blocks())), dim3(kBmThreads), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

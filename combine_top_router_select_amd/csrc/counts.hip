@@ -8,22 +8,23 @@
 // "Method 1": the deduplicating dispatcher sends one row per distinct
 // (token, destination rank).
 //
-// Counting a 64-token tile (one wave, one lane per token): every column
-// (expert; in dedup mode also rank) gets a 64-bit LDS bitmap of the tile's
-// tokens that use it, built with ds_or_b64 (order independent).  popcount of
-// the bits below a lane is the token's rank among the tile's earlier users of
-// the column; popcount of the whole bitmap is the tile's count.  The tile
-// counts are then scanned over tiles, per column, into the absolute first row
-// of each tile in each column.  A row's position is the first row of the
-// tile's 16-tile group in its column (written by the scan) + the counts of the
-// group's earlier tiles (summed by the dispatch kernel) + rank,
-// which makes the send buffer order (rank, expert, token) - or (rank, token) -
-// stable and deterministic.  No global atomics anywhere.
+// Counting 64 tokens (one wave, one lane per token), i.e. 64 / kTile plan
+// tiles: every column (expert; in dedup mode also rank) gets a 64-bit LDS
+// bitmap of the tokens that use it, built with ds_or_b64 (order independent).
+// popcount of the bits of a lane's own tile below the lane is the token's rank
+// among its tile's earlier users of the column; popcount of a tile's bits is
+// its count.  The tile counts are then scanned over tiles,
+// per column, into the absolute first row of each tile in each column.  A
+// row's position is the first row of the tile's 16-tile group in its column
+// (written by the scan) + the counts of the group's earlier tiles (summed by
+// the dispatch kernel) + rank, which makes the send buffer order
+// (rank, expert, token) - or (rank, token) - stable and deterministic.  No
+// global atomics anywhere.
 //
-// Two kernels: tile_counts (one wave per tile, so the per-assignment work and
-// its memory traffic spread over many CUs) and plan_scan (one workgroup, which
-// only reads the per-tile counts, one byte each, and writes the bases).  Both
-// per-tile arrays are column-major, so a scan thread streams a run of one
+// Two kernels: tile_counts (one wave per 64 tokens, so the per-assignment work
+// and its memory traffic spread over many CUs) and plan_scan (one workgroup,
+// which only reads the per-tile counts, one byte each, and writes the bases).
+// Both per-tile arrays are column-major, so a scan thread streams a run of one
 // column's tiles with 16-byte loads and stores.
 //
 // All global loads are issued unconditionally from clamped, in-bounds
@@ -58,12 +59,13 @@ __device__ __forceinline__ void load_tile_ids(int (&raw)[KMAX], const int32_t* _
   }
 }
 
-// Counts one 64-token tile in the calling wave.  `bits` holds C zeroed
-// bitmaps: column c's bit i is set when token i of the tile uses column c.
-// Lane l owns the ids at flat positions l + 64 r of the tile (token
+// Counts 64 tokens (four plan tiles) in the calling wave.  `bits` holds C
+// zeroed bitmaps: column c's bit i is set when token i of the 64 uses column c.
+// Lane l owns the ids at flat positions l + 64 r of the block (token
 // (l + 64 r) / k, slot (l + 64 r) % k) and writes their slot codes back at the
-// same positions, so loads and stores stay coalesced.  In dedup mode every id
-// also sets its token's bit in its rank's bitmap (setting it twice is harmless).
+// same positions, so loads and stores stay coalesced.  A slot's rank counts the
+// earlier tokens of its own plan tile only.  In dedup mode every id also
+// sets its token's bit in its rank's bitmap (setting it twice is harmless).
 // `s_rank` maps expert -> rank (LDS) or is null for contiguous placement.
 // PAD (received rows): negative ids are empty slots and only the first
 // `tvalid` rows of the tile are counted; empty entries get the code kNoSlot.
@@ -78,7 +80,7 @@ __device__ __forceinline__ void count_tile(const int (&raw)[KMAX], int64_t f0, i
     const int f = lane + kWave * r;
     e[r] = clampi(raw[r], 0, E - 1);
     tl[r] = kdiv(uint32_t(f), kmul, k);
-    tl[r] = tl[r] < kTile ? tl[r] : kTile - 1;  // positions past the tile are never used
+    tl[r] = tl[r] < kWaveTile ? tl[r] : kWaveTile - 1;  // positions past the block are unused
     col[r] = DEDUP ? (s_rank ? s_rank[e[r]] : e[r] / m) : e[r];
   }
   bool ok[KMAX];
@@ -98,7 +100,8 @@ __device__ __forceinline__ void count_tile(const int (&raw)[KMAX], int64_t f0, i
 #pragma unroll
   for (int r = 0; r < KMAX; ++r) {
     const uint64_t mb = bits[DEDUP ? E + col[r] : col[r]];
-    const uint64_t below = tl[r] == 0 ? 0ull : (~0ull >> (kWave - tl[r]));
+    const int t0 = tl[r] & ~(kTile - 1);  // first token of the slot's plan tile
+    const uint64_t below = ((1ull << tl[r]) - 1ull) & ~((1ull << t0) - 1ull);
     code[r] = (uint32_t(col[r]) << 8) | uint32_t(__popcll(mb & below));
     if (PAD && !ok[r]) code[r] = kNoSlot;
   }
@@ -120,16 +123,17 @@ tile_counts_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k, int
   uint64_t* bits = s_tdyn;                                        // [C]
   int32_t* s_rank = reinterpret_cast<int32_t*>(s_tdyn + C);      // [E] (dedup, explicit placement)
   const int lane = lane_id();
-  const int64_t b = blockIdx.x;
-  const int64_t f0 = b * kTile * k;
+  const int64_t b = blockIdx.x;  // 64-token block: plan tiles kTilesPerWave b + 0, 1, ...
+  const int64_t f0 = b * kWaveTile * k;
   const int64_t total = T * k;
-  const int nf = int(total - f0 < int64_t(kTile) * k ? total - f0 : int64_t(kTile) * k);
+  const int nf =
+      int(total - f0 < int64_t(kWaveTile) * k ? total - f0 : int64_t(kWaveTile) * k);
   int raw[KMAX];
   load_tile_ids<KMAX>(raw, idx, f0, total, lane);
-  int tvalid = kTile;  // rows of this tile that count (PAD: rows below *n_valid)
+  int tvalid = kWaveTile;  // rows of this block that count (PAD: rows below *n_valid)
   if (PAD) {
-    const int64_t nv = *n_valid;
-    tvalid = int(nv - b * kTile < 0 ? 0 : (nv - b * kTile > kTile ? kTile : nv - b * kTile));
+    const int64_t nv = *n_valid - b * kWaveTile;
+    tvalid = int(nv < 0 ? 0 : (nv > kWaveTile ? kWaveTile : nv));
   }
   for (int c = lane; c < C; c += kWave) bits[c] = 0ull;
   const bool has_rank = DEDUP && place;
@@ -138,8 +142,18 @@ tile_counts_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k, int
   wave_lds_sync();
   count_tile<DEDUP, PAD, KMAX>(raw, f0, nf, k, kmul, E, has_rank ? s_rank : nullptr, m, tvalid,
                                bits, lslot, lane);
-  for (int c = lane; c < C; c += kWave) tcnt[c * Bp + b] = uint8_t(__popcll(bits[c]));
-  if (bm)  // the tile's expert bitmaps, for the co-selection counts
+  // the block's tiles' counts of a column are kTilesPerWave consecutive bytes
+  // (Bp is a multiple of 16, so the last block's stay below Bp); tiles past
+  // the last one get zeros
+  constexpr uint64_t kTileMask = kTile == 64 ? ~0ull : ((1ull << (kTile % 64)) - 1ull);
+  for (int c = lane; c < C; c += kWave) {
+    const uint64_t mb = bits[c];
+#pragma unroll
+    for (int q = 0; q < kTilesPerWave; ++q)
+      tcnt[c * Bp + kTilesPerWave * b + q] =
+          uint8_t(__popcll((mb >> (q * kTile % 64)) & kTileMask));
+  }
+  if (bm)  // the block's expert bitmaps, for the co-selection counts
     for (int e = lane; e < E; e += kWave) bm[b * E + e] = bits[e];
 }
 
@@ -595,11 +609,11 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
     const size_t lds = size_t(pl.cols) * sizeof(uint64_t) + size_t(E) * sizeof(int32_t);
     const uint32_t kmul = kdiv_mul(k);
     if (dedup)
-      hipLaunchKernelGGL((tile_counts_kernel<true, false, KMAX>), dim3(unsigned(pl.tiles)),
+      hipLaunchKernelGGL((tile_counts_kernel<true, false, KMAX>), dim3(unsigned(pl.bm_tiles)),
                          dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
                          n_valid, tcnt, lslot, bm);
     else
-      hipLaunchKernelGGL((tile_counts_kernel<false, PAD, KMAX>), dim3(unsigned(pl.tiles)),
+      hipLaunchKernelGGL((tile_counts_kernel<false, PAD, KMAX>), dim3(unsigned(pl.bm_tiles)),
                          dim3(kWave), lds, stream, idx, T, E, k, R, place, m, kmul, pl.tiles_pad,
                          n_valid, tcnt, lslot, bm);
     const hipError_t err = hipGetLastError();

@@ -1,13 +1,12 @@
 // A4a / A4b - dispatch permute into a rank-contiguous send buffer.
 //
 // Source: "Expert Coupling in MoE Pretraining" (summary), "Method 1: Correlated
-// Expert Placement + Deduplicating Dispatcher": the conventional dispatcher
-// sends one copy of a token's hidden state per (token, expert); the
-// deduplicating one sends one row per distinct (token, destination rank) with
-// the ids and routing probabilities of the rank's selected experts as
-// metadata.  "DODOCO" dataset card, "Reading the counts": a token routed to
-// several experts on one rank is counted (and sent) once per expert by the
-// conventional dispatcher.
+// Expert Placement + Deduplicating Dispatcher".  Plain dispatch repeats a
+// token's row for every expert it selected; the deduplicating variant writes
+// the row once per rank the token needs and attaches to it the ids and gates
+// of all the token's experts on that rank.  "DODOCO" dataset card, "Reading
+// the counts": the plain counts (and rows) repeat a token for each of its
+// experts, also when several of them share a rank.
 //
 // Design: one wave per (token, row chunk).  The wave reads its chunk of x[t]
 // once into registers (16-byte loads, 1 KiB per wave instruction) while lanes
@@ -18,6 +17,7 @@
 // metadata of one token, in a token order that keeps a token range's metadata
 // on one XCD (meta_block below).
 #include "common.hpp"
+#include "coselect_bm.hpp"
 
 namespace moe {
 
@@ -92,11 +92,24 @@ __device__ __forceinline__ void store_chunk(const u32x4 (&v)[NV], uint8_t* dst, 
 // Without META (small grids, where every wave waits on latency rather than
 // bandwidth, and the receive-side expansion, measured slower with it) each
 // wave writes the metadata of its own token.
+// bid, nb: this block and the number of copy blocks (the grid without the
+// co-selection blocks in front, a multiple of 8 of them).
 template <bool META>
-__device__ __forceinline__ int64_t meta_block() {
-  if (!META) return blockIdx.x;
-  const unsigned per = gridDim.x >> 3;
-  return int64_t(blockIdx.x & 7u) * per + (blockIdx.x >> 3);
+__device__ __forceinline__ int64_t meta_block(unsigned bid, unsigned nb) {
+  if (!META) return bid;
+  const unsigned per = nb >> 3;
+  return int64_t(bid & 7u) * per + (bid >> 3);
+}
+
+// With cs_blocks > 0 the first cs_blocks workgroups (a multiple of 8, so the
+// copy blocks keep their XCD order) take the co-selection counts of the plan's
+// expert bitmaps instead: their loads and popcounts overlap the row copies,
+// which are bound by HBM.  Returns true in those workgroups.
+__device__ __forceinline__ bool coselect_part(const CoselectBm& cs, int cs_blocks) {
+  if (int(blockIdx.x) >= cs_blocks) return false;
+  extern __shared__ uint64_t s_cs[];
+  if (int64_t(blockIdx.x) < cs.blocks()) coselect_bm_block(cs, blockIdx.x, s_cs);
+  return true;
 }
 
 // PAD: the receive-side expansion, where a "token" is a received row, slots
@@ -114,14 +127,17 @@ dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
                 int64_t G, uint8_t* __restrict__ send,
                 int32_t* __restrict__ row_token, int32_t* __restrict__ row_expert,
                 float* __restrict__ row_weight, int32_t* __restrict__ slot_row,
-                const int32_t* __restrict__ n_valid, int64_t out_cap) {
+                const int32_t* __restrict__ n_valid, int64_t out_cap, CoselectBm cs,
+                int cs_blocks) {
+  if (coselect_part(cs, cs_blocks)) return;
+  const unsigned bid = blockIdx.x - unsigned(cs_blocks), nb = gridDim.x - unsigned(cs_blocks);
   const int lane = lane_id();
   // lanes j < k own slot j; the other lanes load slot k-1's data and ignore it
   const int jl = lane < k ? lane : k - 1;
   const int64_t nv = PAD ? int64_t(*n_valid) : T;
-  const int64_t wid = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t wid = (int64_t(bid) * blockDim.x + threadIdx.x) / kWave;
   const int64_t t = wid / cpr;
-  const int64_t wm = (meta_block<META>() * blockDim.x + threadIdx.x) / kWave;
+  const int64_t wm = (meta_block<META>(bid, nb) * blockDim.x + threadIdx.x) / kWave;
   const int64_t tm = wm / cpr;
   static_assert(!(PAD && META), "the expansion writes the metadata of its own rows");
   const int c = int(wid - t * cpr);
@@ -184,13 +200,16 @@ dispatch_dedup_kernel(const uint8_t* x, const int32_t* __restrict__ idx,
                       const int32_t* __restrict__ header, uint8_t* __restrict__ send,
                       int32_t* __restrict__ row_token, int32_t* __restrict__ row_experts,
                       float* __restrict__ row_gates, float* __restrict__ row_weight,
-                      int32_t* __restrict__ slot_row, int32_t* __restrict__ n_rows) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *n_rows = header[0];
+                      int32_t* __restrict__ slot_row, int32_t* __restrict__ n_rows,
+                      CoselectBm cs, int cs_blocks) {
+  if (coselect_part(cs, cs_blocks)) return;
+  const unsigned bid = blockIdx.x - unsigned(cs_blocks), nb = gridDim.x - unsigned(cs_blocks);
+  if (bid == 0 && threadIdx.x == 0) *n_rows = header[0];
   const int lane = lane_id();
   const int jl = lane < k ? lane : k - 1;
-  const int64_t wid = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t wid = (int64_t(bid) * blockDim.x + threadIdx.x) / kWave;
   const int64_t t = wid / cpr;
-  const int64_t wm = (meta_block<META>() * blockDim.x + threadIdx.x) / kWave;
+  const int64_t wm = (meta_block<META>(bid, nb) * blockDim.x + threadIdx.x) / kWave;
   const int64_t tm = wm / cpr;
   const bool copy = t < T;                      // wave-uniform
   const bool meta = tm < T && wm == tm * cpr;   // wave-uniform: one wave per token
@@ -293,13 +312,22 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
                                      const void* workspace, int dedup,
                                      void* send, int32_t* row_token, int32_t* row_e,
                                      float* row_gates, float* row_weight, int32_t* slot_row,
-                                     int32_t* n_rows, hipStream_t stream) {
+                                     int32_t* n_rows, int64_t cs_tokens, int32_t* W,
+                                     hipStream_t stream) {
   const PlanLayout pl = plan_layout(T, E, k, R, dedup);
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
   const int32_t* header = reinterpret_cast<const int32_t*>(ws);
   const int32_t* gbase = reinterpret_cast<const int32_t*>(ws + pl.base_off);
   const uint8_t* tcnt = ws + pl.tcnt_off;
   const uint32_t* lslot = reinterpret_cast<const uint32_t*>(ws + pl.lslot_off);
+  CoselectBm cs{};
+  int csb = 0;  // co-selection blocks in front of the copy blocks
+  size_t lds = 0;
+  if (W != nullptr && cs_tokens > 0) {
+    cs = coselect_bm_args(reinterpret_cast<const uint64_t*>(ws + pl.bm_off), cs_tokens, E, W);
+    csb = int((cs.blocks() + 7) & ~int64_t(7));
+    lds = kBmLdsBytes;
+  }
   const int chunk = NV * kWave * 16;
   const int cpr = (row_bytes + chunk - 1) / chunk;
   const int64_t waves = T * cpr;
@@ -312,50 +340,55 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
   constexpr bool NT = MOE_DISPATCH_NT != 0;
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   uint8_t* sb = static_cast<uint8_t*>(send);
-  const dim3 grid{unsigned(blocks)}, block{256};
+  const dim3 grid{unsigned(blocks + csb)}, block{256};
   if (!dedup) {
     if (T == 0) return hipSuccess;
     if (meta)
-      hipLaunchKernelGGL((dispatch_kernel<NV, NT, false, true>), grid, block, 0, stream, xb, gate,
-                         T, row_bytes, k, cpr, gbase, tcnt, lslot, pl.tiles_pad, pl.groups, sb,
-                         row_token, row_e, row_weight, slot_row, nullptr, int64_t(0));
-    else
-      hipLaunchKernelGGL((dispatch_kernel<NV, NT, false, false>), grid, block, 0, stream, xb,
+      hipLaunchKernelGGL((dispatch_kernel<NV, NT, false, true>), grid, block, lds, stream, xb,
                          gate, T, row_bytes, k, cpr, gbase, tcnt, lslot, pl.tiles_pad, pl.groups,
-                         sb, row_token, row_e, row_weight, slot_row, nullptr, int64_t(0));
+                         sb, row_token, row_e, row_weight, slot_row, nullptr, int64_t(0), cs,
+                         csb);
+    else
+      hipLaunchKernelGGL((dispatch_kernel<NV, NT, false, false>), grid, block, lds, stream, xb,
+                         gate, T, row_bytes, k, cpr, gbase, tcnt, lslot, pl.tiles_pad, pl.groups,
+                         sb, row_token, row_e, row_weight, slot_row, nullptr, int64_t(0), cs,
+                         csb);
   } else {
     if (meta)
-      hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT, true>), grid, block, 0, stream, xb, idx,
+      hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT, true>), grid, block, lds, stream, xb, idx,
                          gate, T, row_bytes, E, k, cpr, gbase, tcnt, lslot, pl.tiles_pad,
                          pl.groups, header, sb, row_token, row_e, row_gates, row_weight,
-                         slot_row, n_rows);
+                         slot_row, n_rows, cs, csb);
     else
-      hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT, false>), grid, block, 0, stream, xb, idx,
-                         gate, T, row_bytes, E, k, cpr, gbase, tcnt, lslot, pl.tiles_pad,
+      hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT, false>), grid, block, lds, stream, xb,
+                         idx, gate, T, row_bytes, E, k, cpr, gbase, tcnt, lslot, pl.tiles_pad,
                          pl.groups, header, sb, row_token, row_e, row_gates, row_weight,
-                         slot_row, n_rows);
+                         slot_row, n_rows, cs, csb);
   }
   return hipGetLastError();
 }
 
+// W non-null (and cs_tokens > 0): also the co-selection counts of the first
+// cs_tokens tokens, from the plan's expert bitmaps, in the same launch.
 hipError_t launch_dispatch(const void* x, const int32_t* idx, const float* gate, int64_t T,
                            int row_bytes, int E, int k, int R, const void* workspace, int dedup,
                            void* send, int32_t* row_token,
                            int32_t* row_e, float* row_gates, float* row_weight,
-                           int32_t* slot_row, int32_t* n_rows, hipStream_t stream) {
+                           int32_t* slot_row, int32_t* n_rows, int64_t cs_tokens, int32_t* W,
+                           hipStream_t stream) {
   switch (dispatch_nv(row_bytes)) {
     case 4:
       return launch_dispatch_nv<4>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
                                    send, row_token, row_e, row_gates, row_weight, slot_row,
-                                   n_rows, stream);
+                                   n_rows, cs_tokens, W, stream);
     case 2:
       return launch_dispatch_nv<2>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
                                    send, row_token, row_e, row_gates, row_weight, slot_row,
-                                   n_rows, stream);
+                                   n_rows, cs_tokens, W, stream);
     default:
       return launch_dispatch_nv<1>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
                                    send, row_token, row_e, row_gates, row_weight, slot_row,
-                                   n_rows, stream);
+                                   n_rows, cs_tokens, W, stream);
   }
 }
 
@@ -379,7 +412,7 @@ static hipError_t launch_expand_nv(const void* rows, const float* row_gates,
                      stream, static_cast<const uint8_t*>(rows), row_gates, cap, row_bytes, k, cpr,
                      gbase, tcnt, lslot, pl.tiles_pad, pl.groups,
                      static_cast<uint8_t*>(expanded), exp_row, exp_expert, exp_gate, row_slot,
-                     n_rows, out_cap);
+                     n_rows, out_cap, CoselectBm{}, 0);
   return hipGetLastError();
 }
 

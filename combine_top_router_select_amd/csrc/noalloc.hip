@@ -17,7 +17,7 @@ hipError_t launch_send_counts(const int32_t*, int64_t, int, int, int, const int3
                               int32_t*, int32_t*, int32_t*, int32_t*, void*, hipStream_t);
 hipError_t launch_dispatch(const void*, const int32_t*, const float*, int64_t, int, int, int,
                            int, const void*, int, void*, int32_t*, int32_t*, float*, float*,
-                           int32_t*, int32_t*, hipStream_t);
+                           int32_t*, int32_t*, int64_t, int32_t*, hipStream_t);
 }  // namespace moe
 
 // The plan scratch: every GPU the library runs on holds one copy until the
@@ -81,6 +81,6 @@ MOE_API int moe_dispatch_permute_noalloc(const void* x, const int32_t* topk_idx,
   if (tokens == 0) return MOE_OK;
   err = moe::launch_dispatch(x, topk_idx, topk_gate, tokens, int(rb), n_experts, top_k, n_ranks,
                              ws, 0, send, row_token, row_expert, nullptr, row_weight, slot_row,
-                             nullptr, st);
+                             nullptr, 0, nullptr, st);
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
 }

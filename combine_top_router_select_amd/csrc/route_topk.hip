@@ -8,14 +8,14 @@
 // Design (gfx950, wave64): a group of L lanes owns one token (L = 16, or E
 // rounded up to a power of two when E < 16), so a wave routes 64/L tokens at
 // once; lane i holds experts i, i+L, i+2L, ..., so each logits load has
-// consecutive lanes on consecutive addresses.  Each candidate becomes a 64-bit
-// key (order-preserving float bits << 32 | ~expert): the largest key is the
-// largest logit and, among equal logits, the lowest expert id.  Each of the k
-// rounds takes the lane-local maximum, then the group maximum with a DPP
-// butterfly inside the 16-lane row (quad permutes, half-row mirror, row mirror:
-// no LDS round trip), and retires the winning key.  Lane j of the group keeps
-// the round-j winner.  Gates are computed in fp64 (exp of the logit minus the
-// largest one, divided by their DPP-summed total) and rounded once to fp32.
+// consecutive lanes on consecutive addresses.  Each candidate's key is its
+// logit's order-preserving 32-bit pattern.  Each of the k rounds takes the
+// lane-local maximum, the group maximum with DPP inside the 16-lane row (quad
+// permutes, half-row mirror, row mirror: no LDS round trip), then the group
+// minimum of the expert ids holding that key (the lowest id wins a tie), and
+// retires that candidate.  Lane j of the group keeps the round-j winner.
+// Gates are computed in fp64 (exp of the logit minus the largest one, divided
+// by their DPP-summed total) and rounded once to fp32.
 // FULL: the total runs over all E logits instead of the k selected ones
 // (softmax over every expert, not renormalised over the selection).
 #include <math.h>
@@ -232,29 +232,35 @@ route_topk_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k
   }
 }
 
+__device__ __forceinline__ void lds_or(uint32_t* p, uint32_t v) { atomicOr(p, v); }
+__device__ __forceinline__ void lds_or(uint64_t* p, uint64_t v) {
+  atomicOr(reinterpret_cast<unsigned long long*>(p), static_cast<unsigned long long>(v));
+}
+
 // Routing fused with the per-tile counts of the dispatch plan: one workgroup
-// per 64-token tile, L lanes per token (64 L threads).  Each selected expert
+// per plan tile of kTile = 32 tokens, L lanes per token (32 L threads; at
+// T = 4096 and L = 16, 128 workgroups of 512 threads).  Each selected expert
 // sets its token's bit in an LDS bitmap of its column (the expert; in dedup
-// mode also its rank), after which the popcount of the bits below the token is
-// its rank in the tile and the popcount of the whole bitmap is the tile's
-// count - the same plan entries as the separate counting kernel writes from
-// topk_idx.  Saves that kernel's launch and its reread of the ids.
-// With W, the tile's tokens below cs_tokens also add their co-selection
-// counts: the tokens selecting both a and b are the set bits of
-// bits[a] & bits[b] (a == b: the tokens selecting a), so each ordered pair
-// takes one popcount and at most one global atomic add per tile.
+// mode also its rank),
+// after which the popcount of the bits below the token is its rank in the tile
+// and the popcount of the whole bitmap is the tile's count - the same plan
+// entries as the separate counting kernel writes from topk_idx.  Saves that
+// kernel's launch and its reread of the ids.  The expert bitmaps also go to
+// the plan's 64-token co-selection bitmaps (bm), as this tile's piece of them;
+// the co-selection counts are taken from there by a later kernel (done here,
+// they would cost one atomic add per co-selected pair and tile).
 template <int L, int V, int VEC, bool FULL, bool DEDUP>
 __global__ void __launch_bounds__(kTile * L)
 route_tile_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k, int R,
                   const int32_t* __restrict__ place, int m, int64_t Bp,
                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
-                  uint8_t* __restrict__ tcnt, uint32_t* __restrict__ lslot, int64_t cs_tokens,
-                  int32_t* __restrict__ W) {
-  extern __shared__ uint64_t s_rdyn[];
+                  uint8_t* __restrict__ tcnt, uint32_t* __restrict__ lslot,
+                  TilePiece* __restrict__ bm) {
+  extern __shared__ TileMask s_rdyn[];
   constexpr int NS = RouteSlots<L>::N;
   const int C = E + (DEDUP ? R : 0);
-  uint64_t* bits = s_rdyn;                                       // [C]
-  int32_t* s_rank = reinterpret_cast<int32_t*>(s_rdyn + C);     // [E] (dedup, explicit placement)
+  TileMask* bits = s_rdyn;                                     // [C]
+  int32_t* s_rank = reinterpret_cast<int32_t*>(s_rdyn + C);   // [E] (dedup, explicit placement)
   const int tid = threadIdx.x;
   const int nthreads = kTile * L;
   const int64_t b = blockIdx.x;
@@ -262,14 +268,14 @@ route_tile_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k
   const int tl = tid / L;  // token within the tile
   const int64_t t = b * kTile + tl;
   const bool tok_ok = t < tokens;
-  for (int c = tid; c < C; c += nthreads) bits[c] = 0ull;
+  for (int c = tid; c < C; c += nthreads) bits[c] = 0;
   const bool has_rank = DEDUP && place;
   if (has_rank)
     for (int e = tid; e < E; e += nthreads) s_rank[e] = clampi(place[e], 0, R - 1);
   RouteSlots<L> r;
   route_token<L, V, VEC, FULL>(logits, tokens, E, k, t, tok_ok, li, r);
   __syncthreads();  // bitmaps cleared, ranks loaded
-  const unsigned long long bit = 1ull << tl;
+  const TileMask bit = TileMask(1) << tl;
   int col[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -280,38 +286,25 @@ route_tile_kernel(const float* __restrict__ logits, int64_t tokens, int E, int k
     if (mine) {
       topk_idx[t * k + j] = e;
       topk_gate[t * k + j] = float(r.num[s] / r.den);
-      atomicOr(reinterpret_cast<unsigned long long*>(&bits[e]), bit);
-      if (DEDUP) atomicOr(reinterpret_cast<unsigned long long*>(&bits[E + col[s]]), bit);
+      lds_or(&bits[e], bit);
+      if (DEDUP) lds_or(&bits[E + col[s]], bit);
     }
   }
   __syncthreads();
-  const uint64_t below = tl == 0 ? 0ull : (~0ull >> (kWave - tl));
+  const TileMask below = bit - 1;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int j = li + L * s;
     if (tok_ok && j < k) {
-      const uint64_t mb = bits[DEDUP ? E + col[s] : col[s]];
-      lslot[t * k + j] = (uint32_t(col[s]) << 8) | uint32_t(__popcll(mb & below));
+      const TileMask mb = bits[DEDUP ? E + col[s] : col[s]];
+      lslot[t * k + j] = (uint32_t(col[s]) << 8) | uint32_t(__popcll(uint64_t(mb & below)));
     }
   }
-  for (int c = tid; c < C; c += nthreads) tcnt[c * Bp + b] = uint8_t(__popcll(bits[c]));
-  const int64_t ncs = cs_tokens - b * kTile;  // tokens of this tile in the co-selection counts
-  if (W != nullptr && ncs > 0) {
-    const uint64_t cm = ncs >= kTile ? ~0ull : ((1ull << ncs) - 1ull);
-    if (nthreads % E == 0) {  // a fixed column per thread, rows stepping by nthreads / E
-      const int cb = tid % E;
-      const uint64_t mcol = bits[cb] & cm;
-      for (int a = tid / E; a < E; a += nthreads / E) {
-        const int n = __popcll(bits[a] & mcol);
-        if (n) atomicAdd(&W[a * E + cb], n);
-      }
-    } else {
-      for (int q = tid; q < E * E; q += nthreads) {
-        const int n = __popcll(bits[q / E] & bits[q % E] & cm);
-        if (n) atomicAdd(&W[q], n);
-      }
-    }
-  }
+  for (int c = tid; c < C; c += nthreads) tcnt[c * Bp + b] = uint8_t(__popcll(uint64_t(bits[c])));
+  // piece b % kTilesPerWave of the 64-token block b / kTilesPerWave
+  // (little-endian pieces)
+  for (int e = tid; e < E; e += nthreads)
+    bm[((b / kTilesPerWave) * E + e) * kTilesPerWave + b % kTilesPerWave] = TilePiece(bits[e]);
 }
 
 template <int L, int V, int VEC, bool FULL>
@@ -377,41 +370,37 @@ hipError_t launch_send_counts(const int32_t* idx, int64_t T, int E, int k, int R
                               int32_t* expert_offsets, void* workspace, hipStream_t stream);
 
 // Largest expert count and token count routed by the fused kernel; beyond them
-// the routing, the counting and the co-selection counts run as separate kernels
-// (same results).  The fused kernel has one workgroup per 64-token tile; its
-// co-selection counts take E * E popcounts and up to E * E atomics per tile,
-// which at E = 256 cost more than a separate pass over the tile bitmaps.
-constexpr int kFusedMaxExperts = 128;
+// the routing and the counting run as separate kernels (same results).
+constexpr int kFusedMaxExperts = 256;
 constexpr int64_t kFusedMaxTokens = int64_t(1) << 24;
 
 template <int L, int V, int VEC, bool FULL>
 static hipError_t launch_route_tile(const float* logits, int64_t T, int E, int k, int R,
                                     const int32_t* place, int dedup, int32_t* idx, float* gate,
-                                    int64_t cs_tokens, int32_t* W, void* workspace,
-                                    hipStream_t stream) {
+                                    void* workspace, hipStream_t stream) {
   const PlanLayout pl = plan_layout(T, E, k, R, dedup);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* tcnt = ws + pl.tcnt_off;
   uint32_t* lslot = reinterpret_cast<uint32_t*>(ws + pl.lslot_off);
-  const size_t lds = size_t(pl.cols) * sizeof(uint64_t) + size_t(E) * sizeof(int32_t);
+  TilePiece* bm = reinterpret_cast<TilePiece*>(ws + pl.bm_off);
+  const size_t lds = size_t(pl.cols) * sizeof(TileMask) + size_t(E) * sizeof(int32_t);
   if (dedup)
     hipLaunchKernelGGL((route_tile_kernel<L, V, VEC, FULL, true>), dim3(unsigned(pl.tiles)),
                        dim3(kTile * L), lds, stream, logits, T, E, k, R, place, E / R,
-                       pl.tiles_pad, idx, gate, tcnt, lslot, cs_tokens, W);
+                       pl.tiles_pad, idx, gate, tcnt, lslot, bm);
   else
     hipLaunchKernelGGL((route_tile_kernel<L, V, VEC, FULL, false>), dim3(unsigned(pl.tiles)),
                        dim3(kTile * L), lds, stream, logits, T, E, k, R, place, E / R,
-                       pl.tiles_pad, idx, gate, tcnt, lslot, cs_tokens, W);
+                       pl.tiles_pad, idx, gate, tcnt, lslot, bm);
   return hipGetLastError();
 }
 
 template <bool FULL, int VEC>
 static hipError_t launch_route_tile_e(const float* logits, int64_t T, int E, int k, int R,
                                       const int32_t* place, int dedup, int32_t* idx, float* gate,
-                                      int64_t cs, int32_t* W, void* ws, hipStream_t st) {
-#define MOE_RT(LL, VV, VC)                                                                    \
-  launch_route_tile<LL, VV, VC, FULL>(logits, T, E, k, R, place, dedup, idx, gate, cs, W, ws, \
-                                      st)
+                                      void* ws, hipStream_t st) {
+#define MOE_RT(LL, VV, VC) \
+  launch_route_tile<LL, VV, VC, FULL>(logits, T, E, k, R, place, dedup, idx, gate, ws, st)
   if (E <= 1) return MOE_RT(1, 1, 1);
   if (E <= 2) return MOE_RT(2, 1, 1);
   if (E <= 4) return MOE_RT(4, 1, 1);
@@ -419,7 +408,8 @@ static hipError_t launch_route_tile_e(const float* logits, int64_t T, int E, int
   if (E <= 16) return MOE_RT(16, 1, 1);
   if (E <= 32) return MOE_RT(16, 2, 1);
   if (E <= 64) return MOE_RT(16, 4, VEC);
-  return MOE_RT(16, 8, VEC);
+  if (E <= 128) return MOE_RT(16, 8, VEC);
+  return MOE_RT(16, 16, VEC);
 #undef MOE_RT
 }
 
@@ -428,39 +418,37 @@ hipError_t launch_coselect_bm(const uint64_t* bm, int64_t cs_tokens, int E, int3
 
 // Routing, the dispatch plan and (W non-null) the co-selection counts of the
 // first cs_tokens tokens: the fused kernel then the scan, or (large E or T)
-// the routing kernel, the counting kernel and the scan, then the co-selection
-// counts from the per-tile expert bitmaps the counting kernel left behind.
+// the routing kernel, the counting kernel and the scan; then the co-selection
+// counts from the 64-token expert bitmaps that either path leaves in the plan.
 hipError_t launch_route_plan(const float* logits, int64_t T, int E, int k, int full_softmax,
                              int R, const int32_t* place, int dedup, int32_t* idx, float* gate,
                              int32_t* expert_counts, int32_t* rank_counts, int32_t* rank_offsets,
                              int32_t* expert_offsets, int64_t cs_tokens, int32_t* W,
                              void* workspace, hipStream_t stream) {
   hipError_t err;
-  if (cs_tokens <= 0) W = nullptr;
   if (E > kFusedMaxExperts || T > kFusedMaxTokens) {
     err = launch_route_topk(logits, T, E, k, full_softmax, idx, gate, stream);
     if (err != hipSuccess) return err;
     err = launch_send_counts(idx, T, E, k, R, place, dedup, expert_counts, rank_counts,
                              rank_offsets, expert_offsets, workspace, stream);
-    if (err != hipSuccess || W == nullptr) return err;
-    // the counting kernel left every tile's expert bitmaps in the workspace
-    const PlanLayout pl = plan_layout(T, E, k, R, dedup);
-    const uint64_t* bm =
-        reinterpret_cast<const uint64_t*>(static_cast<const uint8_t*>(workspace) + pl.bm_off);
-    return launch_coselect_bm(bm, cs_tokens, E, W, stream);
-  }
-  if (T > 0) {
-    const bool v4 = E % 4 == 0;
-#define MOE_RTE(FU, VC)                                                                \
-  launch_route_tile_e<FU, VC>(logits, T, E, k, R, place, dedup, idx, gate, cs_tokens, W, \
-                              workspace, stream)
-    err = full_softmax ? (v4 ? MOE_RTE(true, 4) : MOE_RTE(true, 1))
-                       : (v4 ? MOE_RTE(false, 4) : MOE_RTE(false, 1));
+  } else {
+    if (T > 0) {
+      const bool v4 = E % 4 == 0;
+#define MOE_RTE(FU, VC) \
+  launch_route_tile_e<FU, VC>(logits, T, E, k, R, place, dedup, idx, gate, workspace, stream)
+      err = full_softmax ? (v4 ? MOE_RTE(true, 4) : MOE_RTE(true, 1))
+                         : (v4 ? MOE_RTE(false, 4) : MOE_RTE(false, 1));
 #undef MOE_RTE
-    if (err != hipSuccess) return err;
+      if (err != hipSuccess) return err;
+    }
+    err = launch_plan_scan(T, E, k, R, place, dedup, expert_counts, rank_counts, rank_offsets,
+                           expert_offsets, workspace, stream);
   }
-  return launch_plan_scan(T, E, k, R, place, dedup, expert_counts, rank_counts, rank_offsets,
-                          expert_offsets, workspace, stream);
+  if (err != hipSuccess || W == nullptr || cs_tokens <= 0) return err;
+  const PlanLayout pl = plan_layout(T, E, k, R, dedup);
+  const uint64_t* bm =
+      reinterpret_cast<const uint64_t*>(static_cast<const uint8_t*>(workspace) + pl.bm_off);
+  return launch_coselect_bm(bm, cs_tokens, E, W, stream);
 }
 
 }  // namespace moe

@@ -2,14 +2,13 @@
 // assignment that follows is host code, in placement.hip.
 //
 // Source: "Expert Coupling in MoE Pretraining" (summary), "Method 2: Token
-// Shuffling": the planner predicts each token's owner rank at layer l+1 from
-// the experts it selected at the two preceding MoE layers - a pair lookup
-// with a single-expert fallback for sparse observations - and, since every
-// rank must own exactly T/EP tokens, assigns tokens in decreasing confidence
-// to their most preferred rank with room left.  The page prints no formula;
-// the readings (tables of rank counts, score = sum of the pairs' rank
-// distributions, confidence = largest score / sum of scores) are stated in
-// include/moe_route.h.
+// Shuffling".  Reading: the rank that will serve a token at the next MoE layer
+// is guessed from the two expert choices it made at the two layers before
+// (the pair of choices, or the later choice alone when that pair has been seen
+// too few times); ranks then take equal shares of the tokens, the surest
+// guesses placed first.  No formula is printed; the readings (tables of rank
+// counts, score = sum of the pairs' rank distributions, confidence = largest
+// score / sum of scores) are stated in include/moe_route.h.
 //
 // fit: the tables in LDS when a row of E x R counts fits (each workgroup owns
 // a range of layer l-1 experts, scans all tokens and adds its rows to the

@@ -214,11 +214,26 @@ def _routed(x, topk_idx, topk_gate):
     return T, H, k, bpe, dev
 
 
-def moe_dispatch_permute(x, topk_idx, topk_gate, n_experts, n_ranks, ws, out=None, stream=None):
+def _coselect_arg(coselect, coselect_tokens, n_experts, T, dev):
+    """(tokens, matrix) for the optional co-selection counts of a dispatch."""
+    if coselect is None:
+        return 0, None
+    _dev(coselect, "coselect", torch.int32, shape=(n_experts, n_experts), device=dev)
+    n = T if coselect_tokens is None else int(coselect_tokens)
+    if not 0 <= n <= T:
+        raise ValueError(f"coselect_tokens must be in [0, {T}], got {n}")
+    return n, coselect
+
+
+def moe_dispatch_permute(x, topk_idx, topk_gate, n_experts, n_ranks, ws, out=None, stream=None,
+                         coselect=None, coselect_tokens=None):
     """Plain dispatch of the plan in `ws` (from moe_send_counts or
-    moe_route_plan with dedup False, same topk_idx)."""
+    moe_route_plan with dedup False, same topk_idx).  With `coselect` (an
+    [E][E] int32 matrix, accumulated into) the same launch also adds the
+    co-selection counts of the first `coselect_tokens` tokens (default all)."""
     T, H, k, bpe, dev = _routed(x, topk_idx, topk_gate)
     _ws(ws, dev)
+    ncs, W = _coselect_arg(coselect, coselect_tokens, n_experts, T, dev)
     o = dict(out or {})
     N = T * k
     send = _out(o, "send", (N, H), x.dtype, dev, itemsize=bpe)
@@ -228,17 +243,20 @@ def moe_dispatch_permute(x, topk_idx, topk_gate, n_experts, n_ranks, ws, out=Non
     sr = _out(o, "slot_row", (T, k), torch.int32, dev)
     check(lib().moe_dispatch_permute(_ptr(x), _ptr(topk_idx), _ptr(topk_gate), T, H, n_experts,
                                      k, n_ranks, bpe, _ptr(ws), ws.numel(), _ptr(send),
-                                     _ptr(rt), _ptr(re), _ptr(rw), _ptr(sr), _stream(stream)),
+                                     _ptr(rt), _ptr(re), _ptr(rw), _ptr(sr), ncs, _ptr(W),
+                                     _stream(stream)),
           "moe_dispatch_permute")
     return {"send": send, "row_token": rt, "row_expert": re, "row_weight": rw, "slot_row": sr}
 
 
 def moe_dispatch_permute_dedup(x, topk_idx, topk_gate, n_experts, n_ranks, ws, out=None,
-                               stream=None):
+                               stream=None, coselect=None, coselect_tokens=None):
     """Deduplicating dispatch of the plan in `ws` (from moe_send_counts or
-    moe_route_plan with dedup True, same topk_idx).  Buffers hold T*k rows."""
+    moe_route_plan with dedup True, same topk_idx).  Buffers hold T*k rows.
+    `coselect`, `coselect_tokens`: as moe_dispatch_permute."""
     T, H, k, bpe, dev = _routed(x, topk_idx, topk_gate)
     _ws(ws, dev)
+    ncs, W = _coselect_arg(coselect, coselect_tokens, n_experts, T, dev)
     o = dict(out or {})
     N = T * k
     send = _out(o, "send", (N, H), x.dtype, dev, itemsize=bpe)
@@ -251,7 +269,7 @@ def moe_dispatch_permute_dedup(x, topk_idx, topk_gate, n_experts, n_ranks, ws, o
     check(lib().moe_dispatch_permute_dedup(_ptr(x), _ptr(topk_idx), _ptr(topk_gate), T, H,
                                            n_experts, k, n_ranks, bpe, _ptr(ws), ws.numel(),
                                            _ptr(send), _ptr(rt), _ptr(rx), _ptr(rg), _ptr(rw),
-                                           _ptr(sr), _ptr(nr), _stream(stream)),
+                                           _ptr(sr), _ptr(nr), ncs, _ptr(W), _stream(stream)),
           "moe_dispatch_permute_dedup")
     return {"send": send, "row_token": rt, "row_experts": rx, "row_gates": rg,
             "row_weight": rw, "slot_row": sr, "n_rows": nr}

@@ -138,10 +138,12 @@ int moe_send_counts(const int32_t* topk_idx, int64_t tokens, int n_experts, int 
  * it produced, then (coselect_tokens > 0) moe_coselect_counts() on the first
  * coselect_tokens of them - the same outputs bit for bit and the same plan left
  * in the workspace ([EC] "Background", "Method 1", "Correlation Formation and
- * Stability"; [DD] "Setup", "Reading the counts").  For E <= 128 one kernel
- * routes each 64-token tile, counts it and adds its co-selection counts, which
- * saves the counting and co-selection kernels' launches and their rereads of
- * topk_idx; larger E (or T > 2^24) run the separate kernels.
+ * Stability"; [DD] "Setup", "Reading the counts").  For E <= 256 one kernel
+ * routes each 32-token tile and counts it (one workgroup per tile), which saves
+ * the counting kernel's launch and its reread of topk_idx; larger E (or
+ * T > 2^24) run the separate kernels.  Co-selection counts, when asked for,
+ * come from the expert bitmaps the plan keeps, in one more short launch (the
+ * dispatch calls can take them in their own launch instead).
  *   logits, topk_idx, topk_gate   as moe_route_topk() (may be NULL when
  *                                 tokens == 0).
  *   gating                        0 or 1, as above.
@@ -176,14 +178,22 @@ int moe_route_plan(const float* logits, int64_t tokens, int n_experts, int top_k
  *   row_expert   [N] int32 out: expert of each row.
  *   row_weight   [N] fp32 out: the gate of that (token, expert).
  *   slot_row     [T][k] int32 out: the row that carries slot j of token t.
- * Errors: MOE_EINVAL, MOE_EUNSUPPORTED (bytes_per_element not 1/2/4, row bytes
+ *   coselect     [E][E] int32 or NULL.  Non-NULL: the co-selection counts of
+ *                the first coselect_tokens tokens (0 <= coselect_tokens <=
+ *                tokens) are ADDED to it exactly as moe_coselect_counts() would
+ *                add them (A6, [EC] "Method 1"), in the same launch as the row
+ *                copies: the plan holds every token's expert bitmaps.  NULL:
+ *                coselect_tokens is ignored.  The matrix must not alias an
+ *                output and must not be updated concurrently by another call.
+ * Errors: MOE_EINVAL (also coselect_tokens outside [0, tokens] with coselect
+ *         non-NULL), MOE_EUNSUPPORTED (bytes_per_element not 1/2/4, row bytes
  *         not a multiple of 16, limits), MOE_EWORKSPACE. */
 int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* topk_gate,
                          int64_t tokens, int hidden_dim, int n_experts, int top_k,
                          int n_ranks, int bytes_per_element, const void* workspace,
                          size_t workspace_bytes, void* send, int32_t* row_token,
                          int32_t* row_expert, float* row_weight, int32_t* slot_row,
-                         void* stream);
+                         int64_t coselect_tokens, int32_t* coselect, void* stream);
 
 /* Bytes of the per-device scratch array of moe_dispatch_permute_noalloc(). */
 #define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
@@ -198,7 +208,8 @@ int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* to
  * until the process ends.  Nothing is allocated: no hipMalloc, hipFree or
  * allocating library routine is called.
  *   Arguments: those of moe_send_counts() (placement, the counts and offsets,
- *   expert_offsets may be NULL) and moe_dispatch_permute() (x .. slot_row).
+ *   expert_offsets may be NULL) and moe_dispatch_permute() (x .. slot_row; no
+ *   co-selection counts).
  *   Every call on one GPU uses that GPU's one scratch array, which keeps the
  *   last call's plan (nothing in it needs to start at zero): calls that can
  *   overlap in time on one GPU - on streams not ordered with each other, or
@@ -237,13 +248,15 @@ int moe_dispatch_permute_noalloc(const void* x, const int32_t* topk_idx, const f
  *   slot_row     [T][k] int32 out: the row that carries slot j of token t
  *                (slots whose experts share a rank share a row).
  *   n_rows       [1] int32 out: D.
+ *   coselect_tokens, coselect: as moe_dispatch_permute().
  * Errors: as moe_dispatch_permute. */
 int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx, const float* topk_gate,
                                int64_t tokens, int hidden_dim, int n_experts, int top_k,
                                int n_ranks, int bytes_per_element, const void* workspace,
                                size_t workspace_bytes, void* send, int32_t* row_token,
                                int32_t* row_experts, float* row_gates, float* row_weight,
-                               int32_t* slot_row, int32_t* n_rows, void* stream);
+                               int32_t* slot_row, int32_t* n_rows, int64_t coselect_tokens,
+                               int32_t* coselect, void* stream);
 
 /* A5 - combine ([EC] "The Communication Bottleneck"; [DD] "send_matrices.csv
  * columns": combine moves the dispatch volumes back): each token's output is the
@@ -392,13 +405,13 @@ int moe_placement_search(const int32_t* coselect, int n_experts, int n_ranks,
                          int64_t* objective, int* swaps);
 
 /* ------------------------------------------------------------------------
- * Token-shuffle planner ([EC] "Method 2: Token Shuffling": a token's owner
- * rank at layer l+1 is predicted from the experts it selected at the two
- * preceding MoE layers, by a pair lookup with a single-expert fallback for
- * sparse observations; every rank owns exactly T/EP tokens, so tokens are
- * assigned in decreasing confidence to their most preferred rank with room
- * left).  The page prints no formula; the readings are stated per call.  The
- * fused reduce-scatter that moves the tokens is not part of this library.
+ * Token-shuffle planner ([EC] "Method 2: Token Shuffling").  Reading: the
+ * rank that will serve a token at layer l+1 is guessed from its experts at
+ * layers l-1 and l - from the pair, or from the layer-l expert alone when the
+ * pair is rare in the calibration data - and the ranks then take equal shares
+ * of the tokens, the surest guesses first.  No formula is printed; the
+ * readings are stated per call.  The fused reduce-scatter that moves the
+ * tokens is not part of this library.
  * ------------------------------------------------------------------------ */
 
 /* Fit, on a calibration batch: for every token, every expert c it selects at

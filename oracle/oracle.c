@@ -15,11 +15,11 @@
  *        Correlated Placement and Token Shuffling" (summary page).
  *        - "Background": each token goes to its top-k experts.
  *        - "Method 1: Correlated Expert Placement + Deduplicating Dispatcher":
- *          the conventional dispatch sends one row per (token, expert); the
- *          deduplicating dispatcher sends one row per distinct (token,
- *          destination rank) carrying the expert ids and routing probabilities
- *          of that rank's experts; the correlation graph W[e][e'] counts the
- *          tokens that select both e and e'; each GPU holds E/EP experts.
+ *          plain dispatch repeats a token's row for each of its experts; the
+ *          deduplicating variant writes it once per rank the token needs, with
+ *          the ids and gates of the token's experts on that rank attached;
+ *          W[e][e'] is the number of tokens choosing both e and e'; a GPU
+ *          holds E/EP experts.
  *  [DD]  "DODOCO: MoE AlltoAll Traffic Matrices on Real Text" (dataset card).
  *        - "Setup": contiguous placement, rank r holds experts r*E/R..;
  *          the counts are the dispatcher's per-destination input splits.
@@ -497,10 +497,10 @@ int oracle_placement_search(const int32_t* W, int n_experts, int n_ranks, const 
 
 /* ------------------------------------------------ token shuffle planner --- */
 
-/* [EC] "Method 2: Token Shuffling", prediction: a token's owner rank at layer
- * l+1 is predicted from the experts it selected at the two preceding MoE
- * layers (l-1 and l), by a pair lookup with a single-expert fallback when the
- * pair was seen too rarely.  Reading (the page prints no formula): on a
+/* [EC] "Method 2: Token Shuffling", prediction.  The serving rank at layer
+ * l+1 is guessed from the token's experts at layers l-1 and l, or from its
+ * layer-l expert alone when that pair is rare.  Reading (no formula is
+ * printed): on a
  * calibration batch, for every token, every expert c it selects at l+1 (rank
  * r = place_next[c]) and every pair (a, b) of its experts at l-1 and l,
  *   pair[a][b][r] += 1;   and for every b at l:  single[b][r] += 1.

@@ -103,10 +103,11 @@ int main(void) {
   hipStream_t stream;
   CHECK_HIP(hipStreamCreate(&stream));
   CHECK_MOE(moe_route_plan(d_logits, T, E, K, 0, R, NULL, 0, d_idx, d_gate, d_ec, d_rc, d_ro,
-                           d_eo, T, d_W, d_ws, ws_bytes, stream));
+                           d_eo, 0, NULL, d_ws, ws_bytes, stream));
+  /* the co-selection counts of all T tokens, in the dispatch launch */
   CHECK_MOE(moe_dispatch_permute(d_x, d_idx, d_gate, T, H, E, K, R, 2, d_ws, ws_bytes,
                                  d_send, d_row_token, d_row_expert, d_row_weight, d_slot_row,
-                                 stream));
+                                 T, d_W, stream));
   CHECK_MOE(moe_combine(d_send, d_row_weight, d_slot_row, T, H, K, 2, d_out, stream));
   CHECK_HIP(hipStreamSynchronize(stream));
 

@@ -141,9 +141,9 @@ def test_dispatch_errors(lib):
     f = lib.moe_dispatch_permute
     ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)
     base = [FAKE, FAKE, FAKE, 100, 128, 8, 2, 4, 2, FAKE, ws, FAKE, FAKE, FAKE, FAKE, FAKE,
-            None]
+            0, None, None]
     names = ["x", "idx", "gate", "T", "H", "E", "k", "R", "bpe", "ws", "wsb", "send", "rt", "re",
-             "rw", "sr", "stream"]
+             "rw", "sr", "ncs", "W", "stream"]
 
     def call(**kw):
         a = list(base)
@@ -159,12 +159,17 @@ def test_dispatch_errors(lib):
     assert call(send=None) == EINVAL
     assert call(x=None) == EINVAL
     assert call(ws=None) == EINVAL
+    assert call(W=FAKE, ncs=101) == EINVAL         # more co-selection tokens than tokens
+    assert call(W=FAKE, ncs=-1) == EINVAL
     g = lib.moe_dispatch_permute_dedup
     wsd = lib.moe_workspace_bytes(6400, 8, 2, 4, 1)
     args = [FAKE, FAKE, FAKE, 6400, 128, 8, 2, 4, 2, FAKE, wsd, FAKE, FAKE, FAKE, FAKE, FAKE,
-            FAKE, None, None]
+            FAKE, None, 0, None, None]
     assert g(*args) == EINVAL                      # n_rows is NULL
     args[17] = FAKE
+    args[18], args[19] = 6401, FAKE                # more co-selection tokens than tokens
+    assert g(*args) == EINVAL
+    args[18], args[19] = 0, None
     args[10] = wsd - 1                             # one byte short
     assert g(*args) == EWS
 

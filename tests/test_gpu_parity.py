@@ -126,10 +126,13 @@ def test_route_plan_parity(oracle_mod, T, E, k, R, dedup, pl, softmax_all):
     assert (bf16_host(d["send"][:o["n_rows"]]) == o["send"]).all()
 
 
+PLAN_TILE = 32   # tokens per plan tile (kTile of the library's plan layout)
+
+
 def _plan_equal(ws_a, ws_b, T, E, k, R, dedup):
     """Plan regions compared field by field (the tile-count padding bytes past
     the last tile are never read and may differ)."""
-    tiles = (T + 63) // 64
+    tiles = (T + PLAN_TILE - 1) // PLAN_TILE
     tp = (tiles + 15) // 16 * 16
     groups = tp // 16
     cols = E + (R if dedup else 0)
@@ -501,50 +504,101 @@ def test_coselect_parity(oracle_mod, T, E, k, n):
     assert (host(W) == 2 * W_o).all()
 
 
+@pytest.mark.parametrize("T,E,k,R,dedup,n,source", [
+    (4096, 64, 6, 16, False, 4096, "route_plan"),    # the benchmark's plain step
+    (16384, 128, 6, 32, True, 4096, "route_plan"),   # the benchmark's dedup step
+    (5000, 256, 8, 16, True, 5000, "route_plan"),    # 79 bitmap blocks: two chunks, atomics
+    (5000, 64, 6, 16, False, 4999, "send_counts"),   # the separate counting kernel's bitmaps
+    (300, 33, 5, 11, False, 257, "route_plan"),      # partial W blocks, a partial last block
+    (300, 33, 5, 11, True, 300, "send_counts"),
+    (64, 17, 1, 17, False, 64, "route_plan"),
+    (100, 8, 2, 4, True, 0, "route_plan"),           # no co-selection tokens: W untouched
+    (1000, 512, 4, 64, False, 1000, "route_plan"),   # E > 256: separate routing kernels
+])
+def test_dispatch_coselect(oracle_mod, T, E, k, R, dedup, n, source):
+    """The co-selection counts taken in the dispatch launch (from the plan's
+    expert bitmaps, in workgroups in front of the row copies): W identical to
+    the oracle's counts added onto a nonzero matrix, and every dispatch output
+    identical to the same dispatch without them."""
+    say(f"[dispatch coselect] T={T} E={E} k={k} R={R} dedup={dedup} n={n} {source}")
+    inp = WL.make_custom_inputs(T, 128, E, seed=T + E + n)
+    logits = to_dev(inp["logits"])
+    if source == "route_plan":
+        idx, gate, c = ops.moe_route_plan(logits, k, R, None, dedup)
+    else:
+        idx, gate = ops.moe_route_topk(logits, k)
+        c = ops.moe_send_counts(idx, E, R, None, dedup=dedup)
+    x = bf16_dev(inp["x_bits"])
+    f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+    W0 = np.random.default_rng(n).integers(0, 1000, size=(E, E), dtype=np.int32)
+    W = to_dev(W0)
+    d1 = f(x, idx, gate, E, R, c["ws"], coselect=W, coselect_tokens=n)
+    d0 = f(x, idx, gate, E, R, c["ws"])
+    sync()
+    idx_o = host(idx)
+    assert (host(W) == oracle_mod.coselect(idx_o, E, tokens=n, W=W0.copy())).all()
+    rows = int(host(d0["n_rows"])[0]) if dedup else T * k   # rows past D are never written
+    for key in d0:
+        h = bf16_host if d0[key].dtype == torch.bfloat16 else host
+        a, b = h(d1[key]), h(d0[key])
+        if key not in ("slot_row", "n_rows"):
+            a, b = a[:rows], b[:rows]
+        assert (a.view(np.uint8) == b.view(np.uint8)).all(), key
+
+
 # ------------------------------------------------------- full workloads --
 
-def gpu_chain(inp, w, dedup, stream=None, fused=False):
-    """The whole hot path on the GPU, through the C ABI: the separate routing,
-    counting and co-selection calls, or (fused) the combined routing call the
-    benchmark times."""
+def gpu_chain(inp, w, dedup, stream=None, fused=False, cs_in="dispatch"):
+    """The whole hot path on the GPU, through the C ABI.  fused: the combined
+    routing call the benchmark times, with the co-selection counts in the
+    dispatch launch (cs_in "dispatch", the benchmark's setting) or in the
+    routing call ("route"); else the separate routing, counting and
+    co-selection calls."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
     place = to_dev(inp["placement"]) if inp["placement"] is not None else None
     logits = to_dev(inp["logits"])
     x = bf16_dev(inp["x_bits"])
+    W = torch.zeros((E, E), dtype=torch.int32, device=logits.device)
     if fused:
-        W = torch.zeros((E, E), dtype=torch.int32, device=logits.device)
-        idx, gate, c = ops.moe_route_plan(logits, k, R, place, dedup, coselect=W,
+        in_route = cs_in == "route"
+        idx, gate, c = ops.moe_route_plan(logits, k, R, place, dedup,
+                                          coselect=W if in_route else None,
                                           coselect_tokens=w.coselect_tokens, stream=stream)
     else:
         idx, gate = ops.moe_route_topk(logits, k, stream=stream)
         c = ops.moe_send_counts(idx, E, R, place, dedup=dedup, stream=stream)
+    in_disp = fused and cs_in == "dispatch"
     f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-    d = f(x, idx, gate, E, R, c["ws"], stream=stream)
+    d = f(x, idx, gate, E, R, c["ws"], stream=stream, coselect=W if in_disp else None,
+          coselect_tokens=w.coselect_tokens)
     out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], stream=stream)
     if not fused:
-        W = ops.moe_coselect_counts(idx, E, tokens=w.coselect_tokens, stream=stream)
+        ops.moe_coselect_counts(idx, E, tokens=w.coselect_tokens, coselect=W, stream=stream)
     return idx, gate, c, d, out, W
 
 
 def _cases():
     for name in WL.ORDER:
         for mode in WL.get(name).dispatch:
-            yield name, mode == "dedup", True
-    yield "deepseek_moe_16b", False, False
-    yield "zyphra_top6_ep32", True, False
+            yield name, mode == "dedup", True, "dispatch"
+    yield "deepseek_moe_16b", False, True, "route"
+    yield "zyphra_top6_ep32", True, True, "route"
+    yield "deepseek_moe_16b", False, False, "-"
+    yield "zyphra_top6_ep32", True, False, "-"
 
 
-@pytest.mark.parametrize("name,dedup,fused", list(_cases()))
-def test_workload_end_to_end(oracle_mod, name, dedup, fused):
+@pytest.mark.parametrize("name,dedup,fused,cs_in", list(_cases()))
+def test_workload_end_to_end(oracle_mod, name, dedup, fused, cs_in):
     """Full sizes, the launch configuration the benchmark times (fused: the
-    combined routing call; two cases also with the separate calls): logits ->
+    combined routing call, co-selection in the dispatch launch; a few cases
+    also with it in the routing call, or with the separate calls): logits ->
     route, counts, co-selection -> dispatch -> combine (identity experts), all on
     the GPU, against the oracle chain on the same inputs."""
     w = WL.get(name)
-    say(f"[e2e] {name} dedup={dedup} fused={fused} T={w.tokens} H={w.hidden_dim} "
-        f"E={w.n_experts} k={w.top_k} R={w.n_ranks}")
+    say(f"[e2e] {name} dedup={dedup} fused={fused} coselect={cs_in} T={w.tokens} "
+        f"H={w.hidden_dim} E={w.n_experts} k={w.top_k} R={w.n_ranks}")
     inp = WL.make_inputs(w)
-    idx, gate, c, d, out, W = gpu_chain(inp, w, dedup, fused=fused)
+    idx, gate, c, d, out, W = gpu_chain(inp, w, dedup, fused=fused, cs_in=cs_in)
     sync()
     idx_o, gate_o = oracle_mod.route_topk(inp["logits"], w.top_k)
     assert (host(idx) == idx_o).all()
