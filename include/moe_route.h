@@ -216,8 +216,8 @@ int moe_dispatch_permute(const void* x, const int32_t* topk_idx, const float* to
  *   from several host threads - race on it and must not be made.
  * Errors: those of moe_send_counts() and moe_dispatch_permute();
  *   MOE_EUNSUPPORTED when the plan, moe_workspace_bytes(tokens, n_experts,
- *   top_k, n_ranks, 0) bytes, exceeds MOE_NOALLOC_SCRATCH_BYTES (about 34
- *   bytes per token at 64 experts, top-6: some 250,000 tokens); MOE_EHIP when
+ *   top_k, n_ranks, 0) bytes, exceeds MOE_NOALLOC_SCRATCH_BYTES (about 35
+ *   bytes per token at 64 experts, top-6: some 240,000 tokens); MOE_EHIP when
  *   the scratch's device address cannot be obtained or a launch fails. */
 int moe_dispatch_permute_noalloc(const void* x, const int32_t* topk_idx, const float* topk_gate,
                                  int64_t tokens, int hidden_dim, int n_experts, int top_k,
