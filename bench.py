@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
                     [--receive] [--fp8] [--search] [--shuffle] [--streams {0,1,2,3,4}]
-                    [--separate] [--graph] [--overlap] [--coselect-in {dispatch,route}]
-                    [--step-events]
+                    [--separate] [--plan-call] [--graph] [--overlap]
+                    [--coselect-in {dispatch,route}] [--step-events]
                     [--no-cpu-baseline] [--no-reference] [--cpu-seconds S]
                     [--footprint-gib G] [--calib-copy]
 
@@ -25,11 +25,15 @@ same K steps are then timed on the other setting and reported as
 `other_streams`; --streams n fixes the setting.  --overlap instead forks only the co-selection
 counts onto a second stream inside each step.
 
-The co-selection counts (of the workload's first tokens) are taken by default
-in the dispatch launch, from the expert bitmaps of the plan, in workgroups that
-run beside the row copies; --coselect-in route takes them in the routing call
-instead (fused routing: one short kernel more; --separate: the stand-alone
-co-selection kernel at the end of the step).
+By default a step is moe_route_dispatch (routing, counts, offsets, plan, rows
+and the co-selection counts of the workload's first tokens in one call: two
+launches, the dispatch workgroups scanning small plans themselves) and then
+moe_combine.  --plan-call takes moe_route_plan and then the dispatch call
+(three launches); --separate takes moe_route_topk, moe_send_counts and the
+dispatch call.  The co-selection counts go with the dispatch launch, from the
+plan's expert bitmaps; --coselect-in route takes them in the routing call
+instead (implies --plan-call; with --separate, the stand-alone co-selection
+kernel at the end of the step).
 
 The timed steps call the C ABI directly with arguments marshalled once per
 buffer set (the Python binding's per-call checks would otherwise cost about
@@ -110,6 +114,8 @@ def parse():
     p.add_argument("--separate", action="store_true",
                    help="route and count with moe_route_topk + moe_send_counts instead of the "
                         "fused moe_route_plan (one kernel more)")
+    p.add_argument("--plan-call", action="store_true",
+                   help="moe_route_plan then the dispatch call instead of moe_route_dispatch")
     p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     p.add_argument("--overlap", action="store_true",
                    help="run the co-selection counts on a second stream")
@@ -334,18 +340,25 @@ class BufferSet:
         return tot
 
 
-def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True, cs_in="dispatch"):
-    """One pass of the hot path.  The co-selection counts go with the dispatch
-    (cs_in "dispatch") or the routing ("route") call, or with a side stream
-    they run there, after the routing and concurrently with the rest.  With
-    `receive` (dedup mode), the dedup rows are expanded per expert, passed
-    through identity experts, reduced back to one row per received row, and
-    those rows are combined with weight 1."""
+def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True, cs_in="dispatch",
+             one_call=False):
+    """One pass of the hot path.  one_call: moe_route_dispatch (with the
+    co-selection counts), then the rest.  Otherwise the co-selection counts go
+    with the dispatch (cs_in "dispatch") or the routing ("route") call, or with
+    a side stream they run there, after the routing and concurrently with the
+    rest.  With `receive` (dedup mode), the dedup rows are expanded per expert,
+    passed through identity experts, reduced back to one row per received row,
+    and those rows are combined with weight 1."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
     main = torch.cuda.current_stream()
     cs_route = side is None and cs_in == "route"
     cs_disp = side is None and cs_in == "dispatch"
-    if fused:
+    if one_call:
+        d = ops.moe_route_dispatch(b.logits, b.x, k, R, b.place, dedup,
+                                   out={"topk_idx": b.idx, "topk_gate": b.gate, **b.cnt,
+                                        **b.disp},
+                                   ws=b.ws, coselect=b.W, coselect_tokens=w.coselect_tokens)[3]
+    elif fused:
         c = ops.moe_route_plan(b.logits, k, R, b.place, dedup, topk_idx=b.idx, topk_gate=b.gate,
                                ws=b.ws, out=b.cnt, coselect=b.W if cs_route else None,
                                coselect_tokens=w.coselect_tokens)[2]
@@ -357,11 +370,12 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True, cs_i
         ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W,
                                 stream=side)
         b.ev_coselected.record(side)
-    if not fused:
+    if not fused and not one_call:
         c = ops.moe_send_counts(b.idx, E, R, b.place, dedup, ws=b.ws, out=b.cnt)
-    f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-    d = f(b.x, b.idx, b.gate, E, R, c["ws"], out=b.disp, coselect=b.W if cs_disp else None,
-          coselect_tokens=w.coselect_tokens)
+    if not one_call:
+        f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+        d = f(b.x, b.idx, b.gate, E, R, c["ws"], out=b.disp, coselect=b.W if cs_disp else None,
+              coselect_tokens=w.coselect_tokens)
     if receive:
         ops.moe_expand_counts(d["row_experts"], d["n_rows"], E, R, b.place, ws=b.ews, out=b.ecnt)
         ex = ops.moe_expand_permute(d["send"], d["row_gates"], d["n_rows"], E, R, b.ews,
@@ -373,7 +387,7 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True, cs_i
         ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b.out)
     if side is not None:
         main.wait_event(b.ev_coselected)
-    elif cs_route and not fused:
+    elif cs_route and not fused and not one_call:
         ops.moe_coselect_counts(b.idx, E, tokens=w.coselect_tokens, coselect=b.W)
 
 
@@ -437,12 +451,13 @@ def counter_traffic(kernel, workload, mode, dtype="bf16"):
 
 
 def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True, stream=None,
-                   cs_in="dispatch"):
+                   cs_in="dispatch", one_call=False):
     """The C-ABI calls of one step on buffer set b, with every argument
     marshalled once: the timed loop then costs a few microseconds of host time
-    per step instead of the Python binding's checks.  With a side stream the
-    co-selection counts run there, forked after the routing and joined at the
-    end of the step (event record and wait entries return 0)."""
+    per step instead of the Python binding's checks.  one_call: routing, plan,
+    rows and co-selection counts through moe_route_dispatch.  With a side stream
+    the co-selection counts run there, forked after the routing and joined at
+    the end of the step (event record and wait entries return 0)."""
     L = ops.lib()
     T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
     N = T * k
@@ -454,7 +469,14 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
     wsargs = (p(b.ws), b.ws.numel(), st)
     ncs = w.coselect_tokens if side is None and cs_in == "route" else 0
     dcs = w.coselect_tokens if side is None and cs_in == "dispatch" else 0
-    if fused:
+    if one_call:
+        rx = d["row_experts"] if dedup else d["row_expert"]
+        calls = [(L.moe_route_dispatch, (
+            p(b.logits), p(b.x), T, H, E, k, 0, R, p(b.place), int(dedup), bpe, p(b.idx),
+            p(b.gate), *cargs[1:], p(d["send"]), p(d["row_token"]), p(rx), p(d.get("row_gates")),
+            p(d["row_weight"]), p(d["slot_row"]), p(d.get("n_rows")), w.coselect_tokens,
+            p(b.W), *wsargs))]
+    elif fused:
         calls = [(L.moe_route_plan, (p(b.logits), T, E, k, 0, R, p(b.place), *cargs[:1],
                                      p(b.idx), p(b.gate), *cargs[1:], ncs,
                                      p(b.W) if ncs else None, *wsargs))]
@@ -473,9 +495,11 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
             main.wait_event(b.ev_coselected)
             return 0
         calls.append((fork, ()))
-    if not fused:
+    if not fused and not one_call:
         calls.append((L.moe_send_counts, (p(b.idx), T, E, k, R, p(b.place), *cargs, *wsargs)))
-    if dedup:
+    if one_call:
+        pass
+    elif dedup:
         calls.append((L.moe_dispatch_permute_dedup, (
             p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, bpe, p(b.ws), b.ws.numel(),
             p(d["send"]), p(d["row_token"]), p(d["row_experts"]), p(d["row_gates"]),
@@ -505,7 +529,7 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
                                       k, bpe, p(b.out), st)))
     if side is not None:
         calls.append((join, ()))
-    elif not fused and ncs:
+    elif not fused and not one_call and ncs:
         calls.append((L.moe_coselect_counts, (p(b.idx), w.coselect_tokens, E, k, p(b.W), st)))
     return calls
 
@@ -630,6 +654,8 @@ def main():
     dedup = bool(a.dedup)
     receive = bool(a.receive)
     fused = not a.separate
+    # routing, plan, rows and co-selection counts in one call (the default)
+    one_call = fused and not a.plan_call and not a.overlap and a.coselect_in == "dispatch"
     if receive and not dedup:
         print("--receive needs --dedup (the receive side expands deduplicated rows)",
               file=sys.stderr)
@@ -660,13 +686,15 @@ def main():
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for b in sets:       # warm the code paths once outside capture
-                gpu_step(torch, ops, b, w, dedup, side, receive, fused, a.coselect_in)
+                gpu_step(torch, ops, b, w, dedup, side, receive, fused, a.coselect_in,
+                         one_call)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         for b in sets:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                gpu_step(torch, ops, b, w, dedup, side, receive, fused, a.coselect_in)
+                gpu_step(torch, ops, b, w, dedup, side, receive, fused, a.coselect_in,
+                         one_call)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -678,12 +706,14 @@ def main():
 
         def raw_sets(ns):
             return [raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side, fused,
-                                   streams[i % ns], a.coselect_in) for i, b in enumerate(sets)]
+                                   streams[i % ns], a.coselect_in, one_call)
+                    for i, b in enumerate(sets)]
         raw = raw_sets(n_streams)
         if side is None and not a.step_events:
             raw_other = raw_sets(1 if n_streams > 1 else 2)
 
-    timed_kernels = ("moe_dispatch_permute", "moe_dispatch_permute_dedup", "moe_combine",
+    timed_kernels = ("moe_route_dispatch", "moe_dispatch_permute", "moe_dispatch_permute_dedup",
+                     "moe_combine",
                      "moe_expand_permute", "moe_expand_reduce")
     step_ev = {}   # (step, entry point) -> (start event, end event)
     ev_pool = ([torch.cuda.Event(enable_timing=True) for _ in range(8 * a.steps + 8)]
@@ -705,11 +735,13 @@ def main():
                 if rc != 0:
                     raise ops.MoeError(rc, name)
         else:
-            gpu_step(torch, ops, sets[i % nsets], w, dedup, side, receive, fused, a.coselect_in)
+            gpu_step(torch, ops, sets[i % nsets], w, dedup, side, receive, fused, a.coselect_in,
+                     one_call)
 
     for i in range(a.warmup):
         if i == 0 and graphs is None:   # once through the Python binding, with its checks
-            gpu_step(torch, ops, sets[0], w, dedup, side, receive, fused, a.coselect_in)
+            gpu_step(torch, ops, sets[0], w, dedup, side, receive, fused, a.coselect_in,
+                     one_call)
         else:
             step(i)
     torch.cuda.synchronize()
@@ -840,7 +872,7 @@ def main():
         "config": {"workload": w.name, "tokens": T, "hidden_dim": H, "n_experts": E,
                    "top_k": k, "n_ranks": R, "placement": w.placement,
                    "dispatch": "dedup" if dedup else "nondedup", "receive_side": receive,
-                   "routing": "fused" if fused else "separate",
+                   "routing": "one_call" if one_call else ("fused" if fused else "separate"),
                    "bytes_per_element": bpe, "graph": bool(a.graph),
                    "coselect": "side_stream" if a.overlap else a.coselect_in + "_call",
                    "streams": n_streams,

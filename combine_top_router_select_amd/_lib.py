@@ -17,7 +17,7 @@ SYMBOLS = ("moe_status_string", "moe_workspace_bytes", "moe_expand_workspace_byt
            "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
            "moe_placement_search", "moe_route_topk_softmax_all", "moe_shuffle_fit",
            "moe_shuffle_predict", "moe_shuffle_assign", "moe_route_plan",
-           "moe_dispatch_permute_noalloc")
+           "moe_dispatch_permute_noalloc", "moe_route_dispatch")
 
 _lib = None
 
@@ -52,6 +52,9 @@ def lib():
                                                  P, P, P, P, P, P, P, i64, P, P]
         L.moe_dispatch_permute_noalloc.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i32, P,
                                                    P, P, P, P, P, P, P, P, P]
+        L.moe_route_dispatch.argtypes = [P, P, i64, i32, i32, i32, i32, i32, P, i32, i32,
+                                         P, P, P, P, P, P, P, P, P, P, P, P, P, i64, P, P, sz,
+                                         P]
         L.moe_combine.argtypes = [P, P, P, i64, i32, i32, i32, P, P]
         L.moe_coselect_counts.argtypes = [P, i64, i32, i32, P, P]
         L.moe_expand_workspace_bytes.argtypes = [i64, i32, i32, i32]

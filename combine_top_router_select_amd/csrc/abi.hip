@@ -33,6 +33,14 @@ hipError_t launch_coselect(const int32_t*, int64_t, int, int, int32_t*, hipStrea
 hipError_t launch_route_plan(const float*, int64_t, int, int, int, int, const int32_t*, int,
                              int32_t*, float*, int32_t*, int32_t*, int32_t*, int32_t*, int64_t,
                              int32_t*, void*, hipStream_t);
+bool route_tiles_fit(int64_t, int);
+hipError_t launch_route_tiles(const float*, int64_t, int, int, int, int, const int32_t*, int,
+                              int32_t*, float*, void*, hipStream_t);
+bool dispatch_scans_plan(int64_t, int, int, int, int);
+hipError_t launch_dispatch_scan(const void*, const int32_t*, const float*, int64_t, int, int, int,
+                                int, const int32_t*, void*, int, void*, int32_t*, int32_t*,
+                                float*, float*, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*,
+                                int32_t*, int64_t, int32_t*, hipStream_t);
 }  // namespace moe
 
 namespace {
@@ -200,6 +208,58 @@ MOE_API int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx,
                                          row_experts, row_gates, row_weight, slot_row, n_rows,
                                          coselect ? coselect_tokens : 0, coselect,
                                          as_stream(stream)));
+}
+
+MOE_API int moe_route_dispatch(const float* logits, const void* x, int64_t tokens, int hidden_dim,
+                               int n_experts, int top_k, int gating, int n_ranks,
+                               const int32_t* placement, int dedup, int bytes_per_element,
+                               int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+                               int32_t* rank_counts, int32_t* rank_offsets,
+                               int32_t* expert_offsets, void* send, int32_t* row_token,
+                               int32_t* row_experts, float* row_gates, float* row_weight,
+                               int32_t* slot_row, int32_t* n_rows, int64_t coselect_tokens,
+                               int32_t* coselect, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if ((st = check_rows(hidden_dim, bytes_per_element)) != MOE_OK) return st;
+  if (gating != 0 && gating != 1) return MOE_EINVAL;
+  if (coselect && (coselect_tokens < 0 || coselect_tokens > tokens)) return MOE_EINVAL;
+  if (!expert_counts || !rank_counts || !rank_offsets || !workspace || (dedup && !n_rows))
+    return MOE_EINVAL;
+  if (tokens > 0 && (!logits || !x || !topk_idx || !topk_gate || !send || !row_token ||
+                     !row_experts || !row_weight || !slot_row || (dedup && !row_gates)))
+    return MOE_EINVAL;
+  const int d = dedup ? 1 : 0;
+  if (workspace_bytes < moe_workspace_bytes(tokens, n_experts, top_k, n_ranks, d))
+    return MOE_EWORKSPACE;
+  const int rb = hidden_dim * bytes_per_element;
+  const int64_t ncs = coselect ? coselect_tokens : 0;
+  int32_t* eo = d ? nullptr : expert_offsets;
+  hipStream_t s = as_stream(stream);
+  if (moe::route_tiles_fit(tokens, n_experts) &&
+      moe::dispatch_scans_plan(tokens, n_experts, top_k, n_ranks, d)) {
+    // two launches: routing with the tile counts, then the dispatch, whose
+    // workgroups scan the plan themselves
+    if (moe::launch_route_tiles(logits, tokens, n_experts, top_k, gating, n_ranks, placement, d,
+                                topk_idx, topk_gate, workspace, s) != hipSuccess)
+      return MOE_EHIP;
+    return hip_status(moe::launch_dispatch_scan(
+        x, topk_idx, topk_gate, tokens, rb, n_experts, top_k, n_ranks, placement, workspace, d,
+        send, row_token, row_experts, d ? row_gates : nullptr, row_weight, slot_row,
+        d ? n_rows : nullptr, expert_counts, rank_counts, rank_offsets, eo, ncs, coselect, s));
+  }
+  // larger plans: the routing call with its scan, then the dispatch
+  if (moe::launch_route_plan(logits, tokens, n_experts, top_k, gating, n_ranks, placement, d,
+                             topk_idx, topk_gate, expert_counts, rank_counts, rank_offsets, eo, 0,
+                             nullptr, workspace, s) != hipSuccess)
+    return MOE_EHIP;
+  if (tokens == 0 && !d) return MOE_OK;
+  return hip_status(moe::launch_dispatch(x, topk_idx, topk_gate, tokens, rb, n_experts, top_k,
+                                         n_ranks, workspace, d, send, row_token, row_experts,
+                                         d ? row_gates : nullptr, row_weight, slot_row,
+                                         d ? n_rows : nullptr, ncs, coselect, s));
 }
 
 // Rows of bf16 (2 bytes) or fp8 E4M3 (1 byte); the output is bf16.

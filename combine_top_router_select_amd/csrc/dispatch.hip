@@ -18,6 +18,7 @@
 // on one XCD (meta_block below).
 #include "common.hpp"
 #include "coselect_bm.hpp"
+#include "plan_order.hpp"
 
 namespace moe {
 
@@ -64,6 +65,121 @@ __device__ __forceinline__ int tile_first_row(const int32_t* gbase,
   const int g = int(gbase[col * G + (b >> 4)]);
   const u32x4 tv = load16(tcnt + tcol * Bp + (b & ~int64_t(15)));
   return g + byte_sum(keep_bytes(tv, int(b & 15)));
+}
+
+// ------------------------------------------ plans scanned by the dispatch --
+//
+// For a small plan (at most kEmbedMaxVec 16-tile vectors of tile counts) the
+// dispatch workgroups do the plan's scan themselves, so the routing call needs
+// no scan launch of its own (moe_route_dispatch): every workgroup reads all
+// tile counts (L2 hits: 8 KiB at 4096 tokens, 64 experts), takes every
+// column's total and group prefixes in LDS, orders and scans the columns
+// (order_columns, as the scan kernel does), and looks its rows' positions up
+// in LDS.  The tile-count loads are issued before the row loads (a wave's loads
+// complete in order), so the scan runs while the rows are in flight; all of
+// them, four per thread, go out at once, since any load issued after the rows
+// would make the scan wait for the rows.
+// Workgroup 0 also writes the counts, offsets, header and group bases, so the
+// workspace then holds the same plan as after the scan kernel.
+constexpr int kEmbedMaxVec = 1024;
+
+struct ScanArgs {
+  int B;                    // tiles
+  int E, R, m;              // experts, ranks, experts per rank (contiguous placement)
+  const int32_t* place;     // expert -> rank (explicit placement, plain dispatch)
+  int32_t* expert_counts;
+  int32_t* rank_counts;
+  int32_t* rank_offsets;
+  int32_t* expert_offsets;  // may be null
+  int32_t* header;
+  int32_t* gbase;           // the plan's group bases, written by workgroup 0
+};
+
+// Dynamic LDS of scan_small_plan: s_tot[C], s_col[E], s_pre[C * G], OrderLds.
+template <bool RANKED>
+__host__ __device__ inline size_t scan_lds_bytes(int C, int E, int G) {
+  const size_t head = (size_t(C) + size_t(E) + size_t(C) * size_t(G)) * 4;
+  return (head + 7) / 8 * 8 + sizeof(OrderLds<RANKED>);
+}
+
+// The loads of scan_small_plan, issued by the dispatch kernels before their
+// row loads.
+constexpr int kScanEarly = kEmbedMaxVec / 256;  // 16-tile vectors per thread
+struct ScanPrefetch {
+  u32x4 vv[kScanEarly];
+  int my_rank;  // RANKED: the rank of expert threadIdx.x
+};
+
+template <bool RANKED>
+__device__ __forceinline__ void scan_prefetch(const uint8_t* tcnt, int G, int C,
+                                              const ScanArgs& a, ScanPrefetch& pf) {
+  const int tid = threadIdx.x;
+  const int V = C * G;
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);
+#pragma unroll
+  for (int i = 0; i < kScanEarly; ++i) {
+    const int q = tid + i * int(blockDim.x);
+    pf.vv[i] = g4[q < V ? q : V - 1];
+  }
+  pf.my_rank = (RANKED && tid < a.E) ? clampi(a.place[tid], 0, a.R - 1) : 0;
+}
+
+// Every thread of the workgroup calls it (blockDim.x >= max(CP, R), and E
+// when RANKED), after scan_prefetch.  Leaves s_col[p] = the first row of
+// position column p (the expert id when RANKED) and s_pre[c * G + g] = the
+// rows of column c in the groups before g; returns the total number of rows.
+template <bool DEDUP, bool RANKED>
+__device__ __forceinline__ int scan_small_plan(const uint8_t* tcnt, int G, const ScanArgs& a,
+                                               const ScanPrefetch& pf, bool outputs,
+                                               uint8_t* lds, int32_t*& s_col, int32_t*& s_pre) {
+  const int E = a.E, R = a.R;
+  const int C = E + (DEDUP ? R : 0);
+  const int cbase = DEDUP ? E : 0;
+  const int CP = DEDUP ? R : E;
+  int32_t* s_tot = reinterpret_cast<int32_t*>(lds);
+  s_col = s_tot + C;
+  s_pre = s_col + E;
+  const size_t head = (size_t(C) + size_t(E) + size_t(C) * size_t(G)) * 4;
+  OrderLds<RANKED>& L = *reinterpret_cast<OrderLds<RANKED>*>(lds + (head + 7) / 8 * 8);
+  const int tid = threadIdx.x;
+  const int V = C * G;
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);  // column c: vectors c*G .. c*G+G-1
+  const int my_rank = pf.my_rank;
+  // byte sums of every 16-tile vector (V <= kScanEarly * blockDim.x: all prefetched)
+#pragma unroll
+  for (int i = 0; i < kScanEarly; ++i) {
+    const int q = tid + i * int(blockDim.x);
+    if (q < V) s_pre[q] = byte_sum(keep_bytes(pf.vv[i], a.B - 16 * (q % G)));
+  }
+  order_init<RANKED>(L);
+  __syncthreads();
+  // each column's total and exclusive prefix over its groups
+  for (int c = tid; c < C; c += blockDim.x) {
+    int run = 0;
+    for (int g = 0; g < G; ++g) {
+      const int x = s_pre[c * G + g];
+      s_pre[c * G + g] = run;
+      run += x;
+    }
+    s_tot[c] = run;
+  }
+  __syncthreads();
+  const int total = order_columns<DEDUP, RANKED>(s_tot, s_col, L, E, R, a.m, my_rank, outputs,
+                                                 a.expert_counts, a.rank_counts, a.rank_offsets,
+                                                 a.expert_offsets, a.header);
+  if (outputs)
+    for (int i = tid; i < CP * G; i += blockDim.x)
+      a.gbase[i] = s_col[i / G] + s_pre[(cbase + i / G) * G + i % G];
+  return total;
+}
+
+// First row of position column `col` (tcnt column `tcol`) in tile b, from the
+// LDS tables of scan_small_plan.
+__device__ __forceinline__ int lds_first_row(const int32_t* s_col, const int32_t* s_pre,
+                                             const uint8_t* tcnt, int64_t Bp, int64_t G,
+                                             int tcol, int col, int64_t b) {
+  const u32x4 tv = load16(tcnt + tcol * Bp + (b & ~int64_t(15)));
+  return s_col[col] + s_pre[tcol * G + (b >> 4)] + byte_sum(keep_bytes(tv, int(b & 15)));
 }
 
 template <int NV, bool NT>
@@ -119,7 +235,9 @@ __device__ __forceinline__ bool coselect_part(const CoselectBm& cs, int cs_block
 // Each wave copies the row chunk of (token t, chunk c) and writes the metadata
 // of token tm (when its wave index in the metadata order is chunk 0 of tm).
 // Every load of both is issued before the first wait, from in-bounds indices.
-template <int NV, bool NT, bool PAD, bool META>
+// SC: 0 = group bases from the workspace; 1 = the workgroups scan the plan
+// (contiguous placement); 2 = the same with an explicit placement.
+template <int NV, bool NT, bool PAD, bool META, int SC>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
                 int row_bytes, int k, int cpr, const int32_t* gbase,
@@ -128,7 +246,8 @@ dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
                 int32_t* __restrict__ row_token, int32_t* __restrict__ row_expert,
                 float* __restrict__ row_weight, int32_t* __restrict__ slot_row,
                 const int32_t* __restrict__ n_valid, int64_t out_cap, CoselectBm cs,
-                int cs_blocks) {
+                int cs_blocks, ScanArgs sa) {
+  static_assert(!(PAD && SC), "the expansion's plan comes from its scan kernel");
   if (coselect_part(cs, cs_blocks)) return;
   const unsigned bid = blockIdx.x - unsigned(cs_blocks), nb = gridDim.x - unsigned(cs_blocks);
   const int lane = lane_id();
@@ -147,25 +266,42 @@ dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
   }
   const bool copy = t < T && t < nv;            // wave-uniform
   const bool meta = tm < T && wm == tm * cpr;   // wave-uniform: one wave per token
-  if (!copy && !meta) return;
+  if (!SC && !copy && !meta) return;            // (with SC every wave takes the scan's barriers)
   // The loads are unconditional, from tokens in range: a load under a branch
   // the compiler cannot prove uniform is followed by a wait for it.
-  const int64_t tl = copy ? t : tm;
-  const int64_t tml = meta ? tm : t;
+  const int64_t tl = copy ? t : (meta ? tm : T - 1);
+  const int64_t tml = meta ? tm : tl;
   const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
   const uint32_t code = lslot[tl * k + jl];  // (expert << 8) | rank inside the tile
   const uint32_t code_m = META ? lslot[tml * k + jl] : code;
   const float g_m = gate[tml * k + jl];
+  ScanPrefetch pf;
+  if (SC) {
+    scan_prefetch<SC == 2>(tcnt, int(G), sa.E, sa, pf);
+    issue_fence();
+  }
   u32x4 v[NV];
   load_chunk<NV>(v, x + tl * row_bytes, chunk0, row_bytes, lane);
   issue_fence();
+  int32_t* s_col = nullptr;
+  int32_t* s_pre = nullptr;
+  if (SC) {
+    extern __shared__ uint64_t s_scan[];
+    scan_small_plan<false, SC == 2>(tcnt, int(G), sa, pf, bid == 0,
+                                    reinterpret_cast<uint8_t*>(s_scan), s_col, s_pre);
+    if (!copy && !meta) return;
+  }
   const bool has = !PAD || code != kNoSlot;
   const int e = has ? int(code >> 8) : 0;
-  const int pos = tile_first_row(gbase, tcnt, Bp, G, e, e, tl / kTile) + int(code & 255u);
+  const int pos = (SC ? lds_first_row(s_col, s_pre, tcnt, Bp, G, e, e, tl / kTile)
+                      : tile_first_row(gbase, tcnt, Bp, G, e, e, tl / kTile)) +
+                  int(code & 255u);
   const bool has_m = !PAD || code_m != kNoSlot;
   const int e_m = has_m ? int(code_m >> 8) : 0;
   const int pos_m =
-      META ? tile_first_row(gbase, tcnt, Bp, G, e_m, e_m, tml / kTile) + int(code_m & 255u)
+      META ? (SC ? lds_first_row(s_col, s_pre, tcnt, Bp, G, e_m, e_m, tml / kTile)
+                 : tile_first_row(gbase, tcnt, Bp, G, e_m, e_m, tml / kTile)) +
+                 int(code_m & 255u)
            : pos;
   issue_fence();
   ready(pos_m);
@@ -191,20 +327,21 @@ dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
   }
 }
 
-template <int NV, bool NT, bool META>
+// SC: the workgroups scan the plan (see dispatch_kernel).
+template <int NV, bool NT, bool META, bool SC>
 __global__ void __launch_bounds__(256)
 dispatch_dedup_kernel(const uint8_t* x, const int32_t* __restrict__ idx,
                       const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k,
                       int cpr, const int32_t* gbase, const uint8_t* tcnt,
                       const uint32_t* lslot, int64_t Bp, int64_t G,
-                      const int32_t* __restrict__ header, uint8_t* __restrict__ send,
+                      const int32_t* header, uint8_t* __restrict__ send,
                       int32_t* __restrict__ row_token, int32_t* __restrict__ row_experts,
                       float* __restrict__ row_gates, float* __restrict__ row_weight,
                       int32_t* __restrict__ slot_row, int32_t* __restrict__ n_rows,
-                      CoselectBm cs, int cs_blocks) {
+                      CoselectBm cs, int cs_blocks, ScanArgs sa) {
   if (coselect_part(cs, cs_blocks)) return;
   const unsigned bid = blockIdx.x - unsigned(cs_blocks), nb = gridDim.x - unsigned(cs_blocks);
-  if (bid == 0 && threadIdx.x == 0) *n_rows = header[0];
+  if (!SC && bid == 0 && threadIdx.x == 0) *n_rows = header[0];
   const int lane = lane_id();
   const int jl = lane < k ? lane : k - 1;
   const int64_t wid = (int64_t(bid) * blockDim.x + threadIdx.x) / kWave;
@@ -213,24 +350,41 @@ dispatch_dedup_kernel(const uint8_t* x, const int32_t* __restrict__ idx,
   const int64_t tm = wm / cpr;
   const bool copy = t < T;                      // wave-uniform
   const bool meta = tm < T && wm == tm * cpr;   // wave-uniform: one wave per token
-  if (!copy && !meta) return;
-  const int64_t tl = copy ? t : tm;
-  const int64_t tml = meta ? tm : t;
+  if (!SC && !copy && !meta) return;            // (with SC every wave takes the scan's barriers)
+  const int64_t tl = copy ? t : (meta ? tm : T - 1);
+  const int64_t tml = meta ? tm : tl;
   const int c = int(wid - t * cpr);
   const int64_t chunk0 = int64_t(c) * (NV * kWave * 16);
   const uint32_t code = lslot[tl * k + jl];  // (rank << 8) | rank inside the tile
   const uint32_t code_m = META ? lslot[tml * k + jl] : code;
   const int e_m = clampi(idx[tml * k + jl], 0, E - 1);
   const float g_m = gate[tml * k + jl];
+  ScanPrefetch pf;
+  if (SC) {
+    scan_prefetch<false>(tcnt, int(G), E + sa.R, sa, pf);
+    issue_fence();
+  }
   u32x4 v[NV];
   load_chunk<NV>(v, x + tl * row_bytes, chunk0, row_bytes, lane);
   issue_fence();
+  int32_t* s_col = nullptr;
+  int32_t* s_pre = nullptr;
+  if (SC) {
+    extern __shared__ uint64_t s_scan[];
+    const int total = scan_small_plan<true, false>(tcnt, int(G), sa, pf, bid == 0,
+                                                   reinterpret_cast<uint8_t*>(s_scan), s_col,
+                                                   s_pre);
+    if (bid == 0 && threadIdx.x == 0) *n_rows = total;
+    if (!copy && !meta) return;
+  }
   const int r_own = int(code >> 8);
-  const int pos = tile_first_row(gbase, tcnt, Bp, G, E + r_own, r_own, tl / kTile) +
+  const int pos = (SC ? lds_first_row(s_col, s_pre, tcnt, Bp, G, E + r_own, r_own, tl / kTile)
+                      : tile_first_row(gbase, tcnt, Bp, G, E + r_own, r_own, tl / kTile)) +
                   int(code & 255u);
   const int rm_own = int(code_m >> 8);
   const int pos_m =
-      META ? tile_first_row(gbase, tcnt, Bp, G, E + rm_own, rm_own, tml / kTile) +
+      META ? (SC ? lds_first_row(s_col, s_pre, tcnt, Bp, G, E + rm_own, rm_own, tml / kTile)
+                 : tile_first_row(gbase, tcnt, Bp, G, E + rm_own, rm_own, tml / kTile)) +
                  int(code_m & 255u)
            : pos;
   issue_fence();
@@ -313,7 +467,7 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
                                      void* send, int32_t* row_token, int32_t* row_e,
                                      float* row_gates, float* row_weight, int32_t* slot_row,
                                      int32_t* n_rows, int64_t cs_tokens, int32_t* W,
-                                     hipStream_t stream) {
+                                     const ScanArgs* scan, hipStream_t stream) {
   const PlanLayout pl = plan_layout(T, E, k, R, dedup);
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
   const int32_t* header = reinterpret_cast<const int32_t*>(ws);
@@ -328,6 +482,16 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
     csb = int((cs.blocks() + 7) & ~int64_t(7));
     lds = kBmLdsBytes;
   }
+  // the plan scanned by the dispatch workgroups themselves (small plans)
+  ScanArgs sa{};
+  int sc = 0;
+  if (scan != nullptr) {
+    sa = *scan;
+    sc = (!dedup && sa.place != nullptr) ? 2 : 1;
+    const size_t sl = sc == 2 ? scan_lds_bytes<true>(pl.cols, E, int(pl.groups))
+                              : scan_lds_bytes<false>(pl.cols, E, int(pl.groups));
+    lds = lds > sl ? lds : sl;
+  }
   const int chunk = NV * kWave * 16;
   const int cpr = (row_bytes + chunk - 1) / chunk;
   const int64_t waves = T * cpr;
@@ -341,31 +505,62 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   uint8_t* sb = static_cast<uint8_t*>(send);
   const dim3 grid{unsigned(blocks + csb)}, block{256};
+#define MOE_DISPATCH(META, SC)                                                                 \
+  hipLaunchKernelGGL((dispatch_kernel<NV, NT, false, META, SC>), grid, block, lds, stream, xb,  \
+                     gate, T, row_bytes, k, cpr, gbase, tcnt, lslot, pl.tiles_pad, pl.groups,  \
+                     sb, row_token, row_e, row_weight, slot_row, nullptr, int64_t(0), cs, csb, \
+                     sa)
+#define MOE_DISPATCH_DEDUP(META, SC)                                                            \
+  hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT, META, SC>), grid, block, lds, stream, xb,   \
+                     idx, gate, T, row_bytes, E, k, cpr, gbase, tcnt, lslot, pl.tiles_pad,      \
+                     pl.groups, header, sb, row_token, row_e, row_gates, row_weight, slot_row,  \
+                     n_rows, cs, csb, sa)
   if (!dedup) {
     if (T == 0) return hipSuccess;
-    if (meta)
-      hipLaunchKernelGGL((dispatch_kernel<NV, NT, false, true>), grid, block, lds, stream, xb,
-                         gate, T, row_bytes, k, cpr, gbase, tcnt, lslot, pl.tiles_pad, pl.groups,
-                         sb, row_token, row_e, row_weight, slot_row, nullptr, int64_t(0), cs,
-                         csb);
-    else
-      hipLaunchKernelGGL((dispatch_kernel<NV, NT, false, false>), grid, block, lds, stream, xb,
-                         gate, T, row_bytes, k, cpr, gbase, tcnt, lslot, pl.tiles_pad, pl.groups,
-                         sb, row_token, row_e, row_weight, slot_row, nullptr, int64_t(0), cs,
-                         csb);
+    if (meta) {
+      if (sc == 0) MOE_DISPATCH(true, 0);
+      else if (sc == 1) MOE_DISPATCH(true, 1);
+      else MOE_DISPATCH(true, 2);
+    } else {
+      if (sc == 0) MOE_DISPATCH(false, 0);
+      else if (sc == 1) MOE_DISPATCH(false, 1);
+      else MOE_DISPATCH(false, 2);
+    }
   } else {
-    if (meta)
-      hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT, true>), grid, block, lds, stream, xb, idx,
-                         gate, T, row_bytes, E, k, cpr, gbase, tcnt, lslot, pl.tiles_pad,
-                         pl.groups, header, sb, row_token, row_e, row_gates, row_weight,
-                         slot_row, n_rows, cs, csb);
-    else
-      hipLaunchKernelGGL((dispatch_dedup_kernel<NV, NT, false>), grid, block, lds, stream, xb,
-                         idx, gate, T, row_bytes, E, k, cpr, gbase, tcnt, lslot, pl.tiles_pad,
-                         pl.groups, header, sb, row_token, row_e, row_gates, row_weight,
-                         slot_row, n_rows, cs, csb);
+    if (meta) {
+      if (sc == 0) MOE_DISPATCH_DEDUP(true, false);
+      else MOE_DISPATCH_DEDUP(true, true);
+    } else {
+      if (sc == 0) MOE_DISPATCH_DEDUP(false, false);
+      else MOE_DISPATCH_DEDUP(false, true);
+    }
   }
+#undef MOE_DISPATCH
+#undef MOE_DISPATCH_DEDUP
   return hipGetLastError();
+}
+
+static hipError_t launch_dispatch_any(const void* x, const int32_t* idx, const float* gate,
+                                      int64_t T, int row_bytes, int E, int k, int R,
+                                      const void* workspace, int dedup, void* send,
+                                      int32_t* row_token, int32_t* row_e, float* row_gates,
+                                      float* row_weight, int32_t* slot_row, int32_t* n_rows,
+                                      int64_t cs_tokens, int32_t* W, const ScanArgs* scan,
+                                      hipStream_t stream) {
+  switch (dispatch_nv(row_bytes)) {
+    case 4:
+      return launch_dispatch_nv<4>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
+                                   send, row_token, row_e, row_gates, row_weight, slot_row,
+                                   n_rows, cs_tokens, W, scan, stream);
+    case 2:
+      return launch_dispatch_nv<2>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
+                                   send, row_token, row_e, row_gates, row_weight, slot_row,
+                                   n_rows, cs_tokens, W, scan, stream);
+    default:
+      return launch_dispatch_nv<1>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
+                                   send, row_token, row_e, row_gates, row_weight, slot_row,
+                                   n_rows, cs_tokens, W, scan, stream);
+  }
 }
 
 // W non-null (and cs_tokens > 0): also the co-selection counts of the first
@@ -376,20 +571,48 @@ hipError_t launch_dispatch(const void* x, const int32_t* idx, const float* gate,
                            int32_t* row_e, float* row_gates, float* row_weight,
                            int32_t* slot_row, int32_t* n_rows, int64_t cs_tokens, int32_t* W,
                            hipStream_t stream) {
-  switch (dispatch_nv(row_bytes)) {
-    case 4:
-      return launch_dispatch_nv<4>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
-                                   send, row_token, row_e, row_gates, row_weight, slot_row,
-                                   n_rows, cs_tokens, W, stream);
-    case 2:
-      return launch_dispatch_nv<2>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
-                                   send, row_token, row_e, row_gates, row_weight, slot_row,
-                                   n_rows, cs_tokens, W, stream);
-    default:
-      return launch_dispatch_nv<1>(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup,
-                                   send, row_token, row_e, row_gates, row_weight, slot_row,
-                                   n_rows, cs_tokens, W, stream);
-  }
+  return launch_dispatch_any(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup, send,
+                             row_token, row_e, row_gates, row_weight, slot_row, n_rows,
+                             cs_tokens, W, nullptr, stream);
+}
+
+// Whether the dispatch workgroups (256 threads) can scan this plan themselves:
+// at most kEmbedMaxVec tile-count vectors (four per thread), and E and R at
+// most 256 for the column order.
+bool dispatch_scans_plan(int64_t T, int E, int k, int R, int dedup) {
+  const PlanLayout pl = plan_layout(T, E, k, R, dedup);
+  return T > 0 && E <= 256 && R <= 256 && int64_t(pl.cols) * pl.groups <= kEmbedMaxVec;
+}
+
+// The dispatch of a plan whose tile counts, slot codes and bitmaps the fused
+// routing kernel has just written (no scan yet): the dispatch workgroups scan
+// it, and workgroup 0 writes the counts, offsets, header and group bases.
+// Only for plans that dispatch_scans_plan() accepts.
+hipError_t launch_dispatch_scan(const void* x, const int32_t* idx, const float* gate, int64_t T,
+                                int row_bytes, int E, int k, int R, const int32_t* place,
+                                void* workspace, int dedup, void* send, int32_t* row_token,
+                                int32_t* row_e, float* row_gates, float* row_weight,
+                                int32_t* slot_row, int32_t* n_rows, int32_t* expert_counts,
+                                int32_t* rank_counts, int32_t* rank_offsets,
+                                int32_t* expert_offsets, int64_t cs_tokens, int32_t* W,
+                                hipStream_t stream) {
+  const PlanLayout pl = plan_layout(T, E, k, R, dedup);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  ScanArgs sa;
+  sa.B = int(pl.tiles);
+  sa.E = E;
+  sa.R = R;
+  sa.m = E / R;
+  sa.place = dedup ? nullptr : place;
+  sa.expert_counts = expert_counts;
+  sa.rank_counts = rank_counts;
+  sa.rank_offsets = rank_offsets;
+  sa.expert_offsets = dedup ? nullptr : expert_offsets;
+  sa.header = reinterpret_cast<int32_t*>(ws);
+  sa.gbase = reinterpret_cast<int32_t*>(ws + pl.base_off);
+  return launch_dispatch_any(x, idx, gate, T, row_bytes, E, k, R, workspace, dedup, send,
+                             row_token, row_e, row_gates, row_weight, slot_row, n_rows,
+                             cs_tokens, W, &sa, stream);
 }
 
 
@@ -408,11 +631,11 @@ static hipError_t launch_expand_nv(const void* rows, const float* row_gates,
   const int cpr = (row_bytes + chunk - 1) / chunk;
   const int64_t blocks = (cap * cpr + 3) / 4;
   constexpr bool NT = MOE_DISPATCH_NT != 0;
-  hipLaunchKernelGGL((dispatch_kernel<NV, NT, true, false>), dim3(unsigned(blocks)), dim3(256), 0,
-                     stream, static_cast<const uint8_t*>(rows), row_gates, cap, row_bytes, k, cpr,
+  hipLaunchKernelGGL((dispatch_kernel<NV, NT, true, false, 0>), dim3(unsigned(blocks)), dim3(256),
+                     0, stream, static_cast<const uint8_t*>(rows), row_gates, cap, row_bytes, k, cpr,
                      gbase, tcnt, lslot, pl.tiles_pad, pl.groups,
                      static_cast<uint8_t*>(expanded), exp_row, exp_expert, exp_gate, row_slot,
-                     n_rows, out_cap, CoselectBm{}, 0);
+                     n_rows, out_cap, CoselectBm{}, 0, ScanArgs{});
   return hipGetLastError();
 }
 

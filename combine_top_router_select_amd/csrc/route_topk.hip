@@ -416,6 +416,23 @@ static hipError_t launch_route_tile_e(const float* logits, int64_t T, int E, int
 hipError_t launch_coselect_bm(const uint64_t* bm, int64_t cs_tokens, int E, int32_t* W,
                               hipStream_t stream);
 
+// Whether the fused routing kernel takes this shape.
+bool route_tiles_fit(int64_t T, int E) { return T > 0 && E <= kFusedMaxExperts && T <= kFusedMaxTokens; }
+
+// The fused routing kernel alone (routing, tile counts, slot codes, bitmaps):
+// the plan without its scan, for a dispatch that scans it itself.  Only for
+// shapes that route_tiles_fit() accepts.
+hipError_t launch_route_tiles(const float* logits, int64_t T, int E, int k, int full_softmax,
+                              int R, const int32_t* place, int dedup, int32_t* idx, float* gate,
+                              void* workspace, hipStream_t stream) {
+  const bool v4 = E % 4 == 0;
+#define MOE_RTE(FU, VC) \
+  launch_route_tile_e<FU, VC>(logits, T, E, k, R, place, dedup, idx, gate, workspace, stream)
+  return full_softmax ? (v4 ? MOE_RTE(true, 4) : MOE_RTE(true, 1))
+                      : (v4 ? MOE_RTE(false, 4) : MOE_RTE(false, 1));
+#undef MOE_RTE
+}
+
 // Routing, the dispatch plan and (W non-null) the co-selection counts of the
 // first cs_tokens tokens: the fused kernel then the scan, or (large E or T)
 // the routing kernel, the counting kernel and the scan; then the co-selection

@@ -21,7 +21,7 @@ from ._lib import MoeError, check, lib, status_string  # noqa: F401
 __all__ = ["MoeError", "check_placement", "moe_status_string", "moe_workspace_bytes",
            "moe_route_topk", "moe_route_plan",
            "moe_send_counts", "moe_dispatch_permute", "moe_dispatch_permute_dedup",
-           "moe_dispatch_permute_noalloc",
+           "moe_dispatch_permute_noalloc", "moe_route_dispatch",
            "moe_combine", "moe_coselect_counts", "workspace", "moe_expand_workspace_bytes",
            "expand_workspace", "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
            "moe_placement_search", "moe_shuffle_fit", "moe_shuffle_predict",
@@ -273,6 +273,58 @@ def moe_dispatch_permute_dedup(x, topk_idx, topk_gate, n_experts, n_ranks, ws, o
           "moe_dispatch_permute_dedup")
     return {"send": send, "row_token": rt, "row_experts": rx, "row_gates": rg,
             "row_weight": rw, "slot_row": sr, "n_rows": nr}
+
+
+def moe_route_dispatch(logits, x, top_k, n_ranks, placement=None, dedup=False, softmax_all=False,
+                       ws=None, out=None, coselect=None, coselect_tokens=None, stream=None):
+    """moe_route_plan followed by moe_dispatch_permute (dedup: _dedup) in one C
+    call, with the same outputs; for small plans two launches instead of three.
+    `out` may hold any of the routing, count and dispatch outputs.  With
+    `coselect` (an [E][E] int32 matrix, accumulated into) the co-selection
+    counts of the first `coselect_tokens` tokens (default all) are added too.
+    Returns (topk_idx, topk_gate, counts, rows): counts as moe_route_plan
+    returns them (with "ws"), rows as the dispatch call returns them."""
+    _dev(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    bpe = _x_bpe(x)
+    if x.shape[0] != T or x.device != dev:
+        raise ValueError(f"x has {x.shape[0]} rows on {x.device}, logits {T} on {dev}")
+    H = x.shape[1]
+    k = int(top_k)
+    o = dict(out or {})
+    idx = _out(o, "topk_idx", (T, k), torch.int32, dev)
+    gate = _out(o, "topk_gate", (T, k), torch.float32, dev)
+    placement = _placement(placement, E, dev)
+    ws = workspace(T, E, k, n_ranks, dedup, dev) if ws is None else _ws(ws, dev)
+    ec, rc, ro, eo = _count_outputs(o, E, n_ranks, dedup, dev)
+    ncs, W = _coselect_arg(coselect, coselect_tokens, E, T, dev)
+    N = T * k
+    send = _out(o, "send", (N, H), x.dtype, dev, itemsize=bpe)
+    rt = _out(o, "row_token", (N,), torch.int32, dev)
+    rw = _out(o, "row_weight", (N,), torch.float32, dev)
+    sr = _out(o, "slot_row", (T, k), torch.int32, dev)
+    if dedup:
+        rx = _out(o, "row_experts", (N, k), torch.int32, dev)
+        rg = _out(o, "row_gates", (N, k), torch.float32, dev)
+        nr = _out(o, "n_rows", (1,), torch.int32, dev)
+    else:
+        rx = _out(o, "row_expert", (N,), torch.int32, dev)
+        rg = nr = None
+    check(lib().moe_route_dispatch(_ptr(logits), _ptr(x), T, H, E, k, int(bool(softmax_all)),
+                                   n_ranks, _ptr(placement), int(bool(dedup)), bpe, _ptr(idx),
+                                   _ptr(gate), _ptr(ec), _ptr(rc), _ptr(ro), _ptr(eo),
+                                   _ptr(send), _ptr(rt), _ptr(rx), _ptr(rg), _ptr(rw), _ptr(sr),
+                                   _ptr(nr), ncs, _ptr(W), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "moe_route_dispatch")
+    counts = {"expert_counts": ec, "rank_counts": rc, "rank_offsets": ro, "expert_offsets": eo,
+              "ws": ws}
+    rows = {"send": send, "row_token": rt, "row_weight": rw, "slot_row": sr}
+    if dedup:
+        rows.update(row_experts=rx, row_gates=rg, n_rows=nr)
+    else:
+        rows["row_expert"] = rx
+    return idx, gate, counts, rows
 
 
 def moe_dispatch_permute_noalloc(x, topk_idx, topk_gate, n_experts, n_ranks, placement=None,

@@ -258,6 +258,39 @@ int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx, const flo
                                int32_t* slot_row, int32_t* n_rows, int64_t coselect_tokens,
                                int32_t* coselect, void* stream);
 
+/* A1 + A2 + A3 + A4 (+ A6) - the whole send side in one call: the same as
+ * moe_route_plan() (coselect_tokens 0) followed by moe_dispatch_permute()
+ * (dedup = 0) or moe_dispatch_permute_dedup() (dedup = 1) on the same stream,
+ * with the same outputs bit for bit, and afterwards the same plan in the
+ * workspace (so further dispatch calls on it may follow).  For E <= 256 and a
+ * plan of at most 2048 vectors of 16 tile counts (C + R columns x ceil(T/512):
+ * e.g. T = 4096 with up to 256 experts) it takes two launches instead of three:
+ * the routing kernel counts the tiles, and the dispatch workgroups scan the
+ * plan themselves; larger plans take the three.
+ *   logits, gating                as moe_route_plan().
+ *   x, hidden_dim, bytes_per_element   as moe_dispatch_permute().
+ *   topk_idx, topk_gate           [T][k] out.
+ *   expert_counts .. expert_offsets    as moe_route_plan() (expert_offsets may
+ *                                 be NULL; dedup leaves it unwritten).
+ *   send, row_token, row_weight, slot_row   as the dispatch calls.
+ *   row_experts   dedup: [N][k] int32 out, as moe_dispatch_permute_dedup();
+ *                 plain: [N] int32 out, the row_expert of moe_dispatch_permute().
+ *   row_gates     dedup: [N][k] fp32 out; plain: ignored (may be NULL).
+ *   n_rows        dedup: [1] int32 out; plain: ignored (may be NULL).
+ *   coselect_tokens, coselect     as moe_dispatch_permute().
+ *   workspace, workspace_bytes    moe_workspace_bytes(tokens, n_experts,
+ *                                 top_k, n_ranks, dedup) bytes.
+ * Errors: those of moe_route_plan() and the dispatch call. */
+int moe_route_dispatch(const float* logits, const void* x, int64_t tokens, int hidden_dim,
+                       int n_experts, int top_k, int gating, int n_ranks,
+                       const int32_t* placement, int dedup, int bytes_per_element,
+                       int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+                       int32_t* rank_counts, int32_t* rank_offsets, int32_t* expert_offsets,
+                       void* send, int32_t* row_token, int32_t* row_experts, float* row_gates,
+                       float* row_weight, int32_t* slot_row, int32_t* n_rows,
+                       int64_t coselect_tokens, int32_t* coselect, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* A5 - combine ([EC] "The Communication Bottleneck"; [DD] "send_matrices.csv
  * columns": combine moves the dispatch volumes back): each token's output is the
  * weighted sum of the rows that served it.

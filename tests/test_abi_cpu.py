@@ -137,6 +137,39 @@ def test_route_plan_errors(lib):
     assert call(T=6400, dedup=1, wsb=wsd - 1) == EWS
 
 
+def test_route_dispatch_errors(lib):
+    f = lib.moe_route_dispatch
+    ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)
+    names = ["logits", "x", "T", "H", "E", "k", "gating", "R", "place", "dedup", "bpe", "idx",
+             "gate", "ec", "rc", "ro", "eo", "send", "rt", "rx", "rg", "rw", "sr", "nr", "ncs", "W",
+             "ws", "wsb", "stream"]
+    ok = [FAKE, FAKE, 100, 128, 8, 2, 0, 4, None, 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+          FAKE, FAKE, None, FAKE, FAKE, None, 0, None, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(ok)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return f(*a)
+
+    assert call(gating=2) == EINVAL
+    assert call(ncs=101, W=FAKE) == EINVAL                # more co-selection tokens than tokens
+    assert call(ncs=-1, W=FAKE) == EINVAL
+    for name in ("logits", "x", "idx", "gate", "ec", "rc", "ro", "send", "rt", "rx", "rw", "sr",
+                 "ws"):
+        assert call(**{name: None}) == EINVAL, name
+    assert call(bpe=3) == EUNSUP
+    assert call(H=4) == EUNSUP                            # 8-byte rows
+    assert call(R=3) == EINVAL
+    assert call(k=9) == EINVAL
+    assert call(k=17, E=64) == EUNSUP
+    assert call(wsb=ws - 1) == EWS
+    wsd = lib.moe_workspace_bytes(100, 8, 2, 4, 1)
+    assert call(dedup=1, wsb=wsd, rg=FAKE) == EINVAL      # dedup needs n_rows
+    assert call(dedup=1, wsb=wsd, nr=FAKE) == EINVAL      # and row_gates
+    assert call(dedup=1, wsb=wsd - 1, rg=FAKE, nr=FAKE) == EWS
+
+
 def test_dispatch_errors(lib):
     f = lib.moe_dispatch_permute
     ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)

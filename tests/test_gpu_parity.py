@@ -546,19 +546,107 @@ def test_dispatch_coselect(oracle_mod, T, E, k, R, dedup, n, source):
         assert (a.view(np.uint8) == b.view(np.uint8)).all(), key
 
 
+# ------------------------------------------- routing + dispatch in one call --
+
+ROUTE_DISPATCH_CASES = [  # T, E, k, R, H: the dispatch scans the plan itself unless noted
+    (4096, 64, 6, 16, 128),    # the benchmark's plain shape (narrow rows)
+    (4096, 128, 8, 16, 128),
+    (4096, 256, 8, 16, 64),    # 2048 tile-count vectors: the routing call scans, then the dispatch
+    (1000, 64, 6, 16, 256),
+    (300, 33, 5, 11, 128),     # E % 4 != 0, a partial last tile
+    (77, 8, 2, 4, 2048),       # one 4 KiB chunk per row, fewer tokens than a tile group
+    (33, 17, 1, 17, 64),
+    (1, 8, 2, 4, 128),
+    (16384, 128, 6, 32, 64),   # 5120 vectors: the routing call's scan, then the dispatch
+    (1000, 512, 4, 64, 64),    # E > 256: the separate routing and counting kernels
+]
+
+
+@pytest.mark.parametrize("T,E,k,R,H", ROUTE_DISPATCH_CASES)
+@pytest.mark.parametrize("dedup", [False, True])
+@pytest.mark.parametrize("pl", ["contiguous", "random"])
+def test_route_dispatch_parity(oracle_mod, T, E, k, R, H, dedup, pl):
+    """moe_route_dispatch against moe_route_plan + the dispatch call on the same
+    inputs: ids, gates, counts, offsets, every dispatch output, the co-selection
+    counts, and every byte of the plan left in the workspace; the rows also
+    against the oracle."""
+    softmax_all = (T + E) % 2 == 1
+    say(f"[route_dispatch] T={T} E={E} k={k} R={R} H={H} dedup={dedup} placement={pl} "
+        f"softmax_all={softmax_all}")
+    inp = WL.make_custom_inputs(T, H, E, seed=T * 7 + E + k + R)
+    placement = WL.random_placement(E, R, seed=T + 1) if pl == "random" else None
+    place_dev = to_dev(placement) if placement is not None else None
+    logits, x = to_dev(inp["logits"]), bf16_dev(inp["x_bits"])
+    cs = (T * 2) // 3
+    W1 = torch.zeros((E, E), dtype=torch.int32, device=logits.device)
+    W2 = torch.zeros((E, E), dtype=torch.int32, device=logits.device)
+    idx, gate, c, d = ops.moe_route_dispatch(logits, x, k, R, place_dev, dedup, softmax_all,
+                                             coselect=W1, coselect_tokens=cs)
+    idx2, gate2, c2 = ops.moe_route_plan(logits, k, R, place_dev, dedup, softmax_all)
+    f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+    d2 = f(x, idx2, gate2, E, R, c2["ws"], coselect=W2, coselect_tokens=cs)
+    sync()
+    assert (host(idx) == host(idx2)).all()
+    assert (host(gate).view(np.uint32) == host(gate2).view(np.uint32)).all()
+    for key in ("expert_counts", "rank_counts", "rank_offsets", "expert_offsets"):
+        if c[key] is not None:
+            assert (host(c[key]) == host(c2[key])).all(), key
+    rows = int(host(d2["n_rows"])[0]) if dedup else T * k
+    for key in d2:
+        h = bf16_host if d2[key].dtype == torch.bfloat16 else host
+        a, b = h(d[key]), h(d2[key])
+        if key not in ("slot_row", "n_rows"):
+            a, b = a[:rows], b[:rows]
+        assert (a.view(np.uint8) == b.view(np.uint8)).all(), key
+    assert (host(W1) == host(W2)).all()
+    assert _plan_equal(c["ws"], c2["ws"], T, E, k, R, dedup)
+    # and the rows against the oracle
+    idx_o = host(idx)
+    o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(
+        inp["x_bits"], idx_o, host(gate), E, R, placement)
+    assert rows == o["n_rows"]
+    assert (host(d["slot_row"]) == o["slot_row"]).all()
+    assert (bf16_host(d["send"][:rows]) == o["send"]).all()
+    assert (host(W1) == oracle_mod.coselect(idx_o, E, tokens=cs)).all()
+
+
+def test_route_dispatch_zero_tokens():
+    """No tokens: nothing routed or copied, zero counts and offsets, n_rows 0."""
+    dev = torch.device("cuda")
+    for dedup in (False, True):
+        logits = torch.empty((0, 64), dtype=torch.float32, device=dev)
+        x = torch.empty((0, 128), dtype=torch.bfloat16, device=dev)
+        out = {"expert_counts": torch.full((64,), 7, dtype=torch.int32, device=dev),
+               "rank_offsets": torch.full((17,), 7, dtype=torch.int32, device=dev)}
+        if dedup:
+            out["n_rows"] = torch.full((1,), 7, dtype=torch.int32, device=dev)
+        idx, gate, c, d = ops.moe_route_dispatch(logits, x, 6, 16, None, dedup, out=out)
+        sync()
+        assert (host(c["expert_counts"]) == 0).all() and (host(c["rank_offsets"]) == 0).all()
+        if dedup:
+            assert int(host(d["n_rows"])[0]) == 0
+
+
 # ------------------------------------------------------- full workloads --
 
 def gpu_chain(inp, w, dedup, stream=None, fused=False, cs_in="dispatch"):
-    """The whole hot path on the GPU, through the C ABI.  fused: the combined
-    routing call the benchmark times, with the co-selection counts in the
-    dispatch launch (cs_in "dispatch", the benchmark's setting) or in the
-    routing call ("route"); else the separate routing, counting and
-    co-selection calls."""
+    """The whole hot path on the GPU, through the C ABI.  cs_in "one_call":
+    moe_route_dispatch (routing, plan, rows and co-selection counts in one
+    call), the benchmark's setting; fused: the combined routing call, then the
+    dispatch, with the co-selection counts in the dispatch launch (cs_in
+    "dispatch") or in the routing call ("route"); else the separate routing,
+    counting and co-selection calls.  Then the combine."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
     place = to_dev(inp["placement"]) if inp["placement"] is not None else None
     logits = to_dev(inp["logits"])
     x = bf16_dev(inp["x_bits"])
     W = torch.zeros((E, E), dtype=torch.int32, device=logits.device)
+    if cs_in == "one_call":
+        idx, gate, c, d = ops.moe_route_dispatch(logits, x, k, R, place, dedup, coselect=W,
+                                                 coselect_tokens=w.coselect_tokens,
+                                                 stream=stream)
+        out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], stream=stream)
+        return idx, gate, c, d, out, W
     if fused:
         in_route = cs_in == "route"
         idx, gate, c = ops.moe_route_plan(logits, k, R, place, dedup,
@@ -580,20 +668,22 @@ def gpu_chain(inp, w, dedup, stream=None, fused=False, cs_in="dispatch"):
 def _cases():
     for name in WL.ORDER:
         for mode in WL.get(name).dispatch:
-            yield name, mode == "dedup", True, "dispatch"
-    yield "deepseek_moe_16b", False, True, "route"
-    yield "zyphra_top6_ep32", True, True, "route"
-    yield "deepseek_moe_16b", False, False, "-"
-    yield "zyphra_top6_ep32", True, False, "-"
+            yield name, mode == "dedup", True, "one_call"
+    for name, dedup in (("deepseek_moe_16b", False), ("zyphra_top6_ep32", True)):
+        yield name, dedup, True, "dispatch"
+        yield name, dedup, True, "route"
+        yield name, dedup, False, "-"
 
 
 @pytest.mark.parametrize("name,dedup,fused,cs_in", list(_cases()))
 def test_workload_end_to_end(oracle_mod, name, dedup, fused, cs_in):
-    """Full sizes, the launch configuration the benchmark times (fused: the
-    combined routing call, co-selection in the dispatch launch; a few cases
-    also with it in the routing call, or with the separate calls): logits ->
-    route, counts, co-selection -> dispatch -> combine (identity experts), all on
-    the GPU, against the oracle chain on the same inputs."""
+    """Full sizes, the launch configuration the benchmark times (one call for
+    routing, plan, rows and co-selection counts, then the combine; two
+    workloads also through the combined routing call with the co-selection
+    counts in the dispatch or the routing launch, and through the separate
+    calls): logits -> route, counts, co-selection -> dispatch -> combine
+    (identity experts), all on the GPU, against the oracle chain on the same
+    inputs."""
     w = WL.get(name)
     say(f"[e2e] {name} dedup={dedup} fused={fused} coselect={cs_in} T={w.tokens} "
         f"H={w.hidden_dim} E={w.n_experts} k={w.top_k} R={w.n_ranks}")
