@@ -79,7 +79,8 @@ KERNEL_SOURCES = {"moe_dispatch_permute": "csrc/dispatch.hip",
                   "moe_dispatch_permute_dedup": "csrc/dispatch.hip",
                   "moe_combine": "csrc/combine.hip",
                   "moe_expand_permute": "csrc/dispatch.hip",
-                  "moe_expand_reduce": "csrc/combine.hip"}
+                  "moe_expand_reduce": "csrc/combine.hip",
+                  "moe_route_dispatch": "csrc/dispatch.hip"}
 METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak)"
 
 
