@@ -77,11 +77,16 @@ __device__ __forceinline__ int tile_first_row(const int32_t* gbase,
 // (order_columns, as the scan kernel does), and looks its rows' positions up
 // in LDS.  The tile-count loads are issued before the row loads (a wave's loads
 // complete in order), so the scan runs while the rows are in flight; all of
-// them, four per thread, go out at once, since any load issued after the rows
-// would make the scan wait for the rows.
-// Workgroup 0 also writes the counts, offsets, header and group bases, so the
-// workspace then holds the same plan as after the scan kernel.
-constexpr int kEmbedMaxVec = 1024;
+// them, four per thread (eight for plans of more than 1024 vectors), go out at
+// once, since any load issued after the rows would make the scan wait for the
+// rows.  Workgroup 0 also writes the counts, offsets, header and group bases,
+// so the workspace then holds the same plan as after the scan kernel.
+constexpr int kEmbedMaxVec = 2048;
+
+// The dispatch kernels' scan variant: 0 none (bases from the workspace); 1 / 2
+// four vectors per thread, contiguous / explicit placement; 3 / 4 eight.
+constexpr bool sc_ranked(int sc) { return sc == 2 || sc == 4; }
+constexpr int sc_vectors(int sc) { return sc >= 3 ? 8 : 4; }
 
 struct ScanArgs {
   int B;                    // tiles
@@ -103,21 +108,21 @@ __host__ __device__ inline size_t scan_lds_bytes(int C, int E, int G) {
 }
 
 // The loads of scan_small_plan, issued by the dispatch kernels before their
-// row loads.
-constexpr int kScanEarly = kEmbedMaxVec / 256;  // 16-tile vectors per thread
+// row loads: N 16-tile vectors per thread.
+template <int N>
 struct ScanPrefetch {
-  u32x4 vv[kScanEarly];
+  u32x4 vv[N];
   int my_rank;  // RANKED: the rank of expert threadIdx.x
 };
 
-template <bool RANKED>
+template <bool RANKED, int N>
 __device__ __forceinline__ void scan_prefetch(const uint8_t* tcnt, int G, int C,
-                                              const ScanArgs& a, ScanPrefetch& pf) {
+                                              const ScanArgs& a, ScanPrefetch<N>& pf) {
   const int tid = threadIdx.x;
   const int V = C * G;
   const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);
 #pragma unroll
-  for (int i = 0; i < kScanEarly; ++i) {
+  for (int i = 0; i < N; ++i) {
     const int q = tid + i * int(blockDim.x);
     pf.vv[i] = g4[q < V ? q : V - 1];
   }
@@ -128,9 +133,9 @@ __device__ __forceinline__ void scan_prefetch(const uint8_t* tcnt, int G, int C,
 // when RANKED), after scan_prefetch.  Leaves s_col[p] = the first row of
 // position column p (the expert id when RANKED) and s_pre[c * G + g] = the
 // rows of column c in the groups before g; returns the total number of rows.
-template <bool DEDUP, bool RANKED>
+template <bool DEDUP, bool RANKED, int N>
 __device__ __forceinline__ int scan_small_plan(const uint8_t* tcnt, int G, const ScanArgs& a,
-                                               const ScanPrefetch& pf, bool outputs,
+                                               const ScanPrefetch<N>& pf, bool outputs,
                                                uint8_t* lds, int32_t*& s_col, int32_t*& s_pre) {
   const int E = a.E, R = a.R;
   const int C = E + (DEDUP ? R : 0);
@@ -145,9 +150,9 @@ __device__ __forceinline__ int scan_small_plan(const uint8_t* tcnt, int G, const
   const int V = C * G;
   const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);  // column c: vectors c*G .. c*G+G-1
   const int my_rank = pf.my_rank;
-  // byte sums of every 16-tile vector (V <= kScanEarly * blockDim.x: all prefetched)
+  // byte sums of every 16-tile vector (V <= N * blockDim.x: all prefetched)
 #pragma unroll
-  for (int i = 0; i < kScanEarly; ++i) {
+  for (int i = 0; i < N; ++i) {
     const int q = tid + i * int(blockDim.x);
     if (q < V) s_pre[q] = byte_sum(keep_bytes(pf.vv[i], a.B - 16 * (q % G)));
   }
@@ -235,8 +240,8 @@ __device__ __forceinline__ bool coselect_part(const CoselectBm& cs, int cs_block
 // Each wave copies the row chunk of (token t, chunk c) and writes the metadata
 // of token tm (when its wave index in the metadata order is chunk 0 of tm).
 // Every load of both is issued before the first wait, from in-bounds indices.
-// SC: 0 = group bases from the workspace; 1 = the workgroups scan the plan
-// (contiguous placement); 2 = the same with an explicit placement.
+// SC: 0 = group bases from the workspace; else the workgroups scan the plan
+// (sc_ranked, sc_vectors).
 template <int NV, bool NT, bool PAD, bool META, int SC>
 __global__ void __launch_bounds__(256)
 dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
@@ -275,9 +280,9 @@ dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
   const uint32_t code = lslot[tl * k + jl];  // (expert << 8) | rank inside the tile
   const uint32_t code_m = META ? lslot[tml * k + jl] : code;
   const float g_m = gate[tml * k + jl];
-  ScanPrefetch pf;
+  ScanPrefetch<sc_vectors(SC)> pf;
   if (SC) {
-    scan_prefetch<SC == 2>(tcnt, int(G), sa.E, sa, pf);
+    scan_prefetch<sc_ranked(SC)>(tcnt, int(G), sa.E, sa, pf);
     issue_fence();
   }
   u32x4 v[NV];
@@ -287,8 +292,8 @@ dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
   int32_t* s_pre = nullptr;
   if (SC) {
     extern __shared__ uint64_t s_scan[];
-    scan_small_plan<false, SC == 2>(tcnt, int(G), sa, pf, bid == 0,
-                                    reinterpret_cast<uint8_t*>(s_scan), s_col, s_pre);
+    scan_small_plan<false, sc_ranked(SC)>(tcnt, int(G), sa, pf, bid == 0,
+                                          reinterpret_cast<uint8_t*>(s_scan), s_col, s_pre);
     if (!copy && !meta) return;
   }
   const bool has = !PAD || code != kNoSlot;
@@ -327,8 +332,8 @@ dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
   }
 }
 
-// SC: the workgroups scan the plan (see dispatch_kernel).
-template <int NV, bool NT, bool META, bool SC>
+// SC: the workgroups scan the plan (see dispatch_kernel; never ranked).
+template <int NV, bool NT, bool META, int SC>
 __global__ void __launch_bounds__(256)
 dispatch_dedup_kernel(const uint8_t* x, const int32_t* __restrict__ idx,
                       const float* __restrict__ gate, int64_t T, int row_bytes, int E, int k,
@@ -359,7 +364,7 @@ dispatch_dedup_kernel(const uint8_t* x, const int32_t* __restrict__ idx,
   const uint32_t code_m = META ? lslot[tml * k + jl] : code;
   const int e_m = clampi(idx[tml * k + jl], 0, E - 1);
   const float g_m = gate[tml * k + jl];
-  ScanPrefetch pf;
+  ScanPrefetch<sc_vectors(SC)> pf;
   if (SC) {
     scan_prefetch<false>(tcnt, int(G), E + sa.R, sa, pf);
     issue_fence();
@@ -487,9 +492,11 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
   int sc = 0;
   if (scan != nullptr) {
     sa = *scan;
-    sc = (!dedup && sa.place != nullptr) ? 2 : 1;
-    const size_t sl = sc == 2 ? scan_lds_bytes<true>(pl.cols, E, int(pl.groups))
-                              : scan_lds_bytes<false>(pl.cols, E, int(pl.groups));
+    const bool ranked = !dedup && sa.place != nullptr;
+    const bool wide = int64_t(pl.cols) * pl.groups > 4 * 256;
+    sc = (ranked ? 2 : 1) + (wide ? 2 : 0);
+    const size_t sl = ranked ? scan_lds_bytes<true>(pl.cols, E, int(pl.groups))
+                             : scan_lds_bytes<false>(pl.cols, E, int(pl.groups));
     lds = lds > sl ? lds : sl;
   }
   const int chunk = NV * kWave * 16;
@@ -517,22 +524,26 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
                      n_rows, cs, csb, sa)
   if (!dedup) {
     if (T == 0) return hipSuccess;
-    if (meta) {
-      if (sc == 0) MOE_DISPATCH(true, 0);
-      else if (sc == 1) MOE_DISPATCH(true, 1);
-      else MOE_DISPATCH(true, 2);
-    } else {
-      if (sc == 0) MOE_DISPATCH(false, 0);
-      else if (sc == 1) MOE_DISPATCH(false, 1);
-      else MOE_DISPATCH(false, 2);
+    switch (sc * 2 + (meta ? 1 : 0)) {
+      case 0: MOE_DISPATCH(false, 0); break;
+      case 1: MOE_DISPATCH(true, 0); break;
+      case 2: MOE_DISPATCH(false, 1); break;
+      case 3: MOE_DISPATCH(true, 1); break;
+      case 4: MOE_DISPATCH(false, 2); break;
+      case 5: MOE_DISPATCH(true, 2); break;
+      case 6: MOE_DISPATCH(false, 3); break;
+      case 7: MOE_DISPATCH(true, 3); break;
+      case 8: MOE_DISPATCH(false, 4); break;
+      default: MOE_DISPATCH(true, 4); break;
     }
   } else {
-    if (meta) {
-      if (sc == 0) MOE_DISPATCH_DEDUP(true, false);
-      else MOE_DISPATCH_DEDUP(true, true);
-    } else {
-      if (sc == 0) MOE_DISPATCH_DEDUP(false, false);
-      else MOE_DISPATCH_DEDUP(false, true);
+    switch (sc * 2 + (meta ? 1 : 0)) {  // sc is 0, 1 or 3 (never ranked)
+      case 0: MOE_DISPATCH_DEDUP(false, 0); break;
+      case 1: MOE_DISPATCH_DEDUP(true, 0); break;
+      case 2: MOE_DISPATCH_DEDUP(false, 1); break;
+      case 3: MOE_DISPATCH_DEDUP(true, 1); break;
+      case 6: MOE_DISPATCH_DEDUP(false, 3); break;
+      default: MOE_DISPATCH_DEDUP(true, 3); break;
     }
   }
 #undef MOE_DISPATCH
@@ -577,7 +588,7 @@ hipError_t launch_dispatch(const void* x, const int32_t* idx, const float* gate,
 }
 
 // Whether the dispatch workgroups (256 threads) can scan this plan themselves:
-// at most kEmbedMaxVec tile-count vectors (four per thread), and E and R at
+// at most kEmbedMaxVec tile-count vectors (eight per thread), and E and R at
 // most 256 for the column order.
 bool dispatch_scans_plan(int64_t T, int E, int k, int R, int dedup) {
   const PlanLayout pl = plan_layout(T, E, k, R, dedup);

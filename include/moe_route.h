@@ -263,8 +263,8 @@ int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx, const flo
  * (dedup = 0) or moe_dispatch_permute_dedup() (dedup = 1) on the same stream,
  * with the same outputs bit for bit, and afterwards the same plan in the
  * workspace (so further dispatch calls on it may follow).  For E <= 256 and a
- * plan of at most 1024 vectors of 16 tile counts ((E, + R in dedup mode)
- * columns x ceil(T / 512): e.g. T = 4096 with up to 128 experts, plain, or 112
+ * plan of at most 2048 vectors of 16 tile counts ((E, + R in dedup mode)
+ * columns x ceil(T / 512): e.g. T = 4096 with up to 256 experts, plain, or 240
  * experts and 16 ranks, dedup) it takes two launches instead of three: the
  * routing kernel counts the tiles, and the dispatch workgroups scan the plan
  * themselves; larger plans take the three.

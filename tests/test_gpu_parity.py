@@ -550,8 +550,8 @@ def test_dispatch_coselect(oracle_mod, T, E, k, R, dedup, n, source):
 
 ROUTE_DISPATCH_CASES = [  # T, E, k, R, H: the dispatch scans the plan itself unless noted
     (4096, 64, 6, 16, 128),    # the benchmark's plain shape (narrow rows)
-    (4096, 128, 8, 16, 128),
-    (4096, 256, 8, 16, 64),    # 2048 tile-count vectors: the routing call scans, then the dispatch
+    (4096, 128, 8, 16, 128),   # dedup: 1152 vectors, eight per thread
+    (4096, 256, 8, 16, 64),    # 2048 tile-count vectors (eight per thread); dedup: the scan kernel
     (1000, 64, 6, 16, 256),
     (300, 33, 5, 11, 128),     # E % 4 != 0, a partial last tile
     (77, 8, 2, 4, 2048),       # one 4 KiB chunk per row, fewer tokens than a tile group
