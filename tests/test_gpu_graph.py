@@ -55,17 +55,26 @@ def _buffers(w, dedup, dev):
     return b
 
 
-def _step(w, dedup, logits, x, place, b, fused=False):
+def _step(w, dedup, logits, x, place, b, mode="separate"):
+    """mode: "separate" calls; "plan": moe_route_plan (with the co-selection
+    counts) then the dispatch; "one": moe_route_dispatch (with them)."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
-    if fused:   # routing, plan and co-selection counts in one call
-        c = ops.moe_route_plan(logits, k, R, place, dedup, topk_idx=b["idx"], topk_gate=b["gate"],
-                               ws=b["ws"], out=b["cnt"], coselect=b["W"],
-                               coselect_tokens=w.coselect_tokens)[2]
+    if mode == "one":   # routing, plan, rows and co-selection counts in one call
+        d = ops.moe_route_dispatch(logits, x, k, R, place, dedup,
+                                   out={"topk_idx": b["idx"], "topk_gate": b["gate"], **b["cnt"],
+                                        **b["disp"]},
+                                   ws=b["ws"], coselect=b["W"],
+                                   coselect_tokens=w.coselect_tokens)[3]
     else:
-        ops.moe_route_topk(logits, k, b["idx"], b["gate"])
-        c = ops.moe_send_counts(b["idx"], E, R, place, dedup, ws=b["ws"], out=b["cnt"])
-    f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
-    d = f(x, b["idx"], b["gate"], E, R, c["ws"], out=b["disp"])
+        if mode == "plan":   # routing, plan and co-selection counts in one call
+            c = ops.moe_route_plan(logits, k, R, place, dedup, topk_idx=b["idx"],
+                                   topk_gate=b["gate"], ws=b["ws"], out=b["cnt"], coselect=b["W"],
+                                   coselect_tokens=w.coselect_tokens)[2]
+        else:
+            ops.moe_route_topk(logits, k, b["idx"], b["gate"])
+            c = ops.moe_send_counts(b["idx"], E, R, place, dedup, ws=b["ws"], out=b["cnt"])
+        f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+        d = f(x, b["idx"], b["gate"], E, R, c["ws"], out=b["disp"])
     ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b["out"])
     if dedup:
         ops.moe_expand_counts(d["row_experts"], d["n_rows"], E, R, place, ws=b["ews"],
@@ -75,7 +84,7 @@ def _step(w, dedup, logits, x, place, b, fused=False):
         red = ops.moe_expand_reduce(ex["expanded"], ex["exp_gate"], ex["row_slot"], d["n_rows"],
                                     out=b["red"])
         ops.moe_combine(red, None, d["slot_row"], out=b["out2"])
-    if not fused:
+    if mode == "separate":
         ops.moe_coselect_counts(b["idx"], E, tokens=w.coselect_tokens, coselect=b["W"])
 
 
@@ -106,17 +115,20 @@ def _snapshot(b):
     return snap
 
 
-@pytest.mark.parametrize("name,dedup,fused", [
-    ("deepseek_moe_16b", False, False), ("zyphra_top6_ep32", True, False),
-    ("deepseek_moe_16b", False, True), ("e256_top8_h2048", False, True),
-    ("zyphra_top2_ep8", True, True)])
-def test_graph_replays_match_eager(name, dedup, fused):
-    """fused: moe_route_plan in place of the routing, counting and co-selection
-    calls (the fused kernel up to 128 experts, the tile-bitmap co-selection
-    above); the eager reference uses the separate calls, so the replays also
-    check the two paths against each other."""
+@pytest.mark.parametrize("name,dedup,mode", [
+    ("deepseek_moe_16b", False, "separate"), ("zyphra_top6_ep32", True, "separate"),
+    ("deepseek_moe_16b", False, "plan"), ("e256_top8_h2048", False, "plan"),
+    ("zyphra_top2_ep8", True, "plan"),
+    ("deepseek_moe_16b", False, "one"), ("qwen3_30b_a3b", True, "one"),
+    ("e256_top8_h2048", False, "one"), ("zyphra_top6_ep32", True, "one")])
+def test_graph_replays_match_eager(name, dedup, mode):
+    """mode "plan": moe_route_plan in place of the routing, counting and
+    co-selection calls; "one": moe_route_dispatch in place of those and the
+    dispatch (the dispatch scanning the plan itself at 4096 tokens, the scan
+    kernel at 16384).  The eager reference uses the separate calls, so the
+    replays also check the paths against each other."""
     w = WL.get(name)
-    say(f"[graph] {name} dedup={dedup} fused={fused}")
+    say(f"[graph] {name} dedup={dedup} mode={mode}")
     dev = torch.device("cuda:0")
     inp = WL.make_inputs(w)
     logits = to_dev(inp["logits"])
@@ -132,12 +144,12 @@ def test_graph_replays_match_eager(name, dedup, fused):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        _step(w, dedup, logits, x, place, gb, fused)   # warm up outside capture
+        _step(w, dedup, logits, x, place, gb, mode)   # warm up outside capture
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _step(w, dedup, logits, x, place, gb, fused)
+        _step(w, dedup, logits, x, place, gb, mode)
     torch.cuda.synchronize()
     for rep in range(4):
         # scramble the outputs with eager work, then replay

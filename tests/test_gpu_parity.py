@@ -610,6 +610,36 @@ def test_route_dispatch_parity(oracle_mod, T, E, k, R, H, dedup, pl):
     assert (host(W1) == oracle_mod.coselect(idx_o, E, tokens=cs)).all()
 
 
+@pytest.mark.parametrize("bpe,dedup", [(1, False), (1, True), (4, False), (4, True)])
+def test_route_dispatch_row_sizes(bpe, dedup):
+    """fp8 (1-byte) and 4-byte rows through moe_route_dispatch, byte for byte
+    against moe_route_plan + the dispatch call (rows are copied as bytes)."""
+    T, E, k, R, H = 1500, 64, 6, 16, 512
+    say(f"[route_dispatch rows] bpe={bpe} dedup={dedup}")
+    inp = WL.make_custom_inputs(T, 8, E, seed=bpe * 10 + int(dedup))
+    logits = to_dev(inp["logits"])
+    rng = np.random.default_rng(bpe)
+    dt = {1: torch.uint8, 4: torch.int32}[bpe]
+    raw = rng.integers(0, 256, size=(T, H * bpe), dtype=np.uint8)
+    x = to_dev(raw).view(dt)
+    idx, gate, c, d = ops.moe_route_dispatch(logits, x, k, R, None, dedup)
+    idx2, gate2, c2 = ops.moe_route_plan(logits, k, R, None, dedup)
+    f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
+    d2 = f(x, idx2, gate2, E, R, c2["ws"])
+    sync()
+    assert (host(idx) == host(idx2)).all()
+    rows = int(host(d2["n_rows"])[0]) if dedup else T * k
+    assert int(host(c["rank_offsets"])[-1]) == rows
+    for key in d2:
+        a, b = host(d[key]), host(d2[key])
+        if key not in ("slot_row", "n_rows"):
+            a, b = a[:rows], b[:rows]
+        assert (a.view(np.uint8) == b.view(np.uint8)).all(), key
+    # every sent row is its token's row
+    send = host(d["send"])[:rows].view(np.uint8).reshape(rows, H * bpe)
+    assert (send == raw[host(d["row_token"])[:rows]]).all()
+
+
 def test_route_dispatch_zero_tokens():
     """No tokens: nothing routed or copied, zero counts and offsets, n_rows 0."""
     dev = torch.device("cuda")
