@@ -36,7 +36,7 @@ hipError_t launch_route_plan(const float*, int64_t, int, int, int, int, const in
 bool route_tiles_fit(int64_t, int);
 hipError_t launch_route_tiles(const float*, int64_t, int, int, int, int, const int32_t*, int,
                               int32_t*, float*, void*, hipStream_t);
-bool dispatch_scans_plan(int64_t, int, int, int, int);
+bool dispatch_scans_plan(int64_t, int, int, int, int, int);
 hipError_t launch_dispatch_scan(const void*, const int32_t*, const float*, int64_t, int, int, int,
                                 int, const int32_t*, void*, int, void*, int32_t*, int32_t*,
                                 float*, float*, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*,
@@ -239,7 +239,7 @@ MOE_API int moe_route_dispatch(const float* logits, const void* x, int64_t token
   int32_t* eo = d ? nullptr : expert_offsets;
   hipStream_t s = as_stream(stream);
   if (moe::route_tiles_fit(tokens, n_experts) &&
-      moe::dispatch_scans_plan(tokens, n_experts, top_k, n_ranks, d)) {
+      moe::dispatch_scans_plan(tokens, n_experts, top_k, n_ranks, d, rb)) {
     // two launches: routing with the tile counts, then the dispatch, whose
     // workgroups scan the plan themselves
     if (moe::launch_route_tiles(logits, tokens, n_experts, top_k, gating, n_ranks, placement, d,

@@ -69,19 +69,31 @@ __device__ __forceinline__ int tile_first_row(const int32_t* gbase,
 
 // ------------------------------------------ plans scanned by the dispatch --
 //
-// For a small plan (at most kEmbedMaxVec 16-tile vectors of tile counts) the
-// dispatch workgroups do the plan's scan themselves, so the routing call needs
-// no scan launch of its own (moe_route_dispatch): every workgroup reads all
-// tile counts (L2 hits: 8 KiB at 4096 tokens, 64 experts), takes every
-// column's total and group prefixes in LDS, orders and scans the columns
-// (order_columns, as the scan kernel does), and looks its rows' positions up
-// in LDS.  The tile-count loads are issued before the row loads (a wave's loads
-// complete in order), so the scan runs while the rows are in flight; all of
-// them, four per thread (eight for plans of more than 1024 vectors), go out at
-// once, since any load issued after the rows would make the scan wait for the
-// rows.  Workgroup 0 also writes the counts, offsets, header and group bases,
-// so the workspace then holds the same plan as after the scan kernel.
+// For a plan of at most kEmbedMaxVec 16-tile vectors of position-column tile
+// counts (the expert columns; the rank columns in dedup mode) the dispatch
+// workgroups do the plan's scan themselves, so the routing call needs no scan
+// launch of its own (moe_route_dispatch): every workgroup reads the position
+// columns' tile counts (L2 hits: 8 KiB at 4096 tokens and 64 experts, 16 KiB
+// for 32 ranks at 16384 tokens), takes every such column's total and group
+// prefixes in LDS, orders and scans the columns (order_columns, as the scan
+// kernel does), and looks its rows' positions up in LDS.  The tile-count loads
+// are issued before the row loads (a wave's loads complete in order), so the
+// scan runs while the rows are in flight; all of them, four per thread (eight
+// for plans of more than 1024 vectors), go out at once, since any load issued
+// after the rows would make the scan wait for the rows.  Workgroup 0 also
+// writes the counts, offsets, header and group bases, so the workspace then
+// holds the same plan as after the scan kernel; in dedup mode it also adds up
+// the expert columns for the per-expert counts, which no other workgroup needs
+// (loads issued after its rows: only workgroup 0 waits for them).
 constexpr int kEmbedMaxVec = 2048;
+// ... and at most this many tile-count vectors summed over the dispatch's copy
+// workgroups (each reads them all, 16 bytes each: 64 MiB of L2 reads).  The
+// scan costs the dispatch more the more of them there are: at 16384 tokens of
+// 8 KiB rows (8192 workgroups), +2.5 us for 8 ranks (256 vectors: 32 MiB, a
+// net 2.7 us gain on the 110 us top-2 dedup step) but +5.6 us for 32 ranks
+// (1024 vectors: 128 MiB), as much as the scan kernel it replaces (5.4 us), and
+// that top-6 step ran 11 us slower with two batches overlapped on two streams.
+constexpr int64_t kEmbedMaxVecBlocks = int64_t(4) << 20;
 
 // The dispatch kernels' scan variant: 0 none (bases from the workspace); 1 / 2
 // four vectors per thread, contiguous / explicit placement; 3 / 4 eight.
@@ -100,27 +112,32 @@ struct ScanArgs {
   int32_t* gbase;           // the plan's group bases, written by workgroup 0
 };
 
-// Dynamic LDS of scan_small_plan: s_tot[C], s_col[E], s_pre[C * G], OrderLds.
+// Dynamic LDS of scan_small_plan: s_tot[C], s_col[E], s_pre[CP * G], OrderLds
+// (C columns counted, CP of them position columns).
+__host__ __device__ inline size_t scan_head_bytes(int C, int CP, int E, int G) {
+  const size_t head = (size_t(C) + size_t(E) + size_t(CP) * size_t(G)) * 4;
+  return (head + 7) / 8 * 8;
+}
 template <bool RANKED>
-__host__ __device__ inline size_t scan_lds_bytes(int C, int E, int G) {
-  const size_t head = (size_t(C) + size_t(E) + size_t(C) * size_t(G)) * 4;
-  return (head + 7) / 8 * 8 + sizeof(OrderLds<RANKED>);
+__host__ __device__ inline size_t scan_lds_bytes(int C, int CP, int E, int G) {
+  return scan_head_bytes(C, CP, E, G) + sizeof(OrderLds<RANKED>);
 }
 
 // The loads of scan_small_plan, issued by the dispatch kernels before their
-// row loads: N 16-tile vectors per thread.
+// row loads: N 16-tile vectors of the position columns per thread.
 template <int N>
 struct ScanPrefetch {
   u32x4 vv[N];
   int my_rank;  // RANKED: the rank of expert threadIdx.x
 };
 
+// cbase, CP: the tcnt column of position column 0 and the position columns.
 template <bool RANKED, int N>
-__device__ __forceinline__ void scan_prefetch(const uint8_t* tcnt, int G, int C,
+__device__ __forceinline__ void scan_prefetch(const uint8_t* tcnt, int G, int cbase, int CP,
                                               const ScanArgs& a, ScanPrefetch<N>& pf) {
   const int tid = threadIdx.x;
-  const int V = C * G;
-  const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);
+  const int V = CP * G;
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt) + int64_t(cbase) * G;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int q = tid + i * int(blockDim.x);
@@ -130,9 +147,10 @@ __device__ __forceinline__ void scan_prefetch(const uint8_t* tcnt, int G, int C,
 }
 
 // Every thread of the workgroup calls it (blockDim.x >= max(CP, R), and E
-// when RANKED), after scan_prefetch.  Leaves s_col[p] = the first row of
-// position column p (the expert id when RANKED) and s_pre[c * G + g] = the
-// rows of column c in the groups before g; returns the total number of rows.
+// when RANKED or, in dedup mode, with `outputs`), after scan_prefetch.  Leaves
+// s_col[p] = the first row of position column p (the expert id when RANKED)
+// and s_pre[p * G + g] = the rows of position column p in the groups before g;
+// returns the total number of rows.
 template <bool DEDUP, bool RANKED, int N>
 __device__ __forceinline__ int scan_small_plan(const uint8_t* tcnt, int G, const ScanArgs& a,
                                                const ScanPrefetch<N>& pf, bool outputs,
@@ -144,12 +162,10 @@ __device__ __forceinline__ int scan_small_plan(const uint8_t* tcnt, int G, const
   int32_t* s_tot = reinterpret_cast<int32_t*>(lds);
   s_col = s_tot + C;
   s_pre = s_col + E;
-  const size_t head = (size_t(C) + size_t(E) + size_t(C) * size_t(G)) * 4;
-  OrderLds<RANKED>& L = *reinterpret_cast<OrderLds<RANKED>*>(lds + (head + 7) / 8 * 8);
+  OrderLds<RANKED>& L =
+      *reinterpret_cast<OrderLds<RANKED>*>(lds + scan_head_bytes(C, CP, E, G));
   const int tid = threadIdx.x;
-  const int V = C * G;
-  const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);  // column c: vectors c*G .. c*G+G-1
-  const int my_rank = pf.my_rank;
+  const int V = CP * G;
   // byte sums of every 16-tile vector (V <= N * blockDim.x: all prefetched)
 #pragma unroll
   for (int i = 0; i < N; ++i) {
@@ -157,24 +173,39 @@ __device__ __forceinline__ int scan_small_plan(const uint8_t* tcnt, int G, const
     if (q < V) s_pre[q] = byte_sum(keep_bytes(pf.vv[i], a.B - 16 * (q % G)));
   }
   order_init<RANKED>(L);
+  const bool expert_sums = DEDUP && outputs;  // the per-expert counts (workgroup 0)
+  if (expert_sums && tid < E) s_tot[tid] = 0;
   __syncthreads();
-  // each column's total and exclusive prefix over its groups
-  for (int c = tid; c < C; c += blockDim.x) {
+  // each position column's total and exclusive prefix over its groups
+  for (int p = tid; p < CP; p += blockDim.x) {
     int run = 0;
     for (int g = 0; g < G; ++g) {
-      const int x = s_pre[c * G + g];
-      s_pre[c * G + g] = run;
+      const int x = s_pre[p * G + g];
+      s_pre[p * G + g] = run;
       run += x;
     }
-    s_tot[c] = run;
+    s_tot[cbase + p] = run;
+  }
+  if (expert_sums) {  // four loads in flight per thread, then their sums
+    const u32x4* g4 = reinterpret_cast<const u32x4*>(tcnt);
+    const int EV = E * G, nt = blockDim.x;
+    for (int q0 = tid; q0 < EV; q0 += 4 * nt) {
+      u32x4 ev[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ev[i] = g4[q0 + i * nt < EV ? q0 + i * nt : EV - 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = q0 + i * nt;
+        if (q < EV) atomicAdd(&s_tot[q / G], byte_sum(keep_bytes(ev[i], a.B - 16 * (q % G))));
+      }
+    }
   }
   __syncthreads();
-  const int total = order_columns<DEDUP, RANKED>(s_tot, s_col, L, E, R, a.m, my_rank, outputs,
+  const int total = order_columns<DEDUP, RANKED>(s_tot, s_col, L, E, R, a.m, pf.my_rank, outputs,
                                                  a.expert_counts, a.rank_counts, a.rank_offsets,
                                                  a.expert_offsets, a.header);
   if (outputs)
-    for (int i = tid; i < CP * G; i += blockDim.x)
-      a.gbase[i] = s_col[i / G] + s_pre[(cbase + i / G) * G + i % G];
+    for (int i = tid; i < V; i += blockDim.x) a.gbase[i] = s_col[i / G] + s_pre[i];
   return total;
 }
 
@@ -184,7 +215,7 @@ __device__ __forceinline__ int lds_first_row(const int32_t* s_col, const int32_t
                                              const uint8_t* tcnt, int64_t Bp, int64_t G,
                                              int tcol, int col, int64_t b) {
   const u32x4 tv = load16(tcnt + tcol * Bp + (b & ~int64_t(15)));
-  return s_col[col] + s_pre[tcol * G + (b >> 4)] + byte_sum(keep_bytes(tv, int(b & 15)));
+  return s_col[col] + s_pre[col * G + (b >> 4)] + byte_sum(keep_bytes(tv, int(b & 15)));
 }
 
 template <int NV, bool NT>
@@ -282,7 +313,7 @@ dispatch_kernel(const uint8_t* x, const float* __restrict__ gate, int64_t T,
   const float g_m = gate[tml * k + jl];
   ScanPrefetch<sc_vectors(SC)> pf;
   if (SC) {
-    scan_prefetch<sc_ranked(SC)>(tcnt, int(G), sa.E, sa, pf);
+    scan_prefetch<sc_ranked(SC)>(tcnt, int(G), 0, sa.E, sa, pf);
     issue_fence();
   }
   u32x4 v[NV];
@@ -366,7 +397,7 @@ dispatch_dedup_kernel(const uint8_t* x, const int32_t* __restrict__ idx,
   const float g_m = gate[tml * k + jl];
   ScanPrefetch<sc_vectors(SC)> pf;
   if (SC) {
-    scan_prefetch<false>(tcnt, int(G), E + sa.R, sa, pf);
+    scan_prefetch<false>(tcnt, int(G), E, sa.R, sa, pf);
     issue_fence();
   }
   u32x4 v[NV];
@@ -493,10 +524,11 @@ static hipError_t launch_dispatch_nv(const void* x, const int32_t* idx, const fl
   if (scan != nullptr) {
     sa = *scan;
     const bool ranked = !dedup && sa.place != nullptr;
-    const bool wide = int64_t(pl.cols) * pl.groups > 4 * 256;
+    const bool wide = int64_t(pl.pos_cols) * pl.groups > 4 * 256;
     sc = (ranked ? 2 : 1) + (wide ? 2 : 0);
-    const size_t sl = ranked ? scan_lds_bytes<true>(pl.cols, E, int(pl.groups))
-                             : scan_lds_bytes<false>(pl.cols, E, int(pl.groups));
+    const int G = int(pl.groups);
+    const size_t sl = ranked ? scan_lds_bytes<true>(pl.cols, pl.pos_cols, E, G)
+                             : scan_lds_bytes<false>(pl.cols, pl.pos_cols, E, G);
     lds = lds > sl ? lds : sl;
   }
   const int chunk = NV * kWave * 16;
@@ -587,12 +619,23 @@ hipError_t launch_dispatch(const void* x, const int32_t* idx, const float* gate,
                              cs_tokens, W, nullptr, stream);
 }
 
-// Whether the dispatch workgroups (256 threads) can scan this plan themselves:
-// at most kEmbedMaxVec tile-count vectors (eight per thread), and E and R at
-// most 256 for the column order.
-bool dispatch_scans_plan(int64_t T, int E, int k, int R, int dedup) {
+// Copy workgroups of a dispatch of T rows of row_bytes (before padding the
+// grid to a multiple of 8): four waves, each one row chunk.
+static int64_t dispatch_copy_blocks(int64_t T, int row_bytes) {
+  const int chunk = dispatch_nv(row_bytes) * kWave * 16;
+  const int64_t cpr = (row_bytes + chunk - 1) / chunk;
+  return (T * cpr + 3) / 4;
+}
+
+// Whether the dispatch workgroups (256 threads) scan this plan themselves: at
+// most kEmbedMaxVec tile-count vectors of position columns (eight per thread),
+// at most kEmbedMaxVecBlocks of them over all copy workgroups, and E and R at
+// most 256 for the column order and the counts.
+bool dispatch_scans_plan(int64_t T, int E, int k, int R, int dedup, int row_bytes) {
   const PlanLayout pl = plan_layout(T, E, k, R, dedup);
-  return T > 0 && E <= 256 && R <= 256 && int64_t(pl.cols) * pl.groups <= kEmbedMaxVec;
+  const int64_t nvec = int64_t(pl.pos_cols) * pl.groups;
+  return T > 0 && E <= 256 && R <= 256 && nvec <= kEmbedMaxVec &&
+         nvec * dispatch_copy_blocks(T, row_bytes) <= kEmbedMaxVecBlocks;
 }
 
 // The dispatch of a plan whose tile counts, slot codes and bitmaps the fused

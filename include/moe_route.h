@@ -262,12 +262,15 @@ int moe_dispatch_permute_dedup(const void* x, const int32_t* topk_idx, const flo
  * moe_route_plan() (coselect_tokens 0) followed by moe_dispatch_permute()
  * (dedup = 0) or moe_dispatch_permute_dedup() (dedup = 1) on the same stream,
  * with the same outputs bit for bit, and afterwards the same plan in the
- * workspace (so further dispatch calls on it may follow).  For E <= 256 and a
- * plan of at most 2048 vectors of 16 tile counts ((E, + R in dedup mode)
- * columns x ceil(T / 512): e.g. T = 4096 with up to 256 experts, plain, or 240
- * experts and 16 ranks, dedup) it takes two launches instead of three: the
- * routing kernel counts the tiles, and the dispatch workgroups scan the plan
- * themselves; larger plans take the three.
+ * workspace (so further dispatch calls on it may follow).  It takes two
+ * launches instead of three or four - the routing kernel counts the tiles, and
+ * the dispatch workgroups scan the plan themselves - when E <= 256 and the
+ * plan's position columns (E, or R in dedup mode) have V <= 2048 vectors of 16
+ * tile counts (V = columns x ceil(T / 512)) with V x W <= 4 Mi, W being the
+ * dispatch's workgroups (ceil(T x ceil(row bytes / 4 KiB) / 4) for rows of at
+ * least 4 KiB): e.g. T = 4096 with up to 256 experts, plain, or T = 16384 of
+ * 8 KiB rows with up to 16 ranks, dedup.  Other plans take the routing call's
+ * scan (one kernel; two past 16384 tokens).
  *   logits, gating                as moe_route_plan().
  *   x, hidden_dim, bytes_per_element   as moe_dispatch_permute().
  *   topk_idx, topk_gate           [T][k] out.

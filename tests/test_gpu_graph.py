@@ -120,13 +120,15 @@ def _snapshot(b):
     ("deepseek_moe_16b", False, "plan"), ("e256_top8_h2048", False, "plan"),
     ("zyphra_top2_ep8", True, "plan"),
     ("deepseek_moe_16b", False, "one"), ("qwen3_30b_a3b", True, "one"),
-    ("e256_top8_h2048", False, "one"), ("zyphra_top6_ep32", True, "one")])
+    ("e256_top8_h2048", False, "one"), ("zyphra_top2_ep8", True, "one"),
+    ("zyphra_top6_ep32", True, "one")])
 def test_graph_replays_match_eager(name, dedup, mode):
     """mode "plan": moe_route_plan in place of the routing, counting and
     co-selection calls; "one": moe_route_dispatch in place of those and the
-    dispatch (the dispatch scanning the plan itself at 4096 tokens, the scan
-    kernel at 16384).  The eager reference uses the separate calls, so the
-    replays also check the paths against each other."""
+    dispatch (the dispatch scanning the plan itself at 4096 tokens and for the
+    16384-token batch over 8 ranks, the scan kernel for the one over 32).  The
+    eager reference uses the separate calls, so the replays also check the
+    paths against each other."""
     w = WL.get(name)
     say(f"[graph] {name} dedup={dedup} mode={mode}")
     dev = torch.device("cuda:0")

@@ -548,16 +548,24 @@ def test_dispatch_coselect(oracle_mod, T, E, k, R, dedup, n, source):
 
 # ------------------------------------------- routing + dispatch in one call --
 
-ROUTE_DISPATCH_CASES = [  # T, E, k, R, H: the dispatch scans the plan itself unless noted
+# T, E, k, R, H.  The dispatch scans the plan itself when the position columns
+# (experts; ranks in dedup mode) have V <= 2048 16-tile vectors of tile counts
+# (four per thread up to 1024, eight above) and V times the dispatch's
+# workgroups (T / 4 here: every row is one chunk) is at most 4 Mi; else the
+# routing call scans it.
+ROUTE_DISPATCH_CASES = [
     (4096, 64, 6, 16, 128),    # the benchmark's plain shape (narrow rows)
-    (4096, 128, 8, 16, 128),   # dedup: 1152 vectors, eight per thread
-    (4096, 256, 8, 16, 64),    # 2048 tile-count vectors (eight per thread); dedup: the scan kernel
+    (4096, 128, 8, 16, 128),   # plain: 1024 vectors; dedup: 128
+    (4096, 256, 8, 16, 64),    # plain: 2048 vectors, eight per thread
     (1000, 64, 6, 16, 256),
     (300, 33, 5, 11, 128),     # E % 4 != 0, a partial last tile
     (77, 8, 2, 4, 2048),       # one 4 KiB chunk per row, fewer tokens than a tile group
     (33, 17, 1, 17, 64),
     (1, 8, 2, 4, 128),
-    (16384, 128, 6, 32, 64),   # 5120 vectors: the routing call's scan, then the dispatch
+    (16384, 128, 6, 32, 64),   # plain: 4096 vectors, the routing call's scan; dedup: 1024 x 4096
+    (8704, 128, 4, 64, 64),    # dedup: 1088 vectors, eight per thread; plain: 2176, routing call
+    (16384, 128, 2, 64, 64),   # dedup: 2048 vectors x 4096 workgroups, the routing call's scan
+    (20000, 256, 4, 64, 64),   # 2560 rank vectors: the routing call's scan in both modes
     (1000, 512, 4, 64, 64),    # E > 256: the separate routing and counting kernels
 ]
 
