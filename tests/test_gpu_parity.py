@@ -566,6 +566,8 @@ ROUTE_DISPATCH_CASES = [
     (8704, 128, 4, 64, 64),    # dedup: 1088 vectors, eight per thread; plain: 2176, routing call
     (16384, 128, 2, 64, 64),   # dedup: 2048 vectors x 4096 workgroups, the routing call's scan
     (20000, 256, 4, 64, 64),   # 2560 rank vectors: the routing call's scan in both modes
+    (5000, 64, 4, 1, 64),      # one rank: dedup sends every token once; 10 vectors
+    (4096, 64, 8, 64, 64),     # one expert per rank: dedup and plain rows coincide
     (1000, 512, 4, 64, 64),    # E > 256: the separate routing and counting kernels
 ]
 
