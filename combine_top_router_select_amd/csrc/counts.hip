@@ -405,9 +405,10 @@ hipError_t launch_plan_scan(int64_t T, int E, int k, int R, const int32_t* place
     int32_t* ctot = reinterpret_cast<int32_t*>(ws + pl.ctot_off);
     hipLaunchKernelGGL(plan_colsum_kernel, dim3(unsigned(pl.cols)), dim3(kColThreads), 0, stream,
                        tcnt, B, Bp, ctot);
-    int need = CP > R ? CP : R;
-    if (ranked) need = need > E ? need : E;
-    need = need > kColThreads ? need : kColThreads;
+    // a thread per expert: workgroup 0 writes the expert counts (and, ranked,
+    // orders the columns by expert), and E also covers the CP position columns
+    // and the R ranks (R divides E)
+    const int need = E > kColThreads ? E : kColThreads;
     const int threads = (need + kWave - 1) / kWave * kWave;
 #define MOE_BASES(D, RK)                                                                      \
   hipLaunchKernelGGL((plan_bases_kernel<D, RK>), dim3(unsigned(CP)), dim3(threads), 0, stream, \

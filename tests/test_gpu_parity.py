@@ -227,8 +227,8 @@ def test_dispatch_parity_large_plan(oracle_mod, dedup):
 
 @pytest.mark.parametrize("dedup,pl", [(False, "contiguous"), (False, "random"), (True, "random")])
 def test_dispatch_parity_huge_plan(oracle_mod, dedup, pl):
-    """300000 tokens: 4688 tiles, 293 vectors per column, more than the scan
-    keeps in registers, so it takes the looping variant (one lane per column)."""
+    """300000 tokens: 9375 tiles, 586 vectors of 16 tiles per column, past the
+    one-workgroup scan's 32: the two-kernel scan (column totals, then bases)."""
     T, H, E, k, R = 300000, 16, 8, 2, 4
     say(f"[dispatch] huge plan T={T} dedup={dedup} placement={pl}")
     inp = WL.make_custom_inputs(T, H, E, seed=101)
@@ -237,11 +237,34 @@ def test_dispatch_parity_huge_plan(oracle_mod, dedup, pl):
     run_dispatch_parity(oracle_mod, inp["x_bits"], idx_o, gate_o, E, R, placement, dedup)
 
 
+@pytest.mark.parametrize("E,R", [(512, 64), (1024, 64), (512, 8), (256, 16)])
+@pytest.mark.parametrize("dedup", [False, True])
+@pytest.mark.parametrize("pl", ["contiguous", "random"])
+def test_split_scan_many_experts(oracle_mod, E, R, dedup, pl):
+    """17000 tokens: 532 tiles, 34 vectors per column, so the plan takes the
+    two-kernel scan, whose bases kernel must have a thread per expert for the
+    expert counts (dedup mode once ran it with max(R, 256) threads and left the
+    counts of experts past 256 unwritten).  The counting call with its dispatch
+    (counts, rows and metadata), then the routing call's counts, against the
+    oracle."""
+    T, H, k = 17000, 8, 4
+    say(f"[split scan] T={T} E={E} k={k} R={R} dedup={dedup} placement={pl}")
+    inp = WL.make_custom_inputs(T, H, E, seed=E + R + int(dedup))
+    idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+    placement = WL.random_placement(E, R, seed=9) if pl == "random" else None
+    run_dispatch_parity(oracle_mod, inp["x_bits"], idx_o, gate_o, E, R, placement, dedup)
+    place_dev = to_dev(placement) if placement is not None else None
+    idx, _, c = ops.moe_route_plan(to_dev(inp["logits"]), k, R, place_dev, dedup)
+    sync()
+    assert (host(idx) == idx_o).all()
+    _check_counts(c, oracle_mod.send_counts(idx_o, E, R, placement, dedup), dedup)
+
+
 @pytest.mark.parametrize("dedup", [False, True])
 def test_route_plan_huge(oracle_mod, dedup):
-    """The combined routing call at 300000 tokens (4688 tiles: the looping scan)
-    against the oracle's ids, counts and co-selection counts, and its plan
-    against the separate calls byte for byte."""
+    """The combined routing call at 300000 tokens (586 vectors per column: the
+    two-kernel scan) against the oracle's ids, counts and co-selection counts,
+    and its plan against the separate calls byte for byte."""
     T, E, k, R = 300000, 64, 6, 16
     say(f"[route_plan] huge T={T} E={E} k={k} R={R} dedup={dedup}")
     inp = WL.make_custom_inputs(T, 16, E, seed=303)
@@ -665,6 +688,99 @@ def test_route_dispatch_zero_tokens():
         assert (host(c["expert_counts"]) == 0).all() and (host(c["rank_offsets"]) == 0).all()
         if dedup:
             assert int(host(d["n_rows"])[0]) == 0
+
+
+RD_PATHS = ("scan4", "scan8", "kernel_vectors", "kernel_cap", "experts_gt_256")
+
+
+def _rd_path(T, H, E, R, dedup):
+    """Which path moe_route_dispatch takes for this shape, by the rule its
+    header states (bf16 rows): the dispatch scans the plan itself with four or
+    eight tile-count vectors per thread, or the routing call scans it (too many
+    vectors, or too many vectors x workgroups), or E > 256 takes the separate
+    routing and counting kernels."""
+    if E > 256:
+        return "experts_gt_256"
+    groups = ((T + 31) // 32 + 15) // 16
+    V = (R if dedup else E) * groups
+    rb = 2 * H
+    chunk = 4096 if rb >= 4096 else (2048 if rb >= 2048 else 1024)
+    W = (T * ((rb + chunk - 1) // chunk) + 3) // 4
+    if V > 2048:
+        return "kernel_vectors"
+    if V * W > 4 << 20:
+        return "kernel_cap"
+    return "scan8" if V > 1024 else "scan4"
+
+
+def _random_rd_case(i):
+    """Seeded shape draw for the randomized moe_route_dispatch sweep: case i
+    aims at path RD_PATHS[i % 5] and redraws until the shape takes it (1 to
+    20000 tokens, up to 512 experts; rows of at most 64 elements past 5000
+    tokens, to keep the oracle quick)."""
+    rng = np.random.default_rng(5000 + i)
+    target = RD_PATHS[i % len(RD_PATHS)]
+    while True:
+        R = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        E = R * int(rng.choice([1, 2, 3, 4, 8]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        if rng.integers(0, 2):
+            T = int(rng.integers(6000, 20001))
+        else:
+            T = int(np.exp(rng.uniform(0.0, np.log(6000.0))))
+        H = int(rng.choice([8, 64] if T > 5000 else [8, 24, 64, 200, 1024, 2056]))
+        dedup = bool(rng.integers(0, 2))
+        if _rd_path(T, H, E, R, dedup) == target:
+            break
+    pl = str(rng.choice(["contiguous", "random"]))
+    ties = bool(rng.integers(0, 4) == 0)
+    softmax_all = bool(rng.integers(0, 4) == 0)
+    cs = int(rng.integers(0, T + 1))
+    return T, H, E, k, R, dedup, pl, ties, softmax_all, cs
+
+
+@pytest.mark.parametrize("i", range(60))
+def test_random_route_dispatch(oracle_mod, i):
+    """Sixty seeded random shapes through moe_route_dispatch (with the
+    co-selection counts of a random token prefix) and the combine, twelve on
+    each of its paths, every output against the oracle."""
+    T, H, E, k, R, dedup, pl, ties, softmax_all, cs = _random_rd_case(i)
+    say(f"[random route_dispatch {i}] {_rd_path(T, H, E, R, dedup)} T={T} H={H} E={E} k={k} "
+        f"R={R} dedup={dedup} "
+        f"placement={pl} ties={ties} softmax_all={softmax_all} coselect_tokens={cs}")
+    inp = WL.make_custom_inputs(T, H, E, seed=7000 + i,
+                                logit_values=[-1.0, -0.0, 0.0, 1.0] if ties else None)
+    placement = WL.random_placement(E, R, seed=i) if pl == "random" else None
+    place_dev = to_dev(placement) if placement is not None else None
+    W = torch.zeros((E, E), dtype=torch.int32, device=torch.device("cuda:0"))
+    idx, gate, c, d = ops.moe_route_dispatch(to_dev(inp["logits"]), bf16_dev(inp["x_bits"]), k, R,
+                                             place_dev, dedup, softmax_all, coselect=W,
+                                             coselect_tokens=cs)
+    out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"])
+    sync()
+    route = oracle_mod.route_topk_softmax_all if softmax_all else oracle_mod.route_topk
+    idx_o, gate_o = route(inp["logits"], k)
+    assert (host(idx) == idx_o).all()
+    assert f32_ulp_diff(host(gate), gate_o).max() <= 1
+    gate_h = host(gate)
+    o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(
+        inp["x_bits"], idx_o, gate_h, E, R, placement)
+    _check_counts(c, o, dedup)
+    n = o["n_rows"]
+    assert int(host(c["rank_offsets"])[-1]) == n
+    assert (host(d["slot_row"]) == o["slot_row"]).all()
+    assert (bf16_host(d["send"][:n]) == o["send"]).all()
+    assert (host(d["row_token"][:n]) == o["row_token"]).all()
+    assert (host(d["row_weight"][:n]).view(np.uint32) == o["row_weight"].view(np.uint32)).all()
+    if dedup:
+        assert int(host(d["n_rows"])[0]) == n
+        assert (host(d["row_experts"][:n]) == o["row_experts"]).all()
+        assert (host(d["row_gates"][:n]).view(np.uint32) == o["row_gates"].view(np.uint32)).all()
+    else:
+        assert (host(d["row_expert"][:n]) == o["row_expert"]).all()
+    ref = oracle_mod.combine(o["send"], o["row_weight"], o["slot_row"])
+    assert_bf16_equal(bf16_host(out), ref, f"random route_dispatch {i} combine")
+    assert (host(W) == oracle_mod.coselect(idx_o, E, tokens=cs)).all()
 
 
 # ------------------------------------------------------- full workloads --
