@@ -55,6 +55,20 @@ def test_route_parity(oracle_mod, T, E, k, tied):
     assert f32_ulp_diff(host(gate), gate_o).max() <= 1
 
 
+def test_route_grid_stride(oracle_mod):
+    """1,100,000 tokens at 64 experts: more than the 65536 workgroups of 16
+    tokens that the routing kernel's grid is capped at, so its waves loop over
+    the tokens.  Ids exact, gates within 1 ulp of the oracle."""
+    T, E, k = 1_100_000, 64, 6
+    say(f"[route] grid-stride T={T} E={E} k={k}")
+    inp = WL.make_custom_inputs(T, 8, E, seed=11)
+    idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+    idx, gate = ops.moe_route_topk(to_dev(inp["logits"]), k)
+    sync()
+    assert (host(idx) == idx_o).all()
+    assert f32_ulp_diff(host(gate), gate_o).max() <= 1
+
+
 @pytest.mark.parametrize("name", WL.ORDER)
 def test_route_parity_workloads(oracle_mod, name):
     w = WL.get(name)
@@ -327,6 +341,32 @@ def test_random_shapes(oracle_mod, i):
     ref = oracle_mod.combine(o["send"], o["row_weight"], o["slot_row"])
     assert_bf16_equal(bf16_host(out), ref, f"random {i} combine")
     assert (host(W) == oracle_mod.coselect(idx_o, E)).all()
+
+
+@pytest.mark.parametrize("H", [16384, 16392])
+@pytest.mark.parametrize("dedup", [False, True])
+def test_wide_rows_chain(oracle_mod, H, dedup):
+    """Rows of 32 KiB (eight 4 KiB chunks per row) and 32784 bytes (a ninth
+    chunk of 16 bytes) through moe_route_dispatch and the combine, against the
+    oracle."""
+    T, E, k, R = 150, 64, 6, 16
+    say(f"[wide rows] H={H} dedup={dedup}")
+    inp = WL.make_custom_inputs(T, H, E, seed=H + int(dedup))
+    placement = WL.random_placement(E, R, seed=3)
+    idx, gate, c, d = ops.moe_route_dispatch(to_dev(inp["logits"]), bf16_dev(inp["x_bits"]), k, R,
+                                             to_dev(placement), dedup)
+    out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"])
+    sync()
+    idx_o, _ = oracle_mod.route_topk(inp["logits"], k)
+    assert (host(idx) == idx_o).all()
+    o = (oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch)(
+        inp["x_bits"], idx_o, host(gate), E, R, placement)
+    _check_counts(c, o, dedup)
+    n = o["n_rows"]
+    assert (host(d["slot_row"]) == o["slot_row"]).all()
+    assert (bf16_host(d["send"][:n]) == o["send"]).all()
+    ref = oracle_mod.combine(o["send"], o["row_weight"], o["slot_row"])
+    assert_bf16_equal(bf16_host(out), ref, f"wide rows H={H}")
 
 
 @pytest.mark.parametrize("T", [2044, 2048, 2049, 4097])
