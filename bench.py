@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dedup]
                     [--receive] [--fp8] [--search] [--shuffle] [--streams {0,1,2,3,4}]
-                    [--separate] [--plan-call] [--graph] [--overlap]
+                    [--separate] [--plan-call] [--one-call] [--graph] [--overlap]
                     [--coselect-in {dispatch,route}] [--step-events]
                     [--no-cpu-baseline] [--no-reference] [--cpu-seconds S]
                     [--footprint-gib G] [--calib-copy]
@@ -20,20 +20,25 @@ Steps are independent batches.  By default, when a batch's activations are
 at most 64 MiB, consecutive steps alternate between two streams with no waits
 between them (the way a server overlaps two micro-batches), so one batch's
 latency-bound kernels can run beside the other batch's copies; each step's own
-kernels stay in order on its stream.  Larger batches run on one stream.  The
-same K steps are then timed on the other setting and reported as
-`other_streams`; --streams n fixes the setting.  --overlap instead forks only the co-selection
+kernels stay in order on its stream.  Larger batches run on one stream
+(measured: two vary by several percent from run to run there and are slower
+on the receive side).  Each buffer set is only ever used on one stream.  The same K steps are then timed on the other setting
+and reported as `other_streams`; --streams n fixes the setting.  --overlap instead forks only the co-selection
 counts onto a second stream inside each step.
 
-By default a step is moe_route_dispatch (routing, counts, offsets, plan, rows
-and the co-selection counts of the workload's first tokens in one call: two
-launches, the dispatch workgroups scanning small plans themselves) and then
-moe_combine.  --plan-call takes moe_route_plan and then the dispatch call
-(three launches); --separate takes moe_route_topk, moe_send_counts and the
-dispatch call.  The co-selection counts go with the dispatch launch, from the
-plan's expert bitmaps; --coselect-in route takes them in the routing call
-instead (implies --plan-call; with --separate, the stand-alone co-selection
-kernel at the end of the step).
+By default a step is moe_dispatch_routed (the plan's counts, offsets and scan,
+the rows, and the co-selection counts of the workload's first tokens: one
+launch, the dispatch workgroups scanning small plans themselves) and then
+moe_combine_route, whose launch also routes the batch of the next step on the
+same stream (routing, tile counts, slot codes: its workgroups run beside the
+combine's copies); each batch is routed once, one step ahead.  --one-call takes
+moe_route_dispatch (the routing and the dispatch of this batch) and then
+moe_combine; --plan-call takes moe_route_plan and then the dispatch call;
+--separate takes moe_route_topk, moe_send_counts and the dispatch call.  The
+co-selection counts go with the dispatch launch, from the plan's expert
+bitmaps; --coselect-in route takes them in the routing call instead (implies
+--plan-call; with --separate, the stand-alone co-selection kernel at the end
+of the step).
 
 The timed steps call the C ABI directly with arguments marshalled once per
 buffer set (the Python binding's per-call checks would otherwise cost about
@@ -75,12 +80,20 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 PKG = os.path.join(ROOT, "combine_top_router_select_amd")
-KERNEL_SOURCES = {"moe_dispatch_permute": "csrc/dispatch.hip",
-                  "moe_dispatch_permute_dedup": "csrc/dispatch.hip",
-                  "moe_combine": "csrc/combine.hip",
-                  "moe_expand_permute": "csrc/dispatch.hip",
-                  "moe_expand_reduce": "csrc/combine.hip",
-                  "moe_route_dispatch": "csrc/dispatch.hip"}
+# The files that hold each entry point's kernel code (besides COMMON_SOURCES):
+# a committed counter record counts only while their SHA-256 is unchanged.
+_DISPATCH_SRC = ("csrc/dispatch.hip", "csrc/plan_order.hpp", "csrc/coselect_bm.hpp")
+_COMBINE_SRC = ("csrc/combine.hip", "csrc/combine_rows.hpp")
+KERNEL_SOURCES = {"moe_dispatch_permute": _DISPATCH_SRC,
+                  "moe_dispatch_permute_dedup": _DISPATCH_SRC,
+                  "moe_combine": _COMBINE_SRC,
+                  "moe_expand_permute": _DISPATCH_SRC,
+                  "moe_expand_reduce": _COMBINE_SRC,
+                  "moe_route_dispatch": _DISPATCH_SRC,
+                  "moe_dispatch_routed": _DISPATCH_SRC,
+                  "moe_combine_route": ("csrc/combine_route.hip", "csrc/combine_rows.hpp",
+                                        "csrc/route_tile.hpp")}
+COMMON_SOURCES = ("csrc/common.hpp", "build.py")
 METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak)"
 
 
@@ -108,15 +121,16 @@ def parse():
                         "independent batches, between n streams so that one batch's "
                         "latency-bound kernels overlap another's copies (no cross-stream "
                         "waits); 1: every step on one stream; 0 (default): 2 when a batch's "
-                        "activations are at most 64 MiB, else 1 (measured: large batches have "
-                        "nothing latency-bound to hide and their concurrent working sets "
-                        "overflow the Infinity Cache).  The other setting (1, or 2 after 1) is "
-                        "timed too and reported as other_streams")
+                        "activations are at most 64 MiB, else 1.  The other setting (1, or 2 "
+                        "after 1) is timed too and reported as other_streams")
     p.add_argument("--separate", action="store_true",
                    help="route and count with moe_route_topk + moe_send_counts instead of the "
                         "fused moe_route_plan (one kernel more)")
     p.add_argument("--plan-call", action="store_true",
                    help="moe_route_plan then the dispatch call instead of moe_route_dispatch")
+    p.add_argument("--one-call", action="store_true",
+                   help="moe_route_dispatch then moe_combine instead of moe_dispatch_routed "
+                        "then moe_combine_route (which routes the stream's next batch)")
     p.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     p.add_argument("--overlap", action="store_true",
                    help="run the co-selection counts on a second stream")
@@ -341,10 +355,18 @@ class BufferSet:
         return tot
 
 
+def routed_of(b, w, dedup):
+    """Buffer set b's routed batch as moe_dispatch_routed takes it."""
+    return {"topk_idx": b.idx, "topk_gate": b.gate, "ws": b.ws, "n_experts": w.n_experts,
+            "n_ranks": w.n_ranks, "placement": b.place, "dedup": dedup}
+
+
 def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True, cs_in="dispatch",
-             one_call=False):
+             one_call=False, nb=None):
     """One pass of the hot path.  one_call: moe_route_dispatch (with the
-    co-selection counts), then the rest.  Otherwise the co-selection counts go
+    co-selection counts), then the rest.  nb (pipelined): set b was routed by
+    the previous step; moe_dispatch_routed, the rest, and a combine that also
+    routes buffer set nb (moe_combine_route).  Otherwise the co-selection counts go
     with the dispatch (cs_in "dispatch") or the routing ("route") call, or with
     a side stream they run there, after the routing and concurrently with the
     rest.  With `receive` (dedup mode), the dedup rows are expanded per expert,
@@ -354,7 +376,12 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True, cs_i
     main = torch.cuda.current_stream()
     cs_route = side is None and cs_in == "route"
     cs_disp = side is None and cs_in == "dispatch"
-    if one_call:
+    nxt = None
+    if nb is not None:
+        d = ops.moe_dispatch_routed(b.x, routed_of(b, w, dedup), out={**b.cnt, **b.disp},
+                                    coselect=b.W, coselect_tokens=w.coselect_tokens)[1]
+        nxt = {"topk_idx": nb.idx, "topk_gate": nb.gate, "ws": nb.ws}
+    elif one_call:
         d = ops.moe_route_dispatch(b.logits, b.x, k, R, b.place, dedup,
                                    out={"topk_idx": b.idx, "topk_gate": b.gate, **b.cnt,
                                         **b.disp},
@@ -373,7 +400,7 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True, cs_i
         b.ev_coselected.record(side)
     if not fused and not one_call:
         c = ops.moe_send_counts(b.idx, E, R, b.place, dedup, ws=b.ws, out=b.cnt)
-    if not one_call:
+    if not one_call and nb is None:
         f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
         d = f(b.x, b.idx, b.gate, E, R, c["ws"], out=b.disp, coselect=b.W if cs_disp else None,
               coselect_tokens=w.coselect_tokens)
@@ -383,9 +410,14 @@ def gpu_step(torch, ops, b, w, dedup, side=None, receive=False, fused=True, cs_i
                                     out=b.exp)
         red = ops.moe_expand_reduce(ex["expanded"], ex["exp_gate"], ex["row_slot"], d["n_rows"],
                                     out=b.red)
-        ops.moe_combine(red, None, d["slot_row"], out=b.out)
+        rows, weight = red, None
     else:
-        ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b.out)
+        rows, weight = d["send"], d["row_weight"]
+    if nb is not None:
+        ops.moe_combine_route(rows, weight, d["slot_row"], nb.logits, k, R, nb.place, dedup,
+                              out=b.out, next_out=nxt)
+    else:
+        ops.moe_combine(rows, weight, d["slot_row"], out=b.out)
     if side is not None:
         main.wait_event(b.ev_coselected)
     elif cs_route and not fused and not one_call:
@@ -425,6 +457,17 @@ def algorithmic_bytes(T, H, E, k, bpe, n_rows, dedup, n_exp=None):
     return res
 
 
+def sources_digest(kernel, pkg=PKG):
+    """First 16 hex digits of the SHA-256 of the files that hold `kernel`'s
+    code (KERNEL_SOURCES, then COMMON_SOURCES)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + COMMON_SOURCES:
+        with open(os.path.join(pkg, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def counter_traffic(kernel, workload, mode, dtype="bf16"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summaries (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy
@@ -432,12 +475,7 @@ def counter_traffic(kernel, workload, mode, dtype="bf16"):
     and row type (a line without dtype= is bf16) or the kernel's sources have
     changed since the counters were taken."""
     import glob
-    import hashlib
-    h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "csrc/common.hpp", "build.py"):
-        with open(os.path.join(PKG, f), "rb") as fh:
-            h.update(fh.read())
-    digest = h.hexdigest()[:16]
+    digest = sources_digest(kernel)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic_*.md"))):
         with open(path) as fh:
             for line in fh:
@@ -452,11 +490,12 @@ def counter_traffic(kernel, workload, mode, dtype="bf16"):
 
 
 def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True, stream=None,
-                   cs_in="dispatch", one_call=False):
+                   cs_in="dispatch", one_call=False, nb=None):
     """The C-ABI calls of one step on buffer set b, with every argument
     marshalled once: the timed loop then costs a few microseconds of host time
     per step instead of the Python binding's checks.  one_call: routing, plan,
-    rows and co-selection counts through moe_route_dispatch.  With a side stream
+    rows and co-selection counts through moe_route_dispatch.  nb (pipelined): the
+    set that this step's combine launch routes for the next step.  With a side stream
     the co-selection counts run there, forked after the routing and joined at
     the end of the step (event record and wait entries return 0)."""
     L = ops.lib()
@@ -470,7 +509,13 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
     wsargs = (p(b.ws), b.ws.numel(), st)
     ncs = w.coselect_tokens if side is None and cs_in == "route" else 0
     dcs = w.coselect_tokens if side is None and cs_in == "dispatch" else 0
-    if one_call:
+    if nb is not None:
+        rx = d["row_experts"] if dedup else d["row_expert"]
+        calls = [(L.moe_dispatch_routed, (
+            p(b.x), p(b.idx), p(b.gate), T, H, E, k, R, p(b.place), int(dedup), bpe, *cargs[1:],
+            p(d["send"]), p(d["row_token"]), p(rx), p(d.get("row_gates")), p(d["row_weight"]),
+            p(d["slot_row"]), p(d.get("n_rows")), w.coselect_tokens, p(b.W), *wsargs))]
+    elif one_call:
         rx = d["row_experts"] if dedup else d["row_expert"]
         calls = [(L.moe_route_dispatch, (
             p(b.logits), p(b.x), T, H, E, k, 0, R, p(b.place), int(dedup), bpe, p(b.idx),
@@ -496,9 +541,9 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
             main.wait_event(b.ev_coselected)
             return 0
         calls.append((fork, ()))
-    if not fused and not one_call:
+    if not fused and not one_call and nb is None:
         calls.append((L.moe_send_counts, (p(b.idx), T, E, k, R, p(b.place), *cargs, *wsargs)))
-    if one_call:
+    if one_call or nb is not None:
         pass
     elif dedup:
         calls.append((L.moe_dispatch_permute_dedup, (
@@ -523,11 +568,16 @@ def raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side=None, fused=True,
                                     p(x["expanded"]), N, p(x["exp_row"]), p(x["exp_expert"]),
                                     p(x["exp_gate"]), p(x["row_slot"]), st)),
             (L.moe_expand_reduce, (p(x["expanded"]), p(x["exp_gate"]), p(x["row_slot"]),
-                                   p(d["n_rows"]), N, H, k, bpe, p(b.red), st)),
-            (L.moe_combine, (p(b.red), None, p(d["slot_row"]), T, H, k, 2, p(b.out), st))]
+                                   p(d["n_rows"]), N, H, k, bpe, p(b.red), st))]
+        comb = (p(b.red), None, p(d["slot_row"]), T, H, k, 2, p(b.out))
     else:
-        calls.append((L.moe_combine, (p(d["send"]), p(d["row_weight"]), p(d["slot_row"]), T, H,
-                                      k, bpe, p(b.out), st)))
+        comb = (p(d["send"]), p(d["row_weight"]), p(d["slot_row"]), T, H, k, bpe, p(b.out))
+    if nb is not None:
+        calls.append((L.moe_combine_route, (*comb, p(nb.logits), T, E, k, 0, R, p(nb.place),
+                                            int(dedup), p(nb.idx), p(nb.gate), p(nb.ws),
+                                            nb.ws.numel(), st)))
+    else:
+        calls.append((L.moe_combine, (*comb, st)))
     if side is not None:
         calls.append((join, ()))
     elif not fused and not one_call and ncs:
@@ -656,7 +706,12 @@ def main():
     receive = bool(a.receive)
     fused = not a.separate
     # routing, plan, rows and co-selection counts in one call (the default)
-    one_call = fused and not a.plan_call and not a.overlap and a.coselect_in == "dispatch"
+    # the default: each step's combine launch routes the stream's next batch;
+    # --one-call: routing and dispatch of this batch in one call
+    # (graph replay takes the one-call step)
+    direct = fused and not a.plan_call and not a.overlap and a.coselect_in == "dispatch"
+    pipelined = direct and not a.one_call and not a.graph
+    one_call = direct and (bool(a.one_call) or bool(a.graph))
     if receive and not dedup:
         print("--receive needs --dedup (the receive side expands deduplicated rows)",
               file=sys.stderr)
@@ -672,9 +727,21 @@ def main():
         inp["x_fp8"] = xb.float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     T, H, E, k, R = w.tokens, w.hidden_dim, w.n_experts, w.top_k, w.n_ranks
 
+    # streams: the timed setting and the other one timed after it (None: none);
+    # two by default, one for receive-side steps of batches over 64 MiB
+    many = not a.overlap and not a.step_events and not a.graph
+    want = a.streams if a.streams else (2 if T * H * bpe <= 64 * 2 ** 20 else 1)
+    n_streams = want if many else 1
+    other_ns = (1 if n_streams > 1 else 2) if many else None
+
     first = BufferSet(torch, ops, inp, w, dedup, dev, receive, fp8)
     per_set = first.nbytes()
     nsets = max(2, int(np.ceil(a.footprint_gib * 2 ** 30 / per_set)))
+    # each buffer set always on the same stream (steps i and i + nsets use one
+    # set): a multiple of both stream counts, and two sets per stream at least
+    m = int(np.lcm(n_streams, other_ns or 1))
+    nsets = max(nsets, 2 * m)
+    nsets = (nsets + m - 1) // m * m
     sets = [first] + [BufferSet(torch, ops, inp, w, dedup, dev, receive, fp8)
                       for _ in range(nsets - 1)]
     torch.cuda.synchronize()
@@ -700,21 +767,22 @@ def main():
         torch.cuda.synchronize()
 
     raw = raw_other = None
-    want = a.streams if a.streams else (2 if T * H * bpe <= 64 * 2 ** 20 else 1)
-    n_streams = want if (side is None and not a.step_events and graphs is None) else 1
     if graphs is None:
         streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(3)]
 
+        # pipelined: step i's combine launch routes the set of step i + ns, the
+        # next step on the same stream
         def raw_sets(ns):
             return [raw_step_calls(torch, ops, b, w, dedup, receive, bpe, side, fused,
-                                   streams[i % ns], a.coselect_in, one_call)
+                                   streams[i % ns], a.coselect_in, one_call,
+                                   sets[(i + ns) % nsets] if pipelined else None)
                     for i, b in enumerate(sets)]
         raw = raw_sets(n_streams)
-        if side is None and not a.step_events:
-            raw_other = raw_sets(1 if n_streams > 1 else 2)
+        if other_ns is not None:
+            raw_other = raw_sets(other_ns)
 
     timed_kernels = ("moe_route_dispatch", "moe_dispatch_permute", "moe_dispatch_permute_dedup",
-                     "moe_combine",
+                     "moe_combine", "moe_dispatch_routed", "moe_combine_route",
                      "moe_expand_permute", "moe_expand_reduce")
     step_ev = {}   # (step, entry point) -> (start event, end event)
     ev_pool = ([torch.cuda.Event(enable_timing=True) for _ in range(8 * a.steps + 8)]
@@ -737,12 +805,17 @@ def main():
                     raise ops.MoeError(rc, name)
         else:
             gpu_step(torch, ops, sets[i % nsets], w, dedup, side, receive, fused, a.coselect_in,
-                     one_call)
+                     one_call, sets[(i + n_streams) % nsets] if pipelined else None)
 
+    if pipelined:   # every set holds a routed batch before its first dispatch
+        for b in sets:
+            ops.moe_combine_route(None, None, None, b.logits, k, R, b.place, dedup,
+                                  next_out={"topk_idx": b.idx, "topk_gate": b.gate, "ws": b.ws})
+        torch.cuda.synchronize()
     for i in range(a.warmup):
         if i == 0 and graphs is None:   # once through the Python binding, with its checks
             gpu_step(torch, ops, sets[0], w, dedup, side, receive, fused, a.coselect_in,
-                     one_call)
+                     one_call, sets[n_streams % nsets] if pipelined else None)
         else:
             step(i)
     torch.cuda.synchronize()
@@ -763,7 +836,7 @@ def main():
         for i in range(a.steps):
             step(a.warmup + i)
         torch.cuda.synchronize()
-        other = {"streams": 1 if n_streams > 1 else 2,
+        other = {"streams": other_ns,
                  "ms_per_step": (time.perf_counter() - u0) / a.steps * 1e3}
         raw = raw_main
     in_step = {}
@@ -873,7 +946,8 @@ def main():
         "config": {"workload": w.name, "tokens": T, "hidden_dim": H, "n_experts": E,
                    "top_k": k, "n_ranks": R, "placement": w.placement,
                    "dispatch": "dedup" if dedup else "nondedup", "receive_side": receive,
-                   "routing": "one_call" if one_call else ("fused" if fused else "separate"),
+                   "routing": ("pipelined" if pipelined else "one_call" if one_call
+                               else ("fused" if fused else "separate")),
                    "bytes_per_element": bpe, "graph": bool(a.graph),
                    "coselect": "side_stream" if a.overlap else a.coselect_in + "_call",
                    "streams": n_streams,

@@ -17,7 +17,8 @@ SYMBOLS = ("moe_status_string", "moe_workspace_bytes", "moe_expand_workspace_byt
            "moe_expand_counts", "moe_expand_permute", "moe_expand_reduce",
            "moe_placement_search", "moe_route_topk_softmax_all", "moe_shuffle_fit",
            "moe_shuffle_predict", "moe_shuffle_assign", "moe_route_plan",
-           "moe_dispatch_permute_noalloc", "moe_route_dispatch")
+           "moe_dispatch_permute_noalloc", "moe_route_dispatch", "moe_combine_route",
+           "moe_dispatch_routed")
 
 _lib = None
 
@@ -56,6 +57,10 @@ def lib():
                                          P, P, P, P, P, P, P, P, P, P, P, P, P, i64, P, P, sz,
                                          P]
         L.moe_combine.argtypes = [P, P, P, i64, i32, i32, i32, P, P]
+        L.moe_combine_route.argtypes = [P, P, P, i64, i32, i32, i32, P, P, i64, i32, i32, i32,
+                                        i32, P, i32, P, P, P, sz, P]
+        L.moe_dispatch_routed.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i32, i32, P, P,
+                                          P, P, P, P, P, P, P, P, P, i64, P, P, sz, P]
         L.moe_coselect_counts.argtypes = [P, i64, i32, i32, P, P]
         L.moe_expand_workspace_bytes.argtypes = [i64, i32, i32, i32]
         L.moe_expand_workspace_bytes.restype = sz

@@ -24,7 +24,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "route_topk.hip", "counts.hip", "dispatch.hip", "combine.hip",
-           "coselect.hip", "placement.hip", "shuffle.hip", "noalloc.hip"]
+           "combine_route.hip", "coselect.hip", "placement.hip", "shuffle.hip", "noalloc.hip"]
 CEILING_SOURCES = ["hbm_ceiling.hip"]
 CEILING_LIB = os.path.join(PKG, "libmoe_hbm_ceiling.so")
 

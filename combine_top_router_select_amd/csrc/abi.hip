@@ -41,6 +41,11 @@ hipError_t launch_dispatch_scan(const void*, const int32_t*, const float*, int64
                                 int, const int32_t*, void*, int, void*, int32_t*, int32_t*,
                                 float*, float*, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*,
                                 int32_t*, int64_t, int32_t*, hipStream_t);
+hipError_t launch_plan_scan(int64_t, int, int, int, const int32_t*, int, int32_t*, int32_t*,
+                            int32_t*, int32_t*, void*, hipStream_t);
+hipError_t launch_combine_route(const void*, const float*, const int32_t*, int64_t, int, int, int,
+                                void*, const float*, int64_t, int, int, int, int, const int32_t*,
+                                int, int32_t*, float*, void*, hipStream_t);
 }  // namespace moe
 
 namespace {
@@ -262,6 +267,49 @@ MOE_API int moe_route_dispatch(const float* logits, const void* x, int64_t token
                                          d ? n_rows : nullptr, ncs, coselect, s));
 }
 
+MOE_API int moe_dispatch_routed(const void* x, const int32_t* topk_idx, const float* topk_gate,
+                                int64_t tokens, int hidden_dim, int n_experts, int top_k,
+                                int n_ranks, const int32_t* placement, int dedup,
+                                int bytes_per_element, int32_t* expert_counts,
+                                int32_t* rank_counts, int32_t* rank_offsets,
+                                int32_t* expert_offsets, void* send, int32_t* row_token,
+                                int32_t* row_experts, float* row_gates, float* row_weight,
+                                int32_t* slot_row, int32_t* n_rows, int64_t coselect_tokens,
+                                int32_t* coselect, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  int st = check_tek(tokens, n_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if ((st = check_rows(hidden_dim, bytes_per_element)) != MOE_OK) return st;
+  if (coselect && (coselect_tokens < 0 || coselect_tokens > tokens)) return MOE_EINVAL;
+  if (!expert_counts || !rank_counts || !rank_offsets || !workspace || (dedup && !n_rows))
+    return MOE_EINVAL;
+  if (tokens > 0 && (!x || !topk_idx || !topk_gate || !send || !row_token || !row_experts ||
+                     !row_weight || !slot_row || (dedup && !row_gates)))
+    return MOE_EINVAL;
+  const int d = dedup ? 1 : 0;
+  if (workspace_bytes < moe_workspace_bytes(tokens, n_experts, top_k, n_ranks, d))
+    return MOE_EWORKSPACE;
+  const int rb = hidden_dim * bytes_per_element;
+  const int64_t ncs = coselect ? coselect_tokens : 0;
+  int32_t* eo = d ? nullptr : expert_offsets;
+  hipStream_t s = as_stream(stream);
+  if (moe::dispatch_scans_plan(tokens, n_experts, top_k, n_ranks, d, rb))
+    return hip_status(moe::launch_dispatch_scan(
+        x, topk_idx, topk_gate, tokens, rb, n_experts, top_k, n_ranks, placement, workspace, d,
+        send, row_token, row_experts, d ? row_gates : nullptr, row_weight, slot_row,
+        d ? n_rows : nullptr, expert_counts, rank_counts, rank_offsets, eo, ncs, coselect, s));
+  // larger plans: the scan kernel, then the dispatch
+  if (moe::launch_plan_scan(tokens, n_experts, top_k, n_ranks, placement, d, expert_counts,
+                            rank_counts, rank_offsets, eo, workspace, s) != hipSuccess)
+    return MOE_EHIP;
+  if (tokens == 0 && !d) return MOE_OK;
+  return hip_status(moe::launch_dispatch(x, topk_idx, topk_gate, tokens, rb, n_experts, top_k,
+                                         n_ranks, workspace, d, send, row_token, row_experts,
+                                         d ? row_gates : nullptr, row_weight, slot_row,
+                                         d ? n_rows : nullptr, ncs, coselect, s));
+}
+
 // Rows of bf16 (2 bytes) or fp8 E4M3 (1 byte); the output is bf16.
 static int check_combine(int64_t tokens, int hidden_dim, int top_k, int bytes_per_element) {
   if (tokens < 0 || top_k < 1 || hidden_dim < 1 || bytes_per_element < 1) return MOE_EINVAL;
@@ -283,6 +331,31 @@ MOE_API int moe_combine(const void* rows, const float* row_weight, const int32_t
   return hip_status(moe::launch_combine(rows, row_weight, slot_row, tokens,
                                         hidden_dim * bytes_per_element, top_k,
                                         bytes_per_element == 1, nullptr, out, as_stream(stream)));
+}
+
+MOE_API int moe_combine_route(const void* rows, const float* row_weight, const int32_t* slot_row,
+                              int64_t tokens, int hidden_dim, int top_k, int bytes_per_element,
+                              void* out, const float* next_logits, int64_t next_tokens,
+                              int n_experts, int next_top_k, int gating, int n_ranks,
+                              const int32_t* placement, int dedup, int32_t* next_topk_idx,
+                              float* next_topk_gate, void* next_workspace,
+                              size_t next_workspace_bytes, void* stream) {
+  int st = check_combine(tokens, hidden_dim, top_k, bytes_per_element);
+  if (st != MOE_OK) return st;
+  if ((st = check_tek(next_tokens, n_experts, next_top_k)) != MOE_OK) return st;
+  if ((st = check_ranks(n_experts, n_ranks)) != MOE_OK) return st;
+  if (gating != 0 && gating != 1) return MOE_EINVAL;
+  if (tokens > 0 && (!rows || !slot_row || !out)) return MOE_EINVAL;
+  if (!next_workspace ||
+      (next_tokens > 0 && (!next_logits || !next_topk_idx || !next_topk_gate)))
+    return MOE_EINVAL;
+  const int d = dedup ? 1 : 0;
+  if (next_workspace_bytes < moe_workspace_bytes(next_tokens, n_experts, next_top_k, n_ranks, d))
+    return MOE_EWORKSPACE;
+  return hip_status(moe::launch_combine_route(
+      rows, row_weight, slot_row, tokens, hidden_dim * bytes_per_element, top_k,
+      bytes_per_element == 1, out, next_logits, next_tokens, n_experts, next_top_k, gating,
+      n_ranks, placement, d, next_topk_idx, next_topk_gate, next_workspace, as_stream(stream)));
 }
 
 MOE_API size_t moe_expand_workspace_bytes(int64_t capacity, int n_experts, int top_k,

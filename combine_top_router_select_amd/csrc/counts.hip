@@ -465,7 +465,7 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
                                   const int32_t* place, int dedup, const int32_t* n_valid,
                                   int32_t* expert_counts, int32_t* rank_counts,
                                   int32_t* rank_offsets, int32_t* expert_offsets,
-                                  void* workspace, hipStream_t stream) {
+                                  void* workspace, hipStream_t stream, bool scan = true) {
   const PlanLayout pl = plan_layout(T, E, k, R, dedup);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* tcnt = ws + pl.tcnt_off;
@@ -486,6 +486,7 @@ static hipError_t launch_counts_k(const int32_t* idx, int64_t T, int E, int k, i
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  if (!scan) return hipSuccess;
   return launch_plan_scan(T, E, k, R, place, dedup, expert_counts, rank_counts, rank_offsets,
                           expert_offsets, workspace, stream);
 }
@@ -508,6 +509,22 @@ hipError_t launch_send_counts(const int32_t* idx, int64_t T, int E, int k, int R
                                      stream);
   return launch_counts_k<false, 16>(idx, T, E, k, R, place, dedup, nullptr, expert_counts,
                                     rank_counts, rank_offsets, expert_offsets, workspace, stream);
+}
+
+// The tile counts, slot codes and expert bitmaps of the plan of topk_idx,
+// without its scan: the same workspace state as the fused routing kernel
+// leaves (for a dispatch that scans the plan later).
+hipError_t launch_tile_counts(const int32_t* idx, int64_t T, int E, int k, int R,
+                              const int32_t* place, int dedup, void* workspace,
+                              hipStream_t stream) {
+#define MOE_TC(KM)                                                                           \
+  launch_counts_k<false, KM>(idx, T, E, k, R, place, dedup, nullptr, nullptr, nullptr,       \
+                             nullptr, nullptr, workspace, stream, false)
+  if (k <= 2) return MOE_TC(2);
+  if (k <= 4) return MOE_TC(4);
+  if (k <= 8) return MOE_TC(8);
+  return MOE_TC(16);
+#undef MOE_TC
 }
 
 // Receive side: the plan of the per-expert expansion of `cap` received rows, of

@@ -327,6 +327,87 @@ def moe_route_dispatch(logits, x, top_k, n_ranks, placement=None, dedup=False, s
     return idx, gate, counts, rows
 
 
+def moe_combine_route(rows, row_weight, slot_row, next_logits, top_k, n_ranks, placement=None,
+                      dedup=False, softmax_all=False, out=None, next_out=None, stream=None):
+    """moe_combine of this batch (rows None: no combine) and the routing of the
+    next batch (next_logits [Tn][E] fp32) into its plan without the scan, in one
+    launch (moe_combine_route).  `next_out` may hold the next batch's
+    "topk_idx", "topk_gate" and "ws".  Returns (out, routed): the combine's
+    [T][H] bf16 output (None without rows) and a dict of the next batch's ids,
+    gates, workspace and routing parameters, for moe_dispatch_routed."""
+    _dev(next_logits, "next_logits", torch.float32, 2)
+    Tn, E = next_logits.shape
+    dev = next_logits.device
+    k = int(top_k)
+    if rows is None:
+        T, H, kc, bpe, W, sr = 0, 8, 1, 2, None, None
+    else:
+        bpe = _row_bpe(rows, "rows")
+        n_rows, H = rows.shape
+        _dev(slot_row, "slot_row", torch.int32, 2, device=dev)
+        if rows.device != dev:
+            raise ValueError(f"rows are on {rows.device}, next_logits on {dev}")
+        if row_weight is not None:
+            _dev(row_weight, "row_weight", torch.float32, shape=(n_rows,), device=dev)
+        W, sr = row_weight, slot_row
+        T, kc = slot_row.shape
+        out = _out({"out": out}, "out", (T, H), torch.bfloat16, dev, itemsize=2)
+    o = dict(next_out or {})
+    idx = _out(o, "topk_idx", (Tn, k), torch.int32, dev)
+    gate = _out(o, "topk_gate", (Tn, k), torch.float32, dev)
+    placement = _placement(placement, E, dev)
+    ws = o.get("ws")
+    ws = workspace(Tn, E, k, n_ranks, dedup, dev) if ws is None else _ws(ws, dev)
+    check(lib().moe_combine_route(_ptr(rows), _ptr(W), _ptr(sr), T, H, kc, bpe,
+                                  _ptr(out if rows is not None else None), _ptr(next_logits), Tn,
+                                  E, k, int(bool(softmax_all)), n_ranks, _ptr(placement),
+                                  int(bool(dedup)), _ptr(idx), _ptr(gate), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "moe_combine_route")
+    routed = {"topk_idx": idx, "topk_gate": gate, "ws": ws, "n_experts": E, "n_ranks": n_ranks,
+              "placement": placement, "dedup": bool(dedup)}
+    return (out if rows is not None else None), routed
+
+
+def moe_dispatch_routed(x, routed, out=None, coselect=None, coselect_tokens=None, stream=None):
+    """The dispatch of a batch routed by moe_combine_route (`routed` is the dict
+    it returned): the plan's scan and the dispatch (moe_dispatch_routed), with
+    the outputs of the second half of moe_route_dispatch.  `out` may hold any
+    count or dispatch output.  Returns (counts, rows) as moe_route_dispatch."""
+    idx, gate, ws = routed["topk_idx"], routed["topk_gate"], routed["ws"]
+    T, H, k, bpe, dev = _routed(x, idx, gate)
+    E, R, dedup = routed["n_experts"], routed["n_ranks"], routed["dedup"]
+    placement = routed["placement"]
+    ws = _ws(ws, dev)
+    o = dict(out or {})
+    ec, rc, ro, eo = _count_outputs(o, E, R, dedup, dev)
+    ncs, W = _coselect_arg(coselect, coselect_tokens, E, T, dev)
+    N = T * k
+    send = _out(o, "send", (N, H), x.dtype, dev, itemsize=bpe)
+    rt = _out(o, "row_token", (N,), torch.int32, dev)
+    rw = _out(o, "row_weight", (N,), torch.float32, dev)
+    sr = _out(o, "slot_row", (T, k), torch.int32, dev)
+    if dedup:
+        rx = _out(o, "row_experts", (N, k), torch.int32, dev)
+        rg = _out(o, "row_gates", (N, k), torch.float32, dev)
+        nr = _out(o, "n_rows", (1,), torch.int32, dev)
+    else:
+        rx = _out(o, "row_expert", (N,), torch.int32, dev)
+        rg = nr = None
+    check(lib().moe_dispatch_routed(_ptr(x), _ptr(idx), _ptr(gate), T, H, E, k, R,
+                                    _ptr(placement), int(dedup), bpe, _ptr(ec), _ptr(rc),
+                                    _ptr(ro), _ptr(eo), _ptr(send), _ptr(rt), _ptr(rx), _ptr(rg),
+                                    _ptr(rw), _ptr(sr), _ptr(nr), ncs, _ptr(W), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "moe_dispatch_routed")
+    counts = {"expert_counts": ec, "rank_counts": rc, "rank_offsets": ro, "expert_offsets": eo,
+              "ws": ws}
+    rows = {"send": send, "row_token": rt, "row_weight": rw, "slot_row": sr}
+    if dedup:
+        rows.update(row_experts=rx, row_gates=rg, n_rows=nr)
+    else:
+        rows["row_expert"] = rx
+    return counts, rows
+
+
 def moe_dispatch_permute_noalloc(x, topk_idx, topk_gate, n_experts, n_ranks, placement=None,
                                  out=None, stream=None):
     """moe_send_counts (plain) and moe_dispatch_permute in one call whose plan

@@ -325,6 +325,56 @@ int moe_combine(const void* rows, const float* row_weight, const int32_t* slot_r
                 int64_t tokens, int hidden_dim, int top_k, int bytes_per_element,
                 void* out, void* stream);
 
+/* A5 + A1/A2 - the combine of one batch and the routing of the next, for a loop
+ * over independent batches (microbatches of one layer): the same as
+ * moe_combine() on this batch, then the routing and the per-tile counting of
+ * moe_route_dispatch() on the next batch without its scan and its dispatch,
+ * in one launch (the next batch's routing workgroups run beside this batch's
+ * combine; more than 256 experts or 16 Mi next tokens: three launches).  A
+ * moe_dispatch_routed() call on the next batch then scans the plan and
+ * dispatches it.  The first batch of a loop is routed by a call with tokens 0.
+ *   rows .. out, tokens, hidden_dim, top_k, bytes_per_element
+ *                 as moe_combine() (tokens 0: no combine).
+ *   next_logits   [next_tokens][E] fp32, as moe_route_plan()'s logits.
+ *   next_tokens, n_experts, next_top_k, gating, n_ranks, placement, dedup
+ *                 the next batch's routing, as moe_route_plan().
+ *   next_topk_idx, next_topk_gate   [next_tokens][next_top_k] out.  The ids
+ *                 are those of moe_route_topk(); the gates too with gating 0,
+ *                 and within 1 ulp of them with gating 1 (both within 1 ulp
+ *                 of the softmax over all logits: the fp64 sum over the
+ *                 logits runs in another order).
+ *   next_workspace, next_workspace_bytes   the next batch's plan (tile
+ *                 counts, slot codes, expert bitmaps; not yet scanned):
+ *                 moe_workspace_bytes(next_tokens, n_experts, next_top_k,
+ *                 n_ranks, dedup) bytes, handed to moe_dispatch_routed().
+ * The two batches' buffers must not overlap.
+ * Errors: those of moe_combine() and moe_route_plan(). */
+int moe_combine_route(const void* rows, const float* row_weight, const int32_t* slot_row,
+                      int64_t tokens, int hidden_dim, int top_k, int bytes_per_element,
+                      void* out, const float* next_logits, int64_t next_tokens, int n_experts,
+                      int next_top_k, int gating, int n_ranks, const int32_t* placement,
+                      int dedup, int32_t* next_topk_idx, float* next_topk_gate,
+                      void* next_workspace, size_t next_workspace_bytes, void* stream);
+
+/* A3 + A4 (+ A6) - the dispatch of a batch routed by moe_combine_route(): the
+ * plan's scan and the dispatch, with the same outputs as the second half of
+ * moe_route_dispatch() (two launches become one when the dispatch
+ * workgroups scan the plan themselves, under the same limits).  Every
+ * argument as moe_route_dispatch(), with topk_idx and topk_gate read only;
+ * tokens, n_experts, top_k, n_ranks, placement and dedup must be those of the
+ * routing call, and workspace the one it wrote (anything else gives an
+ * undefined plan).
+ * Errors: those of moe_route_dispatch(). */
+int moe_dispatch_routed(const void* x, const int32_t* topk_idx, const float* topk_gate,
+                        int64_t tokens, int hidden_dim, int n_experts, int top_k, int n_ranks,
+                        const int32_t* placement, int dedup, int bytes_per_element,
+                        int32_t* expert_counts, int32_t* rank_counts, int32_t* rank_offsets,
+                        int32_t* expert_offsets, void* send, int32_t* row_token,
+                        int32_t* row_experts, float* row_gates, float* row_weight,
+                        int32_t* slot_row, int32_t* n_rows, int64_t coselect_tokens,
+                        int32_t* coselect, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* A6 - expert co-selection counts ([EC] "Method 1": the correlation graph
  * counts the tokens that select both experts; "Correlation Formation and
  * Stability": about 4096 tokens suffice to fit it).

@@ -170,6 +170,65 @@ def test_route_dispatch_errors(lib):
     assert call(dedup=1, wsb=wsd - 1, rg=FAKE, nr=FAKE) == EWS
 
 
+def test_combine_route_errors(lib):
+    f = lib.moe_combine_route
+    ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)
+    names = ["rows", "w", "sr", "T", "H", "k", "bpe", "out", "logits", "Tn", "E", "kn", "gating",
+             "R", "place", "dedup", "idx", "gate", "ws", "wsb", "stream"]
+    ok = [FAKE, None, FAKE, 50, 128, 2, 2, FAKE, FAKE, 100, 8, 2, 0, 4, None, 0, FAKE, FAKE, FAKE,
+          ws, None]
+
+    def call(**kw):
+        a = list(ok)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return f(*a)
+
+    assert call(gating=2) == EINVAL
+    for name in ("rows", "sr", "out", "logits", "idx", "gate", "ws"):
+        assert call(**{name: None}) == EINVAL, name
+    assert call(bpe=4) == EUNSUP                           # the combine takes bf16 or fp8 rows
+    assert call(H=4) == EUNSUP                             # 8-byte rows
+    assert call(k=17) == EUNSUP
+    assert call(T=-1) == EINVAL
+    assert call(Tn=-1) == EINVAL
+    assert call(R=3) == EINVAL
+    assert call(kn=9) == EINVAL
+    assert call(wsb=ws - 1) == EWS
+    # no combine (tokens 0) needs no rows; no routed tokens need no logits or
+    # ids (and nothing is launched)
+    assert call(T=0, rows=None, sr=None, out=None, Tn=0, logits=None, idx=None, gate=None,
+                wsb=lib.moe_workspace_bytes(0, 8, 2, 4, 0)) == 0
+
+
+def test_dispatch_routed_errors(lib):
+    f = lib.moe_dispatch_routed
+    ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)
+    names = ["x", "idx", "gate", "T", "H", "E", "k", "R", "place", "dedup", "bpe", "ec", "rc",
+             "ro", "eo", "send", "rt", "rx", "rg", "rw", "sr", "nr", "ncs", "W", "ws", "wsb",
+             "stream"]
+    ok = [FAKE, FAKE, FAKE, 100, 128, 8, 2, 4, None, 0, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+          FAKE, None, FAKE, FAKE, None, 0, None, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(ok)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return f(*a)
+
+    assert call(ncs=101, W=FAKE) == EINVAL
+    for name in ("x", "idx", "gate", "ec", "rc", "ro", "send", "rt", "rx", "rw", "sr", "ws"):
+        assert call(**{name: None}) == EINVAL, name
+    assert call(bpe=3) == EUNSUP
+    assert call(H=4) == EUNSUP
+    assert call(R=3) == EINVAL
+    assert call(k=9) == EINVAL
+    assert call(wsb=ws - 1) == EWS
+    wsd = lib.moe_workspace_bytes(100, 8, 2, 4, 1)
+    assert call(dedup=1, wsb=wsd, rg=FAKE) == EINVAL       # dedup needs n_rows
+    assert call(dedup=1, wsb=wsd, nr=FAKE) == EINVAL       # and row_gates
+
+
 def test_dispatch_errors(lib):
     f = lib.moe_dispatch_permute
     ws = lib.moe_workspace_bytes(100, 8, 2, 4, 0)

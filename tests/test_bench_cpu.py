@@ -1,7 +1,6 @@
 """Host-side checks of bench.py that need no GPU: the one-GPU guard, the
 argument checks that run before any device work, and the lookup of counter
 traffic in the committed rocprofv3 summaries (keyed on the kernel's sources)."""
-import hashlib
 import importlib.util
 import os
 import subprocess
@@ -38,11 +37,7 @@ def test_receive_without_dedup_is_refused():
 
 
 def _digest(bench, kernel, pkg):
-    h = hashlib.sha256()
-    for f in (bench.KERNEL_SOURCES[kernel], "csrc/common.hpp", "build.py"):
-        with open(os.path.join(pkg, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    return bench.sources_digest(kernel, pkg)
 
 
 def test_counter_traffic_follows_the_sources(tmp_path, monkeypatch):
@@ -73,6 +68,28 @@ def test_counter_traffic_follows_the_sources(tmp_path, monkeypatch):
     assert bench.counter_traffic(kernel, "wl_b", "nondedup") is None   # stale sources
     assert bench.counter_traffic(kernel, "wl_a", "dedup") is None      # other mode
     assert bench.counter_traffic(kernel, "wl_c", "nondedup") is None   # no line
+
+
+def test_digest_covers_every_source_of_a_kernel(tmp_path):
+    """Changing any file that holds an entry point's kernel code - its .hip
+    file, the headers with its device routines, common.hpp, build.py - changes
+    the digest that gates its counter records."""
+    import shutil
+    bench = _bench_module()
+    pkg = tmp_path / "pkg"
+    shutil.copytree(os.path.join(bench.PKG, "csrc"), pkg / "csrc")
+    shutil.copy(os.path.join(bench.PKG, "build.py"), pkg / "build.py")
+    for kernel, files in bench.KERNEL_SOURCES.items():
+        base = bench.sources_digest(kernel, str(pkg))
+        assert base == bench.sources_digest(kernel)
+        for f in files + bench.COMMON_SOURCES:
+            path = pkg / f
+            text = path.read_bytes()
+            path.write_bytes(text + b"\n")
+            assert bench.sources_digest(kernel, str(pkg)) != base, (kernel, f)
+            path.write_bytes(text)
+    # the combine's routines are in the header the combine kernels share
+    assert "csrc/combine_rows.hpp" in bench.KERNEL_SOURCES["moe_combine"]
 
 
 @pytest.mark.parametrize("path", sorted(

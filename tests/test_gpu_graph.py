@@ -55,11 +55,22 @@ def _buffers(w, dedup, dev):
     return b
 
 
+def _routed(w, dedup, place, b):
+    return {"topk_idx": b["idx"], "topk_gate": b["gate"], "ws": b["ws"], "n_experts": w.n_experts,
+            "n_ranks": w.n_ranks, "placement": place, "dedup": dedup}
+
+
 def _step(w, dedup, logits, x, place, b, mode="separate"):
     """mode: "separate" calls; "plan": moe_route_plan (with the co-selection
-    counts) then the dispatch; "one": moe_route_dispatch (with them)."""
+    counts) then the dispatch; "one": moe_route_dispatch (with them); "pipe":
+    moe_dispatch_routed (with them) on the batch that the previous step's
+    combine launch routed, and a combine launch (moe_combine_route) that routes
+    the same inputs again for the next step."""
     E, k, R = w.n_experts, w.top_k, w.n_ranks
-    if mode == "one":   # routing, plan, rows and co-selection counts in one call
+    if mode == "pipe":
+        d = ops.moe_dispatch_routed(x, _routed(w, dedup, place, b), out={**b["cnt"], **b["disp"]},
+                                    coselect=b["W"], coselect_tokens=w.coselect_tokens)[1]
+    elif mode == "one":   # routing, plan, rows and co-selection counts in one call
         d = ops.moe_route_dispatch(logits, x, k, R, place, dedup,
                                    out={"topk_idx": b["idx"], "topk_gate": b["gate"], **b["cnt"],
                                         **b["disp"]},
@@ -75,7 +86,12 @@ def _step(w, dedup, logits, x, place, b, mode="separate"):
             c = ops.moe_send_counts(b["idx"], E, R, place, dedup, ws=b["ws"], out=b["cnt"])
         f = ops.moe_dispatch_permute_dedup if dedup else ops.moe_dispatch_permute
         d = f(x, b["idx"], b["gate"], E, R, c["ws"], out=b["disp"])
-    ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b["out"])
+    if mode == "pipe":
+        ops.moe_combine_route(d["send"], d["row_weight"], d["slot_row"], logits, k, R, place, dedup,
+                              out=b["out"], next_out={"topk_idx": b["idx"], "topk_gate": b["gate"],
+                                                      "ws": b["ws"]})
+    else:
+        ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], out=b["out"])
     if dedup:
         ops.moe_expand_counts(d["row_experts"], d["n_rows"], E, R, place, ws=b["ews"],
                               out=b["ecnt"])
@@ -121,13 +137,18 @@ def _snapshot(b):
     ("zyphra_top2_ep8", True, "plan"),
     ("deepseek_moe_16b", False, "one"), ("qwen3_30b_a3b", True, "one"),
     ("e256_top8_h2048", False, "one"), ("zyphra_top2_ep8", True, "one"),
-    ("zyphra_top6_ep32", True, "one")])
+    ("zyphra_top6_ep32", True, "one"),
+    ("deepseek_moe_16b", False, "pipe"), ("qwen3_30b_a3b", True, "pipe"),
+    ("e256_top8_h2048", False, "pipe"), ("zyphra_top2_ep8", True, "pipe"),
+    ("zyphra_top6_ep32", True, "pipe")])
 def test_graph_replays_match_eager(name, dedup, mode):
     """mode "plan": moe_route_plan in place of the routing, counting and
     co-selection calls; "one": moe_route_dispatch in place of those and the
     dispatch (the dispatch scanning the plan itself at 4096 tokens and for the
-    16384-token batch over 8 ranks, the scan kernel for the one over 32).  The
-    eager reference uses the separate calls, so the replays also check the
+    16384-token batch over 8 ranks, the scan kernel for the one over 32);
+    "pipe": each replay dispatches the batch that the previous replay's combine
+    launch routed (the first one routed before the warm-up) and routes it again.
+    The eager reference uses the separate calls, so the replays also check the
     paths against each other."""
     w = WL.get(name)
     say(f"[graph] {name} dedup={dedup} mode={mode}")
@@ -143,6 +164,10 @@ def test_graph_replays_match_eager(name, dedup, mode):
     ref = _snapshot(eager)
 
     gb = _buffers(w, dedup, dev)
+    if mode == "pipe":   # the first batch: a routing-only combine launch
+        ops.moe_combine_route(None, None, None, logits, w.top_k, w.n_ranks, place, dedup,
+                              next_out={"topk_idx": gb["idx"], "topk_gate": gb["gate"],
+                                        "ws": gb["ws"]})
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -163,8 +188,9 @@ def test_graph_replays_match_eager(name, dedup, mode):
                 v.view(torch.uint8).fill_(0xA5)
             gb["red"].view(torch.uint8).fill_(0x5A)
             gb["out2"].view(torch.uint8).fill_(0x5A)
-        gb["idx"].fill_(-1)
-        gb["ws"].fill_(0xA5)   # the plan is rebuilt by every replay
+        if mode != "pipe":   # (pipelined: the previous replay routed this one's batch)
+            gb["idx"].fill_(-1)
+            gb["ws"].fill_(0xA5)   # the plan is rebuilt by every replay
         gb["W"].zero_()
         torch.cuda.synchronize()
         g.replay()

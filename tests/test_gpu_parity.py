@@ -823,12 +823,124 @@ def test_random_route_dispatch(oracle_mod, i):
     assert (host(W) == oracle_mod.coselect(idx_o, E, tokens=cs)).all()
 
 
+# ------------------------------- combine + next batch's routing in one launch --
+
+# T_A (combined), T_B (routed next), E, k, R, H
+PIPE_CASES = [
+    (4096, 4096, 64, 6, 16, 128),    # the benchmark's shape, narrow rows
+    (1000, 3000, 128, 8, 16, 64),
+    (300, 77, 33, 5, 11, 128),       # E % 4 != 0, a partial last tile
+    (50, 1, 8, 2, 4, 2048),          # one routed token; 4 KiB rows combined
+    (777, 777, 16, 16, 4, 64),       # k = 16
+    (129, 200, 5, 3, 5, 64),         # fewer experts than the 16 lanes of a token
+    (16384, 16384, 128, 6, 32, 64),  # the next plan is scanned by its own kernel
+    (100, 1000, 512, 4, 64, 64),     # E > 256: routing and counting in launches of their own
+    (0, 500, 64, 6, 16, 64),         # routing only (the first batch of a loop)
+    (500, 0, 64, 6, 16, 64),         # combine only (the last)
+]
+
+
+def _assert_same(a, b, what, ulp=0):
+    if ulp == 0:
+        assert (a.view(np.uint8) == b.view(np.uint8)).all(), what
+    elif a.size:
+        assert f32_ulp_diff(a, b).max() <= ulp, what
+
+
+@pytest.mark.parametrize("TA,TB,E,k,R,H", PIPE_CASES)
+@pytest.mark.parametrize("dedup", [False, True])
+@pytest.mark.parametrize("pl", ["contiguous", "random"])
+@pytest.mark.parametrize("softmax_all", [False, True])
+def test_combine_route_parity(oracle_mod, TA, TB, E, k, R, H, dedup, pl, softmax_all):
+    """moe_combine_route (batch A's combine + batch B's routing) and
+    moe_dispatch_routed (B's dispatch) against moe_combine on A and
+    moe_route_dispatch on B: A's output bit for bit; B's ids, counts, rows,
+    metadata, plan and co-selection counts bit for bit, its gates too with
+    gating over the selected experts, and within the oracle's 1 ulp with the
+    softmax over all experts (the fp64 sum over the logits then runs in another
+    order; the gate-derived row weights and row gates likewise)."""
+    say(f"[combine_route] TA={TA} TB={TB} E={E} k={k} R={R} H={H} dedup={dedup} placement={pl} "
+        f"softmax_all={softmax_all}")
+    inA = WL.make_custom_inputs(TA, H, E, seed=TA + 3 * E + k)
+    inB = WL.make_custom_inputs(TB, H, E, seed=TB + 5 * E + k + 1)
+    placement = WL.random_placement(E, R, seed=TA + TB) if pl == "random" else None
+    place_dev = to_dev(placement) if placement is not None else None
+    dev = torch.device("cuda:0")
+    _, _, _, dA = ops.moe_route_dispatch(to_dev(inA["logits"]), bf16_dev(inA["x_bits"]), k, R,
+                                         place_dev, dedup, softmax_all)
+    ref_out = ops.moe_combine(dA["send"], dA["row_weight"], dA["slot_row"])
+    cs = (2 * TB) // 3
+    W1 = torch.zeros((E, E), dtype=torch.int32, device=dev)
+    W2 = torch.zeros((E, E), dtype=torch.int32, device=dev)
+    idx1, gate1, c1, d1 = ops.moe_route_dispatch(to_dev(inB["logits"]), bf16_dev(inB["x_bits"]),
+                                                 k, R, place_dev, dedup, softmax_all,
+                                                 coselect=W1, coselect_tokens=cs)
+    rows = dA["send"] if TA > 0 else None
+    out, routed = ops.moe_combine_route(rows, dA["row_weight"], dA["slot_row"],
+                                        to_dev(inB["logits"]), k, R, place_dev, dedup,
+                                        softmax_all)
+    c2, d2 = ops.moe_dispatch_routed(bf16_dev(inB["x_bits"]), routed, coselect=W2,
+                                     coselect_tokens=cs)
+    sync()
+    if TA > 0:
+        assert (bf16_host(out).view(np.uint16) == bf16_host(ref_out).view(np.uint16)).all()
+    g = 1 if softmax_all else 0
+    assert (host(routed["topk_idx"]) == host(idx1)).all()
+    _assert_same(host(routed["topk_gate"]), host(gate1), "gates", g)
+    for key in ("expert_counts", "rank_counts", "rank_offsets", "expert_offsets"):
+        if c1[key] is not None:
+            assert (host(c2[key]) == host(c1[key])).all(), key
+    n = int(host(d1["n_rows"])[0]) if dedup else TB * k
+    for key in d1:
+        h = bf16_host if d1[key].dtype == torch.bfloat16 else host
+        a, b = h(d2[key]), h(d1[key])
+        if key not in ("slot_row", "n_rows"):
+            a, b = a[:n], b[:n]
+        if key in ("row_weight", "row_gates"):
+            _assert_same(a, b, key, g)
+        else:
+            _assert_same(a, b, key)
+    assert (host(W2) == host(W1)).all()
+    assert _plan_equal(c2["ws"], c1["ws"], TB, E, k, R, dedup)
+    # and B's routing against the oracle
+    route = oracle_mod.route_topk_softmax_all if softmax_all else oracle_mod.route_topk
+    idx_o, gate_o = route(inB["logits"], k)
+    assert (host(routed["topk_idx"]) == idx_o).all()
+    _assert_same(host(routed["topk_gate"]), gate_o, "gates against the oracle", 1)
+
+
+def test_combine_route_fp8_rows(oracle_mod):
+    """fp8 E4M3 rows in the combine part (decoded to bf16) with the next batch's
+    routing in the same launch: the output against the oracle, the routing
+    against moe_route_dispatch's."""
+    TA, TB, E, k, R, H = 600, 900, 64, 6, 8, 512
+    say("[combine_route] fp8 rows")
+    rng = np.random.default_rng(17)
+    raw = rng.integers(0, 256, size=(TA, H), dtype=np.uint8)
+    raw[(raw & 0x7F) == 0x7F] = 0x3C  # no NaN bytes
+    inA = WL.make_custom_inputs(TA, 8, E, seed=1)
+    inB = WL.make_custom_inputs(TB, H, E, seed=2)
+    _, _, _, dA = ops.moe_route_dispatch(to_dev(inA["logits"]), to_dev(raw), k, R, None, False)
+    out, routed = ops.moe_combine_route(dA["send"], dA["row_weight"], dA["slot_row"],
+                                        to_dev(inB["logits"]), k, R)
+    idx1, gate1, _, _ = ops.moe_route_dispatch(to_dev(inB["logits"]), bf16_dev(inB["x_bits"]),
+                                               k, R, None, False)
+    sync()
+    ref = oracle_mod.combine_fp8(host(dA["send"]), host(dA["row_weight"]), host(dA["slot_row"]))
+    assert_bf16_equal(bf16_host(out), ref, "combine_route fp8")
+    assert (host(routed["topk_idx"]) == host(idx1)).all()
+    assert (host(routed["topk_gate"]).view(np.uint32) == host(gate1).view(np.uint32)).all()
+
+
 # ------------------------------------------------------- full workloads --
 
 def gpu_chain(inp, w, dedup, stream=None, fused=False, cs_in="dispatch"):
-    """The whole hot path on the GPU, through the C ABI.  cs_in "one_call":
-    moe_route_dispatch (routing, plan, rows and co-selection counts in one
-    call), the benchmark's setting; fused: the combined routing call, then the
+    """The whole hot path on the GPU, through the C ABI.  cs_in "pipelined", the
+    benchmark's setting: the batch routed as the next batch of a combine launch
+    (here one with no combine), moe_dispatch_routed, then the combine launch
+    that routes the next batch - the same logits again, whose ids and gates are
+    the ones returned; "one_call": moe_route_dispatch (routing, plan, rows and
+    co-selection counts in one call); fused: the combined routing call, then the
     dispatch, with the co-selection counts in the dispatch launch (cs_in
     "dispatch") or in the routing call ("route"); else the separate routing,
     counting and co-selection calls.  Then the combine."""
@@ -837,6 +949,14 @@ def gpu_chain(inp, w, dedup, stream=None, fused=False, cs_in="dispatch"):
     logits = to_dev(inp["logits"])
     x = bf16_dev(inp["x_bits"])
     W = torch.zeros((E, E), dtype=torch.int32, device=logits.device)
+    if cs_in == "pipelined":
+        _, routed = ops.moe_combine_route(None, None, None, logits, k, R, place, dedup,
+                                          stream=stream)
+        c, d = ops.moe_dispatch_routed(x, routed, coselect=W, coselect_tokens=w.coselect_tokens,
+                                       stream=stream)
+        out, nxt = ops.moe_combine_route(d["send"], d["row_weight"], d["slot_row"], logits, k, R,
+                                         place, dedup, stream=stream)
+        return nxt["topk_idx"], nxt["topk_gate"], c, d, out, W
     if cs_in == "one_call":
         idx, gate, c, d = ops.moe_route_dispatch(logits, x, k, R, place, dedup, coselect=W,
                                                  coselect_tokens=w.coselect_tokens,
@@ -864,8 +984,9 @@ def gpu_chain(inp, w, dedup, stream=None, fused=False, cs_in="dispatch"):
 def _cases():
     for name in WL.ORDER:
         for mode in WL.get(name).dispatch:
-            yield name, mode == "dedup", True, "one_call"
+            yield name, mode == "dedup", True, "pipelined"
     for name, dedup in (("deepseek_moe_16b", False), ("zyphra_top6_ep32", True)):
+        yield name, dedup, True, "one_call"
         yield name, dedup, True, "dispatch"
         yield name, dedup, True, "route"
         yield name, dedup, False, "-"
@@ -873,9 +994,10 @@ def _cases():
 
 @pytest.mark.parametrize("name,dedup,fused,cs_in", list(_cases()))
 def test_workload_end_to_end(oracle_mod, name, dedup, fused, cs_in):
-    """Full sizes, the launch configuration the benchmark times (one call for
-    routing, plan, rows and co-selection counts, then the combine; two
-    workloads also through the combined routing call with the co-selection
+    """Full sizes, the launch configuration the benchmark times (the batch
+    routed inside a combine launch, then moe_dispatch_routed, then the combine
+    launch that routes the next batch; two workloads also through
+    moe_route_dispatch, through the combined routing call with the co-selection
     counts in the dispatch or the routing launch, and through the separate
     calls): logits -> route, counts, co-selection -> dispatch -> combine
     (identity experts), all on the GPU, against the oracle chain on the same
@@ -957,6 +1079,55 @@ def test_two_streams_of_batches(oracle_mod, name):
         assert (bf16_host(d["send"]) == o["send"]).all()
         assert (bf16_host(out) == inp["x_bits"]).all()
         assert (host(W) == oracle_mod.coselect(idx_o, E, tokens=w.coselect_tokens)).all()
+
+@pytest.mark.parametrize("name,dedup", [("deepseek_moe_16b", False), ("qwen3_30b_a3b", True)])
+def test_two_streams_pipelined(oracle_mod, name, dedup):
+    """The benchmark's default launch configuration: independent batches
+    alternate between two streams with no waits between them (four batches,
+    two per stream, each on its own buffers and workspace), each stream routing
+    its next batch inside its combine launch (moe_combine_route) and then
+    dispatching it (moe_dispatch_routed); every batch matches the oracle."""
+    w = WL.get(name)
+    E, k, R = w.n_experts, w.top_k, w.n_ranks
+    say(f"[two streams, pipelined] {name} dedup={dedup}: 4 batches")
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    batches = [WL.make_inputs(w, seed=s) for s in (0, 1, 2, 3)]
+    dev_in = [(to_dev(b["logits"]), bf16_dev(b["x_bits"])) for b in batches]
+    sync()
+    routed = [None] * 4
+    for s in (0, 1):   # each stream's first batch: a routing-only launch
+        with torch.cuda.stream(streams[s]):
+            routed[s] = ops.moe_combine_route(None, None, None, dev_in[s][0], k, R, None, dedup,
+                                              stream=streams[s])[1]
+    res = [None] * 4
+    for i in range(4):
+        st = streams[i % 2]
+        with torch.cuda.stream(st):
+            W = torch.zeros((E, E), dtype=torch.int32, device=dev_in[i][0].device)
+            c, d = ops.moe_dispatch_routed(dev_in[i][1], routed[i], coselect=W,
+                                           coselect_tokens=w.coselect_tokens, stream=st)
+            if i + 2 < 4:
+                out, routed[i + 2] = ops.moe_combine_route(d["send"], d["row_weight"],
+                                                           d["slot_row"], dev_in[i + 2][0], k,
+                                                           R, None, dedup, stream=st)
+            else:
+                out = ops.moe_combine(d["send"], d["row_weight"], d["slot_row"], stream=st)
+        res[i] = (c, d, out, W)
+    sync()
+    for i, inp in enumerate(batches):
+        c, d, out, W = res[i]
+        idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+        assert (host(routed[i]["topk_idx"]) == idx_o).all()
+        assert f32_ulp_diff(host(routed[i]["topk_gate"]), gate_o).max() <= 1
+        f = oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch
+        o = f(inp["x_bits"], idx_o, host(routed[i]["topk_gate"]), E, R)
+        _check_counts(c, o, dedup)
+        n = o["n_rows"]
+        assert (host(d["slot_row"]) == o["slot_row"]).all()
+        assert (bf16_host(d["send"][:n]) == o["send"]).all()
+        assert (bf16_host(out) == inp["x_bits"]).all()
+        assert (host(W) == oracle_mod.coselect(idx_o, E, tokens=w.coselect_tokens)).all()
+
 
 def test_determinism_and_nondefault_stream():
     w = WL.get("qwen3_30b_a3b")
