@@ -126,12 +126,16 @@ hipError_t launch_tile_counts(const int32_t* idx, int64_t T, int E, int k, int R
                               const int32_t* place, int dedup, void* workspace,
                               hipStream_t stream);
 bool route_tiles_fit(int64_t T, int E);
+hipError_t launch_route_tiles(const float* logits, int64_t T, int E, int k, int full_softmax,
+                              int R, const int32_t* place, int dedup, int32_t* idx, float* gate,
+                              void* workspace, hipStream_t stream);
 
 // The combine of T tokens (as launch_combine, no n_valid) and the routing of
 // the next batch of Tn tokens into its plan without the scan (ids, gates,
 // tile counts, slot codes, expert bitmaps in `workspace`): one launch, or for
 // more than 256 experts (or tokens past the fused routing's limit) the combine,
-// the routing kernel and the counting kernel.
+// the routing kernel and the counting kernel.  With no combine (T = 0) the
+// routing takes the fused routing kernel of its own.
 hipError_t launch_combine_route(const void* rows, const float* w, const int32_t* slot_row,
                                 int64_t T, int row_bytes, int k, int in_fp8, void* out,
                                 const float* logits, int64_t Tn, int E, int kn, int full,
@@ -145,7 +149,10 @@ hipError_t launch_combine_route(const void* rows, const float* w, const int32_t*
     if (err != hipSuccess) return err;
     return launch_tile_counts(idx, Tn, E, kn, R, place, dedup, workspace, stream);
   }
-  if (T == 0 && Tn == 0) return hipSuccess;
+  if (T == 0)
+    return Tn == 0 ? hipSuccess
+                   : launch_route_tiles(logits, Tn, E, kn, full, R, place, dedup, idx, gate,
+                                        workspace, stream);
   CombineArgs c{static_cast<const uint8_t*>(rows), w, slot_row, T, row_bytes, k, 1,
                 static_cast<uint8_t*>(out)};
   RouteArgs r{};
@@ -171,7 +178,6 @@ hipError_t launch_combine_route(const void* rows, const float* w, const int32_t*
     r.blocks = pl.tiles;
     lds = route_tile_lds(pl.cols, E);
   }
-  if (T == 0) c.k = 1;  // no combine workgroups: any variant
   return in_fp8 ? launch_cr_f<true>(c, r, lds, stream) : launch_cr_f<false>(c, r, lds, stream);
 }
 

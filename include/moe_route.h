@@ -332,7 +332,8 @@ int moe_combine(const void* rows, const float* row_weight, const int32_t* slot_r
  * in one launch (the next batch's routing workgroups run beside this batch's
  * combine; more than 256 experts or 16 Mi next tokens: three launches).  A
  * moe_dispatch_routed() call on the next batch then scans the plan and
- * dispatches it.  The first batch of a loop is routed by a call with tokens 0.
+ * dispatches it.  The first batch of a loop is routed by a call with tokens 0
+ * (the routing kernel alone).
  *   rows .. out, tokens, hidden_dim, top_k, bytes_per_element
  *                 as moe_combine() (tokens 0: no combine).
  *   next_logits   [next_tokens][E] fp32, as moe_route_plan()'s logits.
