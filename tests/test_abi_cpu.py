@@ -390,3 +390,30 @@ def test_product_path_does_not_touch_oracle():
                 for pat in (r"^\s*(from|import)\s+oracle", r"liboracle", r"oracle\.c\b",
                             r"oracle_[a-z_]+\("):
                     assert not re.search(pat, txt, flags=re.M), (fn, pat)
+
+
+def test_binding_rejects_host_tensors():
+    """Every tensor the binding is handed must be on a GPU: host tensors are
+    refused before the library is called."""
+    import pytest
+    import torch
+    from combine_top_router_select_amd import ops
+    t32 = torch.zeros((8, 2), dtype=torch.int32)
+    f32 = torch.zeros((8, 2), dtype=torch.float32)
+    logits = torch.zeros((8, 4), dtype=torch.float32)
+    x = torch.zeros((8, 8), dtype=torch.bfloat16)
+    calls = [
+        lambda: ops.moe_route_topk(logits, 2),
+        lambda: ops.moe_send_counts(t32, 4, 2),
+        lambda: ops.moe_route_plan(logits, 2, 2),
+        lambda: ops.moe_route_dispatch(logits, x, 2, 2),
+        lambda: ops.moe_combine_route(None, None, None, logits, 2, 2),
+        lambda: ops.moe_dispatch_permute(x, t32, f32, 4, 2, torch.zeros(16, dtype=torch.uint8)),
+        lambda: ops.moe_combine(x, None, t32),
+        lambda: ops.moe_coselect_counts(t32, 4),
+        lambda: ops.moe_shuffle_predict(t32, t32, torch.zeros((4, 4, 2), dtype=torch.int32),
+                                        torch.zeros((4, 2), dtype=torch.int32), 8),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(ValueError, match="GPU device"):
+            call()
