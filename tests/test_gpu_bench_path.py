@@ -1,0 +1,74 @@
+"""The benchmark's timed calls compute the path: bench.py's C-ABI call lists
+(raw_step_calls, every argument marshalled once per buffer set), run the way
+its timed loop runs them - each batch routed inside the combine launch of the
+step before it on the same stream, consecutive steps alternating between the
+streams with no waits - leave every buffer set's ids, gates, counts, rows,
+combined output and co-selection counts equal to the oracle's."""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from combine_top_router_select_amd import ops
+from combine_top_router_select_amd import workloads as WL
+from gpu_util import bf16_host, f32_ulp_diff, host, say
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_path", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("name,dedup,n_streams", [
+    ("deepseek_moe_16b", False, 2), ("qwen3_30b_a3b", True, 2), ("e256_top8_h2048", False, 2),
+    ("zyphra_top2_ep8", True, 1)])
+def test_bench_pipelined_calls(oracle_mod, name, dedup, n_streams):
+    bench = _bench()
+    w = WL.get(name)
+    T, E, k, R = w.tokens, w.n_experts, w.top_k, w.n_ranks
+    say(f"[bench path] {name} dedup={dedup} streams={n_streams}")
+    dev = torch.device("cuda:0")
+    inp = WL.make_inputs(w)
+    nsets = 2 * n_streams
+    sets = [bench.BufferSet(torch, ops, inp, w, dedup, dev) for _ in range(nsets)]
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(n_streams - 1)]
+    for b in sets:   # every set routed before its first dispatch, as the bench does
+        ops.moe_combine_route(None, None, None, b.logits, k, R, b.place, dedup,
+                              next_out={"topk_idx": b.idx, "topk_gate": b.gate, "ws": b.ws})
+    torch.cuda.synchronize()
+    raw = [bench.raw_step_calls(torch, ops, b, w, dedup, False, 2, None, True,
+                                streams[i % n_streams], "dispatch", False,
+                                sets[(i + n_streams) % nsets])
+           for i, b in enumerate(sets)]
+    steps = 3 * nsets
+    for i in range(steps):
+        for fn, args in raw[i % nsets]:
+            rc = fn(*args)
+            assert rc == 0, (i, getattr(fn, "__name__", fn))
+    torch.cuda.synchronize()
+    idx_o, gate_o = oracle_mod.route_topk(inp["logits"], k)
+    W_o = oracle_mod.coselect(idx_o, E, tokens=w.coselect_tokens)
+    f = oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch
+    o = None
+    for b in sets:
+        assert (host(b.idx) == idx_o).all()
+        assert f32_ulp_diff(host(b.gate), gate_o).max() <= 1
+        if o is None:
+            o = f(inp["x_bits"], idx_o, host(b.gate), E, R, inp["placement"])
+        n = o["n_rows"]
+        assert (host(b.cnt["rank_offsets"]) == o["rank_offsets"]).all()
+        assert (host(b.cnt["expert_counts"]) == o["expert_counts"]).all()
+        assert (host(b.disp["slot_row"]) == o["slot_row"]).all()
+        assert (bf16_host(b.disp["send"][:n]) == o["send"]).all()
+        assert (host(b.disp["row_weight"][:n]).view(np.uint32) ==
+                o["row_weight"].view(np.uint32)).all()
+        assert (bf16_host(b.out) == inp["x_bits"]).all()     # identity experts
+        assert (host(b.W) == (steps // nsets) * W_o).all()   # accumulated once per use
