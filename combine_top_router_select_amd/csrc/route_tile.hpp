@@ -210,8 +210,10 @@ __device__ __forceinline__ void lds_or(uint64_t* p, uint64_t v) {
 // entries as the separate counting kernel writes from topk_idx.  Saves that
 // kernel's launch and its reread of the ids.  The expert bitmaps also go to
 // the plan's 64-token co-selection bitmaps (bm), as this tile's piece of them;
-// the co-selection counts are taken from there by a later kernel (done here,
-// they would cost one atomic add per co-selected pair and tile).
+// the co-selection counts are taken from there later, by workgroups of the
+// dispatch launch or by a kernel of their own (done here, they would cost one
+// atomic add per co-selected pair and tile).
+
 // LDS bytes of route_tile_block: C = E (+ R in dedup mode) TileMasks and E
 // ints.
 __host__ __device__ inline size_t route_tile_lds(int C, int E) {
