@@ -932,6 +932,106 @@ def test_combine_route_fp8_rows(oracle_mod):
     assert (host(routed["topk_gate"]).view(np.uint32) == host(gate1).view(np.uint32)).all()
 
 
+def _random_pipe_case(i):
+    """Seeded draw for the randomized pipelined sweep: batch A (combined) and
+    batch B (routed in A's combine launch, then dispatched) share E, R and the
+    placement but not their token counts, top-k, row widths, dedup mode, row
+    type or gating.  Case i aims B at path RD_PATHS[i % 5]; every eighth case
+    has no A (routing only), every eighth from the sixth on no B (combine only)."""
+    rng = np.random.default_rng(9000 + i)
+    target = RD_PATHS[i % len(RD_PATHS)]
+    while True:
+        R = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        E = R * int(rng.choice([1, 2, 3, 4, 8]))
+        kB = int(rng.integers(1, min(E, 16) + 1))
+        if rng.integers(0, 2):
+            TB = int(rng.integers(6000, 20001))
+        else:
+            TB = int(np.exp(rng.uniform(0.0, np.log(6000.0))))
+        HB = int(rng.choice([8, 64] if TB > 5000 else [8, 24, 64, 200, 1024, 2056]))
+        dB = bool(rng.integers(0, 2))
+        if _rd_path(TB, HB, E, R, dB) == target:
+            break
+    kA = int(rng.integers(1, min(E, 16) + 1))
+    TA = int(np.exp(rng.uniform(0.0, np.log(5000.0))))
+    HA = int(rng.choice([8, 64, 200, 1024, 2056]))
+    dA = bool(rng.integers(0, 2))
+    fp8A = bool(rng.integers(0, 4) == 0)
+    if fp8A:
+        HA *= 2   # the same row bytes (a multiple of 16) as the bf16 draw
+    if i % 8 == 3:
+        TA = 0
+    if i % 8 == 6:
+        TB = 0
+    pl = str(rng.choice(["contiguous", "random"]))
+    smA, smB = bool(rng.integers(0, 4) == 0), bool(rng.integers(0, 4) == 0)
+    cs = int(rng.integers(0, TB + 1))
+    return dict(E=E, R=R, TA=TA, HA=HA, kA=kA, dA=dA, fp8A=fp8A, smA=smA,
+                TB=TB, HB=HB, kB=kB, dB=dB, smB=smB, pl=pl, cs=cs)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_pipelined(oracle_mod, i):
+    """Forty seeded random pairs through the pipelined calls: A's rows (from
+    moe_route_dispatch, bf16 or fp8) combined by moe_combine_route while it
+    routes B, then moe_dispatch_routed on B with the co-selection counts of a
+    random prefix.  A's output against the oracle's combine of the same rows;
+    B's ids, gates, counts, rows, metadata and co-selection counts against the
+    oracle."""
+    c_ = _random_pipe_case(i)
+    E, R, TA, TB = c_["E"], c_["R"], c_["TA"], c_["TB"]
+    say(f"[random pipelined {i}] B:{_rd_path(TB, c_['HB'], E, R, c_['dB']) if TB else '-'} "
+        + " ".join(f"{k_}={v_}" for k_, v_ in c_.items()))
+    dev = torch.device("cuda:0")
+    placement = WL.random_placement(E, R, seed=i) if c_["pl"] == "random" else None
+    place_dev = to_dev(placement) if placement is not None else None
+    rows = w = sr = None
+    if TA > 0:
+        inA = WL.make_custom_inputs(TA, c_["HA"], E, seed=11000 + i)
+        if c_["fp8A"]:
+            raw = np.random.default_rng(i).integers(0, 256, size=(TA, c_["HA"]), dtype=np.uint8)
+            raw[(raw & 0x7F) == 0x7F] = 0x3C  # no NaN bytes
+            xA = to_dev(raw)
+        else:
+            xA = bf16_dev(inA["x_bits"])
+        _, _, _, dA = ops.moe_route_dispatch(to_dev(inA["logits"]), xA, c_["kA"], R, place_dev,
+                                             c_["dA"], c_["smA"])
+        rows, w, sr = dA["send"], dA["row_weight"], dA["slot_row"]
+    inB = WL.make_custom_inputs(TB, c_["HB"], E, seed=13000 + i)
+    kB = c_["kB"]
+    out, routed = ops.moe_combine_route(rows, w, sr, to_dev(inB["logits"]), kB, R, place_dev,
+                                        c_["dB"], c_["smB"])
+    W = torch.zeros((E, E), dtype=torch.int32, device=dev)
+    c, d = ops.moe_dispatch_routed(bf16_dev(inB["x_bits"]), routed, coselect=W,
+                                   coselect_tokens=c_["cs"])
+    sync()
+    if TA > 0:
+        comb = oracle_mod.combine_fp8 if c_["fp8A"] else oracle_mod.combine
+        rows_h = host(rows) if c_["fp8A"] else bf16_host(rows)
+        ref = comb(rows_h, host(w), host(sr))
+        assert_bf16_equal(bf16_host(out), ref, f"random pipelined {i} combine")
+    route = oracle_mod.route_topk_softmax_all if c_["smB"] else oracle_mod.route_topk
+    idx_o, gate_o = route(inB["logits"], kB)
+    assert (host(routed["topk_idx"]) == idx_o).all()
+    assert TB == 0 or f32_ulp_diff(host(routed["topk_gate"]), gate_o).max() <= 1
+    o = (oracle_mod.dispatch_dedup if c_["dB"] else oracle_mod.dispatch)(
+        inB["x_bits"], idx_o, host(routed["topk_gate"]), E, R, placement)
+    _check_counts(c, o, c_["dB"])
+    n = o["n_rows"]
+    assert int(host(c["rank_offsets"])[-1]) == n
+    assert (host(d["slot_row"]) == o["slot_row"]).all()
+    assert (bf16_host(d["send"][:n]) == o["send"]).all()
+    assert (host(d["row_token"][:n]) == o["row_token"]).all()
+    assert (host(d["row_weight"][:n]).view(np.uint32) == o["row_weight"].view(np.uint32)).all()
+    if c_["dB"]:
+        assert int(host(d["n_rows"])[0]) == n
+        assert (host(d["row_experts"][:n]) == o["row_experts"]).all()
+        assert (host(d["row_gates"][:n]).view(np.uint32) == o["row_gates"].view(np.uint32)).all()
+    else:
+        assert (host(d["row_expert"][:n]) == o["row_expert"]).all()
+    assert (host(W) == oracle_mod.coselect(idx_o, E, tokens=c_["cs"])).all()
+
+
 # ------------------------------------------------------- full workloads --
 
 def gpu_chain(inp, w, dedup, stream=None, fused=False, cs_in="dispatch"):
