@@ -223,8 +223,10 @@ def ceiling_lib():
     L.hbm_write.argtypes = [P, i64, P]
     L.hbm_copy.argtypes = [P, P, i64, P]
     L.hbm_scatter.argtypes = [P, P, i64, i32, i32, P, P]
+    L.hbm_scatter_distinct.argtypes = [P, P, i64, i32, i32, P, P]
     L.hbm_device_info.argtypes = [P, P, P, P, ctypes.c_char_p, i32]
-    for f in ("hbm_read", "hbm_write", "hbm_copy", "hbm_scatter", "hbm_device_info"):
+    for f in ("hbm_read", "hbm_write", "hbm_copy", "hbm_scatter", "hbm_scatter_distinct",
+              "hbm_device_info"):
         getattr(L, f).restype = i32
     return L
 
@@ -257,9 +259,9 @@ def hbm_ceiling(torch, sets, T, H, k, bpe, n_rows, dedup, launches=100):
       read     a pure read of the dispatch's algorithmic bytes;
       write    a pure write of them;
       copy     half of them read and written elsewhere;
-      scatter  the plain dispatch's own data movement (each x row to its k
-               send rows, positions from the step's own slot_row), on the
-               bench's buffer sets (null for dedup, whose rows differ)."""
+      scatter  the dispatch's own data movement (each x row to its k send
+               rows, or with dedup to its distinct ones, positions from the
+               step's own slot_row), on the bench's buffer sets."""
     L = ceiling_lib()
     st = torch.cuda.current_stream().cuda_stream
     read_b, write_b = T * H * bpe, n_rows * H * bpe
@@ -283,15 +285,13 @@ def hbm_ceiling(torch, sets, T, H, k, bpe, n_rows, dedup, launches=100):
     res["copy"] = {"bytes": 2 * half, "us": round(t * 1e6, 2),
                    "GBps": round(2 * half / t / 1e9, 1)}
     del bufs
-    if not dedup:
-        calls = [(L.hbm_scatter, (b.x.data_ptr(), b.disp["slot_row"].data_ptr(), T, H * bpe, k,
-                                  b.disp["send"].data_ptr(), st))
-                 for b in (sets[i % len(sets)] for i in range(launches))]
-        t = time_launches(torch, calls)
-        res["scatter"] = {"bytes": read_b + write_b, "us": round(t * 1e6, 2),
-                          "GBps": round((read_b + write_b) / t / 1e9, 1)}
-    else:
-        res["scatter"] = None
+    fn = L.hbm_scatter_distinct if dedup else L.hbm_scatter
+    calls = [(fn, (b.x.data_ptr(), b.disp["slot_row"].data_ptr(), T, H * bpe, k,
+                   b.disp["send"].data_ptr(), st))
+             for b in (sets[i % len(sets)] for i in range(launches))]
+    t = time_launches(torch, calls)
+    res["scatter"] = {"bytes": read_b + write_b, "us": round(t * 1e6, 2),
+                      "GBps": round((read_b + write_b) / t / 1e9, 1)}
     return res
 
 

@@ -13,7 +13,10 @@
 //   hbm_write    writes `bytes`;
 //   hbm_copy     reads `bytes` and writes them elsewhere;
 //   hbm_scatter  the dispatch's data movement with the positions given: row t
-//                of x to rows pos[t][0..k-1] of dst.
+//                of x to rows pos[t][0..k-1] of dst;
+//   hbm_scatter_distinct  the same with each distinct position of a token
+//                written once (the deduplicating dispatch's rows, whose
+//                positions repeat where several slots share a row).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -81,8 +84,9 @@ copy_kernel(const uint8_t* src, uint8_t* dst, int64_t bytes) {
 }
 
 // One wave per (row, chunk): the chunk is read once and stored to each of
-// the row's k destinations (positions are assumed in range: they come from a
-// dispatch of the same rows).
+// the row's k destinations, or with DISTINCT to each distinct one (positions
+// are assumed in range: they come from a dispatch of the same rows).
+template <bool DISTINCT>
 __global__ void __launch_bounds__(kThreads)
 scatter_kernel(const uint8_t* x, const int32_t* __restrict__ pos, int64_t rows, int row_bytes,
                int k, int cpr, uint8_t* dst) {
@@ -92,6 +96,14 @@ scatter_kernel(const uint8_t* x, const int32_t* __restrict__ pos, int64_t rows, 
   if (t >= rows) return;  // whole wave
   const int64_t c0 = (wid - t * cpr) * kChunk;
   const int p_lane = pos[t * k + (lane < k ? lane : k - 1)];
+  // bit j set: slot j's position is stored (with DISTINCT, unless an earlier
+  // slot of the token has the same position)
+  uint64_t keep = k == 64 ? ~0ull : (1ull << k) - 1;
+  if (DISTINCT) {
+    bool dup = false;
+    for (int j = 0; j < k; ++j) dup |= j < lane && moe::bcast(p_lane, j) == p_lane;
+    keep &= __ballot(!dup);
+  }
   u32x4 v[kNV];
 #pragma unroll
   for (int i = 0; i < kNV; ++i) {
@@ -100,6 +112,7 @@ scatter_kernel(const uint8_t* x, const int32_t* __restrict__ pos, int64_t rows, 
     v[i] = moe::load16_nt(x + t * row_bytes + off);
   }
   for (int j = 0; j < k; ++j) {
+    if (!((keep >> j) & 1)) continue;  // uniform across the wave
     const int p = moe::bcast(p_lane, j);
     uint8_t* d = dst + int64_t(p) * row_bytes + c0;
 #pragma unroll
@@ -144,18 +157,29 @@ HBM_API int hbm_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   return status(hipGetLastError());
 }
 
-HBM_API int hbm_scatter(const void* x, const int32_t* pos, int64_t rows, int row_bytes, int k,
-                        void* dst, void* stream) {
+static int scatter(bool distinct, const void* x, const int32_t* pos, int64_t rows, int row_bytes,
+                   int k, void* dst, void* stream) {
   if (rows < 1 || row_bytes < 16 || row_bytes % 16 != 0 || k < 1 || k > 64 || !x || !pos ||
       !dst)
     return 2;
   const int cpr = int((row_bytes + kChunk - 1) / kChunk);
   const int64_t waves = rows * cpr;
   const unsigned grid = unsigned((waves + kThreads / kWave - 1) / (kThreads / kWave));
-  hipLaunchKernelGGL(scatter_kernel, dim3(grid), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(x), pos, rows,
-                     row_bytes, k, cpr, static_cast<uint8_t*>(dst));
+  auto kern = distinct ? scatter_kernel<true> : scatter_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(x), pos, rows, row_bytes, k, cpr,
+                     static_cast<uint8_t*>(dst));
   return status(hipGetLastError());
+}
+
+HBM_API int hbm_scatter(const void* x, const int32_t* pos, int64_t rows, int row_bytes, int k,
+                        void* dst, void* stream) {
+  return scatter(false, x, pos, rows, row_bytes, k, dst, stream);
+}
+
+HBM_API int hbm_scatter_distinct(const void* x, const int32_t* pos, int64_t rows, int row_bytes,
+                                 int k, void* dst, void* stream) {
+  return scatter(true, x, pos, rows, row_bytes, k, dst, stream);
 }
 
 // Host: properties of the current device: compute units, memory clock (kHz),

@@ -59,6 +59,34 @@ def test_scatter(L, T, row_bytes, k):
             assert (dh[pos[t, j]] == xh[t]).all()
 
 
+@pytest.mark.parametrize("T,row_bytes,k", [(100, 4096, 6), (37, 8192, 8), (64, 272, 16)])
+def test_scatter_distinct(L, T, row_bytes, k):
+    """Positions that repeat within a token (slots sharing a row, as in the
+    deduplicating dispatch): each distinct position gets the row, and no other
+    row is written."""
+    say(f"[ceiling scatter distinct] T={T} row_bytes={row_bytes} k={k}")
+    rng = np.random.default_rng(T + k)
+    n_distinct = rng.integers(1, k + 1, size=T)
+    starts = np.concatenate([[0], np.cumsum(n_distinct)[:-1]])
+    pos = np.empty((T, k), np.int32)
+    for t in range(T):   # each slot takes one of the token's rows, every row at least once
+        rows_t = starts[t] + np.arange(n_distinct[t])
+        pos[t] = rng.permutation(np.concatenate([rows_t, rng.choice(rows_t, k - n_distinct[t])]))
+    D = int(n_distinct.sum())
+    x = torch.randint(0, 256, (T, row_bytes), dtype=torch.uint8, device="cuda:0")
+    dst = torch.zeros((T * k, row_bytes), dtype=torch.uint8, device="cuda:0")
+    p = torch.from_numpy(pos).to("cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    assert L.hbm_scatter_distinct(x.data_ptr(), p.data_ptr(), T, row_bytes, k, dst.data_ptr(),
+                                  st) == 0
+    torch.cuda.synchronize()
+    xh, dh = host(x), host(dst)
+    for t in range(T):
+        for r in starts[t] + np.arange(n_distinct[t]):
+            assert (dh[r] == xh[t]).all()
+    assert (dh[D:] == 0).all()
+
+
 def test_device_info(L):
     cu, mclk, bus, clk = (ctypes.c_int(0) for _ in range(4))
     arch = ctypes.create_string_buffer(64)
