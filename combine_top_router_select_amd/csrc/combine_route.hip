@@ -55,10 +55,10 @@ struct RouteArgs {
   int64_t blocks;
 };
 
-// With 512-thread workgroups the compiler gives the top-6 combine of bf16 rows
-// in 4-vector chunks 126 registers (4 waves per SIMD; the 256-thread combine
-// kernel takes 88, 5 waves); capping it at 5 waves spills, and routing a tile
-// in two passes of 256 threads took as many registers (launch_cr_k).
+// The top-6 combine of bf16 rows in 4-vector chunks takes 126 registers here
+// (4 waves per SIMD), as in the combine kernel (125); capping it at 5 waves
+// spills, and routing a tile in two passes of 256 threads took as many
+// registers (launch_cr_k).
 template <int NV, int KMAX, bool IN8>
 __global__ void __launch_bounds__(kCrThreads)
 combine_route_kernel(CombineArgs c, RouteArgs r) {
@@ -88,11 +88,14 @@ static hipError_t launch_cr_t(CombineArgs c, const RouteArgs& r, size_t lds,
 
 // The combine kernel's chunk rule, except that 6 or more rows per token over
 // rows longer than one 4-vector chunk take 2-vector chunks: the 4-vector
-// variant takes 126 registers here (4 waves per SIMD) against 74 (6 waves),
-// which the many waves of multi-chunk rows need (a 16384-token top-6 step of
-// 8 KiB rows 308.5 -> 304.5-305.0 us, top-6 hidden 2688 dedup 47.0 -> 45.5 us
-// on two streams), while single-chunk rows gain from the larger chunk (the
-// 4096-token top-6 step of 4 KiB rows 37.0-37.1 against 37.4-38.0 us).
+// variant takes 126 registers (4 waves per SIMD) against 74 (6 waves), and in
+// this launch the 2-vector one is faster there (a 16384-token top-6 dedup step
+// of 8 KiB rows 308.2-309.1 -> 305.4-305.5 us, top-6 hidden 2688 dedup
+// 46.7-47.4 -> 45.4-45.6 us on two streams), while single-chunk rows gain
+// from the larger chunk (the 4096-token top-6 step of 4 KiB rows 37.0-37.1
+// against 37.4-38.0 us).  The combine kernel alone keeps 4-vector chunks: the
+// same rule there slowed the 16384-token top-6 combine (143.5 -> 145.0 us) and
+// the reduction (248.8 -> 254.3 us).
 template <int KMAX, bool IN8>
 static hipError_t launch_cr_k(const CombineArgs& c, const RouteArgs& r, size_t lds,
                               hipStream_t stream) {
