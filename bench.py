@@ -224,9 +224,10 @@ def ceiling_lib():
     L.hbm_copy.argtypes = [P, P, i64, P]
     L.hbm_scatter.argtypes = [P, P, i64, i32, i32, P, P]
     L.hbm_scatter_distinct.argtypes = [P, P, i64, i32, i32, P, P]
+    L.hbm_gather_sum.argtypes = [P, P, i64, i32, i32, P, P]
     L.hbm_device_info.argtypes = [P, P, P, P, ctypes.c_char_p, i32]
     for f in ("hbm_read", "hbm_write", "hbm_copy", "hbm_scatter", "hbm_scatter_distinct",
-              "hbm_device_info"):
+              "hbm_gather_sum", "hbm_device_info"):
         getattr(L, f).restype = i32
     return L
 
@@ -261,7 +262,10 @@ def hbm_ceiling(torch, sets, T, H, k, bpe, n_rows, dedup, launches=100):
       copy     half of them read and written elsewhere;
       scatter  the dispatch's own data movement (each x row to its k send
                rows, or with dedup to its distinct ones, positions from the
-               step's own slot_row), on the bench's buffer sets."""
+               step's own slot_row), on the bench's buffer sets;
+      gather_sum  the combine's own data movement (each token's distinct
+               send rows summed into its output row, same positions), on the
+               bench's buffer sets (bf16 rows only; null for fp8)."""
     L = ceiling_lib()
     st = torch.cuda.current_stream().cuda_stream
     read_b, write_b = T * H * bpe, n_rows * H * bpe
@@ -292,6 +296,14 @@ def hbm_ceiling(torch, sets, T, H, k, bpe, n_rows, dedup, launches=100):
     t = time_launches(torch, calls)
     res["scatter"] = {"bytes": read_b + write_b, "us": round(t * 1e6, 2),
                       "GBps": round((read_b + write_b) / t / 1e9, 1)}
+    res["gather_sum"] = None
+    if bpe == 2:
+        calls = [(L.hbm_gather_sum, (b.disp["send"].data_ptr(), b.disp["slot_row"].data_ptr(), T,
+                                     H * bpe, k, b.out.data_ptr(), st))
+                 for b in (sets[i % len(sets)] for i in range(launches))]
+        t = time_launches(torch, calls)
+        gb = write_b + read_b   # the dispatch's rows read, one output row per token written
+        res["gather_sum"] = {"bytes": gb, "us": round(t * 1e6, 2), "GBps": round(gb / t / 1e9, 1)}
     return res
 
 
@@ -984,7 +996,11 @@ def main():
         # the dispatch's achieved rate as a fraction of each reference rate
         disp_gbps = disp_bytes / t_disp / 1e9
         ceil["dispatch_frac_of"] = {name: round(disp_gbps / v["GBps"], 4)
-                                    for name, v in ceil.items() if v is not None}
+                                    for name, v in ceil.items()
+                                    if v is not None and name != "gather_sum"}
+        if ceil["gather_sum"] is not None:   # the combine against its own data movement
+            ceil["combine_frac_of_gather_sum"] = round(
+                comb_bytes / t_comb / 1e9 / ceil["gather_sum"]["GBps"], 4)
         res["hbm_ceiling"] = ceil
     if recv is not None:
         res["receive"] = recv

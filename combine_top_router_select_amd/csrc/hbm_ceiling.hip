@@ -16,7 +16,10 @@
 //                of x to rows pos[t][0..k-1] of dst;
 //   hbm_scatter_distinct  the same with each distinct position of a token
 //                written once (the deduplicating dispatch's rows, whose
-//                positions repeat where several slots share a row).
+//                positions repeat where several slots share a row);
+//   hbm_gather_sum  the combine's data movement: out[t] = the fp32 sum, in
+//                slot order, of the bf16 rows at token t's distinct positions,
+//                truncated to bf16 (no weights, no ordering of the rows).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -123,6 +126,71 @@ scatter_kernel(const uint8_t* x, const int32_t* __restrict__ pos, int64_t rows, 
   }
 }
 
+// One wave per (token, chunk): the chunks of all K slots' rows are loaded
+// before the first add (K x NV vectors in flight per lane; a repeated
+// position is loaded again: loads under a branch would each wait), and the
+// sum takes each distinct row once.
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+}
+
+template <int NV, int K>
+__global__ void __launch_bounds__(kThreads)
+gather_sum_kernel(const uint8_t* rows, const int32_t* __restrict__ pos, int64_t tokens,
+                  int row_bytes, int cpr, uint8_t* out) {
+  const int lane = moe::lane_id();
+  const int64_t wid = (int64_t(blockIdx.x) * kThreads + threadIdx.x) / kWave;
+  const int64_t t = wid / cpr;
+  if (t >= tokens) return;  // whole wave
+  const int64_t c0 = (wid - t * cpr) * (NV * kWave * 16);
+  const int p_lane = pos[t * K + (lane < K ? lane : K - 1)];
+  u32x4 v[K][NV];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const uint8_t* row = rows + int64_t(moe::bcast(p_lane, j)) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int64_t off = c0 + int64_t(i * kWave + lane) * 16;
+      off = off < row_bytes ? off : row_bytes - 16;
+      v[j][i] = moe::load16_nt(row + off);
+    }
+  }
+  bool dup = false;
+#pragma unroll
+  for (int j = 0; j < K; ++j) dup |= j < lane && moe::bcast(p_lane, j) == p_lane;
+  const uint64_t keep = __ballot(!dup);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (!((keep >> j) & 1)) continue;  // uniform across the wave
+      const u32x4 q = v[j][i];
+      a[0] += bf16_lo(q.x); a[1] += bf16_hi(q.x); a[2] += bf16_lo(q.y); a[3] += bf16_hi(q.y);
+      a[4] += bf16_lo(q.z); a[5] += bf16_hi(q.z); a[6] += bf16_lo(q.w); a[7] += bf16_hi(q.w);
+    }
+    const u32x4 o = {bf16_pair(a[0], a[1]), bf16_pair(a[2], a[3]), bf16_pair(a[4], a[5]),
+                     bf16_pair(a[6], a[7])};
+    const int64_t off = c0 + int64_t(i * kWave + lane) * 16;
+    if (off < row_bytes) moe::store16_nt(out + t * row_bytes + off, o);
+  }
+}
+
+template <int K>
+int launch_gather_sum(const void* rows, const int32_t* pos, int64_t tokens, int row_bytes,
+                      void* out, hipStream_t stream) {
+  constexpr int NV = K <= 6 ? 4 : (K <= 12 ? 2 : 1);  // at most 24 vectors in flight
+  const int cpr = (row_bytes + NV * kWave * 16 - 1) / (NV * kWave * 16);
+  const int64_t waves = tokens * cpr;
+  const unsigned grid = unsigned((waves + kThreads / kWave - 1) / (kThreads / kWave));
+  hipLaunchKernelGGL((gather_sum_kernel<NV, K>), dim3(grid), dim3(kThreads), 0, stream,
+                     static_cast<const uint8_t*>(rows), pos, tokens, row_bytes, cpr,
+                     static_cast<uint8_t*>(out));
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
 unsigned grid_for(int64_t bytes) {
   const int64_t waves = (bytes + kChunk - 1) / kChunk;
   return unsigned((waves + kThreads / kWave - 1) / (kThreads / kWave));
@@ -180,6 +248,26 @@ HBM_API int hbm_scatter(const void* x, const int32_t* pos, int64_t rows, int row
 HBM_API int hbm_scatter_distinct(const void* x, const int32_t* pos, int64_t rows, int row_bytes,
                                  int k, void* dst, void* stream) {
   return scatter(true, x, pos, rows, row_bytes, k, dst, stream);
+}
+
+// rows: bf16 rows of row_bytes bytes; pos [tokens][k] row indices (assumed in
+// range: they come from a dispatch of the same rows); out [tokens][row_bytes].
+// 2 for invalid sizes (row_bytes not a positive multiple of 16, k outside
+// 1..16, no tokens).
+HBM_API int hbm_gather_sum(const void* rows, const int32_t* pos, int64_t tokens, int row_bytes,
+                           int k, void* out, void* stream) {
+  if (tokens < 1 || row_bytes < 16 || row_bytes % 16 != 0 || k < 1 || k > 16 || !rows || !pos ||
+      !out)
+    return 2;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (k) {
+#define MOE_GS(K) \
+  case K: return launch_gather_sum<K>(rows, pos, tokens, row_bytes, out, s);
+    MOE_GS(1) MOE_GS(2) MOE_GS(3) MOE_GS(4) MOE_GS(5) MOE_GS(6) MOE_GS(7) MOE_GS(8)
+    MOE_GS(9) MOE_GS(10) MOE_GS(11) MOE_GS(12) MOE_GS(13) MOE_GS(14) MOE_GS(15) MOE_GS(16)
+#undef MOE_GS
+    default: return 2;
+  }
 }
 
 // Host: properties of the current device: compute units, memory clock (kHz),

@@ -370,12 +370,13 @@ def test_ceiling_library_exports_and_checks():
         pytest.fail(f"{CEILING_LIB} is not built")
     raw = ctypes.CDLL(CEILING_LIB)
     for n in ("hbm_read", "hbm_write", "hbm_copy", "hbm_scatter", "hbm_scatter_distinct",
-              "hbm_device_info"):
+              "hbm_gather_sum", "hbm_device_info"):
         assert hasattr(raw, n), n
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     raw.hbm_copy.argtypes = [P, P, i64, P]
     raw.hbm_scatter.argtypes = [P, P, i64, i32, i32, P, P]
     raw.hbm_scatter_distinct.argtypes = [P, P, i64, i32, i32, P, P]
+    raw.hbm_gather_sum.argtypes = [P, P, i64, i32, i32, P, P]
     assert raw.hbm_copy(FAKE, FAKE, 24, None) == 2       # not a multiple of 16
     assert raw.hbm_copy(None, FAKE, 32, None) == 2
     for f in (raw.hbm_scatter, raw.hbm_scatter_distinct):
@@ -383,6 +384,12 @@ def test_ceiling_library_exports_and_checks():
         assert f(FAKE, FAKE, 10, 32, 0, FAKE, None) == 2
         assert f(FAKE, FAKE, 10, 32, 65, FAKE, None) == 2
         assert f(FAKE, FAKE, 0, 32, 2, FAKE, None) == 2
+    g = raw.hbm_gather_sum
+    assert g(FAKE, FAKE, 10, 24, 2, FAKE, None) == 2      # row bytes not a multiple of 16
+    assert g(FAKE, FAKE, 10, 32, 17, FAKE, None) == 2     # k past 16
+    assert g(FAKE, FAKE, 10, 32, 0, FAKE, None) == 2
+    assert g(FAKE, FAKE, 0, 32, 2, FAKE, None) == 2
+    assert g(None, FAKE, 10, 32, 2, FAKE, None) == 2
 
 
 def test_product_path_does_not_touch_oracle():

@@ -87,6 +87,39 @@ def test_scatter_distinct(L, T, row_bytes, k):
     assert (dh[D:] == 0).all()
 
 
+@pytest.mark.parametrize("T,row_bytes,k", [(100, 4096, 6), (37, 8192, 2), (64, 272, 8),
+                                             (9, 5376, 16), (50, 2048, 3)])
+def test_gather_sum(L, T, row_bytes, k):
+    """Each token's output row is the fp32 sum, in slot order, of its distinct
+    rows (positions repeat in half the tokens), truncated to bf16."""
+    say(f"[ceiling gather_sum] T={T} row_bytes={row_bytes} k={k}")
+    rng = np.random.default_rng(T * k)
+    N = T * k
+    pos = rng.integers(0, N, size=(T, k)).astype(np.int32)
+    pos[::2, -1] = pos[::2, 0]                   # a repeated position
+    H = row_bytes // 2
+    vals = rng.standard_normal((N, H)).astype(np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)   # bf16 by truncation
+    rows = torch.from_numpy(bits.view(np.int16)).to("cuda:0")
+    out = torch.zeros((T, H), dtype=torch.int16, device="cuda:0")
+    p = torch.from_numpy(pos).to("cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    assert L.hbm_gather_sum(rows.data_ptr(), p.data_ptr(), T, row_bytes, k, out.data_ptr(),
+                            st) == 0
+    torch.cuda.synchronize()
+    f = (bits.astype(np.uint32) << 16).view(np.float32)
+    ref = np.empty((T, H), np.uint16)
+    for t in range(T):
+        acc = np.zeros(H, np.float32)
+        seen = []
+        for j in range(k):
+            if pos[t, j] not in seen:
+                seen.append(pos[t, j])
+                acc = (acc + f[pos[t, j]]).astype(np.float32)
+        ref[t] = (acc.view(np.uint32) >> 16).astype(np.uint16)
+    assert (host(out).view(np.uint16) == ref).all()
+
+
 def test_device_info(L):
     cu, mclk, bus, clk = (ctypes.c_int(0) for _ in range(4))
     arch = ctypes.create_string_buffer(64)
