@@ -72,3 +72,38 @@ def test_bench_pipelined_calls(oracle_mod, name, dedup, n_streams):
                 o["row_weight"].view(np.uint32)).all()
         assert (bf16_host(b.out) == inp["x_bits"]).all()     # identity experts
         assert (host(b.W) == (steps // nsets) * W_o).all()   # accumulated once per use
+
+
+@pytest.mark.parametrize("name,dedup,receive,fp8", [
+    ("deepseek_moe_16b", False, False, True), ("qwen3_30b_a3b", True, True, False)])
+def test_prepared_sets_hold_whole_steps(oracle_mod, name, dedup, receive, fp8):
+    """Before timing, every buffer set holds a whole step's plan, positions and
+    rows (bench.prepare_sets): the per-kernel runs and the reference kernels
+    read any set, also sets that no timed step of a short run dispatches."""
+    import torch as _t
+    bench = _bench()
+    w = WL.get(name)
+    T, k, R = w.tokens, w.top_k, w.n_ranks
+    say(f"[bench prepare] {name} dedup={dedup} receive={receive} fp8={fp8}")
+    dev = _t.device("cuda:0")
+    inp = WL.make_inputs(w)
+    if fp8:
+        xb = _t.from_numpy(inp["x_bits"].view(np.int16)).view(_t.bfloat16)
+        inp["x_fp8"] = xb.float().to(_t.float8_e4m3fn).view(_t.uint8).numpy()
+    sets = [bench.BufferSet(_t, ops, inp, w, dedup, dev, receive, fp8) for _ in range(3)]
+    bench.prepare_sets(_t, ops, sets, w, dedup, receive)
+    idx_o, _ = oracle_mod.route_topk(inp["logits"], k)
+    f = oracle_mod.dispatch_dedup if dedup else oracle_mod.dispatch
+    o = f(inp["x_bits"], idx_o, host(sets[0].gate), w.n_experts, R, inp["placement"])
+    n = o["n_rows"]
+    for b in sets:
+        assert (host(b.idx) == idx_o).all()
+        assert (host(b.cnt["rank_offsets"]) == o["rank_offsets"]).all()
+        assert (host(b.disp["slot_row"]) == o["slot_row"]).all()
+        if fp8:
+            assert (host(b.disp["send"][:n].view(_t.uint8)) == inp["x_fp8"][o["row_token"]]).all()
+        else:
+            assert (bf16_host(b.disp["send"][:n]) == o["send"]).all()
+        if receive:
+            assert (host(b.ecnt["rank_offsets"]) == host(sets[0].ecnt["rank_offsets"])).all()
+        assert (bf16_host(b.out) == bf16_host(sets[0].out)).all()
