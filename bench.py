@@ -16,6 +16,10 @@ the receive side runs between dispatch and combine.  The workload defaults to
 4096 tokens, hidden 2048 bf16, 64 experts, top-6, 16 logical ranks, contiguous
 placement (DeepSeek-MoE-16B-shaped), plain (one row per token-expert) dispatch.
 
+Without --steps the timed region holds as many steps as fill about 2 s
+(between 200 and 100000), from the time of 50 untimed steps after the
+warm-up; the JSON line's `warmup` counts those.
+
 Steps are independent batches.  By default, when a batch's activations are
 at most 64 MiB, consecutive steps alternate between two streams with no waits
 between them (the way a server overlaps two micro-batches), so one batch's
@@ -100,7 +104,9 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak)"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default: about 2 s of them, at least 200 and at most "
+                        "100000, from the step time of 50 untimed steps after the warm-up)")
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="deepseek_moe_16b")
     p.add_argument("--dedup", action="store_true")
@@ -807,6 +813,8 @@ def main():
                      "moe_combine", "moe_dispatch_routed", "moe_combine_route",
                      "moe_expand_permute", "moe_expand_reduce")
     step_ev = {}   # (step, entry point) -> (start event, end event)
+    if a.steps is None and a.step_events:
+        a.steps = 200   # one event pair per launch: a fixed count
     ev_pool = ([torch.cuda.Event(enable_timing=True) for _ in range(8 * a.steps + 8)]
                if a.step_events else [])
 
@@ -841,6 +849,19 @@ def main():
         else:
             step(i)
     torch.cuda.synchronize()
+    # without --steps: as many steps as fill about 2 s, from the time of 50
+    # untimed ones (counted with the warm-up); a long timed region leaves out
+    # the start and the end of the launch queue
+    pilot = 0
+    if a.steps is None:
+        pilot = 50
+        p0 = time.perf_counter()
+        for i in range(pilot):
+            step(a.warmup + i)
+        torch.cuda.synchronize()
+        t_est = (time.perf_counter() - p0) / pilot
+        a.steps = int(min(100000, max(200, round(2.0 / t_est))))
+    a.warmup += pilot
     # timed region: exactly K steps, synchronised on both sides
     t0 = time.perf_counter()
     for i in range(a.steps):
