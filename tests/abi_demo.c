@@ -9,6 +9,11 @@
  *     row of its own token;
  *   - identity experts with gates summing to 1: combine returns x exactly;
  *   - the co-selection diagonal sums to T*k.
+ * Then the same batch three times through the pipelined loop over two buffer
+ * sets - moe_combine_route with no rows routes the first batch, then per
+ * batch moe_dispatch_routed and a moe_combine_route that combines it and
+ * routes the next into the other set - and checks that every dispatch gives
+ * the rows and slots of the one-call step above and every combine returns x.
  * Prints "abi_demo ok" and exits 0, or names the first failed check and exits 1.
  * Built by the package build (gcc, linked against libmoe_route.so).
  */
@@ -142,11 +147,58 @@ int main(void) {
   for (int e = 0; e < E; ++e) diag += W[e * E + e];
   REQUIRE(diag == (int64_t)T * K, "co-selection diagonal sums to T*k");
 
+  /* the pipelined loop: set b % 2 holds batch b's ids, gates, plan, rows and
+     output; batch b + 1 is routed into the other set by batch b's combine */
+  enum { NB = 3 };
+  float *p_gate[2], *p_row_weight[2];
+  int32_t *p_idx[2], *p_row_token[2], *p_row_expert[2], *p_slot_row[2];
+  void *p_ws[2], *p_send[2], *p_out[2];
+  static uint16_t send2[T * K * H], out2[T * H];
+  static int32_t slot_row2[T * K];
+  for (int i = 0; i < 2; ++i) {
+    CHECK_HIP(hipMalloc((void**)&p_gate[i], sizeof(float) * T * K));
+    CHECK_HIP(hipMalloc((void**)&p_row_weight[i], sizeof(float) * T * K));
+    CHECK_HIP(hipMalloc((void**)&p_idx[i], sizeof(int32_t) * T * K));
+    CHECK_HIP(hipMalloc((void**)&p_row_token[i], sizeof(int32_t) * T * K));
+    CHECK_HIP(hipMalloc((void**)&p_row_expert[i], sizeof(int32_t) * T * K));
+    CHECK_HIP(hipMalloc((void**)&p_slot_row[i], sizeof(int32_t) * T * K));
+    CHECK_HIP(hipMalloc(&p_ws[i], ws_bytes));
+    CHECK_HIP(hipMalloc(&p_send[i], sizeof send));
+    CHECK_HIP(hipMalloc(&p_out[i], sizeof out));
+  }
+  CHECK_MOE(moe_combine_route(NULL, NULL, NULL, 0, H, K, 2, NULL, d_logits, T, E, K, 0, R, NULL,
+                              0, p_idx[0], p_gate[0], p_ws[0], ws_bytes, stream));
+  for (int b = 0; b < NB; ++b) {
+    const int c = b % 2, n = 1 - c;
+    const int64_t next_tokens = b + 1 < NB ? T : 0;
+    CHECK_MOE(moe_dispatch_routed(d_x, p_idx[c], p_gate[c], T, H, E, K, R, NULL, 0, 2, d_ec,
+                                  d_rc, d_ro, d_eo, p_send[c], p_row_token[c], p_row_expert[c],
+                                  NULL, p_row_weight[c], p_slot_row[c], NULL, 0, NULL, p_ws[c],
+                                  ws_bytes, stream));
+    CHECK_MOE(moe_combine_route(p_send[c], p_row_weight[c], p_slot_row[c], T, H, K, 2, p_out[c],
+                                d_logits, next_tokens, E, K, 0, R, NULL, 0, p_idx[n], p_gate[n],
+                                p_ws[n], ws_bytes, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    CHECK_HIP(hipMemcpy(send2, p_send[c], sizeof send2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(slot_row2, p_slot_row[c], sizeof slot_row2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(out2, p_out[c], sizeof out2, hipMemcpyDeviceToHost));
+    REQUIRE(memcmp(send2, send, sizeof send) == 0, "pipelined rows equal the one-call rows");
+    REQUIRE(memcmp(slot_row2, slot_row, sizeof slot_row) == 0,
+            "pipelined slots equal the one-call slots");
+    REQUIRE(memcmp(out2, x, sizeof x) == 0, "pipelined combine returns x");
+  }
+  for (int i = 0; i < 2; ++i) {
+    hipFree(p_gate[i]); hipFree(p_row_weight[i]); hipFree(p_idx[i]); hipFree(p_row_token[i]);
+    hipFree(p_row_expert[i]); hipFree(p_slot_row[i]); hipFree(p_ws[i]); hipFree(p_send[i]);
+    hipFree(p_out[i]);
+  }
+
   CHECK_HIP(hipStreamDestroy(stream));
   hipFree(d_logits); hipFree(d_gate); hipFree(d_idx); hipFree(d_ec); hipFree(d_rc);
   hipFree(d_ro); hipFree(d_eo); hipFree(d_W); hipFree(d_ws); hipFree(d_x); hipFree(d_send);
   hipFree(d_out); hipFree(d_row_token); hipFree(d_row_expert); hipFree(d_row_weight);
   hipFree(d_slot_row);
-  printf("abi_demo ok: T=%d H=%d E=%d k=%d R=%d\n", T, H, E, K, R);
+  printf("abi_demo ok: T=%d H=%d E=%d k=%d R=%d, one-call step and %d pipelined batches\n", T, H,
+         E, K, R, NB);
   return 0;
 }

@@ -1,7 +1,9 @@
 """The C ABI from a plain C program (tests/abi_demo.c, built by the package
 build with gcc as C11): one step through moe_route_plan, moe_dispatch_permute
 and moe_combine on hipMalloc'd buffers, with its own checks (offsets scan the
-counts, every row is its token's x, identity combine returns x)."""
+counts, every row is its token's x, identity combine returns x), then three
+batches through the pipelined loop (moe_combine_route routing the next batch,
+moe_dispatch_routed) over two buffer sets, each against the one-call step."""
 import os
 import subprocess
 
