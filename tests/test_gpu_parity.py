@@ -1229,6 +1229,57 @@ def test_two_streams_pipelined(oracle_mod, name, dedup):
         assert (host(W) == oracle_mod.coselect(idx_o, E, tokens=w.coselect_tokens)).all()
 
 
+def test_concurrent_host_threads(oracle_mod):
+    """Calls from three host threads at once, each on its own stream with its
+    own inputs and outputs (the library keeps no state between calls): a
+    pipelined loop of ten batches per thread, and every thread's last batch
+    (ids, gates, counts, rows, metadata, combined output) equals the oracle's."""
+    import threading
+    T, H, E, k, R = 2048, 256, 64, 6, 16
+    say(f"[threads] three host threads, T={T} H={H} E={E} k={k} R={R}")
+    dev = torch.device("cuda:0")
+    ins = [WL.make_custom_inputs(T, H, E, seed=300 + i) for i in range(3)]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    res, errors = [None] * 3, []
+
+    def run(i):
+        try:
+            s = streams[i]
+            with torch.cuda.stream(s):
+                logits, x = to_dev(ins[i]["logits"]), bf16_dev(ins[i]["x_bits"])
+                s.wait_stream(torch.cuda.default_stream())   # the copies above
+                _, routed = ops.moe_combine_route(None, None, None, logits, k, R, stream=s)
+                for _ in range(10):
+                    c, d = ops.moe_dispatch_routed(x, routed, stream=s)
+                    out, routed = ops.moe_combine_route(d["send"], d["row_weight"],
+                                                        d["slot_row"], logits, k, R, stream=s)
+                s.synchronize()
+                res[i] = (routed, c, d, out)
+        except Exception as exc:   # reported by the main thread
+            errors.append((i, repr(exc)))
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(3)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    sync()
+    for i in range(3):
+        routed, c, d, out = res[i]
+        idx_o, gate_o = oracle_mod.route_topk(ins[i]["logits"], k)
+        assert (host(routed["topk_idx"]) == idx_o).all()
+        assert (host(routed["topk_gate"]).view(np.uint32) == gate_o.view(np.uint32)).all()
+        o = oracle_mod.dispatch(ins[i]["x_bits"], idx_o, gate_o, E, R, None)
+        _check_counts(c, o, False)
+        assert (host(d["slot_row"]) == o["slot_row"]).all()
+        assert (bf16_host(d["send"]) == o["send"]).all()
+        assert (host(d["row_token"]) == o["row_token"]).all()
+        assert (host(d["row_expert"]) == o["row_expert"]).all()
+        ref = oracle_mod.combine(o["send"], o["row_weight"], o["slot_row"])
+        assert_bf16_equal(bf16_host(out), ref, f"thread {i} combine")
+
+
 def test_determinism_and_nondefault_stream():
     w = WL.get("qwen3_30b_a3b")
     inp = WL.make_inputs(w)
