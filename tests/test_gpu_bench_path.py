@@ -107,3 +107,43 @@ def test_prepared_sets_hold_whole_steps(oracle_mod, name, dedup, receive, fp8):
         if receive:
             assert (host(b.ecnt["rank_offsets"]) == host(sets[0].ecnt["rank_offsets"])).all()
         assert (bf16_host(b.out) == bf16_host(sets[0].out)).all()
+
+
+def test_calls_allocate_nothing():
+    """The entry points keep no device memory (the header's rule that they
+    allocate nothing): with every buffer allocated beforehand, the free device
+    memory reported by the runtime is the same before and after repeated whole
+    steps - pipelined, one-call, separate calls, and dedup with the receive
+    side.  (An allocation freed within the same call would not show here; the
+    graph-capture tests run the same calls under capture.)"""
+    import torch as _t
+    bench = _bench()
+    dev = _t.device("cuda:0")
+    cases = [("deepseek_moe_16b", False, False, "pipe"), ("deepseek_moe_16b", False, False, "one"),
+             ("qwen3_30b_a3b", False, False, "separate"), ("zyphra_top2_ep8", True, True, "pipe")]
+    say("[allocate nothing] " + ", ".join(f"{c[0]}:{c[3]}" for c in cases))
+    runs = []
+    for name, dedup, receive, mode in cases:
+        w = WL.get(name)
+        inp = WL.make_inputs(w)
+        sets = [bench.BufferSet(_t, ops, inp, w, dedup, dev, receive) for _ in range(2)]
+        bench.prepare_sets(_t, ops, sets, w, dedup, receive)
+        pipe = mode == "pipe"
+        calls = [bench.raw_step_calls(_t, ops, b, w, dedup, receive, 2, None, mode != "separate",
+                                      None, "dispatch", mode == "one",
+                                      sets[(i + 1) % 2] if pipe else None)
+                 for i, b in enumerate(sets)]
+        runs.append((sets, calls))   # the sets stay alive: the calls hold their raw pointers
+
+    def steps(n):
+        for _, calls in runs:
+            for i in range(n):
+                for fn, args in calls[i % 2]:
+                    assert fn(*args) == 0
+        _t.cuda.synchronize()
+
+    steps(2)   # first launches: code objects and runtime resources
+    free0 = _t.cuda.mem_get_info()[0]
+    steps(6)
+    free1 = _t.cuda.mem_get_info()[0]
+    assert free1 == free0, (free0, free1)
