@@ -452,8 +452,12 @@ MOE_API int moe_placement_search(const int32_t* coselect, int n_experts, int n_r
     for (int r = 0; r < n_ranks; ++r)
       if (per[r] != n_experts / n_ranks) return MOE_EINVAL;
   }
-  return moe::placement_search(coselect, n_experts, n_ranks, initial, max_swaps, placement,
-                               objective, swaps);
+  try {
+    return moe::placement_search(coselect, n_experts, n_ranks, initial, max_swaps, placement,
+                                 objective, swaps);
+  } catch (...) {  // its host tables could not be allocated; no exception leaves the ABI
+    return MOE_EUNSUPPORTED;
+  }
 }
 
 MOE_API int moe_shuffle_fit(const int32_t* prev_idx, const int32_t* cur_idx,
@@ -493,5 +497,9 @@ MOE_API int moe_shuffle_assign(const float* scores, int64_t tokens, int n_ranks,
   if (tokens % n_ranks != 0) return MOE_EINVAL;
   if (tokens == 0) return MOE_OK;
   if (!scores || !owner) return MOE_EINVAL;
-  return moe::shuffle_assign(scores, tokens, n_ranks, owner);
+  try {
+    return moe::shuffle_assign(scores, tokens, n_ranks, owner);
+  } catch (...) {  // its host tables (16 bytes per token) could not be allocated
+    return MOE_EUNSUPPORTED;
+  }
 }

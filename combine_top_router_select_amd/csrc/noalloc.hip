@@ -37,13 +37,17 @@ void* g_scratch_ptr[kMaxDevices] = {};
 void* scratch_for_current_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (g_scratch_ptr[dev] == nullptr) {
-    void* ptr = nullptr;
-    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
-    g_scratch_ptr[dev] = ptr;
+  try {  // no exception leaves the ABI (a failed lock reads as a HIP error)
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+      void* ptr = nullptr;
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+      g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+  } catch (...) {
+    return nullptr;
   }
-  return g_scratch_ptr[dev];
 }
 
 }  // namespace

@@ -487,7 +487,8 @@ int moe_expand_reduce(const void* expert_out, const float* exp_gate, const int32
  *   swaps      host int out or NULL: swaps made.
  * Errors: MOE_EINVAL (null pointers, E % R != 0, max_swaps < 0, an initial
  *         placement with a value outside [0, R) or not E/R experts per rank),
- *         MOE_EUNSUPPORTED (E > 1024, R > 64). */
+ *         MOE_EUNSUPPORTED (E > 1024, R > 64, or its E x R host table could not
+ *         be allocated). */
 int moe_placement_search(const int32_t* coselect, int n_experts, int n_ranks,
                          const int32_t* initial, int max_swaps, int32_t* placement,
                          int64_t* objective, int* swaps);
@@ -534,7 +535,8 @@ int moe_shuffle_predict(const int32_t* prev_idx, const int32_t* cur_idx, int64_t
  * index), each to its highest-scoring rank that still has room (ties to the
  * lower rank).  Synchronous; host memory only.
  *   scores  host [T][R] fp32;  owner  host [T] int32 out.
- * Errors: MOE_EINVAL (T % R != 0, null pointers), MOE_EUNSUPPORTED (R > 64). */
+ * Errors: MOE_EINVAL (T % R != 0, null pointers), MOE_EUNSUPPORTED (R > 64, or its
+ *         16 bytes per token of host tables could not be allocated). */
 int moe_shuffle_assign(const float* scores, int64_t tokens, int n_ranks, int32_t* owner);
 
 #ifdef __cplusplus

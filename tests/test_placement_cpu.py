@@ -79,3 +79,19 @@ def test_shuffle_assign_errors():
     with pytest.raises(MoeError):
         ops.moe_shuffle_assign(torch.zeros((130, 65)))        # R > 64
     assert ops.moe_shuffle_assign(torch.zeros((0, 4))).numel() == 0
+
+
+def test_shuffle_assign_table_allocation_failure_is_an_error_code():
+    """A token count whose host tables cannot be allocated returns
+    MOE_EUNSUPPORTED instead of letting a C++ exception cross the C ABI (the
+    tables are allocated before the scores are read, so a placeholder scores
+    address is never dereferenced)."""
+    import ctypes
+    from combine_top_router_select_amd import _lib
+    L = _lib.lib()
+    owner = np.zeros(4, dtype=np.int32)
+    scores = np.zeros(4, dtype=np.float32)
+    rc = L.moe_shuffle_assign(scores.ctypes.data_as(ctypes.c_void_p), 1 << 62, 1,
+                              owner.ctypes.data_as(ctypes.c_void_p))
+    assert rc == 2   # MOE_EUNSUPPORTED
+    assert (owner == 0).all()
